@@ -1,0 +1,18 @@
+"""CPU oracle for the DiffusionGemma canvas denoise step — TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, float64 NumPy statement of what one denoise step computes, written from the
+pages' description of the method:
+  * "DiffusionGemma Technical Report 정리" (juhoplayground.github.io), cited as [TR §section]
+  * "Google DiffusionGemma 출시 – 병렬 블록 디코딩" explainer (molayo1419.me), cited as [PBD §section]
+  * "DiffusionGemma 완전분석" (cell-devlog.tistory.com), cited as [CA §section]
+
+Only `tests/`, `__graft_entry__.smoke()` and the `cpu_baseline` leg of `bench.py` may import,
+call or execute anything in this package.  It shares no code with the HIP library and never
+imports it: the two meet only through the seeded arrays of `synth/`.
+
+Parity status per function:
+  philox.philox4x32_10   pinned by statistics (uniformity, bit balance, avalanche) only — no
+                         known-answer vectors are available here, so its exact bit pattern is
+                         pinned to nothing outside itself ("parity unpinned" for the bits).
+  everything else        pinned by closed forms, invariants or brute force in tests/test_oracle_*.py
+"""
