@@ -75,7 +75,9 @@ def noise(x0, t, schedule, seed, step, vocab):
     x0 = np.asarray(x0)
     B, L = x0.shape
     wk, wt = philox.noise_words(seed, step, B, L)
-    keep = philox.unit_open_closed(wk) < float(kappa(schedule, t))
+    # the keep decision is taken against kappa rounded to float32, the precision in which the
+    # kernel holds it (the 24-bit uniform is exact in both)
+    keep = philox.unit_open_closed(wk) < float(np.float32(kappa(schedule, t)))
     return np.where(keep, x0, philox.token(wt, vocab))
 
 
