@@ -1,0 +1,211 @@
+"""Throughput of the canvas denoise step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: (at the first step of each canvas)
+the uniform canvas at t = 1, then dg_denoise_step (30-layer decoder over prefix cache + canvas)
+and dg_step_sample (fused LM head -> Step with lock-in) at the schedule's next grid point.
+Inputs (weights, caches) are resident in HBM before timing starts.
+
+    python bench.py [--steps K] [--warmup W] [--workload C2] [--no-cpu-baseline]
+
+Prints one JSON line.  `value` = canvas tokens refined per second (batch * 256 * steps/s).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=24)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="C2")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown", action="store_true", help="per-class kernel times after the timed region")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(cfg, W, kv, H_dev):
+    """The oracle, untuned, on a bounded sample of the same workload: one local and one global
+    decoder layer (all 256 canvas rows) and the sampler statistics for 8 rows over the full
+    vocabulary, scaled to one full step (local layers x n_local + global x n_global + 256/8 x
+    sampler sample)."""
+    import numpy as np
+    import torch
+    from oracle import model as M
+    from oracle import step as S
+    from oracle.numerics import rounder
+    from tests.helpers import np64, oracle_layer
+    from synth import gen
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    loc = next(l for l in range(cfg.n_layers) if not cfg.is_global(l))
+    glb = next(l for l in range(cfg.n_layers) if cfg.is_global(l))
+    rnd = rounder(cfg.act_dtype)
+    h0 = gen.resid_input(cfg.replace(resid_input=True)).numpy().astype(np.float64)
+    times = {}
+    for tag, l in (("local", loc), ("global", glb)):
+        lw = oracle_layer(W["layers"][l], cfg)                  # conversion: not timed
+        K, V = np64(kv[l][0]), np64(kv[l][1])
+        t0 = time.perf_counter()
+        M.denoise_layer(cfg, l, h0, lw, K, V, [cfg.prefix] * cfg.batch, rnd)
+        times[tag] = time.perf_counter() - t0
+        del lw, K, V
+    E = np64(W["embed"])
+    H = H_dev[:8].float().cpu().numpy().astype(np.float64)
+    rows = np.arange(8)
+    t0 = time.perf_counter()
+    z = S.logits(H, E, cfg.tau)
+    S.sample_stats(z, cfg.seed, 1, rows // cfg.canvas, rows % cfg.canvas)
+    times["sampler8"] = time.perf_counter() - t0
+    n_glob = sum(cfg.is_global(l) for l in range(cfg.n_layers))
+    n_loc = cfg.n_layers - n_glob
+    t_step = n_loc * times["local"] + n_glob * times["global"] + (cfg.rows / 8) * times["sampler8"]
+    sample_s = times["local"] + times["global"] + times["sampler8"]
+    return {"value": round(cfg.rows / t_step, 3), "unit": "canvas-token-steps/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"oracle float64 on host: one local layer ({times['local']:.2f} s) + one global layer "
+                       f"({times['global']:.2f} s) over all {cfg.rows} rows, sampler for 8 of {cfg.rows} rows "
+                       f"({times['sampler8']:.2f} s); scaled to {n_loc} local + {n_glob} global layers + "
+                       f"{cfg.rows} sampler rows = {t_step:.1f} s per step; {sample_s:.1f} s measured")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from discrete_text_diffusion_amd import dg
+    from discrete_text_diffusion_amd.model import Model
+    from synth import configs, gen
+
+    cfg = configs.get(args.workload)
+    dev = torch.device("cuda:0")
+    log(f"[bench] workload {cfg.name}: building inputs on {torch.cuda.get_device_name(0)}")
+    t0 = time.time()
+    W = gen.make_weights(cfg, dev)
+    kv = gen.make_random_kv(cfg, dev)
+    model = Model(cfg, W, kv, [cfg.prefix] * cfg.batch)
+    B, L = cfg.batch, cfg.canvas
+    ws = model.workspace(B, L, cfg.prefix)
+    canvas = torch.empty(B, L, dtype=torch.int32, device=dev)
+    lock = torch.empty(B, L, dtype=torch.uint8, device=dev)
+    n_locked = torch.empty(B, dtype=torch.int32, device=dev)
+    hidden = torch.empty(B * L, cfg.d_model, dtype=torch.bfloat16 if cfg.act_dtype == "bf16" else torch.float32,
+                         device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.time() - t0:.1f} s; HBM used {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
+    T = cfg.steps
+    h = 1.0 / T
+    stream = torch.cuda.current_stream()
+
+    def step(s):
+        k = s % T
+        if k == 0:
+            dg.dg_init_canvas(canvas, lock, B, L, cfg.vocab, cfg.seed + s // T, stream)
+        model.denoise_step(canvas, L, ws, hidden_out=hidden, stream=stream)
+        p = dg.StepParams(schedule=cfg.schedule, t=1.0 - k * h, h=h, tau=cfg.tau, lock_threshold=cfg.lock_threshold,
+                          seed=cfg.seed, step=k)
+        model.step_sample(hidden, canvas, lock, n_locked, p, ws, stream=stream)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps done")
+    assert dg.dg_query_status(model.ctx, ws) == dg.DG_OK, "non-finite values during warmup"
+
+    dg.dg_profile_enable(model.ctx, 1 << dg.PROF_MOE_GATE_UP)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for s in range(args.steps):
+        step(args.warmup + s)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    dg.dg_profile_enable(model.ctx, 0)
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    moe_ms, moe_n = dg.dg_profile_read(model.ctx, dg.PROF_MOE_GATE_UP)
+    log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step")
+
+    # unique experts of the last layer's routing (same workload in every layer)
+    idx = torch.empty(B * L, cfg.top_k, dtype=torch.int32, device=dev)
+    dg.dg_test_read_routing(model.ctx, ws, B * L, None, idx, None, stream)
+    torch.cuda.synchronize()
+    uniq = int(torch.unique(idx).numel())
+    wbytes = 1 if cfg.expert_dtype == "fp8" else 2
+    gate_up_bytes = uniq * 2 * cfg.expert_hidden * cfg.d_model * wbytes
+    moe_avg_ms = moe_ms / max(moe_n, 1)
+    achieved = gate_up_bytes / (moe_avg_ms * 1e-3) / 1e9
+
+    breakdown = None
+    if args.breakdown:
+        dg.dg_profile_enable(model.ctx, (1 << 8) - 1)
+        for s in range(T):
+            step(s)
+        torch.cuda.synchronize()
+        dg.dg_profile_enable(model.ctx, 0)
+        breakdown = {}
+        for c, name in enumerate(dg.PROF_NAMES):
+            ms, n = dg.dg_profile_read(model.ctx, c)
+            breakdown[name] = {"ms_per_step": round(ms / T, 4), "launches_per_step": n // T}
+        log(f"[bench] breakdown {json.dumps(breakdown)}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle) ...")
+        H = torch.empty_like(hidden)
+        dg.dg_init_canvas(canvas, lock, B, L, cfg.vocab, cfg.seed, stream)
+        model.denoise_step(canvas, L, ws, hidden_out=H, stream=stream)
+        torch.cuda.synchronize()
+        cpu = cpu_baseline(cfg, W, kv, H)
+        log(f"[bench] cpu baseline {cpu}")
+
+    steps_per_s = 1000.0 / ms_step
+    out = {
+        "metric": "canvas-token denoise steps/sec (30L, 256 canvas, 1 MI355X) + % of roofline",
+        "value": round(steps_per_s * B * L, 1),
+        "unit": "canvas-token-steps/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "steps_per_s": round(steps_per_s, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.act_dtype if cfg.expert_dtype != "fp8" else "bf16+fp8w",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) caches, uniform canvas)",
+        "config": {"workload": f"{args.workload}: {cfg.name}", "layers": cfg.n_layers, "batch": B, "canvas": L,
+                   "prefix": cfg.prefix, "vocab": cfg.vocab, "d_model": cfg.d_model, "experts": cfg.n_experts,
+                   "top_k": cfg.top_k, "schedule_steps": T},
+        "roofline": {"kernel": "moe_gate_up (routed experts gate/up + SwiGLU)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_ms": round(moe_avg_ms, 5), "launches": moe_n,
+                     "algorithmic_bytes_per_launch": gate_up_bytes, "unique_experts": uniq},
+        "cpu_baseline": cpu,
+    }
+    if breakdown:
+        out["breakdown"] = breakdown
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,110 @@
+// Device-side building blocks shared by the gfx950 kernels of libdg.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define DG_DEV __device__ __forceinline__
+
+namespace dg {
+
+typedef uint16_t bf16_t;  // raw bf16 word
+
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8_v;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_v;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16 bytes, lives in VGPRs
+
+// ---------------------------------------------------------------- bf16 <-> f32 -------------------
+DG_DEV float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// round to nearest even; NaN stays NaN
+DG_DEV bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (bf16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+DG_DEV uint32_t pack_bf2(float a, float b) {
+  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+// element access for the two activation types
+template <class T> struct Elem;
+template <> struct Elem<float> {
+  static DG_DEV float load(const float* p) { return *p; }
+  static DG_DEV float to_f(float v) { return v; }
+  static DG_DEV float from_f(float v) { return v; }
+};
+template <> struct Elem<bf16_t> {
+  static DG_DEV float load(const bf16_t* p) { return bf2f(*p); }
+  static DG_DEV float to_f(bf16_t v) { return bf2f(v); }
+  static DG_DEV bf16_t from_f(float v) { return f2bf(v); }
+};
+
+// ---------------------------------------------------------------- MFMA -------------------------
+// 16x16 output tile; lane l holds rows 4*(l/16)+j (j = 0..3) of column l%16.
+// bf16: one 16x16x32 product; A lane supplies A[l%16][8*(l/16)..+7], B lane B[8*(l/16)..+7][l%16].
+// f32 : a 16-byte fragment holds 4 consecutive k; four 16x16x4 products, product j taking
+//       element j, so the 16 k of a fragment column are summed in full.
+template <class T> struct Mfma;
+template <> struct Mfma<bf16_t> {
+  static constexpr int K_PER_FRAG = 32;  // k covered by one 16-byte-per-lane fragment
+  static DG_DEV void mma(f32x4_v& acc, const u32x4& a, const u32x4& b) {
+    bf16x8_v av = *reinterpret_cast<const bf16x8_v*>(&a);
+    bf16x8_v bv = *reinterpret_cast<const bf16x8_v*>(&b);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+  }
+};
+template <> struct Mfma<float> {
+  static constexpr int K_PER_FRAG = 16;
+  static DG_DEV void mma(f32x4_v& acc, const u32x4& a, const u32x4& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+  }
+};
+
+// ---------------------------------------------------------------- wave reductions --------------
+DG_DEV float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+DG_DEV float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// ---------------------------------------------------------------- Philox4x32-10 ---------------
+// Salmon et al., SC'11: ten rounds; each multiplies counter words 0 and 2 by fixed constants,
+// mixes the high halves with words 1, 3 and the round key; the key is bumped by Weyl constants.
+DG_DEV u32x4 philox(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+    k0 += 0x9E3779B9u; k1 += 0xBB67AE85u;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+
+enum : uint32_t { TAG_GUMBEL = 0, TAG_JUMP = 1, TAG_INIT = 2, TAG_NOISE_KEEP = 3, TAG_NOISE_TOKEN = 4 };
+
+DG_DEV uint32_t pick(const u32x4& w, int j) {
+  return j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : w.w;
+}
+
+// (w >> 8) * 2^-24 in [0, 1): exact in float
+DG_DEV float unit_co(uint32_t w) { return (float)(w >> 8) * 5.9604644775390625e-08f; }
+// ((w >> 9) + 1/2) * 2^-23 in (0, 1): exact in float
+DG_DEV float unit_oo(uint32_t w) { return ((float)(w >> 9) + 0.5f) * 1.1920928955078125e-07f; }
+
+DG_DEV int32_t token_of(uint32_t w, int32_t vocab, int32_t vocab_log2) {
+  if (vocab_log2 >= 0) return vocab_log2 == 0 ? 0 : (int32_t)(w >> (32 - vocab_log2));
+  return (int32_t)(((uint64_t)w * (uint64_t)vocab) >> 32);
+}
+
+}  // namespace dg

@@ -1,0 +1,126 @@
+// Kernel launch interface between the host runtime (runtime.cpp) and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+constexpr int MAX_BATCH = 64;     // canvases per call (prefix lengths travel as kernel arguments)
+constexpr int GROUP_BM = 32;      // rows per expert tile of the grouped GEMMs
+
+enum WKind { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };
+enum Epi { EPI_STORE_F32 = 0, EPI_ADD_F32 = 1, EPI_STORE_ACT = 2, EPI_SWIGLU = 3, EPI_QKV = 4 };
+
+struct DenseArgs {
+  int epi;
+  const void* A; int64_t lda;            // activations [M][K]
+  const void* B; const void* B2;         // weights [N][K]; B2 = up matrix for SwiGLU
+  int64_t ldb;
+  const uint16_t* sB; const uint16_t* sB2;  // fp8 per-row scales (bf16)
+  int M, N, K;                           // N: output columns (SwiGLU: hidden width)
+  void* C; int64_t ldc;
+  const float* bias;                     // per-column fp32 bias or null
+  // QKV + RoPE
+  void* q_out; void* k_out; void* v_out; // q [M][Hq][dh]; k, v [B][Hkv][rows_per_canvas][dh]
+  int Hq, Hkv, dh, rows_per_canvas;
+  double log2_theta;
+  int32_t pos0[MAX_BATCH];               // RoPE position of row 0 of each canvas
+};
+
+struct GroupedArgs {
+  int epi;
+  const void* A; int64_t lda; const int32_t* a_tok;  // A row of grouped position p: a_tok[p] (or p)
+  const void* B; const void* B2; int64_t ldb; int64_t b_estride;
+  const uint16_t* sB; const uint16_t* sB2; int64_t s_estride;
+  int N, K;
+  const int32_t* work; const int32_t* n_items;       // (expert, first row) per tile
+  const int32_t* offsets; const int32_t* counts;
+  void* C; int64_t ldc;                               // output row = grouped position
+};
+
+hipError_t launch_dense(const DenseArgs& a, int act_bf16, int w_kind, hipStream_t s);
+hipError_t launch_grouped(const GroupedArgs& a, int act_bf16, int w_kind, int max_items, hipStream_t s);
+
+// ---- attention -------------------------------------------------------------------------------
+struct AttnArgs {
+  const void* q;          // [B*n][Hq][dh]
+  const void* kn; const void* vn;   // new/canvas keys, values [B][Hkv][n][dh]
+  const void* kc; const void* vc;   // cache [B][Hkv][cap][dh]
+  int B, n, Hq, Hkv, dh, cap;
+  int causal, window, is_global;
+  float scale_log2;       // log2(e) / sqrt(dh)
+  int splits, keys_per_split;       // key-range split (multiple of 64 keys)
+  float* part_o; float* part_ml;    // [splits][B*n][Hq][dh], [splits][B*n][Hq][2] (splits > 1)
+  void* out;              // [B*n][Hq*dh] act (splits == 1)
+  int32_t pos0[MAX_BATCH];          // prefix length per canvas
+};
+hipError_t launch_attention(const AttnArgs& a, int act_bf16, hipStream_t s);
+hipError_t launch_attn_merge(const AttnArgs& a, int act_bf16, hipStream_t s);
+
+// ---- elementwise / small kernels -------------------------------------------------------------
+hipError_t launch_embed(const int32_t* tokens, const void* embed, float* resid, int rows, int d,
+                        int vocab, int act_bf16, hipStream_t s);
+hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
+hipError_t launch_rmsnorm(const float* x, const void* g, void* y, int rows, int d, float eps,
+                          int act_bf16, int* status, hipStream_t s);
+hipError_t launch_kv_append(const void* kn, const void* vn, void* kc, void* vc, int B, int n,
+                            int Hkv, int dh, int cap, int window, int is_global,
+                            const int32_t* pos0, int act_bf16, hipStream_t s);
+hipError_t launch_moe_combine(float* resid, const float* y, const float* shared,
+                              const float* gates, const int32_t* inv_perm, int rows, int d,
+                              int k, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
+
+// ---- routing ---------------------------------------------------------------------------------
+hipError_t launch_router_topk(const float* logits, int T, int E, int k, int32_t* idx,
+                              float* gates, hipStream_t s);
+// counts/offsets [E], perm [T*k], inv_perm [T*k], tok [T*k] (token of grouped position),
+// work [2*max_items] + n_items for BM-row tiles.
+hipError_t launch_route_tables(const int32_t* idx, int T, int E, int k, int32_t* counts,
+                               int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* tok,
+                               int32_t* work, int32_t* n_items, int bm, hipStream_t s);
+size_t route_tables_lds(int E);
+
+// ---- sampler / Step --------------------------------------------------------------------------
+struct SampArgs {
+  const void* H; const void* E;   // [rows][d], [V][d] act
+  int rows, d, V, L;
+  float zscale_log2;              // log2(e) / tau
+  uint32_t k0, k1, step;          // Philox key (seed) and step index
+  int slices, v_per_slice;        // vocabulary split
+  float* part;                    // [slices][rows][5] partial (m2, s, a, g2, y) as floats/ints
+};
+hipError_t launch_lmhead_sampler(const SampArgs& a, int act_bf16, hipStream_t s);
+hipError_t launch_logits_partials(const float* z, int rows, int V, int L, float zscale_log2,
+                                  uint32_t k0, uint32_t k1, uint32_t step, int slices,
+                                  int v_per_slice, float* part, hipStream_t s);
+
+struct StepArgs {
+  const float* part; int slices;  // partials from the sampler
+  int B, L;
+  int32_t* canvas; uint8_t* lock; int32_t* n_locked; const int32_t* done;
+  float lam, theta;
+  uint32_t k0, k1, step;
+  float* stats;                   // [rows][5]: m, a, c, y, best (a, y stored as int bits)
+  int* status;
+  int32_t* steps_taken;           // incremented for canvases that stepped (or null)
+  int32_t* done_out;              // set when all positions locked (adaptive), or null
+};
+hipError_t launch_step_merge(const StepArgs& a, hipStream_t s);
+
+hipError_t launch_init_canvas(int32_t* canvas, uint8_t* lock, int B, int L, int V, uint32_t k0,
+                              uint32_t k1, hipStream_t s);
+hipError_t launch_noise(const int32_t* x0, int32_t* xt, int B, int L, int V, float kappa,
+                        uint32_t k0, uint32_t k1, uint32_t step, hipStream_t s);
+
+}  // namespace dg
+
+namespace dg {
+// Kernels needing more than 64 KB of dynamic LDS must say so once before their first launch.
+template <class F>
+inline hipError_t allow_lds(F* f, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(f), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)bytes);
+}
+}  // namespace dg

@@ -1,0 +1,305 @@
+// Canvas attention: every query row of the canvas attends to the visible prefix cache slots and
+// to all canvas keys (bidirectional, [TR §아키텍처와 블록 자기회귀 생성]); the same kernel with
+// `causal` set serves the causal encoder (prefill), with the sliding window on local layers.
+//
+// Work item = (canvas b, KV head g, 64 query rows of the G = Hq/Hkv heads sharing g, key split).
+// Each wave owns 16 query rows.  Per 64-key tile (K row-major and V transposed in LDS):
+//   S^T = K . Q^T     (A = K from LDS, B = Q^T from registers)   -> lane holds one query column
+//   online softmax    (per lane; row max over the 4 lanes of a column by two xor-shuffles)
+//   O^T += V^T . P^T  (A = V^T from LDS, B = P^T straight from the S^T registers)
+// so probabilities never leave registers and the row rescale is lane-local.  With one split the
+// kernel normalises and writes o; otherwise it writes (O, m, l) partials merged by
+// attn_merge_kernel in split order.
+#include "common.h"
+#include "internal.h"
+
+namespace dg {
+
+constexpr int AT_KEYS = 64;
+
+template <class T, int DH>
+struct AttnCfg {
+  static constexpr int ESZ = sizeof(T);
+  static constexpr int EPL = 16 / ESZ;                    // elements per 16-byte fragment
+  static constexpr int KPF = Mfma<T>::K_PER_FRAG;         // k per fragment (32 bf16, 16 f32)
+  static constexpr int NCH = DH / KPF;                    // fragments along head_dim
+  static constexpr int K_STRIDE = DH * ESZ + 16;          // bytes per K row in LDS
+  static constexpr int V_STRIDE = AT_KEYS * ESZ + 16;     // bytes per V^T row (one d) in LDS
+  static constexpr int LDS_K = AT_KEYS * K_STRIDE;
+  static constexpr int LDS_V = DH * V_STRIDE;
+  static constexpr int LDS = LDS_K + LDS_V;
+  static constexpr int CH_ROW = DH * ESZ / 16;            // 16-byte chunks per key row
+  static constexpr int CHUNKS = AT_KEYS * CH_ROW / 256;   // per thread, per tensor
+  static constexpr int DB = DH / 16;                      // 16-row blocks of head_dim
+};
+
+template <class T>
+DG_DEV void put_elem(char* p, float v);
+template <> DG_DEV void put_elem<bf16_t>(char* p, float v) { *reinterpret_cast<bf16_t*>(p) = f2bf(v); }
+template <> DG_DEV void put_elem<float>(char* p, float v) { *reinterpret_cast<float*>(p) = v; }
+
+template <class T, int DH>
+__global__ __launch_bounds__(256) void attn_kernel(AttnArgs p) {
+  using C = AttnCfg<T, DH>;
+  extern __shared__ __align__(16) char lds[];
+  char* lk = lds;
+  char* lv = lds + C::LDS_K;
+  const int G = p.Hq / p.Hkv;
+  const int mrows = G * p.n;                     // query rows sharing one KV head
+  const int qtiles = (mrows + 63) / 64;
+  int id = blockIdx.x;
+  const int split = id % p.splits; id /= p.splits;
+  const int qt = id % qtiles; id /= qtiles;
+  const int g = id % p.Hkv;
+  const int b = id / p.Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int P = p.pos0[b];
+  const int np = p.is_global ? P : min(P, p.window);       // visible prefix slots
+  const int nkeys = np + p.n;
+  const int k_begin = split * p.keys_per_split;
+  const int k_end = min(nkeys, k_begin + p.keys_per_split);
+
+  // this lane's query column
+  const int mq = qt * 64 + wave * 16 + (lane & 15);
+  const bool q_ok = mq < mrows;
+  const int hj = q_ok ? mq / p.n : 0, qi = q_ok ? mq - hj * p.n : 0;
+  const int head = g * G + hj;
+  const int qpos = P + qi;
+  const int kg = lane >> 4;
+
+  u32x4 qf[C::NCH];
+  {
+    const char* qrow = static_cast<const char*>(p.q) + (((int64_t)(b * p.n + qi) * p.Hq + head) * DH) * C::ESZ;
+#pragma unroll
+    for (int c = 0; c < C::NCH; ++c)
+      qf[c] = q_ok ? *reinterpret_cast<const u32x4*>(qrow + (c * C::KPF + kg * C::EPL) * C::ESZ)
+                   : u32x4{0, 0, 0, 0};
+  }
+
+  f32x4_v acc[C::DB];
+#pragma unroll
+  for (int i = 0; i < C::DB; ++i) acc[i] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_lane = 0.f;
+
+  const char* kc = static_cast<const char*>(p.kc) + ((int64_t)(b * p.Hkv + g) * p.cap) * DH * C::ESZ;
+  const char* vc = static_cast<const char*>(p.vc) + ((int64_t)(b * p.Hkv + g) * p.cap) * DH * C::ESZ;
+  const char* kn = static_cast<const char*>(p.kn) + ((int64_t)(b * p.Hkv + g) * p.n) * DH * C::ESZ;
+  const char* vn = static_cast<const char*>(p.vn) + ((int64_t)(b * p.Hkv + g) * p.n) * DH * C::ESZ;
+  const int ring_lo = max(0, P - p.window);
+
+  for (int k0 = k_begin; k0 < k_end; k0 += AT_KEYS) {
+    // ---- stage K (row-major) and V (transposed) ------------------------------------------
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < C::CHUNKS; ++it) {
+      const int q = threadIdx.x + 256 * it;
+      const int r = q / C::CH_ROW, ch = q % C::CH_ROW;
+      const int kk = k0 + r;
+      u32x4 kv = {0, 0, 0, 0};
+      if (kk < k_end) {
+        const char* src = kk < np ? kc + (int64_t)kk * DH * C::ESZ : kn + (int64_t)(kk - np) * DH * C::ESZ;
+        kv = *reinterpret_cast<const u32x4*>(src + ch * 16);
+      }
+      *reinterpret_cast<u32x4*>(lk + r * C::K_STRIDE + ch * 16) = kv;
+    }
+#pragma unroll
+    for (int it = 0; it < C::CHUNKS; ++it) {
+      const int q = threadIdx.x + 256 * it;
+      // 16 consecutive keys x 4 chunks per 64 lanes: 64-byte global runs, narrow LDS spread
+      const int r = (q & 15) + 16 * ((q >> 6) & 3);
+      const int ch = ((q >> 4) & 3) + 4 * (q >> 8);
+      const int kk = k0 + r;
+      u32x4 vv = {0, 0, 0, 0};
+      if (kk < k_end) {
+        const char* src = kk < np ? vc + (int64_t)kk * DH * C::ESZ : vn + (int64_t)(kk - np) * DH * C::ESZ;
+        vv = *reinterpret_cast<const u32x4*>(src + ch * 16);
+      }
+      const int d0 = ch * C::EPL;
+      if constexpr (C::ESZ == 2) {
+        char* dst = lv + d0 * C::V_STRIDE + r * 2;
+        *reinterpret_cast<uint16_t*>(dst + 0 * C::V_STRIDE) = (uint16_t)(vv.x & 0xffff);
+        *reinterpret_cast<uint16_t*>(dst + 1 * C::V_STRIDE) = (uint16_t)(vv.x >> 16);
+        *reinterpret_cast<uint16_t*>(dst + 2 * C::V_STRIDE) = (uint16_t)(vv.y & 0xffff);
+        *reinterpret_cast<uint16_t*>(dst + 3 * C::V_STRIDE) = (uint16_t)(vv.y >> 16);
+        *reinterpret_cast<uint16_t*>(dst + 4 * C::V_STRIDE) = (uint16_t)(vv.z & 0xffff);
+        *reinterpret_cast<uint16_t*>(dst + 5 * C::V_STRIDE) = (uint16_t)(vv.z >> 16);
+        *reinterpret_cast<uint16_t*>(dst + 6 * C::V_STRIDE) = (uint16_t)(vv.w & 0xffff);
+        *reinterpret_cast<uint16_t*>(dst + 7 * C::V_STRIDE) = (uint16_t)(vv.w >> 16);
+      } else {
+        char* dst = lv + d0 * C::V_STRIDE + r * 4;
+        *reinterpret_cast<uint32_t*>(dst + 0 * C::V_STRIDE) = vv.x;
+        *reinterpret_cast<uint32_t*>(dst + 1 * C::V_STRIDE) = vv.y;
+        *reinterpret_cast<uint32_t*>(dst + 2 * C::V_STRIDE) = vv.z;
+        *reinterpret_cast<uint32_t*>(dst + 3 * C::V_STRIDE) = vv.w;
+      }
+    }
+    __syncthreads();
+
+    // ---- S^T = K . Q^T --------------------------------------------------------------------
+    f32x4_v s[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      s[nb] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+      const char* krow = lk + (nb * 16 + (lane & 15)) * C::K_STRIDE + kg * 16;
+#pragma unroll
+      for (int c = 0; c < C::NCH; ++c)
+        Mfma<T>::mma(s[nb], *reinterpret_cast<const u32x4*>(krow + c * C::KPF * C::ESZ), qf[c]);
+    }
+    // ---- scale, mask, online softmax --------------------------------------------------------
+    float mt = -INFINITY;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kk = k0 + nb * 16 + 4 * kg + j;
+        bool vis = kk < k_end;
+        if (p.causal && vis) {
+          int kpos;
+          if (kk >= np) kpos = P + (kk - np);
+          else kpos = p.is_global ? kk : ring_lo + ((kk - ring_lo) % p.window + p.window) % p.window;
+          vis = kpos <= qpos && (p.is_global || qpos - kpos < p.window);
+        }
+        const float v = vis ? s[nb][j] * p.scale_log2 : -INFINITY;
+        s[nb][j] = v;
+        mt = fmaxf(mt, v);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = (m_new == -INFINITY || m_run == -INFINITY) ? (m_run == -INFINITY ? 0.f : 1.f)
+                                                                 : exp2f(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float e = (s[nb][j] == -INFINITY) ? 0.f : exp2f(s[nb][j] - m_new);
+        s[nb][j] = e;
+        psum += e;
+      }
+    l_lane = l_lane * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < C::DB; ++i) acc[i] *= alpha;
+
+    // ---- O^T += V^T . P^T --------------------------------------------------------------------
+    if constexpr (C::ESZ == 2) {
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        u32x4 pb;
+        pb.x = pack_bf2(s[2 * c2][0], s[2 * c2][1]);
+        pb.y = pack_bf2(s[2 * c2][2], s[2 * c2][3]);
+        pb.z = pack_bf2(s[2 * c2 + 1][0], s[2 * c2 + 1][1]);
+        pb.w = pack_bf2(s[2 * c2 + 1][2], s[2 * c2 + 1][3]);
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const char* vrow = lv + (db * 16 + (lane & 15)) * C::V_STRIDE;
+          const uint2 lo = *reinterpret_cast<const uint2*>(vrow + (32 * c2 + 4 * kg) * 2);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (32 * c2 + 16 + 4 * kg) * 2);
+          const u32x4 va = {lo.x, lo.y, hi.x, hi.y};
+          Mfma<T>::mma(acc[db], va, pb);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const u32x4 pb = {__float_as_uint(s[nb][0]), __float_as_uint(s[nb][1]),
+                          __float_as_uint(s[nb][2]), __float_as_uint(s[nb][3])};
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const char* vrow = lv + (db * 16 + (lane & 15)) * C::V_STRIDE;
+          const u32x4 va = *reinterpret_cast<const u32x4*>(vrow + (16 * nb + 4 * kg) * 4);
+          Mfma<T>::mma(acc[db], va, pb);
+        }
+      }
+    }
+  }
+
+  // ---- finish: total l over the 4 lanes of the column ----------------------------------------
+  float l = l_lane + __shfl_xor(l_lane, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (!q_ok) return;
+  const int64_t row = (int64_t)b * p.n + qi;
+  if (p.splits == 1) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    char* o = static_cast<char*>(p.out) + ((row * p.Hq + head) * DH) * C::ESZ;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) put_elem<T>(o + (db * 16 + 4 * kg + j) * C::ESZ, acc[db][j] * inv);
+  } else {
+    float* o = p.part_o + (((int64_t)split * p.B * p.n + row) * p.Hq + head) * DH;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+      *reinterpret_cast<f32x4_v*>(o + db * 16 + 4 * kg) = acc[db];
+    if (kg == 0) {
+      float* ml = p.part_ml + (((int64_t)split * p.B * p.n + row) * p.Hq + head) * 2;
+      ml[0] = m_run;
+      ml[1] = l;
+    }
+  }
+}
+
+// merge split partials in split order: o = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M)
+template <class T>
+__global__ void attn_merge_kernel(AttnArgs p) {
+  const int64_t rows = (int64_t)p.B * p.n * p.Hq;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (row, head, d/4)
+  const int dq = p.dh / 4;
+  if (idx >= rows * dq) return;
+  const int64_t rh = idx / dq;
+  const int d4 = (int)(idx - rh * dq) * 4;
+  float M = -INFINITY;
+  for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.part_ml[((int64_t)s * rows + rh) * 2]);
+  float L = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+  for (int s = 0; s < p.splits; ++s) {
+    const float m = p.part_ml[((int64_t)s * rows + rh) * 2];
+    if (m == -INFINITY) continue;
+    const float w = exp2f(m - M);
+    L += p.part_ml[((int64_t)s * rows + rh) * 2 + 1] * w;
+    const f32x4_v v = *reinterpret_cast<const f32x4_v*>(p.part_o + ((int64_t)s * rows + rh) * p.dh + d4);
+    o0 += v[0] * w; o1 += v[1] * w; o2 += v[2] * w; o3 += v[3] * w;
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  T* out = static_cast<T*>(p.out) + rh * p.dh + d4;
+  out[0] = Elem<T>::from_f(o0 * inv); out[1] = Elem<T>::from_f(o1 * inv);
+  out[2] = Elem<T>::from_f(o2 * inv); out[3] = Elem<T>::from_f(o3 * inv);
+}
+
+template <class T, int DH>
+static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
+  using C = AttnCfg<T, DH>;
+  const int qtiles = (a.Hq / a.Hkv * a.n + 63) / 64;
+  const int blocks = a.B * a.Hkv * qtiles * a.splits;
+  static const hipError_t attr = allow_lds(attn_kernel<T, DH>, C::LDS);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((attn_kernel<T, DH>), dim3(blocks), dim3(256), C::LDS, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(const AttnArgs& a, int act_bf16, hipStream_t s) {
+  if (act_bf16) {
+    switch (a.dh) {
+      case 64: return launch_attn_t<bf16_t, 64>(a, s);
+      case 128: return launch_attn_t<bf16_t, 128>(a, s);
+      case 256: return launch_attn_t<bf16_t, 256>(a, s);
+    }
+  } else {
+    switch (a.dh) {
+      case 64: return launch_attn_t<float, 64>(a, s);
+      case 128: return launch_attn_t<float, 128>(a, s);
+      case 256: return launch_attn_t<float, 256>(a, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_merge(const AttnArgs& a, int act_bf16, hipStream_t s) {
+  const int64_t n = (int64_t)a.B * a.n * a.Hq * (a.dh / 4);
+  const int blocks = (int)((n + 255) / 256);
+  if (act_bf16) hipLaunchKernelGGL(attn_merge_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(attn_merge_kernel<float>, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace dg

@@ -1,0 +1,288 @@
+// Dense and expert-grouped GEMMs of the decoder layer with their fused epilogues:
+//   QKV projection + RoPE + scatter to q / canvas k / canvas v,
+//   attention output projection + residual add,
+//   router logits (+ bias),
+//   shared- and routed-expert SwiGLU (gate and up in one tile) and down projections.
+// W8A16: fp8 e4m3 weights are widened to bf16 in the tile loader; the per-output-row scale is
+// applied to the fp32 accumulator in the epilogue.
+#include "gemm_core.h"
+#include "internal.h"
+
+namespace dg {
+
+// ---------------------------------------------------------------- B-row maps ----------------
+// A tile column block of 16 columns; "paired" maps put the two members of a pair (gate/up, or
+// RoPE partners j and j + dh/2) in adjacent blocks so one lane holds both.
+enum BMap { MAP_PLAIN = 0, MAP_SWIGLU = 1, MAP_ROPE = 2 };
+
+template <int BN>
+DG_DEV void paired_col(int r, int& u, int& half, int& c) {
+  const int nb = r >> 4;
+  c = r & 15;
+  u = nb >> 1;
+  half = nb & 1;
+}
+
+template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI, int MAP>
+__global__ __launch_bounds__(256) void gemm_dense_kernel(DenseArgs p) {
+  using G = GemmTile<TA, TB, BM, BN, WM, WN>;
+  extern __shared__ __align__(16) char lds[];
+  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+  const TA* A = static_cast<const TA*>(p.A);
+  const TB* B = static_cast<const TB*>(p.B);
+  const TB* B2 = static_cast<const TB*>(p.B2);
+  auto arow = [&](int r) -> const TA* {
+    const int m = m0 + r;
+    return m < p.M ? A + (int64_t)m * p.lda : nullptr;
+  };
+  auto brow = [&](int r) -> const TB* {
+    if constexpr (MAP == MAP_PLAIN) {
+      const int n = n0 + r;
+      return n < p.N ? B + (int64_t)n * p.ldb : nullptr;
+    } else if constexpr (MAP == MAP_SWIGLU) {
+      int u, half, c;
+      paired_col<BN>(r, u, half, c);
+      const int oc = n0 / 2 + u * 16 + c;
+      if (oc >= p.N) return nullptr;
+      return (half ? B2 : B) + (int64_t)oc * p.ldb;
+    } else {  // MAP_ROPE: tile inside one head
+      int u, half, c;
+      paired_col<BN>(r, u, half, c);
+      const int head = n0 / p.dh, pb = (n0 % p.dh) / 2;
+      const int row = head * p.dh + half * (p.dh / 2) + pb + u * 16 + c;
+      return B + (int64_t)row * p.ldb;
+    }
+  };
+  G g;
+  g.setup(arow, brow);
+  f32x4_v acc[G::FM][G::FN];
+  g.run(lds, p.K, acc);
+
+  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) % WN;
+  if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_ADD_F32 || EPI == EPI_STORE_ACT) {
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j) {
+      const int n = n0 + G::col_of(j);
+      if (n >= p.N) continue;
+      float sc = 1.f;
+      if constexpr (sizeof(TB) == 1) sc = bf2f(p.sB[n]);
+      const float bias = p.bias ? p.bias[n] : 0.f;
+#pragma unroll
+      for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = m0 + G::row_of(i, e);
+          if (m >= p.M) continue;
+          const float v = acc[i][j][e] * sc + bias;
+          if constexpr (EPI == EPI_STORE_F32) {
+            static_cast<float*>(p.C)[(int64_t)m * p.ldc + n] = v;
+          } else if constexpr (EPI == EPI_ADD_F32) {
+            static_cast<float*>(p.C)[(int64_t)m * p.ldc + n] += v;
+          } else {
+            static_cast<TA*>(p.C)[(int64_t)m * p.ldc + n] = Elem<TA>::from_f(v);
+          }
+        }
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+    for (int j = 0; j < G::FN; j += 2) {
+      const int u = (wn * G::FN + j) >> 1;
+      const int oc = n0 / 2 + u * 16 + (lane & 15);
+      if (oc >= p.N) continue;
+      float sg = 1.f, su = 1.f;
+      if constexpr (sizeof(TB) == 1) { sg = bf2f(p.sB[oc]); su = bf2f(p.sB2[oc]); }
+#pragma unroll
+      for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = m0 + G::row_of(i, e);
+          if (m >= p.M) continue;
+          const float gt = acc[i][j][e] * sg, up = acc[i][j + 1][e] * su;
+          const float a = gt / (1.f + __expf(-gt)) * up;
+          static_cast<TA*>(p.C)[(int64_t)m * p.ldc + oc] = Elem<TA>::from_f(a);
+        }
+    }
+  } else if constexpr (EPI == EPI_QKV) {
+    const int dh = p.dh, half_dh = dh / 2;
+    const int head = n0 / dh, pb = (n0 % dh) / 2;
+    const bool rot = head < p.Hq + p.Hkv;
+#pragma unroll
+    for (int j = 0; j < G::FN; j += 2) {
+      const int u = (wn * G::FN + j) >> 1;
+      const int jj = pb + u * 16 + (lane & 15);          // pair index in [0, dh/2)
+      const double inv = exp2(-2.0 * jj / dh * p.log2_theta);
+#pragma unroll
+      for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = m0 + G::row_of(i, e);
+          if (m >= p.M) continue;
+          const int b = m / p.rows_per_canvas, ii = m - b * p.rows_per_canvas;
+          float x1 = acc[i][j][e], x2 = acc[i][j + 1][e];
+          if (rot) {
+            const double ang = (double)(p.pos0[b] + ii) * inv;
+            const double red = ang - 6.283185307179586 * floor(ang * 0.15915494309189535);
+            float sn, cs;
+            sincosf((float)red, &sn, &cs);
+            const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
+            x1 = y1; x2 = y2;
+          }
+          TA* dst;
+          if (head < p.Hq) {
+            dst = static_cast<TA*>(p.q_out) + ((int64_t)m * p.Hq + head) * dh;
+          } else {
+            const int g = head < p.Hq + p.Hkv ? head - p.Hq : head - p.Hq - p.Hkv;
+            TA* base = static_cast<TA*>(head < p.Hq + p.Hkv ? p.k_out : p.v_out);
+            dst = base + (((int64_t)b * p.Hkv + g) * p.rows_per_canvas + ii) * dh;
+          }
+          dst[jj] = Elem<TA>::from_f(x1);
+          dst[jj + half_dh] = Elem<TA>::from_f(x2);
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- grouped (MoE) ----------------
+// Work item w < *n_items: expert e = work[2w], first row m0 = work[2w+1] of that expert's rows
+// [offsets[e], offsets[e] + counts[e]) in grouped order.
+template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI>
+__global__ __launch_bounds__(256) void gemm_grouped_kernel(GroupedArgs p) {
+  using G = GemmTile<TA, TB, BM, BN, WM, WN>;
+  extern __shared__ __align__(16) char lds[];
+  const int item = blockIdx.y;
+  if (item >= *p.n_items) return;
+  const int e = p.work[2 * item], m0 = p.work[2 * item + 1];
+  const int base = p.offsets[e] + m0;
+  const int rows = min(BM, p.counts[e] - m0);
+  const int n0 = blockIdx.x * BN;
+  const TA* A = static_cast<const TA*>(p.A);
+  const TB* B = static_cast<const TB*>(p.B) + (int64_t)e * p.b_estride;
+  const TB* B2 = p.B2 ? static_cast<const TB*>(p.B2) + (int64_t)e * p.b_estride : nullptr;
+  auto arow = [&](int r) -> const TA* {
+    if (r >= rows) return nullptr;
+    const int src = p.a_tok ? p.a_tok[base + r] : base + r;
+    return A + (int64_t)src * p.lda;
+  };
+  auto brow = [&](int r) -> const TB* {
+    if constexpr (EPI == EPI_SWIGLU) {
+      int u, half, c;
+      paired_col<BN>(r, u, half, c);
+      const int oc = n0 / 2 + u * 16 + c;
+      if (oc >= p.N) return nullptr;
+      return (half ? B2 : B) + (int64_t)oc * p.ldb;
+    } else {
+      const int n = n0 + r;
+      return n < p.N ? B + (int64_t)n * p.ldb : nullptr;
+    }
+  };
+  G g;
+  g.setup(arow, brow);
+  f32x4_v acc[G::FM][G::FN];
+  g.run(lds, p.K, acc);
+
+  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) % WN;
+  const bf16_t* sB = p.sB ? p.sB + (int64_t)e * p.s_estride : nullptr;
+  const bf16_t* sB2 = p.sB2 ? p.sB2 + (int64_t)e * p.s_estride : nullptr;
+  if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+    for (int j = 0; j < G::FN; j += 2) {
+      const int u = (wn * G::FN + j) >> 1;
+      const int oc = n0 / 2 + u * 16 + (lane & 15);
+      if (oc >= p.N) continue;
+      float sg = 1.f, su = 1.f;
+      if constexpr (sizeof(TB) == 1) { sg = bf2f(sB[oc]); su = bf2f(sB2[oc]); }
+#pragma unroll
+      for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = G::row_of(i, q);
+          if (r >= rows) continue;
+          const float gt = acc[i][j][q] * sg, up = acc[i][j + 1][q] * su;
+          const float a = gt / (1.f + __expf(-gt)) * up;
+          static_cast<TA*>(p.C)[(int64_t)(base + r) * p.ldc + oc] = Elem<TA>::from_f(a);
+        }
+    }
+  } else {  // EPI_STORE_F32
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j) {
+      const int n = n0 + G::col_of(j);
+      if (n >= p.N) continue;
+      float sc = 1.f;
+      if constexpr (sizeof(TB) == 1) sc = bf2f(sB[n]);
+#pragma unroll
+      for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = G::row_of(i, q);
+          if (r >= rows) continue;
+          static_cast<float*>(p.C)[(int64_t)(base + r) * p.ldc + n] = acc[i][j][q] * sc;
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launchers --------------------
+template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI, int MAP>
+static hipError_t launch_dense_t(const DenseArgs& a, int n_eff, hipStream_t s) {
+  using G = GemmTile<TA, TB, BM, BN, WM, WN>;
+  dim3 grid((n_eff + BN - 1) / BN, (a.M + BM - 1) / BM);
+  static const hipError_t attr = allow_lds(gemm_dense_kernel<TA, TB, BM, BN, WM, WN, EPI, MAP>, G::LDS_BYTES);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((gemm_dense_kernel<TA, TB, BM, BN, WM, WN, EPI, MAP>), grid, dim3(256),
+                     G::LDS_BYTES, s, a);
+  return hipGetLastError();
+}
+
+template <class TA, class TB, int EPI, int MAP>
+static hipError_t dense_pick(const DenseArgs& a, int n_eff, hipStream_t s) {
+  // small M: 32-row tiles with 4 waves along N; else 64 x 64 tiles, 2 x 2 waves
+  if (a.M <= 32) return launch_dense_t<TA, TB, 32, 64, 2, 2, EPI, MAP>(a, n_eff, s);
+  return launch_dense_t<TA, TB, 64, 64, 2, 2, EPI, MAP>(a, n_eff, s);
+}
+
+template <class TA, class TB>
+static hipError_t dense_dispatch(const DenseArgs& a, hipStream_t s) {
+  switch (a.epi) {
+    case EPI_STORE_F32: return dense_pick<TA, TB, EPI_STORE_F32, MAP_PLAIN>(a, a.N, s);
+    case EPI_ADD_F32: return dense_pick<TA, TB, EPI_ADD_F32, MAP_PLAIN>(a, a.N, s);
+    case EPI_STORE_ACT: return dense_pick<TA, TB, EPI_STORE_ACT, MAP_PLAIN>(a, a.N, s);
+    case EPI_SWIGLU: return dense_pick<TA, TB, EPI_SWIGLU, MAP_SWIGLU>(a, 2 * a.N, s);
+    case EPI_QKV: return dense_pick<TA, TB, EPI_QKV, MAP_ROPE>(a, a.N, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_dense(const DenseArgs& a, int act_bf16, int w_kind, hipStream_t s) {
+  if (!act_bf16) return dense_dispatch<float, float>(a, s);
+  if (w_kind == W_FP8) {
+    if (a.epi == EPI_QKV) return hipErrorInvalidValue;
+    return dense_dispatch<bf16_t, fp8_t>(a, s);
+  }
+  return dense_dispatch<bf16_t, bf16_t>(a, s);
+}
+
+template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI>
+static hipError_t launch_grouped_t(const GroupedArgs& a, int n_eff, int max_items, hipStream_t s) {
+  using G = GemmTile<TA, TB, BM, BN, WM, WN>;
+  dim3 grid((n_eff + BN - 1) / BN, max_items);
+  static const hipError_t attr = allow_lds(gemm_grouped_kernel<TA, TB, BM, BN, WM, WN, EPI>, G::LDS_BYTES);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((gemm_grouped_kernel<TA, TB, BM, BN, WM, WN, EPI>), grid, dim3(256),
+                     G::LDS_BYTES, s, a);
+  return hipGetLastError();
+}
+
+template <class TA, class TB>
+static hipError_t grouped_dispatch(const GroupedArgs& a, int max_items, hipStream_t s) {
+  if (a.epi == EPI_SWIGLU)
+    return launch_grouped_t<TA, TB, GROUP_BM, 128, 1, 4, EPI_SWIGLU>(a, 2 * a.N, max_items, s);
+  return launch_grouped_t<TA, TB, GROUP_BM, 128, 1, 4, EPI_STORE_F32>(a, a.N, max_items, s);
+}
+
+hipError_t launch_grouped(const GroupedArgs& a, int act_bf16, int w_kind, int max_items, hipStream_t s) {
+  if (!act_bf16) return grouped_dispatch<float, float>(a, max_items, s);
+  if (w_kind == W_FP8) return grouped_dispatch<bf16_t, fp8_t>(a, max_items, s);
+  return grouped_dispatch<bf16_t, bf16_t>(a, max_items, s);
+}
+
+}  // namespace dg

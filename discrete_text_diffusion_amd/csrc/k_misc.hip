@@ -1,0 +1,134 @@
+// Row-wise and elementwise kernels of the decoder layer: embedding lookup into the fp32 residual
+// stream, RMSNorm into the activation dtype, appending encoded keys/values to the caches, and
+// the MoE combine (slot-ordered gate-weighted sum of expert outputs + shared expert + residual).
+#include "common.h"
+#include "internal.h"
+
+namespace dg {
+
+template <class T>
+__global__ void embed_kernel(const int32_t* tok, const T* E, float* resid, int d, int V) {
+  const int r = blockIdx.x;
+  const int t = min(max(tok[r], 0), V - 1);     // out-of-range ids are clamped, never read past E
+  const T* src = E + (int64_t)t * d;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) resid[(int64_t)r * d + c] = Elem<T>::to_f(src[c]);
+}
+
+hipError_t launch_embed(const int32_t* tok, const void* E, float* resid, int rows, int d, int V, int bf,
+                        hipStream_t s) {
+  if (bf) hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(rows), dim3(256), 0, s, tok, (const bf16_t*)E, resid, d, V);
+  else hipLaunchKernelGGL(embed_kernel<float>, dim3(rows), dim3(256), 0, s, tok, (const float*)E, resid, d, V);
+  return hipGetLastError();
+}
+
+__global__ void copy_f32_kernel(const float* a, float* b, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) b[i] = a[i];
+}
+
+hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s) {
+  hipLaunchKernelGGL(copy_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, dst, n);
+  return hipGetLastError();
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int32_t v, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s) {
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+
+// y = x / sqrt(mean(x^2) + eps) * g, one block per row; flags a non-finite row in *status
+template <class T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, const T* g, T* y, int d, float eps,
+                                                      int* status) {
+  const int r = blockIdx.x;
+  const float* xr = x + (int64_t)r * d;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < d; c += 256) { const float v = xr[c]; ss += v * v; }
+  ss = wave_sum(ss);
+  __shared__ float part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = part[0] + part[1] + part[2] + part[3];
+  const float inv = rsqrtf(tot / (float)d + eps);
+  if (threadIdx.x == 0 && status && !isfinite(tot)) atomicOr(status, 2);
+  for (int c = threadIdx.x; c < d; c += 256)
+    y[(int64_t)r * d + c] = Elem<T>::from_f(xr[c] * inv * Elem<T>::to_f(g[c]));
+}
+
+hipError_t launch_rmsnorm(const float* x, const void* g, void* y, int rows, int d, float eps, int bf,
+                          int* status, hipStream_t s) {
+  if (bf) hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(rows), dim3(256), 0, s, x, (const bf16_t*)g, (bf16_t*)y, d, eps, status);
+  else hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(rows), dim3(256), 0, s, x, (const float*)g, (float*)y, d, eps, status);
+  return hipGetLastError();
+}
+
+// new keys/values [B][Hkv][n][dh] -> cache slots: position p in slot p (global) or p % window
+// (local ring; only the last `window` of the new positions are kept)
+struct AppendArgs {
+  const char* kn; const char* vn; char* kc; char* vc;
+  int B, n, Hkv, row_bytes, cap, window, is_global;
+  int32_t pos0[MAX_BATCH];
+};
+
+__global__ void kv_append_kernel(AppendArgs a) {
+  const int chunks = a.row_bytes / 16;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)a.B * a.Hkv * a.n * chunks;
+  if (idx >= total) return;
+  const int ch = (int)(idx % chunks);
+  int64_t t = idx / chunks;
+  const int j = (int)(t % a.n); t /= a.n;
+  const int g = (int)(t % a.Hkv);
+  const int b = (int)(t / a.Hkv);
+  if (!a.is_global && j < a.n - a.window) return;
+  const int pos = a.pos0[b] + j;
+  const int slot = a.is_global ? pos : pos % a.window;
+  const int64_t src = (((int64_t)b * a.Hkv + g) * a.n + j) * a.row_bytes + ch * 16;
+  const int64_t dst = (((int64_t)b * a.Hkv + g) * a.cap + slot) * a.row_bytes + ch * 16;
+  *reinterpret_cast<u32x4*>(a.kc + dst) = *reinterpret_cast<const u32x4*>(a.kn + src);
+  *reinterpret_cast<u32x4*>(a.vc + dst) = *reinterpret_cast<const u32x4*>(a.vn + src);
+}
+
+hipError_t launch_kv_append(const void* kn, const void* vn, void* kc, void* vc, int B, int n, int Hkv,
+                            int dh, int cap, int window, int is_global, const int32_t* pos0, int bf,
+                            hipStream_t s) {
+  AppendArgs a;
+  a.kn = (const char*)kn; a.vn = (const char*)vn; a.kc = (char*)kc; a.vc = (char*)vc;
+  a.B = B; a.n = n; a.Hkv = Hkv; a.row_bytes = dh * (bf ? 2 : 4); a.cap = cap; a.window = window;
+  a.is_global = is_global;
+  for (int b = 0; b < B && b < MAX_BATCH; ++b) a.pos0[b] = pos0[b];
+  const int64_t total = (int64_t)B * Hkv * n * (a.row_bytes / 16);
+  hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// resid[t] += sum_{s<k} gate[t][s] * y[inv_perm[t*k+s]] + shared[t], slots in order
+__global__ void moe_combine_kernel(float* resid, const float* y, const float* shared, const float* gates,
+                                   const int32_t* inv_perm, int d, int k) {
+  const int t = blockIdx.y;
+  const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (c >= d) return;
+  f32x4_v acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < k; ++s) {
+    const float gt = gates[(int64_t)t * k + s];
+    const f32x4_v v = *reinterpret_cast<const f32x4_v*>(y + (int64_t)inv_perm[(int64_t)t * k + s] * d + c);
+    acc += gt * v;
+  }
+  f32x4_v* r = reinterpret_cast<f32x4_v*>(resid + (int64_t)t * d + c);
+  const f32x4_v sh = *reinterpret_cast<const f32x4_v*>(shared + (int64_t)t * d + c);
+  *r = *r + (acc + sh);
+}
+
+hipError_t launch_moe_combine(float* resid, const float* y, const float* shared, const float* gates,
+                              const int32_t* inv_perm, int rows, int d, int k, hipStream_t s) {
+  dim3 grid((d / 4 + 255) / 256, rows);
+  hipLaunchKernelGGL(moe_combine_kernel, grid, dim3(256), 0, s, resid, y, shared, gates, inv_perm, d, k);
+  return hipGetLastError();
+}
+
+}  // namespace dg

@@ -1,0 +1,340 @@
+// Fused LM head -> Step.
+//
+// Logits z = H . E^T / tau are produced tile by tile by the MFMA engine and consumed in
+// registers: per row the kernel keeps a running max and its argmax, the rescaled sum of
+// exp(z - max), and the best Gumbel-perturbed key z + G with its token (Gumbel-max sampling of
+// softmax(z)).  Nothing of size rows x vocab is ever written.  Everything is kept in the log2
+// domain (z2 = z * log2 e) so the exponentials are single exp2 instructions.
+//
+// Each block owns one vocabulary slice for one row tile and writes one partial per row; the
+// Step kernel merges the partials of every slice in ascending slice order (deterministic), then
+// applies the per-position update: lock-in of confident positions, else the Euler jump with
+// probability lambda to the Gumbel-max draw [TR §Backward Denoising Process; PBD glossary].
+#include "gemm_core.h"
+#include "internal.h"
+
+namespace dg {
+
+constexpr float LN2 = 0.69314718055994531f;
+// G * log2(e) = -log2(-log2(u)) - log2(ln 2)
+constexpr float NEG_LOG2_LN2 = 0.52876637294904302f;
+constexpr int PART = 5;  // m2, s, a, g2, y
+
+struct RowState {
+  float m2, s, g2;
+  int a, y;
+};
+
+DG_DEV void state_init(RowState& st) {
+  st.m2 = -INFINITY; st.s = 0.f; st.g2 = -INFINITY; st.a = 0x7fffffff; st.y = 0x7fffffff;
+}
+
+// merge b into a; ties in the max (or the Gumbel key) go to the lower token id
+DG_DEV void state_merge(RowState& a, float m2, float s, int ai, float g2, int y) {
+  const float mn = fmaxf(a.m2, m2);
+  float sa = a.s, sb = s;
+  if (mn != -INFINITY) {
+    sa = a.m2 == -INFINITY ? 0.f : a.s * exp2f(a.m2 - mn);
+    sb = m2 == -INFINITY ? 0.f : s * exp2f(m2 - mn);
+  }
+  const bool take = (m2 > a.m2) || (m2 == a.m2 && ai < a.a);
+  a.s = sa + sb;
+  if (take) a.a = ai;
+  a.m2 = mn;
+  if ((g2 > a.g2) || (g2 == a.g2 && y < a.y)) { a.g2 = g2; a.y = y; }
+}
+
+DG_DEV float gumbel_key2(float z2, uint32_t w) {
+  const float t1 = -__log2f(unit_oo(w));       // > 0
+  return z2 - __log2f(t1) + NEG_LOG2_LN2;
+}
+
+// ------------------------------------------------------------------ fused LM head partials ------
+template <class TA, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(256) void lmhead_sampler_kernel(SampArgs p, int n_mt) {
+  using G = GemmTile<TA, TA, BM, BN, WM, WN>;
+  extern __shared__ __align__(16) char lds[];
+  // blocks of one vocabulary slice run on the same XCD (block id mod 8) so E tiles are shared
+  const int id = blockIdx.x, xcd = id & 7, local = id >> 3;
+  const int mt = local % n_mt;
+  const int slice = (local / n_mt) * 8 + xcd;
+  if (slice >= p.slices) return;
+  const int m0 = mt * BM;
+  const int v_begin = slice * p.v_per_slice;
+  const int v_end = min(p.V, v_begin + p.v_per_slice);
+  const TA* H = static_cast<const TA*>(p.H);
+  const TA* E = static_cast<const TA*>(p.E);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+  RowState st[G::FM][4];
+#pragma unroll
+  for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) state_init(st[i][e]);
+
+  for (int v0 = v_begin; v0 < v_end; v0 += BN) {
+    auto arow = [&](int r) -> const TA* {
+      const int m = m0 + r;
+      return m < p.rows ? H + (int64_t)m * p.d : nullptr;
+    };
+    auto brow = [&](int r) -> const TA* {
+      const int v = v0 + r;
+      return v < v_end ? E + (int64_t)v * p.d : nullptr;
+    };
+    G g;
+    g.setup(arow, brow);
+    f32x4_v acc[G::FM][G::FN];
+    g.run(lds, p.d, acc);
+
+#pragma unroll
+    for (int i = 0; i < G::FM; ++i) {
+      const int rb = m0 + G::row_of(i, 0);       // first of this lane's 4 consecutive rows
+      const int b = rb / p.L, ii = rb - b * p.L;
+      float z[G::FN][4];
+      int vv[G::FN];
+      uint32_t wd[G::FN][4];
+#pragma unroll
+      for (int j = 0; j < G::FN; ++j) {
+        vv[j] = v0 + G::col_of(j);
+        const u32x4 w = philox((uint32_t)vv[j], (uint32_t)(ii >> 2), p.step,
+                               ((uint32_t)b << 8) | TAG_GUMBEL, p.k0, p.k1);
+        wd[j][0] = w.x; wd[j][1] = w.y; wd[j][2] = w.z; wd[j][3] = w.w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[j][e] = vv[j] < v_end ? acc[i][j][e] * p.zscale_log2 : -INFINITY;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        RowState& s = st[i][e];
+        float zmax = z[0][e];
+        int vmax = vv[0];
+#pragma unroll
+        for (int j = 1; j < G::FN; ++j)
+          if (z[j][e] > zmax) { zmax = z[j][e]; vmax = vv[j]; }
+        if (zmax > s.m2) {
+          s.s = s.m2 == -INFINITY ? 0.f : s.s * exp2f(s.m2 - zmax);
+          s.m2 = zmax;
+          s.a = vmax;
+        }
+#pragma unroll
+        for (int j = 0; j < G::FN; ++j) {
+          if (z[j][e] != -INFINITY) s.s += exp2f(z[j][e] - s.m2);
+          const float key = vv[j] < v_end ? gumbel_key2(z[j][e], wd[j][e]) : -INFINITY;
+          if (key > s.g2) { s.g2 = key; s.y = vv[j]; }
+        }
+      }
+    }
+  }
+
+  // reduce over the 16 lanes holding the same rows (lane bits 0..3 select the column)
+#pragma unroll
+  for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      RowState& s = st[i][e];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const float m2 = __shfl_xor(s.m2, o, 64), ss = __shfl_xor(s.s, o, 64);
+        const float g2 = __shfl_xor(s.g2, o, 64);
+        const int a = __shfl_xor(s.a, o, 64), y = __shfl_xor(s.y, o, 64);
+        state_merge(s, m2, ss, a, g2, y);
+      }
+    }
+  // then over the WN waves sharing a row range, through LDS (wave wn = 0 merges and writes)
+  __syncthreads();
+  float* xch = reinterpret_cast<float*>(lds);       // [WN][BM][PART]
+  const int wm = wave / WN, wn = wave % WN;
+  if ((lane & 15) == 0) {
+#pragma unroll
+    for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = G::row_of(i, e);
+        float* q = xch + ((size_t)wn * BM + r) * PART;
+        q[0] = st[i][e].m2; q[1] = st[i][e].s; q[2] = __int_as_float(st[i][e].a);
+        q[3] = st[i][e].g2; q[4] = __int_as_float(st[i][e].y);
+      }
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < BM; r += 256) {
+    const int m = m0 + r;
+    if (m >= p.rows) continue;
+    RowState s;
+    state_init(s);
+    for (int w = 0; w < WN; ++w) {
+      const float* q = xch + ((size_t)w * BM + r) * PART;
+      state_merge(s, q[0], q[1], __float_as_int(q[2]), q[3], __float_as_int(q[4]));
+    }
+    float* o = p.part + ((size_t)slice * p.rows + m) * PART;
+    o[0] = s.m2; o[1] = s.s; o[2] = __int_as_float(s.a); o[3] = s.g2; o[4] = __int_as_float(s.y);
+  }
+  (void)wm;
+}
+
+constexpr int SBM = 128, SBN = 128;
+
+hipError_t launch_lmhead_sampler(const SampArgs& a, int act_bf16, hipStream_t s) {
+  const int n_mt = (a.rows + SBM - 1) / SBM;
+  const int slices8 = (a.slices + 7) / 8 * 8;
+  const int blocks = n_mt * slices8;
+  if (act_bf16) {
+    using G = GemmTile<bf16_t, bf16_t, SBM, SBN, 2, 2>;
+    size_t lds = G::LDS_BYTES > 2 * SBM * PART * 4 ? G::LDS_BYTES : 2 * SBM * PART * 4;
+    static const hipError_t attr = allow_lds(lmhead_sampler_kernel<bf16_t, SBM, SBN, 2, 2>, lds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((lmhead_sampler_kernel<bf16_t, SBM, SBN, 2, 2>), dim3(blocks), dim3(256), lds, s, a, n_mt);
+  } else {
+    using G = GemmTile<float, float, SBM, SBN, 2, 2>;
+    size_t lds = G::LDS_BYTES > 2 * SBM * PART * 4 ? G::LDS_BYTES : 2 * SBM * PART * 4;
+    static const hipError_t attr = allow_lds(lmhead_sampler_kernel<float, SBM, SBN, 2, 2>, lds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((lmhead_sampler_kernel<float, SBM, SBN, 2, 2>), dim3(blocks), dim3(256), lds, s, a, n_mt);
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ partials from given logits --
+// Test hook: the same partials from an fp32 logit array (one block per (row, slice)).
+__global__ __launch_bounds__(256) void logits_partials_kernel(const float* z, int rows, int V, int L,
+                                                              float zs, uint32_t k0, uint32_t k1,
+                                                              uint32_t step, int v_per_slice, float* part) {
+  const int row = blockIdx.x, slice = blockIdx.y;
+  const int b = row / L, ii = row - b * L;
+  const int v_begin = slice * v_per_slice, v_end = min(V, v_begin + v_per_slice);
+  RowState st;
+  state_init(st);
+  for (int v = v_begin + threadIdx.x; v < v_end; v += 256) {
+    const float z2 = z[(int64_t)row * V + v] * zs;
+    const u32x4 w = philox((uint32_t)v, (uint32_t)(ii >> 2), step, ((uint32_t)b << 8) | TAG_GUMBEL, k0, k1);
+    state_merge(st, z2, 1.f, v, gumbel_key2(z2, pick(w, ii & 3)), v);
+  }
+  for (int o = 1; o < 64; o <<= 1) {
+    const float m2 = __shfl_xor(st.m2, o, 64), ss = __shfl_xor(st.s, o, 64), g2 = __shfl_xor(st.g2, o, 64);
+    const int a = __shfl_xor(st.a, o, 64), y = __shfl_xor(st.y, o, 64);
+    state_merge(st, m2, ss, a, g2, y);
+  }
+  __shared__ float xch[4][PART];
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    xch[wave][0] = st.m2; xch[wave][1] = st.s; xch[wave][2] = __int_as_float(st.a);
+    xch[wave][3] = st.g2; xch[wave][4] = __int_as_float(st.y);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    RowState s;
+    state_init(s);
+    for (int w = 0; w < 4; ++w)
+      state_merge(s, xch[w][0], xch[w][1], __float_as_int(xch[w][2]), xch[w][3], __float_as_int(xch[w][4]));
+    float* o = part + ((size_t)slice * rows + row) * PART;
+    o[0] = s.m2; o[1] = s.s; o[2] = __int_as_float(s.a); o[3] = s.g2; o[4] = __int_as_float(s.y);
+  }
+}
+
+hipError_t launch_logits_partials(const float* z, int rows, int V, int L, float zs, uint32_t k0,
+                                  uint32_t k1, uint32_t step, int slices, int v_per_slice,
+                                  float* part, hipStream_t s) {
+  hipLaunchKernelGGL(logits_partials_kernel, dim3(rows, slices), dim3(256), 0, s, z, rows, V, L, zs,
+                     k0, k1, step, v_per_slice, part);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ merge + Step -----------------
+// One block per canvas, one thread per position.
+__global__ __launch_bounds__(1024) void step_merge_kernel(StepArgs p) {
+  const int b = blockIdx.x, i = threadIdx.x;
+  const int rows = p.B * p.L;
+  const bool is_done = p.done && p.done[b] != 0;
+  int locked = 0, bad = 0;
+  if (i < p.L) {
+    const int r = b * p.L + i;
+    RowState s;
+    state_init(s);
+    for (int sl = 0; sl < p.slices; ++sl) {
+      const float* q = p.part + ((size_t)sl * rows + r) * PART;
+      state_merge(s, q[0], q[1], __float_as_int(q[2]), q[3], __float_as_int(q[4]));
+    }
+    const float c = 1.f / s.s;
+    bad = !(isfinite(s.m2) && isfinite(s.s) && isfinite(s.g2));
+    if (p.stats) {
+      float* o = p.stats + (size_t)r * 5;
+      o[0] = s.m2 * LN2; o[1] = __int_as_float(s.a); o[2] = c; o[3] = __int_as_float(s.y);
+      o[4] = s.g2 * LN2;
+    }
+    locked = p.lock[r];
+    if (!is_done && !locked && !bad) {
+      if (c >= p.theta) {
+        p.canvas[r] = s.a;
+        p.lock[r] = 1;
+        locked = 1;
+      } else {
+        const u32x4 w = philox((uint32_t)(i >> 2), 0u, p.step, ((uint32_t)b << 8) | TAG_JUMP, p.k0, p.k1);
+        if (unit_co(pick(w, i & 3)) < p.lam) p.canvas[r] = s.y;
+      }
+    }
+  }
+  __shared__ int red[2][16];
+  int nl = locked, nb = bad;
+  for (int o = 32; o > 0; o >>= 1) { nl += __shfl_xor(nl, o, 64); nb += __shfl_xor(nb, o, 64); }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { red[0][wave] = nl; red[1][wave] = nb; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int tl = 0, tb = 0;
+    for (int w = 0; w < (int)(blockDim.x + 63) / 64; ++w) { tl += red[0][w]; tb += red[1][w]; }
+    if (tb && p.status) atomicOr(p.status, 1);
+    if (p.n_locked) p.n_locked[b] = tb ? -1 : tl;
+    if (!is_done && p.steps_taken) p.steps_taken[b] += 1;
+    if (p.done_out) p.done_out[b] = (tl == p.L) ? 1 : (p.done ? p.done[b] : 0);
+  }
+}
+
+hipError_t launch_step_merge(const StepArgs& a, hipStream_t s) {
+  const int threads = (a.L + 63) / 64 * 64;
+  hipLaunchKernelGGL(step_merge_kernel, dim3(a.B), dim3(threads), 0, s, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ canvas init / noise ----------
+static int log2_exact(int v) {
+  if (v <= 0 || (v & (v - 1))) return -1;
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return l;
+}
+
+__global__ void init_canvas_kernel(int32_t* canvas, uint8_t* lock, int B, int L, int V, int vlog2,
+                                   uint32_t k0, uint32_t k1) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= B * L) return;
+  const int b = r / L, i = r - b * L;
+  const u32x4 w = philox((uint32_t)(i >> 2), 0u, 0u, ((uint32_t)b << 8) | TAG_INIT, k0, k1);
+  canvas[r] = token_of(pick(w, i & 3), V, vlog2);
+  if (lock) lock[r] = 0;
+}
+
+hipError_t launch_init_canvas(int32_t* canvas, uint8_t* lock, int B, int L, int V, uint32_t k0,
+                              uint32_t k1, hipStream_t s) {
+  const int n = B * L;
+  hipLaunchKernelGGL(init_canvas_kernel, dim3((n + 255) / 256), dim3(256), 0, s, canvas, lock, B, L, V,
+                     log2_exact(V), k0, k1);
+  return hipGetLastError();
+}
+
+__global__ void noise_kernel(const int32_t* x0, int32_t* xt, int B, int L, int V, int vlog2, float kappa,
+                             uint32_t k0, uint32_t k1, uint32_t step) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= B * L) return;
+  const int b = r / L, i = r - b * L;
+  const u32x4 wk = philox((uint32_t)(i >> 2), 0u, step, ((uint32_t)b << 8) | TAG_NOISE_KEEP, k0, k1);
+  const u32x4 wt = philox((uint32_t)(i >> 2), 0u, step, ((uint32_t)b << 8) | TAG_NOISE_TOKEN, k0, k1);
+  xt[r] = unit_co(pick(wk, i & 3)) < kappa ? x0[r] : token_of(pick(wt, i & 3), V, vlog2);
+}
+
+hipError_t launch_noise(const int32_t* x0, int32_t* xt, int B, int L, int V, float kappa, uint32_t k0,
+                        uint32_t k1, uint32_t step, hipStream_t s) {
+  const int n = B * L;
+  hipLaunchKernelGGL(noise_kernel, dim3((n + 255) / 256), dim3(256), 0, s, x0, xt, B, L, V, log2_exact(V),
+                     kappa, k0, k1, step);
+  return hipGetLastError();
+}
+
+}  // namespace dg

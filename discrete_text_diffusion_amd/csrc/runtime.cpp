@@ -1,0 +1,728 @@
+// Host side of libdg: argument validation, workspace carving and the launch sequence of each
+// C-ABI call.  Nothing here allocates device memory or synchronises the host (except
+// dg_query_status); every launch goes onto the caller's stream.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/dg.h"
+#include "internal.h"
+
+using namespace dg;
+
+// Event pairs recorded around the launches of the profiled kernel classes.
+struct Prof {
+  uint32_t mask = 0;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> recs[DG_PROF_N];
+  std::vector<hipEvent_t> pool;
+  ~Prof() {
+    for (auto& v : recs)
+      for (auto& p : v) { (void)hipEventDestroy(p.first); (void)hipEventDestroy(p.second); }
+    for (auto e : pool) (void)hipEventDestroy(e);
+  }
+  hipEvent_t get() {
+    if (!pool.empty()) { hipEvent_t e = pool.back(); pool.pop_back(); return e; }
+    hipEvent_t e = nullptr;
+    (void)hipEventCreate(&e);
+    return e;
+  }
+};
+
+struct dg_ctx {
+  dg_model_desc d;
+  std::vector<dg_layer_weights> layers;
+  const void* embed;
+  const void* final_norm;
+  Prof* prof;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+dg_status fail(dg_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+#define HIPCHK(expr)                                                                            \
+  do {                                                                                          \
+    hipError_t e_ = (expr);                                                                     \
+    if (e_ != hipSuccess) return fail(DG_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr size_t ALIGN = 256;
+constexpr int MAX_SPLITS = 16;
+constexpr int SAMP_BM = 128, SAMP_BN = 128;
+
+inline size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+inline int act_bytes(const dg_model_desc& d) { return d.act_dtype == DG_BF16 ? 2 : 4; }
+inline int w_kind(const dg_model_desc& d) {
+  return d.expert_dtype == DG_FP8E4M3 ? W_FP8 : d.expert_dtype == DG_BF16 ? W_BF16 : W_F32;
+}
+inline bool is_global(const dg_model_desc& d, int l) {
+  return d.window <= 0 || d.global_every <= 0 || (l + 1) % d.global_every == 0;
+}
+
+int sampler_slices(const dg_model_desc& d, int rows, int* v_per_slice) {
+  const int n_mt = (rows + SAMP_BM - 1) / SAMP_BM;
+  const int tiles = (d.vocab + SAMP_BN - 1) / SAMP_BN;
+  int want = (1024 + n_mt - 1) / n_mt;
+  if (want > tiles) want = tiles;
+  if (want < 1) want = 1;
+  const int tiles_per = (tiles + want - 1) / want;
+  *v_per_slice = tiles_per * SAMP_BN;
+  return (d.vocab + *v_per_slice - 1) / *v_per_slice;
+}
+
+// Workspace layout.  The inspectable regions (status, stats, routing) come first and depend only
+// on the row count, so the test hooks can find them from `rows` alone.
+struct Layout {
+  size_t status, stats, rlogits, idx, gates;
+  size_t resid, xhat, q, kn, vn, attn_o, part_o, part_ml;
+  size_t counts, offsets, perm, inv_perm, tok, work, n_items;
+  size_t a_grp, y, sh_a, sh_out, samp_part, hidden, done, n_locked;
+  size_t total;
+  int max_items;
+};
+
+Layout layout(const dg_model_desc& d, int B, int n, int max_prefix) {
+  Layout w{};
+  const size_t R = (size_t)B * n, ab = act_bytes(d);
+  const size_t Rk = R * d.top_k;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
+  w.status = take(256);
+  w.stats = take(R * 5 * 4);
+  w.rlogits = take(R * d.n_experts * 4);
+  w.idx = take(Rk * 4);
+  w.gates = take(Rk * 4);
+  w.resid = take(R * d.d_model * 4);
+  w.xhat = take(R * d.d_model * ab);
+  w.q = take(R * d.n_q_heads * d.head_dim * ab);
+  w.kn = take(R * d.n_kv_heads * d.head_dim * ab);
+  w.vn = take(R * d.n_kv_heads * d.head_dim * ab);
+  w.attn_o = take(R * d.n_q_heads * d.head_dim * ab);
+  (void)max_prefix;
+  w.part_o = take((size_t)MAX_SPLITS * R * d.n_q_heads * d.head_dim * 4);
+  w.part_ml = take((size_t)MAX_SPLITS * R * d.n_q_heads * 2 * 4);
+  w.counts = take(d.n_experts * 4);
+  w.offsets = take(d.n_experts * 4);
+  w.perm = take(Rk * 4);
+  w.inv_perm = take(Rk * 4);
+  w.tok = take(Rk * 4);
+  w.max_items = (int)((Rk + GROUP_BM - 1) / GROUP_BM) + d.n_experts;
+  w.work = take((size_t)w.max_items * 2 * 4);
+  w.n_items = take(4);
+  w.a_grp = take(Rk * d.expert_hidden * ab);
+  w.y = take(Rk * d.d_model * 4);
+  w.sh_a = take(R * d.shared_hidden * ab);
+  w.sh_out = take(R * d.d_model * 4);
+  int vps;
+  const int slices = sampler_slices(d, (int)R, &vps);
+  w.samp_part = take((size_t)((slices + 7) / 8 * 8) * R * 5 * 4);
+  w.hidden = take(R * d.d_model * ab);
+  w.done = take(B * 4);
+  w.n_locked = take(B * 4);
+  w.total = o;
+  return w;
+}
+
+template <class T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+dg_status check_ws(const dg_ctx* c, void* ws, size_t ws_bytes, int B, int n, int max_prefix) {
+  if (!ws) return fail(DG_EINVAL, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % ALIGN) return fail(DG_EWORKSPACE, "workspace not 256-byte aligned");
+  const size_t need = layout(c->d, B, n, max_prefix).total;
+  if (ws_bytes < need) return fail(DG_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  return DG_OK;
+}
+
+dg_status check_kv(const dg_ctx* c, const dg_kv* kv, int extra_tokens, int* max_prefix) {
+  const dg_model_desc& d = c->d;
+  if (!kv || !kv->k || !kv->v || !kv->cap || !kv->prefix_len) return fail(DG_EINVAL, "kv: NULL field");
+  if (kv->batch < 1 || kv->batch > MAX_BATCH) return fail(DG_EUNSUPPORTED, "batch %d not in [1, %d]", kv->batch, MAX_BATCH);
+  int mp = 0;
+  for (int b = 0; b < kv->batch; ++b) {
+    if (kv->prefix_len[b] < 0) return fail(DG_EINVAL, "prefix_len[%d] < 0", b);
+    mp = kv->prefix_len[b] > mp ? kv->prefix_len[b] : mp;
+  }
+  for (int l = 0; l < d.n_layers; ++l) {
+    if (!kv->k[l] || !kv->v[l]) return fail(DG_EINVAL, "kv layer %d: NULL cache", l);
+    if (is_global(d, l)) {
+      if (kv->cap[l] < mp + extra_tokens)
+        return fail(DG_EINVAL, "kv layer %d: cap %d < prefix %d + %d", l, kv->cap[l], mp, extra_tokens);
+    } else if (kv->cap[l] != d.window) {
+      return fail(DG_EINVAL, "kv layer %d (local): cap %d != window %d", l, kv->cap[l], d.window);
+    }
+  }
+  *max_prefix = mp;
+  return DG_OK;
+}
+
+uint32_t key0(uint64_t s) { return (uint32_t)(s & 0xffffffffu); }
+uint32_t key1(uint64_t s) { return (uint32_t)(s >> 32); }
+
+double kappa_of(dg_schedule sc, double t) {
+  switch (sc) {
+    case DG_KAPPA_LINEAR: return 1.0 - t;
+    case DG_KAPPA_QUADRATIC: return 1.0 - t * t;
+    case DG_KAPPA_COSINE: return std::cos(M_PI * t / 2.0);
+  }
+  return 0.0;
+}
+double kappa_rate(dg_schedule sc, double t) {
+  switch (sc) {
+    case DG_KAPPA_LINEAR: return 1.0;
+    case DG_KAPPA_QUADRATIC: return 2.0 * t;
+    case DG_KAPPA_COSINE: return (M_PI / 2.0) * std::sin(M_PI * t / 2.0);
+  }
+  return 0.0;
+}
+
+// lambda = min(1, h |kappa'(t)| / (1 - kappa(t))): the Euler jump probability of one Step
+float jump_prob(dg_schedule sc, double t, double h) {
+  const double den = 1.0 - kappa_of(sc, t);
+  const double lam = den <= 0.0 ? 1.0 : std::fmin(1.0, h * kappa_rate(sc, t) / den);
+  return (float)lam;
+}
+
+// Records an event pair around the launches issued while it lives, if `cls` is being profiled.
+struct ProfScope {
+  Prof* p;
+  int cls;
+  hipStream_t s;
+  hipEvent_t e0 = nullptr;
+  ProfScope(const dg_ctx* c, int cls_, hipStream_t s_) : p(c->prof), cls(cls_), s(s_) {
+    if (p && (p->mask >> cls & 1u)) {
+      e0 = p->get();
+      (void)hipEventRecord(e0, s);
+    }
+  }
+  void close() {
+    if (e0) {
+      hipEvent_t e1 = p->get();
+      (void)hipEventRecord(e1, s);
+      p->recs[cls].emplace_back(e0, e1);
+      e0 = nullptr;
+    }
+  }
+  ~ProfScope() { close(); }
+};
+
+// ---------------------------------------------------------------- the layer stack -------------
+struct Pass {
+  const dg_ctx* c;
+  const dg_kv* kv;
+  int B, n;            // canvases, rows per canvas
+  int causal;          // prefill
+  void* ws;
+  Layout w;
+  hipStream_t s;
+};
+
+int attn_splits(const dg_model_desc& d, int B, int n, int nkeys) {
+  const int qtiles = (d.n_q_heads / d.n_kv_heads * n + 63) / 64;
+  const int base = B * d.n_kv_heads * qtiles;
+  const int tiles = (nkeys + 63) / 64;
+  int sp = (512 + base - 1) / base;
+  if (sp > tiles / 2) sp = tiles / 2;
+  if (sp > MAX_SPLITS) sp = MAX_SPLITS;
+  if (sp < 1) sp = 1;
+  return sp;
+}
+
+dg_status run_layer(const Pass& P, int l, bool do_ffn) {
+  const dg_model_desc& d = P.c->d;
+  const dg_layer_weights& L = P.c->layers[l];
+  const int bf = d.act_dtype == DG_BF16;
+  const int R = P.B * P.n;
+  void* ws = P.ws;
+  const Layout& w = P.w;
+  int* status = at<int>(ws, w.status);
+  const bool glob = is_global(d, l);
+
+  HIPCHK(launch_rmsnorm(at<float>(ws, w.resid), L.attn_norm, at<void>(ws, w.xhat), R, d.d_model, d.norm_eps, bf,
+                        status, P.s));
+  // QKV + RoPE
+  DenseArgs qa{};
+  qa.epi = EPI_QKV;
+  qa.A = at<void>(ws, w.xhat); qa.lda = d.d_model;
+  qa.B = L.w_qkv; qa.ldb = d.d_model;
+  qa.M = R; qa.N = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim; qa.K = d.d_model;
+  qa.q_out = at<void>(ws, w.q); qa.k_out = at<void>(ws, w.kn); qa.v_out = at<void>(ws, w.vn);
+  qa.Hq = d.n_q_heads; qa.Hkv = d.n_kv_heads; qa.dh = d.head_dim; qa.rows_per_canvas = P.n;
+  qa.log2_theta = std::log2((double)d.rope_theta);
+  for (int b = 0; b < P.B; ++b) qa.pos0[b] = P.kv->prefix_len[b];
+  {
+    ProfScope ps(P.c, DG_PROF_QKV, P.s);
+    HIPCHK(launch_dense(qa, bf, bf ? W_BF16 : W_F32, P.s));
+  }
+  // attention
+  AttnArgs aa{};
+  aa.q = at<void>(ws, w.q); aa.kn = at<void>(ws, w.kn); aa.vn = at<void>(ws, w.vn);
+  aa.kc = P.kv->k[l]; aa.vc = P.kv->v[l];
+  aa.B = P.B; aa.n = P.n; aa.Hq = d.n_q_heads; aa.Hkv = d.n_kv_heads; aa.dh = d.head_dim; aa.cap = P.kv->cap[l];
+  aa.causal = P.causal; aa.window = d.window > 0 ? d.window : 1; aa.is_global = glob;
+  aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
+  int maxkeys = 0;
+  for (int b = 0; b < P.B; ++b) {
+    aa.pos0[b] = P.kv->prefix_len[b];
+    const int np = glob ? aa.pos0[b] : std::min(aa.pos0[b], d.window);
+    maxkeys = std::max(maxkeys, np + P.n);
+  }
+  aa.splits = attn_splits(d, P.B, P.n, maxkeys);
+  aa.keys_per_split = ((maxkeys + aa.splits - 1) / aa.splits + 63) / 64 * 64;
+  aa.splits = (maxkeys + aa.keys_per_split - 1) / aa.keys_per_split;
+  aa.part_o = at<float>(ws, w.part_o); aa.part_ml = at<float>(ws, w.part_ml);
+  aa.out = at<void>(ws, w.attn_o);
+  {
+    ProfScope ps(P.c, DG_PROF_ATTENTION, P.s);
+    HIPCHK(launch_attention(aa, bf, P.s));
+    if (aa.splits > 1) HIPCHK(launch_attn_merge(aa, bf, P.s));
+  }
+  if (P.causal) {
+    HIPCHK(launch_kv_append(at<void>(ws, w.kn), at<void>(ws, w.vn), P.kv->k[l], P.kv->v[l], P.B, P.n,
+                            d.n_kv_heads, d.head_dim, P.kv->cap[l], d.window, glob, aa.pos0, bf, P.s));
+  }
+  // O projection + residual
+  DenseArgs oa{};
+  oa.epi = EPI_ADD_F32;
+  oa.A = at<void>(ws, w.attn_o); oa.lda = d.n_q_heads * d.head_dim;
+  oa.B = L.w_o; oa.ldb = d.n_q_heads * d.head_dim;
+  oa.M = R; oa.N = d.d_model; oa.K = d.n_q_heads * d.head_dim;
+  oa.C = at<void>(ws, w.resid); oa.ldc = d.d_model;
+  {
+    ProfScope ps(P.c, DG_PROF_O_PROJ, P.s);
+    HIPCHK(launch_dense(oa, bf, bf ? W_BF16 : W_F32, P.s));
+  }
+  if (!do_ffn) return DG_OK;
+
+  // FFN: norm, router, top-k, grouping
+  HIPCHK(launch_rmsnorm(at<float>(ws, w.resid), L.ffn_norm, at<void>(ws, w.xhat), R, d.d_model, d.norm_eps, bf,
+                        status, P.s));
+  DenseArgs ra{};
+  ra.epi = EPI_STORE_F32;
+  ra.A = at<void>(ws, w.xhat); ra.lda = d.d_model;
+  ra.B = L.w_router; ra.ldb = d.d_model;
+  ra.M = R; ra.N = d.n_experts; ra.K = d.d_model;
+  ra.C = at<void>(ws, w.rlogits); ra.ldc = d.n_experts;
+  ra.bias = L.router_bias;
+  ProfScope route_scope(P.c, DG_PROF_ROUTING, P.s);
+  HIPCHK(launch_dense(ra, bf, bf ? W_BF16 : W_F32, P.s));
+  HIPCHK(launch_router_topk(at<float>(ws, w.rlogits), R, d.n_experts, d.top_k, at<int32_t>(ws, w.idx),
+                            at<float>(ws, w.gates), P.s));
+  HIPCHK(launch_route_tables(at<int32_t>(ws, w.idx), R, d.n_experts, d.top_k, at<int32_t>(ws, w.counts),
+                             at<int32_t>(ws, w.offsets), at<int32_t>(ws, w.perm), at<int32_t>(ws, w.inv_perm),
+                             at<int32_t>(ws, w.tok), at<int32_t>(ws, w.work), at<int32_t>(ws, w.n_items),
+                             GROUP_BM, P.s));
+  route_scope.close();
+  const int wk = w_kind(d);
+  // routed experts: gate/up + SwiGLU, then down
+  GroupedArgs ga{};
+  ga.epi = EPI_SWIGLU;
+  ga.A = at<void>(ws, w.xhat); ga.lda = d.d_model; ga.a_tok = at<int32_t>(ws, w.tok);
+  ga.B = L.w_gate; ga.B2 = L.w_up; ga.ldb = d.d_model; ga.b_estride = (int64_t)d.expert_hidden * d.d_model;
+  ga.sB = (const uint16_t*)L.s_gate; ga.sB2 = (const uint16_t*)L.s_up; ga.s_estride = d.expert_hidden;
+  ga.N = d.expert_hidden; ga.K = d.d_model;
+  ga.work = at<int32_t>(ws, w.work); ga.n_items = at<int32_t>(ws, w.n_items);
+  ga.offsets = at<int32_t>(ws, w.offsets); ga.counts = at<int32_t>(ws, w.counts);
+  ga.C = at<void>(ws, w.a_grp); ga.ldc = d.expert_hidden;
+  {
+    ProfScope ps(P.c, DG_PROF_MOE_GATE_UP, P.s);
+    HIPCHK(launch_grouped(ga, bf, wk, w.max_items, P.s));
+  }
+  GroupedArgs da{};
+  da.epi = EPI_STORE_F32;
+  da.A = at<void>(ws, w.a_grp); da.lda = d.expert_hidden; da.a_tok = nullptr;
+  da.B = L.w_down; da.B2 = nullptr; da.ldb = d.expert_hidden; da.b_estride = (int64_t)d.d_model * d.expert_hidden;
+  da.sB = (const uint16_t*)L.s_down; da.sB2 = nullptr; da.s_estride = d.d_model;
+  da.N = d.d_model; da.K = d.expert_hidden;
+  da.work = ga.work; da.n_items = ga.n_items; da.offsets = ga.offsets; da.counts = ga.counts;
+  da.C = at<void>(ws, w.y); da.ldc = d.d_model;
+  {
+    ProfScope ps(P.c, DG_PROF_MOE_DOWN, P.s);
+    HIPCHK(launch_grouped(da, bf, wk, w.max_items, P.s));
+  }
+  // shared expert
+  DenseArgs sa{};
+  sa.epi = EPI_SWIGLU;
+  sa.A = at<void>(ws, w.xhat); sa.lda = d.d_model;
+  sa.B = L.sh_gate; sa.B2 = L.sh_up; sa.ldb = d.d_model;
+  sa.sB = (const uint16_t*)L.sh_s_gate; sa.sB2 = (const uint16_t*)L.sh_s_up;
+  sa.M = R; sa.N = d.shared_hidden; sa.K = d.d_model;
+  sa.C = at<void>(ws, w.sh_a); sa.ldc = d.shared_hidden;
+  ProfScope shared_scope(P.c, DG_PROF_SHARED, P.s);
+  HIPCHK(launch_dense(sa, bf, wk, P.s));
+  DenseArgs sd{};
+  sd.epi = EPI_STORE_F32;
+  sd.A = at<void>(ws, w.sh_a); sd.lda = d.shared_hidden;
+  sd.B = L.sh_down; sd.ldb = d.shared_hidden;
+  sd.sB = (const uint16_t*)L.sh_s_down;
+  sd.M = R; sd.N = d.d_model; sd.K = d.shared_hidden;
+  sd.C = at<void>(ws, w.sh_out); sd.ldc = d.d_model;
+  HIPCHK(launch_dense(sd, bf, wk, P.s));
+  shared_scope.close();
+  HIPCHK(launch_moe_combine(at<float>(ws, w.resid), at<float>(ws, w.y), at<float>(ws, w.sh_out),
+                            at<float>(ws, w.gates), at<int32_t>(ws, w.inv_perm), R, d.d_model, d.top_k, P.s));
+  return DG_OK;
+}
+
+dg_status check_desc(const dg_model_desc& d) {
+  if (d.n_layers < 1 || d.d_model < 1 || d.n_q_heads < 1 || d.n_kv_heads < 1 || d.n_experts < 1 || d.top_k < 1 ||
+      d.expert_hidden < 1 || d.shared_hidden < 1 || d.vocab < 1)
+    return fail(DG_EINVAL, "model descriptor has a non-positive size");
+  if (d.head_dim != 64 && d.head_dim != 128 && d.head_dim != 256)
+    return fail(DG_EUNSUPPORTED, "head_dim %d not in {64, 128, 256}", d.head_dim);
+  if (d.n_q_heads % d.n_kv_heads) return fail(DG_EUNSUPPORTED, "n_q_heads %% n_kv_heads != 0");
+  if (d.d_model % 64 || d.expert_hidden % 64 || d.shared_hidden % 64)
+    return fail(DG_EUNSUPPORTED, "d_model, expert_hidden and shared_hidden must be multiples of 64");
+  if (d.vocab % 16) return fail(DG_EUNSUPPORTED, "vocab %% 16 != 0");
+  if (d.n_experts > 256 || d.top_k > 16 || d.top_k > d.n_experts)
+    return fail(DG_EUNSUPPORTED, "need top_k <= 16 and top_k <= n_experts <= 256");
+  if (d.act_dtype != DG_F32 && d.act_dtype != DG_BF16) return fail(DG_EUNSUPPORTED, "act_dtype must be F32 or BF16");
+  if (!(d.expert_dtype == d.act_dtype || (d.act_dtype == DG_BF16 && d.expert_dtype == DG_FP8E4M3)))
+    return fail(DG_EUNSUPPORTED, "expert_dtype must equal act_dtype, or be FP8E4M3 with BF16 activations");
+  if (!(d.norm_eps >= 0.f) || !(d.rope_theta > 0.f)) return fail(DG_EINVAL, "bad norm_eps or rope_theta");
+  if (d.window > 0 && d.global_every > 0 && d.window < 1) return fail(DG_EINVAL, "bad window");
+  return DG_OK;
+}
+
+dg_status check_rows(int B, int L) {
+  if (B < 1 || B > MAX_BATCH) return fail(DG_EUNSUPPORTED, "batch %d not in [1, %d]", B, MAX_BATCH);
+  if (L < 16 || L > 1024 || L % 16) return fail(DG_EUNSUPPORTED, "canvas length %d: need 16 <= L <= 1024, L %% 16 == 0", L);
+  return DG_OK;
+}
+
+dg_status sample_into(dg_ctx* c, const void* hidden, int32_t* canvas, uint8_t* lock, int32_t* n_locked,
+                      const int32_t* done, int B, int L, const dg_step_params* p, float lam, void* ws,
+                      const Layout& w, int32_t* steps_taken, int32_t* done_out, hipStream_t s) {
+  const dg_model_desc& d = c->d;
+  const int R = B * L;
+  SampArgs sa{};
+  sa.H = hidden; sa.E = c->embed;
+  sa.rows = R; sa.d = d.d_model; sa.V = d.vocab; sa.L = L;
+  sa.zscale_log2 = (float)(1.4426950408889634 / (double)p->tau);
+  sa.k0 = key0(p->seed); sa.k1 = key1(p->seed); sa.step = p->step;
+  sa.slices = sampler_slices(d, R, &sa.v_per_slice);
+  sa.part = at<float>(ws, w.samp_part);
+  {
+    ProfScope ps(c, DG_PROF_SAMPLER, s);
+    HIPCHK(launch_lmhead_sampler(sa, d.act_dtype == DG_BF16, s));
+  }
+  StepArgs st{};
+  st.part = sa.part; st.slices = sa.slices;
+  st.B = B; st.L = L; st.canvas = canvas; st.lock = lock; st.n_locked = n_locked; st.done = done;
+  st.lam = lam; st.theta = p->lock_threshold;
+  st.k0 = sa.k0; st.k1 = sa.k1; st.step = p->step;
+  st.stats = at<float>(ws, w.stats); st.status = at<int>(ws, w.status);
+  st.steps_taken = steps_taken; st.done_out = done_out;
+  HIPCHK(launch_step_merge(st, s));
+  return DG_OK;
+}
+
+dg_status check_step_params(const dg_step_params* p) {
+  if (!p) return fail(DG_EINVAL, "params is NULL");
+  if (!(p->tau > 0.f) || !std::isfinite(p->tau)) return fail(DG_EINVAL, "tau must be > 0");
+  if (!(p->h > 0.f) || !(p->t > 0.f) || p->t > 1.f) return fail(DG_EINVAL, "need 0 < t <= 1 and h > 0");
+  if (p->schedule < DG_KAPPA_LINEAR || p->schedule > DG_KAPPA_COSINE) return fail(DG_EINVAL, "bad schedule");
+  if (!(p->lock_threshold > 0.f)) return fail(DG_EINVAL, "lock_threshold must be > 0");
+  return DG_OK;
+}
+
+}  // namespace
+
+// ================================================================ C ABI ==========================
+extern "C" {
+
+const char* dg_last_error(void) { return g_err.c_str(); }
+
+float dg_jump_prob(dg_schedule schedule, float t, float h) { return jump_prob(schedule, t, h); }
+
+dg_status dg_create(const dg_model_desc* desc, const dg_weights* wts, dg_ctx** out) {
+  g_err.clear();
+  if (!desc || !wts || !out) return fail(DG_EINVAL, "NULL argument");
+  dg_status st = check_desc(*desc);
+  if (st != DG_OK) return st;
+  if (!wts->layers || !wts->final_norm) return fail(DG_EINVAL, "weights: NULL layer table or final_norm");
+  const bool fp8 = desc->expert_dtype == DG_FP8E4M3;
+  for (int l = 0; l < desc->n_layers; ++l) {
+    const dg_layer_weights& L = wts->layers[l];
+    if (!L.attn_norm || !L.w_qkv || !L.w_o || !L.ffn_norm || !L.w_router || !L.w_gate || !L.w_up || !L.w_down ||
+        !L.sh_gate || !L.sh_up || !L.sh_down)
+      return fail(DG_EINVAL, "weights: layer %d has a NULL matrix", l);
+    if (fp8 && (!L.s_gate || !L.s_up || !L.s_down || !L.sh_s_gate || !L.sh_s_up || !L.sh_s_down))
+      return fail(DG_EINVAL, "weights: layer %d: FP8 experts need every scale", l);
+  }
+  dg_ctx* c = new dg_ctx;
+  c->d = *desc;
+  c->layers.assign(wts->layers, wts->layers + desc->n_layers);
+  c->embed = wts->embed;
+  c->final_norm = wts->final_norm;
+  c->prof = new Prof;
+  *out = c;
+  return DG_OK;
+}
+
+void dg_destroy(dg_ctx* ctx) {
+  if (!ctx) return;
+  delete ctx->prof;
+  delete ctx;
+}
+
+dg_status dg_profile_enable(dg_ctx* ctx, uint32_t mask) {
+  if (!ctx) return fail(DG_EINVAL, "NULL context");
+  ctx->prof->mask = mask;
+  return DG_OK;
+}
+
+dg_status dg_profile_read(dg_ctx* ctx, int32_t cls, double* total_ms, int32_t* launches) {
+  if (!ctx || cls < 0 || cls >= DG_PROF_N) return fail(DG_EINVAL, "bad argument");
+  Prof* p = ctx->prof;
+  double tot = 0.0;
+  int n = 0;
+  for (auto& pr : p->recs[cls]) {
+    HIPCHK(hipEventSynchronize(pr.second));
+    float ms = 0.f;
+    HIPCHK(hipEventElapsedTime(&ms, pr.first, pr.second));
+    tot += ms;
+    ++n;
+    p->pool.push_back(pr.first);
+    p->pool.push_back(pr.second);
+  }
+  p->recs[cls].clear();
+  if (total_ms) *total_ms = tot;
+  if (launches) *launches = n;
+  return DG_OK;
+}
+
+dg_status dg_init_canvas(int32_t* canvas, uint8_t* lock, int32_t batch, int32_t L, int32_t vocab, uint64_t seed,
+                         hipStream_t stream) {
+  g_err.clear();
+  if (!canvas || batch < 1 || L < 1 || vocab < 1) return fail(DG_EINVAL, "bad argument");
+  HIPCHK(launch_init_canvas(canvas, lock, batch, L, vocab, key0(seed), key1(seed), stream));
+  return DG_OK;
+}
+
+size_t dg_workspace_bytes(const dg_ctx* ctx, int32_t batch, int32_t rows_per_canvas, int32_t max_prefix) {
+  if (!ctx || batch < 1 || rows_per_canvas < 1) return 0;
+  return layout(ctx->d, batch, rows_per_canvas, max_prefix).total;
+}
+
+dg_status dg_query_status(const dg_ctx* ctx, const void* ws, hipStream_t stream) {
+  if (!ctx || !ws) return fail(DG_EINVAL, "NULL argument");
+  HIPCHK(hipStreamSynchronize(stream));
+  int v = 0;
+  HIPCHK(hipMemcpy(&v, ws, sizeof v, hipMemcpyDeviceToHost));
+  return v ? fail(DG_ENONFINITE, "non-finite value flagged (code %d)", v) : DG_OK;
+}
+
+dg_status dg_clear_status(const dg_ctx* ctx, void* ws, hipStream_t stream) {
+  if (!ctx || !ws) return fail(DG_EINVAL, "NULL argument");
+  HIPCHK(launch_fill_i32(static_cast<int32_t*>(ws), 0, 64, stream));
+  return DG_OK;
+}
+
+dg_status dg_prefill_kv(dg_ctx* ctx, const dg_kv* kv, const int32_t* tokens, int32_t n, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  g_err.clear();
+  if (!ctx || !tokens) return fail(DG_EINVAL, "NULL argument");
+  if (!ctx->embed) return fail(DG_EINVAL, "prefill needs the embedding");
+  if (n < 1) return fail(DG_EINVAL, "n must be >= 1");
+  int mp = 0;
+  dg_status st = check_kv(ctx, kv, n, &mp);
+  if (st != DG_OK) return st;
+  if ((st = check_ws(ctx, ws, ws_bytes, kv->batch, n, mp)) != DG_OK) return st;
+  Pass P{ctx, kv, kv->batch, n, 1, ws, layout(ctx->d, kv->batch, n, mp), stream};
+  const dg_model_desc& d = ctx->d;
+  HIPCHK(launch_embed(tokens, ctx->embed, at<float>(ws, P.w.resid), P.B * n, d.d_model, d.vocab,
+                      d.act_dtype == DG_BF16, stream));
+  for (int l = 0; l < d.n_layers; ++l) {
+    // the last layer's FFN feeds no cache
+    if ((st = run_layer(P, l, l + 1 < d.n_layers)) != DG_OK) return st;
+  }
+  return DG_OK;
+}
+
+dg_status dg_denoise_step(dg_ctx* ctx, const dg_kv* kv, const int32_t* canvas, const float* resid_in, int32_t L,
+                          int32_t layer_begin, int32_t layer_end, void* hidden_out, float* resid_out, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  g_err.clear();
+  if (!ctx) return fail(DG_EINVAL, "NULL context");
+  const dg_model_desc& d = ctx->d;
+  if (!canvas && !resid_in) return fail(DG_EINVAL, "need canvas or resid_in");
+  if (!resid_in && !ctx->embed) return fail(DG_EINVAL, "embedding canvas tokens needs the embedding");
+  if (layer_begin < 0 || layer_end > d.n_layers || layer_begin > layer_end)
+    return fail(DG_EINVAL, "layer range [%d, %d) outside [0, %d]", layer_begin, layer_end, d.n_layers);
+  int mp = 0;
+  dg_status st = check_kv(ctx, kv, 0, &mp);
+  if (st != DG_OK) return st;
+  if ((st = check_rows(kv->batch, L)) != DG_OK) return st;
+  if ((st = check_ws(ctx, ws, ws_bytes, kv->batch, L, mp)) != DG_OK) return st;
+  Pass P{ctx, kv, kv->batch, L, 0, ws, layout(d, kv->batch, L, mp), stream};
+  const int R = P.B * L;
+  const int bf = d.act_dtype == DG_BF16;
+  if (resid_in) HIPCHK(launch_copy_f32(resid_in, at<float>(ws, P.w.resid), (int64_t)R * d.d_model, stream));
+  else HIPCHK(launch_embed(canvas, ctx->embed, at<float>(ws, P.w.resid), R, d.d_model, d.vocab, bf, stream));
+  for (int l = layer_begin; l < layer_end; ++l)
+    if ((st = run_layer(P, l, true)) != DG_OK) return st;
+  if (resid_out) HIPCHK(launch_copy_f32(at<float>(ws, P.w.resid), resid_out, (int64_t)R * d.d_model, stream));
+  if (hidden_out)
+    HIPCHK(launch_rmsnorm(at<float>(ws, P.w.resid), ctx->final_norm, hidden_out, R, d.d_model, d.norm_eps, bf,
+                          at<int>(ws, P.w.status), stream));
+  return DG_OK;
+}
+
+dg_status dg_step_sample(dg_ctx* ctx, const void* hidden, int32_t* canvas, uint8_t* lock, int32_t* n_locked,
+                         const int32_t* done, int32_t batch, int32_t L, const dg_step_params* params, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  g_err.clear();
+  if (!ctx || !hidden || !canvas || !lock) return fail(DG_EINVAL, "NULL argument");
+  if (!ctx->embed) return fail(DG_EINVAL, "the LM head needs the embedding");
+  dg_status st = check_step_params(params);
+  if (st != DG_OK) return st;
+  if ((st = check_rows(batch, L)) != DG_OK) return st;
+  if ((st = check_ws(ctx, ws, ws_bytes, batch, L, 0)) != DG_OK) return st;
+  const Layout w = layout(ctx->d, batch, L, 0);
+  return sample_into(ctx, hidden, canvas, lock, n_locked, done, batch, L, params,
+                     jump_prob(params->schedule, params->t, params->h), ws, w, nullptr, nullptr, stream);
+}
+
+dg_status dg_canvas_run(dg_ctx* ctx, const dg_kv* kv, int32_t* canvas, uint8_t* lock, int32_t* steps_taken, int32_t L,
+                        const dg_run_params* p, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err.clear();
+  if (!ctx || !canvas || !lock || !p) return fail(DG_EINVAL, "NULL argument");
+  if (!ctx->embed) return fail(DG_EINVAL, "the canvas loop needs the embedding");
+  if (p->max_steps < 1) return fail(DG_EINVAL, "max_steps must be >= 1");
+  int mp = 0;
+  dg_status st = check_kv(ctx, kv, 0, &mp);
+  if (st != DG_OK) return st;
+  if ((st = check_rows(kv->batch, L)) != DG_OK) return st;
+  if ((st = check_ws(ctx, ws, ws_bytes, kv->batch, L, mp)) != DG_OK) return st;
+  dg_step_params sp{};
+  sp.schedule = p->schedule; sp.tau = p->tau; sp.lock_threshold = p->lock_threshold; sp.seed = p->seed;
+  sp.t = 1.f; sp.h = 1.f / p->max_steps;
+  if ((st = check_step_params(&sp)) != DG_OK) return st;
+  const Layout w = layout(ctx->d, kv->batch, L, mp);
+  const int B = kv->batch;
+  int32_t* done = at<int32_t>(ws, w.done);
+  HIPCHK(launch_fill_i32(done, 0, B, stream));
+  if (steps_taken) HIPCHK(launch_fill_i32(steps_taken, 0, B, stream));
+  if (p->init_canvas) HIPCHK(launch_init_canvas(canvas, lock, B, L, ctx->d.vocab, key0(p->seed), key1(p->seed), stream));
+  const double h = 1.0 / p->max_steps;
+  for (int s = 0; s < p->max_steps; ++s) {
+    if ((st = dg_denoise_step(ctx, kv, canvas, nullptr, L, 0, ctx->d.n_layers, at<void>(ws, w.hidden), nullptr, ws,
+                              ws_bytes, stream)) != DG_OK)
+      return st;
+    const double t = 1.0 - s * h;
+    sp.t = (float)t;
+    sp.h = (float)h;
+    sp.step = (uint32_t)s;
+    // the jump probability is taken at the double-precision grid point t_s = 1 - s/T
+    if ((st = sample_into(ctx, at<void>(ws, w.hidden), canvas, lock, at<int32_t>(ws, w.n_locked),
+                          p->adaptive ? done : nullptr, B, L, &sp, jump_prob(p->schedule, t, h), ws, w, steps_taken,
+                          p->adaptive ? done : nullptr, stream)) != DG_OK)
+      return st;
+  }
+  return DG_OK;
+}
+
+// ---- test hooks ------------------------------------------------------------------------------
+dg_status dg_test_step_from_logits(dg_ctx* ctx, const float* logits, int32_t* canvas, uint8_t* lock,
+                                   int32_t* n_locked, int32_t batch, int32_t L, const dg_step_params* p, void* ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+  g_err.clear();
+  if (!ctx || !logits || !canvas || !lock) return fail(DG_EINVAL, "NULL argument");
+  dg_status st = check_step_params(p);
+  if (st != DG_OK) return st;
+  if ((st = check_rows(batch, L)) != DG_OK) return st;
+  if ((st = check_ws(ctx, ws, ws_bytes, batch, L, 0)) != DG_OK) return st;
+  const Layout w = layout(ctx->d, batch, L, 0);
+  const int R = batch * L, V = ctx->d.vocab;
+  int vps;
+  int slices = sampler_slices(ctx->d, R, &vps);
+  const uint32_t k0 = key0(p->seed), k1 = key1(p->seed);
+  const float zs = (float)(1.4426950408889634 / (double)p->tau);
+  HIPCHK(launch_logits_partials(logits, R, V, L, zs, k0, k1, p->step, slices, vps, at<float>(ws, w.samp_part),
+                                stream));
+  StepArgs sa{};
+  sa.part = at<float>(ws, w.samp_part); sa.slices = slices;
+  sa.B = batch; sa.L = L; sa.canvas = canvas; sa.lock = lock; sa.n_locked = n_locked; sa.done = nullptr;
+  sa.lam = jump_prob(p->schedule, p->t, p->h); sa.theta = p->lock_threshold;
+  sa.k0 = k0; sa.k1 = k1; sa.step = p->step;
+  sa.stats = at<float>(ws, w.stats); sa.status = at<int>(ws, w.status);
+  HIPCHK(launch_step_merge(sa, stream));
+  return DG_OK;
+}
+
+dg_status dg_test_read_stats(const dg_ctx* ctx, const void* ws, int32_t rows, float* m, int32_t* a, float* c,
+                             int32_t* y, float* best, hipStream_t stream) {
+  if (!ctx || !ws || rows < 1) return fail(DG_EINVAL, "bad argument");
+  const Layout w = layout(ctx->d, 1, rows, 0);
+  const char* base = static_cast<const char*>(ws) + w.stats;
+  void* outs[5] = {m, a, c, y, best};
+  for (int j = 0; j < 5; ++j)
+    if (outs[j])
+      HIPCHK(hipMemcpy2DAsync(outs[j], 4, base + 4 * j, 20, 4, rows, hipMemcpyDeviceToDevice, stream));
+  return DG_OK;
+}
+
+dg_status dg_test_router_topk(const float* scores, int32_t T, int32_t E, int32_t k, int32_t* idx, float* gates,
+                              int32_t* counts, int32_t* offsets, int32_t* perm, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  g_err.clear();
+  if (!scores || T < 1 || E < 1 || E > 256 || k < 1 || k > 16 || k > E) return fail(DG_EINVAL, "bad argument");
+  // scratch: idx, gates, counts, offsets, perm, inv_perm, tok, work, n_items
+  const size_t A = (size_t)T * k;
+  const int max_items = (int)((A + GROUP_BM - 1) / GROUP_BM) + E;
+  const size_t need = 6 * up(A * 4) + 2 * up(E * 4) + up((size_t)max_items * 8) + up(4);
+  if (!ws || ws_bytes < need) return fail(DG_EWORKSPACE, "workspace %zu < %zu", ws_bytes, need);
+  char* p = static_cast<char*>(ws);
+  auto take = [&](size_t b) { char* r = p; p += up(b); return r; };
+  int32_t* i_idx = idx ? idx : (int32_t*)take(A * 4);
+  float* i_g = gates ? gates : (float*)take(A * 4);
+  int32_t* i_c = counts ? counts : (int32_t*)take(E * 4);
+  int32_t* i_o = offsets ? offsets : (int32_t*)take(E * 4);
+  int32_t* i_p = perm ? perm : (int32_t*)take(A * 4);
+  int32_t* inv = (int32_t*)take(A * 4);
+  int32_t* tok = (int32_t*)take(A * 4);
+  int32_t* work = (int32_t*)take((size_t)max_items * 8);
+  int32_t* nit = (int32_t*)take(4);
+  HIPCHK(launch_router_topk(scores, T, E, k, i_idx, i_g, stream));
+  HIPCHK(launch_route_tables(i_idx, T, E, k, i_c, i_o, i_p, inv, tok, work, nit, GROUP_BM, stream));
+  return DG_OK;
+}
+
+dg_status dg_test_read_routing(const dg_ctx* ctx, const void* ws, int32_t rows, float* logits, int32_t* idx,
+                               float* gates, hipStream_t stream) {
+  if (!ctx || !ws || rows < 1) return fail(DG_EINVAL, "bad argument");
+  const Layout w = layout(ctx->d, 1, rows, 0);
+  const char* base = static_cast<const char*>(ws);
+  const size_t Rk = (size_t)rows * ctx->d.top_k;
+  if (logits) HIPCHK(hipMemcpyAsync(logits, base + w.rlogits, (size_t)rows * ctx->d.n_experts * 4, hipMemcpyDeviceToDevice, stream));
+  if (idx) HIPCHK(hipMemcpyAsync(idx, base + w.idx, Rk * 4, hipMemcpyDeviceToDevice, stream));
+  if (gates) HIPCHK(hipMemcpyAsync(gates, base + w.gates, Rk * 4, hipMemcpyDeviceToDevice, stream));
+  return DG_OK;
+}
+
+dg_status dg_test_noise(const int32_t* x0, int32_t* xt, int32_t batch, int32_t L, int32_t vocab, dg_schedule schedule,
+                        float t, uint64_t seed, uint32_t step, hipStream_t stream) {
+  g_err.clear();
+  if (!x0 || !xt || batch < 1 || L < 1 || vocab < 1 || !(t >= 0.f && t <= 1.f)) return fail(DG_EINVAL, "bad argument");
+  const float kappa = (float)kappa_of(schedule, t);
+  HIPCHK(launch_noise(x0, xt, batch, L, vocab, kappa, key0(seed), key1(seed), step, stream));
+  return DG_OK;
+}
+
+
+}  // extern "C"

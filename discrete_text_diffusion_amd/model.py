@@ -1,0 +1,102 @@
+"""Marshalling helpers: build the C structs of dg.h from torch tensors and keep them alive.
+
+`Model` wraps one dg_ctx plus the prefix KV cache description; its methods call the
+same-named C entry points.  Any object with the model-shape attributes (n_layers, d_model, ...,
+act_dtype "f32"/"bf16", expert_dtype "f32"/"bf16"/"fp8") describes the model.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import torch
+
+from . import dg
+
+_DT = {"f32": dg.DG_F32, "bf16": dg.DG_BF16, "fp8": dg.DG_FP8E4M3}
+
+
+def model_desc(cfg) -> dg.ModelDesc:
+    return dg.ModelDesc(n_layers=cfg.n_layers, d_model=cfg.d_model, n_q_heads=cfg.n_q_heads,
+                        n_kv_heads=cfg.n_kv_heads, head_dim=cfg.head_dim, n_experts=cfg.n_experts,
+                        top_k=cfg.top_k, expert_hidden=cfg.expert_hidden, shared_hidden=cfg.shared_hidden,
+                        vocab=cfg.vocab, window=cfg.window, global_every=cfg.global_every,
+                        rope_theta=cfg.rope_theta, norm_eps=cfg.norm_eps, act_dtype=_DT[cfg.act_dtype],
+                        expert_dtype=_DT[cfg.expert_dtype])
+
+
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+class Model:
+    def __init__(self, cfg, weights: dict, kv: list | None = None, prefix_len=None):
+        self.cfg = cfg
+        self._keep = [weights]
+        self.desc = model_desc(cfg)
+        n = cfg.n_layers
+        self._layers = (dg.LayerWeights * n)()
+        for l, L in enumerate(weights["layers"]):
+            for f in dg.LAYER_FIELDS:
+                setattr(self._layers[l], f, _p(L.get(f)))
+        self.weights = dg.Weights(embed=_p(weights.get("embed")), final_norm=_p(weights["final_norm"]),
+                                  layers=C.cast(self._layers, C.POINTER(dg.LayerWeights)))
+        self.ctx = dg.dg_create(self.desc, self.weights)
+        self.kv_struct = None
+        if kv is not None:
+            self.set_kv(kv, prefix_len)
+
+    def set_kv(self, kv: list, prefix_len):
+        """kv: per layer (K, V) tensors [B][Hkv][cap][dh]; prefix_len: ints [B]."""
+        self._kv = kv
+        n = self.cfg.n_layers
+        self._kp = (C.c_void_p * n)(*[k.data_ptr() for k, _ in kv])
+        self._vp = (C.c_void_p * n)(*[v.data_ptr() for _, v in kv])
+        self._cap = (C.c_int32 * n)(*[k.shape[2] for k, _ in kv])
+        self.batch = kv[0][0].shape[0]
+        self._plen = (C.c_int32 * self.batch)(*[int(p) for p in prefix_len])
+        self.kv_struct = dg.KV(k=self._kp, v=self._vp, cap=self._cap, prefix_len=self._plen, batch=self.batch)
+
+    @property
+    def prefix_len(self):
+        return [self._plen[b] for b in range(self.batch)]
+
+    def advance_prefix(self, n):
+        for b in range(self.batch):
+            self._plen[b] += n
+
+    def workspace(self, batch, rows_per_canvas, max_prefix=0, device="cuda"):
+        nbytes = dg.dg_workspace_bytes(self.ctx, batch, rows_per_canvas, max_prefix)
+        ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        off = (-ws.data_ptr()) % 256
+        ws = ws[off:off + nbytes]
+        dg.dg_clear_status(self.ctx, ws)
+        return ws
+
+    # ---- calls -----------------------------------------------------------------------------
+    def prefill_kv(self, tokens, ws, stream=None):
+        dg.dg_prefill_kv(self.ctx, self.kv_struct, tokens, tokens.shape[1], ws, stream)
+        self.advance_prefix(tokens.shape[1])
+
+    def denoise_step(self, canvas, L, ws, hidden_out=None, resid_out=None, resid_in=None, layer_begin=0,
+                     layer_end=None, stream=None):
+        le = self.cfg.n_layers if layer_end is None else layer_end
+        dg.dg_denoise_step(self.ctx, self.kv_struct, canvas, resid_in, L, layer_begin, le, hidden_out, resid_out,
+                           ws, stream)
+
+    def step_sample(self, hidden, canvas, lock, n_locked, params: dg.StepParams, ws, done=None, stream=None):
+        B, L = canvas.shape
+        dg.dg_step_sample(self.ctx, hidden, canvas, lock, n_locked, done, B, L, params, ws, stream)
+
+    def canvas_run(self, canvas, lock, steps_taken, params: dg.RunParams, ws, stream=None):
+        dg.dg_canvas_run(self.ctx, self.kv_struct, canvas, lock, steps_taken, canvas.shape[1], params, ws, stream)
+
+    def close(self):
+        if self.ctx:
+            dg.dg_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,247 @@
+/*
+ * dg.h — C ABI of the MI355X (gfx950) canvas denoise-step library, libdg.so.
+ *
+ * The library runs the data-parallel hot path of DiffusionGemma-style discrete text diffusion:
+ * one denoising step over a block of 256-token canvases.  Sources for what is computed:
+ *   [TR]  "DiffusionGemma Technical Report 정리" (juhoplayground.github.io):
+ *         §Forward Process, §Backward Denoising Process, §아키텍처와 블록 자기회귀 생성 (block-AR
+ *         generation: causal context encoding into a KV cache, bidirectional canvas decoder,
+ *         append-after-encode), §디노이징 반복과 self-conditioning (T steps of size h = 1/T,
+ *         p_hat = softmax(logits / tau)), §CPU-GPU 동기화 제거 (no host synchronisation).
+ *   [PBD] the "parallel block decoding" explainer (molayo1419.me), glossary "Iterative
+ *         denoising": each pass locks in high-confidence tokens and re-evaluates the rest.
+ *   [CA]  "DiffusionGemma 완전분석" (cell-devlog), §스펙 정리: 30 layers, sliding window 1024,
+ *         128 experts with 8 active plus one always-on shared expert, 262K vocabulary,
+ *         256-token canvas.
+ *
+ * Conventions for every call:
+ *   - Pointers named as device pointers must point to device memory allocated by the caller;
+ *     descriptors, parameter structs, pointer tables and `cap`/`prefix_len` are host memory.
+ *   - The library never allocates device memory.  All scratch lives in the caller's workspace
+ *     (`ws`, at least dg_workspace_bytes() bytes, 256-byte aligned).  One workspace must not be
+ *     used by two streams at once.
+ *   - Arguments are validated on the host before anything is enqueued.  On failure the call
+ *     returns a negative dg_status, dg_last_error() describes it, and nothing is enqueued.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream); no call synchronises
+ *     the host except dg_query_status().  Buffers must stay alive until the work completes.
+ *   - Row-major layouts throughout.  "act" = the model's activation dtype (F32 or BF16);
+ *     BF16 tensors are raw 16-bit bf16 words.
+ */
+#ifndef DG_H_
+#define DG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DG_OK = 0,
+  DG_EINVAL = -1,        /* null pointer, bad size, bad parameter value */
+  DG_EUNSUPPORTED = -2,  /* shape outside what the kernels tile (see dg_create) */
+  DG_EWORKSPACE = -3,    /* workspace smaller than dg_workspace_bytes() or misaligned */
+  DG_EHIP = -4,          /* a HIP launch or runtime call failed */
+  DG_ENONFINITE = -5     /* a non-finite hidden state or logit was seen (dg_query_status) */
+} dg_status;
+
+typedef enum { DG_F32 = 0, DG_BF16 = 1, DG_FP8E4M3 = 2 } dg_dtype;
+
+/* Noise schedule kappa_t: decreasing from kappa_0 = 1 to kappa_1 = 0 [TR §Forward Process]. */
+typedef enum {
+  DG_KAPPA_LINEAR = 0,     /* 1 - t          */
+  DG_KAPPA_QUADRATIC = 1,  /* 1 - t^2        */
+  DG_KAPPA_COSINE = 2      /* cos(pi t / 2)  */
+} dg_schedule;
+
+/* Model shape.  Layer l (0-based) is global iff window <= 0, global_every <= 0 or
+ * (l + 1) % global_every == 0; other layers are local (sliding window `window`).
+ * Supported: head_dim in {64, 128, 256}; n_q_heads % n_kv_heads == 0; d_model, expert_hidden
+ * and shared_hidden multiples of 64; vocab % 16 == 0; top_k <= n_experts <= 256, top_k <= 16; act_dtype F32 or BF16;
+ * expert_dtype = act_dtype, or FP8E4M3 when act_dtype is BF16 (weights-only fp8, bf16 math). */
+typedef struct {
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim;
+  int32_t n_experts, top_k, expert_hidden, shared_hidden, vocab;
+  int32_t window, global_every;
+  float rope_theta; /* RoPE base (rotate-half pairs j, j + head_dim/2) */
+  float norm_eps;   /* RMSNorm epsilon */
+  dg_dtype act_dtype, expert_dtype;
+} dg_model_desc;
+
+/* One layer's weights: device pointers, borrowed until dg_destroy().  Every matrix is stored
+ * [out][in] (both GEMM operands K-contiguous).  Expert matrices use expert_dtype; with
+ * FP8E4M3 each has a bf16 scale per output row (s_*), and the weight is code * scale. */
+typedef struct {
+  const void *attn_norm;   /* [d] act, RMSNorm gain before attention                       */
+  const void *w_qkv;       /* [(Hq + 2 Hkv) dh][d] act: q heads, then k heads, then v heads */
+  const void *w_o;         /* [d][Hq dh] act                                                */
+  const void *ffn_norm;    /* [d] act                                                       */
+  const void *w_router;    /* [E][d] act                                                    */
+  const float *router_bias;/* [E] fp32 added to the router logits, or NULL                  */
+  const void *w_gate, *w_up;      /* [E][f][d] expert dtype                                 */
+  const void *w_down;             /* [E][d][f]                                              */
+  const void *s_gate, *s_up;      /* [E][f] bf16 scales (FP8 only, else NULL)               */
+  const void *s_down;             /* [E][d]                                                 */
+  const void *sh_gate, *sh_up;    /* [fs][d] shared expert                                  */
+  const void *sh_down;            /* [d][fs]                                                */
+  const void *sh_s_gate, *sh_s_up, *sh_s_down; /* [fs], [fs], [d] bf16 scales (FP8 only)  */
+} dg_layer_weights;
+
+typedef struct {
+  const void *embed;        /* [V][d] act: tied input embedding and LM head; NULL allowed
+                               only for calls that take resid_in and produce no logits        */
+  const void *final_norm;   /* [d] act                                                        */
+  const dg_layer_weights *layers; /* host array [n_layers]                                    */
+} dg_weights;
+
+/* Prefix KV cache, filled by the causal encoder (dg_prefill_kv) or by the caller.
+ * k[l], v[l]: device [batch][Hkv][cap[l]][dh] act, keys stored after RoPE.  Global layers
+ * keep position p in slot p (cap[l] >= every prefix length).  Local layers keep a ring of
+ * cap[l] == window slots, position p in slot p % window. */
+typedef struct {
+  void *const *k;            /* host array [n_layers] of device pointers */
+  void *const *v;
+  const int32_t *cap;        /* host [n_layers] */
+  const int32_t *prefix_len; /* host [batch]: tokens already encoded for each canvas */
+  int32_t batch;
+} dg_kv;
+
+/* One Step [TR §Backward Denoising Process; PBD "Iterative denoising"].
+ * Unlocked position: c = max_v p(v) >= lock_threshold -> take the argmax and lock; otherwise
+ * with probability lambda = min(1, h |kappa'(t)| / (1 - kappa(t))) jump to a token drawn from
+ * p = softmax(logits / tau) (Gumbel-max with Philox4x32-10 noise), else keep the token. */
+typedef struct {
+  dg_schedule schedule;
+  float t, h, tau, lock_threshold; /* lock_threshold > 1 disables lock-in */
+  uint64_t seed;
+  uint32_t step;                   /* step index s: part of every random-draw counter */
+} dg_step_params;
+
+typedef struct {
+  dg_schedule schedule;
+  int32_t max_steps;            /* T: steps at t_s = 1 - s/T, s = 0..T-1, h = 1/T */
+  float tau, lock_threshold;
+  uint64_t seed;
+  int32_t adaptive;             /* 1: a canvas stops once all its positions are locked */
+  int32_t init_canvas;          /* 1: draw the canvas uniformly at t = 1 and clear the lock */
+} dg_run_params;
+
+typedef struct dg_ctx dg_ctx;   /* opaque, host-side; holds the descriptor and borrowed weights */
+
+/* Validates the descriptor (DG_EUNSUPPORTED outside the supported shapes) and the weight
+ * table (DG_EINVAL on a NULL matrix), then copies both.  *out is owned by the caller. */
+dg_status dg_create(const dg_model_desc *desc, const dg_weights *weights, dg_ctx **out);
+void dg_destroy(dg_ctx *ctx);
+
+/* Workspace needed by any call with up to `batch` canvases of `rows_per_canvas` rows (canvas
+ * length, or tokens per prefill call) and prefixes up to `max_prefix` tokens. */
+size_t dg_workspace_bytes(const dg_ctx *ctx, int32_t batch, int32_t rows_per_canvas,
+                          int32_t max_prefix);
+
+/* Thread-local description of the last failure; valid until the next dg_* call. */
+const char *dg_last_error(void);
+
+/* Waits for `stream`, then reads the workspace status word: DG_ENONFINITE if a non-finite
+ * hidden state or logit was seen since the workspace was last cleared (dg_clear_status). */
+dg_status dg_query_status(const dg_ctx *ctx, const void *ws, hipStream_t stream);
+dg_status dg_clear_status(const dg_ctx *ctx, void *ws, hipStream_t stream);
+
+/* Causal encoder pass ("context encoding" and "append after encode", [TR §아키텍처와 블록
+ * 자기회귀 생성]): tokens [batch][n] (device int32) at positions prefix_len[b] .. + n - 1 attend
+ * causally (window on local layers) to the cache and to each other; their post-RoPE keys and
+ * values are written into every layer's cache.  The caller then adds n to prefix_len[b]. */
+dg_status dg_prefill_kv(dg_ctx *ctx, const dg_kv *kv, const int32_t *tokens, int32_t n,
+                        void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Decoder pass over the canvases: bidirectional attention of every canvas position over the
+ * visible prefix (all of it on global layers, the last `window` positions on local layers)
+ * plus the whole canvas, then the MoE FFN with the shared expert; layers
+ * [layer_begin, layer_end).  Input: canvas tokens (device int32 [batch][L], embedded by row
+ * lookup of `embed`) or, when resid_in is non-NULL, the fp32 residual stream [batch*L][d].
+ * Output: hidden_out [batch*L][d] act = RMSNorm(residual) * final_norm (may be NULL), and
+ * resid_out [batch*L][d] fp32 = the residual after layer_end - 1 (may be NULL).
+ * Canvas position i of canvas b has RoPE position prefix_len[b] + i. */
+dg_status dg_denoise_step(dg_ctx *ctx, const dg_kv *kv, const int32_t *canvas,
+                          const float *resid_in, int32_t L, int32_t layer_begin,
+                          int32_t layer_end, void *hidden_out, float *resid_out,
+                          void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Fused LM head + Step: logits = hidden [batch*L][d] . embed^T are streamed through an online
+ * max / sum-exp / Philox-Gumbel argmax and never stored; then every position of canvas
+ * (device int32 [batch][L], in/out) and lock (device uint8 [batch][L], in/out) is updated as
+ * described at dg_step_params.  n_locked (device int32 [batch], out, may be NULL) receives the
+ * locked count per canvas, or -1 if a non-finite value was seen in that canvas.
+ * `done` (device int32 [batch], may be NULL): canvases with done[b] != 0 are left unchanged. */
+dg_status dg_step_sample(dg_ctx *ctx, const void *hidden, int32_t *canvas, uint8_t *lock,
+                         int32_t *n_locked, const int32_t *done, int32_t batch, int32_t L,
+                         const dg_step_params *params, void *ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/* The denoising loop for one block [TR §디노이징 반복과 self-conditioning]: optional uniform
+ * canvas at t = 1, then up to max_steps of dg_denoise_step + dg_step_sample at t_s = 1 - s/T.
+ * With `adaptive`, a canvas whose positions are all locked is left unchanged by later steps
+ * and steps_taken (device int32 [batch], out) counts the steps each canvas took. */
+dg_status dg_canvas_run(dg_ctx *ctx, const dg_kv *kv, int32_t *canvas, uint8_t *lock,
+                        int32_t *steps_taken, int32_t L, const dg_run_params *params,
+                        void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* lambda of one Step as the library computes it (host function, float32 result). */
+float dg_jump_prob(dg_schedule schedule, float t, float h);
+
+/* The canvas at t = 1 [TR §Forward Process: the uniform prior]: every position an independent
+ * uniform token from the Philox canvas-init stream of `seed`.  canvas device int32 [batch][L];
+ * lock (device uint8 [batch][L], may be NULL) is cleared. */
+dg_status dg_init_canvas(int32_t *canvas, uint8_t *lock, int32_t batch, int32_t L, int32_t vocab,
+                         uint64_t seed, hipStream_t stream);
+
+/* ---- kernel timing (HIP events recorded around the library's own launches) -------------- */
+typedef enum {
+  DG_PROF_MOE_GATE_UP = 0, DG_PROF_MOE_DOWN = 1, DG_PROF_ATTENTION = 2, DG_PROF_SAMPLER = 3,
+  DG_PROF_QKV = 4, DG_PROF_O_PROJ = 5, DG_PROF_SHARED = 6, DG_PROF_ROUTING = 7, DG_PROF_N = 8
+} dg_prof_class;
+
+/* Starts recording a pair of events around every launch of the classes in `mask` (bit i =
+ * class i; 0 stops).  Recording adds an event write before and after each such launch. */
+dg_status dg_profile_enable(dg_ctx *ctx, uint32_t mask);
+/* Waits for the recorded launches of class `cls`, returns their summed duration (ms) and
+ * count, and forgets them. */
+dg_status dg_profile_read(dg_ctx *ctx, int32_t cls, double *total_ms, int32_t *launches);
+
+/* ---- hooks for parity tests (same kernels as the calls above, exposed piecewise) ---------- */
+
+/* Step from given fp32 logits z [batch*L][vocab] (device; divided by tau like the fused path).
+ * Uses the merge/Step kernel of dg_step_sample; the statistics are readable afterwards. */
+dg_status dg_test_step_from_logits(dg_ctx *ctx, const float *logits, int32_t *canvas,
+                                   uint8_t *lock, int32_t *n_locked, int32_t batch, int32_t L,
+                                   const dg_step_params *params, void *ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
+/* Copies the per-row sampler statistics of the last Step out of the workspace (device outputs,
+ * [rows] each, any may be NULL): max logit/tau, its argmax, confidence c, Gumbel argmax y and
+ * its key (logit/tau + Gumbel). */
+dg_status dg_test_read_stats(const dg_ctx *ctx, const void *ws, int32_t rows, float *m,
+                             int32_t *a, float *c, int32_t *y, float *best, hipStream_t stream);
+
+/* Top-k routing of given fp32 scores [T][E] (device): idx/gates [T][k]; counts/offsets [E];
+ * perm [T*k] = assignment id t*k+s at each expert-grouped position.  Any output may be NULL. */
+dg_status dg_test_router_topk(const float *scores, int32_t T, int32_t E, int32_t k,
+                              int32_t *idx, float *gates, int32_t *counts, int32_t *offsets,
+                              int32_t *perm, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Routing of the last layer run by dg_denoise_step, read from the workspace: router logits
+ * [rows][E] fp32 (bias included), idx/gates [rows][k]. */
+dg_status dg_test_read_routing(const dg_ctx *ctx, const void *ws, int32_t rows, float *logits,
+                               int32_t *idx, float *gates, hipStream_t stream);
+
+/* Forward noising x_t ~ p_t(. | x0) [TR §Forward Process] with the library's random streams:
+ * x0, xt device int32 [batch][L]. */
+dg_status dg_test_noise(const int32_t *x0, int32_t *xt, int32_t batch, int32_t L, int32_t vocab,
+                        dg_schedule schedule, float t, uint64_t seed, uint32_t step,
+                        hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DG_H_ */

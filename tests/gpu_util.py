@@ -1,0 +1,73 @@
+"""Shared plumbing for the GPU parity tests: device inputs from `synth`, the library model
+wrapper, and host copies for the oracle."""
+import sys
+
+import numpy as np
+import torch
+
+from discrete_text_diffusion_amd import dg
+from discrete_text_diffusion_amd.model import Model
+from synth import gen
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def build(cfg, kv_mode=None):
+    """Seeded weights and caches for `cfg` on cuda:0 and a library Model around them."""
+    dev = torch.device("cuda:0")
+    W = gen.make_weights(cfg, dev)
+    mode = kv_mode or cfg.kv_source
+    if mode == "random":
+        kv = gen.make_random_kv(cfg, dev)
+        plen = [cfg.prefix] * cfg.batch
+    else:
+        kv = gen.empty_kv(cfg, dev)
+        plen = [0] * cfg.batch
+    return Model(cfg, W, kv, plen), W, kv
+
+
+def step_params(schedule, t, h, tau, theta, seed, step):
+    return dg.StepParams(schedule=schedule, t=t, h=h, tau=tau, lock_threshold=theta, seed=seed, step=step)
+
+
+def read_stats(model, ws, rows):
+    dev = torch.device("cuda:0")
+    m = torch.empty(rows, dtype=torch.float32, device=dev)
+    a = torch.empty(rows, dtype=torch.int32, device=dev)
+    c = torch.empty(rows, dtype=torch.float32, device=dev)
+    y = torch.empty(rows, dtype=torch.int32, device=dev)
+    best = torch.empty(rows, dtype=torch.float32, device=dev)
+    dg.dg_test_read_stats(model.ctx, ws, rows, m, a, c, y, best)
+    torch.cuda.synchronize()
+    return {"m": m.cpu().numpy(), "a": a.cpu().numpy(), "c": c.cpu().numpy(), "y": y.cpu().numpy(),
+            "best": best.cpu().numpy()}
+
+
+def top2_gap(z):
+    p = np.partition(z, -2, axis=-1)
+    return p[..., -1] - p[..., -2]
+
+
+def compare_step(gpu_canvas, gpu_lock, gpu_stats, orc_canvas, orc_lock, orc_stats, z_gap, theta,
+                 y_gap_tol=1e-3, a_gap_tol=1e-5, c_tol=1e-5):
+    """Selection parity: token ids, argmaxes and locks equal except where the oracle's own margin
+    says floating-point order may decide (Gumbel top-2 gap < y_gap_tol, logit top-2 gap <
+    a_gap_tol, |c - theta| < c_tol).  Returns the number of excused rows."""
+    ga, gy, gc = gpu_stats["a"], gpu_stats["y"], gpu_stats["c"]
+    oa, oy, oc = orc_stats["a"], orc_stats["y"], orc_stats["c"]
+    excuse_a = z_gap < a_gap_tol
+    excuse_y = orc_stats["gap"] < y_gap_tol
+    excuse_c = np.abs(oc - theta) < c_tol
+    bad_a = (ga != oa) & ~excuse_a
+    bad_y = (gy != oy) & ~excuse_y
+    assert not bad_a.any(), f"argmax differs at rows {np.nonzero(bad_a)[0][:10]}"
+    assert not bad_y.any(), f"Gumbel argmax differs at rows {np.nonzero(bad_y)[0][:10]}"
+    excused = ((ga != oa) | (gy != oy) | excuse_c).reshape(gpu_canvas.shape)
+    diff_c = (gpu_canvas != orc_canvas) & ~excused
+    diff_l = (gpu_lock.astype(bool) != orc_lock) & ~excused
+    assert not diff_c.any(), f"canvas differs at {np.argwhere(diff_c)[:10]}"
+    assert not diff_l.any(), f"lock differs at {np.argwhere(diff_l)[:10]}"
+    return int(excused.sum())

@@ -1,0 +1,138 @@
+"""Parity of the Step on the GPU against the oracle: random draws (canvas init, forward noise),
+the Step from given logits (selection bit-exact given equal scores), and the fused LM-head
+sampler at the tiny fp32 shape and at the full 262,144-token vocabulary in bf16."""
+import numpy as np
+import pytest
+import torch
+
+from discrete_text_diffusion_amd import dg
+from oracle import philox
+from oracle import step as S
+from synth import configs, gen
+from tests.gpu_util import build, compare_step, log, read_stats, step_params, top2_gap
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+@pytest.mark.parametrize("V", [1024, 262144, 1000])
+def test_init_canvas_bit_exact(V):
+    B, L = 3, 256
+    cv = torch.empty(B, L, dtype=torch.int32, device=DEV)
+    dg.dg_init_canvas(cv, None, B, L, V, 12345678901)
+    torch.cuda.synchronize()
+    assert np.array_equal(cv.cpu().numpy(), S.init_canvas(12345678901, B, L, V))
+
+
+@pytest.mark.parametrize("schedule,t", [(0, 0.3), (1, 0.9), (2, 0.55), (0, 1.0), (2, 0.0)])
+def test_forward_noise_bit_exact(schedule, t):
+    B, L, V = 4, 256, 1024
+    x0 = torch.randint(0, V, (B, L), dtype=torch.int32, device=DEV)
+    xt = torch.empty_like(x0)
+    dg.dg_test_noise(x0, xt, B, L, V, schedule, t, 7, 3)
+    torch.cuda.synchronize()
+    want = S.noise(x0.cpu().numpy(), float(np.float32(t)), schedule, 7, 3, V)
+    assert np.array_equal(xt.cpu().numpy(), want)
+
+
+def _logits_case(B, L, V, seed):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    z = torch.randn(B * L, V, generator=g) * 2.0
+    # plant confident rows (one logit far above the rest) and exact ties in the max
+    conf = torch.arange(0, B * L, 5)
+    z[conf, (conf * 37) % V] = 40.0
+    ties = torch.arange(2, B * L, 11)
+    z[ties, 3] = 30.0
+    z[ties, V - 2] = 30.0
+    return z
+
+
+@pytest.mark.parametrize("B,L,V,tau,t,h,theta", [(2, 64, 1024, 1.0, 1.0, 0.25, 0.9),
+                                                  (1, 64, 262144, 0.7, 0.5, 0.25, 0.95),
+                                                  (3, 32, 1024, 1.0, 0.25, 0.25, 2.0)])
+def test_step_from_logits_selection_parity(B, L, V, tau, t, h, theta):
+    log(f"step_from_logits B={B} L={L} V={V}")
+    z = _logits_case(B, L, V, seed=V + B)
+    model, _, _ = build(configs.C0.replace(vocab=V, batch=B, canvas=L))
+    ws = model.workspace(B, L, 0)
+    canvas0 = torch.from_numpy(S.init_canvas(5, B, L, V).astype(np.int32)).to(DEV)
+    lock0 = torch.zeros(B, L, dtype=torch.uint8, device=DEV)
+    lock0[:, ::7] = 1                          # some positions already locked
+    cv, lk = canvas0.clone(), lock0.clone()
+    nl = torch.empty(B, dtype=torch.int32, device=DEV)
+    p = step_params(0, t, h, tau, theta, 99, 2)
+    dg.dg_test_step_from_logits(model.ctx, z.to(DEV), cv, lk, nl, B, L, p, ws)
+    torch.cuda.synchronize()
+    st = read_stats(model, ws, B * L)
+    z64 = z.numpy().astype(np.float64) / np.float64(np.float32(tau))
+    ocv, olk, onl, ost, lam = S.step_from_logits(z64, canvas0.cpu().numpy(), lock0.cpu().numpy().astype(bool),
+                                                 float(np.float32(t)), float(np.float32(h)), 0, theta, 99, 2)
+    excused = compare_step(cv.cpu().numpy(), lk.cpu().numpy(), st, ocv, olk, ost, top2_gap(z64), theta)
+    log(f"  excused rows: {excused}")
+    assert excused <= max(1, B * L // 1000)
+    assert np.array_equal(nl.cpu().numpy(), olk.sum(axis=1))
+    assert np.allclose(st["c"], ost["c"], rtol=1e-5, atol=1e-7)
+    assert np.allclose(st["m"], ost["m"], atol=1e-5)
+    # exact ties in the max resolve to the lower id
+    ties = np.arange(2, B * L, 11)
+    assert np.all(st["a"][ties] == 3)
+
+
+def test_locked_canvas_is_fixed_point_on_gpu():
+    B, L, V = 2, 64, 1024
+    z = torch.randn(B * L, V, device=DEV) * 3
+    model, _, _ = build(configs.C0.replace(batch=B, canvas=L))
+    ws = model.workspace(B, L, 0)
+    cv0 = torch.randint(0, V, (B, L), dtype=torch.int32, device=DEV)
+    cv, lk = cv0.clone(), torch.ones(B, L, dtype=torch.uint8, device=DEV)
+    nl = torch.empty(B, dtype=torch.int32, device=DEV)
+    for s in range(3):
+        dg.dg_test_step_from_logits(model.ctx, z, cv, lk, nl, B, L, step_params(0, 1 - s / 4, 0.25, 1.0, 0.5, 1, s), ws)
+    torch.cuda.synchronize()
+    assert torch.equal(cv, cv0) and bool(lk.all()) and nl.tolist() == [L, L]
+
+
+@pytest.mark.parametrize("case", ["tiny-fp32", "vocab262k-bf16"])
+def test_fused_sampler_parity(case):
+    if case == "tiny-fp32":
+        cfg = configs.C0
+        rows_checked = None
+    else:
+        cfg = configs.C2.replace(n_layers=1)
+        rows_checked = np.arange(0, 256, 4)            # 64 sampled rows, every 4th position
+    B, L, V = cfg.batch, cfg.canvas, cfg.vocab
+    log(f"fused sampler {case}: rows={B * L} V={V} d={cfg.d_model}")
+    model, W, _ = build(cfg)
+    ws = model.workspace(B, L, cfg.prefix)
+    H = gen.hidden_input(cfg, DEV)
+    cv0 = torch.empty(B, L, dtype=torch.int32, device=DEV)
+    dg.dg_init_canvas(cv0, None, B, L, V, 0)
+    cv, lk = cv0.clone(), torch.zeros(B, L, dtype=torch.uint8, device=DEV)
+    nl = torch.empty(B, dtype=torch.int32, device=DEV)
+    ts, h = S.time_grid(cfg.steps)
+    p = step_params(cfg.schedule, ts[1], h, cfg.tau, cfg.lock_threshold, cfg.seed, 1)
+    model.step_sample(H, cv, lk, nl, p, ws)
+    torch.cuda.synchronize()
+    st = read_stats(model, ws, B * L)
+    H64 = H.float().cpu().numpy().astype(np.float64)
+    E64 = W["embed"].float().cpu().numpy().astype(np.float64)
+    rows = np.arange(B * L) if rows_checked is None else rows_checked
+    z = (H64[rows] @ E64.T) / np.float64(np.float32(cfg.tau))
+    ost = S.sample_stats(z, cfg.seed, 1, rows // L, rows % L)
+    lam = S.jump_prob(cfg.schedule, float(np.float32(ts[1])), float(np.float32(h)))
+    # the Step on the sampled rows
+    b, i = rows // L, rows % L
+    u = philox.jump_uniform(cfg.seed, 1, b, i)
+    c0 = cv0.cpu().numpy().reshape(-1)[rows]
+    conf = ost["c"] >= cfg.lock_threshold
+    want_cv = np.where(conf, ost["a"], np.where(u < lam, ost["y"], c0))
+    gst = {k: v[rows] for k, v in st.items()}
+    excused = compare_step(cv.cpu().numpy().reshape(-1)[rows], lk.cpu().numpy().reshape(-1)[rows], gst,
+                           want_cv, conf, ost, top2_gap(z), cfg.lock_threshold)
+    log(f"  excused rows: {excused} of {len(rows)}")
+    assert excused <= max(1, len(rows) // 1000)
+    tol = 1e-4 if cfg.act_dtype == "f32" else 2e-3
+    assert np.allclose(gst["m"], ost["m"], atol=tol), np.abs(gst["m"] - ost["m"]).max()
+    assert np.allclose(gst["c"], ost["c"], rtol=10 * tol)
+    agree = np.mean(gst["y"] == ost["y"])
+    assert agree >= 0.999 or excused == int(np.sum(gst["y"] != ost["y"]))
