@@ -41,7 +41,8 @@ DG_DEV u32x4 widen_fp8_hi(const u32x4& w) {           // bytes 8..15
   return widen_fp8_lo(t);
 }
 
-template <class TA, class TB, int BM, int BN, int WM, int WN>
+// DEPTH = K tiles in flight from global memory while one is computed (1 or 2).
+template <class TA, class TB, int BM, int BN, int WM, int WN, int DEPTH = 1>
 struct GemmTile {
   static_assert(WM * WN == 4, "4 waves");
   static constexpr int FM = BM / WM / 16;
@@ -57,9 +58,10 @@ struct GemmTile {
   static constexpr int LDS_BYTES = 2 * (LDS_A + LDS_B);
   static_assert(BM * 8 % 256 == 0, "A tile must split evenly over 256 threads");
 
+  static_assert(DEPTH == 1 || DEPTH == 2, "pipeline depth");
   const char* a_ptr[A_CHUNKS];   // row base + chunk offset, or null (zero row)
   const char* b_ptr[B_CHUNKS];
-  u32x4 ra[A_CHUNKS], rb[B_CHUNKS];
+  u32x4 ra[DEPTH][A_CHUNKS], rb[DEPTH][B_CHUNKS];
 
   // arow(r): pointer to A row r of the tile (element 0) or nullptr; likewise brow.
   template <class ARow, class BRow>
@@ -79,25 +81,27 @@ struct GemmTile {
     }
   }
 
-  DG_DEV void load(int kt) {  // global -> registers for K tile kt
+  template <int S>
+  DG_DEV void load(int kt) {  // global -> register set S for K tile kt
     const size_t offa = (size_t)kt * ROW_BYTES;
     const size_t offb = (size_t)kt * (B_FP8 ? ROW_BYTES / 2 : ROW_BYTES);
 #pragma unroll
     for (int i = 0; i < A_CHUNKS; ++i)
-      ra[i] = a_ptr[i] ? *reinterpret_cast<const u32x4*>(a_ptr[i] + offa) : u32x4{0, 0, 0, 0};
+      ra[S][i] = a_ptr[i] ? *reinterpret_cast<const u32x4*>(a_ptr[i] + offa) : u32x4{0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < B_CHUNKS; ++i)
-      rb[i] = b_ptr[i] ? *reinterpret_cast<const u32x4*>(b_ptr[i] + offb) : u32x4{0, 0, 0, 0};
+      rb[S][i] = b_ptr[i] ? *reinterpret_cast<const u32x4*>(b_ptr[i] + offb) : u32x4{0, 0, 0, 0};
   }
 
-  DG_DEV void store(char* lds) {  // registers -> LDS buffer
+  template <int S>
+  DG_DEV void store(char* lds) {  // register set S -> LDS buffer
     const int t = threadIdx.x;
     char* la = lds;
     char* lb = lds + LDS_A;
 #pragma unroll
     for (int i = 0; i < A_CHUNKS; ++i) {
       const int q = t + 256 * i, r = q >> 3, kc = q & 7;
-      *reinterpret_cast<u32x4*>(la + r * ROW_STRIDE + kc * 16) = ra[i];
+      *reinterpret_cast<u32x4*>(la + r * ROW_STRIDE + kc * 16) = ra[S][i];
     }
 #pragma unroll
     for (int i = 0; i < B_CHUNKS; ++i) {
@@ -105,10 +109,10 @@ struct GemmTile {
       if (q >= BN * B_ROWCH) continue;
       const int r = q / B_ROWCH, kc = q % B_ROWCH;
       if constexpr (B_FP8) {
-        *reinterpret_cast<u32x4*>(lb + r * ROW_STRIDE + kc * 32) = widen_fp8_lo(rb[i]);
-        *reinterpret_cast<u32x4*>(lb + r * ROW_STRIDE + kc * 32 + 16) = widen_fp8_hi(rb[i]);
+        *reinterpret_cast<u32x4*>(lb + r * ROW_STRIDE + kc * 32) = widen_fp8_lo(rb[S][i]);
+        *reinterpret_cast<u32x4*>(lb + r * ROW_STRIDE + kc * 32 + 16) = widen_fp8_hi(rb[S][i]);
       } else {
-        *reinterpret_cast<u32x4*>(lb + r * ROW_STRIDE + kc * 16) = rb[i];
+        *reinterpret_cast<u32x4*>(lb + r * ROW_STRIDE + kc * 16) = rb[S][i];
       }
     }
   }
@@ -132,23 +136,48 @@ struct GemmTile {
     }
   }
 
-  // Full K loop; K must be a multiple of KT.  `lds` holds LDS_BYTES.
+  // Full K loop; K must be a multiple of KT.  `lds` holds LDS_BYTES (two tile buffers).
+  // DEPTH 1: tile kt+1 is loaded while kt is computed.  DEPTH 2: tiles kt+1 and kt+2 are in
+  // flight; the loop is unrolled by two so every register set index is a constant.
   DG_DEV void run(char* lds, int K, f32x4_v (&acc)[FM][FN]) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
     const int nk = K / KT;
-    load(0);
-    store(lds);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      char* cur = lds + (kt & 1) * (LDS_A + LDS_B);
-      char* nxt = lds + ((kt + 1) & 1) * (LDS_A + LDS_B);
-      if (kt + 1 < nk) load(kt + 1);
-      compute(cur, acc);
-      if (kt + 1 < nk) store(nxt);
+    char* buf0 = lds;
+    char* buf1 = lds + LDS_A + LDS_B;
+    if constexpr (DEPTH == 1) {
+      load<0>(0);
+      store<0>(buf0);
       __syncthreads();
+      for (int kt = 0; kt < nk; ++kt) {
+        char* cur = (kt & 1) ? buf1 : buf0;
+        char* nxt = (kt & 1) ? buf0 : buf1;
+        if (kt + 1 < nk) load<0>(kt + 1);
+        compute(cur, acc);
+        if (kt + 1 < nk) store<0>(nxt);
+        __syncthreads();
+      }
+    } else {
+      // set 0 carries even tiles, set 1 odd tiles; buffer 0 even tiles, buffer 1 odd tiles
+      load<0>(0);
+      if (nk > 1) load<1>(1);
+      store<0>(buf0);
+      __syncthreads();
+      for (int kt = 0; kt < nk; kt += 2) {
+        // even tile kt in buf0; tile kt+1 in flight in set 1
+        if (kt + 2 < nk) load<0>(kt + 2);
+        compute(buf0, acc);
+        if (kt + 1 < nk) store<1>(buf1);
+        __syncthreads();
+        if (kt + 1 >= nk) break;
+        // odd tile kt+1 in buf1; tile kt+2 in flight in set 0
+        if (kt + 3 < nk) load<1>(kt + 3);
+        compute(buf1, acc);
+        if (kt + 2 < nk) store<0>(buf0);
+        __syncthreads();
+      }
     }
   }
 

@@ -20,6 +20,9 @@ struct DenseArgs {
   int M, N, K;                           // N: output columns (SwiGLU: hidden width)
   void* C; int64_t ldc;
   const float* bias;                     // per-column fp32 bias or null
+  int ksplit;                            // split-K parts (EPI_STORE_F32 only; part s -> C + s*c_split)
+  int64_t c_split;
+  int n_mt, n_nt;                        // filled by the launcher
   // QKV + RoPE
   void* q_out; void* k_out; void* v_out; // q [M][Hq][dh]; k, v [B][Hkv][rows_per_canvas][dh]
   int Hq, Hkv, dh, rows_per_canvas;
@@ -66,20 +69,25 @@ hipError_t launch_rmsnorm(const float* x, const void* g, void* y, int rows, int 
 hipError_t launch_kv_append(const void* kn, const void* vn, void* kc, void* vc, int B, int n,
                             int Hkv, int dh, int cap, int window, int is_global,
                             const int32_t* pos0, int act_bf16, hipStream_t s);
-hipError_t launch_moe_combine(float* resid, const float* y, const float* shared,
-                              const float* gates, const int32_t* inv_perm, int rows, int d,
-                              int k, hipStream_t s);
+hipError_t launch_moe_combine(float* resid, const float* y, const float* shared, int nsp,
+                              int64_t sp_stride, const float* gates, const int32_t* inv_perm,
+                              int rows, int d, int k, hipStream_t s);
+// resid += sum of nparts split-K partials; y = RMSNorm(resid) * g (d <= 4096)
+hipError_t launch_resid_add_rmsnorm(float* resid, const float* parts, int nparts, int64_t pstride,
+                                    const void* g, void* y, int rows, int d, float eps, int act_bf16,
+                                    int* status, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
 
 // ---- routing ---------------------------------------------------------------------------------
-hipError_t launch_router_topk(const float* logits, int T, int E, int k, int32_t* idx,
-                              float* gates, hipStream_t s);
+// router logits = sum of `nparts` split-K partials (part p at parts + p*part_stride) + bias
+hipError_t launch_router_topk(const float* parts, int nparts, int64_t part_stride, const float* bias,
+                              int T, int E, int k, float* logits_out, int32_t* idx, float* gates,
+                              hipStream_t s);
 // counts/offsets [E], perm [T*k], inv_perm [T*k], tok [T*k] (token of grouped position),
 // work [2*max_items] + n_items for BM-row tiles.
 hipError_t launch_route_tables(const int32_t* idx, int T, int E, int k, int32_t* counts,
                                int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* tok,
                                int32_t* work, int32_t* n_items, int bm, hipStream_t s);
-size_t route_tables_lds(int E);
 
 // ---- sampler / Step --------------------------------------------------------------------------
 struct SampArgs {

@@ -87,53 +87,72 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs p) {
   const char* vn = static_cast<const char*>(p.vn) + ((int64_t)(b * p.Hkv + g) * p.n) * DH * C::ESZ;
   const int ring_lo = max(0, P - p.window);
 
-  for (int k0 = k_begin; k0 < k_end; k0 += AT_KEYS) {
-    // ---- stage K (row-major) and V (transposed) ------------------------------------------
-    __syncthreads();
+  // ---- staging: K rows and V rows of one 64-key tile go global -> registers (all loads issued
+  // back to back, for the next tile while the current one is computed) -> LDS.  Rows past the
+  // split's end are clamped to its last key: they are masked out of the softmax (P = 0).
+  // K: chunk q -> key q / CH_ROW, 16-byte column q % CH_ROW (coalesced rows).
+  // V: task q -> keys 4*(q % 16) .. +3 and column q / 16; the four rows are transposed in
+  //    registers so each head-dim row of V^T receives 4 keys in one 8-byte (16-byte fp32) write.
+  constexpr int VTASKS = AT_KEYS / 4 * C::CH_ROW;          // (key quad, column) pairs
+  constexpr int VT = (VTASKS + 255) / 256;                   // V tasks per thread
+  u32x4 kreg[C::CHUNKS], vreg[VT][4];
+  auto key_row = [&](int kk) -> const char* {
+    kk = min(kk, k_end - 1);
+    return kk < np ? kc + (int64_t)kk * DH * C::ESZ : kn + (int64_t)(kk - np) * DH * C::ESZ;
+  };
+  auto val_row = [&](int kk) -> const char* {
+    kk = min(kk, k_end - 1);
+    return kk < np ? vc + (int64_t)kk * DH * C::ESZ : vn + (int64_t)(kk - np) * DH * C::ESZ;
+  };
+  auto load_tile = [&](int k0) {
 #pragma unroll
     for (int it = 0; it < C::CHUNKS; ++it) {
       const int q = threadIdx.x + 256 * it;
-      const int r = q / C::CH_ROW, ch = q % C::CH_ROW;
-      const int kk = k0 + r;
-      u32x4 kv = {0, 0, 0, 0};
-      if (kk < k_end) {
-        const char* src = kk < np ? kc + (int64_t)kk * DH * C::ESZ : kn + (int64_t)(kk - np) * DH * C::ESZ;
-        kv = *reinterpret_cast<const u32x4*>(src + ch * 16);
-      }
-      *reinterpret_cast<u32x4*>(lk + r * C::K_STRIDE + ch * 16) = kv;
+      kreg[it] = *reinterpret_cast<const u32x4*>(key_row(k0 + q / C::CH_ROW) + (q % C::CH_ROW) * 16);
     }
 #pragma unroll
+    for (int it = 0; it < VT; ++it) {
+      const int q = min(threadIdx.x + 256 * it, VTASKS - 1);
+      const int kq = q & 15, ch = q >> 4;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) vreg[it][m] = *reinterpret_cast<const u32x4*>(val_row(k0 + 4 * kq + m) + ch * 16);
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
     for (int it = 0; it < C::CHUNKS; ++it) {
       const int q = threadIdx.x + 256 * it;
-      // 16 consecutive keys x 4 chunks per 64 lanes: 64-byte global runs, narrow LDS spread
-      const int r = (q & 15) + 16 * ((q >> 6) & 3);
-      const int ch = ((q >> 4) & 3) + 4 * (q >> 8);
-      const int kk = k0 + r;
-      u32x4 vv = {0, 0, 0, 0};
-      if (kk < k_end) {
-        const char* src = kk < np ? vc + (int64_t)kk * DH * C::ESZ : vn + (int64_t)(kk - np) * DH * C::ESZ;
-        vv = *reinterpret_cast<const u32x4*>(src + ch * 16);
-      }
-      const int d0 = ch * C::EPL;
+      *reinterpret_cast<u32x4*>(lk + (q / C::CH_ROW) * C::K_STRIDE + (q % C::CH_ROW) * 16) = kreg[it];
+    }
+#pragma unroll
+    for (int it = 0; it < VT; ++it) {
+      const int q = threadIdx.x + 256 * it;
+      if (q >= VTASKS) continue;
+      const int kq = q & 15, ch = q >> 4;
+      char* dst = lv + (ch * C::EPL) * C::V_STRIDE + kq * 4 * C::ESZ;
+      const u32x4* w = vreg[it];
       if constexpr (C::ESZ == 2) {
-        char* dst = lv + d0 * C::V_STRIDE + r * 2;
-        *reinterpret_cast<uint16_t*>(dst + 0 * C::V_STRIDE) = (uint16_t)(vv.x & 0xffff);
-        *reinterpret_cast<uint16_t*>(dst + 1 * C::V_STRIDE) = (uint16_t)(vv.x >> 16);
-        *reinterpret_cast<uint16_t*>(dst + 2 * C::V_STRIDE) = (uint16_t)(vv.y & 0xffff);
-        *reinterpret_cast<uint16_t*>(dst + 3 * C::V_STRIDE) = (uint16_t)(vv.y >> 16);
-        *reinterpret_cast<uint16_t*>(dst + 4 * C::V_STRIDE) = (uint16_t)(vv.z & 0xffff);
-        *reinterpret_cast<uint16_t*>(dst + 5 * C::V_STRIDE) = (uint16_t)(vv.z >> 16);
-        *reinterpret_cast<uint16_t*>(dst + 6 * C::V_STRIDE) = (uint16_t)(vv.w & 0xffff);
-        *reinterpret_cast<uint16_t*>(dst + 7 * C::V_STRIDE) = (uint16_t)(vv.w >> 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int sh = 16 * (e & 1);
+          const uint32_t b0 = (w[0][e >> 1] >> sh) & 0xffffu, b1 = (w[1][e >> 1] >> sh) & 0xffffu;
+          const uint32_t b2 = (w[2][e >> 1] >> sh) & 0xffffu, b3 = (w[3][e >> 1] >> sh) & 0xffffu;
+          *reinterpret_cast<uint2*>(dst + e * C::V_STRIDE) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+        }
       } else {
-        char* dst = lv + d0 * C::V_STRIDE + r * 4;
-        *reinterpret_cast<uint32_t*>(dst + 0 * C::V_STRIDE) = vv.x;
-        *reinterpret_cast<uint32_t*>(dst + 1 * C::V_STRIDE) = vv.y;
-        *reinterpret_cast<uint32_t*>(dst + 2 * C::V_STRIDE) = vv.z;
-        *reinterpret_cast<uint32_t*>(dst + 3 * C::V_STRIDE) = vv.w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          *reinterpret_cast<u32x4*>(dst + e * C::V_STRIDE) = u32x4{w[0][e], w[1][e], w[2][e], w[3][e]};
       }
     }
+  };
+
+  if (k_begin < k_end) load_tile(k_begin);
+  for (int k0 = k_begin; k0 < k_end; k0 += AT_KEYS) {
+    __syncthreads();                  // previous tile fully consumed
+    store_tile();
     __syncthreads();
+    if (k0 + AT_KEYS < k_end) load_tile(k0 + AT_KEYS);   // in flight during this tile's math
 
     // ---- S^T = K . Q^T --------------------------------------------------------------------
     f32x4_v s[4];

@@ -23,40 +23,49 @@ DG_DEV void paired_col(int r, int& u, int& half, int& c) {
   half = nb & 1;
 }
 
+// 1-D grid, XCD-aware: block id mod 8 picks the XCD; the n_mt row tiles of one column (weight)
+// tile get ids congruent mod 8, so they run on one XCD and share its L2 copy of the weights.
+// blockIdx.y is the split-K part.
 template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI, int MAP>
 __global__ __launch_bounds__(256) void gemm_dense_kernel(DenseArgs p) {
-  using G = GemmTile<TA, TB, BM, BN, WM, WN>;
+  using G = GemmTile<TA, TB, BM, BN, WM, WN, 2>;
   extern __shared__ __align__(16) char lds[];
-  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+  const int id = blockIdx.x, xcd = id & 7, local = id >> 3;
+  const int mt = local % p.n_mt;
+  const int nt = (local / p.n_mt) * 8 + xcd;
+  if (nt >= p.n_nt) return;
+  const int n0 = nt * BN, m0 = mt * BM;
+  const int kpart = p.K / p.ksplit, k0 = blockIdx.y * kpart;
   const TA* A = static_cast<const TA*>(p.A);
   const TB* B = static_cast<const TB*>(p.B);
   const TB* B2 = static_cast<const TB*>(p.B2);
   auto arow = [&](int r) -> const TA* {
     const int m = m0 + r;
-    return m < p.M ? A + (int64_t)m * p.lda : nullptr;
+    return m < p.M ? A + (int64_t)m * p.lda + k0 : nullptr;
   };
   auto brow = [&](int r) -> const TB* {
     if constexpr (MAP == MAP_PLAIN) {
       const int n = n0 + r;
-      return n < p.N ? B + (int64_t)n * p.ldb : nullptr;
+      return n < p.N ? B + (int64_t)n * p.ldb + k0 : nullptr;
     } else if constexpr (MAP == MAP_SWIGLU) {
       int u, half, c;
       paired_col<BN>(r, u, half, c);
       const int oc = n0 / 2 + u * 16 + c;
       if (oc >= p.N) return nullptr;
-      return (half ? B2 : B) + (int64_t)oc * p.ldb;
+      return (half ? B2 : B) + (int64_t)oc * p.ldb + k0;
     } else {  // MAP_ROPE: tile inside one head
       int u, half, c;
       paired_col<BN>(r, u, half, c);
       const int head = n0 / p.dh, pb = (n0 % p.dh) / 2;
       const int row = head * p.dh + half * (p.dh / 2) + pb + u * 16 + c;
-      return B + (int64_t)row * p.ldb;
+      return B + (int64_t)row * p.ldb + k0;
     }
   };
   G g;
   g.setup(arow, brow);
   f32x4_v acc[G::FM][G::FN];
-  g.run(lds, p.K, acc);
+  g.run(lds, kpart, acc);
+  float* const C32 = static_cast<float*>(p.C) + (int64_t)blockIdx.y * p.c_split;
 
   const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) % WN;
   if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_ADD_F32 || EPI == EPI_STORE_ACT) {
@@ -75,7 +84,7 @@ __global__ __launch_bounds__(256) void gemm_dense_kernel(DenseArgs p) {
           if (m >= p.M) continue;
           const float v = acc[i][j][e] * sc + bias;
           if constexpr (EPI == EPI_STORE_F32) {
-            static_cast<float*>(p.C)[(int64_t)m * p.ldc + n] = v;
+            C32[(int64_t)m * p.ldc + n] = v;
           } else if constexpr (EPI == EPI_ADD_F32) {
             static_cast<float*>(p.C)[(int64_t)m * p.ldc + n] += v;
           } else {
@@ -147,7 +156,7 @@ __global__ __launch_bounds__(256) void gemm_dense_kernel(DenseArgs p) {
 // [offsets[e], offsets[e] + counts[e]) in grouped order.
 template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(256) void gemm_grouped_kernel(GroupedArgs p) {
-  using G = GemmTile<TA, TB, BM, BN, WM, WN>;
+  using G = GemmTile<TA, TB, BM, BN, WM, WN, 2>;
   extern __shared__ __align__(16) char lds[];
   const int item = blockIdx.y;
   if (item >= *p.n_items) return;
@@ -223,9 +232,13 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GroupedArgs p) {
 
 // ---------------------------------------------------------------- launchers --------------------
 template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI, int MAP>
-static hipError_t launch_dense_t(const DenseArgs& a, int n_eff, hipStream_t s) {
-  using G = GemmTile<TA, TB, BM, BN, WM, WN>;
-  dim3 grid((n_eff + BN - 1) / BN, (a.M + BM - 1) / BM);
+static hipError_t launch_dense_t(DenseArgs a, int n_eff, hipStream_t s) {
+  using G = GemmTile<TA, TB, BM, BN, WM, WN, 2>;
+  a.n_mt = (a.M + BM - 1) / BM;
+  a.n_nt = (n_eff + BN - 1) / BN;
+  if (a.ksplit < 1) a.ksplit = 1;
+  if (a.K % (a.ksplit * G::KT)) return hipErrorInvalidValue;
+  dim3 grid(a.n_mt * ((a.n_nt + 7) / 8 * 8), a.ksplit);
   static const hipError_t attr = allow_lds(gemm_dense_kernel<TA, TB, BM, BN, WM, WN, EPI, MAP>, G::LDS_BYTES);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((gemm_dense_kernel<TA, TB, BM, BN, WM, WN, EPI, MAP>), grid, dim3(256),
@@ -233,15 +246,31 @@ static hipError_t launch_dense_t(const DenseArgs& a, int n_eff, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Tiles.  Up to 256 rows: 128-row tiles (64 for tiny M) so each weight tile is read by at most
+// two blocks, 64 (32 for SwiGLU) columns so enough blocks stream the weights; paired epilogues
+// keep an even count of 16-column blocks per wave.  Above 256 rows: 128 x 128 tiles.
 template <class TA, class TB, int EPI, int MAP>
 static hipError_t dense_pick(const DenseArgs& a, int n_eff, hipStream_t s) {
-  // small M: 32-row tiles with 4 waves along N; else 64 x 64 tiles, 2 x 2 waves
-  if (a.M <= 32) return launch_dense_t<TA, TB, 32, 64, 2, 2, EPI, MAP>(a, n_eff, s);
-  return launch_dense_t<TA, TB, 64, 64, 2, 2, EPI, MAP>(a, n_eff, s);
+  const bool small = a.M <= 64;
+  if constexpr (MAP == MAP_ROPE) {
+    // a column tile must stay inside one head
+    if (a.M > 256 && a.dh >= 128) return launch_dense_t<TA, TB, 128, 128, 2, 2, EPI, MAP>(a, n_eff, s);
+    if (small) return launch_dense_t<TA, TB, 64, 64, 2, 2, EPI, MAP>(a, n_eff, s);
+    return launch_dense_t<TA, TB, 128, 64, 2, 2, EPI, MAP>(a, n_eff, s);
+  } else if constexpr (MAP == MAP_SWIGLU) {
+    if (a.M > 256) return launch_dense_t<TA, TB, 128, 128, 2, 2, EPI, MAP>(a, n_eff, s);
+    if (small) return launch_dense_t<TA, TB, 64, 32, 4, 1, EPI, MAP>(a, n_eff, s);
+    return launch_dense_t<TA, TB, 128, 32, 4, 1, EPI, MAP>(a, n_eff, s);
+  } else {
+    if (a.M > 256) return launch_dense_t<TA, TB, 128, 128, 2, 2, EPI, MAP>(a, n_eff, s);
+    if (small) return launch_dense_t<TA, TB, 64, 64, 2, 2, EPI, MAP>(a, n_eff, s);
+    return launch_dense_t<TA, TB, 128, 64, 2, 2, EPI, MAP>(a, n_eff, s);
+  }
 }
 
 template <class TA, class TB>
 static hipError_t dense_dispatch(const DenseArgs& a, hipStream_t s) {
+  if (a.ksplit > 1 && a.epi != EPI_STORE_F32) return hipErrorInvalidValue;
   switch (a.epi) {
     case EPI_STORE_F32: return dense_pick<TA, TB, EPI_STORE_F32, MAP_PLAIN>(a, a.N, s);
     case EPI_ADD_F32: return dense_pick<TA, TB, EPI_ADD_F32, MAP_PLAIN>(a, a.N, s);
@@ -263,7 +292,7 @@ hipError_t launch_dense(const DenseArgs& a, int act_bf16, int w_kind, hipStream_
 
 template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI>
 static hipError_t launch_grouped_t(const GroupedArgs& a, int n_eff, int max_items, hipStream_t s) {
-  using G = GemmTile<TA, TB, BM, BN, WM, WN>;
+  using G = GemmTile<TA, TB, BM, BN, WM, WN, 2>;
   dim3 grid((n_eff + BN - 1) / BN, max_items);
   static const hipError_t attr = allow_lds(gemm_grouped_kernel<TA, TB, BM, BN, WM, WN, EPI>, G::LDS_BYTES);
   if (attr != hipSuccess) return attr;

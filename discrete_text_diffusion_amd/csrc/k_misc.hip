@@ -67,6 +67,55 @@ hipError_t launch_rmsnorm(const float* x, const void* g, void* y, int rows, int 
   return hipGetLastError();
 }
 
+// resid += sum_s parts[s] (split-K partials, in part order); y = RMSNorm(resid) * g.  One block per
+// row; the updated row stays in registers between the two passes (d <= 256 * RN_MAX).
+constexpr int RN_MAX = 16;
+template <class T>
+__global__ __launch_bounds__(256) void resid_add_rmsnorm_kernel(float* resid, const float* parts, int nparts,
+                                                                int64_t pstride, const T* g, T* y, int d, float eps,
+                                                                int* status) {
+  const int r = blockIdx.x;
+  float* xr = resid + (int64_t)r * d;
+  float v[RN_MAX];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < RN_MAX; ++j) {
+    const int c = threadIdx.x + 256 * j;
+    v[j] = 0.f;
+    if (c < d) {
+      float a = xr[c];
+      for (int q = 0; q < nparts; ++q) a += parts[q * pstride + (int64_t)r * d + c];
+      xr[c] = a;
+      v[j] = a;
+      ss += a * a;
+    }
+  }
+  ss = wave_sum(ss);
+  __shared__ float part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = part[0] + part[1] + part[2] + part[3];
+  const float inv = rsqrtf(tot / (float)d + eps);
+  if (threadIdx.x == 0 && status && !isfinite(tot)) atomicOr(status, 2);
+#pragma unroll
+  for (int j = 0; j < RN_MAX; ++j) {
+    const int c = threadIdx.x + 256 * j;
+    if (c < d) y[(int64_t)r * d + c] = Elem<T>::from_f(v[j] * inv * Elem<T>::to_f(g[c]));
+  }
+}
+
+hipError_t launch_resid_add_rmsnorm(float* resid, const float* parts, int nparts, int64_t pstride, const void* g,
+                                    void* y, int rows, int d, float eps, int bf, int* status, hipStream_t s) {
+  if (d > 256 * RN_MAX) return hipErrorInvalidValue;
+  if (bf)
+    hipLaunchKernelGGL(resid_add_rmsnorm_kernel<bf16_t>, dim3(rows), dim3(256), 0, s, resid, parts, nparts, pstride,
+                       (const bf16_t*)g, (bf16_t*)y, d, eps, status);
+  else
+    hipLaunchKernelGGL(resid_add_rmsnorm_kernel<float>, dim3(rows), dim3(256), 0, s, resid, parts, nparts, pstride,
+                       (const float*)g, (float*)y, d, eps, status);
+  return hipGetLastError();
+}
+
 // new keys/values [B][Hkv][n][dh] -> cache slots: position p in slot p (global) or p % window
 // (local ring; only the last `window` of the new positions are kept)
 struct AppendArgs {
@@ -107,27 +156,32 @@ hipError_t launch_kv_append(const void* kn, const void* vn, void* kc, void* vc, 
   return hipGetLastError();
 }
 
-// resid[t] += sum_{s<k} gate[t][s] * y[inv_perm[t*k+s]] + shared[t], slots in order
-__global__ void moe_combine_kernel(float* resid, const float* y, const float* shared, const float* gates,
-                                   const int32_t* inv_perm, int d, int k) {
+// resid[t] += sum_{s<k} gate[t][s] * y[inv_perm[t*k+s]] + shared[t], slots in order; the shared
+// expert output arrives as `nsp` split-K partials summed in part order
+__global__ void moe_combine_kernel(float* resid, const float* y, const float* shared, int nsp, int64_t sp_stride,
+                                   const float* gates, const int32_t* inv_perm, int rows, int d, int k) {
   const int t = blockIdx.y;
   const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (c >= d) return;
   f32x4_v acc = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < k; ++s) {
     const float gt = gates[(int64_t)t * k + s];
-    const f32x4_v v = *reinterpret_cast<const f32x4_v*>(y + (int64_t)inv_perm[(int64_t)t * k + s] * d + c);
+    // grouped positions are a permutation of [0, rows*k); the clamp only guards the read
+    const int pos = min(max(inv_perm[(int64_t)t * k + s], 0), rows * k - 1);
+    const f32x4_v v = *reinterpret_cast<const f32x4_v*>(y + (int64_t)pos * d + c);
     acc += gt * v;
   }
   f32x4_v* r = reinterpret_cast<f32x4_v*>(resid + (int64_t)t * d + c);
-  const f32x4_v sh = *reinterpret_cast<const f32x4_v*>(shared + (int64_t)t * d + c);
+  f32x4_v sh = *reinterpret_cast<const f32x4_v*>(shared + (int64_t)t * d + c);
+  for (int q = 1; q < nsp; ++q) sh += *reinterpret_cast<const f32x4_v*>(shared + q * sp_stride + (int64_t)t * d + c);
   *r = *r + (acc + sh);
 }
 
-hipError_t launch_moe_combine(float* resid, const float* y, const float* shared, const float* gates,
-                              const int32_t* inv_perm, int rows, int d, int k, hipStream_t s) {
+hipError_t launch_moe_combine(float* resid, const float* y, const float* shared, int nsp, int64_t sp_stride,
+                              const float* gates, const int32_t* inv_perm, int rows, int d, int k, hipStream_t s) {
   dim3 grid((d / 4 + 255) / 256, rows);
-  hipLaunchKernelGGL(moe_combine_kernel, grid, dim3(256), 0, s, resid, y, shared, gates, inv_perm, d, k);
+  hipLaunchKernelGGL(moe_combine_kernel, grid, dim3(256), 0, s, resid, y, shared, nsp, sp_stride, gates, inv_perm,
+                     rows, d, k);
   return hipGetLastError();
 }
 

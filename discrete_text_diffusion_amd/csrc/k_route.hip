@@ -7,8 +7,11 @@
 
 namespace dg {
 
-// one wave per row; E <= 256 (4 values per lane), k <= 16
-__global__ __launch_bounds__(256) void router_topk_kernel(const float* logits, int T, int E, int k,
+// One wave per row; E <= 256 (4 values per lane), k <= 16.  The router logits arrive as
+// `nparts` split-K partial sums, added in part order (deterministic), plus the optional bias.
+template <int K>
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* parts, int nparts, int64_t part_stride,
+                                                          const float* bias, int T, int E, int k, float* logits_out,
                                                           int32_t* idx, float* gates) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -17,116 +20,161 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* logits, i
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + 64 * j;
-    v[j] = e < E ? logits[(int64_t)t * E + e] : -INFINITY;
+    float acc = -INFINITY;
+    if (e < E) {
+      acc = parts[(int64_t)t * E + e];
+      for (int p = 1; p < nparts; ++p) acc += parts[p * part_stride + (int64_t)t * E + e];
+      if (bias) acc += bias[e];
+      if (logits_out) logits_out[(int64_t)t * E + e] = acc;
+    }
+    v[j] = acc;
   }
-  float sel_v[16];
-  int sel_i[16];
-  for (int s = 0; s < k; ++s) {
-    // lane-local best (lowest id on ties: j ascending = id ascending)
-    float bv = v[0]; int bi = lane;
+  // NaN scores count as -inf; an explicit taken mask keeps the k picks distinct even when fewer
+  // than k scores are finite (untaken entries always beat taken ones)
 #pragma unroll
-    for (int j = 1; j < 4; ++j)
-      if (v[j] > bv) { bv = v[j]; bi = lane + 64 * j; }
+  for (int j = 0; j < 4; ++j)
+    if (!(v[j] == v[j])) v[j] = -INFINITY;
+  unsigned taken = 0;
+  float sel_v[K];
+  int sel_i[K];
+#pragma unroll
+  for (int s = 0; s < K; ++s) {
+    if (s >= k) break;
+    // lane-local best among untaken entries (lowest id on ties: j ascending = id ascending)
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + 64 * j;
+      if (e < E && !(taken >> j & 1u) && (v[j] > bv || bi == 0x7fffffff)) { bv = v[j]; bi = e; }
+    }
+#pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       const float ov = __shfl_xor(bv, o, 64);
       const int oi = __shfl_xor(bi, o, 64);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) { bv = ov; bi = oi; }
     }
+    bi = min(max(bi, 0), E - 1);
     sel_v[s] = bv;
     sel_i[s] = bi;
-    if ((bi & 63) == lane) v[bi >> 6] = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (bi == lane + 64 * j) taken |= 1u << j;
   }
   if (lane == 0) {
-    float mx = sel_v[0];
-    float w[16], tot = 0.f;
-    for (int s = 0; s < k; ++s) { w[s] = __expf(sel_v[s] - mx); tot += w[s]; }
-    for (int s = 0; s < k; ++s) {
-      idx[(int64_t)t * k + s] = sel_i[s];
-      gates[(int64_t)t * k + s] = w[s] / tot;
-    }
+    const float mx = sel_v[0];
+    float tot = 0.f;
+#pragma unroll
+    for (int s = 0; s < K; ++s)
+      if (s < k) tot += sel_v[s] == -INFINITY ? 0.f : __expf(sel_v[s] - mx);
+#pragma unroll
+    for (int s = 0; s < K; ++s)
+      if (s < k) {
+        idx[(int64_t)t * k + s] = sel_i[s];
+        gates[(int64_t)t * k + s] = tot > 0.f && sel_v[s] != -INFINITY ? __expf(sel_v[s] - mx) / tot : 0.f;
+      }
   }
 }
 
-hipError_t launch_router_topk(const float* logits, int T, int E, int k, int32_t* idx, float* gates,
-                              hipStream_t s) {
-  hipLaunchKernelGGL(router_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, idx, gates);
+hipError_t launch_router_topk(const float* parts, int nparts, int64_t part_stride, const float* bias, int T, int E,
+                              int k, float* logits_out, int32_t* idx, float* gates, hipStream_t s) {
+  const dim3 grid((T + 3) / 4);
+  if (k <= 2)
+    hipLaunchKernelGGL(router_topk_kernel<2>, grid, dim3(256), 0, s, parts, nparts, part_stride, bias, T, E, k, logits_out, idx, gates);
+  else if (k <= 8)
+    hipLaunchKernelGGL(router_topk_kernel<8>, grid, dim3(256), 0, s, parts, nparts, part_stride, bias, T, E, k, logits_out, idx, gates);
+  else
+    hipLaunchKernelGGL(router_topk_kernel<16>, grid, dim3(256), 0, s, parts, nparts, part_stride, bias, T, E, k, logits_out, idx, gates);
   return hipGetLastError();
 }
 
-// Single block.  Thread t owns the contiguous assignment range [t*chunk, (t+1)*chunk) and a
-// private counter column cnt[e][t]; an exclusive scan over (expert, thread) gives each thread
-// its write base per expert, so the grouped order is ascending assignment id within an expert.
-static int route_threads(int E) { return E <= 128 ? 256 : 128; }
+// ---- grouping -------------------------------------------------------------------------------
+// The experts of one row are distinct, so for expert e the flag "row t chose e" is 0/1 and the
+// grouped position of (t, s) is offsets[e] + (number of earlier rows that chose e).
 
-size_t route_tables_lds(int E) { return (size_t)E * route_threads(E) * 4 + 1024 * 4; }
+DG_DEV int chosen_slot(const int32_t* idx, int t, int k, int e) {
+  int slot = -1;
+  for (int s = 0; s < k; ++s)
+    if (idx[(int64_t)t * k + s] == e) slot = s;
+  return slot;
+}
 
-__global__ void route_tables_kernel(const int32_t* idx, int T, int E, int k, int32_t* counts,
-                                    int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* tok,
-                                    int32_t* work, int32_t* n_items, int bm) {
-  extern __shared__ int32_t sm[];
-  const int NT = blockDim.x, tid = threadIdx.x;
-  int32_t* cnt = sm;                     // [E][NT]
-  int32_t* tsum = sm + E * NT;           // [NT] scan scratch (+ tile scan)
-  const int A = T * k;
-  const int chunk = (A + NT - 1) / NT;
-  const int a0 = min(A, tid * chunk), a1 = min(A, a0 + chunk);
-  for (int e = 0; e < E; ++e) cnt[e * NT + tid] = 0;
-  // ids come from router_topk and are always in [0, E); the clamp keeps a corrupted id in bounds
-  for (int a = a0; a < a1; ++a) cnt[min(max(idx[a], 0), E - 1) * NT + tid] += 1;
+// block e: counts[e]
+__global__ __launch_bounds__(256) void route_count_kernel(const int32_t* idx, int T, int k, int32_t* counts) {
+  const int e = blockIdx.x;
+  int c = 0;
+  for (int t = threadIdx.x; t < T; t += 256) c += chosen_slot(idx, t, k, e) >= 0;
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+  __shared__ int part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = c;
   __syncthreads();
-  // exclusive scan over the flattened [E][NT] array: thread t scans segment [t*E, (t+1)*E)
-  const int seg0 = tid * E;
-  int s = 0;
-  for (int q = 0; q < E; ++q) s += cnt[seg0 + q];
-  tsum[tid] = s;
+  if (threadIdx.x == 0) counts[e] = part[0] + part[1] + part[2] + part[3];
+}
+
+// one block: offsets (exclusive scan of counts) and the (expert, first row) work list of bm-row tiles
+__global__ __launch_bounds__(256) void route_scan_kernel(const int32_t* counts, int E, int bm, int32_t* offsets,
+                                                         int32_t* work, int32_t* n_items) {
+  __shared__ int s_off[256], s_til[256];
+  const int e = threadIdx.x;
+  const int c = e < E ? counts[e] : 0;
+  s_off[e] = c;
+  s_til[e] = (c + bm - 1) / bm;
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int q = 0; q < NT; ++q) { const int v = tsum[q]; tsum[q] = run; run += v; }
-  }
-  __syncthreads();
-  int run = tsum[tid];
-  for (int q = 0; q < E; ++q) { const int v = cnt[seg0 + q]; cnt[seg0 + q] = run; run += v; }
-  __syncthreads();
-  // per-expert counts/offsets and tile counts
-  int32_t* tiles = tsum;                 // reuse: [E] tile offsets
-  if (tid == 0) {
-    int acc = 0;
-    for (int e = 0; e < E; ++e) {
-      const int off = cnt[e * NT];
-      const int nxt = e + 1 < E ? cnt[(e + 1) * NT] : A;
-      offsets[e] = off;
-      counts[e] = nxt - off;
-      tiles[e] = acc;
-      acc += (nxt - off + bm - 1) / bm;
+  if (e == 0) {
+    int ro = 0, rt = 0;
+    for (int q = 0; q < E; ++q) {
+      const int vo = s_off[q], vt = s_til[q];
+      s_off[q] = ro; s_til[q] = rt;
+      ro += vo; rt += vt;
     }
-    *n_items = acc;
+    *n_items = rt;
   }
   __syncthreads();
-  for (int e = tid; e < E; e += NT) {
-    const int off = cnt[e * NT];
-    const int c = (e + 1 < E ? cnt[(e + 1) * NT] : A) - off;
-    int w = tiles[e];
-    for (int m0 = 0; m0 < c; m0 += bm, ++w) { work[2 * w] = e; work[2 * w + 1] = m0; }
+  if (e < E) {
+    offsets[e] = s_off[e];
+    int w = s_til[e];
+    for (int m0 = 0; m0 < c; m0 += bm, ++w) {
+      work[2 * w] = e;
+      work[2 * w + 1] = m0;
+    }
   }
-  // scatter: positions in ascending assignment order within each expert
-  for (int a = a0; a < a1; ++a) {
-    const int e = min(max(idx[a], 0), E - 1);
-    const int pos = cnt[e * NT + tid]++;
-    perm[pos] = a;
-    inv_perm[a] = pos;
-    tok[pos] = a / k;
+}
+
+// block e: positions of expert e's rows in ascending row order
+__global__ __launch_bounds__(256) void route_scatter_kernel(const int32_t* idx, int T, int k, const int32_t* offsets,
+                                                            int32_t* perm, int32_t* inv_perm, int32_t* tok) {
+  const int e = blockIdx.x;
+  __shared__ int wsum[4];
+  int base = offsets[e];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int t0 = 0; t0 < T; t0 += 256) {
+    const int t = t0 + threadIdx.x;
+    const int slot = t < T ? chosen_slot(idx, t, k, e) : -1;
+    const uint64_t m = __ballot(slot >= 0);
+    const int rank_in_wave = __popcll(m & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[wave] = __popcll(m);
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    if (slot >= 0) {
+      const int pos = base + before + rank_in_wave;
+      const int a = t * k + slot;
+      perm[pos] = a;
+      inv_perm[a] = pos;
+      tok[pos] = t;
+    }
+    base += total;
+    __syncthreads();
   }
 }
 
 hipError_t launch_route_tables(const int32_t* idx, int T, int E, int k, int32_t* counts, int32_t* offsets,
-                               int32_t* perm, int32_t* inv_perm, int32_t* tok, int32_t* work,
-                               int32_t* n_items, int bm, hipStream_t s) {
-  const int NT = route_threads(E);
-  static const hipError_t attr = allow_lds(route_tables_kernel, route_tables_lds(256));
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(route_tables_kernel, dim3(1), dim3(NT), route_tables_lds(E), s, idx, T, E, k, counts,
-                     offsets, perm, inv_perm, tok, work, n_items, bm);
+                               int32_t* perm, int32_t* inv_perm, int32_t* tok, int32_t* work, int32_t* n_items,
+                               int bm, hipStream_t s) {
+  hipLaunchKernelGGL(route_count_kernel, dim3(E), dim3(256), 0, s, idx, T, k, counts);
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(256), 0, s, counts, E, bm, offsets, work, n_items);
+  hipLaunchKernelGGL(route_scatter_kernel, dim3(E), dim3(256), 0, s, idx, T, k, offsets, perm, inv_perm, tok);
   return hipGetLastError();
 }
 

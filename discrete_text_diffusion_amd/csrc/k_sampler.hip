@@ -238,49 +238,70 @@ hipError_t launch_logits_partials(const float* z, int rows, int V, int L, float 
 }
 
 // ------------------------------------------------------------------ merge + Step -----------------
-// One block per canvas, one thread per position.
-__global__ __launch_bounds__(1024) void step_merge_kernel(StepArgs p) {
-  const int b = blockIdx.x, i = threadIdx.x;
+// One wave per position: lane j merges slices j, j+64, ... in ascending order, then a fixed xor
+// tree combines the lanes (deterministic).  Lane 0 applies the Step to the position.
+__global__ __launch_bounds__(256) void step_merge_kernel(StepArgs p) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int rows = p.B * p.L;
-  const bool is_done = p.done && p.done[b] != 0;
-  int locked = 0, bad = 0;
-  if (i < p.L) {
-    const int r = b * p.L + i;
-    RowState s;
-    state_init(s);
-    for (int sl = 0; sl < p.slices; ++sl) {
-      const float* q = p.part + ((size_t)sl * rows + r) * PART;
-      state_merge(s, q[0], q[1], __float_as_int(q[2]), q[3], __float_as_int(q[4]));
-    }
-    const float c = 1.f / s.s;
-    bad = !(isfinite(s.m2) && isfinite(s.s) && isfinite(s.g2));
-    if (p.stats) {
-      float* o = p.stats + (size_t)r * 5;
-      o[0] = s.m2 * LN2; o[1] = __int_as_float(s.a); o[2] = c; o[3] = __int_as_float(s.y);
-      o[4] = s.g2 * LN2;
-    }
-    locked = p.lock[r];
-    if (!is_done && !locked && !bad) {
-      if (c >= p.theta) {
-        p.canvas[r] = s.a;
-        p.lock[r] = 1;
-        locked = 1;
-      } else {
-        const u32x4 w = philox((uint32_t)(i >> 2), 0u, p.step, ((uint32_t)b << 8) | TAG_JUMP, p.k0, p.k1);
-        if (unit_co(pick(w, i & 3)) < p.lam) p.canvas[r] = s.y;
-      }
-    }
+  if (r >= rows) return;
+  const int b = r / p.L, i = r - b * p.L;
+  RowState s;
+  state_init(s);
+  for (int sl = lane; sl < p.slices; sl += 64) {
+    const float* q = p.part + ((size_t)sl * rows + r) * PART;
+    state_merge(s, q[0], q[1], __float_as_int(q[2]), q[3], __float_as_int(q[4]));
   }
-  __shared__ int red[2][16];
-  int nl = locked, nb = bad;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float m2 = __shfl_xor(s.m2, o, 64), ss = __shfl_xor(s.s, o, 64), g2 = __shfl_xor(s.g2, o, 64);
+    const int a = __shfl_xor(s.a, o, 64), y = __shfl_xor(s.y, o, 64);
+    state_merge(s, m2, ss, a, g2, y);
+  }
+  if (lane != 0) return;
+  const float c = 1.f / s.s;
+  const bool bad = !(isfinite(s.m2) && isfinite(s.s) && isfinite(s.g2));
+  if (p.stats) {
+    float* o = p.stats + (size_t)r * 5;
+    o[0] = s.m2 * LN2; o[1] = __int_as_float(s.a); o[2] = c; o[3] = __int_as_float(s.y);
+    o[4] = s.g2 * LN2;
+  }
+  if (bad) {
+    if (p.status) atomicOr(p.status, 1);
+    return;
+  }
+  const bool is_done = p.done && p.done[b] != 0;
+  if (is_done || p.lock[r]) return;
+  if (c >= p.theta) {
+    p.canvas[r] = s.a;
+    p.lock[r] = 1;
+  } else {
+    const u32x4 w = philox((uint32_t)(i >> 2), 0u, p.step, ((uint32_t)b << 8) | TAG_JUMP, p.k0, p.k1);
+    if (unit_co(pick(w, i & 3)) < p.lam) p.canvas[r] = s.y;
+  }
+}
+
+// One block per canvas: locked count (-1 if a non-finite statistic was seen in the canvas),
+// steps taken and the done flag of the adaptive loop.
+__global__ __launch_bounds__(256) void step_count_kernel(StepArgs p) {
+  const int b = blockIdx.x;
+  const int rows = p.B * p.L;
+  int nl = 0, nb = 0;
+  for (int i = threadIdx.x; i < p.L; i += 256) {
+    const int r = b * p.L + i;
+    nl += p.lock[r] != 0;
+    if (p.stats) nb += !isfinite(p.stats[(size_t)r * 5 + 2]) || !isfinite(p.stats[(size_t)r * 5]);
+  }
+  (void)rows;
   for (int o = 32; o > 0; o >>= 1) { nl += __shfl_xor(nl, o, 64); nb += __shfl_xor(nb, o, 64); }
+  __shared__ int red[2][4];
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) { red[0][wave] = nl; red[1][wave] = nb; }
   __syncthreads();
   if (threadIdx.x == 0) {
-    int tl = 0, tb = 0;
-    for (int w = 0; w < (int)(blockDim.x + 63) / 64; ++w) { tl += red[0][w]; tb += red[1][w]; }
-    if (tb && p.status) atomicOr(p.status, 1);
+    const int tl = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+    const int tb = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+    const bool is_done = p.done && p.done[b] != 0;
     if (p.n_locked) p.n_locked[b] = tb ? -1 : tl;
     if (!is_done && p.steps_taken) p.steps_taken[b] += 1;
     if (p.done_out) p.done_out[b] = (tl == p.L) ? 1 : (p.done ? p.done[b] : 0);
@@ -288,8 +309,9 @@ __global__ __launch_bounds__(1024) void step_merge_kernel(StepArgs p) {
 }
 
 hipError_t launch_step_merge(const StepArgs& a, hipStream_t s) {
-  const int threads = (a.L + 63) / 64 * 64;
-  hipLaunchKernelGGL(step_merge_kernel, dim3(a.B), dim3(threads), 0, s, a);
+  const int rows = a.B * a.L;
+  hipLaunchKernelGGL(step_merge_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(step_count_kernel, dim3(a.B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -62,6 +62,8 @@ dg_status fail(dg_status s, const char* fmt, ...) {
 
 constexpr size_t ALIGN = 256;
 constexpr int MAX_SPLITS = 16;
+constexpr int MAX_RSPLIT = 16;   // split-K parts of the router GEMM
+constexpr int MAX_KSPLIT = 8;    // split-K parts of the O projection and the shared-expert down GEMM
 constexpr int SAMP_BM = 128, SAMP_BN = 128;
 
 inline size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
@@ -88,9 +90,9 @@ int sampler_slices(const dg_model_desc& d, int rows, int* v_per_slice) {
 // on the row count, so the test hooks can find them from `rows` alone.
 struct Layout {
   size_t status, stats, rlogits, idx, gates;
-  size_t resid, xhat, q, kn, vn, attn_o, part_o, part_ml;
+  size_t resid, xhat, q, kn, vn, attn_o, part_o, part_ml, rparts, o_parts, sh_parts;
   size_t counts, offsets, perm, inv_perm, tok, work, n_items;
-  size_t a_grp, y, sh_a, sh_out, samp_part, hidden, done, n_locked;
+  size_t a_grp, y, sh_a, samp_part, hidden, done, n_locked;
   size_t total;
   int max_items;
 };
@@ -115,6 +117,9 @@ Layout layout(const dg_model_desc& d, int B, int n, int max_prefix) {
   (void)max_prefix;
   w.part_o = take((size_t)MAX_SPLITS * R * d.n_q_heads * d.head_dim * 4);
   w.part_ml = take((size_t)MAX_SPLITS * R * d.n_q_heads * 2 * 4);
+  w.rparts = take((size_t)MAX_RSPLIT * R * d.n_experts * 4);
+  w.o_parts = take((size_t)MAX_KSPLIT * R * d.d_model * 4);
+  w.sh_parts = take((size_t)MAX_KSPLIT * R * d.d_model * 4);
   w.counts = take(d.n_experts * 4);
   w.offsets = take(d.n_experts * 4);
   w.perm = take(Rk * 4);
@@ -126,7 +131,6 @@ Layout layout(const dg_model_desc& d, int B, int n, int max_prefix) {
   w.a_grp = take(Rk * d.expert_hidden * ab);
   w.y = take(Rk * d.d_model * 4);
   w.sh_a = take(R * d.shared_hidden * ab);
-  w.sh_out = take(R * d.d_model * 4);
   int vps;
   const int slices = sampler_slices(d, (int)R, &vps);
   w.samp_part = take((size_t)((slices + 7) / 8 * 8) * R * 5 * 4);
@@ -231,6 +235,34 @@ struct Pass {
   hipStream_t s;
 };
 
+// Block tiles the dense GEMM launcher picks for M rows (mirrors k_gemm.hip's dense_pick).
+int dense_blocks(int M, int N) {
+  const int bm = M > 256 ? 128 : (M > 64 ? 128 : 64), bn = M > 256 ? 128 : 64;
+  return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+}
+
+// split-K parts for a narrow dense GEMM: the largest divisor of the K-tile count (at most
+// MAX_KSPLIT, at least two K tiles per part) that keeps the block count at or below 512
+int ksplit_for(const dg_model_desc& d, int M, int N, int K) {
+  const int nk = K / (d.act_dtype == DG_BF16 ? 64 : 32);
+  const int blocks = dense_blocks(M, N);
+  int best = 1;
+  for (int s = 1; s <= MAX_KSPLIT; ++s)
+    if (nk % s == 0 && nk / s >= 2 && blocks * s <= 512) best = s;
+  return best;
+}
+
+// split-K parts for the router GEMM (N = n_experts is narrow): a divisor of the K-tile count
+// that brings the block count near 256
+int router_splits(const dg_model_desc& d, int R) {
+  const int kt = d.d_model / (d.act_dtype == DG_BF16 ? 64 : 32);
+  const int tiles = dense_blocks(R, d.n_experts);
+  int best = 1;
+  for (int s = 1; s <= MAX_RSPLIT; ++s)
+    if (kt % s == 0 && kt / s >= 2 && tiles * s <= 512) best = s;
+  return best;
+}
+
 int attn_splits(const dg_model_desc& d, int B, int n, int nkeys) {
   const int qtiles = (d.n_q_heads / d.n_kv_heads * n + 63) / 64;
   const int base = B * d.n_kv_heads * qtiles;
@@ -295,33 +327,38 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn) {
     HIPCHK(launch_kv_append(at<void>(ws, w.kn), at<void>(ws, w.vn), P.kv->k[l], P.kv->v[l], P.B, P.n,
                             d.n_kv_heads, d.head_dim, P.kv->cap[l], d.window, glob, aa.pos0, bf, P.s));
   }
-  // O projection + residual
+  // O projection as split-K partials; the fused kernel adds them to the residual (in part order)
+  // and applies the FFN RMSNorm
   DenseArgs oa{};
-  oa.epi = EPI_ADD_F32;
+  oa.epi = EPI_STORE_F32;
   oa.A = at<void>(ws, w.attn_o); oa.lda = d.n_q_heads * d.head_dim;
   oa.B = L.w_o; oa.ldb = d.n_q_heads * d.head_dim;
   oa.M = R; oa.N = d.d_model; oa.K = d.n_q_heads * d.head_dim;
-  oa.C = at<void>(ws, w.resid); oa.ldc = d.d_model;
+  oa.C = at<void>(ws, w.o_parts); oa.ldc = d.d_model;
+  oa.ksplit = ksplit_for(d, R, d.d_model, oa.K);
+  oa.c_split = (int64_t)R * d.d_model;
   {
     ProfScope ps(P.c, DG_PROF_O_PROJ, P.s);
     HIPCHK(launch_dense(oa, bf, bf ? W_BF16 : W_F32, P.s));
   }
+  HIPCHK(launch_resid_add_rmsnorm(at<float>(ws, w.resid), at<float>(ws, w.o_parts), oa.ksplit, oa.c_split,
+                                  L.ffn_norm, at<void>(ws, w.xhat), R, d.d_model, d.norm_eps, bf, status, P.s));
   if (!do_ffn) return DG_OK;
 
-  // FFN: norm, router, top-k, grouping
-  HIPCHK(launch_rmsnorm(at<float>(ws, w.resid), L.ffn_norm, at<void>(ws, w.xhat), R, d.d_model, d.norm_eps, bf,
-                        status, P.s));
+  // FFN: router, top-k, grouping
+  // router logits: split-K partials, summed in order (+ bias) by the top-k kernel
   DenseArgs ra{};
   ra.epi = EPI_STORE_F32;
   ra.A = at<void>(ws, w.xhat); ra.lda = d.d_model;
   ra.B = L.w_router; ra.ldb = d.d_model;
   ra.M = R; ra.N = d.n_experts; ra.K = d.d_model;
-  ra.C = at<void>(ws, w.rlogits); ra.ldc = d.n_experts;
-  ra.bias = L.router_bias;
+  ra.C = at<void>(ws, w.rparts); ra.ldc = d.n_experts;
+  ra.ksplit = router_splits(d, R);
+  ra.c_split = (int64_t)R * d.n_experts;
   ProfScope route_scope(P.c, DG_PROF_ROUTING, P.s);
   HIPCHK(launch_dense(ra, bf, bf ? W_BF16 : W_F32, P.s));
-  HIPCHK(launch_router_topk(at<float>(ws, w.rlogits), R, d.n_experts, d.top_k, at<int32_t>(ws, w.idx),
-                            at<float>(ws, w.gates), P.s));
+  HIPCHK(launch_router_topk(at<float>(ws, w.rparts), ra.ksplit, ra.c_split, L.router_bias, R, d.n_experts, d.top_k,
+                            at<float>(ws, w.rlogits), at<int32_t>(ws, w.idx), at<float>(ws, w.gates), P.s));
   HIPCHK(launch_route_tables(at<int32_t>(ws, w.idx), R, d.n_experts, d.top_k, at<int32_t>(ws, w.counts),
                              at<int32_t>(ws, w.offsets), at<int32_t>(ws, w.perm), at<int32_t>(ws, w.inv_perm),
                              at<int32_t>(ws, w.tok), at<int32_t>(ws, w.work), at<int32_t>(ws, w.n_items),
@@ -370,11 +407,14 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn) {
   sd.B = L.sh_down; sd.ldb = d.shared_hidden;
   sd.sB = (const uint16_t*)L.sh_s_down;
   sd.M = R; sd.N = d.d_model; sd.K = d.shared_hidden;
-  sd.C = at<void>(ws, w.sh_out); sd.ldc = d.d_model;
+  sd.C = at<void>(ws, w.sh_parts); sd.ldc = d.d_model;
+  sd.ksplit = ksplit_for(d, R, d.d_model, sd.K);
+  sd.c_split = (int64_t)R * d.d_model;
   HIPCHK(launch_dense(sd, bf, wk, P.s));
   shared_scope.close();
-  HIPCHK(launch_moe_combine(at<float>(ws, w.resid), at<float>(ws, w.y), at<float>(ws, w.sh_out),
-                            at<float>(ws, w.gates), at<int32_t>(ws, w.inv_perm), R, d.d_model, d.top_k, P.s));
+  HIPCHK(launch_moe_combine(at<float>(ws, w.resid), at<float>(ws, w.y), at<float>(ws, w.sh_parts), sd.ksplit,
+                            sd.c_split, at<float>(ws, w.gates), at<int32_t>(ws, w.inv_perm), R, d.d_model, d.top_k,
+                            P.s));
   return DG_OK;
 }
 
@@ -387,6 +427,7 @@ dg_status check_desc(const dg_model_desc& d) {
   if (d.n_q_heads % d.n_kv_heads) return fail(DG_EUNSUPPORTED, "n_q_heads %% n_kv_heads != 0");
   if (d.d_model % 64 || d.expert_hidden % 64 || d.shared_hidden % 64)
     return fail(DG_EUNSUPPORTED, "d_model, expert_hidden and shared_hidden must be multiples of 64");
+  if (d.d_model > 4096) return fail(DG_EUNSUPPORTED, "d_model %d > 4096", d.d_model);
   if (d.vocab % 16) return fail(DG_EUNSUPPORTED, "vocab %% 16 != 0");
   if (d.n_experts > 256 || d.top_k > 16 || d.top_k > d.n_experts)
     return fail(DG_EUNSUPPORTED, "need top_k <= 16 and top_k <= n_experts <= 256");
@@ -698,7 +739,7 @@ dg_status dg_test_router_topk(const float* scores, int32_t T, int32_t E, int32_t
   int32_t* tok = (int32_t*)take(A * 4);
   int32_t* work = (int32_t*)take((size_t)max_items * 8);
   int32_t* nit = (int32_t*)take(4);
-  HIPCHK(launch_router_topk(scores, T, E, k, i_idx, i_g, stream));
+  HIPCHK(launch_router_topk(scores, 1, 0, nullptr, T, E, k, nullptr, i_idx, i_g, stream));
   HIPCHK(launch_route_tables(i_idx, T, E, k, i_c, i_o, i_p, inv, tok, work, nit, GROUP_BM, stream));
   return DG_OK;
 }

@@ -73,8 +73,9 @@ def test_step_from_logits_selection_parity(B, L, V, tau, t, h, theta):
     assert np.array_equal(nl.cpu().numpy(), olk.sum(axis=1))
     assert np.allclose(st["c"], ost["c"], rtol=1e-5, atol=1e-7)
     assert np.allclose(st["m"], ost["m"], atol=1e-5)
-    # exact ties in the max resolve to the lower id
+    # exact ties in the max resolve to the lower id (rows without a planted 40.0 above the tie)
     ties = np.arange(2, B * L, 11)
+    ties = ties[ties % 5 != 0]
     assert np.all(st["a"][ties] == 3)
 
 
