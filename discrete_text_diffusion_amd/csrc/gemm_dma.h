@@ -1,0 +1,151 @@
+// MFMA tile engine with direct global -> LDS loads (gfx950 global_load_lds_dwordx4).
+//
+// C[BM x BN] += A[BM x K] . B[BN x K]^T, both operands K-contiguous, bf16 or fp32.  Each K tile
+// is 128 bytes of every operand row.  One load instruction moves 16 bytes per lane straight
+// into LDS at (wave-uniform base + 16 * lane), so a wave fills 8 consecutive 128-byte rows per
+// instruction; no registers hold tiles in flight, which lets NS - 1 tiles stream from memory
+// while one is multiplied (an NS-stage LDS ring, one barrier per tile).
+//
+// Bank-conflict-free fragment reads without padding: the 16-byte chunk c of row r lives in slot
+// c ^ ((r >> 1) & 7) of that row.  A fragment read touches 16 consecutive rows at one logical
+// chunk; rows of one parity share a half of the 64 banks and the swizzle gives the 8 rows of
+// each parity 8 different slots, so the 16 lanes hit 64 distinct banks.
+//
+// Rows outside the operand are loaded from a clamped (valid) row: their products land only in
+// output rows/columns that the caller never stores.
+#pragma once
+#include "common.h"
+
+namespace dg {
+
+#define DG_LDS_AS __attribute__((address_space(3)))
+#define DG_GLOBAL_AS __attribute__((address_space(1)))
+
+DG_DEV void dma16(const void* gsrc, char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const DG_GLOBAL_AS void*)gsrc, (DG_LDS_AS void*)lds_wave_base, 16, 0, 0);
+}
+
+// wait until at most n of this wave's vector-memory loads are outstanding (n <= 63)
+template <int N>
+DG_DEV void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] in [15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <class T, int BM, int BN, int WM, int WN, int NS>
+struct GemmDma {
+  static_assert(WM * WN == 4, "4 waves");
+  static_assert(BM % 32 == 0 && BN % 32 == 0, "rows per tile: multiples of 32 (4 waves x 8 rows)");
+  static_assert(NS >= 2 && NS <= 8, "stages");
+  static constexpr int FM = BM / WM / 16;
+  static constexpr int FN = BN / WN / 16;
+  static constexpr int KT = 128 / sizeof(T);          // K elements per tile
+  static constexpr int IA = BM / 32, IB = BN / 32;     // load instructions per wave per tile
+  static constexpr int LPT = IA + IB;
+  static constexpr int STAGE = (BM + BN) * 128;
+  static constexpr int LDS_BYTES = NS * STAGE;
+  static_assert((NS - 2) * LPT < 64, "vmcnt range");
+
+  const char* a_src[IA];   // this lane's source row (+ its swizzled chunk) for each instruction
+  const char* b_src[IB];
+
+  // arow(r)/brow(r): pointer to element 0 of tile row r, or nullptr for rows past the operand,
+  // for which row 0 of the tile (always valid) is loaded instead.
+  template <class ARow, class BRow>
+  DG_DEV void setup(ARow arow, BRow brow) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rr = lane >> 3, slot = lane & 7;
+#pragma unroll
+    for (int i = 0; i < IA; ++i) {
+      const int r = (wave + 4 * i) * 8 + rr;
+      const char* p = reinterpret_cast<const char*>(arow(r));
+      if (!p) p = reinterpret_cast<const char*>(arow(0));
+      a_src[i] = p + ((slot ^ ((r >> 1) & 7)) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < IB; ++i) {
+      const int r = (wave + 4 * i) * 8 + rr;
+      const char* p = reinterpret_cast<const char*>(brow(r));
+      if (!p) p = reinterpret_cast<const char*>(brow(0));
+      b_src[i] = p + ((slot ^ ((r >> 1) & 7)) * 16);
+    }
+  }
+
+  DG_DEV void issue(char* lds, int kt, int stage) {
+    const int wave = threadIdx.x >> 6;
+    char* st = lds + stage * STAGE;
+    const size_t off = (size_t)kt * 128;
+#pragma unroll
+    for (int i = 0; i < IA; ++i) dma16(a_src[i] + off, st + (wave + 4 * i) * 8 * 128);
+#pragma unroll
+    for (int i = 0; i < IB; ++i) dma16(b_src[i] + off, st + BM * 128 + (wave + 4 * i) * 8 * 128);
+  }
+
+  // wait for the oldest of `pending` outstanding tiles (pending = tiles issued and not yet
+  // waited for): at most (pending - 1) tiles' loads may stay in flight
+  template <int P>
+  DG_DEV static void wait_pending(int pending) {
+    if constexpr (P > 1) {
+      if (pending >= P) { wait_vm<(P - 1) * LPT>(); return; }
+      wait_pending<P - 1>(pending);
+    } else {
+      wait_vm<0>();
+    }
+  }
+  DG_DEV static void wait_oldest(int pending) { wait_pending<NS - 1>(pending); }
+
+  DG_DEV static void compute(const char* st, f32x4_v (&acc)[FM][FN]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int swz = (lane & 15) >> 1, kg = lane >> 4;
+    const char* la = st + (wm * FM * 16 + (lane & 15)) * 128;
+    const char* lb = st + BM * 128 + (wn * FN * 16 + (lane & 15)) * 128;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int so = (((4 * c + kg) ^ swz)) * 16;
+      u32x4 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const u32x4*>(la + i * 16 * 128 + so);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const u32x4*>(lb + j * 16 * 128 + so);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) Mfma<T>::mma(acc[i][j], af[i], bfr[j]);
+    }
+  }
+
+  // Full K loop over nk = K / KT tiles.  The stage computed at step kt - 1 is refilled at step kt
+  // only after the barrier that follows every wave's wait for tile kt.
+  DG_DEV void run(char* lds, int K, f32x4_v (&acc)[FM][FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+    const int nk = K / KT;
+    int issued = 0;
+    for (; issued < NS - 1 && issued < nk; ++issued) issue(lds, issued, issued);
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_oldest(issued - kt);
+      __syncthreads();
+      if (issued < nk) {
+        issue(lds, issued, issued % NS);
+        ++issued;
+      }
+      compute(lds + (kt % NS) * STAGE, acc);
+    }
+    __syncthreads();   // the LDS ring may be reused by the caller after this
+  }
+
+  DG_DEV static int row_of(int i, int e) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    return (wave / WN) * FM * 16 + i * 16 + 4 * (lane >> 4) + e;
+  }
+  DG_DEV static int col_of(int j) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    return (wave % WN) * FN * 16 + j * 16 + (lane & 15);
+  }
+};
+
+}  // namespace dg

@@ -259,7 +259,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs p) {
   }
 }
 
-// merge split partials in split order: o = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M)
+// merge split partials in split order: o = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M); every
+// partial of a thread is loaded before the sums (clamped split index, always valid)
+constexpr int MERGE_MAX = 16;
 template <class T>
 __global__ void attn_merge_kernel(AttnArgs p) {
   const int64_t rows = (int64_t)p.B * p.n * p.Hq;
@@ -268,21 +270,33 @@ __global__ void attn_merge_kernel(AttnArgs p) {
   if (idx >= rows * dq) return;
   const int64_t rh = idx / dq;
   const int d4 = (int)(idx - rh * dq) * 4;
+  const int S = p.splits;
+  float mv[MERGE_MAX], lv[MERGE_MAX];
+  f32x4_v ov[MERGE_MAX];
+#pragma unroll
+  for (int s = 0; s < MERGE_MAX; ++s) {
+    const int64_t sr = (int64_t)min(s, S - 1) * rows + rh;
+    mv[s] = p.part_ml[sr * 2];
+    lv[s] = p.part_ml[sr * 2 + 1];
+    ov[s] = *reinterpret_cast<const f32x4_v*>(p.part_o + sr * p.dh + d4);
+  }
   float M = -INFINITY;
-  for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.part_ml[((int64_t)s * rows + rh) * 2]);
-  float L = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-  for (int s = 0; s < p.splits; ++s) {
-    const float m = p.part_ml[((int64_t)s * rows + rh) * 2];
-    if (m == -INFINITY) continue;
-    const float w = exp2f(m - M);
-    L += p.part_ml[((int64_t)s * rows + rh) * 2 + 1] * w;
-    const f32x4_v v = *reinterpret_cast<const f32x4_v*>(p.part_o + ((int64_t)s * rows + rh) * p.dh + d4);
-    o0 += v[0] * w; o1 += v[1] * w; o2 += v[2] * w; o3 += v[3] * w;
+#pragma unroll
+  for (int s = 0; s < MERGE_MAX; ++s)
+    if (s < S) M = fmaxf(M, mv[s]);
+  float L = 0.f;
+  f32x4_v o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < MERGE_MAX; ++s) {
+    if (s >= S || mv[s] == -INFINITY) continue;
+    const float w = exp2f(mv[s] - M);
+    L += lv[s] * w;
+    o += ov[s] * w;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   T* out = static_cast<T*>(p.out) + rh * p.dh + d4;
-  out[0] = Elem<T>::from_f(o0 * inv); out[1] = Elem<T>::from_f(o1 * inv);
-  out[2] = Elem<T>::from_f(o2 * inv); out[3] = Elem<T>::from_f(o3 * inv);
+  out[0] = Elem<T>::from_f(o[0] * inv); out[1] = Elem<T>::from_f(o[1] * inv);
+  out[2] = Elem<T>::from_f(o[2] * inv); out[3] = Elem<T>::from_f(o[3] * inv);
 }
 
 template <class T, int DH>

@@ -5,10 +5,26 @@
 //   shared- and routed-expert SwiGLU (gate and up in one tile) and down projections.
 // W8A16: fp8 e4m3 weights are widened to bf16 in the tile loader; the per-output-row scale is
 // applied to the fp32 accumulator in the epilogue.
+#include <type_traits>
+
 #include "gemm_core.h"
+#include "gemm_dma.h"
 #include "internal.h"
 
 namespace dg {
+
+// bf16/fp32 weights stream through the direct-to-LDS engine; fp8 weights take the
+// register-staged engine, which widens them to bf16 on the way into LDS.  `DEEP` rings fill
+// ~144 KB of LDS (one block per CU, as many tiles in flight as fit: the dense projections run
+// about one block per CU); the others use 3-4 stages so two blocks share a CU.
+constexpr int ring_stages(int stage_bytes, bool deep) {
+  if (!deep) return stage_bytes <= 20480 ? 4 : 3;
+  const int n = 147456 / stage_bytes;
+  return n > 8 ? 8 : (n < 3 ? 3 : n);
+}
+template <class TA, class TB, int BM, int BN, int WM, int WN, bool DEEP = false>
+using TileFor = std::conditional_t<sizeof(TB) == 1, GemmTile<TA, TB, BM, BN, WM, WN, 2>,
+                                   GemmDma<TA, BM, BN, WM, WN, ring_stages((BM + BN) * 128, DEEP)>>;
 
 // ---------------------------------------------------------------- B-row maps ----------------
 // A tile column block of 16 columns; "paired" maps put the two members of a pair (gate/up, or
@@ -28,7 +44,7 @@ DG_DEV void paired_col(int r, int& u, int& half, int& c) {
 // blockIdx.y is the split-K part.
 template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI, int MAP>
 __global__ __launch_bounds__(256) void gemm_dense_kernel(DenseArgs p) {
-  using G = GemmTile<TA, TB, BM, BN, WM, WN, 2>;
+  using G = TileFor<TA, TB, BM, BN, WM, WN, true>;
   extern __shared__ __align__(16) char lds[];
   const int id = blockIdx.x, xcd = id & 7, local = id >> 3;
   const int mt = local % p.n_mt;
@@ -156,7 +172,7 @@ __global__ __launch_bounds__(256) void gemm_dense_kernel(DenseArgs p) {
 // [offsets[e], offsets[e] + counts[e]) in grouped order.
 template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(256) void gemm_grouped_kernel(GroupedArgs p) {
-  using G = GemmTile<TA, TB, BM, BN, WM, WN, 2>;
+  using G = TileFor<TA, TB, BM, BN, WM, WN>;
   extern __shared__ __align__(16) char lds[];
   const int item = blockIdx.y;
   if (item >= *p.n_items) return;
@@ -233,7 +249,7 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GroupedArgs p) {
 // ---------------------------------------------------------------- launchers --------------------
 template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI, int MAP>
 static hipError_t launch_dense_t(DenseArgs a, int n_eff, hipStream_t s) {
-  using G = GemmTile<TA, TB, BM, BN, WM, WN, 2>;
+  using G = TileFor<TA, TB, BM, BN, WM, WN, true>;
   a.n_mt = (a.M + BM - 1) / BM;
   a.n_nt = (n_eff + BN - 1) / BN;
   if (a.ksplit < 1) a.ksplit = 1;
@@ -292,7 +308,7 @@ hipError_t launch_dense(const DenseArgs& a, int act_bf16, int w_kind, hipStream_
 
 template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI>
 static hipError_t launch_grouped_t(const GroupedArgs& a, int n_eff, int max_items, hipStream_t s) {
-  using G = GemmTile<TA, TB, BM, BN, WM, WN, 2>;
+  using G = TileFor<TA, TB, BM, BN, WM, WN>;
   dim3 grid((n_eff + BN - 1) / BN, max_items);
   static const hipError_t attr = allow_lds(gemm_grouped_kernel<TA, TB, BM, BN, WM, WN, EPI>, G::LDS_BYTES);
   if (attr != hipSuccess) return attr;

@@ -41,35 +41,19 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
-// y = x / sqrt(mean(x^2) + eps) * g, one block per row; flags a non-finite row in *status
-template <class T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, const T* g, T* y, int d, float eps,
-                                                      int* status) {
-  const int r = blockIdx.x;
-  const float* xr = x + (int64_t)r * d;
-  float ss = 0.f;
-  for (int c = threadIdx.x; c < d; c += 256) { const float v = xr[c]; ss += v * v; }
-  ss = wave_sum(ss);
-  __shared__ float part[4];
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float tot = part[0] + part[1] + part[2] + part[3];
-  const float inv = rsqrtf(tot / (float)d + eps);
-  if (threadIdx.x == 0 && status && !isfinite(tot)) atomicOr(status, 2);
-  for (int c = threadIdx.x; c < d; c += 256)
-    y[(int64_t)r * d + c] = Elem<T>::from_f(xr[c] * inv * Elem<T>::to_f(g[c]));
-}
+// forward declaration: plain RMSNorm is the fused kernel with no partials to add
+hipError_t launch_resid_add_rmsnorm(float* resid, const float* parts, int nparts, int64_t pstride, const void* g,
+                                    void* y, int rows, int d, float eps, int bf, int* status, hipStream_t s);
 
 hipError_t launch_rmsnorm(const float* x, const void* g, void* y, int rows, int d, float eps, int bf,
                           int* status, hipStream_t s) {
-  if (bf) hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(rows), dim3(256), 0, s, x, (const bf16_t*)g, (bf16_t*)y, d, eps, status);
-  else hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(rows), dim3(256), 0, s, x, (const float*)g, (float*)y, d, eps, status);
-  return hipGetLastError();
+  return launch_resid_add_rmsnorm(const_cast<float*>(x), nullptr, 0, 0, g, y, rows, d, eps, bf, status, s);
 }
 
 // resid += sum_s parts[s] (split-K partials, in part order); y = RMSNorm(resid) * g.  One block per
 // row; the updated row stays in registers between the two passes (d <= 256 * RN_MAX).
 constexpr int RN_MAX = 16;
+constexpr int MAX_PARTS_ADD = 8;
 template <class T>
 __global__ __launch_bounds__(256) void resid_add_rmsnorm_kernel(float* resid, const float* parts, int nparts,
                                                                 int64_t pstride, const T* g, T* y, int d, float eps,
@@ -83,9 +67,15 @@ __global__ __launch_bounds__(256) void resid_add_rmsnorm_kernel(float* resid, co
     const int c = threadIdx.x + 256 * j;
     v[j] = 0.f;
     if (c < d) {
+      // every partial load issues before the in-order sum (clamped part index, always valid)
+      float pv[MAX_PARTS_ADD];
+#pragma unroll
+      for (int q = 0; q < MAX_PARTS_ADD; ++q) pv[q] = parts ? parts[min(q, max(nparts - 1, 0)) * pstride + (int64_t)r * d + c] : 0.f;
       float a = xr[c];
-      for (int q = 0; q < nparts; ++q) a += parts[q * pstride + (int64_t)r * d + c];
-      xr[c] = a;
+#pragma unroll
+      for (int q = 0; q < MAX_PARTS_ADD; ++q)
+        if (q < nparts) a += pv[q];
+      if (nparts > 0) xr[c] = a;
       v[j] = a;
       ss += a * a;
     }
@@ -106,7 +96,7 @@ __global__ __launch_bounds__(256) void resid_add_rmsnorm_kernel(float* resid, co
 
 hipError_t launch_resid_add_rmsnorm(float* resid, const float* parts, int nparts, int64_t pstride, const void* g,
                                     void* y, int rows, int d, float eps, int bf, int* status, hipStream_t s) {
-  if (d > 256 * RN_MAX) return hipErrorInvalidValue;
+  if (d > 256 * RN_MAX || nparts < 0 || nparts > MAX_PARTS_ADD) return hipErrorInvalidValue;
   if (bf)
     hipLaunchKernelGGL(resid_add_rmsnorm_kernel<bf16_t>, dim3(rows), dim3(256), 0, s, resid, parts, nparts, pstride,
                        (const bf16_t*)g, (bf16_t*)y, d, eps, status);
@@ -157,31 +147,49 @@ hipError_t launch_kv_append(const void* kn, const void* vn, void* kc, void* vc, 
 }
 
 // resid[t] += sum_{s<k} gate[t][s] * y[inv_perm[t*k+s]] + shared[t], slots in order; the shared
-// expert output arrives as `nsp` split-K partials summed in part order
+// expert output arrives as `nsp` split-K partials summed in part order.  All loads of a thread
+// issue before the sums (compile-time slot count K >= k, clamped indices).
+template <int K>
 __global__ void moe_combine_kernel(float* resid, const float* y, const float* shared, int nsp, int64_t sp_stride,
                                    const float* gates, const int32_t* inv_perm, int rows, int d, int k) {
   const int t = blockIdx.y;
   const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (c >= d) return;
-  f32x4_v acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < k; ++s) {
-    const float gt = gates[(int64_t)t * k + s];
+  f32x4_v yv[K], sv[MAX_PARTS_ADD];
+  float g[K];
+#pragma unroll
+  for (int s = 0; s < K; ++s) {
+    const int sc = min(s, k - 1);
     // grouped positions are a permutation of [0, rows*k); the clamp only guards the read
-    const int pos = min(max(inv_perm[(int64_t)t * k + s], 0), rows * k - 1);
-    const f32x4_v v = *reinterpret_cast<const f32x4_v*>(y + (int64_t)pos * d + c);
-    acc += gt * v;
+    const int pos = min(max(inv_perm[(int64_t)t * k + sc], 0), rows * k - 1);
+    g[s] = s < k ? gates[(int64_t)t * k + sc] : 0.f;
+    yv[s] = *reinterpret_cast<const f32x4_v*>(y + (int64_t)pos * d + c);
   }
+#pragma unroll
+  for (int q = 0; q < MAX_PARTS_ADD; ++q)
+    sv[q] = *reinterpret_cast<const f32x4_v*>(shared + min(q, nsp - 1) * sp_stride + (int64_t)t * d + c);
+  f32x4_v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < K; ++s)
+    if (s < k) acc += g[s] * yv[s];
+  f32x4_v sh = sv[0];
+#pragma unroll
+  for (int q = 1; q < MAX_PARTS_ADD; ++q)
+    if (q < nsp) sh += sv[q];
   f32x4_v* r = reinterpret_cast<f32x4_v*>(resid + (int64_t)t * d + c);
-  f32x4_v sh = *reinterpret_cast<const f32x4_v*>(shared + (int64_t)t * d + c);
-  for (int q = 1; q < nsp; ++q) sh += *reinterpret_cast<const f32x4_v*>(shared + q * sp_stride + (int64_t)t * d + c);
   *r = *r + (acc + sh);
 }
 
 hipError_t launch_moe_combine(float* resid, const float* y, const float* shared, int nsp, int64_t sp_stride,
                               const float* gates, const int32_t* inv_perm, int rows, int d, int k, hipStream_t s) {
+  if (nsp < 1 || nsp > MAX_PARTS_ADD) return hipErrorInvalidValue;
   dim3 grid((d / 4 + 255) / 256, rows);
-  hipLaunchKernelGGL(moe_combine_kernel, grid, dim3(256), 0, s, resid, y, shared, nsp, sp_stride, gates, inv_perm,
-                     rows, d, k);
+  if (k <= 2)
+    hipLaunchKernelGGL(moe_combine_kernel<2>, grid, dim3(256), 0, s, resid, y, shared, nsp, sp_stride, gates, inv_perm, rows, d, k);
+  else if (k <= 8)
+    hipLaunchKernelGGL(moe_combine_kernel<8>, grid, dim3(256), 0, s, resid, y, shared, nsp, sp_stride, gates, inv_perm, rows, d, k);
+  else
+    hipLaunchKernelGGL(moe_combine_kernel<16>, grid, dim3(256), 0, s, resid, y, shared, nsp, sp_stride, gates, inv_perm, rows, d, k);
   return hipGetLastError();
 }
 

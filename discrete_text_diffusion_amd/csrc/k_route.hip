@@ -7,6 +7,8 @@
 
 namespace dg {
 
+constexpr int MAX_PARTS = 16;   // split-K parts of the router GEMM
+
 // One wave per row; E <= 256 (4 values per lane), k <= 16.  The router logits arrive as
 // `nparts` split-K partial sums, added in part order (deterministic), plus the optional bias.
 template <int K>
@@ -20,14 +22,18 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* parts, in
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + 64 * j;
-    float acc = -INFINITY;
-    if (e < E) {
-      acc = parts[(int64_t)t * E + e];
-      for (int p = 1; p < nparts; ++p) acc += parts[p * part_stride + (int64_t)t * E + e];
-      if (bias) acc += bias[e];
-      if (logits_out) logits_out[(int64_t)t * E + e] = acc;
-    }
-    v[j] = acc;
+    // all partial loads issue back to back (clamped index, always valid); summed in part order
+    const int ec = min(e, E - 1);
+    float pv[MAX_PARTS];
+#pragma unroll
+    for (int p = 0; p < MAX_PARTS; ++p) pv[p] = parts[min(p, nparts - 1) * part_stride + (int64_t)t * E + ec];
+    float acc = pv[0];
+#pragma unroll
+    for (int p = 1; p < MAX_PARTS; ++p)
+      if (p < nparts) acc += pv[p];
+    if (bias) acc += bias[ec];
+    if (e < E && logits_out) logits_out[(int64_t)t * E + e] = acc;
+    v[j] = e < E ? acc : -INFINITY;
   }
   // NaN scores count as -inf; an explicit taken mask keeps the k picks distinct even when fewer
   // than k scores are finite (untaken entries always beat taken ones)
@@ -92,18 +98,24 @@ hipError_t launch_router_topk(const float* parts, int nparts, int64_t part_strid
 // The experts of one row are distinct, so for expert e the flag "row t chose e" is 0/1 and the
 // grouped position of (t, s) is offsets[e] + (number of earlier rows that chose e).
 
+template <int K>
 DG_DEV int chosen_slot(const int32_t* idx, int t, int k, int e) {
+  int v[K];
+#pragma unroll
+  for (int s = 0; s < K; ++s) v[s] = idx[(int64_t)t * k + min(s, k - 1)];
   int slot = -1;
-  for (int s = 0; s < k; ++s)
-    if (idx[(int64_t)t * k + s] == e) slot = s;
+#pragma unroll
+  for (int s = 0; s < K; ++s)
+    if (s < k && v[s] == e) slot = s;
   return slot;
 }
 
 // block e: counts[e]
+template <int K>
 __global__ __launch_bounds__(256) void route_count_kernel(const int32_t* idx, int T, int k, int32_t* counts) {
   const int e = blockIdx.x;
   int c = 0;
-  for (int t = threadIdx.x; t < T; t += 256) c += chosen_slot(idx, t, k, e) >= 0;
+  for (int t = threadIdx.x; t < T; t += 256) c += chosen_slot<K>(idx, t, k, e) >= 0;
   for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
   __shared__ int part[4];
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = c;
@@ -141,6 +153,7 @@ __global__ __launch_bounds__(256) void route_scan_kernel(const int32_t* counts, 
 }
 
 // block e: positions of expert e's rows in ascending row order
+template <int K>
 __global__ __launch_bounds__(256) void route_scatter_kernel(const int32_t* idx, int T, int k, const int32_t* offsets,
                                                             int32_t* perm, int32_t* inv_perm, int32_t* tok) {
   const int e = blockIdx.x;
@@ -149,7 +162,7 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(const int32_t* idx, 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int t0 = 0; t0 < T; t0 += 256) {
     const int t = t0 + threadIdx.x;
-    const int slot = t < T ? chosen_slot(idx, t, k, e) : -1;
+    const int slot = t < T ? chosen_slot<K>(idx, t, k, e) : -1;
     const uint64_t m = __ballot(slot >= 0);
     const int rank_in_wave = __popcll(m & ((1ull << lane) - 1ull));
     if (lane == 0) wsum[wave] = __popcll(m);
@@ -172,9 +185,21 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(const int32_t* idx, 
 hipError_t launch_route_tables(const int32_t* idx, int T, int E, int k, int32_t* counts, int32_t* offsets,
                                int32_t* perm, int32_t* inv_perm, int32_t* tok, int32_t* work, int32_t* n_items,
                                int bm, hipStream_t s) {
-  hipLaunchKernelGGL(route_count_kernel, dim3(E), dim3(256), 0, s, idx, T, k, counts);
+  if (k <= 2) {
+    hipLaunchKernelGGL(route_count_kernel<2>, dim3(E), dim3(256), 0, s, idx, T, k, counts);
+  } else if (k <= 8) {
+    hipLaunchKernelGGL(route_count_kernel<8>, dim3(E), dim3(256), 0, s, idx, T, k, counts);
+  } else {
+    hipLaunchKernelGGL(route_count_kernel<16>, dim3(E), dim3(256), 0, s, idx, T, k, counts);
+  }
   hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(256), 0, s, counts, E, bm, offsets, work, n_items);
-  hipLaunchKernelGGL(route_scatter_kernel, dim3(E), dim3(256), 0, s, idx, T, k, offsets, perm, inv_perm, tok);
+  if (k <= 2) {
+    hipLaunchKernelGGL(route_scatter_kernel<2>, dim3(E), dim3(256), 0, s, idx, T, k, offsets, perm, inv_perm, tok);
+  } else if (k <= 8) {
+    hipLaunchKernelGGL(route_scatter_kernel<8>, dim3(E), dim3(256), 0, s, idx, T, k, offsets, perm, inv_perm, tok);
+  } else {
+    hipLaunchKernelGGL(route_scatter_kernel<16>, dim3(E), dim3(256), 0, s, idx, T, k, offsets, perm, inv_perm, tok);
+  }
   return hipGetLastError();
 }
 

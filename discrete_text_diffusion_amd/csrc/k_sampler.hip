@@ -10,7 +10,7 @@
 // Step kernel merges the partials of every slice in ascending slice order (deterministic), then
 // applies the per-position update: lock-in of confident positions, else the Euler jump with
 // probability lambda to the Gumbel-max draw [TR §Backward Denoising Process; PBD glossary].
-#include "gemm_core.h"
+#include "gemm_dma.h"
 #include "internal.h"
 
 namespace dg {
@@ -52,7 +52,7 @@ DG_DEV float gumbel_key2(float z2, uint32_t w) {
 // ------------------------------------------------------------------ fused LM head partials ------
 template <class TA, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(256) void lmhead_sampler_kernel(SampArgs p, int n_mt) {
-  using G = GemmTile<TA, TA, BM, BN, WM, WN>;
+  using G = GemmDma<TA, BM, BN, WM, WN, 3>;
   extern __shared__ __align__(16) char lds[];
   // blocks of one vocabulary slice run on the same XCD (block id mod 8) so E tiles are shared
   const int id = blockIdx.x, xcd = id & 7, local = id >> 3;
@@ -177,13 +177,13 @@ hipError_t launch_lmhead_sampler(const SampArgs& a, int act_bf16, hipStream_t s)
   const int slices8 = (a.slices + 7) / 8 * 8;
   const int blocks = n_mt * slices8;
   if (act_bf16) {
-    using G = GemmTile<bf16_t, bf16_t, SBM, SBN, 2, 2>;
+    using G = GemmDma<bf16_t, SBM, SBN, 2, 2, 3>;
     size_t lds = G::LDS_BYTES > 2 * SBM * PART * 4 ? G::LDS_BYTES : 2 * SBM * PART * 4;
     static const hipError_t attr = allow_lds(lmhead_sampler_kernel<bf16_t, SBM, SBN, 2, 2>, lds);
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((lmhead_sampler_kernel<bf16_t, SBM, SBN, 2, 2>), dim3(blocks), dim3(256), lds, s, a, n_mt);
   } else {
-    using G = GemmTile<float, float, SBM, SBN, 2, 2>;
+    using G = GemmDma<float, SBM, SBN, 2, 2, 3>;
     size_t lds = G::LDS_BYTES > 2 * SBM * PART * 4 ? G::LDS_BYTES : 2 * SBM * PART * 4;
     static const hipError_t attr = allow_lds(lmhead_sampler_kernel<float, SBM, SBN, 2, 2>, lds);
     if (attr != hipSuccess) return attr;
@@ -248,9 +248,20 @@ __global__ __launch_bounds__(256) void step_merge_kernel(StepArgs p) {
   const int b = r / p.L, i = r - b * p.L;
   RowState s;
   state_init(s);
-  for (int sl = lane; sl < p.slices; sl += 64) {
-    const float* q = p.part + ((size_t)sl * rows + r) * PART;
-    state_merge(s, q[0], q[1], __float_as_int(q[2]), q[3], __float_as_int(q[4]));
+  // four slices per lane per round, loaded before they are merged in ascending order
+  for (int base = lane; base < p.slices; base += 256) {
+    float q[4][PART];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int sl = min(base + 64 * u, p.slices - 1);
+      const float* src = p.part + ((size_t)sl * rows + r) * PART;
+#pragma unroll
+      for (int f = 0; f < PART; ++f) q[u][f] = src[f];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (base + 64 * u < p.slices)
+        state_merge(s, q[u][0], q[u][1], __float_as_int(q[u][2]), q[u][3], __float_as_int(q[u][4]));
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
