@@ -96,7 +96,7 @@ def main():
     import numpy as np
     import torch
     from discrete_text_diffusion_amd import dg
-    from discrete_text_diffusion_amd.model import Model
+    from discrete_text_diffusion_amd.model import Model, values_dmajor
     from synth import configs, gen
 
     cfg = configs.get(args.workload)
@@ -105,7 +105,7 @@ def main():
     t0 = time.time()
     W = gen.make_weights(cfg, dev)
     kv = gen.make_random_kv(cfg, dev)
-    model = Model(cfg, W, kv, [cfg.prefix] * cfg.batch)
+    model = Model(cfg, W, values_dmajor(kv), [cfg.prefix] * cfg.batch)
     B, L = cfg.batch, cfg.canvas
     ws = model.workspace(B, L, cfg.prefix)
     canvas = torch.empty(B, L, dtype=torch.int32, device=dev)

@@ -25,6 +25,12 @@ DG_DEV void dma16(const void* gsrc, char* lds_wave_base) {
   __builtin_amdgcn_global_load_lds((const DG_GLOBAL_AS void*)gsrc, (DG_LDS_AS void*)lds_wave_base, 16, 0, 0);
 }
 
+// Workgroup barrier for LDS hand-offs: waits for this wave's LDS operations only.  A
+// __syncthreads() carries a release fence, for which the compiler also drains every
+// direct-to-LDS load still in flight (vmcnt(0)) and so serialises the load ring.  The memory
+// clobber keeps the compiler from moving memory operations across it.
+DG_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // wait until at most n of this wave's vector-memory loads are outstanding (n <= 63)
 template <int N>
 DG_DEV void wait_vm() {
@@ -128,7 +134,7 @@ struct GemmDma {
     for (; issued < NS - 1 && issued < nk; ++issued) issue(lds, issued, issued);
     for (int kt = 0; kt < nk; ++kt) {
       wait_oldest(issued - kt);
-      __syncthreads();
+      lds_barrier();
       if (issued < nk) {
         issue(lds, issued, issued % NS);
         ++issued;

@@ -24,8 +24,9 @@ struct DenseArgs {
   int64_t c_split;
   int n_mt, n_nt;                        // filled by the launcher
   // QKV + RoPE
-  void* q_out; void* k_out; void* v_out; // q [M][Hq][dh]; k, v [B][Hkv][rows_per_canvas][dh]
-  int Hq, Hkv, dh, rows_per_canvas;
+  void* q_out; void* k_out; void* v_out; // q [M][Hq][dh]; k [B][Hkv][rows_per_canvas][dh];
+                                         // v d-major [B][Hkv][dh][v_ld]
+  int Hq, Hkv, dh, rows_per_canvas, v_ld;
   double log2_theta;
   int32_t pos0[MAX_BATCH];               // RoPE position of row 0 of each canvas
 };
@@ -47,17 +48,19 @@ hipError_t launch_grouped(const GroupedArgs& a, int act_bf16, int w_kind, int ma
 // ---- attention -------------------------------------------------------------------------------
 struct AttnArgs {
   const void* q;          // [B*n][Hq][dh]
-  const void* kn; const void* vn;   // new/canvas keys, values [B][Hkv][n][dh]
-  const void* kc; const void* vc;   // cache [B][Hkv][cap][dh]
-  int B, n, Hq, Hkv, dh, cap;
+  const void* kn; const void* vn;   // new/canvas keys [B][Hkv][n][dh], values d-major [B][Hkv][dh][vn_ld]
+  const void* kc; const void* vc;   // cache keys [B][Hkv][cap][dh], values d-major [B][Hkv][dh][cap]
+  int B, n, Hq, Hkv, dh, cap, vn_ld;  // vn_ld: n rounded up to a multiple of 8
   int causal, window, is_global;
   float scale_log2;       // log2(e) / sqrt(dh)
-  int splits, keys_per_split;       // key-range split (multiple of 64 keys)
+  int splits, keys_per_split;       // key-range split (multiple of 64 keys; fp32 kernel)
+  int tiles_per_split;              // split of the 64-key tile list (bf16 kernel)
   float* part_o; float* part_ml;    // [splits][B*n][Hq][dh], [splits][B*n][Hq][2] (splits > 1)
   void* out;              // [B*n][Hq*dh] act (splits == 1)
   int32_t pos0[MAX_BATCH];          // prefix length per canvas
 };
 hipError_t launch_attention(const AttnArgs& a, int act_bf16, hipStream_t s);
+hipError_t launch_flash(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_merge(const AttnArgs& a, int act_bf16, hipStream_t s);
 
 // ---- elementwise / small kernels -------------------------------------------------------------
@@ -66,7 +69,7 @@ hipError_t launch_embed(const int32_t* tokens, const void* embed, float* resid, 
 hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
 hipError_t launch_rmsnorm(const float* x, const void* g, void* y, int rows, int d, float eps,
                           int act_bf16, int* status, hipStream_t s);
-hipError_t launch_kv_append(const void* kn, const void* vn, void* kc, void* vc, int B, int n,
+hipError_t launch_kv_append(const void* kn, const void* vn, int vn_ld, void* kc, void* vc, int B, int n,
                             int Hkv, int dh, int cap, int window, int is_global,
                             const int32_t* pos0, int act_bf16, hipStream_t s);
 hipError_t launch_moe_combine(float* resid, const float* y, const float* shared, int nsp,

@@ -1,6 +1,7 @@
-// Canvas attention: every query row of the canvas attends to the visible prefix cache slots and
-// to all canvas keys (bidirectional, [TR §아키텍처와 블록 자기회귀 생성]); the same kernel with
-// `causal` set serves the causal encoder (prefill), with the sliding window on local layers.
+// Canvas attention with fp32 activations (bf16 activations take flash_kernel): every query row
+// of the canvas attends to the visible prefix cache slots and to all canvas keys (bidirectional,
+// [TR §아키텍처와 블록 자기회귀 생성]); the same kernel with `causal` set serves the causal
+// encoder (prefill), with the sliding window on local layers.
 //
 // Work item = (canvas b, KV head g, 64 query rows of the G = Hq/Hkv heads sharing g, key split).
 // Each wave owns 16 query rows.  Per 64-key tile (K row-major and V transposed in LDS):
@@ -82,27 +83,28 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs p) {
   float m_run = -INFINITY, l_lane = 0.f;
 
   const char* kc = static_cast<const char*>(p.kc) + ((int64_t)(b * p.Hkv + g) * p.cap) * DH * C::ESZ;
-  const char* vc = static_cast<const char*>(p.vc) + ((int64_t)(b * p.Hkv + g) * p.cap) * DH * C::ESZ;
+  const char* vc = static_cast<const char*>(p.vc) + ((int64_t)(b * p.Hkv + g) * p.cap) * DH * C::ESZ;  // [dh][cap]
   const char* kn = static_cast<const char*>(p.kn) + ((int64_t)(b * p.Hkv + g) * p.n) * DH * C::ESZ;
-  const char* vn = static_cast<const char*>(p.vn) + ((int64_t)(b * p.Hkv + g) * p.n) * DH * C::ESZ;
+  const char* vn = static_cast<const char*>(p.vn) + ((int64_t)(b * p.Hkv + g) * p.vn_ld) * DH * C::ESZ;  // [dh][vn_ld]
   const int ring_lo = max(0, P - p.window);
 
-  // ---- staging: K rows and V rows of one 64-key tile go global -> registers (all loads issued
-  // back to back, for the next tile while the current one is computed) -> LDS.  Rows past the
-  // split's end are clamped to its last key: they are masked out of the softmax (P = 0).
+  // ---- staging: K rows and V^T rows of one 64-key tile go global -> registers (all loads
+  // issued back to back, for the next tile while the current one is computed) -> LDS.  Keys
+  // past the split's end are clamped to its last key: they are masked out of the softmax (P = 0).
   // K: chunk q -> key q / CH_ROW, 16-byte column q % CH_ROW (coalesced rows).
-  // V: task q -> keys 4*(q % 16) .. +3 and column q / 16; the four rows are transposed in
-  //    registers so each head-dim row of V^T receives 4 keys in one 8-byte (16-byte fp32) write.
-  constexpr int VTASKS = AT_KEYS / 4 * C::CH_ROW;          // (key quad, column) pairs
-  constexpr int VT = (VTASKS + 255) / 256;                   // V tasks per thread
-  u32x4 kreg[C::CHUNKS], vreg[VT][4];
+  // V: task q -> head-dim row q / 16 and keys 4 * (q % 16) .. + 3, read from the d-major value
+  //    rows (prefix slots, then canvas keys) and written to LDS as one 4-key vector.
+  constexpr int VTASKS = DH * (AT_KEYS / 4);
+  constexpr int VT = VTASKS / 256;                           // V tasks per thread
+  static_assert(VTASKS % 256 == 0, "V tasks");
+  u32x4 kreg[C::CHUNKS], vreg[VT];
   auto key_row = [&](int kk) -> const char* {
     kk = min(kk, k_end - 1);
     return kk < np ? kc + (int64_t)kk * DH * C::ESZ : kn + (int64_t)(kk - np) * DH * C::ESZ;
   };
-  auto val_row = [&](int kk) -> const char* {
+  auto val_elem = [&](int kk, int d) -> const char* {
     kk = min(kk, k_end - 1);
-    return kk < np ? vc + (int64_t)kk * DH * C::ESZ : vn + (int64_t)(kk - np) * DH * C::ESZ;
+    return kk < np ? vc + ((int64_t)d * p.cap + kk) * C::ESZ : vn + ((int64_t)d * p.vn_ld + (kk - np)) * C::ESZ;
   };
   auto load_tile = [&](int k0) {
 #pragma unroll
@@ -112,10 +114,16 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs p) {
     }
 #pragma unroll
     for (int it = 0; it < VT; ++it) {
-      const int q = min(threadIdx.x + 256 * it, VTASKS - 1);
-      const int kq = q & 15, ch = q >> 4;
+      const int q = threadIdx.x + 256 * it;
+      const int d = q >> 4, kq = q & 15;
+      uint32_t e[4];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) vreg[it][m] = *reinterpret_cast<const u32x4*>(val_row(k0 + 4 * kq + m) + ch * 16);
+      for (int m = 0; m < 4; ++m) {
+        const char* src = val_elem(k0 + 4 * kq + m, d);
+        e[m] = C::ESZ == 2 ? (uint32_t)*reinterpret_cast<const uint16_t*>(src) : *reinterpret_cast<const uint32_t*>(src);
+      }
+      if constexpr (C::ESZ == 2) vreg[it] = u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), 0, 0};
+      else vreg[it] = u32x4{e[0], e[1], e[2], e[3]};
     }
   };
   auto store_tile = [&]() {
@@ -127,23 +135,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs p) {
 #pragma unroll
     for (int it = 0; it < VT; ++it) {
       const int q = threadIdx.x + 256 * it;
-      if (q >= VTASKS) continue;
-      const int kq = q & 15, ch = q >> 4;
-      char* dst = lv + (ch * C::EPL) * C::V_STRIDE + kq * 4 * C::ESZ;
-      const u32x4* w = vreg[it];
-      if constexpr (C::ESZ == 2) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int sh = 16 * (e & 1);
-          const uint32_t b0 = (w[0][e >> 1] >> sh) & 0xffffu, b1 = (w[1][e >> 1] >> sh) & 0xffffu;
-          const uint32_t b2 = (w[2][e >> 1] >> sh) & 0xffffu, b3 = (w[3][e >> 1] >> sh) & 0xffffu;
-          *reinterpret_cast<uint2*>(dst + e * C::V_STRIDE) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          *reinterpret_cast<u32x4*>(dst + e * C::V_STRIDE) = u32x4{w[0][e], w[1][e], w[2][e], w[3][e]};
-      }
+      const int d = q >> 4, kq = q & 15;
+      char* dst = lv + d * C::V_STRIDE + kq * 4 * C::ESZ;
+      if constexpr (C::ESZ == 2) *reinterpret_cast<uint2*>(dst) = make_uint2(vreg[it].x, vreg[it].y);
+      else *reinterpret_cast<u32x4*>(dst) = vreg[it];
     }
   };
 
@@ -311,18 +306,11 @@ static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_attention(const AttnArgs& a, int act_bf16, hipStream_t s) {
-  if (act_bf16) {
-    switch (a.dh) {
-      case 64: return launch_attn_t<bf16_t, 64>(a, s);
-      case 128: return launch_attn_t<bf16_t, 128>(a, s);
-      case 256: return launch_attn_t<bf16_t, 256>(a, s);
-    }
-  } else {
-    switch (a.dh) {
-      case 64: return launch_attn_t<float, 64>(a, s);
-      case 128: return launch_attn_t<float, 128>(a, s);
-      case 256: return launch_attn_t<float, 256>(a, s);
-    }
+  if (act_bf16) return launch_flash(a, s);
+  switch (a.dh) {
+    case 64: return launch_attn_t<float, 64>(a, s);
+    case 128: return launch_attn_t<float, 128>(a, s);
+    case 256: return launch_attn_t<float, 256>(a, s);
   }
   return hipErrorInvalidValue;
 }

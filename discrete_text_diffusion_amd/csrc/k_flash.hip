@@ -1,0 +1,322 @@
+// Canvas attention in bf16 for gfx950: every canvas query attends to the visible prefix cache
+// slots and to all canvas keys (bidirectional, [TR §아키텍처와 블록 자기회귀 생성]); with `causal`
+// set it serves the causal encoder (sliding window on local layers).
+//
+// Block = 4 waves over 128 query rows of the G = Hq/Hkv heads that share KV head g; each wave
+// owns 32 rows (two 16-column MFMA blocks), so every K / V^T fragment read from LDS feeds two
+// MFMAs.  Keys stream in 64-key tiles straight from global memory into LDS (one
+// global_load_lds_dwordx4 moves 16 bytes per lane, no VGPR staging) through an NS-stage ring:
+//   K tile   [64 keys][dh]   as dh/64 sub-tiles of 128-byte rows,
+//   V^T tile [dh][64 keys]   one 128-byte row per head-dim index (the value cache is d-major),
+// both with the 16-byte chunk c of row r stored in slot c ^ ((r >> 1) & 7) (conflict-free
+// fragment reads).  Per tile:
+//   S^T = K . Q^T      (A = K from LDS, B = Q^T held in registers for the whole key loop)
+//   online softmax     lane-local per query column; the running max is raised (and O, l
+//                      rescaled) only when a tile's max exceeds it by more than 2^8, otherwise
+//                      probabilities are taken against the stale max (at most 256, exact in
+//                      fp32; the final O / l is unchanged)
+//   O^T += V^T . P^T   (A = V^T from LDS, B = P^T built in registers from the S^T accumulators)
+// The key list is the prefix slots [0, np) in 64-key tiles, then the canvas keys [0, n) in
+// 64-key tiles; a split covers a contiguous run of tiles.  Rows of a partial tile are loaded
+// from the range's last valid key (finite data) and masked out of the softmax; the value
+// columns of a partial tile are zeroed in LDS so that P = 0 never meets an unwritten slot.
+#include "common.h"
+#include "gemm_dma.h"
+#include "internal.h"
+
+namespace dg {
+
+template <int DH>
+struct FlashCfg {
+  static constexpr int KEYS = 64;
+  static constexpr int QW = 32;                    // query rows per wave
+  static constexpr int WAVES = 4;
+  static constexpr int QROWS = QW * WAVES;         // query rows per block
+  static constexpr int KSUB = DH / 64;             // 128-byte sub-rows of one key row
+  static constexpr int K_BYTES = KEYS * DH * 2;
+  static constexpr int V_BYTES = DH * KEYS * 2;
+  static constexpr int STAGE = K_BYTES + V_BYTES;
+  static constexpr int NS = STAGE * 4 <= 131072 ? 4 : (STAGE * 3 <= 131072 ? 3 : 2);
+  static constexpr int LDS = NS * STAGE;
+  static constexpr int NCH = DH / 32;              // MFMA k-steps along head_dim
+  static constexpr int DB = DH / 16;               // 16-row blocks of head_dim
+  static constexpr int K_INS = KEYS * KSUB / 8 / WAVES;   // DMA instructions per wave per tile
+  static constexpr int V_INS = DH / 8 / WAVES;
+  static constexpr int LPT = K_INS + V_INS;
+  static_assert(K_INS >= 1 && V_INS >= 1 && (NS - 2) * LPT < 64, "tile shape");
+};
+
+template <int DH>
+__global__ __launch_bounds__(256) void flash_kernel(AttnArgs p) {
+  using C = FlashCfg<DH>;
+  extern __shared__ __align__(16) char lds[];
+  const int G = p.Hq / p.Hkv;
+  const int mrows = G * p.n;
+  const int QB = (mrows + C::QROWS - 1) / C::QROWS;
+  // XCD-aware: the QB query blocks of one (canvas, KV head, split) get ids congruent mod 8
+  const int id = blockIdx.x, xcd = id & 7, local = id >> 3;
+  const int qblk = local % QB;
+  int r = (local / QB) * 8 + xcd;
+  if (r >= p.B * p.Hkv * p.splits) return;
+  const int split = r % p.splits; r /= p.splits;
+  const int g = r % p.Hkv;
+  const int b = r / p.Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kg = lane >> 4, l16 = lane & 15;
+
+  const int P = p.pos0[b];
+  const int np = p.is_global ? P : min(P, p.window);
+  const int TP = (np + C::KEYS - 1) / C::KEYS, TC = (p.n + C::KEYS - 1) / C::KEYS;
+  const int t_begin = split * p.tiles_per_split;
+  const int t_end = min(TP + TC, t_begin + p.tiles_per_split);
+  const int ring_lo = max(0, P - p.window);
+
+  // ---- query fragments: column q = l16 of block qb holds head_dim 32c + 8kg .. + 7 ----------
+  int qpos[2], qrow[2], qhead[2];
+  bool qok[2];
+  u32x4 qf[2][C::NCH];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int mq = qblk * C::QROWS + wave * C::QW + qb * 16 + l16;
+    qok[qb] = mq < mrows;
+    const int hj = qok[qb] ? mq / p.n : 0, qi = qok[qb] ? mq - hj * p.n : 0;
+    qhead[qb] = g * G + hj;
+    qrow[qb] = b * p.n + qi;
+    qpos[qb] = P + qi;
+    const char* qp = static_cast<const char*>(p.q) + ((int64_t)qrow[qb] * p.Hq + qhead[qb]) * DH * 2;
+#pragma unroll
+    for (int c = 0; c < C::NCH; ++c)
+      qf[qb][c] = qok[qb] ? *reinterpret_cast<const u32x4*>(qp + (32 * c + 8 * kg) * 2) : u32x4{0, 0, 0, 0};
+  }
+
+  const int64_t bg = (int64_t)b * p.Hkv + g;
+  const char* kpre = static_cast<const char*>(p.kc) + bg * p.cap * DH * 2;
+  const char* kcan = static_cast<const char*>(p.kn) + bg * p.n * DH * 2;
+  const char* vpre = static_cast<const char*>(p.vc) + bg * DH * p.cap * 2;   // [dh][cap]
+  const char* vcan = static_cast<const char*>(p.vn) + bg * DH * p.vn_ld * 2; // [dh][vn_ld]
+
+  // tile t -> range (prefix / canvas), first key of the tile within the range, valid keys
+  auto tile_info = [&](int t, bool& canvas, int& kt0, int& nv) {
+    canvas = t >= TP;
+    kt0 = (canvas ? t - TP : t) * C::KEYS;
+    nv = min(C::KEYS, (canvas ? p.n : np) - kt0);
+  };
+
+  auto issue = [&](int t, int stage) {
+    bool canvas; int kt0, nv;
+    tile_info(t, canvas, kt0, nv);
+    char* st = lds + stage * C::STAGE;
+    const int rr = lane >> 3, slot = lane & 7;
+    const char* kb = canvas ? kcan : kpre;
+#pragma unroll
+    for (int i = 0; i < C::K_INS; ++i) {
+      const int gi = wave + C::WAVES * i;          // sub-tile gi / 8, rows (gi % 8) * 8 + rr
+      const int sub = gi >> 3, row = (gi & 7) * 8 + rr;
+      const int key = kt0 + min(row, nv - 1);
+      const char* src = kb + (int64_t)key * DH * 2 + sub * 128 + ((slot ^ ((row >> 1) & 7)) * 16);
+      dma16(src, st + sub * 8192 + (gi & 7) * 8 * 128);
+    }
+    const char* vb = canvas ? vcan : vpre;
+    const int vstride = canvas ? p.vn_ld : p.cap;
+    const int last_chunk = ((canvas ? p.n : np) - 1) & ~7;    // first key of the range's last 8-key chunk
+#pragma unroll
+    for (int i = 0; i < C::V_INS; ++i) {
+      const int gi = wave + C::WAVES * i;
+      const int d = gi * 8 + rr;
+      const int key = min(kt0 + 8 * (slot ^ ((d >> 1) & 7)), last_chunk);
+      const char* src = vb + ((int64_t)d * vstride + key) * 2;
+      dma16(src, st + C::K_BYTES + gi * 8 * 128);
+    }
+  };
+
+  f32x4_v acc[C::DB][2];
+#pragma unroll
+  for (int i = 0; i < C::DB; ++i) {
+    acc[i][0] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+    acc[i][1] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  }
+  float m_run[2] = {-INFINITY, -INFINITY}, l_lane[2] = {0.f, 0.f};
+
+  int issued = t_begin;
+  for (; issued < t_end && issued < t_begin + C::NS - 1; ++issued) issue(issued, issued - t_begin);
+  for (int t = t_begin; t < t_end; ++t) {
+    const int pending = issued - t;
+    if constexpr (C::NS >= 4) {
+      if (pending >= 3) wait_vm<2 * C::LPT>();
+      else if (pending == 2) wait_vm<C::LPT>();
+      else wait_vm<0>();
+    } else if constexpr (C::NS == 3) {
+      if (pending >= 2) wait_vm<C::LPT>();
+      else wait_vm<0>();
+    } else {
+      wait_vm<0>();
+    }
+    lds_barrier();
+    if (issued < t_end) {
+      issue(issued, (issued - t_begin) % C::NS);
+      ++issued;
+    }
+    bool canvas; int kt0, nv;
+    tile_info(t, canvas, kt0, nv);
+    char* st = lds + ((t - t_begin) % C::NS) * C::STAGE;
+    if (nv < C::KEYS) {
+      // zero the value columns of keys nv..63 (their slots may hold anything)
+      char* vt = st + C::K_BYTES;
+      for (int idx = threadIdx.x; idx < DH * 8; idx += 256) {
+        const int d = idx >> 3, c = idx & 7;
+        if (8 * c + 8 <= nv) continue;
+        u32x4* w = reinterpret_cast<u32x4*>(vt + d * 128 + ((c ^ ((d >> 1) & 7)) * 16));
+        u32x4 v = *w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (8 * c + e < nv) continue;
+          const uint32_t mask = (e & 1) ? 0x0000ffffu : 0xffff0000u;
+          v[e >> 1] &= mask;
+        }
+        *w = v;
+      }
+      lds_barrier();
+    }
+
+    // ---- S^T = K . Q^T ------------------------------------------------------------------------
+    f32x4_v s[4][2];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      s[nb][0] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+      s[nb][1] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+    }
+    const int swz = l16 >> 1;
+#pragma unroll
+    for (int c = 0; c < C::NCH; ++c) {
+      const char* kb = st + (c >> 1) * 8192 + l16 * 128 + (((4 * (c & 1) + kg) ^ swz) * 16);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(kb + nb * 16 * 128);
+        Mfma<bf16_t>::mma(s[nb][0], kf, qf[0][c]);
+        Mfma<bf16_t>::mma(s[nb][1], kf, qf[1][c]);
+      }
+    }
+
+    // ---- mask, scale, online softmax with conditional rescale -----------------------------
+    u32x4 pb[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float mt = -INFINITY;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int kl = nb * 16 + 4 * kg + j;     // key within the tile
+          bool vis = kl < nv;
+          if (p.causal && vis) {
+            const int kk = kt0 + kl;
+            int kpos;
+            if (canvas) kpos = P + kk;
+            else kpos = p.is_global ? kk : ring_lo + ((kk - ring_lo) % p.window + p.window) % p.window;
+            vis = kpos <= qpos[qb] && (p.is_global || qpos[qb] - kpos < p.window);
+          }
+          const float v = vis ? s[nb][qb][j] * p.scale_log2 : -INFINITY;
+          s[nb][qb][j] = v;
+          mt = fmaxf(mt, v);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const bool need = mt > m_run[qb] + 8.f || (m_run[qb] == -INFINITY && mt != -INFINITY);
+      if (__any(need)) {
+        const float alpha = need ? (m_run[qb] == -INFINITY ? 0.f : exp2f(m_run[qb] - mt)) : 1.f;
+        if (need) m_run[qb] = mt;
+        l_lane[qb] *= alpha;
+#pragma unroll
+        for (int i = 0; i < C::DB; ++i) acc[i][qb] *= alpha;
+      }
+      const float mr = m_run[qb];
+      float psum = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float e = s[nb][qb][j] == -INFINITY ? 0.f : exp2f(s[nb][qb][j] - mr);
+          s[nb][qb][j] = e;
+          psum += e;
+        }
+      l_lane[qb] += psum;
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        pb[qb][c2].x = pack_bf2(s[2 * c2][qb][0], s[2 * c2][qb][1]);
+        pb[qb][c2].y = pack_bf2(s[2 * c2][qb][2], s[2 * c2][qb][3]);
+        pb[qb][c2].z = pack_bf2(s[2 * c2 + 1][qb][0], s[2 * c2 + 1][qb][1]);
+        pb[qb][c2].w = pack_bf2(s[2 * c2 + 1][qb][2], s[2 * c2 + 1][qb][3]);
+      }
+    }
+
+    // ---- O^T += V^T . P^T: the fragment of lane (d = l16, kg) holds keys 32c2 + 4kg .. +3 and
+    // 32c2 + 16 + 4kg .. +3, matching the key order of the P^T fragment built above ----------
+    const char* vt = st + C::K_BYTES + (kg & 1) * 8;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const int d = db * 16 + l16;
+      const char* vr = vt + d * 128;
+      const int sw = (d >> 1) & 7;
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(vr + (((4 * c2 + (kg >> 1)) ^ sw) * 16));
+        const uint2 hi = *reinterpret_cast<const uint2*>(vr + (((4 * c2 + 2 + (kg >> 1)) ^ sw) * 16));
+        const u32x4 va = {lo.x, lo.y, hi.x, hi.y};
+        Mfma<bf16_t>::mma(acc[db][0], va, pb[0][c2]);
+        Mfma<bf16_t>::mma(acc[db][1], va, pb[1][c2]);
+      }
+    }
+  }
+
+  // ---- finish --------------------------------------------------------------------------------
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float l = l_lane[qb] + __shfl_xor(l_lane[qb], 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (!qok[qb]) continue;
+    const int64_t row = qrow[qb];
+    if (p.splits == 1) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      bf16_t* o = static_cast<bf16_t*>(p.out) + (row * p.Hq + qhead[qb]) * DH;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        uint2 w;
+        w.x = pack_bf2(acc[db][qb][0] * inv, acc[db][qb][1] * inv);
+        w.y = pack_bf2(acc[db][qb][2] * inv, acc[db][qb][3] * inv);
+        *reinterpret_cast<uint2*>(o + db * 16 + 4 * kg) = w;
+      }
+    } else {
+      float* o = p.part_o + (((int64_t)split * p.B * p.n + row) * p.Hq + qhead[qb]) * DH;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) *reinterpret_cast<f32x4_v*>(o + db * 16 + 4 * kg) = acc[db][qb];
+      if (kg == 0) {
+        float* ml = p.part_ml + (((int64_t)split * p.B * p.n + row) * p.Hq + qhead[qb]) * 2;
+        ml[0] = m_run[qb];
+        ml[1] = l;
+      }
+    }
+  }
+}
+
+template <int DH>
+static hipError_t launch_flash_t(const AttnArgs& a, hipStream_t s) {
+  using C = FlashCfg<DH>;
+  const int QB = (a.Hq / a.Hkv * a.n + C::QROWS - 1) / C::QROWS;
+  const int groups = a.B * a.Hkv * a.splits;
+  const int blocks = QB * ((groups + 7) / 8 * 8);
+  static const hipError_t attr = allow_lds(flash_kernel<DH>, C::LDS);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((flash_kernel<DH>), dim3(blocks), dim3(256), C::LDS, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_flash(const AttnArgs& a, hipStream_t s) {
+  switch (a.dh) {
+    case 64: return launch_flash_t<64>(a, s);
+    case 128: return launch_flash_t<128>(a, s);
+    case 256: return launch_flash_t<256>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dg

@@ -14,17 +14,12 @@
 namespace dg {
 
 // bf16/fp32 weights stream through the direct-to-LDS engine; fp8 weights take the
-// register-staged engine, which widens them to bf16 on the way into LDS.  `DEEP` rings fill
-// ~144 KB of LDS (one block per CU, as many tiles in flight as fit: the dense projections run
-// about one block per CU); the others use 3-4 stages so two blocks share a CU.
-constexpr int ring_stages(int stage_bytes, bool deep) {
-  if (!deep) return stage_bytes <= 20480 ? 4 : 3;
-  const int n = 147456 / stage_bytes;
-  return n > 8 ? 8 : (n < 3 ? 3 : n);
-}
-template <class TA, class TB, int BM, int BN, int WM, int WN, bool DEEP = false>
+// register-staged engine, which widens them to bf16 on the way into LDS.  Rings of 3-4 stages
+// let two blocks share a CU (a single block per CU with a ring twice as deep was slower).
+constexpr int ring_stages(int stage_bytes) { return stage_bytes <= 20480 ? 4 : 3; }
+template <class TA, class TB, int BM, int BN, int WM, int WN>
 using TileFor = std::conditional_t<sizeof(TB) == 1, GemmTile<TA, TB, BM, BN, WM, WN, 2>,
-                                   GemmDma<TA, BM, BN, WM, WN, ring_stages((BM + BN) * 128, DEEP)>>;
+                                   GemmDma<TA, BM, BN, WM, WN, ring_stages((BM + BN) * 128)>>;
 
 // ---------------------------------------------------------------- B-row maps ----------------
 // A tile column block of 16 columns; "paired" maps put the two members of a pair (gate/up, or
@@ -44,7 +39,7 @@ DG_DEV void paired_col(int r, int& u, int& half, int& c) {
 // blockIdx.y is the split-K part.
 template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI, int MAP>
 __global__ __launch_bounds__(256) void gemm_dense_kernel(DenseArgs p) {
-  using G = TileFor<TA, TB, BM, BN, WM, WN, true>;
+  using G = TileFor<TA, TB, BM, BN, WM, WN>;
   extern __shared__ __align__(16) char lds[];
   const int id = blockIdx.x, xcd = id & 7, local = id >> 3;
   const int mt = local % p.n_mt;
@@ -152,16 +147,17 @@ __global__ __launch_bounds__(256) void gemm_dense_kernel(DenseArgs p) {
             const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
             x1 = y1; x2 = y2;
           }
-          TA* dst;
-          if (head < p.Hq) {
-            dst = static_cast<TA*>(p.q_out) + ((int64_t)m * p.Hq + head) * dh;
-          } else {
-            const int g = head < p.Hq + p.Hkv ? head - p.Hq : head - p.Hq - p.Hkv;
-            TA* base = static_cast<TA*>(head < p.Hq + p.Hkv ? p.k_out : p.v_out);
-            dst = base + (((int64_t)b * p.Hkv + g) * p.rows_per_canvas + ii) * dh;
+          if (head < p.Hq + p.Hkv) {     // q [rows][Hq][dh], canvas k [B][Hkv][n][dh]
+            TA* dst = head < p.Hq ? static_cast<TA*>(p.q_out) + ((int64_t)m * p.Hq + head) * dh
+                                  : static_cast<TA*>(p.k_out) +
+                                        (((int64_t)b * p.Hkv + head - p.Hq) * p.rows_per_canvas + ii) * dh;
+            dst[jj] = Elem<TA>::from_f(x1);
+            dst[jj + half_dh] = Elem<TA>::from_f(x2);
+          } else {                        // canvas v, d-major [B][Hkv][dh][v_ld]
+            TA* dst = static_cast<TA*>(p.v_out) + ((int64_t)b * p.Hkv + head - p.Hq - p.Hkv) * dh * p.v_ld + ii;
+            dst[(int64_t)jj * p.v_ld] = Elem<TA>::from_f(x1);
+            dst[(int64_t)(jj + half_dh) * p.v_ld] = Elem<TA>::from_f(x2);
           }
-          dst[jj] = Elem<TA>::from_f(x1);
-          dst[jj + half_dh] = Elem<TA>::from_f(x2);
         }
     }
   }
@@ -249,7 +245,7 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GroupedArgs p) {
 // ---------------------------------------------------------------- launchers --------------------
 template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI, int MAP>
 static hipError_t launch_dense_t(DenseArgs a, int n_eff, hipStream_t s) {
-  using G = TileFor<TA, TB, BM, BN, WM, WN, true>;
+  using G = TileFor<TA, TB, BM, BN, WM, WN>;
   a.n_mt = (a.M + BM - 1) / BM;
   a.n_nt = (n_eff + BN - 1) / BN;
   if (a.ksplit < 1) a.ksplit = 1;

@@ -106,42 +106,59 @@ hipError_t launch_resid_add_rmsnorm(float* resid, const float* parts, int nparts
   return hipGetLastError();
 }
 
-// new keys/values [B][Hkv][n][dh] -> cache slots: position p in slot p (global) or p % window
-// (local ring; only the last `window` of the new positions are kept)
+// new keys [B][Hkv][n][dh] -> cache rows, new values d-major [B][Hkv][dh][vn_ld] -> cache columns
+// ([B][Hkv][dh][cap]): position p in slot p (global) or p % window (local ring; only the last
+// `window` of the new positions are kept)
 struct AppendArgs {
   const char* kn; const char* vn; char* kc; char* vc;
-  int B, n, Hkv, row_bytes, cap, window, is_global;
+  int B, n, vn_ld, Hkv, esz, row_bytes, cap, window, is_global;
   int32_t pos0[MAX_BATCH];
 };
 
 __global__ void kv_append_kernel(AppendArgs a) {
+  // keys: one 16-byte chunk of a key row per thread
   const int chunks = a.row_bytes / 16;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)a.B * a.Hkv * a.n * chunks;
-  if (idx >= total) return;
-  const int ch = (int)(idx % chunks);
-  int64_t t = idx / chunks;
-  const int j = (int)(t % a.n); t /= a.n;
-  const int g = (int)(t % a.Hkv);
-  const int b = (int)(t / a.Hkv);
+  const int64_t total_k = (int64_t)a.B * a.Hkv * a.n * chunks;
+  if (idx < total_k) {
+    const int ch = (int)(idx % chunks);
+    int64_t t = idx / chunks;
+    const int j = (int)(t % a.n); t /= a.n;
+    const int g = (int)(t % a.Hkv);
+    const int b = (int)(t / a.Hkv);
+    if (!a.is_global && j < a.n - a.window) return;
+    const int pos = a.pos0[b] + j;
+    const int slot = a.is_global ? pos : pos % a.window;
+    const int64_t src = (((int64_t)b * a.Hkv + g) * a.n + j) * a.row_bytes + ch * 16;
+    const int64_t dst = (((int64_t)b * a.Hkv + g) * a.cap + slot) * a.row_bytes + ch * 16;
+    *reinterpret_cast<u32x4*>(a.kc + dst) = *reinterpret_cast<const u32x4*>(a.kn + src);
+    return;
+  }
+  // values (d-major): one element per thread, (b, g, d, j) -> column slot of row d
+  const int64_t v = idx - total_k;
+  const int dh = a.row_bytes / a.esz;
+  if (v >= (int64_t)a.B * a.Hkv * dh * a.n) return;
+  const int j = (int)(v % a.n);
+  const int64_t row = v / a.n;                      // (b * Hkv + g) * dh + d
+  const int b = (int)(row / ((int64_t)a.Hkv * dh));
   if (!a.is_global && j < a.n - a.window) return;
   const int pos = a.pos0[b] + j;
   const int slot = a.is_global ? pos : pos % a.window;
-  const int64_t src = (((int64_t)b * a.Hkv + g) * a.n + j) * a.row_bytes + ch * 16;
-  const int64_t dst = (((int64_t)b * a.Hkv + g) * a.cap + slot) * a.row_bytes + ch * 16;
-  *reinterpret_cast<u32x4*>(a.kc + dst) = *reinterpret_cast<const u32x4*>(a.kn + src);
-  *reinterpret_cast<u32x4*>(a.vc + dst) = *reinterpret_cast<const u32x4*>(a.vn + src);
+  if (a.esz == 2)
+    reinterpret_cast<uint16_t*>(a.vc)[row * a.cap + slot] = reinterpret_cast<const uint16_t*>(a.vn)[row * a.vn_ld + j];
+  else
+    reinterpret_cast<uint32_t*>(a.vc)[row * a.cap + slot] = reinterpret_cast<const uint32_t*>(a.vn)[row * a.vn_ld + j];
 }
 
-hipError_t launch_kv_append(const void* kn, const void* vn, void* kc, void* vc, int B, int n, int Hkv,
+hipError_t launch_kv_append(const void* kn, const void* vn, int vn_ld, void* kc, void* vc, int B, int n, int Hkv,
                             int dh, int cap, int window, int is_global, const int32_t* pos0, int bf,
                             hipStream_t s) {
   AppendArgs a;
   a.kn = (const char*)kn; a.vn = (const char*)vn; a.kc = (char*)kc; a.vc = (char*)vc;
-  a.B = B; a.n = n; a.Hkv = Hkv; a.row_bytes = dh * (bf ? 2 : 4); a.cap = cap; a.window = window;
+  a.B = B; a.n = n; a.vn_ld = vn_ld; a.Hkv = Hkv; a.esz = bf ? 2 : 4; a.row_bytes = dh * a.esz; a.cap = cap; a.window = window;
   a.is_global = is_global;
   for (int b = 0; b < B && b < MAX_BATCH; ++b) a.pos0[b] = pos0[b];
-  const int64_t total = (int64_t)B * Hkv * n * (a.row_bytes / 16);
+  const int64_t total = (int64_t)B * Hkv * n * (a.row_bytes / 16) + (int64_t)B * Hkv * dh * n;
   hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }

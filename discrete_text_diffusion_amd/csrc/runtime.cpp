@@ -67,6 +67,7 @@ constexpr int MAX_KSPLIT = 8;    // split-K parts of the O projection and the sh
 constexpr int SAMP_BM = 128, SAMP_BN = 128;
 
 inline size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+inline int up8(int x) { return (x + 7) / 8 * 8; }
 inline int act_bytes(const dg_model_desc& d) { return d.act_dtype == DG_BF16 ? 2 : 4; }
 inline int w_kind(const dg_model_desc& d) {
   return d.expert_dtype == DG_FP8E4M3 ? W_FP8 : d.expert_dtype == DG_BF16 ? W_BF16 : W_F32;
@@ -112,7 +113,7 @@ Layout layout(const dg_model_desc& d, int B, int n, int max_prefix) {
   w.xhat = take(R * d.d_model * ab);
   w.q = take(R * d.n_q_heads * d.head_dim * ab);
   w.kn = take(R * d.n_kv_heads * d.head_dim * ab);
-  w.vn = take(R * d.n_kv_heads * d.head_dim * ab);
+  w.vn = take((size_t)B * up8(n) * d.n_kv_heads * d.head_dim * ab);
   w.attn_o = take(R * d.n_q_heads * d.head_dim * ab);
   (void)max_prefix;
   w.part_o = take((size_t)MAX_SPLITS * R * d.n_q_heads * d.head_dim * 4);
@@ -163,6 +164,7 @@ dg_status check_kv(const dg_ctx* c, const dg_kv* kv, int extra_tokens, int* max_
   }
   for (int l = 0; l < d.n_layers; ++l) {
     if (!kv->k[l] || !kv->v[l]) return fail(DG_EINVAL, "kv layer %d: NULL cache", l);
+    if (kv->cap[l] % 8) return fail(DG_EUNSUPPORTED, "kv layer %d: cap %d not a multiple of 8", l, kv->cap[l]);
     if (is_global(d, l)) {
       if (kv->cap[l] < mp + extra_tokens)
         return fail(DG_EINVAL, "kv layer %d: cap %d < prefix %d + %d", l, kv->cap[l], mp, extra_tokens);
@@ -274,6 +276,18 @@ int attn_splits(const dg_model_desc& d, int B, int n, int nkeys) {
   return sp;
 }
 
+// bf16 attention: blocks of 128 query rows, one block per CU (LDS ring of 128 KB); key splits
+// bring the block count near 256, each split keeping at least two 64-key tiles
+int flash_splits(const dg_model_desc& d, int B, int n, int ntiles) {
+  const int qb = (d.n_q_heads / d.n_kv_heads * n + 127) / 128;
+  const int base = B * d.n_kv_heads * qb;
+  int sp = (256 + base - 1) / base;
+  if (sp > ntiles / 2) sp = ntiles / 2;
+  if (sp > MAX_SPLITS) sp = MAX_SPLITS;
+  if (sp < 1) sp = 1;
+  return sp;
+}
+
 dg_status run_layer(const Pass& P, int l, bool do_ffn) {
   const dg_model_desc& d = P.c->d;
   const dg_layer_weights& L = P.c->layers[l];
@@ -293,7 +307,7 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn) {
   qa.B = L.w_qkv; qa.ldb = d.d_model;
   qa.M = R; qa.N = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim; qa.K = d.d_model;
   qa.q_out = at<void>(ws, w.q); qa.k_out = at<void>(ws, w.kn); qa.v_out = at<void>(ws, w.vn);
-  qa.Hq = d.n_q_heads; qa.Hkv = d.n_kv_heads; qa.dh = d.head_dim; qa.rows_per_canvas = P.n;
+  qa.Hq = d.n_q_heads; qa.Hkv = d.n_kv_heads; qa.dh = d.head_dim; qa.rows_per_canvas = P.n; qa.v_ld = up8(P.n);
   qa.log2_theta = std::log2((double)d.rope_theta);
   for (int b = 0; b < P.B; ++b) qa.pos0[b] = P.kv->prefix_len[b];
   {
@@ -305,17 +319,25 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn) {
   aa.q = at<void>(ws, w.q); aa.kn = at<void>(ws, w.kn); aa.vn = at<void>(ws, w.vn);
   aa.kc = P.kv->k[l]; aa.vc = P.kv->v[l];
   aa.B = P.B; aa.n = P.n; aa.Hq = d.n_q_heads; aa.Hkv = d.n_kv_heads; aa.dh = d.head_dim; aa.cap = P.kv->cap[l];
+  aa.vn_ld = up8(P.n);
   aa.causal = P.causal; aa.window = d.window > 0 ? d.window : 1; aa.is_global = glob;
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
-  int maxkeys = 0;
+  int maxkeys = 0, maxtiles = 0;
   for (int b = 0; b < P.B; ++b) {
     aa.pos0[b] = P.kv->prefix_len[b];
     const int np = glob ? aa.pos0[b] : std::min(aa.pos0[b], d.window);
     maxkeys = std::max(maxkeys, np + P.n);
+    maxtiles = std::max(maxtiles, (np + 63) / 64 + (P.n + 63) / 64);
   }
-  aa.splits = attn_splits(d, P.B, P.n, maxkeys);
-  aa.keys_per_split = ((maxkeys + aa.splits - 1) / aa.splits + 63) / 64 * 64;
-  aa.splits = (maxkeys + aa.keys_per_split - 1) / aa.keys_per_split;
+  if (bf) {
+    aa.splits = flash_splits(d, P.B, P.n, maxtiles);
+    aa.tiles_per_split = (maxtiles + aa.splits - 1) / aa.splits;
+    aa.splits = (maxtiles + aa.tiles_per_split - 1) / aa.tiles_per_split;
+  } else {
+    aa.splits = attn_splits(d, P.B, P.n, maxkeys);
+    aa.keys_per_split = ((maxkeys + aa.splits - 1) / aa.splits + 63) / 64 * 64;
+    aa.splits = (maxkeys + aa.keys_per_split - 1) / aa.keys_per_split;
+  }
   aa.part_o = at<float>(ws, w.part_o); aa.part_ml = at<float>(ws, w.part_ml);
   aa.out = at<void>(ws, w.attn_o);
   {
@@ -324,7 +346,7 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn) {
     if (aa.splits > 1) HIPCHK(launch_attn_merge(aa, bf, P.s));
   }
   if (P.causal) {
-    HIPCHK(launch_kv_append(at<void>(ws, w.kn), at<void>(ws, w.vn), P.kv->k[l], P.kv->v[l], P.B, P.n,
+    HIPCHK(launch_kv_append(at<void>(ws, w.kn), at<void>(ws, w.vn), aa.vn_ld, P.kv->k[l], P.kv->v[l], P.B, P.n,
                             d.n_kv_heads, d.head_dim, P.kv->cap[l], d.window, glob, aa.pos0, bf, P.s));
   }
   // O projection as split-K partials; the fused kernel adds them to the residual (in part order)

@@ -28,6 +28,17 @@ def _p(t):
     return None if t is None else t.data_ptr()
 
 
+def values_dmajor(kv: list) -> list:
+    """Per layer (K, V) with V [B][Hkv][cap][dh] -> (K, V) with V d-major [B][Hkv][dh][cap],
+    the value layout that dg_kv takes."""
+    return [(k, v.transpose(-1, -2).contiguous()) for k, v in kv]
+
+
+def values_rowmajor(kv: list) -> list:
+    """Inverse of values_dmajor (views, no copy)."""
+    return [(k, v.transpose(-1, -2)) for k, v in kv]
+
+
 class Model:
     def __init__(self, cfg, weights: dict, kv: list | None = None, prefix_len=None):
         self.cfg = cfg
@@ -46,7 +57,8 @@ class Model:
             self.set_kv(kv, prefix_len)
 
     def set_kv(self, kv: list, prefix_len):
-        """kv: per layer (K, V) tensors [B][Hkv][cap][dh]; prefix_len: ints [B]."""
+        """kv: per layer (K [B][Hkv][cap][dh], V [B][Hkv][dh][cap]) tensors (see values_dmajor);
+        prefix_len: ints [B]."""
         self._kv = kv
         n = self.cfg.n_layers
         self._kp = (C.c_void_p * n)(*[k.data_ptr() for k, _ in kv])

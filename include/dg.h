@@ -97,9 +97,12 @@ typedef struct {
 } dg_weights;
 
 /* Prefix KV cache, filled by the causal encoder (dg_prefill_kv) or by the caller.
- * k[l], v[l]: device [batch][Hkv][cap[l]][dh] act, keys stored after RoPE.  Global layers
- * keep position p in slot p (cap[l] >= every prefix length).  Local layers keep a ring of
- * cap[l] == window slots, position p in slot p % window. */
+ * k[l]: device [batch][Hkv][cap[l]][dh] act, keys stored after RoPE (slot-major rows).
+ * v[l]: device [batch][Hkv][dh][cap[l]] act, values stored head-dim-major (one row of cap[l]
+ * slots per head-dim index), so value tiles stream into the attention kernel's LDS as stored.
+ * Global layers keep position p in slot p (cap[l] >= every prefix length).  Local layers keep
+ * a ring of cap[l] == window slots, position p in slot p % window.  cap[l] must be a multiple
+ * of 8 (DG_EUNSUPPORTED otherwise). */
 typedef struct {
   void *const *k;            /* host array [n_layers] of device pointers */
   void *const *v;

@@ -6,7 +6,7 @@ import numpy as np
 import torch
 
 from discrete_text_diffusion_amd import dg
-from discrete_text_diffusion_amd.model import Model
+from discrete_text_diffusion_amd.model import Model, values_dmajor
 from synth import gen
 
 
@@ -16,7 +16,8 @@ def log(*a):
 
 
 def build(cfg, kv_mode=None):
-    """Seeded weights and caches for `cfg` on cuda:0 and a library Model around them."""
+    """Seeded weights and caches for `cfg` on cuda:0 and a library Model around them; the caches
+    are returned in the library's layout (values d-major)."""
     dev = torch.device("cuda:0")
     W = gen.make_weights(cfg, dev)
     mode = kv_mode or cfg.kv_source
@@ -26,6 +27,7 @@ def build(cfg, kv_mode=None):
     else:
         kv = gen.empty_kv(cfg, dev)
         plen = [0] * cfg.batch
+    kv = values_dmajor(kv)
     return Model(cfg, W, kv, plen), W, kv
 
 

@@ -25,4 +25,10 @@ def oracle_weights(W: dict, cfg, layers=None) -> dict:
 
 
 def oracle_kv(kv) -> list:
+    """(K, V) tensors with V [B][Hkv][cap][dh] -> float64 arrays."""
     return [(np64(k), np64(v)) for k, v in kv]
+
+
+def oracle_kv_dev(kv) -> list:
+    """The library's cache layout (V d-major [B][Hkv][dh][cap]) -> float64 arrays of the oracle's."""
+    return [(np64(k), np64(v.transpose(-1, -2))) for k, v in kv]

@@ -13,7 +13,7 @@ from oracle import model as M
 from oracle import step as S
 from synth import configs, gen
 from tests.gpu_util import build, compare_step, log, read_stats, step_params, top2_gap
-from tests.helpers import np64, oracle_kv, oracle_weights
+from tests.helpers import np64, oracle_kv, oracle_kv_dev, oracle_weights
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -36,7 +36,8 @@ def test_prefill_matches_oracle():
     assert model.prefix_len == plen == [64]
     for l in range(cfg.n_layers):
         for j in range(2):
-            err = np.abs(np64(kv[l][j]) - okv[l][j]).max()
+            got = np64(kv[l][0]) if j == 0 else np64(kv[l][1].transpose(-1, -2))
+            err = np.abs(got - okv[l][j]).max()
             log(f"  layer {l} {'KV'[j]} cache max err {err:.2e}")
             assert err <= 1e-4
 
@@ -104,7 +105,7 @@ def test_adaptive_run_locks_and_stops_like_the_oracle():
     model.canvas_run(cv, lk, taken, rp, ws)
     torch.cuda.synchronize()
     OW = oracle_weights(W, cfg)
-    okv = oracle_kv(kv)
+    okv = oracle_kv_dev(kv)
     plen = [cfg.prefix] * B
     fwd = lambda c: M.denoise_forward(cfg, OW, okv, plen, canvas=c)[0]
     ocv, olk, otaken = S.canvas_run(cfg, OW, okv, plen, fwd, seed=3)

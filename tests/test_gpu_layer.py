@@ -62,7 +62,7 @@ def _layer_parity(cfg, layer, tol, resid=None):
     st = dg.dg_query_status(model.ctx, ws)
     assert st == dg.DG_OK
     lw = oracle_layer(W["layers"][layer], cfg)
-    K, V = np64(kv[layer][0]), np64(kv[layer][1])
+    K, V = np64(kv[layer][0]), np64(kv[layer][1].transpose(-1, -2))
     h0 = rin.cpu().numpy().astype(np.float64)
     rnd = rounder(cfg.act_dtype)
     # routing: the GPU's selection must be the top-k of the GPU's own fp32 scores (bit-exact given
