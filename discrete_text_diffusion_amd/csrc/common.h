@@ -17,16 +17,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16 bytes, lives 
 // ---------------------------------------------------------------- bf16 <-> f32 -------------------
 DG_DEV float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
-// round to nearest even; NaN stays NaN
-DG_DEV bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u) return (bf16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
+// round to nearest even (gfx950 v_cvt_pk_bf16_f32); NaN stays NaN
+typedef __bf16 hw_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float hw_f32x2 __attribute__((ext_vector_type(2)));
+DG_DEV bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 DG_DEV uint32_t pack_bf2(float a, float b) {
-  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((hw_f32x2){a, b}, hw_bf16x2));
 }
 
 // element access for the two activation types

@@ -61,6 +61,9 @@ struct AttnArgs {
 };
 hipError_t launch_attention(const AttnArgs& a, int act_bf16, hipStream_t s);
 hipError_t launch_flash(const AttnArgs& a, hipStream_t s);
+// bf16 attention blocks: FLASH_WAVES waves of FLASH_QPW 16-row query blocks each
+constexpr int FLASH_QPW = 1, FLASH_WAVES = 8;
+constexpr int FLASH_QROWS = 16 * FLASH_QPW * FLASH_WAVES;
 hipError_t launch_attn_merge(const AttnArgs& a, int act_bf16, hipStream_t s);
 
 // ---- elementwise / small kernels -------------------------------------------------------------

@@ -2,19 +2,21 @@
 // slots and to all canvas keys (bidirectional, [TR §아키텍처와 블록 자기회귀 생성]); with `causal`
 // set it serves the causal encoder (sliding window on local layers).
 //
-// Block = 4 waves over 128 query rows of the G = Hq/Hkv heads that share KV head g; each wave
-// owns 32 rows (two 16-column MFMA blocks), so every K / V^T fragment read from LDS feeds two
-// MFMAs.  Keys stream in 64-key tiles straight from global memory into LDS (one
-// global_load_lds_dwordx4 moves 16 bytes per lane, no VGPR staging) through an NS-stage ring:
-//   K tile   [64 keys][dh]   as dh/64 sub-tiles of 128-byte rows,
+// Block = FLASH_WAVES waves over 128 query rows of the G = Hq/Hkv heads that share KV head g;
+// each wave owns 16 rows (one MFMA column block), two waves per SIMD, so one wave's softmax
+// overlaps the other's matrix work.  Keys stream in 64-key tiles straight from global memory
+// into LDS (one global_load_lds_dwordx4 moves 16 bytes per lane, no VGPR staging) through an
+// NS-stage ring:
+//   K tile   [64 keys][dh]   as dh/64 sub-tiles of 128-byte rows, rows in the key order of
+//                            key_of_row (below),
 //   V^T tile [dh][64 keys]   one 128-byte row per head-dim index (the value cache is d-major),
 // both with the 16-byte chunk c of row r stored in slot c ^ ((r >> 1) & 7) (conflict-free
-// fragment reads).  Per tile:
+// 16-byte fragment reads).  Per tile:
 //   S^T = K . Q^T      (A = K from LDS, B = Q^T held in registers for the whole key loop)
 //   online softmax     lane-local per query column; the running max is raised (and O, l
-//                      rescaled) only when a tile's max exceeds it by more than 2^8, otherwise
-//                      probabilities are taken against the stale max (at most 256, exact in
-//                      fp32; the final O / l is unchanged)
+//                      rescaled) only when a tile's scores exceed it by more than 8 in log2 units,
+//                      otherwise probabilities are taken against the stale max (at most 256,
+//                      exact in fp32; O / l is unchanged)
 //   O^T += V^T . P^T   (A = V^T from LDS, B = P^T built in registers from the S^T accumulators)
 // The key list is the prefix slots [0, np) in 64-key tiles, then the canvas keys [0, n) in
 // 64-key tiles; a split covers a contiguous run of tiles.  Rows of a partial tile are loaded
@@ -26,11 +28,17 @@
 
 namespace dg {
 
-template <int DH>
+// Key held by LDS row p of a K tile.  S^T row p = 32c + 16h + 4g + j (lane group g, element j
+// of 16-key block 2c + h) holds key 32c + 8g + 4h + j, so the eight probabilities a lane packs for
+// k-step c are eight consecutive keys and its V^T fragment is one 16-byte read.
+DG_DEV int key_of_row(int p) { return (p & 0x23) | ((p & 0x0c) << 1) | ((p & 0x10) >> 2); }
+
+template <int DH, int QPW, int NW>
 struct FlashCfg {
   static constexpr int KEYS = 64;
-  static constexpr int QW = 32;                    // query rows per wave
-  static constexpr int WAVES = 4;
+  static constexpr int QPW_ = QPW;                 // 16-column query blocks per wave
+  static constexpr int QW = 16 * QPW;              // query rows per wave
+  static constexpr int WAVES = NW;
   static constexpr int QROWS = QW * WAVES;         // query rows per block
   static constexpr int KSUB = DH / 64;             // 128-byte sub-rows of one key row
   static constexpr int K_BYTES = KEYS * DH * 2;
@@ -46,9 +54,9 @@ struct FlashCfg {
   static_assert(K_INS >= 1 && V_INS >= 1 && (NS - 2) * LPT < 64, "tile shape");
 };
 
-template <int DH>
-__global__ __launch_bounds__(256) void flash_kernel(AttnArgs p) {
-  using C = FlashCfg<DH>;
+template <int DH, bool CAUSAL, int QPW, int NW>
+__global__ __launch_bounds__(NW * 64) void flash_kernel(AttnArgs p) {
+  using C = FlashCfg<DH, QPW, NW>;
   extern __shared__ __align__(16) char lds[];
   const int G = p.Hq / p.Hkv;
   const int mrows = G * p.n;
@@ -70,13 +78,14 @@ __global__ __launch_bounds__(256) void flash_kernel(AttnArgs p) {
   const int t_begin = split * p.tiles_per_split;
   const int t_end = min(TP + TC, t_begin + p.tiles_per_split);
   const int ring_lo = max(0, P - p.window);
+  const int ring_mod = ring_lo % p.window, ring_base = ring_lo - ring_mod;
 
   // ---- query fragments: column q = l16 of block qb holds head_dim 32c + 8kg .. + 7 ----------
-  int qpos[2], qrow[2], qhead[2];
-  bool qok[2];
-  u32x4 qf[2][C::NCH];
+  int qpos[QPW], qrow[QPW], qhead[QPW];
+  bool qok[QPW];
+  u32x4 qf[QPW][C::NCH];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QPW; ++qb) {
     const int mq = qblk * C::QROWS + wave * C::QW + qb * 16 + l16;
     qok[qb] = mq < mrows;
     const int hj = qok[qb] ? mq / p.n : 0, qi = qok[qb] ? mq - hj * p.n : 0;
@@ -112,7 +121,7 @@ __global__ __launch_bounds__(256) void flash_kernel(AttnArgs p) {
     for (int i = 0; i < C::K_INS; ++i) {
       const int gi = wave + C::WAVES * i;          // sub-tile gi / 8, rows (gi % 8) * 8 + rr
       const int sub = gi >> 3, row = (gi & 7) * 8 + rr;
-      const int key = kt0 + min(row, nv - 1);
+      const int key = kt0 + min(key_of_row(row), nv - 1);
       const char* src = kb + (int64_t)key * DH * 2 + sub * 128 + ((slot ^ ((row >> 1) & 7)) * 16);
       dma16(src, st + sub * 8192 + (gi & 7) * 8 * 128);
     }
@@ -129,13 +138,15 @@ __global__ __launch_bounds__(256) void flash_kernel(AttnArgs p) {
     }
   };
 
-  f32x4_v acc[C::DB][2];
+  f32x4_v acc[C::DB][QPW];
+  float m_run[QPW], l_lane[QPW];
 #pragma unroll
-  for (int i = 0; i < C::DB; ++i) {
-    acc[i][0] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-    acc[i][1] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  for (int qb = 0; qb < QPW; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_lane[qb] = 0.f;
+#pragma unroll
+    for (int i = 0; i < C::DB; ++i) acc[i][qb] = f32x4_v{0.f, 0.f, 0.f, 0.f};
   }
-  float m_run[2] = {-INFINITY, -INFINITY}, l_lane[2] = {0.f, 0.f};
 
   int issued = t_begin;
   for (; issued < t_end && issued < t_begin + C::NS - 1; ++issued) issue(issued, issued - t_begin);
@@ -162,7 +173,7 @@ __global__ __launch_bounds__(256) void flash_kernel(AttnArgs p) {
     if (nv < C::KEYS) {
       // zero the value columns of keys nv..63 (their slots may hold anything)
       char* vt = st + C::K_BYTES;
-      for (int idx = threadIdx.x; idx < DH * 8; idx += 256) {
+      for (int idx = threadIdx.x; idx < DH * 8; idx += NW * 64) {
         const int d = idx >> 3, c = idx & 7;
         if (8 * c + 8 <= nv) continue;
         u32x4* w = reinterpret_cast<u32x4*>(vt + d * 128 + ((c ^ ((d >> 1) & 7)) * 16));
@@ -179,12 +190,11 @@ __global__ __launch_bounds__(256) void flash_kernel(AttnArgs p) {
     }
 
     // ---- S^T = K . Q^T ------------------------------------------------------------------------
-    f32x4_v s[4][2];
+    f32x4_v s[4][QPW];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      s[nb][0] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-      s[nb][1] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int qb = 0; qb < QPW; ++qb) s[nb][qb] = f32x4_v{0.f, 0.f, 0.f, 0.f};
     const int swz = l16 >> 1;
 #pragma unroll
     for (int c = 0; c < C::NCH; ++c) {
@@ -192,50 +202,63 @@ __global__ __launch_bounds__(256) void flash_kernel(AttnArgs p) {
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         const u32x4 kf = *reinterpret_cast<const u32x4*>(kb + nb * 16 * 128);
-        Mfma<bf16_t>::mma(s[nb][0], kf, qf[0][c]);
-        Mfma<bf16_t>::mma(s[nb][1], kf, qf[1][c]);
+#pragma unroll
+        for (int qb = 0; qb < QPW; ++qb) Mfma<bf16_t>::mma(s[nb][qb], kf, qf[qb][c]);
       }
     }
 
     // ---- mask, scale, online softmax with conditional rescale -----------------------------
-    u32x4 pb[2][2];
+    // The column max (over the 4 lanes sharing a query column) is only formed when some lane's
+    // scores exceed its running max by more than 8 (log2 units): rare after the first tile.
+    const bool full = !CAUSAL && nv == C::KEYS;
+    u32x4 pb[QPW][2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float mt = -INFINITY;
+    for (int qb = 0; qb < QPW; ++qb) {
+      float ml = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int kl = nb * 16 + 4 * kg + j;     // key within the tile
-          bool vis = kl < nv;
-          if (p.causal && vis) {
-            const int kk = kt0 + kl;
-            int kpos;
-            if (canvas) kpos = P + kk;
-            else kpos = p.is_global ? kk : ring_lo + ((kk - ring_lo) % p.window + p.window) % p.window;
-            vis = kpos <= qpos[qb] && (p.is_global || qpos[qb] - kpos < p.window);
+          for (int j = 0; j < 4; ++j) {
+            const float v = s[nb][qb][j] * p.scale_log2;
+            s[nb][qb][j] = v;
+            ml = fmaxf(ml, v);
           }
-          const float v = vis ? s[nb][qb][j] * p.scale_log2 : -INFINITY;
-          s[nb][qb][j] = v;
-          mt = fmaxf(mt, v);
-        }
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const bool need = mt > m_run[qb] + 8.f || (m_run[qb] == -INFINITY && mt != -INFINITY);
-      if (__any(need)) {
-        const float alpha = need ? (m_run[qb] == -INFINITY ? 0.f : exp2f(m_run[qb] - mt)) : 1.f;
-        if (need) m_run[qb] = mt;
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int kl = key_of_row(nb * 16 + 4 * kg + j);     // key within the tile
+            bool vis = kl < nv;
+            if constexpr (CAUSAL) {
+              const int kk = kt0 + kl;
+              // ring slot -> position: the ring holds positions [ring_lo, ring_lo + window)
+              const int kpos = canvas ? P + kk : (p.is_global ? kk : kk + ring_base + (kk < ring_mod ? p.window : 0));
+              vis = vis && kpos <= qpos[qb] && (p.is_global || qpos[qb] - kpos < p.window);
+            }
+            const float v = vis ? s[nb][qb][j] * p.scale_log2 : -INFINITY;
+            s[nb][qb][j] = v;
+            ml = fmaxf(ml, v);
+          }
+      }
+      if (__any(ml > m_run[qb] + 8.f)) {
+        float mt = fmaxf(ml, __shfl_xor(ml, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const bool need = mt > m_run[qb] + 8.f;     // also true for the first visible scores
+        const float alpha = need ? (m_run[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - mt)) : 1.f;
+        m_run[qb] = need ? mt : m_run[qb];
         l_lane[qb] *= alpha;
 #pragma unroll
         for (int i = 0; i < C::DB; ++i) acc[i][qb] *= alpha;
       }
-      const float mr = m_run[qb];
+      const float mr = m_run[qb] == -INFINITY ? 0.f : m_run[qb];   // all -inf so far: p = 0 below
       float psum = 0.f;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float e = s[nb][qb][j] == -INFINITY ? 0.f : exp2f(s[nb][qb][j] - mr);
+          const float e = __builtin_amdgcn_exp2f(s[nb][qb][j] - mr);   // exp2(-inf) = 0
           s[nb][qb][j] = e;
           psum += e;
         }
@@ -249,9 +272,8 @@ __global__ __launch_bounds__(256) void flash_kernel(AttnArgs p) {
       }
     }
 
-    // ---- O^T += V^T . P^T: the fragment of lane (d = l16, kg) holds keys 32c2 + 4kg .. +3 and
-    // 32c2 + 16 + 4kg .. +3, matching the key order of the P^T fragment built above ----------
-    const char* vt = st + C::K_BYTES + (kg & 1) * 8;
+    // ---- O^T += V^T . P^T: lane (d = l16, kg) supplies keys 32c2 + 8kg .. + 7 of row d -------
+    const char* vt = st + C::K_BYTES;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
       const int d = db * 16 + l16;
@@ -259,18 +281,16 @@ __global__ __launch_bounds__(256) void flash_kernel(AttnArgs p) {
       const int sw = (d >> 1) & 7;
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr + (((4 * c2 + (kg >> 1)) ^ sw) * 16));
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + (((4 * c2 + 2 + (kg >> 1)) ^ sw) * 16));
-        const u32x4 va = {lo.x, lo.y, hi.x, hi.y};
-        Mfma<bf16_t>::mma(acc[db][0], va, pb[0][c2]);
-        Mfma<bf16_t>::mma(acc[db][1], va, pb[1][c2]);
+        const u32x4 va = *reinterpret_cast<const u32x4*>(vr + (((4 * c2 + kg) ^ sw) * 16));
+#pragma unroll
+        for (int qb = 0; qb < QPW; ++qb) Mfma<bf16_t>::mma(acc[db][qb], va, pb[qb][c2]);
       }
     }
   }
 
   // ---- finish --------------------------------------------------------------------------------
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QPW; ++qb) {
     float l = l_lane[qb] + __shfl_xor(l_lane[qb], 16, 64);
     l += __shfl_xor(l, 32, 64);
     if (!qok[qb]) continue;
@@ -298,23 +318,32 @@ __global__ __launch_bounds__(256) void flash_kernel(AttnArgs p) {
   }
 }
 
-template <int DH>
+template <int DH, bool CAUSAL>
 static hipError_t launch_flash_t(const AttnArgs& a, hipStream_t s) {
-  using C = FlashCfg<DH>;
+  using C = FlashCfg<DH, FLASH_QPW, FLASH_WAVES>;
   const int QB = (a.Hq / a.Hkv * a.n + C::QROWS - 1) / C::QROWS;
   const int groups = a.B * a.Hkv * a.splits;
   const int blocks = QB * ((groups + 7) / 8 * 8);
-  static const hipError_t attr = allow_lds(flash_kernel<DH>, C::LDS);
+  auto* k = flash_kernel<DH, CAUSAL, FLASH_QPW, FLASH_WAVES>;
+  static const hipError_t attr = allow_lds(k, C::LDS);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((flash_kernel<DH>), dim3(blocks), dim3(256), C::LDS, s, a);
+  hipLaunchKernelGGL(k, dim3(blocks), dim3(FLASH_WAVES * 64), C::LDS, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_flash(const AttnArgs& a, hipStream_t s) {
-  switch (a.dh) {
-    case 64: return launch_flash_t<64>(a, s);
-    case 128: return launch_flash_t<128>(a, s);
-    case 256: return launch_flash_t<256>(a, s);
+  if (a.causal) {
+    switch (a.dh) {
+      case 64: return launch_flash_t<64, true>(a, s);
+      case 128: return launch_flash_t<128, true>(a, s);
+      case 256: return launch_flash_t<256, true>(a, s);
+    }
+  } else {
+    switch (a.dh) {
+      case 64: return launch_flash_t<64, false>(a, s);
+      case 128: return launch_flash_t<128, false>(a, s);
+      case 256: return launch_flash_t<256, false>(a, s);
+    }
   }
   return hipErrorInvalidValue;
 }

@@ -279,7 +279,7 @@ int attn_splits(const dg_model_desc& d, int B, int n, int nkeys) {
 // bf16 attention: blocks of 128 query rows, one block per CU (LDS ring of 128 KB); key splits
 // bring the block count near 256, each split keeping at least two 64-key tiles
 int flash_splits(const dg_model_desc& d, int B, int n, int ntiles) {
-  const int qb = (d.n_q_heads / d.n_kv_heads * n + 127) / 128;
+  const int qb = (d.n_q_heads / d.n_kv_heads * n + FLASH_QROWS - 1) / FLASH_QROWS;
   const int base = B * d.n_kv_heads * qb;
   int sp = (256 + base - 1) / base;
   if (sp > ntiles / 2) sp = ntiles / 2;
