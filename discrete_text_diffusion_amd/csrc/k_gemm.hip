@@ -164,52 +164,84 @@ __global__ __launch_bounds__(256) void gemm_dense_kernel(DenseArgs p) {
 }
 
 // ---------------------------------------------------------------- grouped (MoE) ----------------
-// Work item w < *n_items: expert e = work[2w], first row m0 = work[2w+1] of that expert's rows
-// [offsets[e], offsets[e] + counts[e]) in grouped order.
+// 1-D grid.  Blocks [0, sh_base): routed tiles, block = item * nt_r + column tile; work item
+// w < *n_items: expert e = work[2w], first row m0 = work[2w+1] of that expert's rows
+// [offsets[e], offsets[e] + counts[e]) in grouped order.  Blocks [sh_base, ...): the shared
+// expert over all rows in row order; the n_sh_items row tiles of one column tile get ids
+// congruent mod 8 (one XCD, one L2 copy of that weight tile).
 template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(256) void gemm_grouped_kernel(GroupedArgs p) {
   using G = TileFor<TA, TB, BM, BN, WM, WN>;
   extern __shared__ __align__(16) char lds[];
-  const int item = blockIdx.y;
-  if (item >= *p.n_items) return;
-  const int e = p.work[2 * item], m0 = p.work[2 * item + 1];
-  const int base = p.offsets[e] + m0;
-  const int rows = min(BM, p.counts[e] - m0);
-  const int n0 = blockIdx.x * BN;
-  const TA* A = static_cast<const TA*>(p.A);
-  const TB* B = static_cast<const TB*>(p.B) + (int64_t)e * p.b_estride;
-  const TB* B2 = p.B2 ? static_cast<const TB*>(p.B2) + (int64_t)e * p.b_estride : nullptr;
+  const int id = blockIdx.x;
+  const bool shared = id >= p.sh_base;
+  int row0, rows, n0, N, K;
+  int64_t lda, ldb, ldc;
+  const TA* A;
+  const TB* B;
+  const TB* B2;
+  const bf16_t* sB;
+  const bf16_t* sB2;
+  const int32_t* a_tok = nullptr;
+  void* Cout;
+  if (!shared) {
+    const int item = id / p.nt_r;
+    if (item >= *p.n_items) return;
+    const int e = p.work[2 * item], m0 = p.work[2 * item + 1];
+    row0 = p.offsets[e] + m0;
+    rows = min(BM, p.counts[e] - m0);
+    n0 = (id - item * p.nt_r) * BN;
+    N = p.N; K = p.K; lda = p.lda; ldb = p.ldb; ldc = p.ldc;
+    A = static_cast<const TA*>(p.A);
+    a_tok = p.a_tok;
+    B = static_cast<const TB*>(p.B) + (int64_t)e * p.b_estride;
+    B2 = p.B2 ? static_cast<const TB*>(p.B2) + (int64_t)e * p.b_estride : nullptr;
+    sB = p.sB ? p.sB + (int64_t)e * p.s_estride : nullptr;
+    sB2 = p.sB2 ? p.sB2 + (int64_t)e * p.s_estride : nullptr;
+    Cout = p.C;
+  } else {
+    const int local = id - p.sh_base, j = local >> 3;
+    const int it = j % p.n_sh_items, nt = (j / p.n_sh_items) * 8 + (local & 7);
+    if (nt >= p.nt_s) return;
+    row0 = it * BM;
+    rows = min(BM, p.sh_rows - row0);
+    n0 = nt * BN;
+    N = p.shN; K = p.shK; lda = p.sh_lda; ldb = p.sh_ldb; ldc = p.sh_ldc;
+    A = static_cast<const TA*>(p.shA);
+    B = static_cast<const TB*>(p.shB);
+    B2 = static_cast<const TB*>(p.shB2);
+    sB = p.sh_sB; sB2 = p.sh_sB2;
+    Cout = p.shC;
+  }
   auto arow = [&](int r) -> const TA* {
     if (r >= rows) return nullptr;
-    const int src = p.a_tok ? p.a_tok[base + r] : base + r;
-    return A + (int64_t)src * p.lda;
+    const int src = a_tok ? a_tok[row0 + r] : row0 + r;
+    return A + (int64_t)src * lda;
   };
   auto brow = [&](int r) -> const TB* {
     if constexpr (EPI == EPI_SWIGLU) {
       int u, half, c;
       paired_col<BN>(r, u, half, c);
       const int oc = n0 / 2 + u * 16 + c;
-      if (oc >= p.N) return nullptr;
-      return (half ? B2 : B) + (int64_t)oc * p.ldb;
+      if (oc >= N) return nullptr;
+      return (half ? B2 : B) + (int64_t)oc * ldb;
     } else {
       const int n = n0 + r;
-      return n < p.N ? B + (int64_t)n * p.ldb : nullptr;
+      return n < N ? B + (int64_t)n * ldb : nullptr;
     }
   };
   G g;
   g.setup(arow, brow);
   f32x4_v acc[G::FM][G::FN];
-  g.run(lds, p.K, acc);
+  g.run(lds, K, acc);
 
   const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) % WN;
-  const bf16_t* sB = p.sB ? p.sB + (int64_t)e * p.s_estride : nullptr;
-  const bf16_t* sB2 = p.sB2 ? p.sB2 + (int64_t)e * p.s_estride : nullptr;
   if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
     for (int j = 0; j < G::FN; j += 2) {
       const int u = (wn * G::FN + j) >> 1;
       const int oc = n0 / 2 + u * 16 + (lane & 15);
-      if (oc >= p.N) continue;
+      if (oc >= N) continue;
       float sg = 1.f, su = 1.f;
       if constexpr (sizeof(TB) == 1) { sg = bf2f(sB[oc]); su = bf2f(sB2[oc]); }
 #pragma unroll
@@ -220,14 +252,14 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GroupedArgs p) {
           if (r >= rows) continue;
           const float gt = acc[i][j][q] * sg, up = acc[i][j + 1][q] * su;
           const float a = gt / (1.f + __expf(-gt)) * up;
-          static_cast<TA*>(p.C)[(int64_t)(base + r) * p.ldc + oc] = Elem<TA>::from_f(a);
+          static_cast<TA*>(Cout)[(int64_t)(row0 + r) * ldc + oc] = Elem<TA>::from_f(a);
         }
     }
   } else {  // EPI_STORE_F32
 #pragma unroll
     for (int j = 0; j < G::FN; ++j) {
       const int n = n0 + G::col_of(j);
-      if (n >= p.N) continue;
+      if (n >= N) continue;
       float sc = 1.f;
       if constexpr (sizeof(TB) == 1) sc = bf2f(sB[n]);
 #pragma unroll
@@ -236,7 +268,7 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GroupedArgs p) {
         for (int q = 0; q < 4; ++q) {
           const int r = G::row_of(i, q);
           if (r >= rows) continue;
-          static_cast<float*>(p.C)[(int64_t)(base + r) * p.ldc + n] = acc[i][j][q] * sc;
+          static_cast<float*>(Cout)[(int64_t)(row0 + r) * ldc + n] = acc[i][j][q] * sc;
         }
     }
   }
@@ -303,12 +335,17 @@ hipError_t launch_dense(const DenseArgs& a, int act_bf16, int w_kind, hipStream_
 }
 
 template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI>
-static hipError_t launch_grouped_t(const GroupedArgs& a, int n_eff, int max_items, hipStream_t s) {
+static hipError_t launch_grouped_t(GroupedArgs a, int n_eff, int sh_eff, int max_items, hipStream_t s) {
   using G = TileFor<TA, TB, BM, BN, WM, WN>;
-  dim3 grid((n_eff + BN - 1) / BN, max_items);
+  a.nt_r = (n_eff + BN - 1) / BN;
+  a.nt_s = (sh_eff + BN - 1) / BN;
+  a.n_sh_items = a.shB ? (a.sh_rows + BM - 1) / BM : 0;
+  a.sh_base = (max_items * a.nt_r + 7) / 8 * 8;
+  const int blocks = a.sh_base + (a.nt_s + 7) / 8 * a.n_sh_items * 8;
+  if (blocks == 0) return hipSuccess;
   static const hipError_t attr = allow_lds(gemm_grouped_kernel<TA, TB, BM, BN, WM, WN, EPI>, G::LDS_BYTES);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((gemm_grouped_kernel<TA, TB, BM, BN, WM, WN, EPI>), grid, dim3(256),
+  hipLaunchKernelGGL((gemm_grouped_kernel<TA, TB, BM, BN, WM, WN, EPI>), dim3(blocks), dim3(256),
                      G::LDS_BYTES, s, a);
   return hipGetLastError();
 }
@@ -316,8 +353,8 @@ static hipError_t launch_grouped_t(const GroupedArgs& a, int n_eff, int max_item
 template <class TA, class TB>
 static hipError_t grouped_dispatch(const GroupedArgs& a, int max_items, hipStream_t s) {
   if (a.epi == EPI_SWIGLU)
-    return launch_grouped_t<TA, TB, GROUP_BM, 128, 1, 4, EPI_SWIGLU>(a, 2 * a.N, max_items, s);
-  return launch_grouped_t<TA, TB, GROUP_BM, 128, 1, 4, EPI_STORE_F32>(a, a.N, max_items, s);
+    return launch_grouped_t<TA, TB, GROUP_BM, 128, 1, 4, EPI_SWIGLU>(a, 2 * a.N, 2 * a.shN, max_items, s);
+  return launch_grouped_t<TA, TB, GROUP_BM, 128, 1, 4, EPI_STORE_F32>(a, a.N, a.shN, max_items, s);
 }
 
 hipError_t launch_grouped(const GroupedArgs& a, int act_bf16, int w_kind, int max_items, hipStream_t s) {

@@ -120,7 +120,7 @@ Layout layout(const dg_model_desc& d, int B, int n, int max_prefix) {
   w.part_ml = take((size_t)MAX_SPLITS * R * d.n_q_heads * 2 * 4);
   w.rparts = take((size_t)MAX_RSPLIT * R * d.n_experts * 4);
   w.o_parts = take((size_t)MAX_KSPLIT * R * d.d_model * 4);
-  w.sh_parts = take((size_t)MAX_KSPLIT * R * d.d_model * 4);
+  w.sh_parts = take(R * d.d_model * 4);
   w.counts = take(d.n_experts * 4);
   w.offsets = take(d.n_experts * 4);
   w.perm = take(Rk * 4);
@@ -387,7 +387,7 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn) {
                              GROUP_BM, P.s));
   route_scope.close();
   const int wk = w_kind(d);
-  // routed experts: gate/up + SwiGLU, then down
+  // routed experts and the shared expert in one launch each: gate/up + SwiGLU, then down
   GroupedArgs ga{};
   ga.epi = EPI_SWIGLU;
   ga.A = at<void>(ws, w.xhat); ga.lda = d.d_model; ga.a_tok = at<int32_t>(ws, w.tok);
@@ -397,6 +397,11 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn) {
   ga.work = at<int32_t>(ws, w.work); ga.n_items = at<int32_t>(ws, w.n_items);
   ga.offsets = at<int32_t>(ws, w.offsets); ga.counts = at<int32_t>(ws, w.counts);
   ga.C = at<void>(ws, w.a_grp); ga.ldc = d.expert_hidden;
+  ga.shA = at<void>(ws, w.xhat); ga.sh_lda = d.d_model;
+  ga.shB = L.sh_gate; ga.shB2 = L.sh_up; ga.sh_ldb = d.d_model;
+  ga.sh_sB = (const uint16_t*)L.sh_s_gate; ga.sh_sB2 = (const uint16_t*)L.sh_s_up;
+  ga.shN = d.shared_hidden; ga.shK = d.d_model; ga.sh_rows = R;
+  ga.shC = at<void>(ws, w.sh_a); ga.sh_ldc = d.shared_hidden;
   {
     ProfScope ps(P.c, DG_PROF_MOE_GATE_UP, P.s);
     HIPCHK(launch_grouped(ga, bf, wk, w.max_items, P.s));
@@ -409,34 +414,18 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn) {
   da.N = d.d_model; da.K = d.expert_hidden;
   da.work = ga.work; da.n_items = ga.n_items; da.offsets = ga.offsets; da.counts = ga.counts;
   da.C = at<void>(ws, w.y); da.ldc = d.d_model;
+  da.shA = at<void>(ws, w.sh_a); da.sh_lda = d.shared_hidden;
+  da.shB = L.sh_down; da.shB2 = nullptr; da.sh_ldb = d.shared_hidden;
+  da.sh_sB = (const uint16_t*)L.sh_s_down; da.sh_sB2 = nullptr;
+  da.shN = d.d_model; da.shK = d.shared_hidden; da.sh_rows = R;
+  da.shC = at<void>(ws, w.sh_parts); da.sh_ldc = d.d_model;
   {
     ProfScope ps(P.c, DG_PROF_MOE_DOWN, P.s);
     HIPCHK(launch_grouped(da, bf, wk, w.max_items, P.s));
   }
-  // shared expert
-  DenseArgs sa{};
-  sa.epi = EPI_SWIGLU;
-  sa.A = at<void>(ws, w.xhat); sa.lda = d.d_model;
-  sa.B = L.sh_gate; sa.B2 = L.sh_up; sa.ldb = d.d_model;
-  sa.sB = (const uint16_t*)L.sh_s_gate; sa.sB2 = (const uint16_t*)L.sh_s_up;
-  sa.M = R; sa.N = d.shared_hidden; sa.K = d.d_model;
-  sa.C = at<void>(ws, w.sh_a); sa.ldc = d.shared_hidden;
-  ProfScope shared_scope(P.c, DG_PROF_SHARED, P.s);
-  HIPCHK(launch_dense(sa, bf, wk, P.s));
-  DenseArgs sd{};
-  sd.epi = EPI_STORE_F32;
-  sd.A = at<void>(ws, w.sh_a); sd.lda = d.shared_hidden;
-  sd.B = L.sh_down; sd.ldb = d.shared_hidden;
-  sd.sB = (const uint16_t*)L.sh_s_down;
-  sd.M = R; sd.N = d.d_model; sd.K = d.shared_hidden;
-  sd.C = at<void>(ws, w.sh_parts); sd.ldc = d.d_model;
-  sd.ksplit = ksplit_for(d, R, d.d_model, sd.K);
-  sd.c_split = (int64_t)R * d.d_model;
-  HIPCHK(launch_dense(sd, bf, wk, P.s));
-  shared_scope.close();
-  HIPCHK(launch_moe_combine(at<float>(ws, w.resid), at<float>(ws, w.y), at<float>(ws, w.sh_parts), sd.ksplit,
-                            sd.c_split, at<float>(ws, w.gates), at<int32_t>(ws, w.inv_perm), R, d.d_model, d.top_k,
-                            P.s));
+  HIPCHK(launch_moe_combine(at<float>(ws, w.resid), at<float>(ws, w.y), at<float>(ws, w.sh_parts), 1,
+                            (int64_t)R * d.d_model, at<float>(ws, w.gates), at<int32_t>(ws, w.inv_perm), R,
+                            d.d_model, d.top_k, P.s));
   return DG_OK;
 }
 

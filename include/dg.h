@@ -202,7 +202,9 @@ dg_status dg_init_canvas(int32_t *canvas, uint8_t *lock, int32_t batch, int32_t 
 /* ---- kernel timing (HIP events recorded around the library's own launches) -------------- */
 typedef enum {
   DG_PROF_MOE_GATE_UP = 0, DG_PROF_MOE_DOWN = 1, DG_PROF_ATTENTION = 2, DG_PROF_SAMPLER = 3,
-  DG_PROF_QKV = 4, DG_PROF_O_PROJ = 5, DG_PROF_SHARED = 6, DG_PROF_ROUTING = 7, DG_PROF_N = 8
+  DG_PROF_QKV = 4, DG_PROF_O_PROJ = 5,
+  DG_PROF_SHARED = 6,   /* records nothing: the shared expert runs inside the two MoE launches */
+  DG_PROF_ROUTING = 7, DG_PROF_N = 8
 } dg_prof_class;
 
 /* Starts recording a pair of events around every launch of the classes in `mask` (bit i =
