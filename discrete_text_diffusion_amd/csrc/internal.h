@@ -27,9 +27,13 @@ struct DenseArgs {
   void* q_out; void* k_out; void* v_out; // q [M][Hq][dh]; k [B][Hkv][rows_per_canvas][dh];
                                          // v d-major [B][Hkv][dh][v_ld]
   int Hq, Hkv, dh, rows_per_canvas, v_ld;
-  double log2_theta;
-  int32_t pos0[MAX_BATCH];               // RoPE position of row 0 of each canvas
+  const float2* rope;                    // (cos, sin) [M][dh/2] from launch_rope_table
 };
+
+struct RopePos { int32_t pos0[MAX_BATCH]; };  // RoPE position of row 0 of each canvas
+// (cos, sin) table [rows][head_dim/2] for the RoPE positions pos0[b] + i of canvas rows
+hipError_t launch_rope_table(float2* tab, int rows, int rows_per_canvas, int head_dim, double log2_theta,
+                             const int32_t* pos0, int B, hipStream_t s);
 
 struct GroupedArgs {
   int epi;
@@ -82,9 +86,10 @@ hipError_t launch_rmsnorm(const float* x, const void* g, void* y, int rows, int 
 hipError_t launch_kv_append(const void* kn, const void* vn, int vn_ld, void* kc, void* vc, int B, int n,
                             int Hkv, int dh, int cap, int window, int is_global,
                             const int32_t* pos0, int act_bf16, hipStream_t s);
-hipError_t launch_moe_combine(float* resid, const float* y, const float* shared, int nsp,
-                              int64_t sp_stride, const float* gates, const int32_t* inv_perm,
-                              int rows, int d, int k, hipStream_t s);
+// resid += MoE output (gated expert rows + shared row); with g, out = RMSNorm(resid) * g
+hipError_t launch_moe_combine_norm(float* resid, const float* y, const float* shared, const float* gates,
+                                   const int32_t* inv_perm, int rows, int d, int k, const void* g, void* out,
+                                   float eps, int bf, int* status, hipStream_t s);
 // resid += sum of nparts split-K partials; y = RMSNorm(resid) * g (d <= 4096)
 hipError_t launch_resid_add_rmsnorm(float* resid, const float* parts, int nparts, int64_t pstride,
                                     const void* g, void* y, int rows, int d, float eps, int act_bf16,
@@ -97,7 +102,7 @@ hipError_t launch_router_topk(const float* parts, int nparts, int64_t part_strid
                               int T, int E, int k, float* logits_out, int32_t* idx, float* gates,
                               hipStream_t s);
 // counts/offsets [E], perm [T*k], inv_perm [T*k], tok [T*k] (token of grouped position),
-// work [2*max_items] + n_items for BM-row tiles.
+// work [2*max_items] + n_items for BM-row tiles
 hipError_t launch_route_tables(const int32_t* idx, int T, int E, int k, int32_t* counts,
                                int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* tok,
                                int32_t* work, int32_t* n_items, int bm, hipStream_t s);

@@ -123,44 +123,93 @@ __global__ __launch_bounds__(256) void gemm_dense_kernel(DenseArgs p) {
         }
     }
   } else if constexpr (EPI == EPI_QKV) {
+    // rotation pairs (jj, jj + dh/2) sit in adjacent column blocks j, j + 1 of one lane; the
+    // angle table holds (cos, sin) of row m's position for pair jj
     const int dh = p.dh, half_dh = dh / 2;
     const int head = n0 / dh, pb = (n0 % dh) / 2;
-    const bool rot = head < p.Hq + p.Hkv;
+    if (head < p.Hq + p.Hkv) {           // q [rows][Hq][dh], canvas k [B][Hkv][n][dh], rotated
 #pragma unroll
-    for (int j = 0; j < G::FN; j += 2) {
-      const int u = (wn * G::FN + j) >> 1;
-      const int jj = pb + u * 16 + (lane & 15);          // pair index in [0, dh/2)
-      const double inv = exp2(-2.0 * jj / dh * p.log2_theta);
+      for (int j = 0; j < G::FN; j += 2) {
+        const int u = (wn * G::FN + j) >> 1;
+        const int jj = pb + u * 16 + (lane & 15);        // pair index in [0, dh/2)
 #pragma unroll
-      for (int i = 0; i < G::FM; ++i)
+        for (int i = 0; i < G::FM; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int m = m0 + G::row_of(i, e);
-          if (m >= p.M) continue;
-          const int b = m / p.rows_per_canvas, ii = m - b * p.rows_per_canvas;
-          float x1 = acc[i][j][e], x2 = acc[i][j + 1][e];
-          if (rot) {
-            const double ang = (double)(p.pos0[b] + ii) * inv;
-            const double red = ang - 6.283185307179586 * floor(ang * 0.15915494309189535);
-            float sn, cs;
-            sincosf((float)red, &sn, &cs);
-            const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
-            x1 = y1; x2 = y2;
-          }
-          if (head < p.Hq + p.Hkv) {     // q [rows][Hq][dh], canvas k [B][Hkv][n][dh]
+          for (int e = 0; e < 4; ++e) {
+            const int m = m0 + G::row_of(i, e);
+            if (m >= p.M) continue;
+            const int b = m / p.rows_per_canvas, ii = m - b * p.rows_per_canvas;
+            const float2 cs = p.rope[(int64_t)m * half_dh + jj];
+            const float x1 = acc[i][j][e], x2 = acc[i][j + 1][e];
             TA* dst = head < p.Hq ? static_cast<TA*>(p.q_out) + ((int64_t)m * p.Hq + head) * dh
                                   : static_cast<TA*>(p.k_out) +
                                         (((int64_t)b * p.Hkv + head - p.Hq) * p.rows_per_canvas + ii) * dh;
-            dst[jj] = Elem<TA>::from_f(x1);
-            dst[jj + half_dh] = Elem<TA>::from_f(x2);
-          } else {                        // canvas v, d-major [B][Hkv][dh][v_ld]
-            TA* dst = static_cast<TA*>(p.v_out) + ((int64_t)b * p.Hkv + head - p.Hq - p.Hkv) * dh * p.v_ld + ii;
-            dst[(int64_t)jj * p.v_ld] = Elem<TA>::from_f(x1);
-            dst[(int64_t)(jj + half_dh) * p.v_ld] = Elem<TA>::from_f(x2);
+            dst[jj] = Elem<TA>::from_f(x1 * cs.x - x2 * cs.y);
+            dst[jj + half_dh] = Elem<TA>::from_f(x2 * cs.x + x1 * cs.y);
+          }
+      }
+    } else {                             // canvas v, d-major [B][Hkv][dh][v_ld], not rotated
+      TA* vbase = static_cast<TA*>(p.v_out) + (int64_t)(head - p.Hq - p.Hkv) * dh * p.v_ld;
+      const int64_t bstride = (int64_t)p.Hkv * dh * p.v_ld;
+#pragma unroll
+      for (int j = 0; j < G::FN; ++j) {
+        const int jj = pb + ((wn * G::FN + j) >> 1) * 16 + (lane & 15);
+        const int d = jj + (j & 1) * half_dh;
+#pragma unroll
+        for (int i = 0; i < G::FM; ++i) {
+          const int m = m0 + G::row_of(i, 0);      // rows m .. m + 3 of this lane
+          const int b = m / p.rows_per_canvas, ii = m - b * p.rows_per_canvas;
+          TA* dst = vbase + b * bstride + (int64_t)d * p.v_ld + ii;
+          if (m + 3 < p.M && ii + 3 < p.rows_per_canvas && (p.rows_per_canvas & 3) == 0) {
+            // four consecutive positions of one canvas: one 8-byte (bf16) / 16-byte (fp32) store
+            if constexpr (sizeof(TA) == 2) {
+              uint2 w;
+              w.x = pack_bf2(acc[i][j][0], acc[i][j][1]);
+              w.y = pack_bf2(acc[i][j][2], acc[i][j][3]);
+              *reinterpret_cast<uint2*>(dst) = w;
+            } else {
+              *reinterpret_cast<f32x4_v*>(dst) = acc[i][j];
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int me = m + e;
+              if (me >= p.M) continue;
+              const int be = me / p.rows_per_canvas, ie = me - be * p.rows_per_canvas;
+              vbase[be * bstride + (int64_t)d * p.v_ld + ie] = Elem<TA>::from_f(acc[i][j][e]);
+            }
           }
         }
+      }
     }
   }
+}
+
+// (cos, sin) of position pos0[b] + i for rotation pair jj: angle = pos * theta^(-2 jj / dh), taken
+// in double and reduced to [0, 2 pi) before the single-precision sincos.  One entry per canvas row
+// and pair: [rows][dh/2].
+__global__ void rope_table_kernel(float2* tab, int rows, int rows_per_canvas, int half_dh, double log2_theta,
+                                  RopePos pos) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)rows * half_dh) return;
+  const int m = (int)(idx / half_dh), jj = (int)(idx - (int64_t)m * half_dh);
+  const int b = m / rows_per_canvas, ii = m - b * rows_per_canvas;
+  const double inv = exp2(-2.0 * jj / (2 * half_dh) * log2_theta);
+  const double ang = (double)(pos.pos0[b] + ii) * inv;
+  const double red = ang - 6.283185307179586 * floor(ang * 0.15915494309189535);
+  float sn, cs;
+  sincosf((float)red, &sn, &cs);
+  tab[idx] = make_float2(cs, sn);
+}
+
+hipError_t launch_rope_table(float2* tab, int rows, int rows_per_canvas, int head_dim, double log2_theta,
+                             const int32_t* pos0, int B, hipStream_t s) {
+  RopePos pos;
+  for (int b = 0; b < B && b < MAX_BATCH; ++b) pos.pos0[b] = pos0[b];
+  const int64_t n = (int64_t)rows * (head_dim / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, tab, rows, rows_per_canvas,
+                     head_dim / 2, log2_theta, pos);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- grouped (MoE) ----------------

@@ -163,50 +163,84 @@ hipError_t launch_kv_append(const void* kn, const void* vn, int vn_ld, void* kc,
   return hipGetLastError();
 }
 
-// resid[t] += sum_{s<k} gate[t][s] * y[inv_perm[t*k+s]] + shared[t], slots in order; the shared
-// expert output arrives as `nsp` split-K partials summed in part order.  All loads of a thread
-// issue before the sums (compile-time slot count K >= k, clamped indices).
-template <int K>
-__global__ void moe_combine_kernel(float* resid, const float* y, const float* shared, int nsp, int64_t sp_stride,
-                                   const float* gates, const int32_t* inv_perm, int rows, int d, int k) {
-  const int t = blockIdx.y;
-  const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
-  if (c >= d) return;
-  f32x4_v yv[K], sv[MAX_PARTS_ADD];
-  float g[K];
+// resid[t] += (sum_{s<k} gate[t][s] * y[inv_perm[t*k+s]] + shared[t]), slots in order; then,
+// when g is given, out[t] = RMSNorm(resid[t]) * g (the next layer's attention norm, or the final
+// norm).  One block per row; each thread owns CPT groups of 4 columns, and every load of the
+// row (k gathered expert rows, the shared row, the residual) issues before the sums.
+constexpr int CPT = 4;   // d <= 256 * 4 * CPT
+template <int K, class T>
+__global__ __launch_bounds__(256) void moe_combine_norm_kernel(float* resid, const float* y, const float* shared,
+                                                               const float* gates, const int32_t* inv_perm,
+                                                               int rows, int d, int k, const T* g, T* out,
+                                                               float eps, int* status) {
+  const int t = blockIdx.x;
+  float gv[K];
+  int pos[K];
 #pragma unroll
   for (int s = 0; s < K; ++s) {
     const int sc = min(s, k - 1);
     // grouped positions are a permutation of [0, rows*k); the clamp only guards the read
-    const int pos = min(max(inv_perm[(int64_t)t * k + sc], 0), rows * k - 1);
-    g[s] = s < k ? gates[(int64_t)t * k + sc] : 0.f;
-    yv[s] = *reinterpret_cast<const f32x4_v*>(y + (int64_t)pos * d + c);
+    pos[s] = min(max(inv_perm[(int64_t)t * k + sc], 0), rows * k - 1);
+    gv[s] = s < k ? gates[(int64_t)t * k + sc] : 0.f;
   }
+  f32x4_v a[CPT];
+  float ss = 0.f;
 #pragma unroll
-  for (int q = 0; q < MAX_PARTS_ADD; ++q)
-    sv[q] = *reinterpret_cast<const f32x4_v*>(shared + min(q, nsp - 1) * sp_stride + (int64_t)t * d + c);
-  f32x4_v acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < CPT; ++j) {
+    const int c = (threadIdx.x + 256 * j) * 4;
+    a[j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+    if (c >= d) continue;
+    f32x4_v yv[K];
 #pragma unroll
-  for (int s = 0; s < K; ++s)
-    if (s < k) acc += g[s] * yv[s];
-  f32x4_v sh = sv[0];
+    for (int s = 0; s < K; ++s) yv[s] = *reinterpret_cast<const f32x4_v*>(y + (int64_t)pos[s] * d + c);
+    const f32x4_v sh = *reinterpret_cast<const f32x4_v*>(shared + (int64_t)t * d + c);
+    f32x4_v* rp = reinterpret_cast<f32x4_v*>(resid + (int64_t)t * d + c);
+    const f32x4_v r0 = *rp;
+    f32x4_v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int q = 1; q < MAX_PARTS_ADD; ++q)
-    if (q < nsp) sh += sv[q];
-  f32x4_v* r = reinterpret_cast<f32x4_v*>(resid + (int64_t)t * d + c);
-  *r = *r + (acc + sh);
+    for (int s = 0; s < K; ++s)
+      if (s < k) acc += gv[s] * yv[s];
+    const f32x4_v r1 = r0 + (acc + sh);
+    *rp = r1;
+    a[j] = r1;
+    ss += r1[0] * r1[0] + r1[1] * r1[1] + r1[2] * r1[2] + r1[3] * r1[3];
+  }
+  if (!g) return;
+  ss = wave_sum(ss);
+  __shared__ float part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = part[0] + part[1] + part[2] + part[3];
+  const float inv = rsqrtf(tot / (float)d + eps);
+  if (threadIdx.x == 0 && status && !isfinite(tot)) atomicOr(status, 2);
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int c = (threadIdx.x + 256 * j) * 4;
+    if (c >= d) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[(int64_t)t * d + c + e] = Elem<T>::from_f(a[j][e] * inv * Elem<T>::to_f(g[c + e]));
+  }
 }
 
-hipError_t launch_moe_combine(float* resid, const float* y, const float* shared, int nsp, int64_t sp_stride,
-                              const float* gates, const int32_t* inv_perm, int rows, int d, int k, hipStream_t s) {
-  if (nsp < 1 || nsp > MAX_PARTS_ADD) return hipErrorInvalidValue;
-  dim3 grid((d / 4 + 255) / 256, rows);
-  if (k <= 2)
-    hipLaunchKernelGGL(moe_combine_kernel<2>, grid, dim3(256), 0, s, resid, y, shared, nsp, sp_stride, gates, inv_perm, rows, d, k);
-  else if (k <= 8)
-    hipLaunchKernelGGL(moe_combine_kernel<8>, grid, dim3(256), 0, s, resid, y, shared, nsp, sp_stride, gates, inv_perm, rows, d, k);
+template <int K>
+static void combine_k(int bf, float* resid, const float* y, const float* shared, const float* gates,
+                      const int32_t* inv_perm, int rows, int d, int k, const void* g, void* out, float eps,
+                      int* status, hipStream_t s) {
+  if (bf)
+    hipLaunchKernelGGL((moe_combine_norm_kernel<K, bf16_t>), dim3(rows), dim3(256), 0, s, resid, y, shared, gates,
+                       inv_perm, rows, d, k, (const bf16_t*)g, (bf16_t*)out, eps, status);
   else
-    hipLaunchKernelGGL(moe_combine_kernel<16>, grid, dim3(256), 0, s, resid, y, shared, nsp, sp_stride, gates, inv_perm, rows, d, k);
+    hipLaunchKernelGGL((moe_combine_norm_kernel<K, float>), dim3(rows), dim3(256), 0, s, resid, y, shared, gates,
+                       inv_perm, rows, d, k, (const float*)g, (float*)out, eps, status);
+}
+
+hipError_t launch_moe_combine_norm(float* resid, const float* y, const float* shared, const float* gates,
+                                   const int32_t* inv_perm, int rows, int d, int k, const void* g, void* out,
+                                   float eps, int bf, int* status, hipStream_t s) {
+  if (d % 4 || d > 256 * 4 * CPT) return hipErrorInvalidValue;
+  if (k <= 2) combine_k<2>(bf, resid, y, shared, gates, inv_perm, rows, d, k, g, out, eps, status, s);
+  else if (k <= 8) combine_k<8>(bf, resid, y, shared, gates, inv_perm, rows, d, k, g, out, eps, status, s);
+  else combine_k<16>(bf, resid, y, shared, gates, inv_perm, rows, d, k, g, out, eps, status, s);
   return hipGetLastError();
 }
 

@@ -1,7 +1,7 @@
 // MoE routing: top-k experts per row (ties to the lower expert id), gates = softmax over the
-// selected router logits, then the expert-grouped row order (rows of each expert in ascending
-// (token, slot) order), its inverse, and the tile work list of the grouped GEMMs.  Everything is
-// deterministic: no atomics decide an order.
+// selected router logits, then per-expert row counts, the expert-grouped row order (rows of each
+// expert in ascending (token, slot) order), its inverse, and the tile work list of the grouped
+// GEMMs.  Everything is deterministic: counts are integer sums and no atomic decides an order.
 #include "common.h"
 #include "internal.h"
 
@@ -110,55 +110,50 @@ DG_DEV int chosen_slot(const int32_t* idx, int t, int k, int e) {
   return slot;
 }
 
-// block e: counts[e]
-template <int K>
-__global__ __launch_bounds__(256) void route_count_kernel(const int32_t* idx, int T, int k, int32_t* counts) {
-  const int e = blockIdx.x;
-  int c = 0;
-  for (int t = threadIdx.x; t < T; t += 256) c += chosen_slot<K>(idx, t, k, e) >= 0;
-  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
-  __shared__ int part[4];
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = c;
+// Block e (one launch for all experts): every block forms the per-expert row counts of all T*k
+// picks in LDS; offsets[e] and expert e's first tile index are the sums of counts / tiles of the
+// experts below e; expert e's work-list tiles (e, m0); then the positions of its rows in
+// ascending row order (wave ballots over row chunks).
+DG_DEV int block_sum_int(int v, int* red) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   __syncthreads();
-  if (threadIdx.x == 0) counts[e] = part[0] + part[1] + part[2] + part[3];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
 }
 
-// one block: offsets (exclusive scan of counts) and the (expert, first row) work list of bm-row tiles
-__global__ __launch_bounds__(256) void route_scan_kernel(const int32_t* counts, int E, int bm, int32_t* offsets,
-                                                         int32_t* work, int32_t* n_items) {
-  __shared__ int s_off[256], s_til[256];
-  const int e = threadIdx.x;
-  const int c = e < E ? counts[e] : 0;
-  s_off[e] = c;
-  s_til[e] = (c + bm - 1) / bm;
-  __syncthreads();
-  if (e == 0) {
-    int ro = 0, rt = 0;
-    for (int q = 0; q < E; ++q) {
-      const int vo = s_off[q], vt = s_til[q];
-      s_off[q] = ro; s_til[q] = rt;
-      ro += vo; rt += vt;
-    }
-    *n_items = rt;
-  }
-  __syncthreads();
-  if (e < E) {
-    offsets[e] = s_off[e];
-    int w = s_til[e];
-    for (int m0 = 0; m0 < c; m0 += bm, ++w) {
-      work[2 * w] = e;
-      work[2 * w + 1] = m0;
-    }
-  }
-}
-
-// block e: positions of expert e's rows in ascending row order
 template <int K>
-__global__ __launch_bounds__(256) void route_scatter_kernel(const int32_t* idx, int T, int k, const int32_t* offsets,
-                                                            int32_t* perm, int32_t* inv_perm, int32_t* tok) {
+__global__ __launch_bounds__(256) void route_place_kernel(const int32_t* idx, int T, int E, int k, int32_t* counts,
+                                                          int bm, int32_t* offsets, int32_t* work,
+                                                          int32_t* n_items, int32_t* perm, int32_t* inv_perm,
+                                                          int32_t* tok) {
   const int e = blockIdx.x;
+  __shared__ int red[4];
   __shared__ int wsum[4];
-  int base = offsets[e];
+  __shared__ int hist[256];
+  for (int q = threadIdx.x; q < 256; q += 256) hist[q] = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < T * k; i += 256) atomicAdd(&hist[min(max(idx[i], 0), E - 1)], 1);
+  __syncthreads();
+  int ro = 0, rt = 0;
+  for (int q = threadIdx.x; q < e; q += 256) {
+    const int c = hist[q];
+    ro += c;
+    rt += (c + bm - 1) / bm;
+  }
+  int base = block_sum_int(ro, red);
+  const int tile0 = block_sum_int(rt, red);
+  const int c = hist[e];
+  if (threadIdx.x == 0) {
+    counts[e] = c;
+    offsets[e] = base;
+    if (e == E - 1) *n_items = tile0 + (c + bm - 1) / bm;
+  }
+  for (int m0 = threadIdx.x * bm; m0 < c; m0 += 256 * bm) {
+    const int w = tile0 + m0 / bm;
+    work[2 * w] = e;
+    work[2 * w + 1] = m0;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int t0 = 0; t0 < T; t0 += 256) {
     const int t = t0 + threadIdx.x;
@@ -185,21 +180,12 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(const int32_t* idx, 
 hipError_t launch_route_tables(const int32_t* idx, int T, int E, int k, int32_t* counts, int32_t* offsets,
                                int32_t* perm, int32_t* inv_perm, int32_t* tok, int32_t* work, int32_t* n_items,
                                int bm, hipStream_t s) {
-  if (k <= 2) {
-    hipLaunchKernelGGL(route_count_kernel<2>, dim3(E), dim3(256), 0, s, idx, T, k, counts);
-  } else if (k <= 8) {
-    hipLaunchKernelGGL(route_count_kernel<8>, dim3(E), dim3(256), 0, s, idx, T, k, counts);
-  } else {
-    hipLaunchKernelGGL(route_count_kernel<16>, dim3(E), dim3(256), 0, s, idx, T, k, counts);
-  }
-  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(256), 0, s, counts, E, bm, offsets, work, n_items);
-  if (k <= 2) {
-    hipLaunchKernelGGL(route_scatter_kernel<2>, dim3(E), dim3(256), 0, s, idx, T, k, offsets, perm, inv_perm, tok);
-  } else if (k <= 8) {
-    hipLaunchKernelGGL(route_scatter_kernel<8>, dim3(E), dim3(256), 0, s, idx, T, k, offsets, perm, inv_perm, tok);
-  } else {
-    hipLaunchKernelGGL(route_scatter_kernel<16>, dim3(E), dim3(256), 0, s, idx, T, k, offsets, perm, inv_perm, tok);
-  }
+  if (k <= 2)
+    hipLaunchKernelGGL(route_place_kernel<2>, dim3(E), dim3(256), 0, s, idx, T, E, k, counts, bm, offsets, work, n_items, perm, inv_perm, tok);
+  else if (k <= 8)
+    hipLaunchKernelGGL(route_place_kernel<8>, dim3(E), dim3(256), 0, s, idx, T, E, k, counts, bm, offsets, work, n_items, perm, inv_perm, tok);
+  else
+    hipLaunchKernelGGL(route_place_kernel<16>, dim3(E), dim3(256), 0, s, idx, T, E, k, counts, bm, offsets, work, n_items, perm, inv_perm, tok);
   return hipGetLastError();
 }
 

@@ -91,7 +91,7 @@ int sampler_slices(const dg_model_desc& d, int rows, int* v_per_slice) {
 // on the row count, so the test hooks can find them from `rows` alone.
 struct Layout {
   size_t status, stats, rlogits, idx, gates;
-  size_t resid, xhat, q, kn, vn, attn_o, part_o, part_ml, rparts, o_parts, sh_parts;
+  size_t resid, xhat, rope, q, kn, vn, attn_o, part_o, part_ml, rparts, o_parts, sh_parts;
   size_t counts, offsets, perm, inv_perm, tok, work, n_items;
   size_t a_grp, y, sh_a, samp_part, hidden, done, n_locked;
   size_t total;
@@ -111,6 +111,7 @@ Layout layout(const dg_model_desc& d, int B, int n, int max_prefix) {
   w.gates = take(Rk * 4);
   w.resid = take(R * d.d_model * 4);
   w.xhat = take(R * d.d_model * ab);
+  w.rope = take(R * (d.head_dim / 2) * 8);
   w.q = take(R * d.n_q_heads * d.head_dim * ab);
   w.kn = take(R * d.n_kv_heads * d.head_dim * ab);
   w.vn = take((size_t)B * up8(n) * d.n_kv_heads * d.head_dim * ab);
@@ -288,7 +289,10 @@ int flash_splits(const dg_model_desc& d, int B, int n, int ntiles) {
   return sp;
 }
 
-dg_status run_layer(const Pass& P, int l, bool do_ffn) {
+// One decoder layer.  xhat_ready: the previous layer's combine already wrote RMSNorm(resid) *
+// attn_norm into xhat.  next_g / next_out: the combine also writes RMSNorm(resid) * next_g
+// (the next layer's attention norm or the final norm) into next_out.
+dg_status run_layer(const Pass& P, int l, bool do_ffn, bool xhat_ready, const void* next_g, void* next_out) {
   const dg_model_desc& d = P.c->d;
   const dg_layer_weights& L = P.c->layers[l];
   const int bf = d.act_dtype == DG_BF16;
@@ -298,8 +302,9 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn) {
   int* status = at<int>(ws, w.status);
   const bool glob = is_global(d, l);
 
-  HIPCHK(launch_rmsnorm(at<float>(ws, w.resid), L.attn_norm, at<void>(ws, w.xhat), R, d.d_model, d.norm_eps, bf,
-                        status, P.s));
+  if (!xhat_ready)
+    HIPCHK(launch_rmsnorm(at<float>(ws, w.resid), L.attn_norm, at<void>(ws, w.xhat), R, d.d_model, d.norm_eps, bf,
+                          status, P.s));
   // QKV + RoPE
   DenseArgs qa{};
   qa.epi = EPI_QKV;
@@ -308,8 +313,7 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn) {
   qa.M = R; qa.N = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim; qa.K = d.d_model;
   qa.q_out = at<void>(ws, w.q); qa.k_out = at<void>(ws, w.kn); qa.v_out = at<void>(ws, w.vn);
   qa.Hq = d.n_q_heads; qa.Hkv = d.n_kv_heads; qa.dh = d.head_dim; qa.rows_per_canvas = P.n; qa.v_ld = up8(P.n);
-  qa.log2_theta = std::log2((double)d.rope_theta);
-  for (int b = 0; b < P.B; ++b) qa.pos0[b] = P.kv->prefix_len[b];
+  qa.rope = at<float2>(ws, w.rope);
   {
     ProfScope ps(P.c, DG_PROF_QKV, P.s);
     HIPCHK(launch_dense(qa, bf, bf ? W_BF16 : W_F32, P.s));
@@ -423,9 +427,9 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn) {
     ProfScope ps(P.c, DG_PROF_MOE_DOWN, P.s);
     HIPCHK(launch_grouped(da, bf, wk, w.max_items, P.s));
   }
-  HIPCHK(launch_moe_combine(at<float>(ws, w.resid), at<float>(ws, w.y), at<float>(ws, w.sh_parts), 1,
-                            (int64_t)R * d.d_model, at<float>(ws, w.gates), at<int32_t>(ws, w.inv_perm), R,
-                            d.d_model, d.top_k, P.s));
+  HIPCHK(launch_moe_combine_norm(at<float>(ws, w.resid), at<float>(ws, w.y), at<float>(ws, w.sh_parts),
+                                 at<float>(ws, w.gates), at<int32_t>(ws, w.inv_perm), R, d.d_model, d.top_k, next_g,
+                                 next_out, d.norm_eps, bf, status, P.s));
   return DG_OK;
 }
 
@@ -599,9 +603,14 @@ dg_status dg_prefill_kv(dg_ctx* ctx, const dg_kv* kv, const int32_t* tokens, int
   const dg_model_desc& d = ctx->d;
   HIPCHK(launch_embed(tokens, ctx->embed, at<float>(ws, P.w.resid), P.B * n, d.d_model, d.vocab,
                       d.act_dtype == DG_BF16, stream));
+  HIPCHK(launch_rope_table(at<float2>(ws, P.w.rope), P.B * n, n, d.head_dim, std::log2((double)d.rope_theta),
+                           kv->prefix_len, P.B, stream));
   for (int l = 0; l < d.n_layers; ++l) {
-    // the last layer's FFN feeds no cache
-    if ((st = run_layer(P, l, l + 1 < d.n_layers)) != DG_OK) return st;
+    // the last layer's FFN feeds no cache; each combine writes the next layer's normalised rows
+    const bool more = l + 1 < d.n_layers;
+    if ((st = run_layer(P, l, more, l > 0, more ? ctx->layers[l + 1].attn_norm : nullptr,
+                        at<void>(ws, P.w.xhat))) != DG_OK)
+      return st;
   }
   return DG_OK;
 }
@@ -626,10 +635,17 @@ dg_status dg_denoise_step(dg_ctx* ctx, const dg_kv* kv, const int32_t* canvas, c
   const int bf = d.act_dtype == DG_BF16;
   if (resid_in) HIPCHK(launch_copy_f32(resid_in, at<float>(ws, P.w.resid), (int64_t)R * d.d_model, stream));
   else HIPCHK(launch_embed(canvas, ctx->embed, at<float>(ws, P.w.resid), R, d.d_model, d.vocab, bf, stream));
-  for (int l = layer_begin; l < layer_end; ++l)
-    if ((st = run_layer(P, l, true)) != DG_OK) return st;
+  HIPCHK(launch_rope_table(at<float2>(ws, P.w.rope), R, L, d.head_dim, std::log2((double)d.rope_theta),
+                           kv->prefix_len, P.B, stream));
+  // each layer's combine writes the next layer's normalised rows, the last one the final norm
+  for (int l = layer_begin; l < layer_end; ++l) {
+    const bool last = l + 1 == layer_end;
+    const void* ng = last ? (hidden_out ? ctx->final_norm : nullptr) : ctx->layers[l + 1].attn_norm;
+    void* no = last ? hidden_out : at<void>(ws, P.w.xhat);
+    if ((st = run_layer(P, l, true, l > layer_begin, ng, no)) != DG_OK) return st;
+  }
   if (resid_out) HIPCHK(launch_copy_f32(at<float>(ws, P.w.resid), resid_out, (int64_t)R * d.d_model, stream));
-  if (hidden_out)
+  if (hidden_out && layer_begin == layer_end)
     HIPCHK(launch_rmsnorm(at<float>(ws, P.w.resid), ctx->final_norm, hidden_out, R, d.d_model, d.norm_eps, bf,
                           at<int>(ws, P.w.status), stream));
   return DG_OK;
