@@ -31,7 +31,29 @@ def parse():
     ap.add_argument("--workload", default="C2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="per-class kernel times after the timed region")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after the timed region, copy 512 MiB device to device 4 times (a plain copy of known "
+                         "size for scaling hardware byte counters)")
     return ap.parse_args()
+
+
+# HBM bytes of one MoE gate/up launch on this workload, from two rocprofv3 --pmc passes
+# (FETCH_SIZE, WRITE_SIZE; KiB per dispatch, mean of 90 launches), each scaled by the same counter
+# on a 512 MiB device-to-device copy (FETCH_SIZE reads 262155.6 KiB for 524288 KiB read: x1.9999;
+# WRITE_SIZE reads 524288 KiB: x1).  Valid only while the kernel sources hash to `sources`.
+MOE_TRAFFIC = {"sources": "880173230ae08c08cce246cb3b82a1d34e9b960cfe4bdd4fb397702aced9ff58",
+               "fetch_kib": 557366.1, "write_kib": 3872.2, "bytes_per_launch": 1145400288}
+TRAFFIC_SOURCES = ("k_gemm.hip", "gemm_dma.h", "gemm_core.h", "common.h", "internal.h")
+
+
+def kernel_digest():
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "discrete_text_diffusion_amd", "csrc")
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def log(*a):
@@ -39,10 +61,10 @@ def log(*a):
 
 
 def cpu_baseline(cfg, W, kv, H_dev):
-    """The oracle, untuned, on a bounded sample of the same workload: one local and one global
-    decoder layer (all 256 canvas rows) and the sampler statistics for 8 rows over the full
-    vocabulary, scaled to one full step (local layers x n_local + global x n_global + 256/8 x
-    sampler sample)."""
+    """The oracle, untuned, on a bounded sample of the same workload: the first two local/global
+    periods of decoder layers (12 layers at the 5:1 pattern, all canvas rows) and the sampler
+    statistics for every canvas row over the full vocabulary, scaled to one full step (mean local
+    layer x n_local + mean global layer x n_global + sampler)."""
     import numpy as np
     import torch
     from oracle import model as M
@@ -56,35 +78,38 @@ def cpu_baseline(cfg, W, kv, H_dev):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    loc = next(l for l in range(cfg.n_layers) if not cfg.is_global(l))
-    glb = next(l for l in range(cfg.n_layers) if cfg.is_global(l))
+    period = cfg.global_every if cfg.global_every > 0 else 1
+    sample_layers = list(range(min(cfg.n_layers, 2 * period)))
     rnd = rounder(cfg.act_dtype)
     h0 = gen.resid_input(cfg.replace(resid_input=True)).numpy().astype(np.float64)
-    times = {}
-    for tag, l in (("local", loc), ("global", glb)):
+    times = {"local": [], "global": []}
+    for tag, l in [("global" if cfg.is_global(l) else "local", l) for l in sample_layers]:
         lw = oracle_layer(W["layers"][l], cfg)                  # conversion: not timed
         K, V = np64(kv[l][0]), np64(kv[l][1])
         t0 = time.perf_counter()
         M.denoise_layer(cfg, l, h0, lw, K, V, [cfg.prefix] * cfg.batch, rnd)
-        times[tag] = time.perf_counter() - t0
+        times[tag].append(time.perf_counter() - t0)
         del lw, K, V
     E = np64(W["embed"])
-    H = H_dev[:8].float().cpu().numpy().astype(np.float64)
-    rows = np.arange(8)
+    ns = cfg.rows
+    H = H_dev[:ns].float().cpu().numpy().astype(np.float64)
+    rows = np.arange(ns)
     t0 = time.perf_counter()
     z = S.logits(H, E, cfg.tau)
     S.sample_stats(z, cfg.seed, 1, rows // cfg.canvas, rows % cfg.canvas)
-    times["sampler8"] = time.perf_counter() - t0
+    t_samp = time.perf_counter() - t0
+    t_loc = sum(times["local"]) / max(len(times["local"]), 1)
+    t_glb = sum(times["global"]) / max(len(times["global"]), 1)
     n_glob = sum(cfg.is_global(l) for l in range(cfg.n_layers))
     n_loc = cfg.n_layers - n_glob
-    t_step = n_loc * times["local"] + n_glob * times["global"] + (cfg.rows / 8) * times["sampler8"]
-    sample_s = times["local"] + times["global"] + times["sampler8"]
+    t_step = n_loc * t_loc + n_glob * t_glb + (cfg.rows / ns) * t_samp
+    sample_s = sum(times["local"]) + sum(times["global"]) + t_samp
     return {"value": round(cfg.rows / t_step, 3), "unit": "canvas-token-steps/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": (f"oracle float64 on host: one local layer ({times['local']:.2f} s) + one global layer "
-                       f"({times['global']:.2f} s) over all {cfg.rows} rows, sampler for 8 of {cfg.rows} rows "
-                       f"({times['sampler8']:.2f} s); scaled to {n_loc} local + {n_glob} global layers + "
-                       f"{cfg.rows} sampler rows = {t_step:.1f} s per step; {sample_s:.1f} s measured")}
+            "sample": (f"oracle float64 on host: layers 0-{len(sample_layers) - 1} ({len(times['local'])} local at "
+                       f"{t_loc:.2f} s, {len(times['global'])} global at {t_glb:.2f} s) over all {cfg.rows} rows, "
+                       f"sampler for {ns} of {cfg.rows} rows ({t_samp:.2f} s); scaled to {n_loc} local + {n_glob} "
+                       f"global layers = {t_step:.1f} s per step; {sample_s:.1f} s measured")}
 
 
 def main():
@@ -162,7 +187,18 @@ def main():
                      + R * cfg.d_model * abytes
                      + (R * cfg.top_k * cfg.expert_hidden + R * cfg.shared_hidden) * abytes)
     moe_avg_ms = moe_ms / max(moe_n, 1)
+    traffic = (MOE_TRAFFIC["bytes_per_launch"]
+               if args.workload == "C2" and kernel_digest() == MOE_TRAFFIC["sources"] else None)
     achieved = gate_up_bytes / (moe_avg_ms * 1e-3) / 1e9
+
+    if args.calib_copy:
+        src = torch.ones(256 << 20, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copies: 4 x {src.numel() * 2} bytes read and written")
+        del src, dst
 
     breakdown = None
     if args.breakdown:
@@ -204,7 +240,7 @@ def main():
                    "top_k": cfg.top_k, "schedule_steps": T},
         "roofline": {"kernel": "moe_gate_up (routed + shared experts gate/up + SwiGLU, one launch)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "avg_launch_ms": round(moe_avg_ms, 5), "launches": moe_n,
                      "algorithmic_bytes_per_launch": gate_up_bytes, "unique_experts": uniq},
         "cpu_baseline": cpu,
