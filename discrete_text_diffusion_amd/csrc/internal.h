@@ -44,13 +44,13 @@ struct GroupedArgs {
   const int32_t* work; const int32_t* n_items;       // (expert, first row) per tile
   const int32_t* offsets; const int32_t* counts;
   void* C; int64_t ldc;                               // output row = grouped position
-  // shared expert (every row, in row order), tiles of GROUP_BM rows after the routed tiles
+  // shared expert (every row, in row order), tiles of GROUP_BM rows before the routed tiles
   const void* shA; int64_t sh_lda;
   const void* shB; const void* shB2; int64_t sh_ldb;
   const uint16_t* sh_sB; const uint16_t* sh_sB2;
   int shN, shK, sh_rows;
   void* shC; int64_t sh_ldc;
-  int nt_r, nt_s, sh_base, n_sh_items;                // filled by the launcher
+  int nt_r, nt_s, sh_blocks, n_sh_items;              // filled by the launcher
 };
 
 hipError_t launch_dense(const DenseArgs& a, int act_bf16, int w_kind, hipStream_t s);

@@ -213,17 +213,18 @@ hipError_t launch_rope_table(float2* tab, int rows, int rows_per_canvas, int hea
 }
 
 // ---------------------------------------------------------------- grouped (MoE) ----------------
-// 1-D grid.  Blocks [0, sh_base): routed tiles, block = item * nt_r + column tile; work item
-// w < *n_items: expert e = work[2w], first row m0 = work[2w+1] of that expert's rows
-// [offsets[e], offsets[e] + counts[e]) in grouped order.  Blocks [sh_base, ...): the shared
-// expert over all rows in row order; the n_sh_items row tiles of one column tile get ids
-// congruent mod 8 (one XCD, one L2 copy of that weight tile).
+// 1-D grid.  Blocks [0, sh_blocks): the shared expert over all rows in row order, first (it
+// re-reads each weight tile once per row tile, so it goes before the uniform routed tiles rather
+// than into the tail); the n_sh_items row tiles of one column tile get ids congruent mod 8 (one
+// XCD, one L2 copy of that weight tile).  Blocks [sh_blocks, ...): routed tiles, block -
+// sh_blocks = item * nt_r + column tile; work item w < *n_items: expert e = work[2w], first row
+// m0 = work[2w+1] of that expert's rows [offsets[e], offsets[e] + counts[e]) in grouped order.
 template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(256) void gemm_grouped_kernel(GroupedArgs p) {
   using G = TileFor<TA, TB, BM, BN, WM, WN>;
   extern __shared__ __align__(16) char lds[];
   const int id = blockIdx.x;
-  const bool shared = id >= p.sh_base;
+  const bool shared = id < p.sh_blocks;
   int row0, rows, n0, N, K;
   int64_t lda, ldb, ldc;
   const TA* A;
@@ -234,12 +235,13 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GroupedArgs p) {
   const int32_t* a_tok = nullptr;
   void* Cout;
   if (!shared) {
-    const int item = id / p.nt_r;
+    const int rid = id - p.sh_blocks;
+    const int item = rid / p.nt_r;
     if (item >= *p.n_items) return;
     const int e = p.work[2 * item], m0 = p.work[2 * item + 1];
     row0 = p.offsets[e] + m0;
     rows = min(BM, p.counts[e] - m0);
-    n0 = (id - item * p.nt_r) * BN;
+    n0 = (rid - item * p.nt_r) * BN;
     N = p.N; K = p.K; lda = p.lda; ldb = p.ldb; ldc = p.ldc;
     A = static_cast<const TA*>(p.A);
     a_tok = p.a_tok;
@@ -249,7 +251,7 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GroupedArgs p) {
     sB2 = p.sB2 ? p.sB2 + (int64_t)e * p.s_estride : nullptr;
     Cout = p.C;
   } else {
-    const int local = id - p.sh_base, j = local >> 3;
+    const int local = id, j = local >> 3;
     const int it = j % p.n_sh_items, nt = (j / p.n_sh_items) * 8 + (local & 7);
     if (nt >= p.nt_s) return;
     row0 = it * BM;
@@ -389,8 +391,8 @@ static hipError_t launch_grouped_t(GroupedArgs a, int n_eff, int sh_eff, int max
   a.nt_r = (n_eff + BN - 1) / BN;
   a.nt_s = (sh_eff + BN - 1) / BN;
   a.n_sh_items = a.shB ? (a.sh_rows + BM - 1) / BM : 0;
-  a.sh_base = (max_items * a.nt_r + 7) / 8 * 8;
-  const int blocks = a.sh_base + (a.nt_s + 7) / 8 * a.n_sh_items * 8;
+  a.sh_blocks = (a.nt_s + 7) / 8 * a.n_sh_items * 8;
+  const int blocks = a.sh_blocks + max_items * a.nt_r;
   if (blocks == 0) return hipSuccess;
   static const hipError_t attr = allow_lds(gemm_grouped_kernel<TA, TB, BM, BN, WM, WN, EPI>, G::LDS_BYTES);
   if (attr != hipSuccess) return attr;
