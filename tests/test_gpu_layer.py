@@ -130,3 +130,58 @@ def test_layer_is_deterministic():
         outs.append(r)
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1])
+
+
+def test_fp8_batch8_layers_parity_full_shape():
+    """Eight canvases over a 4096-token prefix each, fp8 e4m3 experts with a Zipf(1.1) router
+    prior: one local and one global layer at the full 2048-row shape."""
+    cfg = configs.C4.replace(n_layers=6, resid_input=True)
+    _layer_parity(cfg, 0, 2e-2)
+    _layer_parity(cfg, 5, 2e-2)
+
+
+def test_long_prefix_global_layer_sampled_rows():
+    """A global layer over a 131072-token prefix (131328 keys per query).  The GPU runs the whole
+    layer; the oracle recomputes q/k/v for every canvas row (the canvas keys need all of them) and
+    the attention, output projection and MoE for 12 sampled rows, which depend on no other row."""
+    cfg = configs.C3.replace(n_layers=6, resid_input=True)
+    layer = 5
+    log(f"sampled-row parity: {cfg.name} layer {layer}, prefix {cfg.prefix}")
+    model, W, kv = build(cfg)
+    B, L = cfg.batch, cfg.canvas
+    ws = model.workspace(B, L, cfg.prefix)
+    rin = gen.resid_input(cfg, DEV)
+    rout = torch.empty_like(rin)
+    model.denoise_step(None, L, ws, resid_out=rout, resid_in=rin, layer_begin=layer, layer_end=layer + 1)
+    r_logits = torch.empty(B * L, cfg.n_experts, dtype=torch.float32, device=DEV)
+    r_idx = torch.empty(B * L, cfg.top_k, dtype=torch.int32, device=DEV)
+    dg.dg_test_read_routing(model.ctx, ws, B * L, r_logits, r_idx, None)
+    torch.cuda.synchronize()
+    assert dg.dg_query_status(model.ctx, ws) == dg.DG_OK
+    rows = np.array([0, 1, 17, 63, 64, 100, 127, 128, 191, 200, 254, 255])
+    lw = oracle_layer(W["layers"][layer], cfg)
+    K = np64(kv[layer][0])[0]
+    V = np64(kv[layer][1].transpose(-1, -2))[0]
+    rnd = rounder(cfg.act_dtype)
+    h0 = rin.cpu().numpy().astype(np.float64)
+    x = rnd(M.rmsnorm(h0, lw["attn_norm"], cfg.norm_eps))
+    pos = cfg.prefix + np.arange(L)
+    q, k, v = M.qkv(cfg, x, lw, pos, rnd)
+    o = M.canvas_attention(cfg, layer, q[rows], k.transpose(1, 0, 2), v.transpose(1, 0, 2), K, V, cfg.prefix)
+    o = rnd(o.reshape(len(rows), -1))
+    h1 = h0[rows] + o @ lw["w_o"].T
+    a2 = rnd(M.rmsnorm(h1, lw["ffn_norm"], cfg.norm_eps))
+    f, info = M.moe(cfg, a2, lw, rnd)
+    gidx = r_idx.cpu().numpy()[rows]
+    g_r = r_logits.cpu().numpy()[rows]
+    assert np.array_equal(gidx, M.router_topk(g_r, cfg.top_k)[0])
+    lg_err = float(np.abs(g_r - info["r32"]).max())
+    srt = -np.sort(-info["r32"].astype(np.float64), axis=1)
+    near = srt[:, cfg.top_k - 1] - srt[:, cfg.top_k] <= 2 * lg_err + 1e-6
+    mism = np.any(np.sort(gidx, 1) != np.sort(info["idx"], 1), axis=1)
+    assert lg_err <= 2e-2 and not (mism & ~near).any()
+    if mism.any():
+        f, _ = M.moe(cfg, a2, lw, rnd, forced_idx=np.where(mism[:, None], gidx, info["idx"]))
+    err = np.abs(rout.cpu().numpy()[rows] - (h1 + f)).max()
+    log(f"  max |resid - oracle| over {len(rows)} rows = {err:.3e}; router logits max err {lg_err:.2e}")
+    assert err <= 2e-2
