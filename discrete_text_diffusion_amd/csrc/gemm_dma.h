@@ -41,13 +41,14 @@ DG_DEV void wait_vm() {
 
 template <class T, int BM, int BN, int WM, int WN, int NS>
 struct GemmDma {
-  static_assert(WM * WN == 4, "4 waves");
-  static_assert(BM % 32 == 0 && BN % 32 == 0, "rows per tile: multiples of 32 (4 waves x 8 rows)");
+  static constexpr int NW = WM * WN;                   // waves per block
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "rows per tile: multiples of 8 x waves");
   static_assert(NS >= 2 && NS <= 8, "stages");
   static constexpr int FM = BM / WM / 16;
   static constexpr int FN = BN / WN / 16;
   static constexpr int KT = 128 / sizeof(T);          // K elements per tile
-  static constexpr int IA = BM / 32, IB = BN / 32;     // load instructions per wave per tile
+  static constexpr int IA = BM / (8 * NW), IB = BN / (8 * NW);   // load instructions per wave per tile
   static constexpr int LPT = IA + IB;
   static constexpr int STAGE = (BM + BN) * 128;
   static constexpr int LDS_BYTES = NS * STAGE;
@@ -64,14 +65,14 @@ struct GemmDma {
     const int rr = lane >> 3, slot = lane & 7;
 #pragma unroll
     for (int i = 0; i < IA; ++i) {
-      const int r = (wave + 4 * i) * 8 + rr;
+      const int r = (wave + NW * i) * 8 + rr;
       const char* p = reinterpret_cast<const char*>(arow(r));
       if (!p) p = reinterpret_cast<const char*>(arow(0));
       a_src[i] = p + ((slot ^ ((r >> 1) & 7)) * 16);
     }
 #pragma unroll
     for (int i = 0; i < IB; ++i) {
-      const int r = (wave + 4 * i) * 8 + rr;
+      const int r = (wave + NW * i) * 8 + rr;
       const char* p = reinterpret_cast<const char*>(brow(r));
       if (!p) p = reinterpret_cast<const char*>(brow(0));
       b_src[i] = p + ((slot ^ ((r >> 1) & 7)) * 16);
@@ -83,9 +84,9 @@ struct GemmDma {
     char* st = lds + stage * STAGE;
     const size_t off = (size_t)kt * 128;
 #pragma unroll
-    for (int i = 0; i < IA; ++i) dma16(a_src[i] + off, st + (wave + 4 * i) * 8 * 128);
+    for (int i = 0; i < IA; ++i) dma16(a_src[i] + off, st + (wave + NW * i) * 8 * 128);
 #pragma unroll
-    for (int i = 0; i < IB; ++i) dma16(b_src[i] + off, st + BM * 128 + (wave + 4 * i) * 8 * 128);
+    for (int i = 0; i < IB; ++i) dma16(b_src[i] + off, st + BM * 128 + (wave + NW * i) * 8 * 128);
   }
 
   // wait for the oldest of `pending` outstanding tiles (pending = tiles issued and not yet

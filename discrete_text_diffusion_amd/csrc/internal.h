@@ -117,6 +117,8 @@ struct SampArgs {
   float* part;                    // [slices][rows][5] partial (m2, s, a, g2, y) as floats/ints
 };
 hipError_t launch_lmhead_sampler(const SampArgs& a, int act_bf16, hipStream_t s);
+// fused LM head tiles: rows x vocabulary entries per block step (bf16: 8 waves as 4 x 2)
+constexpr int SAMPLER_BM = 128, SAMPLER_BN_BF16 = 256, SAMPLER_BN_F32 = 128;
 hipError_t launch_logits_partials(const float* z, int rows, int V, int L, float zscale_log2,
                                   uint32_t k0, uint32_t k1, uint32_t step, int slices,
                                   int v_per_slice, float* part, hipStream_t s);

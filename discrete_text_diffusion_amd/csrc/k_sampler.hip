@@ -50,9 +50,13 @@ DG_DEV float gumbel_key2(float z2, uint32_t w) {
 }
 
 // ------------------------------------------------------------------ fused LM head partials ------
-template <class TA, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(256) void lmhead_sampler_kernel(SampArgs p, int n_mt) {
-  using G = GemmDma<TA, BM, BN, WM, WN, 3>;
+// Block = (vocabulary slice, BM-row tile).  The slice's vocabulary tiles stream through one
+// continuous direct-to-LDS ring: step s = (tile t, K tile kt), so the ring never drains between
+// vocabulary tiles; after the last K tile of t the logits of t are consumed in registers.
+template <class TA, int BM, int BN, int WM, int WN, int NS>
+__global__ __launch_bounds__(WM * WN * 64) void lmhead_sampler_kernel(SampArgs p, int n_mt) {
+  using G = GemmDma<TA, BM, BN, WM, WN, NS>;
+  constexpr int NW = WM * WN;
   extern __shared__ __align__(16) char lds[];
   // blocks of one vocabulary slice run on the same XCD (block id mod 8) so E tiles are shared
   const int id = blockIdx.x, xcd = id & 7, local = id >> 3;
@@ -62,30 +66,64 @@ __global__ __launch_bounds__(256) void lmhead_sampler_kernel(SampArgs p, int n_m
   const int m0 = mt * BM;
   const int v_begin = slice * p.v_per_slice;
   const int v_end = min(p.V, v_begin + p.v_per_slice);
-  const TA* H = static_cast<const TA*>(p.H);
-  const TA* E = static_cast<const TA*>(p.E);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nk = p.d / G::KT;
+  const int nsteps = (v_end - v_begin + BN - 1) / BN * nk;
+
+  // DMA sources: this lane's H row (fixed) and E row index within a tile, each with its swizzled chunk
+  const int rr = lane >> 3, slot = lane & 7;
+  const char* a_src[G::IA];
+#pragma unroll
+  for (int i = 0; i < G::IA; ++i) {
+    const int r = (wave + NW * i) * 8 + rr;
+    const int m = m0 + r < p.rows ? m0 + r : m0;
+    a_src[i] = static_cast<const char*>(p.H) + (int64_t)m * p.d * sizeof(TA) + ((slot ^ ((r >> 1) & 7)) * 16);
+  }
+  const char* E = static_cast<const char*>(p.E);
+  int it_t = 0, it_k = 0;                      // (tile, K tile) of the next step to issue
+  auto issue = [&](int stage) {
+    char* st = lds + stage * G::STAGE;
+    const size_t koff = (size_t)it_k * 128;
+#pragma unroll
+    for (int i = 0; i < G::IA; ++i) dma16(a_src[i] + koff, st + (wave + NW * i) * 8 * 128);
+    const int v0 = v_begin + it_t * BN;
+#pragma unroll
+    for (int i = 0; i < G::IB; ++i) {
+      const int r = (wave + NW * i) * 8 + rr;
+      const int v = min(v0 + r, v_end - 1);
+      dma16(E + (int64_t)v * p.d * sizeof(TA) + ((slot ^ ((r >> 1) & 7)) * 16) + koff,
+            st + BM * 128 + (wave + NW * i) * 8 * 128);
+    }
+    if (++it_k == nk) { it_k = 0; ++it_t; }
+  };
 
   RowState st[G::FM][4];
 #pragma unroll
   for (int i = 0; i < G::FM; ++i)
 #pragma unroll
     for (int e = 0; e < 4; ++e) state_init(st[i][e]);
+  f32x4_v acc[G::FM][G::FN];
+#pragma unroll
+  for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j) acc[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
 
-  for (int v0 = v_begin; v0 < v_end; v0 += BN) {
-    auto arow = [&](int r) -> const TA* {
-      const int m = m0 + r;
-      return m < p.rows ? H + (int64_t)m * p.d : nullptr;
-    };
-    auto brow = [&](int r) -> const TA* {
-      const int v = v0 + r;
-      return v < v_end ? E + (int64_t)v * p.d : nullptr;
-    };
-    G g;
-    g.setup(arow, brow);
-    f32x4_v acc[G::FM][G::FN];
-    g.run(lds, p.d, acc);
-
+  int issued = 0;
+  for (; issued < NS - 1 && issued < nsteps; ++issued) issue(issued);
+  int t = 0, kt = 0;
+  for (int s = 0; s < nsteps; ++s) {
+    G::wait_oldest(issued - s);
+    lds_barrier();
+    if (issued < nsteps) {
+      issue(issued % NS);
+      ++issued;
+    }
+    G::compute(lds + (s % NS) * G::STAGE, acc);
+    if (++kt < nk) continue;
+    kt = 0;
+    // ---- logits of vocabulary tile t: z = acc / tau (log2 units), running statistics --------
+    const int v0 = v_begin + t * BN;
+    ++t;
 #pragma unroll
     for (int i = 0; i < G::FM; ++i) {
       const int rb = m0 + G::row_of(i, 0);       // first of this lane's 4 consecutive rows
@@ -101,25 +139,26 @@ __global__ __launch_bounds__(256) void lmhead_sampler_kernel(SampArgs p, int n_m
         wd[j][0] = w.x; wd[j][1] = w.y; wd[j][2] = w.z; wd[j][3] = w.w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) z[j][e] = vv[j] < v_end ? acc[i][j][e] * p.zscale_log2 : -INFINITY;
+        acc[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        RowState& s = st[i][e];
+        RowState& rs = st[i][e];
         float zmax = z[0][e];
         int vmax = vv[0];
 #pragma unroll
         for (int j = 1; j < G::FN; ++j)
           if (z[j][e] > zmax) { zmax = z[j][e]; vmax = vv[j]; }
-        if (zmax > s.m2) {
-          s.s = s.m2 == -INFINITY ? 0.f : s.s * exp2f(s.m2 - zmax);
-          s.m2 = zmax;
-          s.a = vmax;
+        if (zmax > rs.m2) {
+          rs.s = rs.m2 == -INFINITY ? 0.f : rs.s * exp2f(rs.m2 - zmax);
+          rs.m2 = zmax;
+          rs.a = vmax;
         }
 #pragma unroll
         for (int j = 0; j < G::FN; ++j) {
-          if (z[j][e] != -INFINITY) s.s += exp2f(z[j][e] - s.m2);
+          if (z[j][e] != -INFINITY) rs.s += exp2f(z[j][e] - rs.m2);
           const float key = vv[j] < v_end ? gumbel_key2(z[j][e], wd[j][e]) : -INFINITY;
-          if (key > s.g2) { s.g2 = key; s.y = vv[j]; }
+          if (key > rs.g2) { rs.g2 = key; rs.y = vv[j]; }
         }
       }
     }
@@ -170,26 +209,23 @@ __global__ __launch_bounds__(256) void lmhead_sampler_kernel(SampArgs p, int n_m
   (void)wm;
 }
 
-constexpr int SBM = 128, SBN = 128;
-
-hipError_t launch_lmhead_sampler(const SampArgs& a, int act_bf16, hipStream_t s) {
-  const int n_mt = (a.rows + SBM - 1) / SBM;
-  const int slices8 = (a.slices + 7) / 8 * 8;
-  const int blocks = n_mt * slices8;
-  if (act_bf16) {
-    using G = GemmDma<bf16_t, SBM, SBN, 2, 2, 3>;
-    size_t lds = G::LDS_BYTES > 2 * SBM * PART * 4 ? G::LDS_BYTES : 2 * SBM * PART * 4;
-    static const hipError_t attr = allow_lds(lmhead_sampler_kernel<bf16_t, SBM, SBN, 2, 2>, lds);
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((lmhead_sampler_kernel<bf16_t, SBM, SBN, 2, 2>), dim3(blocks), dim3(256), lds, s, a, n_mt);
-  } else {
-    using G = GemmDma<float, SBM, SBN, 2, 2, 3>;
-    size_t lds = G::LDS_BYTES > 2 * SBM * PART * 4 ? G::LDS_BYTES : 2 * SBM * PART * 4;
-    static const hipError_t attr = allow_lds(lmhead_sampler_kernel<float, SBM, SBN, 2, 2>, lds);
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((lmhead_sampler_kernel<float, SBM, SBN, 2, 2>), dim3(blocks), dim3(256), lds, s, a, n_mt);
-  }
+template <class TA, int BM, int BN, int WM, int WN, int NS>
+static hipError_t launch_sampler_t(const SampArgs& a, hipStream_t s) {
+  using G = GemmDma<TA, BM, BN, WM, WN, NS>;
+  const int n_mt = (a.rows + BM - 1) / BM;
+  const int blocks = n_mt * ((a.slices + 7) / 8 * 8);
+  const size_t lds = G::LDS_BYTES > (size_t)WN * BM * PART * 4 ? G::LDS_BYTES : (size_t)WN * BM * PART * 4;
+  static const hipError_t attr = allow_lds(lmhead_sampler_kernel<TA, BM, BN, WM, WN, NS>, lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((lmhead_sampler_kernel<TA, BM, BN, WM, WN, NS>), dim3(blocks), dim3(WM * WN * 64), lds, s, a,
+                     n_mt);
   return hipGetLastError();
+}
+
+// tiles: bf16 128 rows x 256 vocabulary entries, 8 waves (4 x 2); fp32 128 x 128, 4 waves
+hipError_t launch_lmhead_sampler(const SampArgs& a, int act_bf16, hipStream_t s) {
+  if (act_bf16) return launch_sampler_t<bf16_t, SAMPLER_BM, SAMPLER_BN_BF16, 4, 2, 3>(a, s);
+  return launch_sampler_t<float, SAMPLER_BM, SAMPLER_BN_F32, 2, 2, 3>(a, s);
 }
 
 // ------------------------------------------------------------------ partials from given logits --

@@ -64,7 +64,6 @@ constexpr size_t ALIGN = 256;
 constexpr int MAX_SPLITS = 16;
 constexpr int MAX_RSPLIT = 16;   // split-K parts of the router GEMM
 constexpr int MAX_KSPLIT = 8;    // split-K parts of the O projection and the shared-expert down GEMM
-constexpr int SAMP_BM = 128, SAMP_BN = 128;
 
 inline size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 inline int up8(int x) { return (x + 7) / 8 * 8; }
@@ -77,13 +76,16 @@ inline bool is_global(const dg_model_desc& d, int l) {
 }
 
 int sampler_slices(const dg_model_desc& d, int rows, int* v_per_slice) {
-  const int n_mt = (rows + SAMP_BM - 1) / SAMP_BM;
-  const int tiles = (d.vocab + SAMP_BN - 1) / SAMP_BN;
-  int want = (1024 + n_mt - 1) / n_mt;
+  // one block per (slice, row tile), about one block per CU: each block streams its slice's
+  // vocabulary tiles through one continuous ring
+  const int bn = d.act_dtype == DG_BF16 ? SAMPLER_BN_BF16 : SAMPLER_BN_F32;
+  const int n_mt = (rows + SAMPLER_BM - 1) / SAMPLER_BM;
+  const int tiles = (d.vocab + bn - 1) / bn;
+  int want = (256 + n_mt - 1) / n_mt;
   if (want > tiles) want = tiles;
   if (want < 1) want = 1;
   const int tiles_per = (tiles + want - 1) / want;
-  *v_per_slice = tiles_per * SAMP_BN;
+  *v_per_slice = tiles_per * bn;
   return (d.vocab + *v_per_slice - 1) / *v_per_slice;
 }
 
