@@ -51,58 +51,83 @@ hipError_t launch_rmsnorm(const float* x, const void* g, void* y, int rows, int 
 }
 
 // resid += sum_s parts[s] (split-K partials, in part order); y = RMSNorm(resid) * g.  One block per
-// row; the updated row stays in registers between the two passes (d <= 256 * RN_MAX).
-constexpr int RN_MAX = 16;
+// row and one thread per 4 columns (d / 4 threads rounded up to whole waves, d <= 4096), so a row's
+// loads are spread over up to 16 waves and every load of a thread issues before its sums.
 constexpr int MAX_PARTS_ADD = 8;
-template <class T>
-__global__ __launch_bounds__(256) void resid_add_rmsnorm_kernel(float* resid, const float* parts, int nparts,
-                                                                int64_t pstride, const T* g, T* y, int d, float eps,
-                                                                int* status) {
-  const int r = blockIdx.x;
-  float* xr = resid + (int64_t)r * d;
-  float v[RN_MAX];
-  float ss = 0.f;
-#pragma unroll
-  for (int j = 0; j < RN_MAX; ++j) {
-    const int c = threadIdx.x + 256 * j;
-    v[j] = 0.f;
-    if (c < d) {
-      // every partial load issues before the in-order sum (clamped part index, always valid)
-      float pv[MAX_PARTS_ADD];
-#pragma unroll
-      for (int q = 0; q < MAX_PARTS_ADD; ++q) pv[q] = parts ? parts[min(q, max(nparts - 1, 0)) * pstride + (int64_t)r * d + c] : 0.f;
-      float a = xr[c];
-#pragma unroll
-      for (int q = 0; q < MAX_PARTS_ADD; ++q)
-        if (q < nparts) a += pv[q];
-      if (nparts > 0) xr[c] = a;
-      v[j] = a;
-      ss += a * a;
-    }
-  }
-  ss = wave_sum(ss);
-  __shared__ float part[4];
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+DG_DEV float block_sum_f(float v, float* red) {
+  v = wave_sum(v);
+  const int nw = (blockDim.x + 63) >> 6;
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  const float tot = part[0] + part[1] + part[2] + part[3];
+  float tot = 0.f;
+  for (int w = 0; w < nw; ++w) tot += red[w];   // fixed order: every thread gets the same sum
+  return tot;
+}
+
+template <class T>
+DG_DEV void store4(T* dst, f32x4_v v);
+template <>
+DG_DEV void store4<float>(float* dst, f32x4_v v) { *reinterpret_cast<f32x4_v*>(dst) = v; }
+template <>
+DG_DEV void store4<bf16_t>(bf16_t* dst, f32x4_v v) {
+  uint2 w;
+  w.x = pack_bf2(v[0], v[1]);
+  w.y = pack_bf2(v[2], v[3]);
+  *reinterpret_cast<uint2*>(dst) = w;
+}
+template <class T>
+DG_DEV f32x4_v load4(const T* src);
+template <>
+DG_DEV f32x4_v load4<float>(const float* src) { return *reinterpret_cast<const f32x4_v*>(src); }
+template <>
+DG_DEV f32x4_v load4<bf16_t>(const bf16_t* src) {
+  const uint2 w = *reinterpret_cast<const uint2*>(src);
+  return f32x4_v{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+                 __uint_as_float(w.y & 0xffff0000u)};
+}
+
+// NP = number of partials, a compile-time constant so the loads stay in registers
+template <class T, int NP>
+__global__ __launch_bounds__(1024) void resid_add_rmsnorm_kernel(float* resid, const float* parts, int64_t pstride,
+                                                                 const T* g, T* y, int d, float eps, int* status) {
+  __shared__ float red[16];
+  const int r = blockIdx.x;
+  const int c = threadIdx.x * 4;
+  f32x4_v a = {0.f, 0.f, 0.f, 0.f};
+  if (c < d) {
+    float* xr = resid + (int64_t)r * d + c;
+    f32x4_v pv[NP > 0 ? NP : 1];
+#pragma unroll
+    for (int q = 0; q < NP; ++q) pv[q] = *reinterpret_cast<const f32x4_v*>(parts + q * pstride + (int64_t)r * d + c);
+    a = *reinterpret_cast<const f32x4_v*>(xr);
+#pragma unroll
+    for (int q = 0; q < NP; ++q) a += pv[q];
+    if constexpr (NP > 0) *reinterpret_cast<f32x4_v*>(xr) = a;
+  }
+  const float tot = block_sum_f(a[0] * a[0] + a[1] * a[1] + a[2] * a[2] + a[3] * a[3], red);
   const float inv = rsqrtf(tot / (float)d + eps);
   if (threadIdx.x == 0 && status && !isfinite(tot)) atomicOr(status, 2);
-#pragma unroll
-  for (int j = 0; j < RN_MAX; ++j) {
-    const int c = threadIdx.x + 256 * j;
-    if (c < d) y[(int64_t)r * d + c] = Elem<T>::from_f(v[j] * inv * Elem<T>::to_f(g[c]));
+  if (c < d) store4<T>(y + (int64_t)r * d + c, a * inv * load4<T>(g + c));
+}
+
+template <class T, int NP>
+static void launch_ran(dim3 grid, dim3 block, hipStream_t s, float* resid, const float* parts, int nparts,
+                       int64_t pstride, const void* g, void* y, int d, float eps, int* status) {
+  if constexpr (NP < MAX_PARTS_ADD) {
+    if (nparts > NP) return launch_ran<T, NP + 1>(grid, block, s, resid, parts, nparts, pstride, g, y, d, eps, status);
   }
+  hipLaunchKernelGGL((resid_add_rmsnorm_kernel<T, NP>), grid, block, 0, s, resid, parts, pstride, (const T*)g, (T*)y,
+                     d, eps, status);
 }
 
 hipError_t launch_resid_add_rmsnorm(float* resid, const float* parts, int nparts, int64_t pstride, const void* g,
                                     void* y, int rows, int d, float eps, int bf, int* status, hipStream_t s) {
-  if (d > 256 * RN_MAX || nparts < 0 || nparts > MAX_PARTS_ADD) return hipErrorInvalidValue;
-  if (bf)
-    hipLaunchKernelGGL(resid_add_rmsnorm_kernel<bf16_t>, dim3(rows), dim3(256), 0, s, resid, parts, nparts, pstride,
-                       (const bf16_t*)g, (bf16_t*)y, d, eps, status);
-  else
-    hipLaunchKernelGGL(resid_add_rmsnorm_kernel<float>, dim3(rows), dim3(256), 0, s, resid, parts, nparts, pstride,
-                       (const float*)g, (float*)y, d, eps, status);
+  if (d % 4 || d > 4096 || nparts < 0 || nparts > MAX_PARTS_ADD) return hipErrorInvalidValue;
+  const uintptr_t al = bf ? 7 : 15;   // 4-column vector accesses of g and y
+  if (((uintptr_t)g & al) || ((uintptr_t)y & al)) return hipErrorInvalidValue;
+  const dim3 block((d / 4 + 63) / 64 * 64);
+  if (bf) launch_ran<bf16_t, 0>(dim3(rows), block, s, resid, parts, nparts, pstride, g, y, d, eps, status);
+  else launch_ran<float, 0>(dim3(rows), block, s, resid, parts, nparts, pstride, g, y, d, eps, status);
   return hipGetLastError();
 }
 

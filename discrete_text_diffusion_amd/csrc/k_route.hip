@@ -9,31 +9,32 @@ namespace dg {
 
 constexpr int MAX_PARTS = 16;   // split-K parts of the router GEMM
 
-// One wave per row; E <= 256 (4 values per lane), k <= 16.  The router logits arrive as
-// `nparts` split-K partial sums, added in part order (deterministic), plus the optional bias.
+// One wave (one block) per row; lane l holds experts 4l .. 4l+3 (E <= 256, E % 4 == 0), k <= 16.
+// The router logits arrive as `nparts` split-K partial sums, added in part order (deterministic),
+// plus the optional bias.
 template <int K>
-__global__ __launch_bounds__(256) void router_topk_kernel(const float* parts, int nparts, int64_t part_stride,
-                                                          const float* bias, int T, int E, int k, float* logits_out,
-                                                          int32_t* idx, float* gates) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  float v[4];
+__global__ __launch_bounds__(64) void router_topk_kernel(const float* parts, int nparts, int64_t part_stride,
+                                                         const float* bias, int T, int E, int k, float* logits_out,
+                                                         int32_t* idx, float* gates) {
+  const int lane = threadIdx.x;
+  const int t = blockIdx.x;
+  const int e0 = 4 * lane;
+  const bool on = e0 < E;
+  float v[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  if (on) {
+    const float* src = parts + (int64_t)t * E + e0;
+    f32x4_v pv[MAX_PARTS];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = lane + 64 * j;
-    // all partial loads issue back to back (clamped index, always valid); summed in part order
-    const int ec = min(e, E - 1);
-    float pv[MAX_PARTS];
-#pragma unroll
-    for (int p = 0; p < MAX_PARTS; ++p) pv[p] = parts[min(p, nparts - 1) * part_stride + (int64_t)t * E + ec];
-    float acc = pv[0];
+    for (int p = 0; p < MAX_PARTS; ++p)
+      if (p < nparts) pv[p] = *reinterpret_cast<const f32x4_v*>(src + p * part_stride);
+    f32x4_v acc = pv[0];
 #pragma unroll
     for (int p = 1; p < MAX_PARTS; ++p)
       if (p < nparts) acc += pv[p];
-    if (bias) acc += bias[ec];
-    if (e < E && logits_out) logits_out[(int64_t)t * E + e] = acc;
-    v[j] = e < E ? acc : -INFINITY;
+    if (bias) acc += *reinterpret_cast<const f32x4_v*>(bias + e0);
+    if (logits_out) *reinterpret_cast<f32x4_v*>(logits_out + (int64_t)t * E + e0) = acc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = acc[j];
   }
   // NaN scores count as -inf; an explicit taken mask keeps the k picks distinct even when fewer
   // than k scores are finite (untaken entries always beat taken ones)
@@ -51,7 +52,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* parts, in
     int bi = 0x7fffffff;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
+      const int e = e0 + j;
       if (e < E && !(taken >> j & 1u) && (v[j] > bv || bi == 0x7fffffff)) { bv = v[j]; bi = e; }
     }
 #pragma unroll
@@ -63,9 +64,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* parts, in
     bi = min(max(bi, 0), E - 1);
     sel_v[s] = bv;
     sel_i[s] = bi;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (bi == lane + 64 * j) taken |= 1u << j;
+    if ((bi >> 2) == lane) taken |= 1u << (bi & 3);
   }
   if (lane == 0) {
     const float mx = sel_v[0];
@@ -84,13 +83,16 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* parts, in
 
 hipError_t launch_router_topk(const float* parts, int nparts, int64_t part_stride, const float* bias, int T, int E,
                               int k, float* logits_out, int32_t* idx, float* gates, hipStream_t s) {
-  const dim3 grid((T + 3) / 4);
+  if (E > 256 || E % 4 || k > 16 || nparts < 1 || nparts > MAX_PARTS || part_stride % 4) return hipErrorInvalidValue;
+  if (((uintptr_t)parts & 15) || ((uintptr_t)bias & 15) || ((uintptr_t)logits_out & 15)) return hipErrorInvalidValue;
+  if (T == 0) return hipSuccess;
+  const dim3 grid(T);
   if (k <= 2)
-    hipLaunchKernelGGL(router_topk_kernel<2>, grid, dim3(256), 0, s, parts, nparts, part_stride, bias, T, E, k, logits_out, idx, gates);
+    hipLaunchKernelGGL(router_topk_kernel<2>, grid, dim3(64), 0, s, parts, nparts, part_stride, bias, T, E, k, logits_out, idx, gates);
   else if (k <= 8)
-    hipLaunchKernelGGL(router_topk_kernel<8>, grid, dim3(256), 0, s, parts, nparts, part_stride, bias, T, E, k, logits_out, idx, gates);
+    hipLaunchKernelGGL(router_topk_kernel<8>, grid, dim3(64), 0, s, parts, nparts, part_stride, bias, T, E, k, logits_out, idx, gates);
   else
-    hipLaunchKernelGGL(router_topk_kernel<16>, grid, dim3(256), 0, s, parts, nparts, part_stride, bias, T, E, k, logits_out, idx, gates);
+    hipLaunchKernelGGL(router_topk_kernel<16>, grid, dim3(64), 0, s, parts, nparts, part_stride, bias, T, E, k, logits_out, idx, gates);
   return hipGetLastError();
 }
 

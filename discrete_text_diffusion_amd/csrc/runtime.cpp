@@ -242,7 +242,8 @@ struct Pass {
 
 // Block tiles the dense GEMM launcher picks for M rows (mirrors k_gemm.hip's dense_pick).
 int dense_blocks(int M, int N) {
-  const int bm = M > 256 ? 128 : (M > 64 ? 128 : 64), bn = M > 256 ? 128 : 64;
+  int bm = M > 256 ? 128 : (M > 64 ? 128 : 64), bn = M > 256 ? 128 : 64;
+  if (M > 64 && M <= 256 && N <= 256) bm = 64, bn = 32;
   return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
 }
 
@@ -446,8 +447,8 @@ dg_status check_desc(const dg_model_desc& d) {
     return fail(DG_EUNSUPPORTED, "d_model, expert_hidden and shared_hidden must be multiples of 64");
   if (d.d_model > 4096) return fail(DG_EUNSUPPORTED, "d_model %d > 4096", d.d_model);
   if (d.vocab % 16) return fail(DG_EUNSUPPORTED, "vocab %% 16 != 0");
-  if (d.n_experts > 256 || d.top_k > 16 || d.top_k > d.n_experts)
-    return fail(DG_EUNSUPPORTED, "need top_k <= 16 and top_k <= n_experts <= 256");
+  if (d.n_experts > 256 || d.n_experts % 4 || d.top_k > 16 || d.top_k > d.n_experts)
+    return fail(DG_EUNSUPPORTED, "need top_k <= 16, top_k <= n_experts <= 256 and n_experts %% 4 == 0");
   if (d.act_dtype != DG_F32 && d.act_dtype != DG_BF16) return fail(DG_EUNSUPPORTED, "act_dtype must be F32 or BF16");
   if (!(d.expert_dtype == d.act_dtype || (d.act_dtype == DG_BF16 && d.expert_dtype == DG_FP8E4M3)))
     return fail(DG_EUNSUPPORTED, "expert_dtype must equal act_dtype, or be FP8E4M3 with BF16 activations");
@@ -521,7 +522,13 @@ dg_status dg_create(const dg_model_desc* desc, const dg_weights* wts, dg_ctx** o
       return fail(DG_EINVAL, "weights: layer %d has a NULL matrix", l);
     if (fp8 && (!L.s_gate || !L.s_up || !L.s_down || !L.sh_s_gate || !L.sh_s_up || !L.sh_s_down))
       return fail(DG_EINVAL, "weights: layer %d: FP8 experts need every scale", l);
+    const void* ptrs[] = {L.attn_norm, L.w_qkv, L.w_o, L.ffn_norm, L.w_router, L.router_bias, L.w_gate, L.w_up,
+                          L.w_down, L.sh_gate, L.sh_up, L.sh_down};
+    for (const void* q : ptrs)
+      if ((uintptr_t)q & 15) return fail(DG_EINVAL, "weights: layer %d has a pointer that is not 16-byte aligned", l);
   }
+  if (((uintptr_t)wts->final_norm & 15) || ((uintptr_t)wts->embed & 15))
+    return fail(DG_EINVAL, "weights: embed / final_norm not 16-byte aligned");
   dg_ctx* c = new dg_ctx;
   c->d = *desc;
   c->layers.assign(wts->layers, wts->layers + desc->n_layers);
@@ -752,6 +759,7 @@ dg_status dg_test_router_topk(const float* scores, int32_t T, int32_t E, int32_t
                               hipStream_t stream) {
   g_err.clear();
   if (!scores || T < 1 || E < 1 || E > 256 || k < 1 || k > 16 || k > E) return fail(DG_EINVAL, "bad argument");
+  if (E % 4) return fail(DG_EUNSUPPORTED, "E %% 4 != 0");
   // scratch: idx, gates, counts, offsets, perm, inv_perm, tok, work, n_items
   const size_t A = (size_t)T * k;
   const int max_items = (int)((A + GROUP_BM - 1) / GROUP_BM) + E;

@@ -17,6 +17,7 @@
  * Conventions for every call:
  *   - Pointers named as device pointers must point to device memory allocated by the caller;
  *     descriptors, parameter structs, pointer tables and `cap`/`prefix_len` are host memory.
+ *     Weight pointers must be 16-byte aligned (dg_create checks), as every allocator's are.
  *   - The library never allocates device memory.  All scratch lives in the caller's workspace
  *     (`ws`, at least dg_workspace_bytes() bytes, 256-byte aligned).  One workspace must not be
  *     used by two streams at once.
@@ -59,7 +60,8 @@ typedef enum {
 /* Model shape.  Layer l (0-based) is global iff window <= 0, global_every <= 0 or
  * (l + 1) % global_every == 0; other layers are local (sliding window `window`).
  * Supported: head_dim in {64, 128, 256}; n_q_heads % n_kv_heads == 0; d_model, expert_hidden
- * and shared_hidden multiples of 64; vocab % 16 == 0; top_k <= n_experts <= 256, top_k <= 16; act_dtype F32 or BF16;
+ * and shared_hidden multiples of 64; vocab % 16 == 0; top_k <= n_experts <= 256, n_experts % 4 == 0, top_k <= 16;
+ * act_dtype F32 or BF16;
  * expert_dtype = act_dtype, or FP8E4M3 when act_dtype is BF16 (weights-only fp8, bf16 math). */
 typedef struct {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim;
