@@ -91,7 +91,7 @@ __global__ __launch_bounds__(WM * WN * 64) void lmhead_sampler_kernel(SampArgs p
     for (int i = 0; i < G::IB; ++i) {
       const int r = (wave + NW * i) * 8 + rr;
       const int v = min(v0 + r, v_end - 1);
-      dma16(E + (int64_t)v * p.d * sizeof(TA) + ((slot ^ ((r >> 1) & 7)) * 16) + koff,
+      dma16<DMA_STREAM>(E + (int64_t)v * p.d * sizeof(TA) + ((slot ^ ((r >> 1) & 7)) * 16) + koff,
             st + BM * 128 + (wave + NW * i) * 8 * 128);
     }
     if (++it_k == nk) { it_k = 0; ++it_t; }
