@@ -254,44 +254,62 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs p) {
   }
 }
 
-// merge split partials in split order: o = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M); every
-// partial of a thread is loaded before the sums (clamped split index, always valid)
+// merge split partials in split order: o = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).  S (the
+// split count) is a compile-time constant, so every partial of a thread is loaded before the sums
+// and nothing beyond the S partials is read.
 constexpr int MERGE_MAX = 16;
 template <class T>
-__global__ void attn_merge_kernel(AttnArgs p) {
+DG_DEV void put4(T* dst, f32x4_v v);
+template <>
+DG_DEV void put4<float>(float* dst, f32x4_v v) { *reinterpret_cast<f32x4_v*>(dst) = v; }
+template <>
+DG_DEV void put4<bf16_t>(bf16_t* dst, f32x4_v v) {
+  uint2 w;
+  w.x = pack_bf2(v[0], v[1]);
+  w.y = pack_bf2(v[2], v[3]);
+  *reinterpret_cast<uint2*>(dst) = w;
+}
+
+template <class T, int S>
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p) {
   const int64_t rows = (int64_t)p.B * p.n * p.Hq;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (row, head, d/4)
   const int dq = p.dh / 4;
   if (idx >= rows * dq) return;
   const int64_t rh = idx / dq;
   const int d4 = (int)(idx - rh * dq) * 4;
-  const int S = p.splits;
-  float mv[MERGE_MAX], lv[MERGE_MAX];
-  f32x4_v ov[MERGE_MAX];
+  float mv[S], lv[S];
+  f32x4_v ov[S];
 #pragma unroll
-  for (int s = 0; s < MERGE_MAX; ++s) {
-    const int64_t sr = (int64_t)min(s, S - 1) * rows + rh;
-    mv[s] = p.part_ml[sr * 2];
-    lv[s] = p.part_ml[sr * 2 + 1];
+  for (int s = 0; s < S; ++s) {
+    const int64_t sr = (int64_t)s * rows + rh;
+    const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + sr * 2);
+    mv[s] = ml.x;
+    lv[s] = ml.y;
     ov[s] = *reinterpret_cast<const f32x4_v*>(p.part_o + sr * p.dh + d4);
   }
   float M = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < MERGE_MAX; ++s)
-    if (s < S) M = fmaxf(M, mv[s]);
+  for (int s = 0; s < S; ++s) M = fmaxf(M, mv[s]);
   float L = 0.f;
   f32x4_v o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < MERGE_MAX; ++s) {
-    if (s >= S || mv[s] == -INFINITY) continue;
+  for (int s = 0; s < S; ++s) {
+    if (mv[s] == -INFINITY) continue;
     const float w = exp2f(mv[s] - M);
     L += lv[s] * w;
     o += ov[s] * w;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  T* out = static_cast<T*>(p.out) + rh * p.dh + d4;
-  out[0] = Elem<T>::from_f(o[0] * inv); out[1] = Elem<T>::from_f(o[1] * inv);
-  out[2] = Elem<T>::from_f(o[2] * inv); out[3] = Elem<T>::from_f(o[3] * inv);
+  put4<T>(static_cast<T*>(p.out) + rh * p.dh + d4, o * inv);
+}
+
+template <class T, int S>
+static void launch_merge_s(const AttnArgs& a, int blocks, hipStream_t s) {
+  if constexpr (S < MERGE_MAX) {
+    if (a.splits > S) return launch_merge_s<T, S + 1>(a, blocks, s);
+  }
+  hipLaunchKernelGGL((attn_merge_kernel<T, S>), dim3(blocks), dim3(256), 0, s, a);
 }
 
 template <class T, int DH>
@@ -316,10 +334,11 @@ hipError_t launch_attention(const AttnArgs& a, int act_bf16, hipStream_t s) {
 }
 
 hipError_t launch_attn_merge(const AttnArgs& a, int act_bf16, hipStream_t s) {
+  if (a.splits < 2 || a.splits > MERGE_MAX || a.dh % 4) return hipErrorInvalidValue;
   const int64_t n = (int64_t)a.B * a.n * a.Hq * (a.dh / 4);
   const int blocks = (int)((n + 255) / 256);
-  if (act_bf16) hipLaunchKernelGGL(attn_merge_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(attn_merge_kernel<float>, dim3(blocks), dim3(256), 0, s, a);
+  if (act_bf16) launch_merge_s<bf16_t, 2>(a, blocks, s);
+  else launch_merge_s<float, 2>(a, blocks, s);
   return hipGetLastError();
 }
 

@@ -219,9 +219,9 @@ hipError_t launch_rope_table(float2* tab, int rows, int rows_per_canvas, int hea
 // XCD, one L2 copy of that weight tile).  Blocks [sh_blocks, ...): routed tiles, block -
 // sh_blocks = item * nt_r + column tile; work item w < *n_items: expert e = work[2w], first row
 // m0 = work[2w+1] of that expert's rows [offsets[e], offsets[e] + counts[e]) in grouped order.
-template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI>
-__global__ __launch_bounds__(256) void gemm_grouped_kernel(GroupedArgs p) {
-  using G = TileFor<TA, TB, BM, BN, WM, WN>;
+template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI, int NS = 0>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_grouped_kernel(GroupedArgs p) {
+  using G = TileFor<TA, TB, BM, BN, WM, WN, NS>;
   extern __shared__ __align__(16) char lds[];
   const int id = blockIdx.x;
   const bool shared = id < p.sh_blocks;
@@ -389,18 +389,18 @@ hipError_t launch_dense(const DenseArgs& a, int act_bf16, int w_kind, hipStream_
   return dense_dispatch<bf16_t, bf16_t>(a, s);
 }
 
-template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI>
+template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI, int NS = 0>
 static hipError_t launch_grouped_t(GroupedArgs a, int n_eff, int sh_eff, int max_items, hipStream_t s) {
-  using G = TileFor<TA, TB, BM, BN, WM, WN>;
+  using G = TileFor<TA, TB, BM, BN, WM, WN, NS>;
   a.nt_r = (n_eff + BN - 1) / BN;
   a.nt_s = (sh_eff + BN - 1) / BN;
   a.n_sh_items = a.shB ? (a.sh_rows + BM - 1) / BM : 0;
   a.sh_blocks = (a.nt_s + 7) / 8 * a.n_sh_items * 8;
   const int blocks = a.sh_blocks + max_items * a.nt_r;
   if (blocks == 0) return hipSuccess;
-  static const hipError_t attr = allow_lds(gemm_grouped_kernel<TA, TB, BM, BN, WM, WN, EPI>, G::LDS_BYTES);
+  static const hipError_t attr = allow_lds(gemm_grouped_kernel<TA, TB, BM, BN, WM, WN, EPI, NS>, G::LDS_BYTES);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((gemm_grouped_kernel<TA, TB, BM, BN, WM, WN, EPI>), dim3(blocks), dim3(256),
+  hipLaunchKernelGGL((gemm_grouped_kernel<TA, TB, BM, BN, WM, WN, EPI, NS>), dim3(blocks), dim3(WM * WN * 64),
                      G::LDS_BYTES, s, a);
   return hipGetLastError();
 }
