@@ -39,10 +39,10 @@ def parse():
 
 # HBM bytes of one MoE gate/up launch on this workload, from two rocprofv3 --pmc passes
 # (FETCH_SIZE, WRITE_SIZE; KiB per dispatch, mean of 90 launches), each scaled by the same counter
-# on a 512 MiB device-to-device copy (FETCH_SIZE reads 262155.6 KiB for 524288 KiB read: x1.9999;
+# on a 512 MiB device-to-device copy (FETCH_SIZE reads 262155.5 KiB for 524288 KiB read: x1.9999;
 # WRITE_SIZE reads 524288 KiB: x1).  Valid only while the kernel sources hash to `sources`.
-MOE_TRAFFIC = {"sources": "880173230ae08c08cce246cb3b82a1d34e9b960cfe4bdd4fb397702aced9ff58",
-               "fetch_kib": 557366.1, "write_kib": 3872.2, "bytes_per_launch": 1145400288}
+MOE_TRAFFIC = {"sources": "2f3f983d82dacdd648790b439137b7802adaad7cf9b5a070cfd46882838e5a5d",
+               "fetch_kib": 533379.5, "write_kib": 3872.1, "bytes_per_launch": 1096278366}
 TRAFFIC_SOURCES = ("k_gemm.hip", "gemm_dma.h", "gemm_core.h", "common.h", "internal.h")
 
 
