@@ -12,6 +12,7 @@ Every random number the method draws is one 32-bit word of one Philox block.  St
     uniform canvas token at t = 1 for (b, i)     ctr = (i >> 2, 0, 0, b << 8 | 2), word i & 3
     forward-noise keep test (b, i) at step s     ctr = (i >> 2, 0, s, b << 8 | 3), word i & 3
     forward-noise token (b, i) at step s         ctr = (i >> 2, 0, s, b << 8 | 4), word i & 3
+    re-noise token of the entropy-bounded step   ctr = (i >> 2, 0, s, b << 8 | 5), word i & 3
 key = (seed mod 2^32, seed >> 32).
 """
 from __future__ import annotations
@@ -24,7 +25,7 @@ WEYL0 = 0x9E3779B9
 WEYL1 = 0xBB67AE85
 MASK32 = 0xFFFFFFFF
 
-TAG_GUMBEL, TAG_JUMP, TAG_INIT, TAG_NOISE_KEEP, TAG_NOISE_TOKEN = 0, 1, 2, 3, 4
+TAG_GUMBEL, TAG_JUMP, TAG_INIT, TAG_NOISE_KEEP, TAG_NOISE_TOKEN, TAG_RENOISE = 0, 1, 2, 3, 4, 5
 
 
 def philox4x32_10(ctr, key):
@@ -111,3 +112,9 @@ def noise_words(seed, step, batch, length):
     keep = word(seed, i >> 2, 0, step, (b << 8) | TAG_NOISE_KEEP, i & 3)
     tok = word(seed, i >> 2, 0, step, (b << 8) | TAG_NOISE_TOKEN, i & 3)
     return keep, tok
+
+
+def renoise_tokens(seed, step, batch, length, vocab):
+    """Uniform replacement tokens of the entropy-bounded step s for every (b, i)."""
+    b, i = np.meshgrid(np.arange(batch), np.arange(length), indexing="ij")
+    return token(word(seed, i >> 2, 0, step, (b << 8) | TAG_RENOISE, i & 3), vocab)
