@@ -88,7 +88,7 @@ DG_DEV u32x4 philox(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t
   return u32x4{c0, c1, c2, c3};
 }
 
-enum : uint32_t { TAG_GUMBEL = 0, TAG_JUMP = 1, TAG_INIT = 2, TAG_NOISE_KEEP = 3, TAG_NOISE_TOKEN = 4 };
+enum : uint32_t { TAG_GUMBEL = 0, TAG_JUMP = 1, TAG_INIT = 2, TAG_NOISE_KEEP = 3, TAG_NOISE_TOKEN = 4, TAG_RENOISE = 5 };
 
 DG_DEV uint32_t pick(const u32x4& w, int j) {
   return j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : w.w;

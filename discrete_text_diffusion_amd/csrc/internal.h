@@ -119,6 +119,7 @@ struct SampArgs {
 hipError_t launch_lmhead_sampler(const SampArgs& a, int act_bf16, hipStream_t s);
 // fused LM head tiles: rows x vocabulary entries per block step (bf16: 8 waves as 4 x 2)
 constexpr int SAMPLER_BM = 128, SAMPLER_BN_BF16 = 256, SAMPLER_BN_F32 = 128;
+constexpr int SAMPLER_PART = 6;   // floats per (row, slice) partial: m2, s, a, g2, y, w
 hipError_t launch_logits_partials(const float* z, int rows, int V, int L, float zscale_log2,
                                   uint32_t k0, uint32_t k1, uint32_t step, int slices,
                                   int v_per_slice, float* part, hipStream_t s);
@@ -129,12 +130,30 @@ struct StepArgs {
   int32_t* canvas; uint8_t* lock; int32_t* n_locked; const int32_t* done;
   float lam, theta;
   uint32_t k0, k1, step;
-  float* stats;                   // [rows][5]: m, a, c, y, best (a, y stored as int bits)
+  float* stats;                   // [rows][STAT_FIELDS]: m, a, c, y, best, H (a, y stored as int bits)
   int* status;
   int32_t* steps_taken;           // incremented for canvases that stepped (or null)
   int32_t* done_out;              // set when all positions locked (adaptive), or null
+  int stats_only;                 // merge and write stats; leave canvas / lock / counts alone
 };
+constexpr int STAT_FIELDS = 6;
 hipError_t launch_step_merge(const StepArgs& a, hipStream_t s);
+
+// entropy-bounded step over merged stats: one block per canvas (L <= 1024)
+struct EbArgs {
+  const float* stats;             // [B*L][STAT_FIELDS]
+  int B, L;
+  int32_t* canvas;                // [B][L] out (canvases not done)
+  int32_t* prev;                  // [B][L] argmax of the previous step (read if has_prev), then this step's
+  int32_t* done;                  // [B] inout
+  int32_t* n_accepted;            // [B] out, or null
+  float* mean_entropy;            // [B] out, or null
+  int32_t* steps_taken;           // [B] incremented for canvases that stepped, or null
+  float gamma, stop_entropy;
+  int has_prev, final_step, adaptive, vocab, vocab_log2;
+  uint32_t k0, k1, step;
+};
+hipError_t launch_eb_select(EbArgs a, hipStream_t s);
 
 hipError_t launch_init_canvas(int32_t* canvas, uint8_t* lock, int B, int L, int V, uint32_t k0,
                               uint32_t k1, hipStream_t s);

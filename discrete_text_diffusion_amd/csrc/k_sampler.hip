@@ -2,9 +2,11 @@
 //
 // Logits z = H . E^T / tau are produced tile by tile by the MFMA engine and consumed in
 // registers: per row the kernel keeps a running max and its argmax, the rescaled sum of
-// exp(z - max), and the best Gumbel-perturbed key z + G with its token (Gumbel-max sampling of
-// softmax(z)).  Nothing of size rows x vocab is ever written.  Everything is kept in the log2
-// domain (z2 = z * log2 e) so the exponentials are single exp2 instructions.
+// exp(z - max), the rescaled sum of exp(z - max) * (z - max) (for the entropy of softmax(z)),
+// and the best Gumbel-perturbed key z + G with its token (Gumbel-max sampling of softmax(z)).
+// Nothing of size rows x vocab is ever written.  Everything is kept in the log2 domain
+// (z2 = z * log2 e) so the exponentials are single exp2 instructions; with S = sum 2^(z2 - m2)
+// and W = sum 2^(z2 - m2) (z2 - m2), the entropy in nats is ln 2 * (log2 S - W / S).
 //
 // Each block owns one vocabulary slice for one row tile and writes one partial per row; the
 // Step kernel merges the partials of every slice in ascending slice order (deterministic), then
@@ -18,31 +20,48 @@ namespace dg {
 constexpr float LN2 = 0.69314718055994531f;
 // G * log2(e) = -log2(-log2(u)) - log2(ln 2)
 constexpr float NEG_LOG2_LN2 = 0.52876637294904302f;
-constexpr int PART = 5;  // m2, s, a, g2, y
+constexpr int PART = SAMPLER_PART;  // m2, s, a, g2, y, w
 
 struct RowState {
-  float m2, s, g2;
+  float m2, s, g2, w;
   int a, y;
 };
 
 DG_DEV void state_init(RowState& st) {
-  st.m2 = -INFINITY; st.s = 0.f; st.g2 = -INFINITY; st.a = 0x7fffffff; st.y = 0x7fffffff;
+  st.m2 = -INFINITY; st.s = 0.f; st.g2 = -INFINITY; st.w = 0.f; st.a = 0x7fffffff; st.y = 0x7fffffff;
 }
 
-// merge b into a; ties in the max (or the Gumbel key) go to the lower token id
-DG_DEV void state_merge(RowState& a, float m2, float s, int ai, float g2, int y) {
+// merge b into a; ties in the max (or the Gumbel key) go to the lower token id.  Moving a sum
+// from max m to max mn: S' = S 2^(m - mn), W' = 2^(m - mn) (W + (m - mn) S).
+DG_DEV void state_merge(RowState& a, float m2, float s, float w, int ai, float g2, int y) {
   const float mn = fmaxf(a.m2, m2);
-  float sa = a.s, sb = s;
+  float sa = a.s, sb = s, wa = a.w, wb = w;
   if (mn != -INFINITY) {
-    sa = a.m2 == -INFINITY ? 0.f : a.s * exp2f(a.m2 - mn);
-    sb = m2 == -INFINITY ? 0.f : s * exp2f(m2 - mn);
+    if (a.m2 == -INFINITY) {
+      sa = 0.f; wa = 0.f;
+    } else {
+      const float f = exp2f(a.m2 - mn);
+      wa = f * (a.w + (a.m2 - mn) * a.s);
+      sa = a.s * f;
+    }
+    if (m2 == -INFINITY) {
+      sb = 0.f; wb = 0.f;
+    } else {
+      const float f = exp2f(m2 - mn);
+      wb = f * (w + (m2 - mn) * s);
+      sb = s * f;
+    }
   }
   const bool take = (m2 > a.m2) || (m2 == a.m2 && ai < a.a);
   a.s = sa + sb;
+  a.w = wa + wb;
   if (take) a.a = ai;
   a.m2 = mn;
   if ((g2 > a.g2) || (g2 == a.g2 && y < a.y)) { a.g2 = g2; a.y = y; }
 }
+
+// entropy in nats of softmax over a row, from the merged sums
+DG_DEV float row_entropy(const RowState& r) { return LN2 * (__log2f(r.s) - r.w / r.s); }
 
 DG_DEV float gumbel_key2(float z2, uint32_t w) {
   const float t1 = -__log2f(unit_oo(w));       // > 0
@@ -150,13 +169,24 @@ __global__ __launch_bounds__(WM * WN * 64) void lmhead_sampler_kernel(SampArgs p
         for (int j = 1; j < G::FN; ++j)
           if (z[j][e] > zmax) { zmax = z[j][e]; vmax = vv[j]; }
         if (zmax > rs.m2) {
-          rs.s = rs.m2 == -INFINITY ? 0.f : rs.s * exp2f(rs.m2 - zmax);
+          if (rs.m2 == -INFINITY) {
+            rs.s = 0.f; rs.w = 0.f;
+          } else {
+            const float f = exp2f(rs.m2 - zmax);
+            rs.w = f * (rs.w + (rs.m2 - zmax) * rs.s);
+            rs.s *= f;
+          }
           rs.m2 = zmax;
           rs.a = vmax;
         }
 #pragma unroll
         for (int j = 0; j < G::FN; ++j) {
-          if (z[j][e] != -INFINITY) rs.s += exp2f(z[j][e] - rs.m2);
+          if (z[j][e] != -INFINITY) {
+            const float dz = z[j][e] - rs.m2;
+            const float ex = exp2f(dz);
+            rs.s += ex;
+            rs.w += ex * dz;
+          }
           const float key = vv[j] < v_end ? gumbel_key2(z[j][e], wd[j][e]) : -INFINITY;
           if (key > rs.g2) { rs.g2 = key; rs.y = vv[j]; }
         }
@@ -173,9 +203,9 @@ __global__ __launch_bounds__(WM * WN * 64) void lmhead_sampler_kernel(SampArgs p
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) {
         const float m2 = __shfl_xor(s.m2, o, 64), ss = __shfl_xor(s.s, o, 64);
-        const float g2 = __shfl_xor(s.g2, o, 64);
+        const float g2 = __shfl_xor(s.g2, o, 64), ww = __shfl_xor(s.w, o, 64);
         const int a = __shfl_xor(s.a, o, 64), y = __shfl_xor(s.y, o, 64);
-        state_merge(s, m2, ss, a, g2, y);
+        state_merge(s, m2, ss, ww, a, g2, y);
       }
     }
   // then over the WN waves sharing a row range, through LDS (wave wn = 0 merges and writes)
@@ -190,7 +220,7 @@ __global__ __launch_bounds__(WM * WN * 64) void lmhead_sampler_kernel(SampArgs p
         const int r = G::row_of(i, e);
         float* q = xch + ((size_t)wn * BM + r) * PART;
         q[0] = st[i][e].m2; q[1] = st[i][e].s; q[2] = __int_as_float(st[i][e].a);
-        q[3] = st[i][e].g2; q[4] = __int_as_float(st[i][e].y);
+        q[3] = st[i][e].g2; q[4] = __int_as_float(st[i][e].y); q[5] = st[i][e].w;
       }
   }
   __syncthreads();
@@ -201,10 +231,10 @@ __global__ __launch_bounds__(WM * WN * 64) void lmhead_sampler_kernel(SampArgs p
     state_init(s);
     for (int w = 0; w < WN; ++w) {
       const float* q = xch + ((size_t)w * BM + r) * PART;
-      state_merge(s, q[0], q[1], __float_as_int(q[2]), q[3], __float_as_int(q[4]));
+      state_merge(s, q[0], q[1], q[5], __float_as_int(q[2]), q[3], __float_as_int(q[4]));
     }
     float* o = p.part + ((size_t)slice * p.rows + m) * PART;
-    o[0] = s.m2; o[1] = s.s; o[2] = __int_as_float(s.a); o[3] = s.g2; o[4] = __int_as_float(s.y);
+    o[0] = s.m2; o[1] = s.s; o[2] = __int_as_float(s.a); o[3] = s.g2; o[4] = __int_as_float(s.y); o[5] = s.w;
   }
   (void)wm;
 }
@@ -241,27 +271,29 @@ __global__ __launch_bounds__(256) void logits_partials_kernel(const float* z, in
   for (int v = v_begin + threadIdx.x; v < v_end; v += 256) {
     const float z2 = z[(int64_t)row * V + v] * zs;
     const u32x4 w = philox((uint32_t)v, (uint32_t)(ii >> 2), step, ((uint32_t)b << 8) | TAG_GUMBEL, k0, k1);
-    state_merge(st, z2, 1.f, v, gumbel_key2(z2, pick(w, ii & 3)), v);
+    state_merge(st, z2, 1.f, 0.f, v, gumbel_key2(z2, pick(w, ii & 3)), v);
   }
   for (int o = 1; o < 64; o <<= 1) {
     const float m2 = __shfl_xor(st.m2, o, 64), ss = __shfl_xor(st.s, o, 64), g2 = __shfl_xor(st.g2, o, 64);
+    const float ww = __shfl_xor(st.w, o, 64);
     const int a = __shfl_xor(st.a, o, 64), y = __shfl_xor(st.y, o, 64);
-    state_merge(st, m2, ss, a, g2, y);
+    state_merge(st, m2, ss, ww, a, g2, y);
   }
   __shared__ float xch[4][PART];
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
     xch[wave][0] = st.m2; xch[wave][1] = st.s; xch[wave][2] = __int_as_float(st.a);
-    xch[wave][3] = st.g2; xch[wave][4] = __int_as_float(st.y);
+    xch[wave][3] = st.g2; xch[wave][4] = __int_as_float(st.y); xch[wave][5] = st.w;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
     RowState s;
     state_init(s);
     for (int w = 0; w < 4; ++w)
-      state_merge(s, xch[w][0], xch[w][1], __float_as_int(xch[w][2]), xch[w][3], __float_as_int(xch[w][4]));
+      state_merge(s, xch[w][0], xch[w][1], xch[w][5], __float_as_int(xch[w][2]), xch[w][3],
+                  __float_as_int(xch[w][4]));
     float* o = part + ((size_t)slice * rows + row) * PART;
-    o[0] = s.m2; o[1] = s.s; o[2] = __int_as_float(s.a); o[3] = s.g2; o[4] = __int_as_float(s.y);
+    o[0] = s.m2; o[1] = s.s; o[2] = __int_as_float(s.a); o[3] = s.g2; o[4] = __int_as_float(s.y); o[5] = s.w;
   }
 }
 
@@ -297,26 +329,29 @@ __global__ __launch_bounds__(256) void step_merge_kernel(StepArgs p) {
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       if (base + 64 * u < p.slices)
-        state_merge(s, q[u][0], q[u][1], __float_as_int(q[u][2]), q[u][3], __float_as_int(q[u][4]));
+        state_merge(s, q[u][0], q[u][1], q[u][5], __float_as_int(q[u][2]), q[u][3], __float_as_int(q[u][4]));
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const float m2 = __shfl_xor(s.m2, o, 64), ss = __shfl_xor(s.s, o, 64), g2 = __shfl_xor(s.g2, o, 64);
+    const float ww = __shfl_xor(s.w, o, 64);
     const int a = __shfl_xor(s.a, o, 64), y = __shfl_xor(s.y, o, 64);
-    state_merge(s, m2, ss, a, g2, y);
+    state_merge(s, m2, ss, ww, a, g2, y);
   }
   if (lane != 0) return;
   const float c = 1.f / s.s;
-  const bool bad = !(isfinite(s.m2) && isfinite(s.s) && isfinite(s.g2));
+  const float H = row_entropy(s);
+  const bool bad = !(isfinite(s.m2) && isfinite(s.s) && isfinite(s.g2) && isfinite(H));
   if (p.stats) {
-    float* o = p.stats + (size_t)r * 5;
+    float* o = p.stats + (size_t)r * STAT_FIELDS;
     o[0] = s.m2 * LN2; o[1] = __int_as_float(s.a); o[2] = c; o[3] = __int_as_float(s.y);
-    o[4] = s.g2 * LN2;
+    o[4] = s.g2 * LN2; o[5] = H;
   }
   if (bad) {
     if (p.status) atomicOr(p.status, 1);
     return;
   }
+  if (p.stats_only) return;
   const bool is_done = p.done && p.done[b] != 0;
   if (is_done || p.lock[r]) return;
   if (c >= p.theta) {
@@ -337,7 +372,7 @@ __global__ __launch_bounds__(256) void step_count_kernel(StepArgs p) {
   for (int i = threadIdx.x; i < p.L; i += 256) {
     const int r = b * p.L + i;
     nl += p.lock[r] != 0;
-    if (p.stats) nb += !isfinite(p.stats[(size_t)r * 5 + 2]) || !isfinite(p.stats[(size_t)r * 5]);
+    if (p.stats) nb += !isfinite(p.stats[(size_t)r * STAT_FIELDS + 2]) || !isfinite(p.stats[(size_t)r * STAT_FIELDS]);
   }
   (void)rows;
   for (int o = 32; o > 0; o >>= 1) { nl += __shfl_xor(nl, o, 64); nb += __shfl_xor(nb, o, 64); }
@@ -358,7 +393,94 @@ __global__ __launch_bounds__(256) void step_count_kernel(StepArgs p) {
 hipError_t launch_step_merge(const StepArgs& a, hipStream_t s) {
   const int rows = a.B * a.L;
   hipLaunchKernelGGL(step_merge_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(step_count_kernel, dim3(a.B), dim3(256), 0, s, a);
+  if (!a.stats_only) hipLaunchKernelGGL(step_count_kernel, dim3(a.B), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ entropy-bounded step ---------
+// One block per canvas ([TR §DiffusionGemma 샘플러]): positions sorted by (entropy, position) with a
+// bitonic sort of 64-bit keys in LDS (entropies are >= 0, so their float bits order like the
+// values); one thread takes the float32 running sum in that order to find the largest k whose
+// sum stays within gamma, and the mean entropy (the same sum over all L, divided by L).  The k
+// lowest-entropy positions take the Gumbel-max draw y, the rest a uniform re-noise token; a canvas
+// whose argmax sequence equals the previous step's and whose mean entropy is below the threshold
+// stops (adaptive), and a stopped or final canvas takes its argmax sequence.
+constexpr int EB_MAX_L = 1024;
+__global__ __launch_bounds__(EB_MAX_L) void eb_select_kernel(EbArgs p) {
+  __shared__ unsigned long long key[EB_MAX_L];
+  __shared__ int rank[EB_MAX_L];
+  __shared__ int sh_k, sh_unstable;
+  __shared__ float sh_mean;
+  const int b = blockIdx.x, i = threadIdx.x, NT = blockDim.x;
+  if (p.done[b]) return;                              // the whole block leaves together
+  const int r = b * p.L + i;
+  float H = 0.f;
+  int a = 0, y = 0;
+  if (i < p.L) {
+    const float* st = p.stats + (size_t)r * STAT_FIELDS;
+    a = __float_as_int(st[1]);
+    y = __float_as_int(st[3]);
+    H = fmaxf(st[5], 0.f) + 0.f;                      // rounding below zero counts as (+)zero
+  }
+  key[i] = i < p.L ? ((unsigned long long)__float_as_uint(H) << 32) | (unsigned)i : ~0ull;
+  if (i == 0) sh_unstable = 0;
+  __syncthreads();
+  if (i < p.L && p.has_prev && p.prev[r] != a) sh_unstable = 1;
+  for (int k = 2; k <= NT; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      __syncthreads();
+      const int ixj = i ^ j;
+      if (ixj > i) {
+        const unsigned long long x = key[i], z = key[ixj];
+        if ((x > z) == ((i & k) == 0)) { key[i] = z; key[ixj] = x; }
+      }
+    }
+  __syncthreads();
+  if (i < p.L) rank[key[i] & 0xffffffffu] = i;
+  if (i == 0) {
+    float run = 0.f;
+    int kk = 0;
+    for (int q = 0; q < p.L; ++q) {
+      run += __uint_as_float((unsigned)(key[q] >> 32));
+      if (run <= p.gamma) kk = q + 1;
+    }
+    sh_k = kk;
+    sh_mean = run / (float)p.L;
+  }
+  __syncthreads();
+  const int k = sh_k;
+  const float mean = sh_mean;
+  const bool stop = p.adaptive && p.has_prev && !sh_unstable && mean < p.stop_entropy;
+  const bool fin = stop || p.final_step;
+  if (i < p.L) {
+    int x;
+    if (fin) {
+      x = a;
+    } else if (rank[i] < k) {
+      x = y;
+    } else {
+      const u32x4 w = philox((uint32_t)(i >> 2), 0u, p.step, ((uint32_t)b << 8) | TAG_RENOISE, p.k0, p.k1);
+      x = token_of(pick(w, i & 3), p.vocab, p.vocab_log2);
+    }
+    p.canvas[r] = x;
+    p.prev[r] = a;
+  }
+  if (i == 0) {
+    if (fin) p.done[b] = 1;
+    if (p.n_accepted) p.n_accepted[b] = k;
+    if (p.mean_entropy) p.mean_entropy[b] = mean;
+    if (p.steps_taken) p.steps_taken[b] += 1;
+  }
+}
+
+static int log2_exact(int v);
+
+hipError_t launch_eb_select(EbArgs a, hipStream_t s) {
+  if (a.L < 1 || a.L > EB_MAX_L) return hipErrorInvalidValue;
+  int nt = 64;
+  while (nt < a.L) nt <<= 1;
+  a.vocab_log2 = log2_exact(a.vocab);
+  hipLaunchKernelGGL(eb_select_kernel, dim3(a.B), dim3(nt), 0, s, a);
   return hipGetLastError();
 }
 

@@ -95,7 +95,7 @@ struct Layout {
   size_t status, stats, rlogits, idx, gates;
   size_t resid, xhat, rope, q, kn, vn, attn_o, part_o, part_ml, rparts, o_parts, sh_parts;
   size_t counts, offsets, perm, inv_perm, tok, work, n_items;
-  size_t a_grp, y, sh_a, samp_part, hidden, done, n_locked;
+  size_t a_grp, y, sh_a, samp_part, hidden, done, n_locked, prev;
   size_t total;
   int max_items;
 };
@@ -107,7 +107,7 @@ Layout layout(const dg_model_desc& d, int B, int n, int max_prefix) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
   w.status = take(256);
-  w.stats = take(R * 5 * 4);
+  w.stats = take(R * STAT_FIELDS * 4);
   w.rlogits = take(R * d.n_experts * 4);
   w.idx = take(Rk * 4);
   w.gates = take(Rk * 4);
@@ -137,10 +137,11 @@ Layout layout(const dg_model_desc& d, int B, int n, int max_prefix) {
   w.sh_a = take(R * d.shared_hidden * ab);
   int vps;
   const int slices = sampler_slices(d, (int)R, &vps);
-  w.samp_part = take((size_t)((slices + 7) / 8 * 8) * R * 5 * 4);
+  w.samp_part = take((size_t)((slices + 7) / 8 * 8) * R * SAMPLER_PART * 4);
   w.hidden = take(R * d.d_model * ab);
   w.done = take(B * 4);
   w.n_locked = take(B * 4);
+  w.prev = take(R * 4);
   w.total = o;
   return w;
 }
@@ -490,6 +491,68 @@ dg_status sample_into(dg_ctx* c, const void* hidden, int32_t* canvas, uint8_t* l
   return DG_OK;
 }
 
+dg_status check_eb_params(const dg_eb_params* p) {
+  if (!p) return fail(DG_EINVAL, "params is NULL");
+  if (!(p->t > 0.f) || p->t > 1.f) return fail(DG_EINVAL, "need 0 < t <= 1");
+  if (!(p->tau_start > 0.f) || !(p->tau_end > 0.f) || !std::isfinite(p->tau_start) || !std::isfinite(p->tau_end))
+    return fail(DG_EINVAL, "temperatures must be > 0");
+  if (!(p->gamma >= 0.f) || !(p->stop_entropy >= 0.f)) return fail(DG_EINVAL, "gamma and stop_entropy must be >= 0");
+  return DG_OK;
+}
+
+// tau_t = tau_end + (tau_start - tau_end) t, in double, as a float
+float eb_tau(const dg_eb_params* p) {
+  return (float)((double)p->tau_end + ((double)p->tau_start - (double)p->tau_end) * (double)p->t);
+}
+
+EbArgs eb_args(const dg_ctx* c, int32_t* canvas, int32_t* prev, int32_t* done, int32_t* n_accepted,
+               float* mean_entropy, int B, int L, const dg_eb_params* p, void* ws, const Layout& w,
+               int32_t* steps_taken) {
+  EbArgs e{};
+  e.stats = at<float>(ws, w.stats);
+  e.B = B; e.L = L; e.canvas = canvas; e.prev = prev; e.done = done;
+  e.n_accepted = n_accepted; e.mean_entropy = mean_entropy; e.steps_taken = steps_taken;
+  e.gamma = p->gamma; e.stop_entropy = p->stop_entropy;
+  e.has_prev = p->has_prev != 0; e.final_step = p->final_step != 0; e.adaptive = p->adaptive != 0;
+  e.vocab = c->d.vocab;
+  e.k0 = key0(p->seed); e.k1 = key1(p->seed); e.step = p->step;
+  return e;
+}
+
+// the entropy-bounded step: statistics of every row (from the fused LM head over `src` = hidden
+// states, or from given logits), merged without touching the canvas, then the per-canvas selection
+dg_status eb_into(dg_ctx* c, const void* src, bool from_logits, int32_t* canvas, int32_t* prev, int32_t* done,
+                  int32_t* n_accepted, float* mean_entropy, int B, int L, const dg_eb_params* p, void* ws,
+                  const Layout& w, int32_t* steps_taken, hipStream_t s) {
+  const dg_model_desc& d = c->d;
+  const int R = B * L;
+  const uint32_t k0 = key0(p->seed), k1 = key1(p->seed);
+  const float zs = (float)(1.4426950408889634 / (double)eb_tau(p));
+  int vps;
+  const int slices = sampler_slices(d, R, &vps);
+  float* part = at<float>(ws, w.samp_part);
+  {
+    ProfScope ps(c, DG_PROF_SAMPLER, s);
+    if (from_logits) {
+      HIPCHK(launch_logits_partials(static_cast<const float*>(src), R, d.vocab, L, zs, k0, k1, p->step, slices, vps,
+                                    part, s));
+    } else {
+      SampArgs sa{};
+      sa.H = src; sa.E = c->embed;
+      sa.rows = R; sa.d = d.d_model; sa.V = d.vocab; sa.L = L;
+      sa.zscale_log2 = zs; sa.k0 = k0; sa.k1 = k1; sa.step = p->step;
+      sa.slices = slices; sa.v_per_slice = vps; sa.part = part;
+      HIPCHK(launch_lmhead_sampler(sa, d.act_dtype == DG_BF16, s));
+    }
+  }
+  StepArgs st{};
+  st.part = part; st.slices = slices; st.B = B; st.L = L;
+  st.stats = at<float>(ws, w.stats); st.status = at<int>(ws, w.status); st.stats_only = 1;
+  HIPCHK(launch_step_merge(st, s));
+  HIPCHK(launch_eb_select(eb_args(c, canvas, prev, done, n_accepted, mean_entropy, B, L, p, ws, w, steps_taken), s));
+  return DG_OK;
+}
+
 dg_status check_step_params(const dg_step_params* p) {
   if (!p) return fail(DG_EINVAL, "params is NULL");
   if (!(p->tau > 0.f) || !std::isfinite(p->tau)) return fail(DG_EINVAL, "tau must be > 0");
@@ -675,10 +738,67 @@ dg_status dg_step_sample(dg_ctx* ctx, const void* hidden, int32_t* canvas, uint8
                      jump_prob(params->schedule, params->t, params->h), ws, w, nullptr, nullptr, stream);
 }
 
+// dg_canvas_run with the entropy-bounded sampler
+dg_status eb_run(dg_ctx* ctx, const dg_kv* kv, int32_t* canvas, uint8_t* lock, int32_t* steps_taken, int32_t L,
+                 const dg_run_params* p, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ctx->embed) return fail(DG_EINVAL, "the canvas loop needs the embedding");
+  if (p->max_steps < 1) return fail(DG_EINVAL, "max_steps must be >= 1");
+  int mp = 0;
+  dg_status st = check_kv(ctx, kv, 0, &mp);
+  if (st != DG_OK) return st;
+  if ((st = check_rows(kv->batch, L)) != DG_OK) return st;
+  if ((st = check_ws(ctx, ws, ws_bytes, kv->batch, L, mp)) != DG_OK) return st;
+  if (L > 1024) return fail(DG_EUNSUPPORTED, "entropy-bounded sampler: L %d > 1024", L);
+  dg_eb_params ep{};
+  ep.t = 1.f; ep.tau_start = p->tau; ep.tau_end = p->tau_end; ep.gamma = p->gamma; ep.stop_entropy = p->stop_entropy;
+  ep.seed = p->seed; ep.adaptive = p->adaptive != 0;
+  if ((st = check_eb_params(&ep)) != DG_OK) return st;
+  const Layout w = layout(ctx->d, kv->batch, L, mp);
+  const int B = kv->batch;
+  int32_t* done = at<int32_t>(ws, w.done);
+  HIPCHK(launch_fill_i32(done, 0, B, stream));
+  if (steps_taken) HIPCHK(launch_fill_i32(steps_taken, 0, B, stream));
+  if (p->init_canvas) HIPCHK(launch_init_canvas(canvas, lock, B, L, ctx->d.vocab, key0(p->seed), key1(p->seed), stream));
+  const double h = 1.0 / p->max_steps;
+  for (int s = 0; s < p->max_steps; ++s) {
+    if ((st = dg_denoise_step(ctx, kv, canvas, nullptr, L, 0, ctx->d.n_layers, at<void>(ws, w.hidden), nullptr, ws,
+                              ws_bytes, stream)) != DG_OK)
+      return st;
+    ep.t = (float)(1.0 - s * h);
+    ep.step = (uint32_t)s;
+    ep.has_prev = s > 0;
+    ep.final_step = s == p->max_steps - 1;
+    if ((st = eb_into(ctx, at<void>(ws, w.hidden), false, canvas, at<int32_t>(ws, w.prev), done, nullptr, nullptr,
+                      B, L, &ep, ws, w, steps_taken, stream)) != DG_OK)
+      return st;
+  }
+  return DG_OK;
+}
+
+dg_status dg_step_entropy_bounded(dg_ctx* ctx, const void* hidden, int32_t* canvas, int32_t* prev_argmax,
+                                  int32_t* done, int32_t* n_accepted, float* mean_entropy, int32_t batch, int32_t L,
+                                  const dg_eb_params* params, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err.clear();
+  if (!ctx || !hidden || !canvas || !prev_argmax || !done) return fail(DG_EINVAL, "NULL argument");
+  if (!ctx->embed) return fail(DG_EINVAL, "the LM head needs the embedding");
+  dg_status st = check_eb_params(params);
+  if (st != DG_OK) return st;
+  if ((st = check_rows(batch, L)) != DG_OK) return st;
+  if ((st = check_ws(ctx, ws, ws_bytes, batch, L, 0)) != DG_OK) return st;
+  const Layout w = layout(ctx->d, batch, L, 0);
+  return eb_into(ctx, hidden, false, canvas, prev_argmax, done, n_accepted, mean_entropy, batch, L, params, ws, w,
+                 nullptr, stream);
+}
+
 dg_status dg_canvas_run(dg_ctx* ctx, const dg_kv* kv, int32_t* canvas, uint8_t* lock, int32_t* steps_taken, int32_t L,
                         const dg_run_params* p, void* ws, size_t ws_bytes, hipStream_t stream) {
   g_err.clear();
-  if (!ctx || !canvas || !lock || !p) return fail(DG_EINVAL, "NULL argument");
+  if (!ctx || !canvas || !p) return fail(DG_EINVAL, "NULL argument");
+  if (p->sampler != DG_SAMPLER_EULER && p->sampler != DG_SAMPLER_ENTROPY_BOUNDED)
+    return fail(DG_EINVAL, "unknown sampler %d", (int)p->sampler);
+  if (p->sampler == DG_SAMPLER_ENTROPY_BOUNDED) return eb_run(ctx, kv, canvas, lock, steps_taken, L, p, ws, ws_bytes,
+                                                              stream);
+  if (!lock) return fail(DG_EINVAL, "NULL argument");
   if (!ctx->embed) return fail(DG_EINVAL, "the canvas loop needs the embedding");
   if (p->max_steps < 1) return fail(DG_EINVAL, "max_steps must be >= 1");
   int mp = 0;
@@ -743,14 +863,49 @@ dg_status dg_test_step_from_logits(dg_ctx* ctx, const float* logits, int32_t* ca
 }
 
 dg_status dg_test_read_stats(const dg_ctx* ctx, const void* ws, int32_t rows, float* m, int32_t* a, float* c,
-                             int32_t* y, float* best, hipStream_t stream) {
+                             int32_t* y, float* best, float* entropy, hipStream_t stream) {
   if (!ctx || !ws || rows < 1) return fail(DG_EINVAL, "bad argument");
   const Layout w = layout(ctx->d, 1, rows, 0);
   const char* base = static_cast<const char*>(ws) + w.stats;
-  void* outs[5] = {m, a, c, y, best};
-  for (int j = 0; j < 5; ++j)
+  void* outs[STAT_FIELDS] = {m, a, c, y, best, entropy};
+  for (int j = 0; j < STAT_FIELDS; ++j)
     if (outs[j])
-      HIPCHK(hipMemcpy2DAsync(outs[j], 4, base + 4 * j, 20, 4, rows, hipMemcpyDeviceToDevice, stream));
+      HIPCHK(hipMemcpy2DAsync(outs[j], 4, base + 4 * j, 4 * STAT_FIELDS, 4, rows, hipMemcpyDeviceToDevice, stream));
+  return DG_OK;
+}
+
+dg_status dg_test_eb_from_logits(dg_ctx* ctx, const float* logits, int32_t* canvas, int32_t* prev, int32_t* done,
+                                 int32_t* n_accepted, float* mean_entropy, int32_t batch, int32_t L,
+                                 const dg_eb_params* p, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err.clear();
+  if (!ctx || !logits || !canvas || !prev || !done) return fail(DG_EINVAL, "NULL argument");
+  dg_status st = check_eb_params(p);
+  if (st != DG_OK) return st;
+  if ((st = check_rows(batch, L)) != DG_OK) return st;
+  if ((st = check_ws(ctx, ws, ws_bytes, batch, L, 0)) != DG_OK) return st;
+  const Layout w = layout(ctx->d, batch, L, 0);
+  return eb_into(ctx, logits, true, canvas, prev, done, n_accepted, mean_entropy, batch, L, p, ws, w, nullptr,
+                 stream);
+}
+
+dg_status dg_test_eb_select(dg_ctx* ctx, const float* entropy, const int32_t* argmax, const int32_t* draw,
+                            int32_t* canvas, int32_t* prev, int32_t* done, int32_t* n_accepted, float* mean_entropy,
+                            int32_t batch, int32_t L, const dg_eb_params* p, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  g_err.clear();
+  if (!ctx || !entropy || !argmax || !draw || !canvas || !prev || !done) return fail(DG_EINVAL, "NULL argument");
+  dg_status st = check_eb_params(p);
+  if (st != DG_OK) return st;
+  if ((st = check_rows(batch, L)) != DG_OK) return st;
+  if ((st = check_ws(ctx, ws, ws_bytes, batch, L, 0)) != DG_OK) return st;
+  const Layout w = layout(ctx->d, batch, L, 0);
+  const size_t R = (size_t)batch * L;
+  char* base = static_cast<char*>(ws) + w.stats;
+  HIPCHK(hipMemcpy2DAsync(base + 4 * 1, 4 * STAT_FIELDS, argmax, 4, 4, R, hipMemcpyDeviceToDevice, stream));
+  HIPCHK(hipMemcpy2DAsync(base + 4 * 3, 4 * STAT_FIELDS, draw, 4, 4, R, hipMemcpyDeviceToDevice, stream));
+  HIPCHK(hipMemcpy2DAsync(base + 4 * 5, 4 * STAT_FIELDS, entropy, 4, 4, R, hipMemcpyDeviceToDevice, stream));
+  HIPCHK(launch_eb_select(eb_args(ctx, canvas, prev, done, n_accepted, mean_entropy, batch, L, p, ws, w, nullptr),
+                          stream));
   return DG_OK;
 }
 

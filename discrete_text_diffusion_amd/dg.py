@@ -54,7 +54,17 @@ class StepParams(C.Structure):
 
 class RunParams(C.Structure):
     _fields_ = [("schedule", C.c_int), ("max_steps", C.c_int32), ("tau", C.c_float), ("lock_threshold", C.c_float),
-                ("seed", C.c_uint64), ("adaptive", C.c_int32), ("init_canvas", C.c_int32)]
+                ("seed", C.c_uint64), ("adaptive", C.c_int32), ("init_canvas", C.c_int32), ("sampler", C.c_int),
+                ("gamma", C.c_float), ("stop_entropy", C.c_float), ("tau_end", C.c_float)]
+
+
+DG_SAMPLER_EULER, DG_SAMPLER_ENTROPY_BOUNDED = 0, 1
+
+
+class EbParams(C.Structure):
+    _fields_ = [("t", C.c_float), ("tau_start", C.c_float), ("tau_end", C.c_float), ("gamma", C.c_float),
+                ("stop_entropy", C.c_float), ("seed", C.c_uint64), ("step", C.c_uint32), ("has_prev", C.c_int32),
+                ("final_step", C.c_int32), ("adaptive", C.c_int32)]
 
 
 EXPORTS = {
@@ -76,7 +86,16 @@ EXPORTS = {
     "dg_test_step_from_logits": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
                                            C.c_int32, C.POINTER(StepParams), C.c_void_p, C.c_size_t, C.c_void_p]),
     "dg_test_read_stats": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
-                                     C.c_void_p, C.c_void_p, C.c_void_p]),
+                                     C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "dg_step_entropy_bounded": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                          C.c_void_p, C.c_int32, C.c_int32, C.POINTER(EbParams), C.c_void_p,
+                                          C.c_size_t, C.c_void_p]),
+    "dg_test_eb_from_logits": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                         C.c_void_p, C.c_int32, C.c_int32, C.POINTER(EbParams), C.c_void_p,
+                                         C.c_size_t, C.c_void_p]),
+    "dg_test_eb_select": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                    C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.POINTER(EbParams),
+                                    C.c_void_p, C.c_size_t, C.c_void_p]),
     "dg_test_router_topk": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
                                       C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "dg_test_read_routing": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
@@ -190,9 +209,30 @@ def dg_test_step_from_logits(ctx, logits, canvas, lock, n_locked, batch, L, para
                                            _stream(stream)))
 
 
-def dg_test_read_stats(ctx, ws, rows, m=None, a=None, c=None, y=None, best=None, stream=None):
+def dg_test_read_stats(ctx, ws, rows, m=None, a=None, c=None, y=None, best=None, entropy=None, stream=None):
     _check(load().dg_test_read_stats(ctx, _ptr(ws), rows, _ptr(m), _ptr(a), _ptr(c), _ptr(y), _ptr(best),
-                                     _stream(stream)))
+                                     _ptr(entropy), _stream(stream)))
+
+
+def dg_step_entropy_bounded(ctx, hidden, canvas, prev_argmax, done, n_accepted, mean_entropy, batch, L,
+                            params: EbParams, ws, stream=None):
+    _check(load().dg_step_entropy_bounded(ctx, _ptr(hidden), _ptr(canvas), _ptr(prev_argmax), _ptr(done),
+                                          _ptr(n_accepted), _ptr(mean_entropy), batch, L, C.byref(params), _ptr(ws),
+                                          ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def dg_test_eb_from_logits(ctx, logits, canvas, prev_argmax, done, n_accepted, mean_entropy, batch, L,
+                           params: EbParams, ws, stream=None):
+    _check(load().dg_test_eb_from_logits(ctx, _ptr(logits), _ptr(canvas), _ptr(prev_argmax), _ptr(done),
+                                         _ptr(n_accepted), _ptr(mean_entropy), batch, L, C.byref(params), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def dg_test_eb_select(ctx, entropy, argmax, draw, canvas, prev_argmax, done, n_accepted, mean_entropy, batch, L,
+                      params: EbParams, ws, stream=None):
+    _check(load().dg_test_eb_select(ctx, _ptr(entropy), _ptr(argmax), _ptr(draw), _ptr(canvas), _ptr(prev_argmax),
+                                    _ptr(done), _ptr(n_accepted), _ptr(mean_entropy), batch, L, C.byref(params),
+                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def dg_test_router_topk(scores, T, E, k, idx, gates, counts, offsets, perm, ws, stream=None):

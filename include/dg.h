@@ -124,13 +124,39 @@ typedef struct {
   uint32_t step;                   /* step index s: part of every random-draw counter */
 } dg_step_params;
 
+/* The pages' default sampler, one entropy-bounded step [TR §DiffusionGemma 샘플러].  With
+ * p = softmax(logits / tau_t), tau_t = tau_end + (tau_start - tau_end) t (0.8 -> 0.4 on the pages),
+ * each position has entropy H (nats), argmax a and a Gumbel-max draw y from p.  Positions are
+ * taken in ascending (H, position) order while the float32 running sum of their entropies stays
+ * <= gamma (0.1): those take y, every other position a uniform re-noise token (Philox stream tag 5).
+ * A canvas stops (adaptive) when has_prev is set, its argmax sequence equals the previous step's
+ * and its mean entropy (float32 sum in the same order / L) is below stop_entropy (0.005); a
+ * stopped canvas, and every canvas at final_step, takes its argmax sequence and is marked done. */
+typedef struct {
+  float t;                         /* denoising time of this step, 0 < t <= 1 */
+  float tau_start, tau_end;        /* temperature at t = 1 and at t = 0 */
+  float gamma, stop_entropy;
+  uint64_t seed;
+  uint32_t step;                   /* step index s: part of every random-draw counter */
+  int32_t has_prev;                /* prev_argmax holds the previous step's argmax sequence */
+  int32_t final_step;              /* last step of the loop */
+  int32_t adaptive;                /* 0: never stop before final_step */
+} dg_eb_params;
+
+typedef enum {
+  DG_SAMPLER_EULER = 0,            /* dg_step_sample: Euler jump + confidence lock-in */
+  DG_SAMPLER_ENTROPY_BOUNDED = 1   /* dg_step_entropy_bounded (lock is not used) */
+} dg_sampler;
+
 typedef struct {
   dg_schedule schedule;
   int32_t max_steps;            /* T: steps at t_s = 1 - s/T, s = 0..T-1, h = 1/T */
-  float tau, lock_threshold;
+  float tau, lock_threshold;    /* entropy-bounded: tau is tau_start */
   uint64_t seed;
-  int32_t adaptive;             /* 1: a canvas stops once all its positions are locked */
-  int32_t init_canvas;          /* 1: draw the canvas uniformly at t = 1 and clear the lock */
+  int32_t adaptive;             /* 1: a canvas stops early (all locked / the entropy stop rule) */
+  int32_t init_canvas;          /* 1: draw the canvas uniformly at t = 1 (and clear the lock) */
+  dg_sampler sampler;           /* DG_SAMPLER_EULER (0) or DG_SAMPLER_ENTROPY_BOUNDED */
+  float gamma, stop_entropy, tau_end;   /* entropy-bounded sampler only */
 } dg_run_params;
 
 typedef struct dg_ctx dg_ctx;   /* opaque, host-side; holds the descriptor and borrowed weights */
@@ -184,10 +210,23 @@ dg_status dg_step_sample(dg_ctx *ctx, const void *hidden, int32_t *canvas, uint8
                          const dg_step_params *params, void *ws, size_t ws_bytes,
                          hipStream_t stream);
 
+/* One entropy-bounded step (see dg_eb_params) from final-normed hidden states [batch*L][d]:
+ * the fused LM head accumulates argmax, Gumbel-max draw and entropy in one pass over the
+ * vocabulary, then one block per canvas selects.  canvas device int32 [batch][L] (out for
+ * canvases not done); prev_argmax device int32 [batch][L] (in when has_prev, out: this step's
+ * argmax); done device int32 [batch] (inout: done canvases are skipped); n_accepted (int32
+ * [batch]) and mean_entropy (float [batch]) are optional outputs.  L <= 1024. */
+dg_status dg_step_entropy_bounded(dg_ctx *ctx, const void *hidden, int32_t *canvas, int32_t *prev_argmax,
+                                  int32_t *done, int32_t *n_accepted, float *mean_entropy, int32_t batch,
+                                  int32_t L, const dg_eb_params *params, void *ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
 /* The denoising loop for one block [TR §디노이징 반복과 self-conditioning]: optional uniform
- * canvas at t = 1, then up to max_steps of dg_denoise_step + dg_step_sample at t_s = 1 - s/T.
- * With `adaptive`, a canvas whose positions are all locked is left unchanged by later steps
- * and steps_taken (device int32 [batch], out) counts the steps each canvas took. */
+ * canvas at t = 1, then up to max_steps of dg_denoise_step + the sampler's step at t_s = 1 - s/T.
+ * DG_SAMPLER_EULER: dg_step_sample; with `adaptive`, a canvas whose positions are all locked is
+ * left unchanged by later steps.  DG_SAMPLER_ENTROPY_BOUNDED: dg_step_entropy_bounded with
+ * tau_start = tau and the given tau_end, gamma, stop_entropy; `lock` may be NULL.
+ * steps_taken (device int32 [batch], out, may be NULL) counts the steps each canvas took. */
 dg_status dg_canvas_run(dg_ctx *ctx, const dg_kv *kv, int32_t *canvas, uint8_t *lock,
                         int32_t *steps_taken, int32_t L, const dg_run_params *params,
                         void *ws, size_t ws_bytes, hipStream_t stream);
@@ -225,11 +264,26 @@ dg_status dg_test_step_from_logits(dg_ctx *ctx, const float *logits, int32_t *ca
                                    const dg_step_params *params, void *ws, size_t ws_bytes,
                                    hipStream_t stream);
 
+/* Entropy-bounded step from given fp32 logits z [batch*L][vocab] (device; divided by tau_t like
+ * the fused path); same outputs as dg_step_entropy_bounded, statistics readable afterwards. */
+dg_status dg_test_eb_from_logits(dg_ctx *ctx, const float *logits, int32_t *canvas, int32_t *prev_argmax,
+                                 int32_t *done, int32_t *n_accepted, float *mean_entropy, int32_t batch,
+                                 int32_t L, const dg_eb_params *params, void *ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
+/* The selection of the entropy-bounded step alone, from given per-position float32 entropies,
+ * argmax and Gumbel-max draws (device, [batch*L] each); same outputs as dg_step_entropy_bounded. */
+dg_status dg_test_eb_select(dg_ctx *ctx, const float *entropy, const int32_t *argmax, const int32_t *draw,
+                            int32_t *canvas, int32_t *prev_argmax, int32_t *done, int32_t *n_accepted,
+                            float *mean_entropy, int32_t batch, int32_t L, const dg_eb_params *params, void *ws,
+                            size_t ws_bytes, hipStream_t stream);
+
 /* Copies the per-row sampler statistics of the last Step out of the workspace (device outputs,
- * [rows] each, any may be NULL): max logit/tau, its argmax, confidence c, Gumbel argmax y and
- * its key (logit/tau + Gumbel). */
+ * [rows] each, any may be NULL): max logit/tau, its argmax, confidence c, Gumbel argmax y, its
+ * key (logit/tau + Gumbel) and the entropy of softmax(logit/tau) in nats. */
 dg_status dg_test_read_stats(const dg_ctx *ctx, const void *ws, int32_t rows, float *m,
-                             int32_t *a, float *c, int32_t *y, float *best, hipStream_t stream);
+                             int32_t *a, float *c, int32_t *y, float *best, float *entropy,
+                             hipStream_t stream);
 
 /* Top-k routing of given fp32 scores [T][E] (device): idx/gates [T][k]; counts/offsets [E];
  * perm [T*k] = assignment id t*k+s at each expert-grouped position.  Any output may be NULL. */

@@ -42,10 +42,11 @@ def read_stats(model, ws, rows):
     c = torch.empty(rows, dtype=torch.float32, device=dev)
     y = torch.empty(rows, dtype=torch.int32, device=dev)
     best = torch.empty(rows, dtype=torch.float32, device=dev)
-    dg.dg_test_read_stats(model.ctx, ws, rows, m, a, c, y, best)
+    H = torch.empty(rows, dtype=torch.float32, device=dev)
+    dg.dg_test_read_stats(model.ctx, ws, rows, m, a, c, y, best, H)
     torch.cuda.synchronize()
     return {"m": m.cpu().numpy(), "a": a.cpu().numpy(), "c": c.cpu().numpy(), "y": y.cpu().numpy(),
-            "best": best.cpu().numpy()}
+            "best": best.cpu().numpy(), "H": H.cpu().numpy()}
 
 
 def top2_gap(z):

@@ -6,6 +6,7 @@ import pytest
 import torch
 
 from discrete_text_diffusion_amd import dg
+from oracle import eb
 from oracle import philox
 from oracle import step as S
 from synth import configs, gen
@@ -137,3 +138,8 @@ def test_fused_sampler_parity(case):
     assert np.allclose(gst["c"], ost["c"], rtol=10 * tol)
     agree = np.mean(gst["y"] == ost["y"])
     assert agree >= 0.999 or excused == int(np.sum(gst["y"] != ost["y"]))
+    # entropy of softmax(z / tau), accumulated in the same pass [TR §DiffusionGemma 샘플러]
+    oH = eb.entropy(z)
+    eH = np.abs(gst["H"] - oH)
+    log(f"  entropy max err {eH.max():.2e} (oracle range {oH.min():.3f} .. {oH.max():.3f})")
+    assert np.all(eH <= (2e-5 + 1e-5 * oH if cfg.act_dtype == "f32" else 2e-3 + 1e-3 * oH))
