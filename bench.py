@@ -5,9 +5,15 @@ the uniform canvas at t = 1, then dg_denoise_step (30-layer decoder over prefix 
 and dg_step_sample (fused LM head -> Step with lock-in) at the schedule's next grid point.
 Inputs (weights, caches) are resident in HBM before timing starts.
 
-    python bench.py [--steps K] [--warmup W] [--workload C2] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload C2] [--sampler euler|eb] [--no-cpu-baseline]
+                    [--no-breakdown]
 
-Prints one JSON line.  `value` = canvas tokens refined per second (batch * 256 * steps/s).
+Prints one JSON line.  `value` = canvas tokens refined per second (batch * 256 * steps/s).  After
+the timed region one more schedule of steps runs with per-class launch timing: `breakdown` gives
+each kernel class's time per step and its achieved rate against the roof that bounds it (HBM
+bytes or bf16 MFMA FLOPs, algorithmic: what the method must move or compute).
+With `--sampler eb` a step samples with the pages' default sampler (entropy-bounded acceptance,
+temperature 0.8 -> 0.4, adaptive stop) instead of the Euler Step with lock-in.
 """
 from __future__ import annotations
 
@@ -21,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def parse():
@@ -30,7 +37,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="C2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--breakdown", action="store_true", help="per-class kernel times after the timed region")
+    ap.add_argument("--no-breakdown", action="store_true", help="skip the per-class timing after the timed region")
+    ap.add_argument("--breakdown", action="store_true", help="(default) per-class timing after the timed region")
+    ap.add_argument("--sampler", choices=("euler", "eb"), default="euler")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed region, copy 512 MiB device to device 4 times (a plain copy of known "
                          "size for scaling hardware byte counters)")
@@ -58,6 +67,35 @@ def kernel_digest():
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def class_roofs(cfg, uniq, gate_up_bytes):
+    """Algorithmic work per step of each timed kernel class and the roof that bounds it at this
+    workload: (bound, amount, unit, peak) with amount in bytes (HBM) or FLOPs (bf16 MFMA)."""
+    wb = 1 if cfg.expert_dtype == "fp8" else 2
+    ab = 2 if cfg.act_dtype == "bf16" else 4
+    B, L, d, nl = cfg.batch, cfg.canvas, cfg.d_model, cfg.n_layers
+    R = B * L
+    hbm = lambda b: ("hbm", b, "GB/s", HBM_PEAK_GBS)
+    mfma = lambda f: ("mfma", f, "TFLOP/s", MFMA_BF16_PEAK_TFLOPS)
+    down = ((uniq * cfg.expert_hidden + cfg.shared_hidden) * d * wb
+            + (R * cfg.top_k * cfg.expert_hidden + R * cfg.shared_hidden) * ab + (R * cfg.top_k + R) * d * 4)
+    flops = 0.0
+    for l in range(nl):
+        keys = (cfg.prefix if cfg.is_global(l) else min(cfg.window, cfg.prefix)) + L
+        flops += 4.0 * R * cfg.n_q_heads * cfg.head_dim * keys
+    samp_bytes = cfg.vocab * d * ab
+    samp_flops = 2.0 * R * cfg.vocab * d
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    return {
+        "moe_gate_up": hbm(nl * gate_up_bytes),
+        "moe_down": hbm(nl * down),
+        "attention": mfma(flops),
+        "sampler": hbm(samp_bytes) if samp_flops / samp_bytes < ridge else mfma(samp_flops),
+        "qkv_rope": hbm(nl * (cfg.n_q_heads + 2 * cfg.n_kv_heads) * cfg.head_dim * d * ab),
+        "o_proj": hbm(nl * cfg.n_q_heads * cfg.head_dim * d * ab),
+        "routing": hbm(nl * cfg.n_experts * d * ab),
+    }
 
 
 def cpu_baseline(cfg, W, kv, H_dev):
@@ -144,11 +182,21 @@ def main():
     h = 1.0 / T
     stream = torch.cuda.current_stream()
 
+    prev = torch.zeros(B, L, dtype=torch.int32, device=dev)
+    done = torch.zeros(B, dtype=torch.int32, device=dev)
+
     def step(s):
         k = s % T
         if k == 0:
             dg.dg_init_canvas(canvas, lock, B, L, cfg.vocab, cfg.seed + s // T, stream)
+            if args.sampler == "eb":
+                done.zero_()
         model.denoise_step(canvas, L, ws, hidden_out=hidden, stream=stream)
+        if args.sampler == "eb":
+            p = dg.EbParams(t=1.0 - k * h, tau_start=0.8, tau_end=0.4, gamma=0.1, stop_entropy=0.005,
+                            seed=cfg.seed, step=k, has_prev=int(k > 0), final_step=int(k == T - 1), adaptive=1)
+            dg.dg_step_entropy_bounded(model.ctx, hidden, canvas, prev, done, None, None, B, L, p, ws, stream)
+            return
         p = dg.StepParams(schedule=cfg.schedule, t=1.0 - k * h, h=h, tau=cfg.tau, lock_threshold=cfg.lock_threshold,
                           seed=cfg.seed, step=k)
         model.step_sample(hidden, canvas, lock, n_locked, p, ws, stream=stream)
@@ -201,17 +249,25 @@ def main():
         del src, dst
 
     breakdown = None
-    if args.breakdown:
+    if not args.no_breakdown:
         dg.dg_profile_enable(model.ctx, (1 << 8) - 1)
         for s in range(T):
             step(s)
         torch.cuda.synchronize()
         dg.dg_profile_enable(model.ctx, 0)
+        roofs = class_roofs(cfg, uniq, gate_up_bytes)
         breakdown = {}
         for c, name in enumerate(dg.PROF_NAMES):
             ms, n = dg.dg_profile_read(model.ctx, c)
-            if n:
-                breakdown[name] = {"ms_per_step": round(ms / T, 4), "launches_per_step": n // T}
+            if not n:
+                continue
+            e = {"ms_per_step": round(ms / T, 4), "launches_per_step": n // T}
+            if name in roofs:
+                bound, amount, unit, peak = roofs[name]
+                rate = amount / (ms / T * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
+                e.update({"bound": bound, "achieved": round(rate, 1), "peak": peak, "unit": unit,
+                          "frac": round(rate / peak, 4)})
+            breakdown[name] = e
         log(f"[bench] breakdown {json.dumps(breakdown)}")
 
     cpu = None
@@ -237,7 +293,8 @@ def main():
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) caches, uniform canvas)",
         "config": {"workload": f"{args.workload}: {cfg.name}", "layers": cfg.n_layers, "batch": B, "canvas": L,
                    "prefix": cfg.prefix, "vocab": cfg.vocab, "d_model": cfg.d_model, "experts": cfg.n_experts,
-                   "top_k": cfg.top_k, "schedule_steps": T},
+                   "top_k": cfg.top_k, "schedule_steps": T,
+                   "sampler": "entropy-bounded" if args.sampler == "eb" else "euler+lock-in"},
         "roofline": {"kernel": "moe_gate_up (routed + shared experts gate/up + SwiGLU, one launch)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
