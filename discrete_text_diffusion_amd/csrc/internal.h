@@ -117,8 +117,9 @@ struct SampArgs {
   float* part;                    // [slices][rows][5] partial (m2, s, a, g2, y) as floats/ints
 };
 hipError_t launch_lmhead_sampler(const SampArgs& a, int act_bf16, hipStream_t s);
-// fused LM head tiles: rows x vocabulary entries per block step (bf16: 8 waves as 4 x 2)
-constexpr int SAMPLER_BM = 128, SAMPLER_BN_BF16 = 256, SAMPLER_BN_F32 = 128;
+// fused LM head tiles: rows x vocabulary entries per block step (bf16: 256 x 128 on 8 waves as
+// 4 x 2, so a 256-row canvas is one row tile and every embedding tile streams once)
+constexpr int SAMPLER_BM_BF16 = 256, SAMPLER_BN_BF16 = 128, SAMPLER_BM_F32 = 128, SAMPLER_BN_F32 = 128;
 constexpr int SAMPLER_PART = 6;   // floats per (row, slice) partial: m2, s, a, g2, y, w
 hipError_t launch_logits_partials(const float* z, int rows, int V, int L, float zscale_log2,
                                   uint32_t k0, uint32_t k1, uint32_t step, int slices,

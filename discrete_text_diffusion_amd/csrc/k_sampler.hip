@@ -252,10 +252,10 @@ static hipError_t launch_sampler_t(const SampArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// tiles: bf16 128 rows x 256 vocabulary entries, 8 waves (4 x 2); fp32 128 x 128, 4 waves
+// tiles: bf16 256 rows x 128 vocabulary entries, 8 waves (4 x 2); fp32 128 x 128, 4 waves
 hipError_t launch_lmhead_sampler(const SampArgs& a, int act_bf16, hipStream_t s) {
-  if (act_bf16) return launch_sampler_t<bf16_t, SAMPLER_BM, SAMPLER_BN_BF16, 4, 2, 3>(a, s);
-  return launch_sampler_t<float, SAMPLER_BM, SAMPLER_BN_F32, 2, 2, 3>(a, s);
+  if (act_bf16) return launch_sampler_t<bf16_t, SAMPLER_BM_BF16, SAMPLER_BN_BF16, 4, 2, 3>(a, s);
+  return launch_sampler_t<float, SAMPLER_BM_F32, SAMPLER_BN_F32, 2, 2, 3>(a, s);
 }
 
 // ------------------------------------------------------------------ partials from given logits --

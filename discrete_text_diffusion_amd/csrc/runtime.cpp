@@ -79,7 +79,8 @@ int sampler_slices(const dg_model_desc& d, int rows, int* v_per_slice) {
   // one block per (slice, row tile), about one block per CU: each block streams its slice's
   // vocabulary tiles through one continuous ring
   const int bn = d.act_dtype == DG_BF16 ? SAMPLER_BN_BF16 : SAMPLER_BN_F32;
-  const int n_mt = (rows + SAMPLER_BM - 1) / SAMPLER_BM;
+  const int bm = d.act_dtype == DG_BF16 ? SAMPLER_BM_BF16 : SAMPLER_BM_F32;
+  const int n_mt = (rows + bm - 1) / bm;
   const int tiles = (d.vocab + bn - 1) / bn;
   int want = (256 + n_mt - 1) / n_mt;
   if (want > tiles) want = tiles;
