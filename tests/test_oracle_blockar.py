@@ -1,0 +1,55 @@
+"""Pins of the oracle's block-AR accounting [TR §추론 효율 지표] and loop [TR §아키텍처와 블록
+자기회귀 생성] (CPU): valid-token counts by hand, the TPF / effective-step formulas on a worked
+example and their single-canvas special case, and the append-after-encode loop against chunked
+prefill (appending canvas k equals encoding prompt + canvases 0..k in one causal pass)."""
+import numpy as np
+import pytest
+
+from oracle import blockar as BA
+from oracle import model as M
+from synth import configs, gen
+from tests.helpers import oracle_kv, oracle_weights
+
+
+def test_valid_counts_by_hand():
+    eos = 7
+    out = np.array([[[1, 2, 3, 4], [7, 1, 1, 1]],
+                    [[5, 7, 7, 2], [1, 2, 3, 4]],
+                    [[7, 1, 2, 3], [1, 1, 7, 1]]])            # [K=3][B=2][L=4]
+    n = BA.valid_counts(out, eos)
+    assert n.tolist() == [[4, 0], [1, 0], [0, 0]]
+    assert BA.eos_mask(out, eos).tolist() == [[False, True], [True, False], [True, True]]
+
+
+def test_metrics_worked_example_and_single_canvas():
+    # three canvases of 256: 256 + 256 + 40 tokens in 10, 14, 6 steps; EOS in the third
+    steps = np.array([[10], [14], [6]]); valid = np.array([[256], [256], [40]])
+    seen = np.array([[False], [False], [True]])
+    m = BA.metrics(steps, valid, seen)[0]
+    assert m["canvases"] == 3 and m["tokens"] == 552 and m["steps"] == 30
+    assert m["tpf"] == pytest.approx(552 / 32)
+    assert m["effective_steps"] == pytest.approx((256 * 10 + 256 * 14 + 40 * 6) / 552)
+    # canvases after the EOS canvas do not count
+    m2 = BA.metrics(np.vstack([steps, [[9]]]), np.vstack([valid, [[0]]]), np.vstack([seen, [[True]]]))[0]
+    assert m2 == m
+    # one canvas: TPF = n / s, effective steps = s
+    m1 = BA.metrics(np.array([[12]]), np.array([[200]]), np.array([[True]]))[0]
+    assert m1["tpf"] == pytest.approx(200 / 12) and m1["effective_steps"] == pytest.approx(12)
+
+
+def test_append_after_encode_equals_one_causal_pass():
+    cfg = configs.C0.replace(batch=2)
+    W = gen.make_weights(cfg, "cpu")
+    OW = oracle_weights(W, cfg)
+    rng = np.random.default_rng(3)
+    prompt = rng.integers(0, cfg.vocab, (cfg.batch, 24))
+    canv = [rng.integers(0, cfg.vocab, (cfg.batch, 16)) for _ in range(2)]
+    kv0 = oracle_kv(gen.empty_kv(cfg))
+    kv, plen = M.prefill(cfg, OW, kv0, [0, 0], prompt)
+    for c in canv:
+        kv, plen = M.prefill(cfg, OW, kv, plen, c)
+    kv1, plen1 = M.prefill(cfg, OW, kv0, [0, 0], np.concatenate([prompt] + canv, axis=1))
+    assert plen == plen1 == [56, 56]
+    for (K, V), (K1, V1) in zip(kv, kv1):
+        assert np.allclose(K[:, :, :56], K1[:, :, :56], atol=1e-10)
+        assert np.allclose(V[:, :, :56], V1[:, :, :56], atol=1e-10)
