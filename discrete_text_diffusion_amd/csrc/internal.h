@@ -95,6 +95,9 @@ hipError_t launch_resid_add_rmsnorm(float* resid, const float* parts, int nparts
                                     const void* g, void* y, int rows, int d, float eps, int act_bf16,
                                     int* status, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
+// block-AR: tokens before each sequence's first eos per canvas of out [K][B][L]
+hipError_t launch_valid_tokens(const int32_t* out, int K, int B, int L, int32_t eos, int32_t* valid, int32_t* seen,
+                               hipStream_t s);
 
 // ---- routing ---------------------------------------------------------------------------------
 // router logits = sum of `nparts` split-K partials (part p at parts + p*part_stride) + bias

@@ -269,4 +269,31 @@ hipError_t launch_moe_combine_norm(float* resid, const float* y, const float* sh
   return hipGetLastError();
 }
 
+// Valid tokens of block-AR canvases out [K][B][L]: one wave per sequence b walks the canvases in
+// order; n[k][b] = position of the sequence's first eos in canvas k (tokens before it), L when
+// the canvas holds none, 0 for canvases after the first eos; seen[k][b] = canvas k holds an eos.
+__global__ __launch_bounds__(64) void valid_tokens_kernel(const int32_t* out, int K, int B, int L, int32_t eos,
+                                                          int32_t* valid, int32_t* seen) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  bool ended = false;
+  for (int k = 0; k < K; ++k) {
+    const int32_t* c = out + ((int64_t)k * B + b) * L;
+    int first = L;
+    for (int i = lane; i < L; i += 64)
+      if (c[i] == eos) { first = i; break; }
+    for (int o = 32; o > 0; o >>= 1) first = min(first, __shfl_xor(first, o, 64));
+    if (lane == 0) {
+      valid[(int64_t)k * B + b] = ended ? 0 : first;
+      if (seen) seen[(int64_t)k * B + b] = first < L;
+    }
+    ended = ended || first < L;
+  }
+}
+
+hipError_t launch_valid_tokens(const int32_t* out, int K, int B, int L, int32_t eos, int32_t* valid, int32_t* seen,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(valid_tokens_kernel, dim3(B), dim3(64), 0, s, out, K, B, L, eos, valid, seen);
+  return hipGetLastError();
+}
+
 }  // namespace dg

@@ -96,7 +96,7 @@ struct Layout {
   size_t status, stats, rlogits, idx, gates;
   size_t resid, xhat, rope, q, kn, vn, attn_o, part_o, part_ml, rparts, o_parts, sh_parts;
   size_t counts, offsets, perm, inv_perm, tok, work, n_items;
-  size_t a_grp, y, sh_a, samp_part, hidden, done, n_locked, prev;
+  size_t a_grp, y, sh_a, samp_part, hidden, done, n_locked, prev, lockbuf;
   size_t total;
   int max_items;
 };
@@ -143,6 +143,7 @@ Layout layout(const dg_model_desc& d, int B, int n, int max_prefix) {
   w.done = take(B * 4);
   w.n_locked = take(B * 4);
   w.prev = take(R * 4);
+  w.lockbuf = take(R);
   w.total = o;
   return w;
 }
@@ -832,6 +833,45 @@ dg_status dg_canvas_run(dg_ctx* ctx, const dg_kv* kv, int32_t* canvas, uint8_t* 
                           p->adaptive ? done : nullptr, stream)) != DG_OK)
       return st;
   }
+  return DG_OK;
+}
+
+dg_status dg_generate(dg_ctx* ctx, const dg_kv* kv, int32_t* out, int32_t* steps, int32_t* valid, int32_t* eos_seen,
+                      int32_t K, int32_t L, int32_t eos_id, const dg_run_params* params, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  g_err.clear();
+  if (!ctx || !kv || !out || !params || !kv->prefix_len) return fail(DG_EINVAL, "NULL argument");
+  if (K < 1) return fail(DG_EINVAL, "K must be >= 1");
+  const int B = kv->batch;
+  if (B < 1 || B > MAX_BATCH) return fail(DG_EUNSUPPORTED, "batch %d not in [1, %d]", B, MAX_BATCH);
+  // room for the appended canvases: checked up front so nothing is enqueued on failure
+  std::vector<int32_t> plen(kv->prefix_len, kv->prefix_len + B);
+  dg_kv last = *kv;
+  std::vector<int32_t> end(B);
+  for (int b = 0; b < B; ++b) end[b] = plen[b] + (K - 1) * L;
+  last.prefix_len = end.data();
+  int mp = 0;
+  dg_status st = check_kv(ctx, &last, 0, &mp);
+  if (st != DG_OK) return st;
+  if ((st = check_ws(ctx, ws, ws_bytes, B, L, mp)) != DG_OK) return st;
+  const Layout w = layout(ctx->d, B, L, mp);
+  uint8_t* lock = at<uint8_t>(ws, w.lockbuf);
+  for (int k = 0; k < K; ++k) {
+    dg_kv cur = *kv;
+    cur.prefix_len = plen.data();
+    dg_run_params p = *params;
+    p.seed = params->seed + (uint64_t)k;
+    p.init_canvas = 1;
+    int32_t* canvas = out + (size_t)k * B * L;
+    if ((st = dg_canvas_run(ctx, &cur, canvas, lock, steps ? steps + (size_t)k * B : nullptr, L, &p, ws, ws_bytes,
+                            stream)) != DG_OK)
+      return st;
+    if (k + 1 < K) {
+      if ((st = dg_prefill_kv(ctx, &cur, canvas, L, ws, ws_bytes, stream)) != DG_OK) return st;
+      for (int b = 0; b < B; ++b) plen[b] += L;
+    }
+  }
+  if (valid) HIPCHK(launch_valid_tokens(out, K, B, L, eos_id, valid, eos_seen, stream));
   return DG_OK;
 }
 

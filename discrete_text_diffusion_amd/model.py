@@ -102,6 +102,13 @@ class Model:
     def canvas_run(self, canvas, lock, steps_taken, params: dg.RunParams, ws, stream=None):
         dg.dg_canvas_run(self.ctx, self.kv_struct, canvas, lock, steps_taken, canvas.shape[1], params, ws, stream)
 
+    def generate(self, out, steps, valid, eos_seen, eos_id, params: dg.RunParams, ws, stream=None):
+        """Block-AR generation into out [K][B][L] after the encoded prompt; the prefix then
+        covers the K - 1 appended canvases."""
+        K, _, L = out.shape
+        dg.dg_generate(self.ctx, self.kv_struct, out, steps, valid, eos_seen, K, L, eos_id, params, ws, stream)
+        self.advance_prefix((K - 1) * L)
+
     def close(self):
         if self.ctx:
             dg.dg_destroy(self.ctx)

@@ -231,6 +231,20 @@ dg_status dg_canvas_run(dg_ctx *ctx, const dg_kv *kv, int32_t *canvas, uint8_t *
                         int32_t *steps_taken, int32_t L, const dg_run_params *params,
                         void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Block-AR generation [TR §아키텍처와 블록 자기회귀 생성; §추론 효율 지표] after the caller has
+ * encoded the prompt with dg_prefill_kv (kv->prefix_len = prompt lengths): K canvases of L tokens;
+ * canvas k is denoised by dg_canvas_run with `params` (random streams of seed + k, canvas drawn
+ * uniform at t = 1) and, except the last, appended to the KV cache by the causal encoder at
+ * positions prefix_len[b] + k L.  Every layer's cache must hold prefix_len[b] + (K - 1) L
+ * positions (global layers).  out: device int32 [K][batch][L]; steps: device int32 [K][batch]
+ * (denoising steps of each canvas, may be NULL); valid: device int32 [K][batch] (tokens before the
+ * sequence's first eos_id, L for a canvas without one, 0 after it; may be NULL); eos_seen: device
+ * int32 [K][batch] (canvas holds an eos_id; may be NULL).  kv->prefix_len is not modified: the
+ * caller adds (K - 1) L.  No host synchronisation; eos only decides which tokens count. */
+dg_status dg_generate(dg_ctx *ctx, const dg_kv *kv, int32_t *out, int32_t *steps, int32_t *valid,
+                      int32_t *eos_seen, int32_t K, int32_t L, int32_t eos_id, const dg_run_params *params,
+                      void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* lambda of one Step as the library computes it (host function, float32 result). */
 float dg_jump_prob(dg_schedule schedule, float t, float h);
 

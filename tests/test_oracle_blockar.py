@@ -53,3 +53,19 @@ def test_append_after_encode_equals_one_causal_pass():
     for (K, V), (K1, V1) in zip(kv, kv1):
         assert np.allclose(K[:, :, :56], K1[:, :, :56], atol=1e-10)
         assert np.allclose(V[:, :, :56], V1[:, :, :56], atol=1e-10)
+
+
+def test_package_metrics_match_the_oracle():
+    from discrete_text_diffusion_amd.metrics import block_ar_metrics
+    rng = np.random.default_rng(9)
+    for _ in range(20):
+        K, B = int(rng.integers(1, 5)), int(rng.integers(1, 4))
+        steps = rng.integers(1, 49, (K, B))
+        seen = rng.random((K, B)) < 0.3
+        valid = np.where(seen, rng.integers(0, 256, (K, B)), 256)
+        want = BA.metrics(steps, valid, seen)
+        got = block_ar_metrics(steps, valid, seen, t_fwd_s=0.0125)
+        for g, w in zip(got, want):
+            for key in ("canvases", "tokens", "steps", "effective_steps", "tpf"):
+                assert g[key] == pytest.approx(w[key])
+            assert g["tps"] == pytest.approx(w["tpf"] / 0.0125)
