@@ -45,19 +45,23 @@ DG_DEV void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// B_AUX: cache policy of the B (weight) operand loads
-template <class T, int BM, int BN, int WM, int WN, int NS, int B_AUX = DMA_STREAM>
+// B_AUX: cache policy of the B (weight) operand loads.  KPS: K tiles per ring stage (one wait and
+// one barrier per stage: two tiles per stage halve the per-step synchronisation of long K loops).
+template <class T, int BM, int BN, int WM, int WN, int NS, int B_AUX = DMA_STREAM, int KPS = 1>
 struct GemmDma {
   static constexpr int NW = WM * WN;                   // waves per block
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "rows per tile: multiples of 8 x waves");
   static_assert(NS >= 2 && NS <= 8, "stages");
+  static_assert(KPS == 1 || KPS == 2, "K tiles per stage");
   static constexpr int FM = BM / WM / 16;
   static constexpr int FN = BN / WN / 16;
   static constexpr int KT = 128 / sizeof(T);          // K elements per tile
+  static constexpr int KSTEP = KT * KPS;              // K elements per ring stage
   static constexpr int IA = BM / (8 * NW), IB = BN / (8 * NW);   // load instructions per wave per tile
-  static constexpr int LPT = IA + IB;
-  static constexpr int STAGE = (BM + BN) * 128;
+  static constexpr int LPT = (IA + IB) * KPS;         // load instructions per wave per stage
+  static constexpr int SUB = (BM + BN) * 128;         // one K tile of both operands
+  static constexpr int STAGE = SUB * KPS;
   static constexpr int LDS_BYTES = NS * STAGE;
   static_assert((NS - 2) * LPT < 64, "vmcnt range");
 
@@ -86,14 +90,18 @@ struct GemmDma {
     }
   }
 
+  // stage `stage` <- K tiles kt * KPS .. kt * KPS + KPS - 1
   DG_DEV void issue(char* lds, int kt, int stage) {
     const int wave = threadIdx.x >> 6;
-    char* st = lds + stage * STAGE;
-    const size_t off = (size_t)kt * 128;
 #pragma unroll
-    for (int i = 0; i < IA; ++i) dma16(a_src[i] + off, st + (wave + NW * i) * 8 * 128);
+    for (int p = 0; p < KPS; ++p) {
+      char* st = lds + stage * STAGE + p * SUB;
+      const size_t off = (size_t)(kt * KPS + p) * 128;
 #pragma unroll
-    for (int i = 0; i < IB; ++i) dma16<B_AUX>(b_src[i] + off, st + BM * 128 + (wave + NW * i) * 8 * 128);
+      for (int i = 0; i < IA; ++i) dma16(a_src[i] + off, st + (wave + NW * i) * 8 * 128);
+#pragma unroll
+      for (int i = 0; i < IB; ++i) dma16<B_AUX>(b_src[i] + off, st + BM * 128 + (wave + NW * i) * 8 * 128);
+    }
   }
 
   // wait for the oldest of `pending` outstanding tiles (pending = tiles issued and not yet
@@ -113,31 +121,34 @@ struct GemmDma {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int swz = (lane & 15) >> 1, kg = lane >> 4;
-    const char* la = st + (wm * FM * 16 + (lane & 15)) * 128;
-    const char* lb = st + BM * 128 + (wn * FN * 16 + (lane & 15)) * 128;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int so = (((4 * c + kg) ^ swz)) * 16;
-      u32x4 af[FM], bfr[FN];
+    for (int p = 0; p < KPS; ++p) {
+      const char* la = st + p * SUB + (wm * FM * 16 + (lane & 15)) * 128;
+      const char* lb = st + p * SUB + BM * 128 + (wn * FN * 16 + (lane & 15)) * 128;
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const u32x4*>(la + i * 16 * 128 + so);
+      for (int c = 0; c < 2; ++c) {
+        const int so = (((4 * c + kg) ^ swz)) * 16;
+        u32x4 af[FM], bfr[FN];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const u32x4*>(lb + j * 16 * 128 + so);
+        for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const u32x4*>(la + i * 16 * 128 + so);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+        for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const u32x4*>(lb + j * 16 * 128 + so);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) Mfma<T>::mma(acc[i][j], af[i], bfr[j]);
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) Mfma<T>::mma(acc[i][j], af[i], bfr[j]);
+      }
     }
   }
 
-  // Full K loop over nk = K / KT tiles.  The stage computed at step kt - 1 is refilled at step kt
-  // only after the barrier that follows every wave's wait for tile kt.
+  // Full K loop over nk = K / KSTEP stages (K a multiple of KSTEP).  The stage computed at step
+  // kt - 1 is refilled at step kt only after the barrier that follows every wave's wait for kt.
   DG_DEV void run(char* lds, int K, f32x4_v (&acc)[FM][FN]) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-    const int nk = K / KT;
+    const int nk = K / KSTEP;
     int issued = 0;
     for (; issued < NS - 1 && issued < nk; ++issued) issue(lds, issued, issued);
     for (int kt = 0; kt < nk; ++kt) {

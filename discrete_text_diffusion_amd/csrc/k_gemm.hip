@@ -17,9 +17,9 @@ namespace dg {
 // register-staged engine, which widens them to bf16 on the way into LDS.  Rings of 3-4 stages
 // let two blocks share a CU (a single block per CU with a ring twice as deep was slower).
 constexpr int ring_stages(int stage_bytes) { return stage_bytes <= 20480 ? 4 : 3; }
-template <class TA, class TB, int BM, int BN, int WM, int WN, int NS = 0>
+template <class TA, class TB, int BM, int BN, int WM, int WN, int NS = 0, int KPS = 1>
 using TileFor = std::conditional_t<sizeof(TB) == 1, GemmTile<TA, TB, BM, BN, WM, WN, 2>,
-                                   GemmDma<TA, BM, BN, WM, WN, NS ? NS : ring_stages((BM + BN) * 128)>>;
+                                   GemmDma<TA, BM, BN, WM, WN, NS ? NS : ring_stages((BM + BN) * 128), DMA_STREAM, KPS>>;
 
 // ---------------------------------------------------------------- B-row maps ----------------
 // A tile column block of 16 columns; "paired" maps put the two members of a pair (gate/up, or
@@ -37,9 +37,9 @@ DG_DEV void paired_col(int r, int& u, int& half, int& c) {
 // 1-D grid, XCD-aware: block id mod 8 picks the XCD; the n_mt row tiles of one column (weight)
 // tile get ids congruent mod 8, so they run on one XCD and share its L2 copy of the weights.
 // blockIdx.y is the split-K part.
-template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI, int MAP, int NS = 0>
+template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI, int MAP, int NS = 0, int KPS = 1>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_dense_kernel(DenseArgs p) {
-  using G = TileFor<TA, TB, BM, BN, WM, WN, NS>;
+  using G = TileFor<TA, TB, BM, BN, WM, WN, NS, KPS>;
   extern __shared__ __align__(16) char lds[];
   const int id = blockIdx.x, xcd = id & 7, local = id >> 3;
   const int mt = local % p.n_mt;
@@ -326,17 +326,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_grouped_kernel(GroupedArgs 
 }
 
 // ---------------------------------------------------------------- launchers --------------------
-template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI, int MAP, int NS = 0>
+template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI, int MAP, int NS = 0, int KPS = 1>
 static hipError_t launch_dense_t(DenseArgs a, int n_eff, hipStream_t s) {
-  using G = TileFor<TA, TB, BM, BN, WM, WN, NS>;
+  using G = TileFor<TA, TB, BM, BN, WM, WN, NS, KPS>;
   a.n_mt = (a.M + BM - 1) / BM;
   a.n_nt = (n_eff + BN - 1) / BN;
   if (a.ksplit < 1) a.ksplit = 1;
-  if (a.K % (a.ksplit * G::KT)) return hipErrorInvalidValue;
+  if (a.K % (a.ksplit * G::KT * KPS)) return hipErrorInvalidValue;
   dim3 grid(a.n_mt * ((a.n_nt + 7) / 8 * 8), a.ksplit);
-  static const hipError_t attr = allow_lds(gemm_dense_kernel<TA, TB, BM, BN, WM, WN, EPI, MAP, NS>, G::LDS_BYTES);
+  static const hipError_t attr = allow_lds(gemm_dense_kernel<TA, TB, BM, BN, WM, WN, EPI, MAP, NS, KPS>, G::LDS_BYTES);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((gemm_dense_kernel<TA, TB, BM, BN, WM, WN, EPI, MAP, NS>), grid, dim3(WM * WN * 64),
+  hipLaunchKernelGGL((gemm_dense_kernel<TA, TB, BM, BN, WM, WN, EPI, MAP, NS, KPS>), grid, dim3(WM * WN * 64),
                      G::LDS_BYTES, s, a);
   return hipGetLastError();
 }
@@ -363,6 +363,12 @@ static hipError_t dense_pick(const DenseArgs& a, int n_eff, hipStream_t s) {
     if (a.M > 256) return launch_dense_t<TA, TB, 128, 128, 2, 2, EPI, MAP>(a, n_eff, s);
     if (small) return launch_dense_t<TA, TB, 64, 64, 2, 2, EPI, MAP>(a, n_eff, s);
     if (a.N <= 256) return launch_dense_t<TA, TB, 64, 32, 4, 1, EPI, MAP>(a, n_eff, s);
+    if constexpr (sizeof(TB) != 1) {
+      // wide outputs up to 256 rows (the attention output projection): 8 waves, two K tiles per
+      // ring stage, about one block per CU
+      constexpr int KSTEP = 2 * 128 / (int)sizeof(TA);
+      if ((a.K / a.ksplit) % KSTEP == 0) return launch_dense_t<TA, TB, 128, 64, 4, 2, EPI, MAP, 3, 2>(a, n_eff, s);
+    }
     return launch_dense_t<TA, TB, 128, 64, 2, 2, EPI, MAP>(a, n_eff, s);
   }
 }

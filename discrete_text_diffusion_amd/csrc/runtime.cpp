@@ -250,14 +250,16 @@ int dense_blocks(int M, int N) {
   return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
 }
 
-// split-K parts for a narrow dense GEMM: the largest divisor of the K-tile count (at most
-// MAX_KSPLIT, at least two K tiles per part) that keeps the block count at or below 512
+// split-K parts for the attention output projection: the largest divisor of the K-tile count (at
+// most MAX_KSPLIT, at least two K tiles per part) that keeps the block count at or below 512, or
+// at or below 256 (one 8-wave block per CU) for the 128 x 64 tiles of 65..256 rows
 int ksplit_for(const dg_model_desc& d, int M, int N, int K) {
   const int nk = K / (d.act_dtype == DG_BF16 ? 64 : 32);
   const int blocks = dense_blocks(M, N);
+  const int cap = (M > 64 && M <= 256 && N > 256) ? 256 : 512;
   int best = 1;
   for (int s = 1; s <= MAX_KSPLIT; ++s)
-    if (nk % s == 0 && nk / s >= 2 && blocks * s <= 512) best = s;
+    if (nk % s == 0 && nk / s >= 2 && blocks * s <= cap) best = s;
   return best;
 }
 
