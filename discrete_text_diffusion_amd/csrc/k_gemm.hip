@@ -213,57 +213,12 @@ hipError_t launch_rope_table(float2* tab, int rows, int rows_per_canvas, int hea
 }
 
 // ---------------------------------------------------------------- grouped (MoE) ----------------
-// 1-D grid.  Blocks [0, sh_blocks): the shared expert over all rows in row order, first (it
-// re-reads each weight tile once per row tile, so it goes before the uniform routed tiles rather
-// than into the tail); the n_sh_items row tiles of one column tile get ids congruent mod 8 (one
-// XCD, one L2 copy of that weight tile).  Blocks [sh_blocks, ...): routed tiles, block -
-// sh_blocks = item * nt_r + column tile; work item w < *n_items: expert e = work[2w], first row
-// m0 = work[2w+1] of that expert's rows [offsets[e], offsets[e] + counts[e]) in grouped order.
-template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI, int NS = 0>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_grouped_kernel(GroupedArgs p) {
-  using G = TileFor<TA, TB, BM, BN, WM, WN, NS>;
-  extern __shared__ __align__(16) char lds[];
-  const int id = blockIdx.x;
-  const bool shared = id < p.sh_blocks;
-  int row0, rows, n0, N, K;
-  int64_t lda, ldb, ldc;
-  const TA* A;
-  const TB* B;
-  const TB* B2;
-  const bf16_t* sB;
-  const bf16_t* sB2;
-  const int32_t* a_tok = nullptr;
-  void* Cout;
-  if (!shared) {
-    const int rid = id - p.sh_blocks;
-    const int item = rid / p.nt_r;
-    if (item >= *p.n_items) return;
-    const int e = p.work[2 * item], m0 = p.work[2 * item + 1];
-    row0 = p.offsets[e] + m0;
-    rows = min(BM, p.counts[e] - m0);
-    n0 = (rid - item * p.nt_r) * BN;
-    N = p.N; K = p.K; lda = p.lda; ldb = p.ldb; ldc = p.ldc;
-    A = static_cast<const TA*>(p.A);
-    a_tok = p.a_tok;
-    B = static_cast<const TB*>(p.B) + (int64_t)e * p.b_estride;
-    B2 = p.B2 ? static_cast<const TB*>(p.B2) + (int64_t)e * p.b_estride : nullptr;
-    sB = p.sB ? p.sB + (int64_t)e * p.s_estride : nullptr;
-    sB2 = p.sB2 ? p.sB2 + (int64_t)e * p.s_estride : nullptr;
-    Cout = p.C;
-  } else {
-    const int local = id, j = local >> 3;
-    const int it = j % p.n_sh_items, nt = (j / p.n_sh_items) * 8 + (local & 7);
-    if (nt >= p.nt_s) return;
-    row0 = it * BM;
-    rows = min(BM, p.sh_rows - row0);
-    n0 = nt * BN;
-    N = p.shN; K = p.shK; lda = p.sh_lda; ldb = p.sh_ldb; ldc = p.sh_ldc;
-    A = static_cast<const TA*>(p.shA);
-    B = static_cast<const TB*>(p.shB);
-    B2 = static_cast<const TB*>(p.shB2);
-    sB = p.sh_sB; sB2 = p.sh_sB2;
-    Cout = p.shC;
-  }
+// One tile: rows [row0, row0 + rows) of A (through a_tok, or in order) times the weight rows from
+// n0 (gate/up rows paired for SwiGLU) over the full K, then the tile's epilogue.
+template <class G, int BN, int WN, int EPI, class TA, class TB>
+DG_DEV void grouped_tile(char* lds, const TA* A, int64_t lda, const int32_t* a_tok, int row0, int rows,
+                         const TB* B, const TB* B2, int64_t ldb, const bf16_t* sB, const bf16_t* sB2, int N,
+                         int K, int n0, void* Cout, int64_t ldc) {
   auto arow = [&](int r) -> const TA* {
     if (r >= rows) return nullptr;
     const int src = a_tok ? a_tok[row0 + r] : row0 + r;
@@ -322,6 +277,42 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_grouped_kernel(GroupedArgs 
           static_cast<float*>(Cout)[(int64_t)(row0 + r) * ldc + n] = acc[i][j][q] * sc;
         }
     }
+  }
+}
+
+// 1-D grid.  Blocks [0, sh_blocks): the shared expert over all rows in row order, in row tiles of
+// BMS rows (every shared weight tile passes through a CU once per row tile), first (its tiles are
+// the longest, so they go before the routed tiles rather than into the tail); the n_sh_items row
+// tiles of one column tile get ids congruent mod 8 (one XCD, one L2 copy of that weight tile).
+// Blocks [sh_blocks, ...): routed tiles of BM rows, block - sh_blocks = item * nt_r + column
+// tile; work item w < *n_items: expert e = work[2w], first row m0 = work[2w+1] of that expert's
+// rows [offsets[e], offsets[e] + counts[e]) in grouped order.  The dynamic LDS holds the larger
+// of the two tile shapes' rings.
+template <class TA, class TB, int BM, int BMS, int BN, int WM, int WN, int EPI, int NS = 0>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_grouped_kernel(GroupedArgs p) {
+  using G = TileFor<TA, TB, BM, BN, WM, WN, NS>;
+  using GS = TileFor<TA, TB, BMS, BN, WM, WN, NS>;
+  extern __shared__ __align__(16) char lds[];
+  const int id = blockIdx.x;
+  if (id >= p.sh_blocks) {
+    const int rid = id - p.sh_blocks;
+    const int item = rid / p.nt_r;
+    if (item >= *p.n_items) return;
+    const int e = p.work[2 * item], m0 = p.work[2 * item + 1];
+    grouped_tile<G, BN, WN, EPI>(lds, static_cast<const TA*>(p.A), p.lda, p.a_tok, p.offsets[e] + m0,
+                                 min(BM, p.counts[e] - m0), static_cast<const TB*>(p.B) + (int64_t)e * p.b_estride,
+                                 p.B2 ? static_cast<const TB*>(p.B2) + (int64_t)e * p.b_estride : nullptr, p.ldb,
+                                 p.sB ? p.sB + (int64_t)e * p.s_estride : nullptr,
+                                 p.sB2 ? p.sB2 + (int64_t)e * p.s_estride : nullptr, p.N, p.K,
+                                 (rid - item * p.nt_r) * BN, p.C, p.ldc);
+  } else {
+    const int j = id >> 3;
+    const int it = j % p.n_sh_items, nt = (j / p.n_sh_items) * 8 + (id & 7);
+    if (nt >= p.nt_s) return;
+    grouped_tile<GS, BN, WN, EPI>(lds, static_cast<const TA*>(p.shA), p.sh_lda, nullptr, it * BMS,
+                                  min(BMS, p.sh_rows - it * BMS), static_cast<const TB*>(p.shB),
+                                  static_cast<const TB*>(p.shB2), p.sh_ldb, p.sh_sB, p.sh_sB2, p.shN, p.shK, nt * BN,
+                                  p.shC, p.sh_ldc);
   }
 }
 
@@ -395,27 +386,40 @@ hipError_t launch_dense(const DenseArgs& a, int act_bf16, int w_kind, hipStream_
   return dense_dispatch<bf16_t, bf16_t>(a, s);
 }
 
-template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI, int NS = 0>
+template <class TA, class TB, int BM, int BMS, int BN, int WM, int WN, int EPI, int NS = 0>
 static hipError_t launch_grouped_t(GroupedArgs a, int n_eff, int sh_eff, int max_items, hipStream_t s) {
   using G = TileFor<TA, TB, BM, BN, WM, WN, NS>;
+  using GS = TileFor<TA, TB, BMS, BN, WM, WN, NS>;
+  constexpr size_t LDS = G::LDS_BYTES > GS::LDS_BYTES ? G::LDS_BYTES : GS::LDS_BYTES;
   a.nt_r = (n_eff + BN - 1) / BN;
   a.nt_s = (sh_eff + BN - 1) / BN;
-  a.n_sh_items = a.shB ? (a.sh_rows + BM - 1) / BM : 0;
+  a.n_sh_items = a.shB ? (a.sh_rows + BMS - 1) / BMS : 0;
   a.sh_blocks = (a.nt_s + 7) / 8 * a.n_sh_items * 8;
   const int blocks = a.sh_blocks + max_items * a.nt_r;
   if (blocks == 0) return hipSuccess;
-  static const hipError_t attr = allow_lds(gemm_grouped_kernel<TA, TB, BM, BN, WM, WN, EPI, NS>, G::LDS_BYTES);
+  if (a.K % G::KT || (a.shB && a.shK % GS::KT)) return hipErrorInvalidValue;
+  static const hipError_t attr = allow_lds(gemm_grouped_kernel<TA, TB, BM, BMS, BN, WM, WN, EPI, NS>, LDS);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((gemm_grouped_kernel<TA, TB, BM, BN, WM, WN, EPI, NS>), dim3(blocks), dim3(WM * WN * 64),
-                     G::LDS_BYTES, s, a);
+  hipLaunchKernelGGL((gemm_grouped_kernel<TA, TB, BM, BMS, BN, WM, WN, EPI, NS>), dim3(blocks), dim3(WM * WN * 64),
+                     LDS, s, a);
   return hipGetLastError();
 }
 
+// Routed tiles of GROUP_BM rows x 128 weight rows on 4 waves.  Weights of the activation type: the
+// shared expert in tiles of 2 x GROUP_BM rows (its ring one stage shorter, so the launch still
+// fits two blocks per CU); fp8 weights (register-staged widening engine): GROUP_BM-row tiles for
+// both.
 template <class TA, class TB>
 static hipError_t grouped_dispatch(const GroupedArgs& a, int max_items, hipStream_t s) {
-  if (a.epi == EPI_SWIGLU)
-    return launch_grouped_t<TA, TB, GROUP_BM, 128, 1, 4, EPI_SWIGLU>(a, 2 * a.N, 2 * a.shN, max_items, s);
-  return launch_grouped_t<TA, TB, GROUP_BM, 128, 1, 4, EPI_STORE_F32>(a, a.N, a.shN, max_items, s);
+  if constexpr (sizeof(TB) == 1) {
+    if (a.epi == EPI_SWIGLU)
+      return launch_grouped_t<TA, TB, GROUP_BM, GROUP_BM, 128, 1, 4, EPI_SWIGLU>(a, 2 * a.N, 2 * a.shN, max_items, s);
+    return launch_grouped_t<TA, TB, GROUP_BM, GROUP_BM, 128, 1, 4, EPI_STORE_F32>(a, a.N, a.shN, max_items, s);
+  } else {
+    if (a.epi == EPI_SWIGLU)
+      return launch_grouped_t<TA, TB, GROUP_BM, 2 * GROUP_BM, 128, 1, 4, EPI_SWIGLU>(a, 2 * a.N, 2 * a.shN, max_items, s);
+    return launch_grouped_t<TA, TB, GROUP_BM, 2 * GROUP_BM, 128, 1, 4, EPI_STORE_F32>(a, a.N, a.shN, max_items, s);
+  }
 }
 
 hipError_t launch_grouped(const GroupedArgs& a, int act_bf16, int w_kind, int max_items, hipStream_t s) {
