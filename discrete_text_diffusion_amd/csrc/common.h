@@ -79,8 +79,10 @@ DG_DEV float wave_max(float v) {
 DG_DEV u32x4 philox(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
-    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    // one 32 x 32 -> 64-bit product per word (v_mad_u64_u32 gives both halves in one instruction)
+    const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u, p1 = (uint64_t)c2 * 0xCD9E8D57u;
+    const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
+    const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
     const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
     c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
     k0 += 0x9E3779B9u; k1 += 0xBB67AE85u;
@@ -96,8 +98,9 @@ DG_DEV uint32_t pick(const u32x4& w, int j) {
 
 // (w >> 8) * 2^-24 in [0, 1): exact in float
 DG_DEV float unit_co(uint32_t w) { return (float)(w >> 8) * 5.9604644775390625e-08f; }
-// ((w >> 9) + 1/2) * 2^-23 in (0, 1): exact in float
-DG_DEV float unit_oo(uint32_t w) { return ((float)(w >> 9) + 0.5f) * 1.1920928955078125e-07f; }
+// ((w >> 9) + 1/2) * 2^-23 in (0, 1), exact in float: the float 1 + (w >> 9) 2^-23 (mantissa bits
+// set directly) minus (1 - 2^-24); the difference of two floats within a factor 2 is exact
+DG_DEV float unit_oo(uint32_t w) { return __uint_as_float(0x3f800000u | (w >> 9)) - 0.999999940395355224609375f; }
 
 DG_DEV int32_t token_of(uint32_t w, int32_t vocab, int32_t vocab_log2) {
   if (vocab_log2 >= 0) return vocab_log2 == 0 ? 0 : (int32_t)(w >> (32 - vocab_log2));

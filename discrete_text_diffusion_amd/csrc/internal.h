@@ -117,12 +117,12 @@ struct SampArgs {
   float zscale_log2;              // log2(e) / tau
   uint32_t k0, k1, step;          // Philox key (seed) and step index
   int slices, v_per_slice;        // vocabulary split
-  float* part;                    // [slices][rows][5] partial (m2, s, a, g2, y) as floats/ints
+  float* part;                    // [slices][rows][6] partial (m2, s, a, g2, y, w) as floats/ints
 };
 hipError_t launch_lmhead_sampler(const SampArgs& a, int act_bf16, hipStream_t s);
-// fused LM head tiles: rows x vocabulary entries per block step (bf16: 256 x 128 on 8 waves as
-// 4 x 2, so a 256-row canvas is one row tile and every embedding tile streams once)
-constexpr int SAMPLER_BM_BF16 = 256, SAMPLER_BN_BF16 = 128, SAMPLER_BM_F32 = 128, SAMPLER_BN_F32 = 128;
+// fused LM head tiles: rows x vocabulary entries per block step (bf16: 256 x 256 on 8 waves of 32
+// rows, so a 256-row canvas is one row tile and every embedding tile streams once)
+constexpr int SAMPLER_BM_BF16 = 256, SAMPLER_BN_BF16 = 256, SAMPLER_BM_F32 = 128, SAMPLER_BN_F32 = 128;
 constexpr int SAMPLER_PART = 6;   // floats per (row, slice) partial: m2, s, a, g2, y, w
 hipError_t launch_logits_partials(const float* z, int rows, int V, int L, float zscale_log2,
                                   uint32_t k0, uint32_t k1, uint32_t step, int slices,

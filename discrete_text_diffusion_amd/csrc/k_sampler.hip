@@ -63,20 +63,28 @@ DG_DEV void state_merge(RowState& a, float m2, float s, float w, int ai, float g
 // entropy in nats of softmax over a row, from the merged sums
 DG_DEV float row_entropy(const RowState& r) { return LN2 * (__log2f(r.s) - r.w / r.s); }
 
-DG_DEV float gumbel_key2(float z2, uint32_t w) {
+// Gumbel-perturbed key in log2 units without the constant -log2(ln 2) (added once per row)
+DG_DEV float gumbel_key2_nc(float z2, uint32_t w) {
   const float t1 = -__log2f(unit_oo(w));       // > 0
-  return z2 - __log2f(t1) + NEG_LOG2_LN2;
+  return z2 - __log2f(t1);
 }
+DG_DEV float gumbel_key2(float z2, uint32_t w) { return gumbel_key2_nc(z2, w) + NEG_LOG2_LN2; }
 
 // ------------------------------------------------------------------ fused LM head partials ------
-// Block = (vocabulary slice, BM-row tile).  The slice's vocabulary tiles stream through one
-// continuous direct-to-LDS ring: step s = (tile t, K tile kt), so the ring never drains between
-// vocabulary tiles; after the last K tile of t the logits of t are consumed in registers.
+// Block = (vocabulary slice, BM-row tile) on WM x WN waves; wave (wm, wn) owns rows
+// [BM/WM * wm, +BM/WM) of the tile and columns [BN/WN * wn, +BN/WN).  The slice's vocabulary
+// tiles stream through one continuous direct-to-LDS ring: step s = (tile t, K tile kt), so the
+// ring never drains between vocabulary tiles.  After the last K tile of t the logits of t are
+// consumed in registers: the 16 lanes holding a row reduce the tile's row max, the sums against
+// it, the argmax and the best Gumbel key with shuffles, and one lane merges the result into the
+// wave's running state of that row, which lives in LDS (the registers hold only the
+// accumulators); the WN states of a row are merged in wave order at the end.
 template <class TA, int BM, int BN, int WM, int WN, int NS>
 __global__ __launch_bounds__(WM * WN * 64) void lmhead_sampler_kernel(SampArgs p, int n_mt) {
   using G = GemmDma<TA, BM, BN, WM, WN, NS>;
   constexpr int NW = WM * WN;
   extern __shared__ __align__(16) char lds[];
+  float* rowst_all = reinterpret_cast<float*>(lds + G::LDS_BYTES);   // [WN][BM][PART] running row states
   // blocks of one vocabulary slice run on the same XCD (block id mod 8) so E tiles are shared
   const int id = blockIdx.x, xcd = id & 7, local = id >> 3;
   const int mt = local % n_mt;
@@ -85,9 +93,16 @@ __global__ __launch_bounds__(WM * WN * 64) void lmhead_sampler_kernel(SampArgs p
   const int m0 = mt * BM;
   const int v_begin = slice * p.v_per_slice;
   const int v_end = min(p.V, v_begin + p.v_per_slice);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15;
   const int nk = p.d / G::KT;
   const int nsteps = (v_end - v_begin + BN - 1) / BN * nk;
+  float* rowst = rowst_all + (size_t)(wave % WN) * BM * PART;
+
+  for (int r = threadIdx.x; r < WN * BM; r += NW * 64) {    // visible after the ring's first barrier
+    float* q = rowst_all + r * PART;
+    q[0] = -INFINITY; q[1] = 0.f; q[2] = __int_as_float(0x7fffffff);
+    q[3] = -INFINITY; q[4] = __int_as_float(0x7fffffff); q[5] = 0.f;
+  }
 
   // DMA sources: this lane's H row (fixed) and E row index within a tile, each with its swizzled chunk
   const int rr = lane >> 3, slot = lane & 7;
@@ -116,11 +131,6 @@ __global__ __launch_bounds__(WM * WN * 64) void lmhead_sampler_kernel(SampArgs p
     if (++it_k == nk) { it_k = 0; ++it_t; }
   };
 
-  RowState st[G::FM][4];
-#pragma unroll
-  for (int i = 0; i < G::FM; ++i)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) state_init(st[i][e]);
   f32x4_v acc[G::FM][G::FN];
 #pragma unroll
   for (int i = 0; i < G::FM; ++i)
@@ -140,103 +150,98 @@ __global__ __launch_bounds__(WM * WN * 64) void lmhead_sampler_kernel(SampArgs p
     G::compute(lds + (s % NS) * G::STAGE, acc);
     if (++kt < nk) continue;
     kt = 0;
-    // ---- logits of vocabulary tile t: z = acc / tau (log2 units), running statistics --------
+    // ---- logits of vocabulary tile t: z = acc / tau (log2 units) ---------------------------------
     const int v0 = v_begin + t * BN;
     ++t;
 #pragma unroll
     for (int i = 0; i < G::FM; ++i) {
       const int rb = m0 + G::row_of(i, 0);       // first of this lane's 4 consecutive rows
       const int b = rb / p.L, ii = rb - b * p.L;
-      float z[G::FN][4];
-      int vv[G::FN];
-      uint32_t wd[G::FN][4];
+      // the row max over the tile (lowest token on ties): lane-local, then over the 16 lanes
+      float rm[4];
+      int ra[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float zmax = -INFINITY;
+        int vmax = 0x7fffffff;
+#pragma unroll
+        for (int j = 0; j < G::FN; ++j) {
+          const int v = v0 + G::col_of(j);
+          const float z = v < v_end ? acc[i][j][e] * p.zscale_log2 : -INFINITY;
+          acc[i][j][e] = z;
+          if (z > zmax) { zmax = z; vmax = v; }
+        }
+        float m = zmax;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+        int a = zmax == m ? vmax : 0x7fffffff;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) a = min(a, __shfl_xor(a, o, 64));
+        rm[e] = m;
+        ra[e] = a;
+      }
+      // sums against the row max and the Gumbel keys; one Philox block serves the lane's 4
+      // consecutive rows of one token
+      float ss[4] = {0.f, 0.f, 0.f, 0.f}, ww[4] = {0.f, 0.f, 0.f, 0.f};
+      float g2[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      int yy[4] = {0x7fffffff, 0x7fffffff, 0x7fffffff, 0x7fffffff};
 #pragma unroll
       for (int j = 0; j < G::FN; ++j) {
-        vv[j] = v0 + G::col_of(j);
-        const u32x4 w = philox((uint32_t)vv[j], (uint32_t)(ii >> 2), p.step,
-                               ((uint32_t)b << 8) | TAG_GUMBEL, p.k0, p.k1);
-        wd[j][0] = w.x; wd[j][1] = w.y; wd[j][2] = w.z; wd[j][3] = w.w;
+        const int v = v0 + G::col_of(j);
+        if (v < v_end) {
+          const u32x4 w = philox((uint32_t)v, (uint32_t)(ii >> 2), p.step, ((uint32_t)b << 8) | TAG_GUMBEL, p.k0, p.k1);
+          const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) z[j][e] = vv[j] < v_end ? acc[i][j][e] * p.zscale_log2 : -INFINITY;
+          for (int e = 0; e < 4; ++e) {
+            const float z = acc[i][j][e];
+            const float dz = z - rm[e];
+            const float ex = __builtin_amdgcn_exp2f(dz);   // dz <= 0; terms below 2^-126 do not count
+            ss[e] += ex;
+            ww[e] += ex * dz;
+            const float key = gumbel_key2_nc(z, wd[e]);
+            if (key > g2[e]) { g2[e] = key; yy[e] = v; }
+          }
+        }
         acc[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        RowState& rs = st[i][e];
-        float zmax = z[0][e];
-        int vmax = vv[0];
 #pragma unroll
-        for (int j = 1; j < G::FN; ++j)
-          if (z[j][e] > zmax) { zmax = z[j][e]; vmax = vv[j]; }
-        if (zmax > rs.m2) {
-          if (rs.m2 == -INFINITY) {
-            rs.s = 0.f; rs.w = 0.f;
-          } else {
-            const float f = exp2f(rs.m2 - zmax);
-            rs.w = f * (rs.w + (rs.m2 - zmax) * rs.s);
-            rs.s *= f;
-          }
-          rs.m2 = zmax;
-          rs.a = vmax;
+        for (int o = 1; o < 16; o <<= 1) {
+          ss[e] += __shfl_xor(ss[e], o, 64);
+          ww[e] += __shfl_xor(ww[e], o, 64);
+          const float og = __shfl_xor(g2[e], o, 64);
+          const int oy = __shfl_xor(yy[e], o, 64);
+          if (og > g2[e] || (og == g2[e] && oy < yy[e])) { g2[e] = og; yy[e] = oy; }
         }
+      }
+      // lane l16 = e merges row e of its group into the running state
 #pragma unroll
-        for (int j = 0; j < G::FN; ++j) {
-          if (z[j][e] != -INFINITY) {
-            const float dz = z[j][e] - rs.m2;
-            const float ex = exp2f(dz);
-            rs.s += ex;
-            rs.w += ex * dz;
-          }
-          const float key = vv[j] < v_end ? gumbel_key2(z[j][e], wd[j][e]) : -INFINITY;
-          if (key > rs.g2) { rs.g2 = key; rs.y = vv[j]; }
-        }
+      for (int e = 0; e < 4; ++e) {
+        if (l16 != e) continue;
+        float* q = rowst + G::row_of(i, e) * PART;
+        RowState r;
+        r.m2 = q[0]; r.s = q[1]; r.a = __float_as_int(q[2]); r.g2 = q[3]; r.y = __float_as_int(q[4]); r.w = q[5];
+        state_merge(r, rm[e], ss[e], ww[e], ra[e], g2[e] + NEG_LOG2_LN2, yy[e]);
+        q[0] = r.m2; q[1] = r.s; q[2] = __int_as_float(r.a); q[3] = r.g2; q[4] = __int_as_float(r.y); q[5] = r.w;
       }
     }
   }
 
-  // reduce over the 16 lanes holding the same rows (lane bits 0..3 select the column)
-#pragma unroll
-  for (int i = 0; i < G::FM; ++i)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      RowState& s = st[i][e];
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const float m2 = __shfl_xor(s.m2, o, 64), ss = __shfl_xor(s.s, o, 64);
-        const float g2 = __shfl_xor(s.g2, o, 64), ww = __shfl_xor(s.w, o, 64);
-        const int a = __shfl_xor(s.a, o, 64), y = __shfl_xor(s.y, o, 64);
-        state_merge(s, m2, ss, ww, a, g2, y);
-      }
-    }
-  // then over the WN waves sharing a row range, through LDS (wave wn = 0 merges and writes)
   __syncthreads();
-  float* xch = reinterpret_cast<float*>(lds);       // [WN][BM][PART]
-  const int wm = wave / WN, wn = wave % WN;
-  if ((lane & 15) == 0) {
-#pragma unroll
-    for (int i = 0; i < G::FM; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = G::row_of(i, e);
-        float* q = xch + ((size_t)wn * BM + r) * PART;
-        q[0] = st[i][e].m2; q[1] = st[i][e].s; q[2] = __int_as_float(st[i][e].a);
-        q[3] = st[i][e].g2; q[4] = __int_as_float(st[i][e].y); q[5] = st[i][e].w;
-      }
-  }
-  __syncthreads();
-  for (int r = threadIdx.x; r < BM; r += 256) {
+  for (int r = threadIdx.x; r < BM; r += NW * 64) {
     const int m = m0 + r;
     if (m >= p.rows) continue;
+    const float* q = rowst_all + r * PART;
     RowState s;
-    state_init(s);
-    for (int w = 0; w < WN; ++w) {
-      const float* q = xch + ((size_t)w * BM + r) * PART;
+    s.m2 = q[0]; s.s = q[1]; s.a = __float_as_int(q[2]); s.g2 = q[3]; s.y = __float_as_int(q[4]); s.w = q[5];
+    for (int w = 1; w < WN; ++w) {
+      q = rowst_all + ((size_t)w * BM + r) * PART;
       state_merge(s, q[0], q[1], q[5], __float_as_int(q[2]), q[3], __float_as_int(q[4]));
     }
     float* o = p.part + ((size_t)slice * p.rows + m) * PART;
     o[0] = s.m2; o[1] = s.s; o[2] = __int_as_float(s.a); o[3] = s.g2; o[4] = __int_as_float(s.y); o[5] = s.w;
   }
-  (void)wm;
 }
 
 template <class TA, int BM, int BN, int WM, int WN, int NS>
@@ -244,7 +249,8 @@ static hipError_t launch_sampler_t(const SampArgs& a, hipStream_t s) {
   using G = GemmDma<TA, BM, BN, WM, WN, NS>;
   const int n_mt = (a.rows + BM - 1) / BM;
   const int blocks = n_mt * ((a.slices + 7) / 8 * 8);
-  const size_t lds = G::LDS_BYTES > (size_t)WN * BM * PART * 4 ? G::LDS_BYTES : (size_t)WN * BM * PART * 4;
+  const size_t lds = G::LDS_BYTES + (size_t)WN * BM * PART * 4;
+  if (a.d % G::KT) return hipErrorInvalidValue;
   static const hipError_t attr = allow_lds(lmhead_sampler_kernel<TA, BM, BN, WM, WN, NS>, lds);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((lmhead_sampler_kernel<TA, BM, BN, WM, WN, NS>), dim3(blocks), dim3(WM * WN * 64), lds, s, a,
@@ -252,10 +258,11 @@ static hipError_t launch_sampler_t(const SampArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// tiles: bf16 256 rows x 128 vocabulary entries, 8 waves (4 x 2); fp32 128 x 128, 4 waves
+// tiles: bf16 256 rows x 256 vocabulary entries on 8 waves of 32 rows (a row's statistics stay
+// in one wave), two ring stages; fp32 128 x 128 on 4 waves of 32 rows, three stages
 hipError_t launch_lmhead_sampler(const SampArgs& a, int act_bf16, hipStream_t s) {
-  if (act_bf16) return launch_sampler_t<bf16_t, SAMPLER_BM_BF16, SAMPLER_BN_BF16, 4, 2, 3>(a, s);
-  return launch_sampler_t<float, SAMPLER_BM_F32, SAMPLER_BN_F32, 2, 2, 3>(a, s);
+  if (act_bf16) return launch_sampler_t<bf16_t, SAMPLER_BM_BF16, SAMPLER_BN_BF16, 8, 1, 2>(a, s);
+  return launch_sampler_t<float, SAMPLER_BM_F32, SAMPLER_BN_F32, 4, 1, 3>(a, s);
 }
 
 // ------------------------------------------------------------------ partials from given logits --
