@@ -26,6 +26,17 @@ DG_DEV uint32_t pack_bf2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((hw_f32x2){a, b}, hw_bf16x2));
 }
 
+// two floats as IEEE half (round to nearest even) in one word, and back
+typedef _Float16 hw_f16x2 __attribute__((ext_vector_type(2)));
+DG_DEV uint32_t pack_h2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((hw_f32x2){a, b}, hw_f16x2));
+}
+DG_DEV void unpack_h2(uint32_t w, float& a, float& b) {
+  const hw_f32x2 f = __builtin_convertvector(__builtin_bit_cast(hw_f16x2, w), hw_f32x2);
+  a = f[0];
+  b = f[1];
+}
+
 // element access for the two activation types
 template <class T> struct Elem;
 template <> struct Elem<float> {

@@ -66,7 +66,8 @@ struct AttnArgs {
   float scale_log2;       // log2(e) / sqrt(dh)
   int splits, keys_per_split;       // key-range split (multiple of 64 keys; fp32 kernel)
   int tiles_per_split;              // split of the 64-key tile list (bf16 kernel)
-  float* part_o; float* part_ml;    // [splits][B*n][Hq][dh], [splits][B*n][Hq][2] (splits > 1)
+  float* part_o; float* part_ml;    // [splits][B*n][Hq][dh], [splits][B*n][Hq][2] (splits > 1);
+                                    // part_o holds fp32 sums (fp32 kernel) or IEEE-half O_s / l_s (bf16)
   void* out;              // [B*n][Hq*dh] act (splits == 1)
   int32_t pos0[MAX_BATCH];          // prefix length per canvas
 };

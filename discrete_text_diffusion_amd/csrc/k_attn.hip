@@ -254,9 +254,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs p) {
   }
 }
 
-// merge split partials in split order: o = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).  S (the
-// split count) is a compile-time constant, so every partial of a thread is loaded before the sums
-// and nothing beyond the S partials is read.
+// merge split partials in split order: o = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), where
+// the fp32 kernel stores the sums O_s (fp32) and the bf16 kernel the normalised O_s / l_s (IEEE
+// half).  S (the split count) is a compile-time constant, so every partial of a thread is loaded
+// before the sums and nothing beyond the S partials is read.
 constexpr int MERGE_MAX = 16;
 template <class T>
 DG_DEV void put4(T* dst, f32x4_v v);
@@ -286,7 +287,15 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p) {
     const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + sr * 2);
     mv[s] = ml.x;
     lv[s] = ml.y;
-    ov[s] = *reinterpret_cast<const f32x4_v*>(p.part_o + sr * p.dh + d4);
+    if constexpr (sizeof(T) == 2) {
+      const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint32_t*>(p.part_o) + (sr * p.dh + d4) / 2);
+      float a, b, c, d;
+      unpack_h2(w.x, a, b);
+      unpack_h2(w.y, c, d);
+      ov[s] = f32x4_v{a, b, c, d};
+    } else {
+      ov[s] = *reinterpret_cast<const f32x4_v*>(p.part_o + sr * p.dh + d4);
+    }
   }
   float M = -INFINITY;
 #pragma unroll
@@ -298,7 +307,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p) {
     if (mv[s] == -INFINITY) continue;
     const float w = exp2f(mv[s] - M);
     L += lv[s] * w;
-    o += ov[s] * w;
+    o += ov[s] * (sizeof(T) == 2 ? lv[s] * w : w);
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   put4<T>(static_cast<T*>(p.out) + rh * p.dh + d4, o * inv);

@@ -306,9 +306,18 @@ __global__ __launch_bounds__(NW * 64) void flash_kernel(AttnArgs p) {
         *reinterpret_cast<uint2*>(o + db * 16 + 4 * kg) = w;
       }
     } else {
-      float* o = p.part_o + (((int64_t)split * p.B * p.n + row) * p.Hq + qhead[qb]) * DH;
+      // the split's output normalised by its own sum, O_s / l_s (a convex combination of value
+      // rows, so bounded by max |v|), as IEEE half: half the bytes of the fp32 sums at 2^-11
+      // relative precision; (m_s, l_s) stay fp32
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      uint32_t* o = reinterpret_cast<uint32_t*>(p.part_o) + ((((int64_t)split * p.B * p.n + row) * p.Hq + qhead[qb]) * DH) / 2;
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) *reinterpret_cast<f32x4_v*>(o + db * 16 + 4 * kg) = acc[db][qb];
+      for (int db = 0; db < C::DB; ++db) {
+        uint2 w;
+        w.x = pack_h2(acc[db][qb][0] * inv, acc[db][qb][1] * inv);
+        w.y = pack_h2(acc[db][qb][2] * inv, acc[db][qb][3] * inv);
+        *reinterpret_cast<uint2*>(o + (db * 16 + 4 * kg) / 2) = w;
+      }
       if (kg == 0) {
         float* ml = p.part_ml + (((int64_t)split * p.B * p.n + row) * p.Hq + qhead[qb]) * 2;
         ml[0] = m_run[qb];
