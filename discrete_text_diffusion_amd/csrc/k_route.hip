@@ -9,9 +9,59 @@ namespace dg {
 
 constexpr int MAX_PARTS = 16;   // split-K parts of the router GEMM
 
-// One wave (one block) per row; lane l holds experts 4l .. 4l+3 (E <= 256, E % 4 == 0), k <= 16.
-// The router logits arrive as `nparts` split-K partial sums, added in part order (deterministic),
-// plus the optional bias.
+// Candidate order as one 64-bit key: the score mapped to an order-preserving uint32 (NaN counts as
+// -inf, -0 as +0) above 0xffff - expert id, so a larger key is a larger score, then a lower id;
+// 0 (below every candidate) marks "none".
+DG_DEV uint64_t topk_key(float v, int e) {
+  if (!(v == v)) v = -INFINITY;
+  if (v == 0.f) v = 0.f;
+  uint32_t u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)(0xffff - e);
+}
+DG_DEV float key_score(uint64_t k) {
+  const uint32_t u = (uint32_t)(k >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+DG_DEV int key_expert(uint64_t k) { return 0xffff - (int)(uint32_t)k; }
+
+DG_DEV uint64_t key_max(uint64_t a, uint32_t blo, uint32_t bhi) {
+  const uint64_t b = ((uint64_t)bhi << 32) | blo;
+  return b > a ? b : a;
+}
+// lane key combined with the key of the lane that the DPP control names (full row and bank masks:
+// quad permutes and row rotations have a source in every lane)
+template <int CTRL>
+DG_DEV uint64_t key_max_dpp(uint64_t k) {
+  const uint32_t lo = (uint32_t)k, hi = (uint32_t)(k >> 32);
+  return key_max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, CTRL, 0xf, 0xf, false),
+                 (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, CTRL, 0xf, 0xf, false));
+}
+// the maximum key over the wave, in every lane, without LDS: quad swaps (xor 1, xor 2) and row
+// rotations (4, 8) give every lane its 16-lane row's maximum; the row-pair and half swaps of
+// gfx950 (permlane16 / permlane32) then combine rows
+DG_DEV uint64_t wave_max_key(uint64_t k) {
+  k = key_max_dpp<0xB1>(k);    // quad_perm [1, 0, 3, 2]
+  k = key_max_dpp<0x4E>(k);    // quad_perm [2, 3, 0, 1]
+  k = key_max_dpp<0x124>(k);   // row_ror 4
+  k = key_max_dpp<0x128>(k);   // row_ror 8
+  {
+    const auto l = __builtin_amdgcn_permlane16_swap((uint32_t)k, (uint32_t)k, false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap((uint32_t)(k >> 32), (uint32_t)(k >> 32), false, false);
+    k = key_max(key_max(0, l[0], h[0]), l[1], h[1]);
+  }
+  {
+    const auto l = __builtin_amdgcn_permlane32_swap((uint32_t)k, (uint32_t)k, false, false);
+    const auto h = __builtin_amdgcn_permlane32_swap((uint32_t)(k >> 32), (uint32_t)(k >> 32), false, false);
+    k = key_max(key_max(0, l[0], h[0]), l[1], h[1]);
+  }
+  return k;
+}
+
+// One wave (one block) per row; lane l holds experts 4l .. 4l+3 (E <= 256, E % 4 == 0), k <= E,
+// k <= 16.  The router logits arrive as `nparts` split-K partial sums, added in part order
+// (deterministic), plus the optional bias.  Each of the k rounds takes the wave's largest key
+// among the untaken candidates.
 template <int K>
 __global__ __launch_bounds__(64) void router_topk_kernel(const float* parts, int nparts, int64_t part_stride,
                                                          const float* bias, int T, int E, int k, float* logits_out,
@@ -20,7 +70,7 @@ __global__ __launch_bounds__(64) void router_topk_kernel(const float* parts, int
   const int t = blockIdx.x;
   const int e0 = 4 * lane;
   const bool on = e0 < E;
-  float v[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  uint64_t key[4] = {0, 0, 0, 0};
   if (on) {
     const float* src = parts + (int64_t)t * E + e0;
     f32x4_v pv[MAX_PARTS];
@@ -34,37 +84,22 @@ __global__ __launch_bounds__(64) void router_topk_kernel(const float* parts, int
     if (bias) acc += *reinterpret_cast<const f32x4_v*>(bias + e0);
     if (logits_out) *reinterpret_cast<f32x4_v*>(logits_out + (int64_t)t * E + e0) = acc;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = acc[j];
+    for (int j = 0; j < 4; ++j) key[j] = topk_key(acc[j], e0 + j);
   }
-  // NaN scores count as -inf; an explicit taken mask keeps the k picks distinct even when fewer
-  // than k scores are finite (untaken entries always beat taken ones)
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    if (!(v[j] == v[j])) v[j] = -INFINITY;
-  unsigned taken = 0;
   float sel_v[K];
   int sel_i[K];
 #pragma unroll
   for (int s = 0; s < K; ++s) {
     if (s >= k) break;
-    // lane-local best among untaken entries (lowest id on ties: j ascending = id ascending)
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+    uint64_t b = key[0];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + j;
-      if (e < E && !(taken >> j & 1u) && (v[j] > bv || bi == 0x7fffffff)) { bv = v[j]; bi = e; }
-    }
+    for (int j = 1; j < 4; ++j) b = key[j] > b ? key[j] : b;
+    b = wave_max_key(b);
+    sel_v[s] = key_score(b);
+    sel_i[s] = key_expert(b);
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) { bv = ov; bi = oi; }
-    }
-    bi = min(max(bi, 0), E - 1);
-    sel_v[s] = bv;
-    sel_i[s] = bi;
-    if ((bi >> 2) == lane) taken |= 1u << (bi & 3);
+    for (int j = 0; j < 4; ++j)
+      if (key[j] == b) key[j] = 0;     // keys are distinct (distinct expert ids)
   }
   if (lane == 0) {
     const float mx = sel_v[0];
@@ -83,7 +118,8 @@ __global__ __launch_bounds__(64) void router_topk_kernel(const float* parts, int
 
 hipError_t launch_router_topk(const float* parts, int nparts, int64_t part_stride, const float* bias, int T, int E,
                               int k, float* logits_out, int32_t* idx, float* gates, hipStream_t s) {
-  if (E > 256 || E % 4 || k > 16 || nparts < 1 || nparts > MAX_PARTS || part_stride % 4) return hipErrorInvalidValue;
+  if (E > 256 || E % 4 || k > 16 || k > E || nparts < 1 || nparts > MAX_PARTS || part_stride % 4)
+    return hipErrorInvalidValue;
   if (((uintptr_t)parts & 15) || ((uintptr_t)bias & 15) || ((uintptr_t)logits_out & 15)) return hipErrorInvalidValue;
   if (T == 0) return hipSuccess;
   const dim3 grid(T);

@@ -28,6 +28,9 @@ def test_router_topk_and_grouping_bit_exact(T, E, k):
     s = torch.randn(T, E, generator=g)
     s[::9, 5] = s[::9, 6] = s[::9, 7] = 3.5           # exact ties at the top
     s[1::13] = 0.0                                      # all-equal rows
+    s[5::29] = 0.0
+    s[5::29, ::3] = -0.0                                # signed zeros compare equal
+    s[6::31, 3:] = -float("inf")                        # fewer finite scores than k
     sd = s.to(DEV)
     idx = torch.empty(T, k, dtype=torch.int32, device=DEV)
     gates = torch.empty(T, k, dtype=torch.float32, device=DEV)
