@@ -37,6 +37,64 @@ DG_DEV void unpack_h2(uint32_t w, float& a, float& b) {
   b = f[1];
 }
 
+// All-reduce over the 16 lanes of each row (lanes 16r .. 16r + 15) with DPP moves, no LDS: quad
+// swaps (xor 1, xor 2), then the half-row and row mirrors.  Every step pairs lanes (i with its
+// partner, the partner with i), so all lanes of a row end with the same value, sums included.
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+template <int CTRL>
+DG_DEV int dpp_mov(int v) { return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false); }
+template <int CTRL>
+DG_DEV float dpp_movf(float v) { return __int_as_float(dpp_mov<CTRL>(__float_as_int(v))); }
+DG_DEV float row16_max(float v) {
+  v = fmaxf(v, dpp_movf<DPP_XOR1>(v));
+  v = fmaxf(v, dpp_movf<DPP_XOR2>(v));
+  v = fmaxf(v, dpp_movf<DPP_HALF_MIRROR>(v));
+  return fmaxf(v, dpp_movf<DPP_MIRROR>(v));
+}
+DG_DEV int row16_min(int v) {
+  v = min(v, dpp_mov<DPP_XOR1>(v));
+  v = min(v, dpp_mov<DPP_XOR2>(v));
+  v = min(v, dpp_mov<DPP_HALF_MIRROR>(v));
+  return min(v, dpp_mov<DPP_MIRROR>(v));
+}
+DG_DEV float row16_sum(float v) {
+  v += dpp_movf<DPP_XOR1>(v);
+  v += dpp_movf<DPP_XOR2>(v);
+  v += dpp_movf<DPP_HALF_MIRROR>(v);
+  return v + dpp_movf<DPP_MIRROR>(v);
+}
+DG_DEV int row16_sum_i(int v) {
+  v += dpp_mov<DPP_XOR1>(v);
+  v += dpp_mov<DPP_XOR2>(v);
+  v += dpp_mov<DPP_HALF_MIRROR>(v);
+  return v + dpp_mov<DPP_MIRROR>(v);
+}
+// largest key, ties to the lower id
+template <int CTRL>
+DG_DEV void argmax_step(float& k, int& id) {
+  const float ok = dpp_movf<CTRL>(k);
+  const int oi = dpp_mov<CTRL>(id);
+  if (ok > k || (ok == k && oi < id)) { k = ok; id = oi; }
+}
+DG_DEV void row16_argmax(float& k, int& id) {
+  argmax_step<DPP_XOR1>(k, id);
+  argmax_step<DPP_XOR2>(k, id);
+  argmax_step<DPP_HALF_MIRROR>(k, id);
+  argmax_step<DPP_MIRROR>(k, id);
+}
+// the two values a lane sees after the gfx950 row-pair swap (rows 2j, 2j + 1) or half swap
+// (lanes 0..31, 32..63) of v with itself: its own and its partner's, in the same order in both
+DG_DEV void pair16(uint32_t v, uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  a = r[0];
+  b = r[1];
+}
+DG_DEV void pair32(uint32_t v, uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  a = r[0];
+  b = r[1];
+}
+
 // element access for the two activation types
 template <class T> struct Elem;
 template <> struct Elem<float> {
@@ -75,13 +133,30 @@ template <> struct Mfma<float> {
 };
 
 // ---------------------------------------------------------------- wave reductions --------------
+// over the wave, the same value in every lane: row all-reduce, then rows paired, then halves
 DG_DEV float wave_sum(float v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  uint32_t a, b;
+  v = row16_sum(v);
+  pair16(__float_as_uint(v), a, b);
+  v = __uint_as_float(a) + __uint_as_float(b);
+  pair32(__float_as_uint(v), a, b);
+  return __uint_as_float(a) + __uint_as_float(b);
+}
+DG_DEV int wave_sum_i(int v) {
+  uint32_t a, b;
+  v = row16_sum_i(v);
+  pair16((uint32_t)v, a, b);
+  v = (int)(a + b);
+  pair32((uint32_t)v, a, b);
+  return (int)(a + b);
 }
 DG_DEV float wave_max(float v) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  uint32_t a, b;
+  v = row16_max(v);
+  pair16(__float_as_uint(v), a, b);
+  v = fmaxf(__uint_as_float(a), __uint_as_float(b));
+  pair32(__float_as_uint(v), a, b);
+  return fmaxf(__uint_as_float(a), __uint_as_float(b));
 }
 
 // ---------------------------------------------------------------- Philox4x32-10 ---------------

@@ -153,7 +153,7 @@ DG_DEV int chosen_slot(const int32_t* idx, int t, int k, int e) {
 // experts below e; expert e's work-list tiles (e, m0); then the positions of its rows in
 // ascending row order (wave ballots over row chunks).
 DG_DEV int block_sum_int(int v, int* red) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  v = wave_sum_i(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();

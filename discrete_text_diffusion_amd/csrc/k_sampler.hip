@@ -171,14 +171,9 @@ __global__ __launch_bounds__(WM * WN * 64) void lmhead_sampler_kernel(SampArgs p
           acc[i][j][e] = z;
           if (z > zmax) { zmax = z; vmax = v; }
         }
-        float m = zmax;
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-        int a = zmax == m ? vmax : 0x7fffffff;
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) a = min(a, __shfl_xor(a, o, 64));
+        const float m = row16_max(zmax);
         rm[e] = m;
-        ra[e] = a;
+        ra[e] = row16_min(zmax == m ? vmax : 0x7fffffff);
       }
       // sums against the row max and the Gumbel keys; one Philox block serves the lane's 4
       // consecutive rows of one token
@@ -206,16 +201,12 @@ __global__ __launch_bounds__(WM * WN * 64) void lmhead_sampler_kernel(SampArgs p
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-          ss[e] += __shfl_xor(ss[e], o, 64);
-          ww[e] += __shfl_xor(ww[e], o, 64);
-          const float og = __shfl_xor(g2[e], o, 64);
-          const int oy = __shfl_xor(yy[e], o, 64);
-          if (og > g2[e] || (og == g2[e] && oy < yy[e])) { g2[e] = og; yy[e] = oy; }
-        }
+        ss[e] = row16_sum(ss[e]);
+        ww[e] = row16_sum(ww[e]);
+        row16_argmax(g2[e], yy[e]);
       }
-      // lane l16 = e merges row e of its group into the running state
+      // lane l16 = e merges row e of its group into the running state (one fixed lane per row,
+      // so the sums it publishes do not depend on timing)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if (l16 != e) continue;
