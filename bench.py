@@ -50,8 +50,8 @@ def parse():
 # (FETCH_SIZE, WRITE_SIZE; KiB per dispatch, mean of 90 launches), each scaled by the same counter
 # on a 512 MiB device-to-device copy (FETCH_SIZE reads 262155.5 KiB for 524288 KiB read: x1.9999;
 # WRITE_SIZE reads 524288 KiB: x1).  Valid only while the kernel sources hash to `sources`.
-MOE_TRAFFIC = {"sources": "2f3f983d82dacdd648790b439137b7802adaad7cf9b5a070cfd46882838e5a5d",
-               "fetch_kib": 533379.5, "write_kib": 3872.1, "bytes_per_launch": 1096278366}
+MOE_TRAFFIC = {"sources": "5ac14a578713a03184d6eb9b9b5a7b50f8b3e9524c5a69e88023b1819b372809",
+               "fetch_kib": 528621.8, "write_kib": 3872.1, "bytes_per_launch": 1086534986}
 TRAFFIC_SOURCES = ("k_gemm.hip", "gemm_dma.h", "gemm_core.h", "common.h", "internal.h")
 
 
