@@ -18,14 +18,15 @@ from __future__ import annotations
 
 import numpy as np
 
-from .numerics import dequant_rows, rounder
+from .numerics import dequant_rows, mxfp4_dequant, rounder
 
 
 # ---------------------------------------------------------------- weights in float64 -----------
 
 def layer_arrays(L: dict, expert_dtype: str) -> dict:
-    """Storage arrays of one layer (float64 values, or uint8 codes + scales for fp8) -> float64
-    weight matrices.  fp8 weights are q * s with the per-output-row scale."""
+    """Storage arrays of one layer (float64 values, or uint8 codes + scales for fp8 / mxfp4) ->
+    float64 weight matrices.  fp8 weights are q * s with the per-output-row scale; mxfp4 weights
+    are e2m1(q) * 2^(s - 127) with one scale per 32 consecutive input elements."""
     out = {}
     for k in ("attn_norm", "ffn_norm", "w_qkv", "w_o", "w_router"):
         out[k] = np.asarray(L[k], dtype=np.float64)
@@ -34,6 +35,8 @@ def layer_arrays(L: dict, expert_dtype: str) -> dict:
                  ("sh_gate", "sh_s_gate"), ("sh_up", "sh_s_up"), ("sh_down", "sh_s_down")):
         if expert_dtype == "fp8":
             out[k] = dequant_rows(L[k], L[s])
+        elif expert_dtype == "mxfp4":
+            out[k] = mxfp4_dequant(L[k], L[s])
         else:
             out[k] = np.asarray(L[k], dtype=np.float64)
     return out

@@ -3,7 +3,9 @@
 bf16 is IEEE binary32 truncated to 8 significant bits (1 sign, 8 exponent, 7 stored mantissa
 bits); rounding to it is round-to-nearest, ties to even.  e4m3 is the OCP 8-bit float format
 "E4M3FN": 1 sign, 4 exponent (bias 7) and 3 mantissa bits, no infinities, the all-ones
-exponent-and-mantissa pattern is NaN, largest finite value 448.
+exponent-and-mantissa pattern is NaN, largest finite value 448.  MXFP4 is the OCP microscaling
+format: e2m1 elements (1 sign, 2 exponent bits with bias 1, 1 mantissa bit; largest magnitude 6)
+in blocks of 32 sharing one e8m0 scale (an 8-bit biased exponent, value 2^(s - 127)).
 """
 from __future__ import annotations
 
@@ -64,3 +66,30 @@ _E4M3 = e4m3_decode_table()
 def dequant_rows(codes, scales):
     """fp8 weight [..., N, K] codes + per-row scale [..., N] -> float64 values q * s."""
     return _E4M3[np.asarray(codes, dtype=np.uint8)] * np.asarray(scales, dtype=np.float64)[..., None]
+
+
+def e2m1_decode_table():
+    """Value of each of the 16 e2m1 codes, from the format definition: exponent field 0 is
+    subnormal (m / 2), otherwise (1 + m / 2) * 2^(e - 1)."""
+    tab = np.zeros(16, dtype=np.float64)
+    for code in range(16):
+        s = -1.0 if code & 0x8 else 1.0
+        e = (code >> 1) & 0x3
+        m = code & 0x1
+        tab[code] = s * (m / 2.0 if e == 0 else (1.0 + m / 2.0) * 2.0 ** (e - 1))
+    return tab
+
+
+_E2M1 = e2m1_decode_table()
+MX_BLOCK = 32
+
+
+def mxfp4_dequant(codes, scales):
+    """MXFP4 weight -> float64 [..., N, K]: codes uint8 [..., N, K/2] with element 2j in the low
+    nibble of byte j, scales uint8 [..., N, K/32] (e8m0, 2^(s - 127); 255 would be NaN)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    s = np.asarray(scales, dtype=np.uint8)
+    el = np.stack([c & 0xF, c >> 4], axis=-1).reshape(*c.shape[:-1], c.shape[-1] * 2)
+    val = _E2M1[el]
+    sc = np.where(s == 255, np.nan, np.ldexp(1.0, s.astype(np.int64) - 127))
+    return val * np.repeat(sc, MX_BLOCK, axis=-1)

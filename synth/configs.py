@@ -18,7 +18,7 @@ KAPPA_LINEAR = 0      # kappa_t = 1 - t
 KAPPA_QUADRATIC = 1   # kappa_t = 1 - t^2
 KAPPA_COSINE = 2      # kappa_t = cos(pi t / 2)
 
-F32, BF16, FP8 = "f32", "bf16", "fp8"
+F32, BF16, FP8, MXFP4 = "f32", "bf16", "fp8", "mxfp4"
 
 
 @dataclass(frozen=True)
@@ -38,7 +38,7 @@ class Workload:
     window: int            # <= 0: every layer global
     global_every: int      # layer l (0-based) is global iff (l+1) % global_every == 0; 0: all global
     act_dtype: str         # "f32" | "bf16": activations, attention and embedding storage
-    expert_dtype: str      # "f32" | "bf16" | "fp8": routed and shared expert weights
+    expert_dtype: str      # "f32" | "bf16" | "fp8" | "mxfp4": routed and shared expert weights
     # inputs
     batch: int
     canvas: int

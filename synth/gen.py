@@ -2,8 +2,9 @@
 
 This module holds no step of the method: it draws random weights, caches, tokens and residuals
 of the workloads' shapes and stores them in the storage formats the library reads (fp32, bf16,
-or fp8 e4m3 with per-output-row bf16 scales).  torch is used as a random-number and dtype
-plumbing library only; the same call on the same device returns the same tensors.
+fp8 e4m3 with per-output-row bf16 scales, or OCP MXFP4: e2m1 codes with one e8m0 power-of-two
+scale per 32 consecutive K-elements).  torch is used as a random-number and dtype plumbing
+library only; the same call on the same device returns the same tensors.
 
 Layouts (row-major; every weight matrix is [out][in] so both GEMM operands are K-contiguous):
   embed      [V][d]                 tied input embedding and LM head
@@ -13,6 +14,8 @@ Layouts (row-major; every weight matrix is [out][in] so both GEMM operands are K
   w_router   [E][d], router_bias [E] fp32 (None unless the workload sets a Zipf prior)
   w_gate, w_up [E][f][d]; w_down [E][d][f]; sh_gate, sh_up [fs][d]; sh_down [d][fs]
   fp8 only:  s_gate, s_up [E][f]; s_down [E][d]; sh_s_gate, sh_s_up [fs]; sh_s_down [d]  (bf16)
+  mxfp4:     expert matrices as codes uint8 [..][N][K/2] (element 2j in the low nibble of byte j)
+             with scales uint8 [..][N][K/32] (e8m0: 2^(s - 127)) under the same s_* names
   kv         per layer K and V [B][Hkv][cap][dh]
 """
 from __future__ import annotations
@@ -23,9 +26,11 @@ import math
 import numpy as np
 import torch
 
-from .configs import Workload, F32, BF16, FP8
+from .configs import Workload, F32, BF16, FP8, MXFP4
 
 FP8_MAX = 448.0
+MX_BLOCK = 32          # elements sharing one scale (OCP MX)
+E2M1_EMAX = 2          # exponent of the largest e2m1 magnitude, 6 = 1.5 * 2^2
 
 
 def tensor_seed(seed: int, name: str) -> int:
@@ -73,6 +78,32 @@ def fp8_rows(w: torch.Tensor):
     return codes, scale.contiguous()
 
 
+def mxfp4_rows(w: torch.Tensor):
+    """OCP MX "MXFP4" storage of an fp32 [..., N, K] matrix, K a multiple of 32.
+
+    Per block of 32 consecutive K-elements: X = floor(log2(max |w|)) - 2 (the largest e2m1
+    exponent), clamped to [-127, 127] (-127 for an all-zero block), stored as the e8m0 byte X + 127;
+    each element is the e2m1 code of w / 2^X rounded to nearest, ties to even, magnitudes above 6
+    saturated to 6 (the format's conversion rule).  Codes pack two per byte, element 2j in the low
+    nibble.  Returns (codes uint8 [..., N, K/2], scales uint8 [..., N, K/32])."""
+    *lead, K = w.shape
+    assert K % MX_BLOCK == 0
+    blk = w.reshape(*lead, K // MX_BLOCK, MX_BLOCK)
+    amax = blk.abs().amax(dim=-1)
+    _, ex = torch.frexp(amax)                         # amax = m 2^ex, m in [0.5, 1): floor(log2) = ex - 1
+    X = (ex.to(torch.int32) - 1 - E2M1_EMAX).clamp(-127, 127)
+    X = torch.where(amax > 0, X, torch.full_like(X, -127))
+    y = blk * torch.exp2(-X.to(torch.float32)).unsqueeze(-1)   # power-of-two scaling: exact
+    a = y.abs().clamp(max=6.0)
+    # e2m1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 (codes 0..7); a tie goes to the even code
+    mag = ((a > 0.25).int() + (a >= 0.75).int() + (a > 1.25).int() + (a >= 1.75).int()
+           + (a > 2.5).int() + (a >= 3.5).int() + (a > 5.0).int())
+    code = (mag | torch.where(y < 0, 8, 0)).to(torch.uint8).reshape(*lead, K)
+    pairs = code.reshape(*lead, K // 2, 2)
+    packed = (pairs[..., 0] | (pairs[..., 1] << 4)).to(torch.uint8).contiguous()
+    return packed, (X + 127).to(torch.uint8).contiguous()
+
+
 def zipf_bias(n_experts: int, exponent: float, seed: int) -> torch.Tensor:
     """ln p_e with p_e proportional to rank^-exponent, ranks assigned by a seeded permutation."""
     rng = np.random.default_rng(tensor_seed(seed, "zipf-perm") & 0xFFFFFFFF)
@@ -85,6 +116,10 @@ def zipf_bias(n_experts: int, exponent: float, seed: int) -> torch.Tensor:
 def _expert_store(w32: torch.Tensor, cfg: Workload, out: dict, key: str, skey: str):
     if cfg.expert_dtype == FP8:
         codes, scale = fp8_rows(w32)
+        out[key] = codes
+        out[skey] = scale
+    elif cfg.expert_dtype == MXFP4:
+        codes, scale = mxfp4_rows(w32)
         out[key] = codes
         out[skey] = scale
     else:
@@ -169,7 +204,7 @@ def bf16_bits_to_f64(t: torch.Tensor) -> np.ndarray:
 
 
 def to_numpy_f64(t: torch.Tensor) -> np.ndarray:
-    """Storage tensor -> float64 numpy (bf16/fp32 exactly; fp8 codes stay uint8)."""
+    """Storage tensor -> float64 numpy (bf16/fp32 exactly; fp8 / mxfp4 codes and scales stay uint8)."""
     if t.dtype == torch.uint8:
         return t.cpu().numpy()
     return t.float().cpu().numpy().astype(np.float64)

@@ -3,7 +3,9 @@
 Philox has no known-answer vectors available here, so its words are pinned by what any correct
 implementation must show: uniform words, balanced bits, avalanche on a one-bit counter change,
 and the exact distributions of the converters built on top of it.  bf16 rounding and the e4m3
-table are pinned against independent library conversions (torch) and the format's definition.
+table are pinned against independent library conversions (torch) and the format's definition;
+the MXFP4 decode against the values the OCP microscaling specification lists for e2m1 and
+hand-packed blocks, and the MXFP4 storage conversion by exact round trips and its tie rule.
 """
 import math
 
@@ -13,7 +15,8 @@ import scipy.stats as st
 import torch
 
 from oracle import philox
-from oracle.numerics import round_bf16, e4m3_decode_table, dequant_rows
+from oracle.numerics import round_bf16, e4m3_decode_table, dequant_rows, e2m1_decode_table, mxfp4_dequant
+from synth.gen import mxfp4_rows
 
 
 def _words(n, seed=123, tag=0):
@@ -150,3 +153,70 @@ def test_dequant_rows():
     codes = np.array([[0x38, 0x40], [0xB8, 0x00]], dtype=np.uint8)   # 1, 2 / -1, 0
     s = np.array([0.5, 4.0])
     assert np.array_equal(dequant_rows(codes, s), np.array([[0.5, 1.0], [-4.0, 0.0]]))
+
+
+# ---- MXFP4 (OCP microscaling: e2m1 elements, e8m0 scale per 32) --------------------------------
+
+def test_e2m1_table_lists_the_format_values():
+    # the eight magnitudes of FP4 E2M1 as listed by the OCP MX specification; codes 8..15 negate
+    t = e2m1_decode_table()
+    assert list(t[:8]) == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert list(t[8:]) == [-0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+
+
+def test_mxfp4_dequant_hand_packed():
+    # one row of 64 elements = 2 blocks; byte j holds element 2j (low nibble) and 2j + 1 (high)
+    codes = np.zeros((1, 32), dtype=np.uint8)
+    codes[0, 0] = 0x72          # element 0 = code 2 (1.0), element 1 = code 7 (6.0)
+    codes[0, 15] = 0x9F         # element 30 = code 15 (-6), element 31 = code 9 (-0.5)
+    codes[0, 16] = 0x01         # element 32 = code 1 (0.5), first element of block 1
+    scales = np.array([[126, 130]], dtype=np.uint8)   # 2^-1, 2^3
+    w = mxfp4_dequant(codes, scales)
+    assert w.shape == (1, 64)
+    expect = np.zeros(64)
+    expect[0], expect[1], expect[30], expect[31], expect[32] = 0.5, 3.0, -3.0, -0.25, 4.0
+    assert np.array_equal(w[0], expect)
+    assert math.isnan(mxfp4_dequant(np.zeros((1, 16), np.uint8) + 0x22, np.array([[255]], np.uint8))[0, 0])
+
+
+def test_mxfp4_storage_exact_blocks_round_trip():
+    rng = np.random.default_rng(5)
+    grid = e2m1_decode_table()
+    for X in (-9, -1, 0, 4):
+        idx = rng.integers(0, 16, size=(3, 64))
+        idx[:, 0] = 7                                   # each block holds its maximum 6
+        idx[:, 32] = 15
+        w = np.ldexp(grid[idx], X).astype(np.float32)
+        codes, scales = mxfp4_rows(torch.from_numpy(w))
+        assert np.array_equal(scales.numpy(), np.full((3, 2), X + 127, np.uint8))
+        assert np.array_equal(mxfp4_dequant(codes.numpy(), scales.numpy()), w.astype(np.float64))
+
+
+def test_mxfp4_storage_ties_saturation_and_zero():
+    # block maximum 4 gives X = floor(log2 4) - 2 = 0, so elements are rounded in units of 1
+    row = np.zeros(32, np.float32)
+    row[:10] = [4.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, -5.0, -0.1, 0.3]
+    codes, scales = mxfp4_rows(torch.from_numpy(row[None]))
+    assert scales.numpy()[0, 0] == 127
+    got = mxfp4_dequant(codes.numpy(), scales.numpy())[0]
+    # ties go to the even code: 0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4
+    assert list(got[:10]) == [4.0, 0.0, 1.0, 1.0, 2.0, 2.0, 4.0, -4.0, -0.0, 0.5]
+    sat = np.zeros(32, np.float32)
+    sat[0], sat[1] = 7.9, -7.0                             # X = 0; magnitudes above 6 saturate
+    g = mxfp4_dequant(*[t.numpy() for t in mxfp4_rows(torch.from_numpy(sat[None]))])[0]
+    assert g[0] == 6.0 and g[1] == -6.0
+    zc, zs = mxfp4_rows(torch.zeros(1, 32))
+    assert zs.numpy()[0, 0] == 0 and not zc.numpy().any()
+
+
+def test_mxfp4_storage_error_bound():
+    # within a block: half a step of the e2m1 grid below 6 * 2^X, at most 2 * 2^X at saturation
+    w = torch.randn(8, 4, 128) * 0.02
+    codes, scales = mxfp4_rows(w)
+    q = mxfp4_dequant(codes.numpy(), scales.numpy())
+    unit = np.repeat(np.ldexp(1.0, scales.numpy().astype(np.int64) - 127), 32, axis=-1)
+    err = np.abs(q - w.numpy().astype(np.float64)) / unit
+    y = np.abs(w.numpy().astype(np.float64)) / unit
+    step = np.where(y < 2, 0.5, np.where(y < 4, 1.0, 2.0))
+    assert np.all(err <= np.where(y > 6, y - 6, step / 2) + 1e-12)
+    assert np.all(y < 8)
