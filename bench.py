@@ -6,14 +6,16 @@ and dg_step_sample (fused LM head -> Step with lock-in) at the schedule's next g
 Inputs (weights, caches) are resident in HBM before timing starts.
 
     python bench.py [--steps K] [--warmup W] [--workload C2] [--sampler euler|eb] [--no-cpu-baseline]
-                    [--no-breakdown]
+                    [--no-breakdown] [--experts bf16|fp8|mxfp4]
 
 Prints one JSON line.  `value` = canvas tokens refined per second (batch * 256 * steps/s).  After
 the timed region one more schedule of steps runs with per-class launch timing: `breakdown` gives
 each kernel class's time per step and its achieved rate against the roof that bounds it (HBM
 bytes or bf16 MFMA FLOPs, algorithmic: what the method must move or compute).
 With `--sampler eb` a step samples with the pages' default sampler (entropy-bounded acceptance,
-temperature 0.8 -> 0.4, adaptive stop) instead of the Euler Step with lock-in.
+temperature 0.8 -> 0.4, adaptive stop) instead of the Euler Step with lock-in.  `--experts`
+swaps the workload's expert weight format (fp8 e4m3 or MXFP4, weights-only with bf16
+activations): a variant of the workload, named in `config.workload`, not the headline figure.
 """
 from __future__ import annotations
 
@@ -40,6 +42,9 @@ def parse():
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-class timing after the timed region")
     ap.add_argument("--breakdown", action="store_true", help="(default) per-class timing after the timed region")
     ap.add_argument("--sampler", choices=("euler", "eb"), default="euler")
+    ap.add_argument("--experts", choices=("bf16", "fp8", "mxfp4"), default=None,
+                    help="expert weight format (default: the workload's); fp8 and mxfp4 are weights-only "
+                         "formats with bf16 activations")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed region, copy 512 MiB device to device 4 times (a plain copy of known "
                          "size for scaling hardware byte counters)")
@@ -69,10 +74,16 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def weight_bytes(expert_dtype):
+    """Stored bytes per expert weight: fp8 one (plus one bf16 scale per row, not counted), MXFP4 a
+    half-byte code plus one scale byte per 32 weights, bf16 two."""
+    return {"fp8": 1.0, "mxfp4": 0.5 + 1.0 / 32}.get(expert_dtype, 2.0)
+
+
 def class_roofs(cfg, uniq, gate_up_bytes):
     """Algorithmic work per step of each timed kernel class and the roof that bounds it at this
     workload: (bound, amount, unit, peak) with amount in bytes (HBM) or FLOPs (bf16 MFMA)."""
-    wb = 1 if cfg.expert_dtype == "fp8" else 2
+    wb = weight_bytes(cfg.expert_dtype)
     ab = 2 if cfg.act_dtype == "bf16" else 4
     B, L, d, nl = cfg.batch, cfg.canvas, cfg.d_model, cfg.n_layers
     R = B * L
@@ -163,6 +174,8 @@ def main():
     from synth import configs, gen
 
     cfg = configs.get(args.workload)
+    if args.experts is not None and args.experts != cfg.expert_dtype:
+        cfg = cfg.replace(expert_dtype=args.experts, name=f"{cfg.name}-{args.experts}experts")
     dev = torch.device("cuda:0")
     log(f"[bench] workload {cfg.name}: building inputs on {torch.cuda.get_device_name(0)}")
     t0 = time.time()
@@ -226,17 +239,18 @@ def main():
     dg.dg_test_read_routing(model.ctx, ws, B * L, None, idx, None, stream)
     torch.cuda.synchronize()
     uniq = int(torch.unique(idx).numel())
-    wbytes = 1 if cfg.expert_dtype == "fp8" else 2
+    wbytes = weight_bytes(cfg.expert_dtype)
     abytes = 2 if cfg.act_dtype == "bf16" else 4
     R = B * L
     # one launch: gate+up weights of the routed experts in use and of the shared expert, the
     # normalised rows read once, the SwiGLU rows written once
-    gate_up_bytes = ((uniq * 2 * cfg.expert_hidden + 2 * cfg.shared_hidden) * cfg.d_model * wbytes
+    gate_up_bytes = int((uniq * 2 * cfg.expert_hidden + 2 * cfg.shared_hidden) * cfg.d_model * wbytes
                      + R * cfg.d_model * abytes
                      + (R * cfg.top_k * cfg.expert_hidden + R * cfg.shared_hidden) * abytes)
     moe_avg_ms = moe_ms / max(moe_n, 1)
     traffic = (MOE_TRAFFIC["bytes_per_launch"]
-               if args.workload == "C2" and kernel_digest() == MOE_TRAFFIC["sources"] else None)
+               if args.workload == "C2" and cfg.expert_dtype == "bf16" and kernel_digest() == MOE_TRAFFIC["sources"]
+               else None)
     achieved = gate_up_bytes / (moe_avg_ms * 1e-3) / 1e9
 
     if args.calib_copy:
@@ -289,7 +303,7 @@ def main():
         "ms_per_step": round(ms_step, 4),
         "steps_per_s": round(steps_per_s, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": cfg.act_dtype if cfg.expert_dtype != "fp8" else "bf16+fp8w",
+        "dtype": cfg.act_dtype if cfg.expert_dtype in ("f32", "bf16") else f"bf16+{cfg.expert_dtype}w",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) caches, uniform canvas)",
         "config": {"workload": f"{args.workload}: {cfg.name}", "layers": cfg.n_layers, "batch": B, "canvas": L,
                    "prefix": cfg.prefix, "vocab": cfg.vocab, "d_model": cfg.d_model, "experts": cfg.n_experts,

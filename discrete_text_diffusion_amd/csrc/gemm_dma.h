@@ -90,6 +90,10 @@ struct GemmDma {
     }
   }
 
+  // weights of the activation type carry no scales
+  template <class ARow, class BRow, class SRow>
+  DG_DEV void setup(ARow arow, BRow brow, SRow) { setup(arow, brow); }
+
   // stage `stage` <- K tiles kt * KPS .. kt * KPS + KPS - 1
   DG_DEV void issue(char* lds, int kt, int stage) {
     const int wave = threadIdx.x >> 6;

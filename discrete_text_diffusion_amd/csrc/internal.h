@@ -8,7 +8,7 @@ namespace dg {
 constexpr int MAX_BATCH = 64;     // canvases per call (prefix lengths travel as kernel arguments)
 constexpr int GROUP_BM = 32;      // rows per expert tile of the grouped GEMMs
 
-enum WKind { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };
+enum WKind { W_F32 = 0, W_BF16 = 1, W_FP8 = 2, W_MXFP4 = 3 };
 enum Epi { EPI_STORE_F32 = 0, EPI_ADD_F32 = 1, EPI_STORE_ACT = 2, EPI_SWIGLU = 3, EPI_QKV = 4 };
 
 struct DenseArgs {
@@ -38,8 +38,10 @@ hipError_t launch_rope_table(float2* tab, int rows, int rows_per_canvas, int hea
 struct GroupedArgs {
   int epi;
   const void* A; int64_t lda; const int32_t* a_tok;  // A row of grouped position p: a_tok[p] (or p)
-  const void* B; const void* B2; int64_t ldb; int64_t b_estride;
-  const uint16_t* sB; const uint16_t* sB2; int64_t s_estride;
+  const void* B; const void* B2; int64_t ldb; int64_t b_estride;  // ldb, b_estride in storage units
+  // quantised weights: fp8 per-row bf16 scales [E][N], or MXFP4 e8m0 block scales [E][N][K/32];
+  // s_estride = bytes per expert, s_ld = bytes per weight row (MXFP4)
+  const void* sB; const void* sB2; int64_t s_estride; int64_t s_ld;
   int N, K;
   const int32_t* work; const int32_t* n_items;       // (expert, first row) per tile
   const int32_t* offsets; const int32_t* counts;
@@ -47,7 +49,7 @@ struct GroupedArgs {
   // shared expert (every row, in row order), tiles of GROUP_BM rows before the routed tiles
   const void* shA; int64_t sh_lda;
   const void* shB; const void* shB2; int64_t sh_ldb;
-  const uint16_t* sh_sB; const uint16_t* sh_sB2;
+  const void* sh_sB; const void* sh_sB2; int64_t sh_s_ld;
   int shN, shK, sh_rows;
   void* shC; int64_t sh_ldc;
   int nt_r, nt_s, sh_blocks, n_sh_items;              // filled by the launcher

@@ -18,7 +18,7 @@ namespace dg {
 // let two blocks share a CU (a single block per CU with a ring twice as deep was slower).
 constexpr int ring_stages(int stage_bytes) { return stage_bytes <= 20480 ? 4 : 3; }
 template <class TA, class TB, int BM, int BN, int WM, int WN, int NS = 0, int KPS = 1>
-using TileFor = std::conditional_t<sizeof(TB) == 1, GemmTile<TA, TB, BM, BN, WM, WN, 2>,
+using TileFor = std::conditional_t<sizeof(TB) == 1, GemmTile<TA, TB, BM, BN, WM, WN, 4>,
                                    GemmDma<TA, BM, BN, WM, WN, NS ? NS : ring_stages((BM + BN) * 128), DMA_STREAM, KPS>>;
 
 // ---------------------------------------------------------------- B-row maps ----------------
@@ -217,8 +217,8 @@ hipError_t launch_rope_table(float2* tab, int rows, int rows_per_canvas, int hea
 // n0 (gate/up rows paired for SwiGLU) over the full K, then the tile's epilogue.
 template <class G, int BN, int WN, int EPI, class TA, class TB>
 DG_DEV void grouped_tile(char* lds, const TA* A, int64_t lda, const int32_t* a_tok, int row0, int rows,
-                         const TB* B, const TB* B2, int64_t ldb, const bf16_t* sB, const bf16_t* sB2, int N,
-                         int K, int n0, void* Cout, int64_t ldc) {
+                         const TB* B, const TB* B2, int64_t ldb, const char* sB, const char* sB2, int64_t s_ld,
+                         int N, int K, int n0, void* Cout, int64_t ldc) {
   auto arow = [&](int r) -> const TA* {
     if (r >= rows) return nullptr;
     const int src = a_tok ? a_tok[row0 + r] : row0 + r;
@@ -236,8 +236,25 @@ DG_DEV void grouped_tile(char* lds, const TA* A, int64_t lda, const int32_t* a_t
       return n < N ? B + (int64_t)n * ldb : nullptr;
     }
   };
+  // MXFP4: the block-scale bytes of weight row r, paired like its weights
+  auto srow = [&](int r) -> const uint8_t* {
+    if constexpr (is_fp4_v<TB>) {
+      if constexpr (EPI == EPI_SWIGLU) {
+        int u, half, c;
+        paired_col<BN>(r, u, half, c);
+        const int oc = n0 / 2 + u * 16 + c;
+        if (oc >= N) return nullptr;
+        return reinterpret_cast<const uint8_t*>(half ? sB2 : sB) + (int64_t)oc * s_ld;
+      } else {
+        const int n = n0 + r;
+        return n < N ? reinterpret_cast<const uint8_t*>(sB) + (int64_t)n * s_ld : nullptr;
+      }
+    } else {
+      return nullptr;
+    }
+  };
   G g;
-  g.setup(arow, brow);
+  g.setup(arow, brow, srow);
   f32x4_v acc[G::FM][G::FN];
   g.run(lds, K, acc);
 
@@ -249,7 +266,10 @@ DG_DEV void grouped_tile(char* lds, const TA* A, int64_t lda, const int32_t* a_t
       const int oc = n0 / 2 + u * 16 + (lane & 15);
       if (oc >= N) continue;
       float sg = 1.f, su = 1.f;
-      if constexpr (sizeof(TB) == 1) { sg = bf2f(sB[oc]); su = bf2f(sB2[oc]); }
+      if constexpr (is_fp8_v<TB>) {
+        sg = bf2f(reinterpret_cast<const bf16_t*>(sB)[oc]);
+        su = bf2f(reinterpret_cast<const bf16_t*>(sB2)[oc]);
+      }
 #pragma unroll
       for (int i = 0; i < G::FM; ++i)
 #pragma unroll
@@ -267,7 +287,7 @@ DG_DEV void grouped_tile(char* lds, const TA* A, int64_t lda, const int32_t* a_t
       const int n = n0 + G::col_of(j);
       if (n >= N) continue;
       float sc = 1.f;
-      if constexpr (sizeof(TB) == 1) sc = bf2f(sB[n]);
+      if constexpr (is_fp8_v<TB>) sc = bf2f(reinterpret_cast<const bf16_t*>(sB)[n]);
 #pragma unroll
       for (int i = 0; i < G::FM; ++i)
 #pragma unroll
@@ -302,8 +322,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_grouped_kernel(GroupedArgs 
     grouped_tile<G, BN, WN, EPI>(lds, static_cast<const TA*>(p.A), p.lda, p.a_tok, p.offsets[e] + m0,
                                  min(BM, p.counts[e] - m0), static_cast<const TB*>(p.B) + (int64_t)e * p.b_estride,
                                  p.B2 ? static_cast<const TB*>(p.B2) + (int64_t)e * p.b_estride : nullptr, p.ldb,
-                                 p.sB ? p.sB + (int64_t)e * p.s_estride : nullptr,
-                                 p.sB2 ? p.sB2 + (int64_t)e * p.s_estride : nullptr, p.N, p.K,
+                                 p.sB ? static_cast<const char*>(p.sB) + (int64_t)e * p.s_estride : nullptr,
+                                 p.sB2 ? static_cast<const char*>(p.sB2) + (int64_t)e * p.s_estride : nullptr,
+                                 p.s_ld, p.N, p.K,
                                  (rid - item * p.nt_r) * BN, p.C, p.ldc);
   } else {
     const int j = id >> 3;
@@ -311,7 +332,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_grouped_kernel(GroupedArgs 
     if (nt >= p.nt_s) return;
     grouped_tile<GS, BN, WN, EPI>(lds, static_cast<const TA*>(p.shA), p.sh_lda, nullptr, it * BMS,
                                   min(BMS, p.sh_rows - it * BMS), static_cast<const TB*>(p.shB),
-                                  static_cast<const TB*>(p.shB2), p.sh_ldb, p.sh_sB, p.sh_sB2, p.shN, p.shK, nt * BN,
+                                  static_cast<const TB*>(p.shB2), p.sh_ldb, static_cast<const char*>(p.sh_sB),
+                                  static_cast<const char*>(p.sh_sB2), p.sh_s_ld, p.shN, p.shK, nt * BN,
                                   p.shC, p.sh_ldc);
   }
 }
@@ -407,8 +429,8 @@ static hipError_t launch_grouped_t(GroupedArgs a, int n_eff, int sh_eff, int max
 
 // Routed tiles of GROUP_BM rows x 128 weight rows on 4 waves.  Weights of the activation type: the
 // shared expert in tiles of 2 x GROUP_BM rows (its ring one stage shorter, so the launch still
-// fits two blocks per CU); fp8 weights (register-staged widening engine): GROUP_BM-row tiles for
-// both.
+// fits two blocks per CU); fp8 / MXFP4 weights (register-staged widening engine): GROUP_BM-row
+// tiles for both.
 template <class TA, class TB>
 static hipError_t grouped_dispatch(const GroupedArgs& a, int max_items, hipStream_t s) {
   if constexpr (sizeof(TB) == 1) {
@@ -425,6 +447,7 @@ static hipError_t grouped_dispatch(const GroupedArgs& a, int max_items, hipStrea
 hipError_t launch_grouped(const GroupedArgs& a, int act_bf16, int w_kind, int max_items, hipStream_t s) {
   if (!act_bf16) return grouped_dispatch<float, float>(a, max_items, s);
   if (w_kind == W_FP8) return grouped_dispatch<bf16_t, fp8_t>(a, max_items, s);
+  if (w_kind == W_MXFP4) return grouped_dispatch<bf16_t, fp4x2_t>(a, max_items, s);
   return grouped_dispatch<bf16_t, bf16_t>(a, max_items, s);
 }
 

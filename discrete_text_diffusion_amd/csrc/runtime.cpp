@@ -69,7 +69,8 @@ inline size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 inline int up8(int x) { return (x + 7) / 8 * 8; }
 inline int act_bytes(const dg_model_desc& d) { return d.act_dtype == DG_BF16 ? 2 : 4; }
 inline int w_kind(const dg_model_desc& d) {
-  return d.expert_dtype == DG_FP8E4M3 ? W_FP8 : d.expert_dtype == DG_BF16 ? W_BF16 : W_F32;
+  return d.expert_dtype == DG_FP8E4M3 ? W_FP8 : d.expert_dtype == DG_MXFP4 ? W_MXFP4
+                                      : d.expert_dtype == DG_BF16 ? W_BF16 : W_F32;
 }
 inline bool is_global(const dg_model_desc& d, int l) {
   return d.window <= 0 || d.global_every <= 0 || (l + 1) % d.global_every == 0;
@@ -403,15 +404,21 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn, bool xhat_ready, const vo
   GroupedArgs ga{};
   ga.epi = EPI_SWIGLU;
   ga.A = at<void>(ws, w.xhat); ga.lda = d.d_model; ga.a_tok = at<int32_t>(ws, w.tok);
-  ga.B = L.w_gate; ga.B2 = L.w_up; ga.ldb = d.d_model; ga.b_estride = (int64_t)d.expert_hidden * d.d_model;
-  ga.sB = (const uint16_t*)L.s_gate; ga.sB2 = (const uint16_t*)L.s_up; ga.s_estride = d.expert_hidden;
+  // storage units per weight row: MXFP4 packs two codes per byte and has one scale byte per 32
+  // elements; fp8 has one bf16 scale per row
+  const bool mx = wk == W_MXFP4;
+  const int pk = mx ? 2 : 1;
+  ga.B = L.w_gate; ga.B2 = L.w_up; ga.ldb = d.d_model / pk;
+  ga.b_estride = (int64_t)d.expert_hidden * d.d_model / pk;
+  ga.sB = L.s_gate; ga.sB2 = L.s_up; ga.s_ld = mx ? d.d_model / 32 : 2;
+  ga.s_estride = (int64_t)d.expert_hidden * ga.s_ld;
   ga.N = d.expert_hidden; ga.K = d.d_model;
   ga.work = at<int32_t>(ws, w.work); ga.n_items = at<int32_t>(ws, w.n_items);
   ga.offsets = at<int32_t>(ws, w.offsets); ga.counts = at<int32_t>(ws, w.counts);
   ga.C = at<void>(ws, w.a_grp); ga.ldc = d.expert_hidden;
   ga.shA = at<void>(ws, w.xhat); ga.sh_lda = d.d_model;
-  ga.shB = L.sh_gate; ga.shB2 = L.sh_up; ga.sh_ldb = d.d_model;
-  ga.sh_sB = (const uint16_t*)L.sh_s_gate; ga.sh_sB2 = (const uint16_t*)L.sh_s_up;
+  ga.shB = L.sh_gate; ga.shB2 = L.sh_up; ga.sh_ldb = d.d_model / pk;
+  ga.sh_sB = L.sh_s_gate; ga.sh_sB2 = L.sh_s_up; ga.sh_s_ld = ga.s_ld;
   ga.shN = d.shared_hidden; ga.shK = d.d_model; ga.sh_rows = R;
   ga.shC = at<void>(ws, w.sh_a); ga.sh_ldc = d.shared_hidden;
   {
@@ -421,14 +428,16 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn, bool xhat_ready, const vo
   GroupedArgs da{};
   da.epi = EPI_STORE_F32;
   da.A = at<void>(ws, w.a_grp); da.lda = d.expert_hidden; da.a_tok = nullptr;
-  da.B = L.w_down; da.B2 = nullptr; da.ldb = d.expert_hidden; da.b_estride = (int64_t)d.d_model * d.expert_hidden;
-  da.sB = (const uint16_t*)L.s_down; da.sB2 = nullptr; da.s_estride = d.d_model;
+  da.B = L.w_down; da.B2 = nullptr; da.ldb = d.expert_hidden / pk;
+  da.b_estride = (int64_t)d.d_model * d.expert_hidden / pk;
+  da.sB = L.s_down; da.sB2 = nullptr; da.s_ld = mx ? d.expert_hidden / 32 : 2;
+  da.s_estride = (int64_t)d.d_model * da.s_ld;
   da.N = d.d_model; da.K = d.expert_hidden;
   da.work = ga.work; da.n_items = ga.n_items; da.offsets = ga.offsets; da.counts = ga.counts;
   da.C = at<void>(ws, w.y); da.ldc = d.d_model;
   da.shA = at<void>(ws, w.sh_a); da.sh_lda = d.shared_hidden;
-  da.shB = L.sh_down; da.shB2 = nullptr; da.sh_ldb = d.shared_hidden;
-  da.sh_sB = (const uint16_t*)L.sh_s_down; da.sh_sB2 = nullptr;
+  da.shB = L.sh_down; da.shB2 = nullptr; da.sh_ldb = d.shared_hidden / pk;
+  da.sh_sB = L.sh_s_down; da.sh_sB2 = nullptr; da.sh_s_ld = mx ? d.shared_hidden / 32 : 2;
   da.shN = d.d_model; da.shK = d.shared_hidden; da.sh_rows = R;
   da.shC = at<void>(ws, w.sh_parts); da.sh_ldc = d.d_model;
   {
@@ -455,8 +464,9 @@ dg_status check_desc(const dg_model_desc& d) {
   if (d.n_experts > 256 || d.n_experts % 4 || d.top_k > 16 || d.top_k > d.n_experts)
     return fail(DG_EUNSUPPORTED, "need top_k <= 16, top_k <= n_experts <= 256 and n_experts %% 4 == 0");
   if (d.act_dtype != DG_F32 && d.act_dtype != DG_BF16) return fail(DG_EUNSUPPORTED, "act_dtype must be F32 or BF16");
-  if (!(d.expert_dtype == d.act_dtype || (d.act_dtype == DG_BF16 && d.expert_dtype == DG_FP8E4M3)))
-    return fail(DG_EUNSUPPORTED, "expert_dtype must equal act_dtype, or be FP8E4M3 with BF16 activations");
+  if (!(d.expert_dtype == d.act_dtype ||
+        (d.act_dtype == DG_BF16 && (d.expert_dtype == DG_FP8E4M3 || d.expert_dtype == DG_MXFP4))))
+    return fail(DG_EUNSUPPORTED, "expert_dtype must equal act_dtype, or be FP8E4M3 / MXFP4 with BF16 activations");
   if (!(d.norm_eps >= 0.f) || !(d.rope_theta > 0.f)) return fail(DG_EINVAL, "bad norm_eps or rope_theta");
   if (d.window > 0 && d.global_every > 0 && d.window < 1) return fail(DG_EINVAL, "bad window");
   return DG_OK;
@@ -581,14 +591,14 @@ dg_status dg_create(const dg_model_desc* desc, const dg_weights* wts, dg_ctx** o
   dg_status st = check_desc(*desc);
   if (st != DG_OK) return st;
   if (!wts->layers || !wts->final_norm) return fail(DG_EINVAL, "weights: NULL layer table or final_norm");
-  const bool fp8 = desc->expert_dtype == DG_FP8E4M3;
+  const bool fp8 = desc->expert_dtype == DG_FP8E4M3 || desc->expert_dtype == DG_MXFP4;
   for (int l = 0; l < desc->n_layers; ++l) {
     const dg_layer_weights& L = wts->layers[l];
     if (!L.attn_norm || !L.w_qkv || !L.w_o || !L.ffn_norm || !L.w_router || !L.w_gate || !L.w_up || !L.w_down ||
         !L.sh_gate || !L.sh_up || !L.sh_down)
       return fail(DG_EINVAL, "weights: layer %d has a NULL matrix", l);
     if (fp8 && (!L.s_gate || !L.s_up || !L.s_down || !L.sh_s_gate || !L.sh_s_up || !L.sh_s_down))
-      return fail(DG_EINVAL, "weights: layer %d: FP8 experts need every scale", l);
+      return fail(DG_EINVAL, "weights: layer %d: FP8 / MXFP4 experts need every scale", l);
     const void* ptrs[] = {L.attn_norm, L.w_qkv, L.w_o, L.ffn_norm, L.w_router, L.router_bias, L.w_gate, L.w_up,
                           L.w_down, L.sh_gate, L.sh_up, L.sh_down};
     for (const void* q : ptrs)

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdg.so")
 
 DG_OK, DG_EINVAL, DG_EUNSUPPORTED, DG_EWORKSPACE, DG_EHIP, DG_ENONFINITE = 0, -1, -2, -3, -4, -5
-DG_F32, DG_BF16, DG_FP8E4M3 = 0, 1, 2
+DG_F32, DG_BF16, DG_FP8E4M3, DG_MXFP4 = 0, 1, 2, 3
 DG_KAPPA_LINEAR, DG_KAPPA_QUADRATIC, DG_KAPPA_COSINE = 0, 1, 2
 
 

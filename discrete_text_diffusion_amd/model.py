@@ -2,7 +2,7 @@
 
 `Model` wraps one dg_ctx plus the prefix KV cache description; its methods call the
 same-named C entry points.  Any object with the model-shape attributes (n_layers, d_model, ...,
-act_dtype "f32"/"bf16", expert_dtype "f32"/"bf16"/"fp8") describes the model.
+act_dtype "f32"/"bf16", expert_dtype "f32"/"bf16"/"fp8"/"mxfp4") describes the model.
 """
 from __future__ import annotations
 
@@ -12,7 +12,7 @@ import torch
 
 from . import dg
 
-_DT = {"f32": dg.DG_F32, "bf16": dg.DG_BF16, "fp8": dg.DG_FP8E4M3}
+_DT = {"f32": dg.DG_F32, "bf16": dg.DG_BF16, "fp8": dg.DG_FP8E4M3, "mxfp4": dg.DG_MXFP4}
 
 
 def model_desc(cfg) -> dg.ModelDesc:

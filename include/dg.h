@@ -48,7 +48,10 @@ typedef enum {
   DG_ENONFINITE = -5     /* a non-finite hidden state or logit was seen (dg_query_status) */
 } dg_status;
 
-typedef enum { DG_F32 = 0, DG_BF16 = 1, DG_FP8E4M3 = 2 } dg_dtype;
+/* MXFP4 is the OCP microscaling format: e2m1 elements (1 sign, 2 exponent bits with bias 1, 1
+ * mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) in blocks of 32 consecutive K-elements
+ * sharing one e8m0 scale byte s (value 2^(s - 127); 255 is NaN). */
+typedef enum { DG_F32 = 0, DG_BF16 = 1, DG_FP8E4M3 = 2, DG_MXFP4 = 3 } dg_dtype;
 
 /* Noise schedule kappa_t: decreasing from kappa_0 = 1 to kappa_1 = 0 [TR §Forward Process]. */
 typedef enum {
@@ -62,7 +65,8 @@ typedef enum {
  * Supported: head_dim in {64, 128, 256}; n_q_heads % n_kv_heads == 0; d_model, expert_hidden
  * and shared_hidden multiples of 64; vocab % 16 == 0; top_k <= n_experts <= 256, n_experts % 4 == 0, top_k <= 16;
  * act_dtype F32 or BF16;
- * expert_dtype = act_dtype, or FP8E4M3 when act_dtype is BF16 (weights-only fp8, bf16 math). */
+ * expert_dtype = act_dtype, or FP8E4M3 / MXFP4 when act_dtype is BF16 (weights-only: the codes are
+ * widened exactly to bf16 and the math is bf16 MFMA). */
 typedef struct {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim;
   int32_t n_experts, top_k, expert_hidden, shared_hidden, vocab;
@@ -74,7 +78,11 @@ typedef struct {
 
 /* One layer's weights: device pointers, borrowed until dg_destroy().  Every matrix is stored
  * [out][in] (both GEMM operands K-contiguous).  Expert matrices use expert_dtype; with
- * FP8E4M3 each has a bf16 scale per output row (s_*), and the weight is code * scale. */
+ * FP8E4M3 each has a bf16 scale per output row (s_*), and the weight is code * scale.  With
+ * MXFP4 an expert matrix [N][K] is stored as N rows of K/2 bytes (element 2j in the low nibble of
+ * byte j) and its s_* array holds N rows of K/32 e8m0 bytes (one per 32 consecutive elements):
+ * weight = e2m1(code) * 2^(s - 127).  Matrix pointers must be 16-byte aligned; scale arrays have
+ * no alignment requirement. */
 typedef struct {
   const void *attn_norm;   /* [d] act, RMSNorm gain before attention                       */
   const void *w_qkv;       /* [(Hq + 2 Hkv) dh][d] act: q heads, then k heads, then v heads */
@@ -84,11 +92,12 @@ typedef struct {
   const float *router_bias;/* [E] fp32 added to the router logits, or NULL                  */
   const void *w_gate, *w_up;      /* [E][f][d] expert dtype                                 */
   const void *w_down;             /* [E][d][f]                                              */
-  const void *s_gate, *s_up;      /* [E][f] bf16 scales (FP8 only, else NULL)               */
-  const void *s_down;             /* [E][d]                                                 */
+  const void *s_gate, *s_up;      /* [E][f] bf16 (FP8), [E][f][d/32] e8m0 (MXFP4), else NULL */
+  const void *s_down;             /* [E][d] bf16 (FP8), [E][d][f/32] e8m0 (MXFP4)            */
   const void *sh_gate, *sh_up;    /* [fs][d] shared expert                                  */
   const void *sh_down;            /* [d][fs]                                                */
-  const void *sh_s_gate, *sh_s_up, *sh_s_down; /* [fs], [fs], [d] bf16 scales (FP8 only)  */
+  const void *sh_s_gate, *sh_s_up, *sh_s_down; /* [fs], [fs], [d] bf16 scales (FP8) or
+                                  [fs][d/32], [fs][d/32], [d][fs/32] e8m0 (MXFP4)          */
 } dg_layer_weights;
 
 typedef struct {

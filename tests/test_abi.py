@@ -53,10 +53,11 @@ def test_create_rejects_unsupported_shapes_and_null_weights():
     with pytest.raises(dg.DGError) as e:
         dg.dg_create(bad, w)
     assert e.value.status == dg.DG_EUNSUPPORTED and "head_dim" in dg.dg_last_error()
-    bad = model_desc(configs.C0.replace(act_dtype="f32", expert_dtype="fp8"))
-    with pytest.raises(dg.DGError) as e:
-        dg.dg_create(bad, w)
-    assert e.value.status == dg.DG_EUNSUPPORTED
+    for q in ("fp8", "mxfp4"):                  # quantised experts need bf16 activations
+        bad = model_desc(configs.C0.replace(act_dtype="f32", expert_dtype=q))
+        with pytest.raises(dg.DGError) as e:
+            dg.dg_create(bad, w)
+        assert e.value.status == dg.DG_EUNSUPPORTED
     ok = model_desc(configs.C0)
     with pytest.raises(dg.DGError) as e:
         dg.dg_create(ok, w)                     # NULL matrices

@@ -121,6 +121,15 @@ def test_fp8_experts_batched_layer_parity():
     _layer_parity(cfg, 0, 2e-2)
 
 
+def test_mxfp4_experts_layer_parity():
+    """MXFP4 expert weights (e2m1 codes, one e8m0 scale per 32 inputs; weights-only, bf16 math):
+    one global layer over a 2048-token prefix, and two Zipf-routed canvases."""
+    _layer_parity(configs.C1.replace(expert_dtype="mxfp4"), 0, 2e-2)
+    cfg = configs.C4.replace(expert_dtype="mxfp4", n_layers=1, batch=2, prefix=1024, resid_input=True,
+                             window=0, global_every=0)
+    _layer_parity(cfg, 0, 2e-2)
+
+
 def test_layer_is_deterministic():
     cfg = configs.C1
     model, W, kv = build(cfg)
