@@ -15,6 +15,7 @@
 // output rows/columns that the caller never stores.
 #pragma once
 #include "common.h"
+#include "gemm_core.h"
 
 namespace dg {
 
@@ -165,6 +166,165 @@ struct GemmDma {
       compute(lds + (kt % NS) * STAGE, acc);
     }
     __syncthreads();   // the LDS ring may be reused by the caller after this
+  }
+
+  DG_DEV static int row_of(int i, int e) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    return (wave / WN) * FM * 16 + i * 16 + 4 * (lane >> 4) + e;
+  }
+  DG_DEV static int col_of(int j) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    return (wave % WN) * FN * 16 + j * 16 + (lane & 15);
+  }
+};
+
+// Weights-only quantised B on the same direct-to-LDS ring: fp8 e4m3 codes (their per-row scale is
+// applied by the caller's epilogue) or MXFP4 (e2m1 codes with one e8m0 scale per 32 elements).  A
+// stage is 64 K-elements: A (bf16) as 128-byte rows in the GemmDma layout; B as its raw codes, 64
+// bytes (fp8) or 32 bytes (MXFP4) per row, the 16-byte chunk c of row r stored in slot
+// c ^ ((r >> 2) & 3) (fp8) or c ^ ((r >> 3) & 1) (MXFP4) so 16-row fragment reads hit distinct
+// banks; MXFP4 scales as one 32-bit word per (row, 32-element block) (a byte-sized direct load
+// writes each byte zero-extended to a word).  Codes are widened to bf16 in registers just before
+// the MFMA, so no widened copy passes through LDS.
+// K order inside a stage: lane group kg = lane >> 4 owns elements [16 kg, 16 kg + 16) of every
+// row (half an MXFP4 scale block, one fp8 chunk), its MFMA chunk c in {0, 1} the elements
+// 16 kg + 8 c .. + 7; A is read with the same map, so the sum over the stage is unchanged.
+template <class TB, int BM, int BN, int WM, int WN, int NS>
+struct GemmDmaQ {
+  static constexpr bool FP4 = is_fp4_v<TB>;
+  static_assert(FP4 || is_fp8_v<TB>, "quantised weights");
+  static constexpr int NW = WM * WN;
+  static constexpr int FM = BM / WM / 16, FN = BN / WN / 16;
+  static_assert(FM >= 1 && FN >= 1, "wave tile at least 16 x 16");
+  static constexpr int KT = 64;                          // K elements per stage
+  static constexpr int BROW = FP4 ? 32 : 64;             // code bytes per B row per stage
+  static constexpr int BRPI = 1024 / BROW;               // B rows per load instruction
+  static constexpr int IA = BM / (8 * NW), IB = BN / (BRPI * NW), IS = FP4 ? 1 : 0;
+  static_assert(IA * 8 * NW == BM && IB * BRPI * NW == BN, "rows per tile: whole load instructions");
+  static_assert(!FP4 || BN * 2 == 64 * NW, "MXFP4: one scale entry per lane of each wave");
+  static constexpr int LPT = IA + IB + IS;               // load instructions per wave per stage
+  static constexpr int A_BYTES = BM * 128, B_BYTES = BN * BROW, S_BYTES = FP4 ? BN * 2 * 4 : 0;
+  static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+  static constexpr int LDS_BYTES = NS * STAGE;
+  static_assert(NS >= 2 && (NS - 2) * LPT < 64, "stages / vmcnt range");
+
+  const char* a_src[IA];
+  const char* b_src[IB];
+  const uint8_t* s_src;
+
+  // arow / brow as in GemmDma; srow(r): the scale bytes of B row r (MXFP4) or nullptr
+  template <class ARow, class BRow, class SRow>
+  DG_DEV void setup(ARow arow, BRow brow, SRow srow) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    {
+      const int rr = lane >> 3, slot = lane & 7;
+#pragma unroll
+      for (int i = 0; i < IA; ++i) {
+        const int r = (wave + NW * i) * 8 + rr;
+        const char* p = reinterpret_cast<const char*>(arow(r));
+        if (!p) p = reinterpret_cast<const char*>(arow(0));
+        a_src[i] = p + ((slot ^ ((r >> 1) & 7)) * 16);
+      }
+    }
+    {
+      constexpr int CPR = BROW / 16;                     // 16-byte chunks per row
+      const int rr = lane / CPR, slot = lane % CPR;
+#pragma unroll
+      for (int i = 0; i < IB; ++i) {
+        const int r = (wave + NW * i) * BRPI + rr;
+        const char* p = reinterpret_cast<const char*>(brow(r));
+        if (!p) p = reinterpret_cast<const char*>(brow(0));
+        const int sw = FP4 ? ((r >> 3) & 1) : ((r >> 2) & 3);
+        b_src[i] = p + ((slot ^ sw) * 16);
+      }
+    }
+    if constexpr (FP4) {
+      const int e = wave * 64 + lane, r = e >> 1;        // entry e = (row r, block e & 1)
+      const uint8_t* sp = srow(r);
+      if (!sp) sp = srow(0);
+      s_src = sp + (e & 1);
+    }
+  }
+
+  DG_DEV void issue(char* lds, int kt, int stage) {
+    const int wave = threadIdx.x >> 6;
+    char* st = lds + stage * STAGE;
+#pragma unroll
+    for (int i = 0; i < IA; ++i) dma16(a_src[i] + (size_t)kt * 128, st + (wave + NW * i) * 8 * 128);
+#pragma unroll
+    for (int i = 0; i < IB; ++i)
+      dma16<DMA_STREAM>(b_src[i] + (size_t)kt * BROW, st + A_BYTES + (wave + NW * i) * 1024);
+    if constexpr (FP4)
+      __builtin_amdgcn_global_load_lds((const DG_GLOBAL_AS void*)(s_src + (size_t)kt * 2),
+                                       (DG_LDS_AS void*)(st + A_BYTES + B_BYTES + wave * 256), 1, 0, DMA_CACHED);
+  }
+
+  template <int P>
+  DG_DEV static void wait_pending(int pending) {
+    if constexpr (P > 1) {
+      if (pending >= P) { wait_vm<(P - 1) * LPT>(); return; }
+      wait_pending<P - 1>(pending);
+    } else {
+      wait_vm<0>();
+    }
+  }
+  DG_DEV static void wait_oldest(int pending) { wait_pending<NS - 1>(pending); }
+
+  DG_DEV static void compute(const char* st, f32x4_v (&acc)[FM][FN]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int l16 = lane & 15, kg = lane >> 4, swa = l16 >> 1;
+    u32x4 bfr[FN][2];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = wn * FN * 16 + j * 16 + l16;
+      if constexpr (FP4) {
+        // elements [16 kg, 16 kg + 16) = bytes [8 kg, 8 kg + 8) of the row: chunk kg >> 1, half kg & 1
+        const char* row = st + A_BYTES + n * 32;
+        const uint2 w = *reinterpret_cast<const uint2*>(row + (((kg >> 1) ^ ((n >> 3) & 1)) * 16) + (kg & 1) * 8);
+        const uint32_t s = *reinterpret_cast<const uint32_t*>(st + A_BYTES + B_BYTES + (n * 2 + (kg >> 1)) * 4);
+        const float sc = e8m0_scale(s & 0xffu);
+        bfr[j][0] = widen_fp4_word(w.x, sc);
+        bfr[j][1] = widen_fp4_word(w.y, sc);
+      } else {
+        const char* row = st + A_BYTES + n * 64;
+        const u32x4 w = *reinterpret_cast<const u32x4*>(row + ((kg ^ ((n >> 2) & 3)) * 16));
+        bfr[j][0] = widen_fp8_lo(w);
+        bfr[j][1] = widen_fp8_hi(w);
+      }
+    }
+    const char* la = st + (wm * FM * 16 + l16) * 128;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int so = (((2 * kg + c) ^ swa)) * 16;     // A elements 16 kg + 8 c .. + 7
+      u32x4 af[FM];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const u32x4*>(la + i * 16 * 128 + so);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) Mfma<bf16_t>::mma(acc[i][j], af[i], bfr[j][c]);
+    }
+  }
+
+  DG_DEV void run(char* lds, int K, f32x4_v (&acc)[FM][FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+    const int nk = K / KT;
+    int issued = 0;
+    for (; issued < NS - 1 && issued < nk; ++issued) issue(lds, issued, issued);
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_oldest(issued - kt);
+      lds_barrier();
+      if (issued < nk) {
+        issue(lds, issued, issued % NS);
+        ++issued;
+      }
+      compute(lds + (kt % NS) * STAGE, acc);
+    }
+    __syncthreads();
   }
 
   DG_DEV static int row_of(int i, int e) {

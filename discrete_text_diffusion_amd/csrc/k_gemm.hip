@@ -20,6 +20,13 @@ constexpr int ring_stages(int stage_bytes) { return stage_bytes <= 20480 ? 4 : 3
 template <class TA, class TB, int BM, int BN, int WM, int WN, int NS = 0, int KPS = 1>
 using TileFor = std::conditional_t<sizeof(TB) == 1, GemmTile<TA, TB, BM, BN, WM, WN, 4>,
                                    GemmDma<TA, BM, BN, WM, WN, NS ? NS : ring_stages((BM + BN) * 128), DMA_STREAM, KPS>>;
+// grouped (expert) GEMMs: fp8 weights stream as raw codes on the direct-to-LDS ring, widened in
+// registers (12 KB stages x 6, two blocks per CU); MXFP4 weights go through the register-staged
+// engine, which measured faster for them (its stages carry 64 elements of all 128 rows widened
+// once per block, where the ring's per-stage scale loads and short stages cost more)
+template <class TA, class TB, int BM, int BN, int WM, int WN, int NS = 0>
+using GroupTileFor = std::conditional_t<is_fp8_v<TB>, GemmDmaQ<TB, BM, BN, WM, WN, 6>,
+                                        TileFor<TA, TB, BM, BN, WM, WN, NS>>;
 
 // ---------------------------------------------------------------- B-row maps ----------------
 // A tile column block of 16 columns; "paired" maps put the two members of a pair (gate/up, or
@@ -310,8 +317,8 @@ DG_DEV void grouped_tile(char* lds, const TA* A, int64_t lda, const int32_t* a_t
 // of the two tile shapes' rings.
 template <class TA, class TB, int BM, int BMS, int BN, int WM, int WN, int EPI, int NS = 0>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_grouped_kernel(GroupedArgs p) {
-  using G = TileFor<TA, TB, BM, BN, WM, WN, NS>;
-  using GS = TileFor<TA, TB, BMS, BN, WM, WN, NS>;
+  using G = GroupTileFor<TA, TB, BM, BN, WM, WN, NS>;
+  using GS = GroupTileFor<TA, TB, BMS, BN, WM, WN, NS>;
   extern __shared__ __align__(16) char lds[];
   const int id = blockIdx.x;
   if (id >= p.sh_blocks) {
@@ -410,8 +417,8 @@ hipError_t launch_dense(const DenseArgs& a, int act_bf16, int w_kind, hipStream_
 
 template <class TA, class TB, int BM, int BMS, int BN, int WM, int WN, int EPI, int NS = 0>
 static hipError_t launch_grouped_t(GroupedArgs a, int n_eff, int sh_eff, int max_items, hipStream_t s) {
-  using G = TileFor<TA, TB, BM, BN, WM, WN, NS>;
-  using GS = TileFor<TA, TB, BMS, BN, WM, WN, NS>;
+  using G = GroupTileFor<TA, TB, BM, BN, WM, WN, NS>;
+  using GS = GroupTileFor<TA, TB, BMS, BN, WM, WN, NS>;
   constexpr size_t LDS = G::LDS_BYTES > GS::LDS_BYTES ? G::LDS_BYTES : GS::LDS_BYTES;
   a.nt_r = (n_eff + BN - 1) / BN;
   a.nt_s = (sh_eff + BN - 1) / BN;
@@ -429,8 +436,8 @@ static hipError_t launch_grouped_t(GroupedArgs a, int n_eff, int sh_eff, int max
 
 // Routed tiles of GROUP_BM rows x 128 weight rows on 4 waves.  Weights of the activation type: the
 // shared expert in tiles of 2 x GROUP_BM rows (its ring one stage shorter, so the launch still
-// fits two blocks per CU); fp8 / MXFP4 weights (register-staged widening engine): GROUP_BM-row
-// tiles for both.
+// fits two blocks per CU); fp8 / MXFP4 weights (raw codes on the ring, widened in registers):
+// GROUP_BM-row tiles for both.
 template <class TA, class TB>
 static hipError_t grouped_dispatch(const GroupedArgs& a, int max_items, hipStream_t s) {
   if constexpr (sizeof(TB) == 1) {
