@@ -16,7 +16,7 @@ namespace dg {
 // bf16/fp32 weights stream through the direct-to-LDS engine; fp8 weights take the
 // register-staged engine, which widens them to bf16 on the way into LDS.  Rings of 3-4 stages
 // let two blocks share a CU (a single block per CU with a ring twice as deep was slower).
-constexpr int ring_stages(int stage_bytes) { return stage_bytes <= 20480 ? 4 : 3; }
+constexpr int ring_stages(int stage_bytes) { return stage_bytes <= 20480 ? 4 : stage_bytes <= 24576 ? 3 : 2; }
 template <class TA, class TB, int BM, int BN, int WM, int WN, int NS = 0, int KPS = 1>
 using TileFor = std::conditional_t<sizeof(TB) == 1, GemmTile<TA, TB, BM, BN, WM, WN, 4>,
                                    GemmDma<TA, BM, BN, WM, WN, NS ? NS : ring_stages((BM + BN) * 128), DMA_STREAM, KPS>>;
@@ -435,8 +435,8 @@ static hipError_t launch_grouped_t(GroupedArgs a, int n_eff, int sh_eff, int max
 }
 
 // Routed tiles of GROUP_BM rows x 128 weight rows on 4 waves.  Weights of the activation type: the
-// shared expert in tiles of 2 x GROUP_BM rows (its ring one stage shorter, so the launch still
-// fits two blocks per CU); fp8 / MXFP4 weights (raw codes on the ring, widened in registers):
+// shared expert in tiles of 4 x GROUP_BM rows on a two-stage ring (32 KB stages: the launch's LDS
+// stays the routed ring's 80 KB, two blocks per CU; its few long blocks start first); fp8 / MXFP4 weights (raw codes on the ring, widened in registers):
 // GROUP_BM-row tiles for both.
 template <class TA, class TB>
 static hipError_t grouped_dispatch(const GroupedArgs& a, int max_items, hipStream_t s) {
@@ -446,8 +446,8 @@ static hipError_t grouped_dispatch(const GroupedArgs& a, int max_items, hipStrea
     return launch_grouped_t<TA, TB, GROUP_BM, GROUP_BM, 128, 1, 4, EPI_STORE_F32>(a, a.N, a.shN, max_items, s);
   } else {
     if (a.epi == EPI_SWIGLU)
-      return launch_grouped_t<TA, TB, GROUP_BM, 2 * GROUP_BM, 128, 1, 4, EPI_SWIGLU>(a, 2 * a.N, 2 * a.shN, max_items, s);
-    return launch_grouped_t<TA, TB, GROUP_BM, 2 * GROUP_BM, 128, 1, 4, EPI_STORE_F32>(a, a.N, a.shN, max_items, s);
+      return launch_grouped_t<TA, TB, GROUP_BM, 4 * GROUP_BM, 128, 1, 4, EPI_SWIGLU>(a, 2 * a.N, 2 * a.shN, max_items, s);
+    return launch_grouped_t<TA, TB, GROUP_BM, 4 * GROUP_BM, 128, 1, 4, EPI_STORE_F32>(a, a.N, a.shN, max_items, s);
   }
 }
 
