@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+PROF_EVERY = 4          # one timed step in PROF_EVERY carries the MoE gate/up timing events
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -220,11 +221,15 @@ def main():
     log(f"[bench] warmup {args.warmup} steps done")
     assert dg.dg_query_status(model.ctx, ws) == dg.DG_OK, "non-finite values during warmup"
 
-    dg.dg_profile_enable(model.ctx, 1 << dg.PROF_MOE_GATE_UP)
+    # The MoE gate/up launches are timed live with HIP events in every PROF_EVERY-th timed step: an
+    # event between two launches keeps the next kernel from starting under the previous one's
+    # tail (~4.5 us per event), so sampling the launches keeps the measurement from slowing the
+    # step it measures.
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record(stream)
     for s in range(args.steps):
+        dg.dg_profile_enable(model.ctx, (1 << dg.PROF_MOE_GATE_UP) if s % PROF_EVERY == 0 else 0)
         step(args.warmup + s)
     ev1.record(stream)
     torch.cuda.synchronize()

@@ -26,8 +26,10 @@ struct Prof {
   }
   hipEvent_t get() {
     if (!pool.empty()) { hipEvent_t e = pool.back(); pool.pop_back(); return e; }
+    // timing-only events: no system-scope fence on record (a fence writes back and invalidates
+    // the caches, a ~5 us stall of the next launch; elapsed times are read after the event syncs)
     hipEvent_t e = nullptr;
-    (void)hipEventCreate(&e);
+    (void)hipEventCreateWithFlags(&e, hipEventDisableSystemFence);
     return e;
   }
 };

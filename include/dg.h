@@ -272,7 +272,8 @@ typedef enum {
 } dg_prof_class;
 
 /* Starts recording a pair of events around every launch of the classes in `mask` (bit i =
- * class i; 0 stops).  Recording adds an event write before and after each such launch. */
+ * class i; 0 stops).  Recording adds a timestamp write before and after each such launch (timing
+ * events without a system-scope fence, so they do not stall the following launch). */
 dg_status dg_profile_enable(dg_ctx *ctx, uint32_t mask);
 /* Waits for the recorded launches of class `cls`, returns their summed duration (ms) and
  * count, and forgets them. */
