@@ -65,6 +65,8 @@ struct AttnArgs {
   const void* kc; const void* vc;   // cache keys [B][Hkv][cap][dh], values d-major [B][Hkv][dh][cap]
   int B, n, Hq, Hkv, dh, cap, vn_ld;  // vn_ld: n rounded up to a multiple of 8
   int causal, window, is_global;
+  const int32_t* seq_causal;        // device [B] or null: canvas b is causal iff seq_causal[b] != 0
+                                    // (a mixed batch); null: `causal` holds for every canvas
   float scale_log2;       // log2(e) / sqrt(dh)
   int splits, keys_per_split;       // key-range split (multiple of 64 keys; fp32 kernel)
   int tiles_per_split;              // split of the 64-key tile list (bf16 kernel)
@@ -86,9 +88,10 @@ hipError_t launch_embed(const int32_t* tokens, const void* embed, float* resid, 
 hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
 hipError_t launch_rmsnorm(const float* x, const void* g, void* y, int rows, int d, float eps,
                           int act_bf16, int* status, hipStream_t s);
+// seq_mask: device [B] or null; with it only canvases b with seq_mask[b] != 0 are appended
 hipError_t launch_kv_append(const void* kn, const void* vn, int vn_ld, void* kc, void* vc, int B, int n,
                             int Hkv, int dh, int cap, int window, int is_global,
-                            const int32_t* pos0, int act_bf16, hipStream_t s);
+                            const int32_t* pos0, const int32_t* seq_mask, int act_bf16, hipStream_t s);
 // resid += MoE output (gated expert rows + shared row); with g, out = RMSNorm(resid) * g
 hipError_t launch_moe_combine_norm(float* resid, const float* y, const float* shared, const float* gates,
                                    const int32_t* inv_perm, int rows, int d, int k, const void* g, void* out,

@@ -55,6 +55,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs p) {
   const int b = id / p.Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int P = p.pos0[b];
+  const bool causal = p.seq_causal ? p.seq_causal[b] != 0 : p.causal != 0;
   const int np = p.is_global ? P : min(P, p.window);       // visible prefix slots
   const int nkeys = np + p.n;
   const int k_begin = split * p.keys_per_split;
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs p) {
       for (int j = 0; j < 4; ++j) {
         const int kk = k0 + nb * 16 + 4 * kg + j;
         bool vis = kk < k_end;
-        if (p.causal && vis) {
+        if (causal && vis) {
           int kpos;
           if (kk >= np) kpos = P + (kk - np);
           else kpos = p.is_global ? kk : ring_lo + ((kk - ring_lo) % p.window + p.window) % p.window;

@@ -1,6 +1,7 @@
 // Canvas attention in bf16 for gfx950: every canvas query attends to the visible prefix cache
 // slots and to all canvas keys (bidirectional, [TR §아키텍처와 블록 자기회귀 생성]); with `causal`
-// set it serves the causal encoder (sliding window on local layers).
+// set it serves the causal encoder (sliding window on local layers), and with per-canvas flags a
+// batch that mixes the two kinds of pass ([TR §CPU-GPU 동기화 제거]).
 //
 // Block = FLASH_WAVES waves over 128 query rows of the G = Hq/Hkv heads that share KV head g;
 // each wave owns 16 rows (one MFMA column block), two waves per SIMD, so one wave's softmax
@@ -69,6 +70,8 @@ __global__ __launch_bounds__(NW * 64) void flash_kernel(AttnArgs p) {
   const int split = r % p.splits; r /= p.splits;
   const int g = r % p.Hkv;
   const int b = r / p.Hkv;
+  // a mixed batch runs both instantiations over the whole grid: each takes the canvases of its kind
+  if (p.seq_causal && (p.seq_causal[b] != 0) != CAUSAL) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kg = lane >> 4, l16 = lane & 15;
 
@@ -341,6 +344,23 @@ static hipError_t launch_flash_t(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_flash(const AttnArgs& a, hipStream_t s) {
+  // a mixed batch (per-canvas kinds, flags on the device): the bidirectional and the causal
+  // kernel each cover the grid and leave the other kind's blocks at once
+  if (a.seq_causal) {
+    hipError_t e = hipErrorInvalidValue;
+    switch (a.dh) {
+      case 64: e = launch_flash_t<64, false>(a, s); break;
+      case 128: e = launch_flash_t<128, false>(a, s); break;
+      case 256: e = launch_flash_t<256, false>(a, s); break;
+    }
+    if (e != hipSuccess) return e;
+    switch (a.dh) {
+      case 64: return launch_flash_t<64, true>(a, s);
+      case 128: return launch_flash_t<128, true>(a, s);
+      case 256: return launch_flash_t<256, true>(a, s);
+    }
+    return hipErrorInvalidValue;
+  }
   if (a.causal) {
     switch (a.dh) {
       case 64: return launch_flash_t<64, true>(a, s);

@@ -136,6 +136,7 @@ hipError_t launch_resid_add_rmsnorm(float* resid, const float* parts, int nparts
 // `window` of the new positions are kept)
 struct AppendArgs {
   const char* kn; const char* vn; char* kc; char* vc;
+  const int32_t* mask;    // device [B] or null: canvases with mask[b] == 0 are not appended
   int B, n, vn_ld, Hkv, esz, row_bytes, cap, window, is_global;
   int32_t pos0[MAX_BATCH];
 };
@@ -152,6 +153,7 @@ __global__ void kv_append_kernel(AppendArgs a) {
     const int g = (int)(t % a.Hkv);
     const int b = (int)(t / a.Hkv);
     if (!a.is_global && j < a.n - a.window) return;
+    if (a.mask && a.mask[b] == 0) return;
     const int pos = a.pos0[b] + j;
     const int slot = a.is_global ? pos : pos % a.window;
     const int64_t src = (((int64_t)b * a.Hkv + g) * a.n + j) * a.row_bytes + ch * 16;
@@ -167,6 +169,7 @@ __global__ void kv_append_kernel(AppendArgs a) {
   const int64_t row = v / a.n;                      // (b * Hkv + g) * dh + d
   const int b = (int)(row / ((int64_t)a.Hkv * dh));
   if (!a.is_global && j < a.n - a.window) return;
+  if (a.mask && a.mask[b] == 0) return;
   const int pos = a.pos0[b] + j;
   const int slot = a.is_global ? pos : pos % a.window;
   if (a.esz == 2)
@@ -176,10 +179,11 @@ __global__ void kv_append_kernel(AppendArgs a) {
 }
 
 hipError_t launch_kv_append(const void* kn, const void* vn, int vn_ld, void* kc, void* vc, int B, int n, int Hkv,
-                            int dh, int cap, int window, int is_global, const int32_t* pos0, int bf,
-                            hipStream_t s) {
+                            int dh, int cap, int window, int is_global, const int32_t* pos0,
+                            const int32_t* seq_mask, int bf, hipStream_t s) {
   AppendArgs a;
   a.kn = (const char*)kn; a.vn = (const char*)vn; a.kc = (char*)kc; a.vc = (char*)vc;
+  a.mask = seq_mask;
   a.B = B; a.n = n; a.vn_ld = vn_ld; a.Hkv = Hkv; a.esz = bf ? 2 : 4; a.row_bytes = dh * a.esz; a.cap = cap; a.window = window;
   a.is_global = is_global;
   for (int b = 0; b < B && b < MAX_BATCH; ++b) a.pos0[b] = pos0[b];

@@ -244,6 +244,7 @@ struct Pass {
   void* ws;
   Layout w;
   hipStream_t s;
+  const int32_t* seq_causal = nullptr;   // mixed batch: device [B] per-canvas kind (1 = append)
 };
 
 // Block tiles the dense GEMM launcher picks for M rows (mirrors k_gemm.hip's dense_pick).
@@ -336,6 +337,7 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn, bool xhat_ready, const vo
   aa.B = P.B; aa.n = P.n; aa.Hq = d.n_q_heads; aa.Hkv = d.n_kv_heads; aa.dh = d.head_dim; aa.cap = P.kv->cap[l];
   aa.vn_ld = up8(P.n);
   aa.causal = P.causal; aa.window = d.window > 0 ? d.window : 1; aa.is_global = glob;
+  aa.seq_causal = P.seq_causal;
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
   int maxkeys = 0, maxtiles = 0;
   for (int b = 0; b < P.B; ++b) {
@@ -360,9 +362,10 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn, bool xhat_ready, const vo
     HIPCHK(launch_attention(aa, bf, P.s));
     if (aa.splits > 1) HIPCHK(launch_attn_merge(aa, bf, P.s));
   }
-  if (P.causal) {
+  if (P.causal || P.seq_causal) {
     HIPCHK(launch_kv_append(at<void>(ws, w.kn), at<void>(ws, w.vn), aa.vn_ld, P.kv->k[l], P.kv->v[l], P.B, P.n,
-                            d.n_kv_heads, d.head_dim, P.kv->cap[l], d.window, glob, aa.pos0, bf, P.s));
+                            d.n_kv_heads, d.head_dim, P.kv->cap[l], d.window, glob, aa.pos0, P.seq_causal, bf,
+                            P.s));
   }
   // O projection as split-K partials; the fused kernel adds them to the residual (in part order)
   // and applies the FFN RMSNorm
@@ -736,6 +739,33 @@ dg_status dg_denoise_step(dg_ctx* ctx, const dg_kv* kv, const int32_t* canvas, c
   if (hidden_out && layer_begin == layer_end)
     HIPCHK(launch_rmsnorm(at<float>(ws, P.w.resid), ctx->final_norm, hidden_out, R, d.d_model, d.norm_eps, bf,
                           at<int>(ws, P.w.status), stream));
+  return DG_OK;
+}
+
+dg_status dg_mixed_forward(dg_ctx* ctx, const dg_kv* kv, const int32_t* tokens, const int32_t* append, int32_t L,
+                           void* hidden_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err.clear();
+  if (!ctx || !tokens || !append || !hidden_out) return fail(DG_EINVAL, "NULL argument");
+  if (!ctx->embed) return fail(DG_EINVAL, "embedding tokens needs the embedding");
+  int mp = 0;
+  // every canvas may be an append one: room for L more positions on the global layers
+  dg_status st = check_kv(ctx, kv, L, &mp);
+  if (st != DG_OK) return st;
+  if ((st = check_rows(kv->batch, L)) != DG_OK) return st;
+  if ((st = check_ws(ctx, ws, ws_bytes, kv->batch, L, mp)) != DG_OK) return st;
+  const dg_model_desc& d = ctx->d;
+  Pass P{ctx, kv, kv->batch, L, 0, ws, layout(d, kv->batch, L, mp), stream, append};
+  const int R = P.B * L;
+  HIPCHK(launch_embed(tokens, ctx->embed, at<float>(ws, P.w.resid), R, d.d_model, d.vocab, d.act_dtype == DG_BF16,
+                      stream));
+  HIPCHK(launch_rope_table(at<float2>(ws, P.w.rope), R, L, d.head_dim, std::log2((double)d.rope_theta),
+                           kv->prefix_len, P.B, stream));
+  for (int l = 0; l < d.n_layers; ++l) {
+    const bool last = l + 1 == d.n_layers;
+    if ((st = run_layer(P, l, true, l > 0, last ? ctx->final_norm : ctx->layers[l + 1].attn_norm,
+                        last ? hidden_out : at<void>(ws, P.w.xhat))) != DG_OK)
+      return st;
+  }
   return DG_OK;
 }
 

@@ -78,6 +78,8 @@ EXPORTS = {
                                 C.c_void_p]),
     "dg_denoise_step": (C.c_int, [C.c_void_p, C.POINTER(KV), C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
                                   C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "dg_mixed_forward": (C.c_int, [C.c_void_p, C.POINTER(KV), C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p,
+                                   C.c_void_p, C.c_size_t, C.c_void_p]),
     "dg_step_sample": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                  C.c_int32, C.c_int32, C.POINTER(StepParams), C.c_void_p, C.c_size_t, C.c_void_p]),
     "dg_canvas_run": (C.c_int, [C.c_void_p, C.POINTER(KV), C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
@@ -189,6 +191,11 @@ def dg_denoise_step(ctx, kv: KV, canvas, resid_in, L, layer_begin, layer_end, hi
     _check(load().dg_denoise_step(ctx, C.byref(kv), _ptr(canvas), _ptr(resid_in), L, layer_begin, layer_end,
                                   _ptr(hidden_out), _ptr(resid_out), _ptr(ws), ws.numel() * ws.element_size(),
                                   _stream(stream)))
+
+
+def dg_mixed_forward(ctx, kv: KV, tokens, append, L, hidden_out, ws, stream=None):
+    _check(load().dg_mixed_forward(ctx, C.byref(kv), _ptr(tokens), _ptr(append), L, _ptr(hidden_out), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def dg_step_sample(ctx, hidden, canvas, lock, n_locked, done, batch, L, params: StepParams, ws, stream=None):

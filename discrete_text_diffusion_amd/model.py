@@ -95,6 +95,18 @@ class Model:
         dg.dg_denoise_step(self.ctx, self.kv_struct, canvas, resid_in, L, layer_begin, le, hidden_out, resid_out,
                            ws, stream)
 
+    def mixed_forward(self, tokens, append, hidden_out, ws, stream=None):
+        """One pass over canvases of two kinds: append[b] != 0 (device int32 [B]) encodes canvas b
+        causally into the cache, the others take the bidirectional denoising pass.  The prefix
+        lengths here are not advanced (the flags stay on the device): call advance_rows for the
+        append canvases."""
+        dg.dg_mixed_forward(self.ctx, self.kv_struct, tokens, append, tokens.shape[1], hidden_out, ws, stream)
+
+    def advance_rows(self, rows, n):
+        """Add n to the prefix length of each canvas in rows."""
+        for b in rows:
+            self._plen[b] += n
+
     def step_sample(self, hidden, canvas, lock, n_locked, params: dg.StepParams, ws, done=None, stream=None):
         B, L = canvas.shape
         dg.dg_step_sample(self.ctx, hidden, canvas, lock, n_locked, done, B, L, params, ws, stream)

@@ -208,6 +208,21 @@ dg_status dg_denoise_step(dg_ctx *ctx, const dg_kv *kv, const int32_t *canvas,
                           int32_t layer_end, void *hidden_out, float *resid_out,
                           void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* One pass over a batch that mixes the two kinds of forward pass ([TR §CPU-GPU 동기화 제거]:
+ * denoising steps and cache updates share a batch, told apart by a per-sequence causal flag, with
+ * no host synchronisation).  tokens: device int32 [batch][L]; append: device int32 [batch], read
+ * only by the kernels.  Canvas b with append[b] != 0 takes the dg_prefill_kv pass: causal
+ * attention to the cache and to itself, its keys and values written at positions prefix_len[b]
+ * .. + L - 1 of every layer's cache (the caller then adds L to prefix_len[b]).  Canvas b with
+ * append[b] == 0 takes the dg_denoise_step pass: bidirectional attention over its prefix and
+ * canvas, its cache untouched.  Every row then runs the MoE FFN of every layer; hidden_out
+ * [batch*L][d] act = RMSNorm(residual) * final_norm for all rows (for an append canvas, the causal
+ * encoder's output).  Pass `append` as dg_step_sample's `done` to step only the denoising
+ * canvases.  The global-layer caches need room for L more positions on every canvas. */
+dg_status dg_mixed_forward(dg_ctx *ctx, const dg_kv *kv, const int32_t *tokens,
+                           const int32_t *append, int32_t L, void *hidden_out, void *ws,
+                           size_t ws_bytes, hipStream_t stream);
+
 /* Fused LM head + Step: logits = hidden [batch*L][d] . embed^T are streamed through an online
  * max / sum-exp / Philox-Gumbel argmax and never stored; then every position of canvas
  * (device int32 [batch][L], in/out) and lock (device uint8 [batch][L], in/out) is updated as

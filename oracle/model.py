@@ -266,6 +266,19 @@ def denoise_forward(cfg, W, kv, prefix_len, canvas=None, resid_in=None, n_layers
     return H, h
 
 
+def write_cache(cfg, layer, Kb, Vb, pos, kn, vn):
+    """Store new keys / values kn, vn [Hkv][n][dh] at positions pos in one canvas's caches
+    Kb, Vb [Hkv][cap][dh]: slot p on global layers; on local layers a ring of `window` slots
+    (slot p mod window) that keeps only the last `window` positions."""
+    if is_global(cfg, layer):
+        Kb[:, pos] = kn
+        Vb[:, pos] = vn
+    else:
+        keep = pos >= pos[-1] + 1 - cfg.window
+        Kb[:, pos[keep] % cfg.window] = kn[:, keep]
+        Vb[:, pos[keep] % cfg.window] = vn[:, keep]
+
+
 def prefill(cfg, W, kv, prefix_len, tokens):
     """Causal encoder pass over tokens [B][n] at positions prefix_len[b].. that appends their
     post-RoPE keys and values to the caches [TR §아키텍처와 블록 자기회귀 생성: context encoding
@@ -292,16 +305,53 @@ def prefill(cfg, W, kv, prefix_len, tokens):
             o[rows] = ob.reshape(n, Hq * dh)
             news.append((pos, kn, vn))
         for b, (pos, kn, vn) in enumerate(news):
-            if is_global(cfg, l):
-                K[b][:, pos] = kn
-                V[b][:, pos] = vn
-            else:                              # a ring keeps only the last `window` positions
-                keep = pos >= pos[-1] + 1 - cfg.window
-                K[b][:, pos[keep] % cfg.window] = kn[:, keep]
-                V[b][:, pos[keep] % cfg.window] = vn[:, keep]
+            write_cache(cfg, l, K[b], V[b], pos, kn, vn)
         o = rnd(o)
         h = h + o @ lw["w_o"].T
         a2 = rnd(rmsnorm(h, lw["ffn_norm"], cfg.norm_eps))
         f, _ = moe(cfg, a2, lw, rnd)
         h = h + f
     return kv, [p + n for p in prefix_len]
+
+
+def mixed_forward(cfg, W, kv, prefix_len, tokens, append):
+    """One pass over a batch whose canvases take different passes [TR §CPU-GPU 동기화 제거: denoising
+    steps and KV-cache updates share a batch, told apart by a per-sequence causal flag].
+
+    tokens [B][n]; append[b] true: canvas b takes the causal encoder pass of `prefill` (causal
+    attention to its cache and itself; its keys and values written to its caches); false: the
+    bidirectional decoder pass of `denoise_forward` (its cache untouched).  Every row runs every
+    layer's FFN.  Canvases share nothing but the weights, so each canvas's result is that of its
+    own pass run alone.  Returns (H [B*n][d] = stored(RMSNorm(resid) * g_final), new caches)."""
+    rnd = rounder(cfg.act_dtype)
+    tokens = np.asarray(tokens)
+    B, n = tokens.shape
+    Hq, dh = cfg.n_q_heads, cfg.head_dim
+    kv = [(K.copy(), V.copy()) for K, V in kv]
+    h = W["embed"][tokens.reshape(-1)].astype(np.float64)
+    for l in range(cfg.n_layers):
+        lw = W["layers"][l]
+        K, V = kv[l]
+        x = rnd(rmsnorm(h, lw["attn_norm"], cfg.norm_eps))
+        o = np.zeros((B * n, Hq * dh))
+        news = []
+        for b in range(B):
+            rows = slice(b * n, (b + 1) * n)
+            pos = prefix_len[b] + np.arange(n)
+            q, k, v = qkv(cfg, x[rows], lw, pos, rnd)
+            kn, vn = k.transpose(1, 0, 2), v.transpose(1, 0, 2)
+            if append[b]:
+                ob = causal_attention(cfg, l, q, kn, vn, K[b], V[b], prefix_len[b])
+                news.append((b, pos, kn, vn))
+            else:
+                ob = canvas_attention(cfg, l, q, kn, vn, K[b], V[b], prefix_len[b])
+            o[rows] = ob.reshape(n, Hq * dh)
+        for b, pos, kn, vn in news:
+            write_cache(cfg, l, K[b], V[b], pos, kn, vn)
+        o = rnd(o)
+        h = h + o @ lw["w_o"].T
+        a2 = rnd(rmsnorm(h, lw["ffn_norm"], cfg.norm_eps))
+        f, _ = moe(cfg, a2, lw, rnd)
+        h = h + f
+    H = rnd(rmsnorm(h, W["final_norm"], cfg.norm_eps))
+    return H, kv

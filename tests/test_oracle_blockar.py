@@ -69,3 +69,63 @@ def test_package_metrics_match_the_oracle():
             for key in ("canvases", "tokens", "steps", "effective_steps", "tpf"):
                 assert g[key] == pytest.approx(w[key])
             assert g["tps"] == pytest.approx(w["tpf"] / 0.0125)
+
+
+def _mixed_case():
+    """Tiny fp32 model with a sliding-window layer (ring of 16 slots) and a global layer; random
+    caches; three canvases at different prefix lengths (the first wraps its ring)."""
+    cfg = configs.C0.replace(batch=3, window=16, global_every=2, prefix=80, kv_source="random")
+    W = gen.make_weights(cfg, "cpu")
+    OW = oracle_weights(W, cfg)
+    kv = oracle_kv(gen.make_random_kv(cfg, "cpu"))
+    rng = np.random.default_rng(21)
+    toks = rng.integers(0, cfg.vocab, (cfg.batch, 16))
+    return cfg, OW, kv, [40, 25, 48], toks
+
+
+def _one(kv, b):
+    return [(K[b:b + 1], V[b:b + 1]) for K, V in kv]
+
+
+def test_mixed_pass_single_kind_batches_are_the_plain_passes():
+    """[TR §CPU-GPU 동기화 제거] all-denoise: the decoder pass's hidden states and untouched caches;
+    all-append: the causal encoder pass's caches."""
+    cfg, OW, kv, plen, toks = _mixed_case()
+    H, kv2 = M.mixed_forward(cfg, OW, kv, plen, toks, [0, 0, 0])
+    H0, _ = M.denoise_forward(cfg, OW, kv, plen, canvas=toks)
+    assert np.allclose(H, H0, rtol=0, atol=1e-12)
+    for (K, V), (K2, V2) in zip(kv, kv2):
+        assert np.array_equal(K, K2) and np.array_equal(V, V2)
+    _, kv3 = M.mixed_forward(cfg, OW, kv, plen, toks, [1, 1, 1])
+    kv4, plen4 = M.prefill(cfg, OW, kv, plen, toks)
+    assert plen4 == [p + 16 for p in plen]
+    for (K, V), (K4, V4) in zip(kv3, kv4):
+        assert np.allclose(K, K4, rtol=0, atol=1e-12) and np.allclose(V, V4, rtol=0, atol=1e-12)
+
+
+def test_mixed_pass_equals_each_canvas_alone():
+    """A batch of [append, denoise, append]: each canvas's hidden states and caches equal those of
+    its own kind of pass run on that canvas alone; the denoising canvas's caches are untouched and
+    the appended ones differ from the input exactly at the new positions' slots."""
+    cfg, OW, kv, plen, toks = _mixed_case()
+    flags = [1, 0, 1]
+    H, kv2 = M.mixed_forward(cfg, OW, kv, plen, toks, flags)
+    n = toks.shape[1]
+    for b, f in enumerate(flags):
+        kvb = _one(kv, b)
+        rows = slice(b * n, (b + 1) * n)
+        if f:
+            want, _ = M.prefill(cfg, OW, kvb, [plen[b]], toks[b:b + 1])
+            for l, ((K2, V2), (Kw, Vw), (K0, _)) in enumerate(zip(kv2, want, kv)):
+                assert np.allclose(K2[b:b + 1], Kw, rtol=0, atol=1e-12)
+                assert np.allclose(V2[b:b + 1], Vw, rtol=0, atol=1e-12)
+                changed = np.nonzero(np.any(K2[b] != K0[b], axis=(0, 2)))[0]
+                pos = plen[b] + np.arange(n)
+                slots = pos if cfg.is_global(l) else np.unique(pos[pos >= pos[-1] + 1 - cfg.window] % cfg.window)
+                assert np.array_equal(changed, np.sort(slots))
+            Hb, _ = M.mixed_forward(cfg, OW, kvb, [plen[b]], toks[b:b + 1], [1])
+        else:
+            for (K2, V2), (K0, V0) in zip(kv2, kv):
+                assert np.array_equal(K2[b], K0[b]) and np.array_equal(V2[b], V0[b])
+            Hb, _ = M.denoise_forward(cfg, OW, kvb, [plen[b]], canvas=toks[b:b + 1])
+        assert np.allclose(H[rows], Hb, rtol=0, atol=1e-12)
