@@ -6,7 +6,10 @@
 namespace dg {
 
 constexpr int MAX_BATCH = 64;     // canvases per call (prefix lengths travel as kernel arguments)
-constexpr int GROUP_BM = 32;      // rows per expert tile of the grouped GEMMs
+constexpr int GROUP_BM = 32;       // rows per expert tile of the grouped GEMMs
+constexpr int GROUP_BM_WIDE = 128; // ... once experts average 64 rows or more (batched canvases)
+// rows per routed expert tile for `picks` = rows x top_k routed rows over E experts
+inline int group_bm(int64_t picks, int E) { return picks >= (int64_t)64 * E ? GROUP_BM_WIDE : GROUP_BM; }
 
 enum WKind { W_F32 = 0, W_BF16 = 1, W_FP8 = 2, W_MXFP4 = 3 };
 enum Epi { EPI_STORE_F32 = 0, EPI_ADD_F32 = 1, EPI_STORE_ACT = 2, EPI_SWIGLU = 3, EPI_QKV = 4 };
@@ -52,6 +55,7 @@ struct GroupedArgs {
   const void* sh_sB; const void* sh_sB2; int64_t sh_s_ld;
   int shN, shK, sh_rows;
   void* shC; int64_t sh_ldc;
+  int bm;                                             // rows per routed tile: GROUP_BM or GROUP_BM_WIDE
   int nt_r, nt_s, sh_blocks, n_sh_items;              // filled by the launcher
 };
 

@@ -24,8 +24,8 @@ using TileFor = std::conditional_t<sizeof(TB) == 1, GemmTile<TA, TB, BM, BN, WM,
 // registers (12 KB stages x 6, two blocks per CU); MXFP4 weights go through the register-staged
 // engine, which measured faster for them (its stages carry 64 elements of all 128 rows widened
 // once per block, where the ring's per-stage scale loads and short stages cost more)
-template <class TA, class TB, int BM, int BN, int WM, int WN, int NS = 0>
-using GroupTileFor = std::conditional_t<is_fp8_v<TB>, GemmDmaQ<TB, BM, BN, WM, WN, 6>,
+template <class TA, class TB, int BM, int BN, int WM, int WN, int NS = 0, int QNS = 6>
+using GroupTileFor = std::conditional_t<is_fp8_v<TB>, GemmDmaQ<TB, BM, BN, WM, WN, QNS>,
                                         TileFor<TA, TB, BM, BN, WM, WN, NS>>;
 
 // ---------------------------------------------------------------- B-row maps ----------------
@@ -315,10 +315,10 @@ DG_DEV void grouped_tile(char* lds, const TA* A, int64_t lda, const int32_t* a_t
 // tile; work item w < *n_items: expert e = work[2w], first row m0 = work[2w+1] of that expert's
 // rows [offsets[e], offsets[e] + counts[e]) in grouped order.  The dynamic LDS holds the larger
 // of the two tile shapes' rings.
-template <class TA, class TB, int BM, int BMS, int BN, int WM, int WN, int EPI, int NS = 0>
+template <class TA, class TB, int BM, int BMS, int BN, int WM, int WN, int EPI, int NS = 0, int QNS = 6>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_grouped_kernel(GroupedArgs p) {
-  using G = GroupTileFor<TA, TB, BM, BN, WM, WN, NS>;
-  using GS = GroupTileFor<TA, TB, BMS, BN, WM, WN, NS>;
+  using G = GroupTileFor<TA, TB, BM, BN, WM, WN, NS, QNS>;
+  using GS = GroupTileFor<TA, TB, BMS, BN, WM, WN, NS, QNS>;
   extern __shared__ __align__(16) char lds[];
   const int id = blockIdx.x;
   if (id >= p.sh_blocks) {
@@ -415,10 +415,10 @@ hipError_t launch_dense(const DenseArgs& a, int act_bf16, int w_kind, hipStream_
   return dense_dispatch<bf16_t, bf16_t>(a, s);
 }
 
-template <class TA, class TB, int BM, int BMS, int BN, int WM, int WN, int EPI, int NS = 0>
+template <class TA, class TB, int BM, int BMS, int BN, int WM, int WN, int EPI, int NS = 0, int QNS = 6>
 static hipError_t launch_grouped_t(GroupedArgs a, int n_eff, int sh_eff, int max_items, hipStream_t s) {
-  using G = GroupTileFor<TA, TB, BM, BN, WM, WN, NS>;
-  using GS = GroupTileFor<TA, TB, BMS, BN, WM, WN, NS>;
+  using G = GroupTileFor<TA, TB, BM, BN, WM, WN, NS, QNS>;
+  using GS = GroupTileFor<TA, TB, BMS, BN, WM, WN, NS, QNS>;
   constexpr size_t LDS = G::LDS_BYTES > GS::LDS_BYTES ? G::LDS_BYTES : GS::LDS_BYTES;
   a.nt_r = (n_eff + BN - 1) / BN;
   a.nt_s = (sh_eff + BN - 1) / BN;
@@ -427,9 +427,9 @@ static hipError_t launch_grouped_t(GroupedArgs a, int n_eff, int sh_eff, int max
   const int blocks = a.sh_blocks + max_items * a.nt_r;
   if (blocks == 0) return hipSuccess;
   if (a.K % G::KT || (a.shB && a.shK % GS::KT)) return hipErrorInvalidValue;
-  static const hipError_t attr = allow_lds(gemm_grouped_kernel<TA, TB, BM, BMS, BN, WM, WN, EPI, NS>, LDS);
+  static const hipError_t attr = allow_lds(gemm_grouped_kernel<TA, TB, BM, BMS, BN, WM, WN, EPI, NS, QNS>, LDS);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((gemm_grouped_kernel<TA, TB, BM, BMS, BN, WM, WN, EPI, NS>), dim3(blocks), dim3(WM * WN * 64),
+  hipLaunchKernelGGL((gemm_grouped_kernel<TA, TB, BM, BMS, BN, WM, WN, EPI, NS, QNS>), dim3(blocks), dim3(WM * WN * 64),
                      LDS, s, a);
   return hipGetLastError();
 }
@@ -438,8 +438,24 @@ static hipError_t launch_grouped_t(GroupedArgs a, int n_eff, int sh_eff, int max
 // shared expert in tiles of 4 x GROUP_BM rows on a two-stage ring (32 KB stages: the launch's LDS
 // stays the routed ring's 80 KB, two blocks per CU; its few long blocks start first); fp8 / MXFP4 weights (raw codes on the ring, widened in registers):
 // GROUP_BM-row tiles for both.
+// Batched canvases (experts averaging 64 rows or more): 128-row tiles for the routed experts and
+// the shared expert, so a popular expert's weights stream once per 128 rows rather than per 32.
+// bf16 and fp8 on 8 waves (3- and 4-stage rings, one block per CU), MXFP4 on the 4-wave
+// register-staged engine.
+template <class TA, class TB, int EPI>
+static hipError_t grouped_wide(const GroupedArgs& a, int n_eff, int sh_eff, int max_items, hipStream_t s) {
+  constexpr int W = GROUP_BM_WIDE;
+  if constexpr (is_fp4_v<TB>) return launch_grouped_t<TA, TB, W, W, 128, 2, 2, EPI>(a, n_eff, sh_eff, max_items, s);
+  else return launch_grouped_t<TA, TB, W, W, 128, 2, 4, EPI, 3, 4>(a, n_eff, sh_eff, max_items, s);
+}
+
 template <class TA, class TB>
 static hipError_t grouped_dispatch(const GroupedArgs& a, int max_items, hipStream_t s) {
+  if (a.bm == GROUP_BM_WIDE) {
+    if (a.epi == EPI_SWIGLU) return grouped_wide<TA, TB, EPI_SWIGLU>(a, 2 * a.N, 2 * a.shN, max_items, s);
+    return grouped_wide<TA, TB, EPI_STORE_F32>(a, a.N, a.shN, max_items, s);
+  }
+  if (a.bm != GROUP_BM) return hipErrorInvalidValue;
   if constexpr (sizeof(TB) == 1) {
     if (a.epi == EPI_SWIGLU)
       return launch_grouped_t<TA, TB, GROUP_BM, GROUP_BM, 128, 1, 4, EPI_SWIGLU>(a, 2 * a.N, 2 * a.shN, max_items, s);

@@ -399,10 +399,13 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn, bool xhat_ready, const vo
   HIPCHK(launch_dense(ra, bf, bf ? W_BF16 : W_F32, P.s));
   HIPCHK(launch_router_topk(at<float>(ws, w.rparts), ra.ksplit, ra.c_split, L.router_bias, R, d.n_experts, d.top_k,
                             at<float>(ws, w.rlogits), at<int32_t>(ws, w.idx), at<float>(ws, w.gates), P.s));
+  const int gbm = group_bm((int64_t)R * d.top_k, d.n_experts);
+  // tiles the grouped launches may see: the workspace's bound is for GROUP_BM-row tiles
+  const int max_items = gbm == GROUP_BM ? w.max_items : (R * d.top_k + gbm - 1) / gbm + d.n_experts;
   HIPCHK(launch_route_tables(at<int32_t>(ws, w.idx), R, d.n_experts, d.top_k, at<int32_t>(ws, w.counts),
                              at<int32_t>(ws, w.offsets), at<int32_t>(ws, w.perm), at<int32_t>(ws, w.inv_perm),
                              at<int32_t>(ws, w.tok), at<int32_t>(ws, w.work), at<int32_t>(ws, w.n_items),
-                             GROUP_BM, P.s));
+                             gbm, P.s));
   route_scope.close();
   const int wk = w_kind(d);
   // routed experts and the shared expert in one launch each: gate/up + SwiGLU, then down
@@ -418,7 +421,7 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn, bool xhat_ready, const vo
   ga.sB = L.s_gate; ga.sB2 = L.s_up; ga.s_ld = mx ? d.d_model / 32 : 2;
   ga.s_estride = (int64_t)d.expert_hidden * ga.s_ld;
   ga.N = d.expert_hidden; ga.K = d.d_model;
-  ga.work = at<int32_t>(ws, w.work); ga.n_items = at<int32_t>(ws, w.n_items);
+  ga.work = at<int32_t>(ws, w.work); ga.n_items = at<int32_t>(ws, w.n_items); ga.bm = gbm;
   ga.offsets = at<int32_t>(ws, w.offsets); ga.counts = at<int32_t>(ws, w.counts);
   ga.C = at<void>(ws, w.a_grp); ga.ldc = d.expert_hidden;
   ga.shA = at<void>(ws, w.xhat); ga.sh_lda = d.d_model;
@@ -428,7 +431,7 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn, bool xhat_ready, const vo
   ga.shC = at<void>(ws, w.sh_a); ga.sh_ldc = d.shared_hidden;
   {
     ProfScope ps(P.c, DG_PROF_MOE_GATE_UP, P.s);
-    HIPCHK(launch_grouped(ga, bf, wk, w.max_items, P.s));
+    HIPCHK(launch_grouped(ga, bf, wk, max_items, P.s));
   }
   GroupedArgs da{};
   da.epi = EPI_STORE_F32;
@@ -438,7 +441,7 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn, bool xhat_ready, const vo
   da.sB = L.s_down; da.sB2 = nullptr; da.s_ld = mx ? d.expert_hidden / 32 : 2;
   da.s_estride = (int64_t)d.d_model * da.s_ld;
   da.N = d.d_model; da.K = d.expert_hidden;
-  da.work = ga.work; da.n_items = ga.n_items; da.offsets = ga.offsets; da.counts = ga.counts;
+  da.work = ga.work; da.n_items = ga.n_items; da.offsets = ga.offsets; da.counts = ga.counts; da.bm = gbm;
   da.C = at<void>(ws, w.y); da.ldc = d.d_model;
   da.shA = at<void>(ws, w.sh_a); da.sh_lda = d.shared_hidden;
   da.shB = L.sh_down; da.shB2 = nullptr; da.sh_ldb = d.shared_hidden / pk;
@@ -447,7 +450,7 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn, bool xhat_ready, const vo
   da.shC = at<void>(ws, w.sh_parts); da.sh_ldc = d.d_model;
   {
     ProfScope ps(P.c, DG_PROF_MOE_DOWN, P.s);
-    HIPCHK(launch_grouped(da, bf, wk, w.max_items, P.s));
+    HIPCHK(launch_grouped(da, bf, wk, max_items, P.s));
   }
   HIPCHK(launch_moe_combine_norm(at<float>(ws, w.resid), at<float>(ws, w.y), at<float>(ws, w.sh_parts),
                                  at<float>(ws, w.gates), at<int32_t>(ws, w.inv_perm), R, d.d_model, d.top_k, next_g,

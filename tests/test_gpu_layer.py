@@ -152,6 +152,15 @@ def test_fp8_batch8_layers_parity_full_shape():
     _layer_parity(cfg, 5, 2e-2)
 
 
+@pytest.mark.parametrize("experts", ["bf16", "mxfp4"])
+def test_batch8_wide_expert_tiles_layer_parity(experts):
+    """Eight canvases (2048 rows, Zipf-routed experts averaging 128 rows): the grouped GEMMs take
+    128-row expert tiles; bf16 and MXFP4 expert weights (fp8 runs in the full-shape test above)."""
+    cfg = configs.C4.replace(expert_dtype=experts, n_layers=1, prefix=1024, resid_input=True, window=0,
+                             global_every=0)
+    _layer_parity(cfg, 0, 2e-2)
+
+
 def test_long_prefix_global_layer_sampled_rows():
     """A global layer over a 131072-token prefix (131328 keys per query).  The GPU runs the whole
     layer; the oracle recomputes q/k/v for every canvas row (the canvas keys need all of them) and
