@@ -136,8 +136,8 @@ hipError_t launch_router_topk(const float* parts, int nparts, int64_t part_strid
 // The experts of one row are distinct, so for expert e the flag "row t chose e" is 0/1 and the
 // grouped position of (t, s) is offsets[e] + (number of earlier rows that chose e).
 
-template <int K>
-DG_DEV int chosen_slot(const int32_t* idx, int t, int k, int e) {
+template <int K, class P>
+DG_DEV int chosen_slot(P idx, int t, int k, int e) {
   int v[K];
 #pragma unroll
   for (int s = 0; s < K; ++s) v[s] = idx[(int64_t)t * k + min(s, k - 1)];
@@ -160,8 +160,11 @@ DG_DEV int block_sum_int(int v, int* red) {
   return red[0] + red[1] + red[2] + red[3];
 }
 
-template <int K>
-__global__ __launch_bounds__(256) void route_place_kernel(const int32_t* idx, int T, int E, int k, int32_t* counts,
+// STAGED: the T*k picks are first copied to LDS (every block reads all of them twice).
+constexpr int ROUTE_STAGE_MAX = 16384;   // picks staged in LDS (64 KB)
+
+template <int K, bool STAGED>
+__global__ __launch_bounds__(256) void route_place_kernel(const int32_t* idx_g, int T, int E, int k, int32_t* counts,
                                                           int bm, int32_t* offsets, int32_t* work,
                                                           int32_t* n_items, int32_t* perm, int32_t* inv_perm,
                                                           int32_t* tok) {
@@ -169,8 +172,12 @@ __global__ __launch_bounds__(256) void route_place_kernel(const int32_t* idx, in
   __shared__ int red[4];
   __shared__ int wsum[4];
   __shared__ int hist[256];
+  extern __shared__ int32_t idx_s[];
   for (int q = threadIdx.x; q < 256; q += 256) hist[q] = 0;
+  if constexpr (STAGED)
+    for (int i = threadIdx.x; i < T * k; i += 256) idx_s[i] = idx_g[i];
   __syncthreads();
+  const int32_t* idx = STAGED ? idx_s : idx_g;
   for (int i = threadIdx.x; i < T * k; i += 256) atomicAdd(&hist[min(max(idx[i], 0), E - 1)], 1);
   __syncthreads();
   int ro = 0, rt = 0;
@@ -215,16 +222,28 @@ __global__ __launch_bounds__(256) void route_place_kernel(const int32_t* idx, in
   }
 }
 
+template <int K>
+static hipError_t launch_place(const int32_t* idx, int T, int E, int k, int32_t* counts, int32_t* offsets,
+                               int32_t* perm, int32_t* inv_perm, int32_t* tok, int32_t* work, int32_t* n_items,
+                               int bm, hipStream_t s) {
+  if ((int64_t)T * k <= ROUTE_STAGE_MAX) {
+    static const hipError_t attr = allow_lds(route_place_kernel<K, true>, ROUTE_STAGE_MAX * 4);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((route_place_kernel<K, true>), dim3(E), dim3(256), (size_t)T * k * 4, s, idx, T, E, k, counts,
+                       bm, offsets, work, n_items, perm, inv_perm, tok);
+  } else {
+    hipLaunchKernelGGL((route_place_kernel<K, false>), dim3(E), dim3(256), 0, s, idx, T, E, k, counts, bm, offsets,
+                       work, n_items, perm, inv_perm, tok);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_route_tables(const int32_t* idx, int T, int E, int k, int32_t* counts, int32_t* offsets,
                                int32_t* perm, int32_t* inv_perm, int32_t* tok, int32_t* work, int32_t* n_items,
                                int bm, hipStream_t s) {
-  if (k <= 2)
-    hipLaunchKernelGGL(route_place_kernel<2>, dim3(E), dim3(256), 0, s, idx, T, E, k, counts, bm, offsets, work, n_items, perm, inv_perm, tok);
-  else if (k <= 8)
-    hipLaunchKernelGGL(route_place_kernel<8>, dim3(E), dim3(256), 0, s, idx, T, E, k, counts, bm, offsets, work, n_items, perm, inv_perm, tok);
-  else
-    hipLaunchKernelGGL(route_place_kernel<16>, dim3(E), dim3(256), 0, s, idx, T, E, k, counts, bm, offsets, work, n_items, perm, inv_perm, tok);
-  return hipGetLastError();
+  if (k <= 2) return launch_place<2>(idx, T, E, k, counts, offsets, perm, inv_perm, tok, work, n_items, bm, s);
+  if (k <= 8) return launch_place<8>(idx, T, E, k, counts, offsets, perm, inv_perm, tok, work, n_items, bm, s);
+  return launch_place<16>(idx, T, E, k, counts, offsets, perm, inv_perm, tok, work, n_items, bm, s);
 }
 
 }  // namespace dg

@@ -250,7 +250,7 @@ struct Pass {
 // Block tiles the dense GEMM launcher picks for M rows (mirrors k_gemm.hip's dense_pick).
 int dense_blocks(int M, int N) {
   int bm = M > 256 ? 128 : (M > 64 ? 128 : 64), bn = M > 256 ? 128 : 64;
-  if (M > 64 && M <= 256 && N <= 256) bm = 64, bn = 32;
+  if (M > 64 && N <= 256) bm = 64, bn = 32;
   return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
 }
 
