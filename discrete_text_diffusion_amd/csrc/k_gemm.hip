@@ -442,13 +442,14 @@ static hipError_t launch_grouped_t(GroupedArgs a, int n_eff, int sh_eff, int max
 // GROUP_BM-row tiles for both.
 // Batched canvases (experts averaging 64 rows or more): 128-row tiles for the routed experts and
 // the shared expert, so a popular expert's weights stream once per 128 rows rather than per 32.
-// bf16 and fp8 on 8 waves (3- and 4-stage rings, one block per CU), MXFP4 on the 4-wave
-// register-staged engine.
+// bf16 and fp8 on 8 waves with 256-column tiles (the activation rows, which outweigh fp8 weights
+// per stage, are re-read by half as many column tiles; 3- and 4-stage rings, one block per CU),
+// MXFP4 on the 4-wave register-staged engine (128 columns).
 template <class TA, class TB, int EPI>
 static hipError_t grouped_wide(const GroupedArgs& a, int n_eff, int sh_eff, int max_items, hipStream_t s) {
   constexpr int W = GROUP_BM_WIDE;
   if constexpr (is_fp4_v<TB>) return launch_grouped_t<TA, TB, W, W, 128, 2, 2, EPI>(a, n_eff, sh_eff, max_items, s);
-  else return launch_grouped_t<TA, TB, W, W, 128, 2, 4, EPI, 3, 4>(a, n_eff, sh_eff, max_items, s);
+  else return launch_grouped_t<TA, TB, W, W, 256, 2, 4, EPI, 3, 4>(a, n_eff, sh_eff, max_items, s);
 }
 
 template <class TA, class TB>
