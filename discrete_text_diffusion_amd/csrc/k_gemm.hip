@@ -364,7 +364,8 @@ static hipError_t launch_dense_t(DenseArgs a, int n_eff, hipStream_t s) {
 // Tiles.  Up to 256 rows: 128-row tiles (64 for tiny M) so each weight tile is read by at most
 // two blocks, 64 (32 for SwiGLU) columns so enough blocks stream the weights; paired epilogues
 // keep an even count of 16-column blocks per wave.  Above 256 rows: 128 x 128 tiles, except narrow
-// outputs.  QKV up to
+// outputs; with bf16 weights 256 x 128 tiles of 8 waves (3-stage ring): half the weight re-reads
+// per output.  QKV up to
 // 256 rows: 8 waves on the 128 x 64 tile with a 4-stage ring (one block per CU; 8 waves keep more
 // loads and MFMAs in flight than 4).  Narrow outputs (the router, N <= 256) above 64 rows: 64 x 32
 // tiles at any row count (few split-K parts where rows alone give enough blocks).
@@ -373,7 +374,10 @@ static hipError_t dense_pick(const DenseArgs& a, int n_eff, hipStream_t s) {
   const bool small = a.M <= 64;
   if constexpr (MAP == MAP_ROPE) {
     // a column tile must stay inside one head
-    if (a.M > 256 && a.dh >= 128) return launch_dense_t<TA, TB, 128, 128, 2, 2, EPI, MAP>(a, n_eff, s);
+    if (a.M > 256 && a.dh >= 128) {
+      if constexpr (sizeof(TB) == 1) return launch_dense_t<TA, TB, 128, 128, 2, 2, EPI, MAP>(a, n_eff, s);
+      else return launch_dense_t<TA, TB, 256, 128, 4, 2, EPI, MAP, 3>(a, n_eff, s);
+    }
     if (small) return launch_dense_t<TA, TB, 64, 64, 2, 2, EPI, MAP>(a, n_eff, s);
     if constexpr (sizeof(TB) == 1) return launch_dense_t<TA, TB, 128, 64, 2, 2, EPI, MAP>(a, n_eff, s);
     else return launch_dense_t<TA, TB, 128, 64, 4, 2, EPI, MAP, 4>(a, n_eff, s);
@@ -384,7 +388,10 @@ static hipError_t dense_pick(const DenseArgs& a, int n_eff, hipStream_t s) {
   } else {
     if (small) return launch_dense_t<TA, TB, 64, 64, 2, 2, EPI, MAP>(a, n_eff, s);
     if (a.N <= 256) return launch_dense_t<TA, TB, 64, 32, 4, 1, EPI, MAP>(a, n_eff, s);
-    if (a.M > 256) return launch_dense_t<TA, TB, 128, 128, 2, 2, EPI, MAP>(a, n_eff, s);
+    if (a.M > 256) {
+      if constexpr (sizeof(TB) == 1) return launch_dense_t<TA, TB, 128, 128, 2, 2, EPI, MAP>(a, n_eff, s);
+      else return launch_dense_t<TA, TB, 256, 128, 4, 2, EPI, MAP, 3>(a, n_eff, s);
+    }
     if constexpr (sizeof(TB) != 1) {
       // wide outputs up to 256 rows (the attention output projection): 8 waves, two K tiles per
       // ring stage, about one block per CU

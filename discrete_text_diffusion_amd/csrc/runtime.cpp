@@ -247,20 +247,22 @@ struct Pass {
   const int32_t* seq_causal = nullptr;   // mixed batch: device [B] per-canvas kind (1 = append)
 };
 
-// Block tiles the dense GEMM launcher picks for M rows (mirrors k_gemm.hip's dense_pick).
+// Block tiles the dense GEMM launcher picks for M rows with bf16 / fp32 weights (mirrors k_gemm.hip's
+// dense_pick).
 int dense_blocks(int M, int N) {
-  int bm = M > 256 ? 128 : (M > 64 ? 128 : 64), bn = M > 256 ? 128 : 64;
+  int bm = M > 256 ? 256 : (M > 64 ? 128 : 64), bn = M > 256 ? 128 : 64;
   if (M > 64 && N <= 256) bm = 64, bn = 32;
   return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
 }
 
 // split-K parts for the attention output projection: the largest divisor of the K-tile count (at
 // most MAX_KSPLIT, at least two K tiles per part) that keeps the block count at or below 512, or
-// at or below 256 (one 8-wave block per CU) for the 128 x 64 tiles of 65..256 rows
+// at or below 256 (one 8-wave block per CU) for the 8-wave tiles above 64 rows (128 x 64 up to 256
+// rows, 256 x 128 above)
 int ksplit_for(const dg_model_desc& d, int M, int N, int K) {
   const int nk = K / (d.act_dtype == DG_BF16 ? 64 : 32);
   const int blocks = dense_blocks(M, N);
-  const int cap = (M > 64 && M <= 256 && N > 256) ? 256 : 512;
+  const int cap = (M > 64 && N > 256) ? 256 : 512;
   int best = 1;
   for (int s = 1; s <= MAX_KSPLIT; ++s)
     if (nk % s == 0 && nk / s >= 2 && blocks * s <= cap) best = s;
