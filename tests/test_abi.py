@@ -140,5 +140,26 @@ def test_validation_enqueues_nothing_on_bad_calls():
             dg.dg_prefill_kv(ctx, kv, tok, 100, _FakeTensor(ws.addr, 1 << 40), 0)
         assert e.value.status == dg.DG_EINVAL and "cap" in dg.dg_last_error()
         del tok
+        # mixed pass: flags and output required, room for L more positions on every canvas, the
+        # canvas-length rule of the decoder pass
+        flags = _FakeTensor(0x9000, 4)
+        hid = _FakeTensor(0xa000, 4 * 32 * cfg.d_model)
+        with pytest.raises(dg.DGError) as e:
+            dg.dg_mixed_forward(ctx, kv, canvas, None, 32, hid, ws, 0)
+        assert e.value.status == dg.DG_EINVAL
+        with pytest.raises(dg.DGError) as e:
+            dg.dg_mixed_forward(ctx, kv, canvas, flags, 32, None, ws, 0)
+        assert e.value.status == dg.DG_EINVAL
+        cap[0] = cap[1] = 64 + 16
+        with pytest.raises(dg.DGError) as e:
+            dg.dg_mixed_forward(ctx, kv, canvas, flags, 32, hid, ws, 0)
+        assert e.value.status == dg.DG_EINVAL and "cap" in dg.dg_last_error()
+        cap[0] = cap[1] = 128
+        with pytest.raises(dg.DGError) as e:
+            dg.dg_mixed_forward(ctx, kv, canvas, flags, 24, hid, ws, 0)
+        assert e.value.status == dg.DG_EUNSUPPORTED
+        with pytest.raises(dg.DGError) as e:
+            dg.dg_mixed_forward(ctx, kv, canvas, flags, 32, hid, _FakeTensor(0x10000000, need - 1), 0)
+        assert e.value.status == dg.DG_EWORKSPACE
     finally:
         dg.dg_destroy(ctx)
