@@ -56,8 +56,8 @@ def parse():
 # (FETCH_SIZE, WRITE_SIZE; KiB per dispatch, mean of 90 launches), each scaled by the same counter
 # on a 512 MiB device-to-device copy (FETCH_SIZE reads 262155.5 KiB for 524288 KiB read: x1.9999;
 # WRITE_SIZE reads 524288 KiB: x1).  Valid only while the kernel sources hash to `sources`.
-MOE_TRAFFIC = {"sources": "3b23669b67396d735115fb67662deda8dbf11a2968d927cf407407ac0852e54e",
-               "fetch_kib": 527799.6, "write_kib": 3872.1, "bytes_per_launch": 1084850678}
+MOE_TRAFFIC = {"sources": "0d5cb1be9142ad995c74d4ab9ef2e2572d0c0cdb5878351a9b158c51cfa9ac18",
+               "fetch_kib": 527731.9, "write_kib": 3872.1, "bytes_per_launch": 1084712550}
 TRAFFIC_SOURCES = ("k_gemm.hip", "gemm_dma.h", "gemm_core.h", "common.h", "internal.h")
 
 
