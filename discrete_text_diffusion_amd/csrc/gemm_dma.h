@@ -180,15 +180,18 @@ struct GemmDma {
 
 // Weights-only quantised B on the same direct-to-LDS ring: fp8 e4m3 codes (their per-row scale is
 // applied by the caller's epilogue) or MXFP4 (e2m1 codes with one e8m0 scale per 32 elements).  A
-// stage is 64 K-elements: A (bf16) as 128-byte rows in the GemmDma layout; B as its raw codes, 64
-// bytes (fp8) or 32 bytes (MXFP4) per row, the 16-byte chunk c of row r stored in slot
-// c ^ ((r >> 2) & 3) (fp8) or c ^ ((r >> 3) & 1) (MXFP4) so 16-row fragment reads hit distinct
-// banks; MXFP4 scales as one 32-bit word per (row, 32-element block) (a byte-sized direct load
-// writes each byte zero-extended to a word).  Codes are widened to bf16 in registers just before
-// the MFMA, so no widened copy passes through LDS.
+// stage is 64 K-elements: A (bf16) as 128-byte rows; B as its raw codes, 64 bytes (fp8) or 32 bytes
+// (MXFP4) per row, the 16-byte chunk c of row r stored in slot c ^ ((r >> 1) & 3) (fp8) or
+// c ^ ((r >> 3) & 1) (MXFP4); MXFP4 scales as one 32-bit word per (row, 32-element block) (a
+// byte-sized direct load writes each byte zero-extended to a word).  Codes are widened to bf16 in
+// registers just before the MFMA, so no widened copy passes through LDS.
 // K order inside a stage: lane group kg = lane >> 4 owns elements [16 kg, 16 kg + 16) of every
 // row (half an MXFP4 scale block, one fp8 chunk), its MFMA chunk c in {0, 1} the elements
-// 16 kg + 8 c .. + 7; A is read with the same map, so the sum over the stage is unchanged.
+// 16 kg + 8 c .. + 7; A is read with the same map, so the sum over the stage is unchanged.  The A
+// row keeps that chunk (2 kg + c) in slot (4 c + kg) ^ ((r >> 1) & 7): a 16-row fragment read then
+// has the bank pattern of the bf16 ring's.  Measured on gfx950 (16-byte reads, 8 waves): this A
+// pattern and the fp8 B swizzle on r >> 1 read at ~188 B/clock per CU; kg in the high chunk bits
+// (2 kg + c) ^ (r >> 1), or a B swizzle on r >> 2, r & 3 or none, at ~110 (bank conflicts).
 template <class TB, int BM, int BN, int WM, int WN, int NS>
 struct GemmDmaQ {
   static constexpr bool FP4 = is_fp4_v<TB>;
@@ -223,7 +226,8 @@ struct GemmDmaQ {
         const int r = (wave + NW * i) * 8 + rr;
         const char* p = reinterpret_cast<const char*>(arow(r));
         if (!p) p = reinterpret_cast<const char*>(arow(0));
-        a_src[i] = p + ((slot ^ ((r >> 1) & 7)) * 16);
+        const int s = slot ^ ((r >> 1) & 7);             // = 4 c + kg of the chunk this lane fetches
+        a_src[i] = p + ((((s & 3) << 1) | (s >> 2)) * 16);
       }
     }
     {
@@ -234,7 +238,7 @@ struct GemmDmaQ {
         const int r = (wave + NW * i) * BRPI + rr;
         const char* p = reinterpret_cast<const char*>(brow(r));
         if (!p) p = reinterpret_cast<const char*>(brow(0));
-        const int sw = FP4 ? ((r >> 3) & 1) : ((r >> 2) & 3);
+        const int sw = FP4 ? ((r >> 3) & 1) : ((r >> 1) & 3);
         b_src[i] = p + ((slot ^ sw) * 16);
       }
     }
@@ -288,7 +292,7 @@ struct GemmDmaQ {
         bfr[j][1] = widen_fp4_word(w.y, sc);
       } else {
         const char* row = st + A_BYTES + n * 64;
-        const u32x4 w = *reinterpret_cast<const u32x4*>(row + ((kg ^ ((n >> 2) & 3)) * 16));
+        const u32x4 w = *reinterpret_cast<const u32x4*>(row + ((kg ^ ((n >> 1) & 3)) * 16));
         bfr[j][0] = widen_fp8_lo(w);
         bfr[j][1] = widen_fp8_hi(w);
       }
@@ -296,7 +300,7 @@ struct GemmDmaQ {
     const char* la = st + (wm * FM * 16 + l16) * 128;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const int so = (((2 * kg + c) ^ swa)) * 16;     // A elements 16 kg + 8 c .. + 7
+      const int so = (((4 * c + kg) ^ swa)) * 16;     // A elements 16 kg + 8 c .. + 7
       u32x4 af[FM];
 #pragma unroll
       for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const u32x4*>(la + i * 16 * 128 + so);
