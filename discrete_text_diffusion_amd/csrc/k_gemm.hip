@@ -311,19 +311,33 @@ DG_DEV void grouped_tile(char* lds, const TA* A, int64_t lda, const int32_t* a_t
 // BMS rows (every shared weight tile passes through a CU once per row tile), first (its tiles are
 // the longest, so they go before the routed tiles rather than into the tail); the n_sh_items row
 // tiles of one column tile get ids congruent mod 8 (one XCD, one L2 copy of that weight tile).
-// Blocks [sh_blocks, ...): routed tiles of BM rows, block - sh_blocks = item * nt_r + column
-// tile; work item w < *n_items: expert e = work[2w], first row m0 = work[2w+1] of that expert's
-// rows [offsets[e], offsets[e] + counts[e]) in grouped order.  The dynamic LDS holds the larger
-// of the two tile shapes' rings.
-template <class TA, class TB, int BM, int BMS, int BN, int WM, int WN, int EPI, int NS = 0, int QNS = 6>
+// Blocks [sh_blocks, ...): routed tiles of BM rows; work item w < *n_items: expert e = work[2w],
+// first row m0 = work[2w+1] of that expert's rows [offsets[e], offsets[e] + counts[e]) in grouped
+// order.  XCDR = 0: block - sh_blocks = item * nt_r + column tile.  XCDR = 1 (large experts cut
+// into many items): the items fall into groups of XG; unit u = group * nt_r + column tile holds
+// that column tile of the group's XG items, and all XG blocks of unit u sit on XCD u mod 8 (block
+// id mod 8).  An expert's items are consecutive, so its items in one group read each weight tile
+// on one XCD and share its L2 copy, while consecutive units still cycle over all 8 XCDs.  The
+// dynamic LDS holds the larger of the two tile shapes' rings.
+constexpr int XG = 16;
+
+template <class TA, class TB, int BM, int BMS, int BN, int WM, int WN, int EPI, int NS = 0, int QNS = 6, int XCDR = 0>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_grouped_kernel(GroupedArgs p) {
   using G = GroupTileFor<TA, TB, BM, BN, WM, WN, NS, QNS>;
   using GS = GroupTileFor<TA, TB, BMS, BN, WM, WN, NS, QNS>;
   extern __shared__ __align__(16) char lds[];
   const int id = blockIdx.x;
   if (id >= p.sh_blocks) {
-    const int rid = id - p.sh_blocks;
-    const int item = rid / p.nt_r;
+    const int rid = id - p.sh_blocks;      // sh_blocks is a multiple of 8: rid and id share an XCD
+    int item, col;
+    if constexpr (XCDR) {
+      const int k = rid >> 3, u = 8 * (k / XG) + (rid & 7), g = u / p.nt_r;
+      col = u - g * p.nt_r;
+      item = g * XG + k % XG;
+    } else {
+      item = rid / p.nt_r;
+      col = rid - item * p.nt_r;
+    }
     if (item >= *p.n_items) return;
     const int e = p.work[2 * item], m0 = p.work[2 * item + 1];
     grouped_tile<G, BN, WN, EPI>(lds, static_cast<const TA*>(p.A), p.lda, p.a_tok, p.offsets[e] + m0,
@@ -331,8 +345,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_grouped_kernel(GroupedArgs 
                                  p.B2 ? static_cast<const TB*>(p.B2) + (int64_t)e * p.b_estride : nullptr, p.ldb,
                                  p.sB ? static_cast<const char*>(p.sB) + (int64_t)e * p.s_estride : nullptr,
                                  p.sB2 ? static_cast<const char*>(p.sB2) + (int64_t)e * p.s_estride : nullptr,
-                                 p.s_ld, p.N, p.K,
-                                 (rid - item * p.nt_r) * BN, p.C, p.ldc);
+                                 p.s_ld, p.N, p.K, col * BN, p.C, p.ldc);
   } else {
     const int j = id >> 3;
     const int it = j % p.n_sh_items, nt = (j / p.n_sh_items) * 8 + (id & 7);
@@ -424,7 +437,7 @@ hipError_t launch_dense(const DenseArgs& a, int act_bf16, int w_kind, hipStream_
   return dense_dispatch<bf16_t, bf16_t>(a, s);
 }
 
-template <class TA, class TB, int BM, int BMS, int BN, int WM, int WN, int EPI, int NS = 0, int QNS = 6>
+template <class TA, class TB, int BM, int BMS, int BN, int WM, int WN, int EPI, int NS = 0, int QNS = 6, int XCDR = 0>
 static hipError_t launch_grouped_t(GroupedArgs a, int n_eff, int sh_eff, int max_items, hipStream_t s) {
   using G = GroupTileFor<TA, TB, BM, BN, WM, WN, NS, QNS>;
   using GS = GroupTileFor<TA, TB, BMS, BN, WM, WN, NS, QNS>;
@@ -433,12 +446,13 @@ static hipError_t launch_grouped_t(GroupedArgs a, int n_eff, int sh_eff, int max
   a.nt_s = (sh_eff + BN - 1) / BN;
   a.n_sh_items = a.shB ? (a.sh_rows + BMS - 1) / BMS : 0;
   a.sh_blocks = (a.nt_s + 7) / 8 * a.n_sh_items * 8;
-  const int blocks = a.sh_blocks + max_items * a.nt_r;
+  const int units = (max_items + XG - 1) / XG * a.nt_r;
+  const int blocks = a.sh_blocks + (XCDR ? (units + 7) / 8 * 8 * XG : max_items * a.nt_r);
   if (blocks == 0) return hipSuccess;
   if (a.K % G::KT || (a.shB && a.shK % GS::KT)) return hipErrorInvalidValue;
-  static const hipError_t attr = allow_lds(gemm_grouped_kernel<TA, TB, BM, BMS, BN, WM, WN, EPI, NS, QNS>, LDS);
+  static const hipError_t attr = allow_lds(gemm_grouped_kernel<TA, TB, BM, BMS, BN, WM, WN, EPI, NS, QNS, XCDR>, LDS);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((gemm_grouped_kernel<TA, TB, BM, BMS, BN, WM, WN, EPI, NS, QNS>), dim3(blocks), dim3(WM * WN * 64),
+  hipLaunchKernelGGL((gemm_grouped_kernel<TA, TB, BM, BMS, BN, WM, WN, EPI, NS, QNS, XCDR>), dim3(blocks), dim3(WM * WN * 64),
                      LDS, s, a);
   return hipGetLastError();
 }
@@ -455,8 +469,8 @@ static hipError_t launch_grouped_t(GroupedArgs a, int n_eff, int sh_eff, int max
 template <class TA, class TB, int EPI>
 static hipError_t grouped_wide(const GroupedArgs& a, int n_eff, int sh_eff, int max_items, hipStream_t s) {
   constexpr int W = GROUP_BM_WIDE;
-  if constexpr (is_fp4_v<TB>) return launch_grouped_t<TA, TB, W, W, 128, 2, 2, EPI>(a, n_eff, sh_eff, max_items, s);
-  else return launch_grouped_t<TA, TB, W, W, 256, 2, 4, EPI, 3, 4>(a, n_eff, sh_eff, max_items, s);
+  if constexpr (is_fp4_v<TB>) return launch_grouped_t<TA, TB, W, W, 128, 2, 2, EPI, 0, 6, 1>(a, n_eff, sh_eff, max_items, s);
+  else return launch_grouped_t<TA, TB, W, W, 256, 2, 4, EPI, 3, 4, 1>(a, n_eff, sh_eff, max_items, s);
 }
 
 template <class TA, class TB>
