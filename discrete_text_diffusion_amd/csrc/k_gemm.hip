@@ -317,8 +317,9 @@ DG_DEV void grouped_tile(char* lds, const TA* A, int64_t lda, const int32_t* a_t
 // into many items): the items fall into groups of XG; unit u = group * nt_r + column tile holds
 // that column tile of the group's XG items, and all XG blocks of unit u sit on XCD u mod 8 (block
 // id mod 8).  An expert's items are consecutive, so its items in one group read each weight tile
-// on one XCD and share its L2 copy, while consecutive units still cycle over all 8 XCDs.  The
-// dynamic LDS holds the larger of the two tile shapes' rings.
+// on one XCD and share its L2 copy, while consecutive units still cycle over all 8 XCDs; an
+// expert's last item, when it holds BM/2 rows or fewer, runs on a BM/2-row tile.  The dynamic LDS
+// holds the larger of the tile shapes' rings.
 constexpr int XG = 16;
 
 template <class TA, class TB, int BM, int BMS, int BN, int WM, int WN, int EPI, int NS = 0, int QNS = 6, int XCDR = 0>
@@ -339,9 +340,21 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_grouped_kernel(GroupedArgs 
       col = rid - item * p.nt_r;
     }
     if (item >= *p.n_items) return;
-    const int e = p.work[2 * item], m0 = p.work[2 * item + 1];
+    const int e = p.work[2 * item], m0 = p.work[2 * item + 1], rows = min(BM, p.counts[e] - m0);
+    if constexpr (XCDR) {
+      if (rows <= BM / 2) {
+        using GH = GroupTileFor<TA, TB, BM / 2, BN, WM, WN, NS, QNS>;
+        grouped_tile<GH, BN, WN, EPI>(lds, static_cast<const TA*>(p.A), p.lda, p.a_tok, p.offsets[e] + m0, rows,
+                                      static_cast<const TB*>(p.B) + (int64_t)e * p.b_estride,
+                                      p.B2 ? static_cast<const TB*>(p.B2) + (int64_t)e * p.b_estride : nullptr, p.ldb,
+                                      p.sB ? static_cast<const char*>(p.sB) + (int64_t)e * p.s_estride : nullptr,
+                                      p.sB2 ? static_cast<const char*>(p.sB2) + (int64_t)e * p.s_estride : nullptr,
+                                      p.s_ld, p.N, p.K, col * BN, p.C, p.ldc);
+        return;
+      }
+    }
     grouped_tile<G, BN, WN, EPI>(lds, static_cast<const TA*>(p.A), p.lda, p.a_tok, p.offsets[e] + m0,
-                                 min(BM, p.counts[e] - m0), static_cast<const TB*>(p.B) + (int64_t)e * p.b_estride,
+                                 rows, static_cast<const TB*>(p.B) + (int64_t)e * p.b_estride,
                                  p.B2 ? static_cast<const TB*>(p.B2) + (int64_t)e * p.b_estride : nullptr, p.ldb,
                                  p.sB ? static_cast<const char*>(p.sB) + (int64_t)e * p.s_estride : nullptr,
                                  p.sB2 ? static_cast<const char*>(p.sB2) + (int64_t)e * p.s_estride : nullptr,
