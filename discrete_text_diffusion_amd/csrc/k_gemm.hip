@@ -399,10 +399,14 @@ template <class TA, class TB, int EPI, int MAP>
 static hipError_t dense_pick(const DenseArgs& a, int n_eff, hipStream_t s) {
   const bool small = a.M <= 64;
   if constexpr (MAP == MAP_ROPE) {
-    // a column tile must stay inside one head
+    // a column tile must stay inside one head; above 256 rows bf16 weights take 256 x 256 tiles
+    // (128 x 64 per wave, two 64 KB ring stages) when a head spans 256 columns
     if (a.M > 256 && a.dh >= 128) {
       if constexpr (sizeof(TB) == 1) return launch_dense_t<TA, TB, 128, 128, 2, 2, EPI, MAP>(a, n_eff, s);
-      else return launch_dense_t<TA, TB, 256, 128, 4, 2, EPI, MAP, 3>(a, n_eff, s);
+      else {
+        if (a.dh % 256 == 0) return launch_dense_t<TA, TB, 256, 256, 2, 4, EPI, MAP, 2>(a, n_eff, s);
+        return launch_dense_t<TA, TB, 256, 128, 4, 2, EPI, MAP, 3>(a, n_eff, s);
+      }
     }
     if (small) return launch_dense_t<TA, TB, 64, 64, 2, 2, EPI, MAP>(a, n_eff, s);
     if constexpr (sizeof(TB) == 1) return launch_dense_t<TA, TB, 128, 64, 2, 2, EPI, MAP>(a, n_eff, s);
