@@ -419,8 +419,10 @@ static hipError_t dense_pick(const DenseArgs& a, int n_eff, hipStream_t s) {
     if (small) return launch_dense_t<TA, TB, 64, 64, 2, 2, EPI, MAP>(a, n_eff, s);
     if (a.N <= 256) return launch_dense_t<TA, TB, 64, 32, 4, 1, EPI, MAP>(a, n_eff, s);
     if (a.M > 256) {
+      // bf16 weights: 128 x 192 tiles on 8 waves (64 x 48 per wave): at 2048 x 2816 (the attention
+      // output projection of 8 canvases) 240 blocks where 256 x 128 tiles give 176 of 256 CUs
       if constexpr (sizeof(TB) == 1) return launch_dense_t<TA, TB, 128, 128, 2, 2, EPI, MAP>(a, n_eff, s);
-      else return launch_dense_t<TA, TB, 256, 128, 4, 2, EPI, MAP, 3>(a, n_eff, s);
+      else return launch_dense_t<TA, TB, 128, 192, 2, 4, EPI, MAP, 3>(a, n_eff, s);
     }
     if constexpr (sizeof(TB) != 1) {
       // wide outputs up to 256 rows (the attention output projection): 8 waves, two K tiles per
