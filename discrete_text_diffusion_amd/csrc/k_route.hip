@@ -172,10 +172,15 @@ __global__ __launch_bounds__(256) void route_place_kernel(const int32_t* idx_g, 
   __shared__ int red[4];
   __shared__ int wsum[4];
   __shared__ int hist[256];
-  extern __shared__ int32_t idx_s[];
+  extern __shared__ __align__(16) int32_t idx_s[];
   for (int q = threadIdx.x; q < 256; q += 256) hist[q] = 0;
-  if constexpr (STAGED)
-    for (int i = threadIdx.x; i < T * k; i += 256) idx_s[i] = idx_g[i];
+  if constexpr (STAGED) {
+    // 16-byte loads when the picks are 16-byte aligned, then the tail one by one
+    const int n4 = (reinterpret_cast<uintptr_t>(idx_g) & 15) == 0 ? (T * k) >> 2 : 0;
+    for (int i = threadIdx.x; i < n4; i += 256)
+      reinterpret_cast<int4*>(idx_s)[i] = reinterpret_cast<const int4*>(idx_g)[i];
+    for (int i = 4 * n4 + threadIdx.x; i < T * k; i += 256) idx_s[i] = idx_g[i];
+  }
   __syncthreads();
   const int32_t* idx = STAGED ? idx_s : idx_g;
   for (int i = threadIdx.x; i < T * k; i += 256) atomicAdd(&hist[min(max(idx[i], 0), E - 1)], 1);
