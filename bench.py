@@ -56,8 +56,8 @@ def parse():
 # (FETCH_SIZE, WRITE_SIZE; KiB per dispatch, mean of 90 launches), each scaled by the same counter
 # on a 512 MiB device-to-device copy (FETCH_SIZE reads 262155.5 KiB for 524288 KiB read: x1.9999;
 # WRITE_SIZE reads 524288 KiB: x1).  Valid only while the kernel sources hash to `sources`.
-MOE_TRAFFIC = {"sources": "06d2e7204ba51940b6ece2349b8cb22b869b896d3c1e8e98a9a8ad58429fc64e",
-               "fetch_kib": 527749.1, "write_kib": 3872.1, "bytes_per_launch": 1084744167}
+MOE_TRAFFIC = {"sources": "ff301ebbffeb3a85b5c2b1b655e4de0d3c02d2f66b11c3e250b26fa5ab2dfa59",
+               "fetch_kib": 527744.2, "write_kib": 3872.1, "bytes_per_launch": 1084734132}
 TRAFFIC_SOURCES = ("k_gemm.hip", "gemm_dma.h", "gemm_core.h", "common.h", "internal.h")
 
 
