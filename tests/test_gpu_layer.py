@@ -22,8 +22,11 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
-@pytest.mark.parametrize("T,E,k", [(256, 128, 8), (2048, 128, 8), (37, 8, 2), (64, 256, 16)])
-def test_router_topk_and_grouping_bit_exact(T, E, k):
+@pytest.mark.parametrize("T,E,k,shift", [(256, 128, 8, 0), (2048, 128, 8, 0), (2048, 128, 8, 1), (37, 8, 2, 0),
+                                         (37, 8, 2, 3), (64, 256, 16, 0)])
+def test_router_topk_and_grouping_bit_exact(T, E, k, shift):
+    """shift > 0 places the caller's pick buffer `shift` int32 past a 16-byte boundary: the routing
+    tables then stage the picks element by element instead of in 16-byte loads."""
     g = torch.Generator(device="cpu").manual_seed(T * 7 + E)
     s = torch.randn(T, E, generator=g)
     s[::9, 5] = s[::9, 6] = s[::9, 7] = 3.5           # exact ties at the top
@@ -32,7 +35,8 @@ def test_router_topk_and_grouping_bit_exact(T, E, k):
     s[5::29, ::3] = -0.0                                # signed zeros compare equal
     s[6::31, 3:] = -float("inf")                        # fewer finite scores than k
     sd = s.to(DEV)
-    idx = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    idx = torch.empty(T * k + shift, dtype=torch.int32, device=DEV)[shift:].view(T, k)
+    assert (idx.data_ptr() % 16 != 0) == (shift != 0)
     gates = torch.empty(T, k, dtype=torch.float32, device=DEV)
     counts = torch.empty(E, dtype=torch.int32, device=DEV)
     offs = torch.empty(E, dtype=torch.int32, device=DEV)
