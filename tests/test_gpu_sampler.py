@@ -94,14 +94,22 @@ def test_locked_canvas_is_fixed_point_on_gpu():
     assert torch.equal(cv, cv0) and bool(lk.all()) and nl.tolist() == [L, L]
 
 
-@pytest.mark.parametrize("case", ["tiny-fp32", "vocab262k-bf16"])
+@pytest.mark.parametrize("case", ["tiny-fp32", "vocab262k-bf16", "vocab262k-bf16-b8", "vocab262k-bf16-ragged"])
 def test_fused_sampler_parity(case):
+    """Row tiles of 256: one canvas is one tile; eight canvases (2048 rows, the batched workload)
+    are 8 row tiles per vocabulary slice; 3 canvases of 112 end in a ragged 80-row tile."""
     if case == "tiny-fp32":
         cfg = configs.C0
         rows_checked = None
-    else:
+    elif case == "vocab262k-bf16":
         cfg = configs.C2.replace(n_layers=1)
         rows_checked = np.arange(0, 256, 4)            # 64 sampled rows, every 4th position
+    elif case == "vocab262k-bf16-b8":
+        cfg = configs.C2.replace(n_layers=1, batch=8)
+        rows_checked = np.arange(5, 2048, 32)          # 64 rows, two in every row tile
+    else:
+        cfg = configs.C2.replace(n_layers=1, batch=3, canvas=112)
+        rows_checked = np.arange(0, 336, 3)            # 112 rows, 27 in the ragged tile
     B, L, V = cfg.batch, cfg.canvas, cfg.vocab
     log(f"fused sampler {case}: rows={B * L} V={V} d={cfg.d_model}")
     model, W, _ = build(cfg)
