@@ -483,13 +483,18 @@ static hipError_t launch_grouped_t(GroupedArgs a, int n_eff, int sh_eff, int max
 // Batched canvases (experts averaging 64 rows or more): 128-row tiles for the routed experts and
 // the shared expert, so a popular expert's weights stream once per 128 rows rather than per 32.
 // bf16 and fp8 on 8 waves with 256-column tiles (the activation rows, which outweigh fp8 weights
-// per stage, are re-read by half as many column tiles; 3- and 4-stage rings, one block per CU),
+// per stage, are re-read by half as many column tiles),
 // MXFP4 on the 4-wave register-staged engine (128 columns).
 template <class TA, class TB, int EPI>
 static hipError_t grouped_wide(const GroupedArgs& a, int n_eff, int sh_eff, int max_items, hipStream_t s) {
   constexpr int W = GROUP_BM_WIDE;
   if constexpr (is_fp4_v<TB>) return launch_grouped_t<TA, TB, W, W, 128, 2, 2, EPI, 0, 6, 1>(a, n_eff, sh_eff, max_items, s);
-  else return launch_grouped_t<TA, TB, W, W, 256, 2, 4, EPI, 3, 4, 1>(a, n_eff, sh_eff, max_items, s);
+  else if constexpr (is_fp8_v<TB>) {
+    // fp8 rings: 3 stages (96 KB, one block per CU) for gate/up over K = d_model; 2 stages (64 KB,
+    // two blocks per CU, which hide each other's short K loops) for down over K = expert width
+    constexpr int Q = EPI == EPI_SWIGLU ? 3 : 2;
+    return launch_grouped_t<TA, TB, W, W, 256, 2, 4, EPI, 3, Q, 1>(a, n_eff, sh_eff, max_items, s);
+  } else return launch_grouped_t<TA, TB, W, W, 256, 2, 4, EPI, 3, 4, 1>(a, n_eff, sh_eff, max_items, s);
 }
 
 template <class TA, class TB>
