@@ -56,8 +56,8 @@ def parse():
 # (FETCH_SIZE, WRITE_SIZE; KiB per dispatch, mean of 90 launches), each scaled by the same counter
 # on a 512 MiB device-to-device copy (FETCH_SIZE reads 262155.5 KiB for 524288 KiB read: x1.9999;
 # WRITE_SIZE reads 524288 KiB: x1).  Valid only while the kernel sources hash to `sources`.
-MOE_TRAFFIC = {"sources": "ff301ebbffeb3a85b5c2b1b655e4de0d3c02d2f66b11c3e250b26fa5ab2dfa59",
-               "fetch_kib": 527744.2, "write_kib": 3872.1, "bytes_per_launch": 1084734132}
+MOE_TRAFFIC = {"sources": "1236a6494d419fab5078079aebf4a8aac57e398780059e61e0d90191b55c1160",
+               "fetch_kib": 527794.2, "write_kib": 3872.1, "bytes_per_launch": 1084839620}
 TRAFFIC_SOURCES = ("k_gemm.hip", "gemm_dma.h", "gemm_core.h", "common.h", "internal.h")
 
 
