@@ -5,10 +5,11 @@ the uniform canvas at t = 1, then dg_denoise_step (30-layer decoder over prefix 
 and dg_step_sample (fused LM head -> Step with lock-in) at the schedule's next grid point.
 Inputs (weights, caches) are resident in HBM before timing starts.
 
-    python bench.py [--steps K] [--warmup W] [--workload C2] [--sampler euler|eb] [--no-cpu-baseline]
-                    [--no-breakdown] [--experts bf16|fp8|mxfp4]
+    python bench.py [--steps K] [--warmup W] [--repeats R] [--workload C2] [--sampler euler|eb]
+                    [--no-cpu-baseline] [--no-breakdown] [--experts bf16|fp8|mxfp4]
 
-Prints one JSON line.  `value` = canvas tokens refined per second (batch * 256 * steps/s).  After
+Prints one JSON line.  `value` = canvas tokens refined per second (batch * 256 * steps/s), from the
+median of R timed runs of K steps each (each run bracketed by device synchronisations).  After
 the timed region one more schedule of steps runs with per-class launch timing: `breakdown` gives
 each kernel class's time per step and its achieved rate against the roof that bounds it (HBM
 bytes or bf16 MFMA FLOPs, algorithmic: what the method must move or compute).
@@ -38,6 +39,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=24)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="timed runs of K steps each; ms_per_step is their median")
     ap.add_argument("--workload", default="C2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-class timing after the timed region")
@@ -120,8 +123,8 @@ def cpu_baseline(cfg, W, kv, H_dev):
     from oracle import model as M
     from oracle import step as S
     from oracle.numerics import rounder
-    from tests.helpers import np64, oracle_layer
     from synth import gen
+    from synth.host import layer_np, np64
 
     try:
         from threadpoolctl import threadpool_info
@@ -134,7 +137,7 @@ def cpu_baseline(cfg, W, kv, H_dev):
     h0 = gen.resid_input(cfg.replace(resid_input=True)).numpy().astype(np.float64)
     times = {"local": [], "global": []}
     for tag, l in [("global" if cfg.is_global(l) else "local", l) for l in sample_layers]:
-        lw = oracle_layer(W["layers"][l], cfg)                  # conversion: not timed
+        lw = M.layer_arrays(layer_np(W["layers"][l]), cfg.expert_dtype)   # conversion: not timed
         K, V = np64(kv[l][0]), np64(kv[l][1])
         t0 = time.perf_counter()
         M.denoise_layer(cfg, l, h0, lw, K, V, [cfg.prefix] * cfg.batch, rnd)
@@ -226,18 +229,23 @@ def main():
     # tail (~4.5 us per event), so sampling the launches keeps the measurement from slowing the
     # step it measures.
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for s in range(args.steps):
-        dg.dg_profile_enable(model.ctx, (1 << dg.PROF_MOE_GATE_UP) if s % PROF_EVERY == 0 else 0)
-        step(args.warmup + s)
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    reps = []
+    done_steps = args.warmup
+    for r in range(max(args.repeats, 1)):
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for s in range(args.steps):
+            dg.dg_profile_enable(model.ctx, (1 << dg.PROF_MOE_GATE_UP) if s % PROF_EVERY == 0 else 0)
+            step(done_steps + s)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        done_steps += args.steps
+        reps.append(ev0.elapsed_time(ev1) / args.steps)
+        log(f"[bench] timed run {r + 1}/{max(args.repeats, 1)}: {reps[-1]:.4f} ms/step")
     dg.dg_profile_enable(model.ctx, 0)
-    ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / args.steps
+    ms_step = float(np.median(reps))
     moe_ms, moe_n = dg.dg_profile_read(model.ctx, dg.PROF_MOE_GATE_UP)
-    log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step")
+    log(f"[bench] median of {len(reps)} timed runs of {args.steps} steps: {ms_step:.3f} ms/step")
 
     # unique experts of the last layer's routing (same workload in every layer)
     idx = torch.empty(B * L, cfg.top_k, dtype=torch.int32, device=dev)
@@ -306,6 +314,7 @@ def main():
         "unit": "canvas-token-steps/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "repeats": len(reps), "ms_per_step_runs": [round(x, 4) for x in reps],
         "steps_per_s": round(steps_per_s, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.act_dtype if cfg.expert_dtype in ("f32", "bf16") else f"bf16+{cfg.expert_dtype}w",

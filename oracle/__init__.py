@@ -11,8 +11,10 @@ call or execute anything in this package.  It shares no code with the HIP librar
 imports it: the two meet only through the seeded arrays of `synth/`.
 
 Parity status per function:
-  philox.philox4x32_10   pinned by statistics (uniformity, bit balance, avalanche) only — no
-                         known-answer vectors are available here, so its exact bit pattern is
-                         pinned to nothing outside itself ("parity unpinned" for the bits).
+  philox.philox4x32_10   pinned to the published Random123 known-answer vectors (Salmon et al.,
+                         SC'11) and by statistics (uniformity, bit balance, avalanche)
+  model.denoise_layer / denoise_forward
+                         pinned by zero-weight reductions to independently written attention and
+                         MoE expectations (pre-norm composition, both residual adds)
   everything else        pinned by closed forms, invariants or brute force in tests/test_oracle_*.py
 """

@@ -1,21 +1,10 @@
 """Test plumbing: turn the seeded storage tensors of `synth` into the oracle's float64 arrays."""
-import numpy as np
-import torch
-
 from oracle.model import layer_arrays
-
-
-def np64(t):
-    if t is None:
-        return None
-    if t.dtype == torch.uint8:
-        return t.cpu().numpy()
-    return t.float().cpu().numpy().astype(np.float64)
+from synth.host import layer_np, np64  # noqa: F401  (re-exported for the tests)
 
 
 def oracle_layer(L: dict, cfg) -> dict:
-    raw = {k: np64(v) for k, v in L.items()}
-    return layer_arrays(raw, cfg.expert_dtype)
+    return layer_arrays(layer_np(L), cfg.expert_dtype)
 
 
 def oracle_weights(W: dict, cfg, layers=None) -> dict:
