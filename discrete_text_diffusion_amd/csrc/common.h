@@ -7,6 +7,13 @@
 
 namespace dg {
 
+// A closed launch gate (see launch_gate): the whole grid returns before doing anything.
+DG_DEV bool gate_closed(const int32_t* gate) { return gate != nullptr && *gate != 0; }
+
+// A canvas's prefix length from the device array, clamped to [0, max_prefix] so that no cache
+// access can leave the slots the host validated.
+DG_DEV int prefix_of(const int32_t* plen, int b, int max_prefix) { return min(max(plen[b], 0), max_prefix); }
+
 typedef uint16_t bf16_t;  // raw bf16 word
 
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8_v;

@@ -5,7 +5,19 @@
 
 namespace dg {
 
-constexpr int MAX_BATCH = 64;     // canvases per call (prefix lengths travel as kernel arguments)
+// Launch gate: a device int32 that, when nonzero as a kernel starts, makes every block of that
+// kernel return at once.  The canvas loops point it at a flag their Step sets once every canvas is
+// done, so the passes enqueued up front for the remaining steps cost only their launches, with no
+// host read.  The current gate belongs to the calling host thread while a GateScope lives; every
+// launcher below passes it to its kernel (null: always open).
+const int32_t* launch_gate();
+struct GateScope {
+  const int32_t* prev;
+  explicit GateScope(const int32_t* gate);
+  ~GateScope();
+};
+
+constexpr int MAX_BATCH = 64;     // canvases per call
 constexpr int GROUP_BM = 32;       // rows per expert tile of the grouped GEMMs
 constexpr int GROUP_BM_WIDE = 128; // ... once experts average 64 rows or more (batched canvases)
 // rows per routed expert tile for `picks` = rows x top_k routed rows over E experts
@@ -31,12 +43,13 @@ struct DenseArgs {
                                          // v d-major [B][Hkv][dh][v_ld]
   int Hq, Hkv, dh, rows_per_canvas, v_ld;
   const float2* rope;                    // (cos, sin) [M][dh/2] from launch_rope_table
+  const int32_t* gate;                   // launch gate (set by the launcher)
 };
 
-struct RopePos { int32_t pos0[MAX_BATCH]; };  // RoPE position of row 0 of each canvas
-// (cos, sin) table [rows][head_dim/2] for the RoPE positions pos0[b] + i of canvas rows
+// (cos, sin) table [rows][head_dim/2] for the RoPE positions plen[b] + i of canvas rows; plen is
+// device [B], each value clamped to [0, max_prefix] (a value outside sets bit 4 of *status)
 hipError_t launch_rope_table(float2* tab, int rows, int rows_per_canvas, int head_dim, double log2_theta,
-                             const int32_t* pos0, int B, hipStream_t s);
+                             const int32_t* plen, int max_prefix, int* status, hipStream_t s);
 
 struct GroupedArgs {
   int epi;
@@ -57,6 +70,7 @@ struct GroupedArgs {
   void* shC; int64_t sh_ldc;
   int bm;                                             // rows per routed tile: GROUP_BM or GROUP_BM_WIDE
   int nt_r, nt_s, sh_blocks, n_sh_items;              // filled by the launcher
+  const int32_t* gate;                                // launch gate (set by the launcher)
 };
 
 hipError_t launch_dense(const DenseArgs& a, int act_bf16, int w_kind, hipStream_t s);
@@ -77,7 +91,9 @@ struct AttnArgs {
   float* part_o; float* part_ml;    // [splits][B*n][Hq][dh], [splits][B*n][Hq][2] (splits > 1);
                                     // part_o holds fp32 sums (fp32 kernel) or IEEE-half O_s / l_s (bf16)
   void* out;              // [B*n][Hq*dh] act (splits == 1)
-  int32_t pos0[MAX_BATCH];          // prefix length per canvas
+  const int32_t* plen;    // device [B]: prefix length per canvas, clamped to [0, max_prefix]
+  int max_prefix;
+  const int32_t* gate;    // launch gate (set by the launcher)
 };
 hipError_t launch_attention(const AttnArgs& a, int act_bf16, hipStream_t s);
 hipError_t launch_flash(const AttnArgs& a, hipStream_t s);
@@ -92,10 +108,16 @@ hipError_t launch_embed(const int32_t* tokens, const void* embed, float* resid, 
 hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
 hipError_t launch_rmsnorm(const float* x, const void* g, void* y, int rows, int d, float eps,
                           int act_bf16, int* status, hipStream_t s);
-// seq_mask: device [B] or null; with it only canvases b with seq_mask[b] != 0 are appended
+// seq_mask: device [B] or null; with it only canvases b with seq_mask[b] != 0 are appended at
+// positions plen[b] .. (device [B], clamped to [0, max_prefix])
 hipError_t launch_kv_append(const void* kn, const void* vn, int vn_ld, void* kc, void* vc, int B, int n,
                             int Hkv, int dh, int cap, int window, int is_global,
-                            const int32_t* pos0, const int32_t* seq_mask, int act_bf16, hipStream_t s);
+                            const int32_t* plen, int max_prefix, const int32_t* seq_mask, int act_bf16,
+                            hipStream_t s);
+// plen[b] += n for every canvas (seq_mask null) or those with seq_mask[b] != 0 (gated like the passes)
+hipError_t launch_advance_prefix(int32_t* plen, int B, int n, const int32_t* seq_mask, hipStream_t s);
+// *flag = 1 if every v[0..n) is nonzero, else 0 (never gated, nor is launch_fill_i32)
+hipError_t launch_all_set(const int32_t* v, int n, int32_t* flag, hipStream_t s);
 // resid += MoE output (gated expert rows + shared row); with g, out = RMSNorm(resid) * g
 hipError_t launch_moe_combine_norm(float* resid, const float* y, const float* shared, const float* gates,
                                    const int32_t* inv_perm, int rows, int d, int k, const void* g, void* out,
@@ -128,6 +150,7 @@ struct SampArgs {
   uint32_t k0, k1, step;          // Philox key (seed) and step index
   int slices, v_per_slice;        // vocabulary split
   float* part;                    // [slices][rows][6] partial (m2, s, a, g2, y, w) as floats/ints
+  const int32_t* gate;            // launch gate (set by the launcher)
 };
 hipError_t launch_lmhead_sampler(const SampArgs& a, int act_bf16, hipStream_t s);
 // fused LM head tiles: rows x vocabulary entries per block step (bf16: 256 x 256 on 8 waves of 32
@@ -149,9 +172,10 @@ struct StepArgs {
   int32_t* steps_taken;           // incremented for canvases that stepped (or null)
   int32_t* done_out;              // set when all positions locked (adaptive), or null
   int stats_only;                 // merge and write stats; leave canvas / lock / counts alone
+  const int32_t* gate;            // launch gate (set by the launcher)
 };
 constexpr int STAT_FIELDS = 6;
-hipError_t launch_step_merge(const StepArgs& a, hipStream_t s);
+hipError_t launch_step_merge(StepArgs a, hipStream_t s);
 
 // entropy-bounded step over merged stats: one block per canvas (L <= 1024)
 struct EbArgs {
@@ -166,6 +190,7 @@ struct EbArgs {
   float gamma, stop_entropy;
   int has_prev, final_step, adaptive, vocab, vocab_log2;
   uint32_t k0, k1, step;
+  const int32_t* gate;            // launch gate (set by the launcher)
 };
 hipError_t launch_eb_select(EbArgs a, hipStream_t s);
 

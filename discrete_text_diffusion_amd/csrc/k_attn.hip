@@ -41,6 +41,7 @@ template <> DG_DEV void put_elem<float>(char* p, float v) { *reinterpret_cast<fl
 
 template <class T, int DH>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs p) {
+  if (gate_closed(p.gate)) return;
   using C = AttnCfg<T, DH>;
   extern __shared__ __align__(16) char lds[];
   char* lk = lds;
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs p) {
   const int g = id % p.Hkv;
   const int b = id / p.Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int P = p.pos0[b];
+  const int P = prefix_of(p.plen, b, p.max_prefix);
   const bool causal = p.seq_causal ? p.seq_causal[b] != 0 : p.causal != 0;
   const int np = p.is_global ? P : min(P, p.window);       // visible prefix slots
   const int nkeys = np + p.n;
@@ -274,6 +275,7 @@ DG_DEV void put4<bf16_t>(bf16_t* dst, f32x4_v v) {
 
 template <class T, int S>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p) {
+  if (gate_closed(p.gate)) return;
   const int64_t rows = (int64_t)p.B * p.n * p.Hq;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (row, head, d/4)
   const int dq = p.dh / 4;
@@ -315,7 +317,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p) {
 }
 
 template <class T, int S>
-static void launch_merge_s(const AttnArgs& a, int blocks, hipStream_t s) {
+static void launch_merge_s(AttnArgs a, int blocks, hipStream_t s) {
+  a.gate = launch_gate();
   if constexpr (S < MERGE_MAX) {
     if (a.splits > S) return launch_merge_s<T, S + 1>(a, blocks, s);
   }
@@ -323,7 +326,8 @@ static void launch_merge_s(const AttnArgs& a, int blocks, hipStream_t s) {
 }
 
 template <class T, int DH>
-static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
+static hipError_t launch_attn_t(AttnArgs a, hipStream_t s) {
+  a.gate = launch_gate();
   using C = AttnCfg<T, DH>;
   const int qtiles = (a.Hq / a.Hkv * a.n + 63) / 64;
   const int blocks = a.B * a.Hkv * qtiles * a.splits;

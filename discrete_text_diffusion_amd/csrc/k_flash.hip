@@ -57,6 +57,7 @@ struct FlashCfg {
 
 template <int DH, bool CAUSAL, int QPW, int NW>
 __global__ __launch_bounds__(NW * 64) void flash_kernel(AttnArgs p) {
+  if (gate_closed(p.gate)) return;
   using C = FlashCfg<DH, QPW, NW>;
   extern __shared__ __align__(16) char lds[];
   const int G = p.Hq / p.Hkv;
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(NW * 64) void flash_kernel(AttnArgs p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kg = lane >> 4, l16 = lane & 15;
 
-  const int P = p.pos0[b];
+  const int P = prefix_of(p.plen, b, p.max_prefix);
   const int np = p.is_global ? P : min(P, p.window);
   const int TP = (np + C::KEYS - 1) / C::KEYS, TC = (p.n + C::KEYS - 1) / C::KEYS;
   const int t_begin = split * p.tiles_per_split;
@@ -331,7 +332,8 @@ __global__ __launch_bounds__(NW * 64) void flash_kernel(AttnArgs p) {
 }
 
 template <int DH, bool CAUSAL>
-static hipError_t launch_flash_t(const AttnArgs& a, hipStream_t s) {
+static hipError_t launch_flash_t(AttnArgs a, hipStream_t s) {
+  a.gate = launch_gate();
   using C = FlashCfg<DH, FLASH_QPW, FLASH_WAVES>;
   const int QB = (a.Hq / a.Hkv * a.n + C::QROWS - 1) / C::QROWS;
   const int groups = a.B * a.Hkv * a.splits;

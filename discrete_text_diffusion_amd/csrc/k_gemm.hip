@@ -46,6 +46,7 @@ DG_DEV void paired_col(int r, int& u, int& half, int& c) {
 // blockIdx.y is the split-K part.
 template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI, int MAP, int NS = 0, int KPS = 1>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_dense_kernel(DenseArgs p) {
+  if (gate_closed(p.gate)) return;
   using G = TileFor<TA, TB, BM, BN, WM, WN, NS, KPS>;
   extern __shared__ __align__(16) char lds[];
   const int id = blockIdx.x, xcd = id & 7, local = id >> 3;
@@ -196,13 +197,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dense_kernel(DenseArgs p) {
 // in double and reduced to [0, 2 pi) before the single-precision sincos.  One entry per canvas row
 // and pair: [rows][dh/2].
 __global__ void rope_table_kernel(float2* tab, int rows, int rows_per_canvas, int half_dh, double log2_theta,
-                                  RopePos pos) {
+                                  const int32_t* plen, int max_prefix, int* status, const int32_t* gate) {
+  if (gate_closed(gate)) return;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)rows * half_dh) return;
   const int m = (int)(idx / half_dh), jj = (int)(idx - (int64_t)m * half_dh);
   const int b = m / rows_per_canvas, ii = m - b * rows_per_canvas;
+  // a prefix length outside [0, max_prefix] is a caller error: flagged once per canvas, clamped
+  if (ii == 0 && jj == 0 && status && (plen[b] < 0 || plen[b] > max_prefix)) atomicOr(status, 4);
   const double inv = exp2(-2.0 * jj / (2 * half_dh) * log2_theta);
-  const double ang = (double)(pos.pos0[b] + ii) * inv;
+  const double ang = (double)(prefix_of(plen, b, max_prefix) + ii) * inv;
   const double red = ang - 6.283185307179586 * floor(ang * 0.15915494309189535);
   float sn, cs;
   sincosf((float)red, &sn, &cs);
@@ -210,12 +214,10 @@ __global__ void rope_table_kernel(float2* tab, int rows, int rows_per_canvas, in
 }
 
 hipError_t launch_rope_table(float2* tab, int rows, int rows_per_canvas, int head_dim, double log2_theta,
-                             const int32_t* pos0, int B, hipStream_t s) {
-  RopePos pos;
-  for (int b = 0; b < B && b < MAX_BATCH; ++b) pos.pos0[b] = pos0[b];
+                             const int32_t* plen, int max_prefix, int* status, hipStream_t s) {
   const int64_t n = (int64_t)rows * (head_dim / 2);
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, tab, rows, rows_per_canvas,
-                     head_dim / 2, log2_theta, pos);
+                     head_dim / 2, log2_theta, plen, max_prefix, status, launch_gate());
   return hipGetLastError();
 }
 
@@ -324,6 +326,7 @@ constexpr int XG = 16;
 
 template <class TA, class TB, int BM, int BMS, int BN, int WM, int WN, int EPI, int NS = 0, int QNS = 6, int XCDR = 0>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_grouped_kernel(GroupedArgs p) {
+  if (gate_closed(p.gate)) return;
   using G = GroupTileFor<TA, TB, BM, BN, WM, WN, NS, QNS>;
   using GS = GroupTileFor<TA, TB, BMS, BN, WM, WN, NS, QNS>;
   extern __shared__ __align__(16) char lds[];
@@ -380,6 +383,7 @@ static hipError_t launch_dense_t(DenseArgs a, int n_eff, hipStream_t s) {
   if (a.ksplit < 1) a.ksplit = 1;
   if (a.K % (a.ksplit * G::KT * KPS)) return hipErrorInvalidValue;
   dim3 grid(a.n_mt * ((a.n_nt + 7) / 8 * 8), a.ksplit);
+  a.gate = launch_gate();
   static const hipError_t attr = allow_lds(gemm_dense_kernel<TA, TB, BM, BN, WM, WN, EPI, MAP, NS, KPS>, G::LDS_BYTES);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((gemm_dense_kernel<TA, TB, BM, BN, WM, WN, EPI, MAP, NS, KPS>), grid, dim3(WM * WN * 64),
@@ -469,6 +473,7 @@ static hipError_t launch_grouped_t(GroupedArgs a, int n_eff, int sh_eff, int max
   const int blocks = a.sh_blocks + (XCDR ? (units + 7) / 8 * 8 * XG : max_items * a.nt_r);
   if (blocks == 0) return hipSuccess;
   if (a.K % G::KT || (a.shB && a.shK % GS::KT)) return hipErrorInvalidValue;
+  a.gate = launch_gate();
   static const hipError_t attr = allow_lds(gemm_grouped_kernel<TA, TB, BM, BMS, BN, WM, WN, EPI, NS, QNS, XCDR>, LDS);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((gemm_grouped_kernel<TA, TB, BM, BMS, BN, WM, WN, EPI, NS, QNS, XCDR>), dim3(blocks), dim3(WM * WN * 64),

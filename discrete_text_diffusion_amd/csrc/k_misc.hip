@@ -6,8 +6,17 @@
 
 namespace dg {
 
+// The host side of the launch gate: one current gate per host thread.
+namespace {
+thread_local const int32_t* t_gate = nullptr;
+}
+const int32_t* launch_gate() { return t_gate; }
+GateScope::GateScope(const int32_t* gate) : prev(t_gate) { t_gate = gate; }
+GateScope::~GateScope() { t_gate = prev; }
+
 template <class T>
-__global__ void embed_kernel(const int32_t* tok, const T* E, float* resid, int d, int V) {
+__global__ void embed_kernel(const int32_t* tok, const T* E, float* resid, int d, int V, const int32_t* gate) {
+  if (gate_closed(gate)) return;
   const int r = blockIdx.x;
   const int t = min(max(tok[r], 0), V - 1);     // out-of-range ids are clamped, never read past E
   const T* src = E + (int64_t)t * d;
@@ -16,18 +25,23 @@ __global__ void embed_kernel(const int32_t* tok, const T* E, float* resid, int d
 
 hipError_t launch_embed(const int32_t* tok, const void* E, float* resid, int rows, int d, int V, int bf,
                         hipStream_t s) {
-  if (bf) hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(rows), dim3(256), 0, s, tok, (const bf16_t*)E, resid, d, V);
-  else hipLaunchKernelGGL(embed_kernel<float>, dim3(rows), dim3(256), 0, s, tok, (const float*)E, resid, d, V);
+  if (bf)
+    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(rows), dim3(256), 0, s, tok, (const bf16_t*)E, resid, d, V,
+                       launch_gate());
+  else
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(rows), dim3(256), 0, s, tok, (const float*)E, resid, d, V,
+                       launch_gate());
   return hipGetLastError();
 }
 
-__global__ void copy_f32_kernel(const float* a, float* b, int64_t n) {
+__global__ void copy_f32_kernel(const float* a, float* b, int64_t n, const int32_t* gate) {
+  if (gate_closed(gate)) return;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) b[i] = a[i];
 }
 
 hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s) {
-  hipLaunchKernelGGL(copy_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, dst, n);
+  hipLaunchKernelGGL(copy_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, dst, n, launch_gate());
   return hipGetLastError();
 }
 
@@ -89,7 +103,9 @@ DG_DEV f32x4_v load4<bf16_t>(const bf16_t* src) {
 // NP = number of partials, a compile-time constant so the loads stay in registers
 template <class T, int NP>
 __global__ __launch_bounds__(1024) void resid_add_rmsnorm_kernel(float* resid, const float* parts, int64_t pstride,
-                                                                 const T* g, T* y, int d, float eps, int* status) {
+                                                                 const T* g, T* y, int d, float eps, int* status,
+                                                                 const int32_t* gate) {
+  if (gate_closed(gate)) return;
   __shared__ float red[16];
   const int r = blockIdx.x;
   const int c = threadIdx.x * 4;
@@ -117,7 +133,7 @@ static void launch_ran(dim3 grid, dim3 block, hipStream_t s, float* resid, const
     if (nparts > NP) return launch_ran<T, NP + 1>(grid, block, s, resid, parts, nparts, pstride, g, y, d, eps, status);
   }
   hipLaunchKernelGGL((resid_add_rmsnorm_kernel<T, NP>), grid, block, 0, s, resid, parts, pstride, (const T*)g, (T*)y,
-                     d, eps, status);
+                     d, eps, status, launch_gate());
 }
 
 hipError_t launch_resid_add_rmsnorm(float* resid, const float* parts, int nparts, int64_t pstride, const void* g,
@@ -138,10 +154,13 @@ struct AppendArgs {
   const char* kn; const char* vn; char* kc; char* vc;
   const int32_t* mask;    // device [B] or null: canvases with mask[b] == 0 are not appended
   int B, n, vn_ld, Hkv, esz, row_bytes, cap, window, is_global;
-  int32_t pos0[MAX_BATCH];
+  const int32_t* plen;    // device [B] prefix lengths (first position of the new rows)
+  int max_prefix;
+  const int32_t* gate;
 };
 
 __global__ void kv_append_kernel(AppendArgs a) {
+  if (gate_closed(a.gate)) return;
   // keys: one 16-byte chunk of a key row per thread
   const int chunks = a.row_bytes / 16;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -154,7 +173,7 @@ __global__ void kv_append_kernel(AppendArgs a) {
     const int b = (int)(t / a.Hkv);
     if (!a.is_global && j < a.n - a.window) return;
     if (a.mask && a.mask[b] == 0) return;
-    const int pos = a.pos0[b] + j;
+    const int pos = prefix_of(a.plen, b, a.max_prefix) + j;
     const int slot = a.is_global ? pos : pos % a.window;
     const int64_t src = (((int64_t)b * a.Hkv + g) * a.n + j) * a.row_bytes + ch * 16;
     const int64_t dst = (((int64_t)b * a.Hkv + g) * a.cap + slot) * a.row_bytes + ch * 16;
@@ -170,7 +189,7 @@ __global__ void kv_append_kernel(AppendArgs a) {
   const int b = (int)(row / ((int64_t)a.Hkv * dh));
   if (!a.is_global && j < a.n - a.window) return;
   if (a.mask && a.mask[b] == 0) return;
-  const int pos = a.pos0[b] + j;
+  const int pos = prefix_of(a.plen, b, a.max_prefix) + j;
   const int slot = a.is_global ? pos : pos % a.window;
   if (a.esz == 2)
     reinterpret_cast<uint16_t*>(a.vc)[row * a.cap + slot] = reinterpret_cast<const uint16_t*>(a.vn)[row * a.vn_ld + j];
@@ -179,14 +198,16 @@ __global__ void kv_append_kernel(AppendArgs a) {
 }
 
 hipError_t launch_kv_append(const void* kn, const void* vn, int vn_ld, void* kc, void* vc, int B, int n, int Hkv,
-                            int dh, int cap, int window, int is_global, const int32_t* pos0,
+                            int dh, int cap, int window, int is_global, const int32_t* plen, int max_prefix,
                             const int32_t* seq_mask, int bf, hipStream_t s) {
   AppendArgs a;
   a.kn = (const char*)kn; a.vn = (const char*)vn; a.kc = (char*)kc; a.vc = (char*)vc;
   a.mask = seq_mask;
   a.B = B; a.n = n; a.vn_ld = vn_ld; a.Hkv = Hkv; a.esz = bf ? 2 : 4; a.row_bytes = dh * a.esz; a.cap = cap; a.window = window;
   a.is_global = is_global;
-  for (int b = 0; b < B && b < MAX_BATCH; ++b) a.pos0[b] = pos0[b];
+  a.plen = plen;
+  a.max_prefix = max_prefix;
+  a.gate = launch_gate();
   const int64_t total = (int64_t)B * Hkv * n * (a.row_bytes / 16) + (int64_t)B * Hkv * dh * n;
   hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
@@ -201,7 +222,8 @@ template <int K, class T>
 __global__ __launch_bounds__(256) void moe_combine_norm_kernel(float* resid, const float* y, const float* shared,
                                                                const float* gates, const int32_t* inv_perm,
                                                                int rows, int d, int k, const T* g, T* out,
-                                                               float eps, int* status) {
+                                                               float eps, int* status, const int32_t* gate) {
+  if (gate_closed(gate)) return;
   const int t = blockIdx.x;
   float gv[K];
   int pos[K];
@@ -257,10 +279,10 @@ static void combine_k(int bf, float* resid, const float* y, const float* shared,
                       int* status, hipStream_t s) {
   if (bf)
     hipLaunchKernelGGL((moe_combine_norm_kernel<K, bf16_t>), dim3(rows), dim3(256), 0, s, resid, y, shared, gates,
-                       inv_perm, rows, d, k, (const bf16_t*)g, (bf16_t*)out, eps, status);
+                       inv_perm, rows, d, k, (const bf16_t*)g, (bf16_t*)out, eps, status, launch_gate());
   else
     hipLaunchKernelGGL((moe_combine_norm_kernel<K, float>), dim3(rows), dim3(256), 0, s, resid, y, shared, gates,
-                       inv_perm, rows, d, k, (const float*)g, (float*)out, eps, status);
+                       inv_perm, rows, d, k, (const float*)g, (float*)out, eps, status, launch_gate());
 }
 
 hipError_t launch_moe_combine_norm(float* resid, const float* y, const float* shared, const float* gates,
@@ -270,6 +292,30 @@ hipError_t launch_moe_combine_norm(float* resid, const float* y, const float* sh
   if (k <= 2) combine_k<2>(bf, resid, y, shared, gates, inv_perm, rows, d, k, g, out, eps, status, s);
   else if (k <= 8) combine_k<8>(bf, resid, y, shared, gates, inv_perm, rows, d, k, g, out, eps, status, s);
   else combine_k<16>(bf, resid, y, shared, gates, inv_perm, rows, d, k, g, out, eps, status, s);
+  return hipGetLastError();
+}
+
+__global__ void advance_prefix_kernel(int32_t* plen, int B, int n, const int32_t* mask, const int32_t* gate) {
+  if (gate_closed(gate)) return;
+  const int b = threadIdx.x;
+  if (b < B && (!mask || mask[b] != 0)) plen[b] += n;
+}
+
+hipError_t launch_advance_prefix(int32_t* plen, int B, int n, const int32_t* seq_mask, hipStream_t s) {
+  if (B > 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(advance_prefix_kernel, dim3(1), dim3(1024), 0, s, plen, B, n, seq_mask, launch_gate());
+  return hipGetLastError();
+}
+
+__global__ void all_set_kernel(const int32_t* v, int n, int32_t* flag) {
+  int all = 1;
+  for (int i = threadIdx.x; i < n; i += 64) all &= v[i] != 0;
+  for (int o = 32; o > 0; o >>= 1) all &= __shfl_xor(all, o, 64);
+  if (threadIdx.x == 0) *flag = all;
+}
+
+hipError_t launch_all_set(const int32_t* v, int n, int32_t* flag, hipStream_t s) {
+  hipLaunchKernelGGL(all_set_kernel, dim3(1), dim3(64), 0, s, v, n, flag);
   return hipGetLastError();
 }
 

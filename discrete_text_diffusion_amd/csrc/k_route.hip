@@ -65,7 +65,8 @@ DG_DEV uint64_t wave_max_key(uint64_t k) {
 template <int K>
 __global__ __launch_bounds__(64) void router_topk_kernel(const float* parts, int nparts, int64_t part_stride,
                                                          const float* bias, int T, int E, int k, float* logits_out,
-                                                         int32_t* idx, float* gates) {
+                                                         int32_t* idx, float* gates, const int32_t* gate) {
+  if (gate_closed(gate)) return;
   const int lane = threadIdx.x;
   const int t = blockIdx.x;
   const int e0 = 4 * lane;
@@ -124,11 +125,11 @@ hipError_t launch_router_topk(const float* parts, int nparts, int64_t part_strid
   if (T == 0) return hipSuccess;
   const dim3 grid(T);
   if (k <= 2)
-    hipLaunchKernelGGL(router_topk_kernel<2>, grid, dim3(64), 0, s, parts, nparts, part_stride, bias, T, E, k, logits_out, idx, gates);
+    hipLaunchKernelGGL(router_topk_kernel<2>, grid, dim3(64), 0, s, parts, nparts, part_stride, bias, T, E, k, logits_out, idx, gates, launch_gate());
   else if (k <= 8)
-    hipLaunchKernelGGL(router_topk_kernel<8>, grid, dim3(64), 0, s, parts, nparts, part_stride, bias, T, E, k, logits_out, idx, gates);
+    hipLaunchKernelGGL(router_topk_kernel<8>, grid, dim3(64), 0, s, parts, nparts, part_stride, bias, T, E, k, logits_out, idx, gates, launch_gate());
   else
-    hipLaunchKernelGGL(router_topk_kernel<16>, grid, dim3(64), 0, s, parts, nparts, part_stride, bias, T, E, k, logits_out, idx, gates);
+    hipLaunchKernelGGL(router_topk_kernel<16>, grid, dim3(64), 0, s, parts, nparts, part_stride, bias, T, E, k, logits_out, idx, gates, launch_gate());
   return hipGetLastError();
 }
 
@@ -167,7 +168,8 @@ template <int K, bool STAGED>
 __global__ __launch_bounds__(256) void route_place_kernel(const int32_t* idx_g, int T, int E, int k, int32_t* counts,
                                                           int bm, int32_t* offsets, int32_t* work,
                                                           int32_t* n_items, int32_t* perm, int32_t* inv_perm,
-                                                          int32_t* tok) {
+                                                          int32_t* tok, const int32_t* gate) {
+  if (gate_closed(gate)) return;
   const int e = blockIdx.x;
   __shared__ int red[4];
   __shared__ int wsum[4];
@@ -235,10 +237,10 @@ static hipError_t launch_place(const int32_t* idx, int T, int E, int k, int32_t*
     static const hipError_t attr = allow_lds(route_place_kernel<K, true>, ROUTE_STAGE_MAX * 4);
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((route_place_kernel<K, true>), dim3(E), dim3(256), (size_t)T * k * 4, s, idx, T, E, k, counts,
-                       bm, offsets, work, n_items, perm, inv_perm, tok);
+                       bm, offsets, work, n_items, perm, inv_perm, tok, launch_gate());
   } else {
     hipLaunchKernelGGL((route_place_kernel<K, false>), dim3(E), dim3(256), 0, s, idx, T, E, k, counts, bm, offsets,
-                       work, n_items, perm, inv_perm, tok);
+                       work, n_items, perm, inv_perm, tok, launch_gate());
   }
   return hipGetLastError();
 }

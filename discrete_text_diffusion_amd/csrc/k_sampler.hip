@@ -81,6 +81,7 @@ DG_DEV float gumbel_key2(float z2, uint32_t w) { return gumbel_key2_nc(z2, w) + 
 // accumulators); the WN states of a row are merged in wave order at the end.
 template <class TA, int BM, int BN, int WM, int WN, int NS>
 __global__ __launch_bounds__(WM * WN * 64) void lmhead_sampler_kernel(SampArgs p, int n_mt) {
+  if (gate_closed(p.gate)) return;
   using G = GemmDma<TA, BM, BN, WM, WN, NS>;
   constexpr int NW = WM * WN;
   extern __shared__ __align__(16) char lds[];
@@ -236,8 +237,9 @@ __global__ __launch_bounds__(WM * WN * 64) void lmhead_sampler_kernel(SampArgs p
 }
 
 template <class TA, int BM, int BN, int WM, int WN, int NS>
-static hipError_t launch_sampler_t(const SampArgs& a, hipStream_t s) {
+static hipError_t launch_sampler_t(SampArgs a, hipStream_t s) {
   using G = GemmDma<TA, BM, BN, WM, WN, NS>;
+  a.gate = launch_gate();
   const int n_mt = (a.rows + BM - 1) / BM;
   const int blocks = n_mt * ((a.slices + 7) / 8 * 8);
   const size_t lds = G::LDS_BYTES + (size_t)WN * BM * PART * 4;
@@ -307,6 +309,7 @@ hipError_t launch_logits_partials(const float* z, int rows, int V, int L, float 
 // One wave per position: lane j merges slices j, j+64, ... in ascending order, then a fixed xor
 // tree combines the lanes (deterministic).  Lane 0 applies the Step to the position.
 __global__ __launch_bounds__(256) void step_merge_kernel(StepArgs p) {
+  if (gate_closed(p.gate)) return;
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int rows = p.B * p.L;
@@ -364,6 +367,7 @@ __global__ __launch_bounds__(256) void step_merge_kernel(StepArgs p) {
 // One block per canvas: locked count (-1 if a non-finite statistic was seen in the canvas),
 // steps taken and the done flag of the adaptive loop.
 __global__ __launch_bounds__(256) void step_count_kernel(StepArgs p) {
+  if (gate_closed(p.gate)) return;
   const int b = blockIdx.x;
   const int rows = p.B * p.L;
   int nl = 0, nb = 0;
@@ -388,7 +392,8 @@ __global__ __launch_bounds__(256) void step_count_kernel(StepArgs p) {
   }
 }
 
-hipError_t launch_step_merge(const StepArgs& a, hipStream_t s) {
+hipError_t launch_step_merge(StepArgs a, hipStream_t s) {
+  a.gate = launch_gate();
   const int rows = a.B * a.L;
   hipLaunchKernelGGL(step_merge_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, a);
   if (!a.stats_only) hipLaunchKernelGGL(step_count_kernel, dim3(a.B), dim3(256), 0, s, a);
@@ -410,7 +415,7 @@ __global__ __launch_bounds__(EB_MAX_L) void eb_select_kernel(EbArgs p) {
   __shared__ int sh_k, sh_unstable;
   __shared__ float sh_mean;
   const int b = blockIdx.x, i = threadIdx.x, NT = blockDim.x;
-  if (p.done[b]) return;                              // the whole block leaves together
+  if (gate_closed(p.gate) || p.done[b]) return;                              // the whole block leaves together
   const int r = b * p.L + i;
   float H = 0.f;
   int a = 0, y = 0;
@@ -478,6 +483,7 @@ hipError_t launch_eb_select(EbArgs a, hipStream_t s) {
   int nt = 64;
   while (nt < a.L) nt <<= 1;
   a.vocab_log2 = log2_exact(a.vocab);
+  a.gate = launch_gate();
   hipLaunchKernelGGL(eb_select_kernel, dim3(a.B), dim3(nt), 0, s, a);
   return hipGetLastError();
 }

@@ -99,7 +99,7 @@ struct Layout {
   size_t status, stats, rlogits, idx, gates;
   size_t resid, xhat, rope, q, kn, vn, attn_o, part_o, part_ml, rparts, o_parts, sh_parts;
   size_t counts, offsets, perm, inv_perm, tok, work, n_items;
-  size_t a_grp, y, sh_a, samp_part, hidden, done, n_locked, prev, lockbuf;
+  size_t a_grp, y, sh_a, samp_part, hidden, done, n_locked, prev, lockbuf, all_done;
   size_t total;
   int max_items;
 };
@@ -147,6 +147,7 @@ Layout layout(const dg_model_desc& d, int B, int n, int max_prefix) {
   w.n_locked = take(B * 4);
   w.prev = take(R * 4);
   w.lockbuf = take(R);
+  w.all_done = take(4);
   w.total = o;
   return w;
 }
@@ -166,11 +167,9 @@ dg_status check_kv(const dg_ctx* c, const dg_kv* kv, int extra_tokens, int* max_
   const dg_model_desc& d = c->d;
   if (!kv || !kv->k || !kv->v || !kv->cap || !kv->prefix_len) return fail(DG_EINVAL, "kv: NULL field");
   if (kv->batch < 1 || kv->batch > MAX_BATCH) return fail(DG_EUNSUPPORTED, "batch %d not in [1, %d]", kv->batch, MAX_BATCH);
-  int mp = 0;
-  for (int b = 0; b < kv->batch; ++b) {
-    if (kv->prefix_len[b] < 0) return fail(DG_EINVAL, "prefix_len[%d] < 0", b);
-    mp = kv->prefix_len[b] > mp ? kv->prefix_len[b] : mp;
-  }
+  // the prefix lengths themselves live on the device: caches are validated against their host bound
+  const int mp = kv->max_prefix;
+  if (mp < 0) return fail(DG_EINVAL, "max_prefix %d < 0", mp);
   for (int l = 0; l < d.n_layers; ++l) {
     if (!kv->k[l] || !kv->v[l]) return fail(DG_EINVAL, "kv layer %d: NULL cache", l);
     if (kv->cap[l] % 8) return fail(DG_EUNSUPPORTED, "kv layer %d: cap %d not a multiple of 8", l, kv->cap[l]);
@@ -341,13 +340,13 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn, bool xhat_ready, const vo
   aa.causal = P.causal; aa.window = d.window > 0 ? d.window : 1; aa.is_global = glob;
   aa.seq_causal = P.seq_causal;
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
-  int maxkeys = 0, maxtiles = 0;
-  for (int b = 0; b < P.B; ++b) {
-    aa.pos0[b] = P.kv->prefix_len[b];
-    const int np = glob ? aa.pos0[b] : std::min(aa.pos0[b], d.window);
-    maxkeys = std::max(maxkeys, np + P.n);
-    maxtiles = std::max(maxtiles, (np + 63) / 64 + (P.n + 63) / 64);
-  }
+  aa.plen = P.kv->prefix_len;
+  aa.max_prefix = P.kv->max_prefix;
+  // grids are sized for the host bound on the prefixes; a split past a canvas's own key tiles
+  // writes an empty partial (m = -inf, l = 0) that the merge skips
+  const int np_max = glob ? aa.max_prefix : std::min(aa.max_prefix, d.window);
+  const int maxkeys = np_max + P.n;
+  const int maxtiles = (np_max + 63) / 64 + (P.n + 63) / 64;
   if (bf) {
     aa.splits = flash_splits(d, P.B, P.n, maxtiles);
     aa.tiles_per_split = (maxtiles + aa.splits - 1) / aa.splits;
@@ -366,8 +365,8 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn, bool xhat_ready, const vo
   }
   if (P.causal || P.seq_causal) {
     HIPCHK(launch_kv_append(at<void>(ws, w.kn), at<void>(ws, w.vn), aa.vn_ld, P.kv->k[l], P.kv->v[l], P.B, P.n,
-                            d.n_kv_heads, d.head_dim, P.kv->cap[l], d.window, glob, aa.pos0, P.seq_causal, bf,
-                            P.s));
+                            d.n_kv_heads, d.head_dim, P.kv->cap[l], d.window, glob, aa.plen, aa.max_prefix,
+                            P.seq_causal, bf, P.s));
   }
   // O projection as split-K partials; the fused kernel adds them to the residual (in part order)
   // and applies the FFN RMSNorm
@@ -676,6 +675,7 @@ dg_status dg_query_status(const dg_ctx* ctx, const void* ws, hipStream_t stream)
   HIPCHK(hipStreamSynchronize(stream));
   int v = 0;
   HIPCHK(hipMemcpy(&v, ws, sizeof v, hipMemcpyDeviceToHost));
+  if (v & 4) return fail(DG_EINVAL, "a device prefix_len was outside [0, max_prefix] (code %d)", v);
   return v ? fail(DG_ENONFINITE, "non-finite value flagged (code %d)", v) : DG_OK;
 }
 
@@ -700,7 +700,7 @@ dg_status dg_prefill_kv(dg_ctx* ctx, const dg_kv* kv, const int32_t* tokens, int
   HIPCHK(launch_embed(tokens, ctx->embed, at<float>(ws, P.w.resid), P.B * n, d.d_model, d.vocab,
                       d.act_dtype == DG_BF16, stream));
   HIPCHK(launch_rope_table(at<float2>(ws, P.w.rope), P.B * n, n, d.head_dim, std::log2((double)d.rope_theta),
-                           kv->prefix_len, P.B, stream));
+                           kv->prefix_len, kv->max_prefix, at<int>(ws, P.w.status), stream));
   for (int l = 0; l < d.n_layers; ++l) {
     // the last layer's FFN feeds no cache; each combine writes the next layer's normalised rows
     const bool more = l + 1 < d.n_layers;
@@ -708,6 +708,7 @@ dg_status dg_prefill_kv(dg_ctx* ctx, const dg_kv* kv, const int32_t* tokens, int
                         at<void>(ws, P.w.xhat))) != DG_OK)
       return st;
   }
+  HIPCHK(launch_advance_prefix(kv->prefix_len, P.B, n, nullptr, stream));
   return DG_OK;
 }
 
@@ -732,7 +733,7 @@ dg_status dg_denoise_step(dg_ctx* ctx, const dg_kv* kv, const int32_t* canvas, c
   if (resid_in) HIPCHK(launch_copy_f32(resid_in, at<float>(ws, P.w.resid), (int64_t)R * d.d_model, stream));
   else HIPCHK(launch_embed(canvas, ctx->embed, at<float>(ws, P.w.resid), R, d.d_model, d.vocab, bf, stream));
   HIPCHK(launch_rope_table(at<float2>(ws, P.w.rope), R, L, d.head_dim, std::log2((double)d.rope_theta),
-                           kv->prefix_len, P.B, stream));
+                           kv->prefix_len, kv->max_prefix, at<int>(ws, P.w.status), stream));
   // each layer's combine writes the next layer's normalised rows, the last one the final norm
   for (int l = layer_begin; l < layer_end; ++l) {
     const bool last = l + 1 == layer_end;
@@ -764,13 +765,14 @@ dg_status dg_mixed_forward(dg_ctx* ctx, const dg_kv* kv, const int32_t* tokens, 
   HIPCHK(launch_embed(tokens, ctx->embed, at<float>(ws, P.w.resid), R, d.d_model, d.vocab, d.act_dtype == DG_BF16,
                       stream));
   HIPCHK(launch_rope_table(at<float2>(ws, P.w.rope), R, L, d.head_dim, std::log2((double)d.rope_theta),
-                           kv->prefix_len, P.B, stream));
+                           kv->prefix_len, kv->max_prefix, at<int>(ws, P.w.status), stream));
   for (int l = 0; l < d.n_layers; ++l) {
     const bool last = l + 1 == d.n_layers;
     if ((st = run_layer(P, l, true, l > 0, last ? ctx->final_norm : ctx->layers[l + 1].attn_norm,
                         last ? hidden_out : at<void>(ws, P.w.xhat))) != DG_OK)
       return st;
   }
+  HIPCHK(launch_advance_prefix(kv->prefix_len, P.B, L, append, stream));
   return DG_OK;
 }
 
@@ -807,10 +809,15 @@ dg_status eb_run(dg_ctx* ctx, const dg_kv* kv, int32_t* canvas, uint8_t* lock, i
   const Layout w = layout(ctx->d, kv->batch, L, mp);
   const int B = kv->batch;
   int32_t* done = at<int32_t>(ws, w.done);
+  int32_t* all_done = at<int32_t>(ws, w.all_done);
   HIPCHK(launch_fill_i32(done, 0, B, stream));
+  HIPCHK(launch_fill_i32(all_done, 0, 1, stream));
   if (steps_taken) HIPCHK(launch_fill_i32(steps_taken, 0, B, stream));
   if (p->init_canvas) HIPCHK(launch_init_canvas(canvas, lock, B, L, ctx->d.vocab, key0(p->seed), key1(p->seed), stream));
   const double h = 1.0 / p->max_steps;
+  // every pass is enqueued up front; once all canvases have stopped, the gate turns the remaining
+  // passes' kernels away at entry (adaptive mode)
+  GateScope gate(p->adaptive ? all_done : nullptr);
   for (int s = 0; s < p->max_steps; ++s) {
     if ((st = dg_denoise_step(ctx, kv, canvas, nullptr, L, 0, ctx->d.n_layers, at<void>(ws, w.hidden), nullptr, ws,
                               ws_bytes, stream)) != DG_OK)
@@ -822,6 +829,7 @@ dg_status eb_run(dg_ctx* ctx, const dg_kv* kv, int32_t* canvas, uint8_t* lock, i
     if ((st = eb_into(ctx, at<void>(ws, w.hidden), false, canvas, at<int32_t>(ws, w.prev), done, nullptr, nullptr,
                       B, L, &ep, ws, w, steps_taken, stream)) != DG_OK)
       return st;
+    if (p->adaptive) HIPCHK(launch_all_set(done, B, all_done, stream));
   }
   return DG_OK;
 }
@@ -864,10 +872,15 @@ dg_status dg_canvas_run(dg_ctx* ctx, const dg_kv* kv, int32_t* canvas, uint8_t* 
   const Layout w = layout(ctx->d, kv->batch, L, mp);
   const int B = kv->batch;
   int32_t* done = at<int32_t>(ws, w.done);
+  int32_t* all_done = at<int32_t>(ws, w.all_done);
   HIPCHK(launch_fill_i32(done, 0, B, stream));
+  HIPCHK(launch_fill_i32(all_done, 0, 1, stream));
   if (steps_taken) HIPCHK(launch_fill_i32(steps_taken, 0, B, stream));
   if (p->init_canvas) HIPCHK(launch_init_canvas(canvas, lock, B, L, ctx->d.vocab, key0(p->seed), key1(p->seed), stream));
   const double h = 1.0 / p->max_steps;
+  // every pass is enqueued up front (no host read of `done`); once all canvases have locked every
+  // position, the gate turns the remaining passes' kernels away at entry (adaptive mode)
+  GateScope gate(p->adaptive ? all_done : nullptr);
   for (int s = 0; s < p->max_steps; ++s) {
     if ((st = dg_denoise_step(ctx, kv, canvas, nullptr, L, 0, ctx->d.n_layers, at<void>(ws, w.hidden), nullptr, ws,
                               ws_bytes, stream)) != DG_OK)
@@ -881,6 +894,7 @@ dg_status dg_canvas_run(dg_ctx* ctx, const dg_kv* kv, int32_t* canvas, uint8_t* 
                           p->adaptive ? done : nullptr, B, L, &sp, jump_prob(p->schedule, t, h), ws, w, steps_taken,
                           p->adaptive ? done : nullptr, stream)) != DG_OK)
       return st;
+    if (p->adaptive) HIPCHK(launch_all_set(done, B, all_done, stream));
   }
   return DG_OK;
 }
@@ -894,11 +908,8 @@ dg_status dg_generate(dg_ctx* ctx, const dg_kv* kv, int32_t* out, int32_t* steps
   const int B = kv->batch;
   if (B < 1 || B > MAX_BATCH) return fail(DG_EUNSUPPORTED, "batch %d not in [1, %d]", B, MAX_BATCH);
   // room for the appended canvases: checked up front so nothing is enqueued on failure
-  std::vector<int32_t> plen(kv->prefix_len, kv->prefix_len + B);
   dg_kv last = *kv;
-  std::vector<int32_t> end(B);
-  for (int b = 0; b < B; ++b) end[b] = plen[b] + (K - 1) * L;
-  last.prefix_len = end.data();
+  last.max_prefix = kv->max_prefix + (K - 1) * L;
   int mp = 0;
   dg_status st = check_kv(ctx, &last, 0, &mp);
   if (st != DG_OK) return st;
@@ -906,8 +917,9 @@ dg_status dg_generate(dg_ctx* ctx, const dg_kv* kv, int32_t* out, int32_t* steps
   const Layout w = layout(ctx->d, B, L, mp);
   uint8_t* lock = at<uint8_t>(ws, w.lockbuf);
   for (int k = 0; k < K; ++k) {
+    // the device prefix lengths grow by L per appended canvas; the host bound follows
     dg_kv cur = *kv;
-    cur.prefix_len = plen.data();
+    cur.max_prefix = kv->max_prefix + k * L;
     dg_run_params p = *params;
     p.seed = params->seed + (uint64_t)k;
     p.init_canvas = 1;
@@ -915,10 +927,7 @@ dg_status dg_generate(dg_ctx* ctx, const dg_kv* kv, int32_t* out, int32_t* steps
     if ((st = dg_canvas_run(ctx, &cur, canvas, lock, steps ? steps + (size_t)k * B : nullptr, L, &p, ws, ws_bytes,
                             stream)) != DG_OK)
       return st;
-    if (k + 1 < K) {
-      if ((st = dg_prefill_kv(ctx, &cur, canvas, L, ws, ws_bytes, stream)) != DG_OK) return st;
-      for (int b = 0; b < B; ++b) plen[b] += L;
-    }
+    if (k + 1 < K && (st = dg_prefill_kv(ctx, &cur, canvas, L, ws, ws_bytes, stream)) != DG_OK) return st;
   }
   if (valid) HIPCHK(launch_valid_tokens(out, K, B, L, eos_id, valid, eos_seen, stream));
   return DG_OK;

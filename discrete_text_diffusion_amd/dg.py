@@ -44,7 +44,7 @@ class Weights(C.Structure):
 
 class KV(C.Structure):
     _fields_ = [("k", C.POINTER(C.c_void_p)), ("v", C.POINTER(C.c_void_p)), ("cap", C.POINTER(C.c_int32)),
-                ("prefix_len", C.POINTER(C.c_int32)), ("batch", C.c_int32)]
+                ("prefix_len", C.c_void_p), ("max_prefix", C.c_int32), ("batch", C.c_int32)]
 
 
 class StepParams(C.Structure):

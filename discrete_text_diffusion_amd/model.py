@@ -56,25 +56,41 @@ class Model:
         if kv is not None:
             self.set_kv(kv, prefix_len)
 
-    def set_kv(self, kv: list, prefix_len):
+    def set_kv(self, kv: list, prefix_len, max_prefix=None):
         """kv: per layer (K [B][Hkv][cap][dh], V [B][Hkv][dh][cap]) tensors (see values_dmajor);
-        prefix_len: ints [B]."""
+        prefix_len: ints [B] (copied to a device int32 tensor, `plen_dev`, which the library reads
+        and advances); max_prefix: the host bound passed with every call (default max(prefix_len))."""
         self._kv = kv
         n = self.cfg.n_layers
         self._kp = (C.c_void_p * n)(*[k.data_ptr() for k, _ in kv])
         self._vp = (C.c_void_p * n)(*[v.data_ptr() for _, v in kv])
         self._cap = (C.c_int32 * n)(*[k.shape[2] for k, _ in kv])
         self.batch = kv[0][0].shape[0]
-        self._plen = (C.c_int32 * self.batch)(*[int(p) for p in prefix_len])
-        self.kv_struct = dg.KV(k=self._kp, v=self._vp, cap=self._cap, prefix_len=self._plen, batch=self.batch)
+        plen = [int(p) for p in prefix_len]
+        self.plen_dev = torch.tensor(plen, dtype=torch.int32, device=kv[0][0].device)
+        self._plen_host = plen
+        bound = max(plen) if max_prefix is None else int(max_prefix)
+        self.kv_struct = dg.KV(k=self._kp, v=self._vp, cap=self._cap, prefix_len=self.plen_dev.data_ptr(),
+                               max_prefix=bound, batch=self.batch)
+
+    @property
+    def max_prefix(self):
+        return self.kv_struct.max_prefix
 
     @property
     def prefix_len(self):
-        return [self._plen[b] for b in range(self.batch)]
+        """Host copy of the prefix lengths; read back from the device (a synchronisation) after a
+        pass whose appends were decided there."""
+        if self._plen_host is None:
+            self._plen_host = [int(x) for x in self.plen_dev.cpu().tolist()]
+        return list(self._plen_host)
 
-    def advance_prefix(self, n):
-        for b in range(self.batch):
-            self._plen[b] += n
+    def _grew(self, n, known=True):
+        self.kv_struct.max_prefix += n
+        if known and self._plen_host is not None:
+            self._plen_host = [p + n for p in self._plen_host]
+        else:
+            self._plen_host = None
 
     def workspace(self, batch, rows_per_canvas, max_prefix=0, device="cuda"):
         nbytes = dg.dg_workspace_bytes(self.ctx, batch, rows_per_canvas, max_prefix)
@@ -87,7 +103,7 @@ class Model:
     # ---- calls -----------------------------------------------------------------------------
     def prefill_kv(self, tokens, ws, stream=None):
         dg.dg_prefill_kv(self.ctx, self.kv_struct, tokens, tokens.shape[1], ws, stream)
-        self.advance_prefix(tokens.shape[1])
+        self._grew(tokens.shape[1])
 
     def denoise_step(self, canvas, L, ws, hidden_out=None, resid_out=None, resid_in=None, layer_begin=0,
                      layer_end=None, stream=None):
@@ -97,15 +113,10 @@ class Model:
 
     def mixed_forward(self, tokens, append, hidden_out, ws, stream=None):
         """One pass over canvases of two kinds: append[b] != 0 (device int32 [B]) encodes canvas b
-        causally into the cache, the others take the bidirectional denoising pass.  The prefix
-        lengths here are not advanced (the flags stay on the device): call advance_rows for the
-        append canvases."""
+        causally into the cache (its device prefix length grows by L), the others take the
+        bidirectional denoising pass."""
         dg.dg_mixed_forward(self.ctx, self.kv_struct, tokens, append, tokens.shape[1], hidden_out, ws, stream)
-
-    def advance_rows(self, rows, n):
-        """Add n to the prefix length of each canvas in rows."""
-        for b in rows:
-            self._plen[b] += n
+        self._grew(tokens.shape[1], known=False)
 
     def step_sample(self, hidden, canvas, lock, n_locked, params: dg.StepParams, ws, done=None, stream=None):
         B, L = canvas.shape
@@ -119,7 +130,7 @@ class Model:
         covers the K - 1 appended canvases."""
         K, _, L = out.shape
         dg.dg_generate(self.ctx, self.kv_struct, out, steps, valid, eos_seen, K, L, eos_id, params, ws, stream)
-        self.advance_prefix((K - 1) * L)
+        self._grew((K - 1) * L)
 
     def close(self):
         if self.ctx:

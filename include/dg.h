@@ -16,7 +16,7 @@
  *
  * Conventions for every call:
  *   - Pointers named as device pointers must point to device memory allocated by the caller;
- *     descriptors, parameter structs, pointer tables and `cap`/`prefix_len` are host memory.
+ *     descriptors, parameter structs, pointer tables and `cap` are host memory.
  *     Weight pointers must be 16-byte aligned (dg_create checks), as every allocator's are.
  *   - The library never allocates device memory.  All scratch lives in the caller's workspace
  *     (`ws`, at least dg_workspace_bytes() bytes, 256-byte aligned).  One workspace must not be
@@ -107,7 +107,10 @@ typedef struct {
   const dg_layer_weights *layers; /* host array [n_layers]                                    */
 } dg_weights;
 
-/* Prefix KV cache, filled by the causal encoder (dg_prefill_kv) or by the caller.
+/* Prefix KV cache, filled by the causal encoder (dg_prefill_kv) or by the caller.  The prefix
+ * lengths live on the device, so a loop on the device can advance them without a host read
+ * ([TR §CPU-GPU 동기화 제거]); the host passes only an upper bound, used to size the grids and to
+ * check the caches' capacity before anything is enqueued.
  * k[l]: device [batch][Hkv][cap[l]][dh] act, keys stored after RoPE (slot-major rows).
  * v[l]: device [batch][Hkv][dh][cap[l]] act, values stored head-dim-major (one row of cap[l]
  * slots per head-dim index), so value tiles stream into the attention kernel's LDS as stored.
@@ -118,7 +121,12 @@ typedef struct {
   void *const *k;            /* host array [n_layers] of device pointers */
   void *const *v;
   const int32_t *cap;        /* host [n_layers] */
-  const int32_t *prefix_len; /* host [batch]: tokens already encoded for each canvas */
+  int32_t *prefix_len;       /* device [batch], in/out: tokens already encoded for each canvas.
+                                dg_prefill_kv and the append canvases of dg_mixed_forward add the
+                                tokens they encode; every other call only reads it. */
+  int32_t max_prefix;        /* host: an upper bound on every prefix_len[b] when the call starts.
+                                A device value outside [0, max_prefix] is clamped into it and
+                                flagged: dg_query_status then returns DG_EINVAL. */
   int32_t batch;
 } dg_kv;
 
@@ -191,11 +199,15 @@ dg_status dg_clear_status(const dg_ctx *ctx, void *ws, hipStream_t stream);
 /* Causal encoder pass ("context encoding" and "append after encode", [TR §아키텍처와 블록
  * 자기회귀 생성]): tokens [batch][n] (device int32) at positions prefix_len[b] .. + n - 1 attend
  * causally (window on local layers) to the cache and to each other; their post-RoPE keys and
- * values are written into every layer's cache.  The caller then adds n to prefix_len[b]. */
+ * values are written into every layer's cache, and n is added to prefix_len[b] on the device.
+ * Global-layer caches need cap >= max_prefix + n. */
 dg_status dg_prefill_kv(dg_ctx *ctx, const dg_kv *kv, const int32_t *tokens, int32_t n,
                         void *ws, size_t ws_bytes, hipStream_t stream);
 
-/* Decoder pass over the canvases: bidirectional attention of every canvas position over the
+/* Decoder pass over the canvases ([TR §아키텍처와 블록 자기회귀 생성]: the decoder refines the
+ * canvas with bidirectional attention over the encoder's KV cache, no causal mask inside the canvas;
+ * [CA §스펙 정리]: sliding window 1024 on local layers, 8 of 128 routed experts plus one always-on
+ * shared expert): bidirectional attention of every canvas position over the
  * visible prefix (all of it on global layers, the last `window` positions on local layers)
  * plus the whole canvas, then the MoE FFN with the shared expert; layers
  * [layer_begin, layer_end).  Input: canvas tokens (device int32 [batch][L], embedded by row
@@ -213,12 +225,12 @@ dg_status dg_denoise_step(dg_ctx *ctx, const dg_kv *kv, const int32_t *canvas,
  * no host synchronisation).  tokens: device int32 [batch][L]; append: device int32 [batch], read
  * only by the kernels.  Canvas b with append[b] != 0 takes the dg_prefill_kv pass: causal
  * attention to the cache and to itself, its keys and values written at positions prefix_len[b]
- * .. + L - 1 of every layer's cache (the caller then adds L to prefix_len[b]).  Canvas b with
+ * .. + L - 1 of every layer's cache, and L added to prefix_len[b] on the device.  Canvas b with
  * append[b] == 0 takes the dg_denoise_step pass: bidirectional attention over its prefix and
  * canvas, its cache untouched.  Every row then runs the MoE FFN of every layer; hidden_out
  * [batch*L][d] act = RMSNorm(residual) * final_norm for all rows (for an append canvas, the causal
  * encoder's output).  Pass `append` as dg_step_sample's `done` to step only the denoising
- * canvases.  The global-layer caches need room for L more positions on every canvas. */
+ * canvases.  The global-layer caches need cap >= max_prefix + L. */
 dg_status dg_mixed_forward(dg_ctx *ctx, const dg_kv *kv, const int32_t *tokens,
                            const int32_t *append, int32_t L, void *hidden_out, void *ws,
                            size_t ws_bytes, hipStream_t stream);
@@ -247,6 +259,10 @@ dg_status dg_step_entropy_bounded(dg_ctx *ctx, const void *hidden, int32_t *canv
 
 /* The denoising loop for one block [TR §디노이징 반복과 self-conditioning]: optional uniform
  * canvas at t = 1, then up to max_steps of dg_denoise_step + the sampler's step at t_s = 1 - s/T.
+ * All max_steps passes are enqueued at once with no host synchronisation ([TR §CPU-GPU 동기화
+ * 제거]); with `adaptive`, once every canvas has stopped ([TR §DiffusionGemma 샘플러, adaptive
+ * stopping]) each kernel of the remaining passes returns at entry, so a batch that stops early
+ * costs only the launches of the passes it skips.
  * DG_SAMPLER_EULER: dg_step_sample; with `adaptive`, a canvas whose positions are all locked is
  * left unchanged by later steps.  DG_SAMPLER_ENTROPY_BOUNDED: dg_step_entropy_bounded with
  * tau_start = tau and the given tau_end, gamma, stop_entropy; `lock` may be NULL.
@@ -259,12 +275,12 @@ dg_status dg_canvas_run(dg_ctx *ctx, const dg_kv *kv, int32_t *canvas, uint8_t *
  * encoded the prompt with dg_prefill_kv (kv->prefix_len = prompt lengths): K canvases of L tokens;
  * canvas k is denoised by dg_canvas_run with `params` (random streams of seed + k, canvas drawn
  * uniform at t = 1) and, except the last, appended to the KV cache by the causal encoder at
- * positions prefix_len[b] + k L.  Every layer's cache must hold prefix_len[b] + (K - 1) L
- * positions (global layers).  out: device int32 [K][batch][L]; steps: device int32 [K][batch]
+ * positions prefix_len[b] .. (which then advance by L on the device).  Global-layer caches need
+ * cap >= max_prefix + (K - 1) L.  out: device int32 [K][batch][L]; steps: device int32 [K][batch]
  * (denoising steps of each canvas, may be NULL); valid: device int32 [K][batch] (tokens before the
  * sequence's first eos_id, L for a canvas without one, 0 after it; may be NULL); eos_seen: device
- * int32 [K][batch] (canvas holds an eos_id; may be NULL).  kv->prefix_len is not modified: the
- * caller adds (K - 1) L.  No host synchronisation; eos only decides which tokens count. */
+ * int32 [K][batch] (canvas holds an eos_id; may be NULL).  On return kv->prefix_len has grown by
+ * (K - 1) L.  No host synchronisation; eos only decides which tokens count. */
 dg_status dg_generate(dg_ctx *ctx, const dg_kv *kv, int32_t *out, int32_t *steps, int32_t *valid,
                       int32_t *eos_seen, int32_t K, int32_t L, int32_t eos_id, const dg_run_params *params,
                       void *ws, size_t ws_bytes, hipStream_t stream);

@@ -100,8 +100,7 @@ def test_validation_enqueues_nothing_on_bad_calls():
         n = cfg.n_layers
         kp = (C.c_void_p * n)(0x5000, 0x6000)
         cap = (C.c_int32 * n)(128, 128)
-        plen = (C.c_int32 * 1)(64)
-        kv = dg.KV(k=kp, v=kp, cap=cap, prefix_len=plen, batch=1)
+        kv = dg.KV(k=kp, v=kp, cap=cap, prefix_len=0x8000, max_prefix=64, batch=1)
         ws = _FakeTensor(0x10000000, need)
         canvas = _FakeTensor(0x7000, 128)
         # workspace too small

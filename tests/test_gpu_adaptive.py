@@ -1,0 +1,129 @@
+"""Adaptive stopping and device-side prefix lengths.
+
+[TR §DiffusionGemma 샘플러, adaptive stopping]: a canvas stops refining once it has settled; here
+(the Euler sampler with lock-in) once every position is locked.  [TR §CPU-GPU 동기화 제거]: the loop
+runs with no host synchronisation, so dg_canvas_run enqueues every pass up front and the kernels
+of the passes after the last canvas stops return at entry.
+
+  * low-temperature tiny fp32 runs where the canvases stop early and at different steps (and one
+    where a canvas runs to the cap): steps taken, locks and canvas equal to the oracle's loop
+  * a 6-layer bf16 model with the Gemma-like widths and the 262,144-token vocabulary, 48-step cap:
+    the adaptive run ends with the canvas and locks of the non-adaptive run and takes a fraction of
+    its time
+  * prefix lengths live on the device: the append canvases of a mixed pass advance them there, and
+    a device value beyond the host bound is clamped and flagged (DG_EINVAL from dg_query_status)
+"""
+import numpy as np
+import pytest
+import torch
+
+from discrete_text_diffusion_amd import dg
+from oracle import model as M
+from oracle import step as S
+from synth import configs, gen
+from tests.gpu_util import build, log
+from tests.helpers import oracle_kv_dev, oracle_weights
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _run(model, cfg, ws, adaptive, seed):
+    B, L = cfg.batch, cfg.canvas
+    cv = torch.empty(B, L, dtype=torch.int32, device=DEV)
+    lk = torch.empty(B, L, dtype=torch.uint8, device=DEV)
+    taken = torch.empty(B, dtype=torch.int32, device=DEV)
+    rp = dg.RunParams(schedule=cfg.schedule, max_steps=cfg.steps, tau=cfg.tau, lock_threshold=cfg.lock_threshold,
+                      seed=seed, adaptive=int(adaptive), init_canvas=1)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    model.canvas_run(cv, lk, taken, rp, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    return cv.cpu().numpy(), lk.cpu().numpy().astype(bool), taken.cpu().numpy(), e0.elapsed_time(e1)
+
+
+@pytest.mark.parametrize("tau,seed", [(0.015, 5), (0.02, 3)])
+def test_tiny_adaptive_run_stops_like_the_oracle(tau, seed):
+    """tau 0.015 / seed 5: every canvas stops early, each at its own step; tau 0.02 / seed 3: one
+    canvas never locks all its positions and runs to the cap."""
+    cfg = configs.C0.replace(batch=3, steps=8, adaptive=True, lock_threshold=0.9, tau=tau, kv_source="random")
+    model, W, kv = build(cfg)
+    ws = model.workspace(cfg.batch, cfg.canvas, cfg.prefix)
+    log(f"[adaptive tiny] tau {tau} seed {seed}")
+    cv, lk, taken, _ = _run(model, cfg, ws, True, seed)
+    OW = oracle_weights(W, cfg)
+    okv = oracle_kv_dev(kv)
+    plen = [cfg.prefix] * cfg.batch
+    fwd = lambda c: M.denoise_forward(cfg, OW, okv, plen, canvas=c)[0]
+    ocv, olk, otaken = S.canvas_run(cfg, OW, okv, plen, fwd, seed=seed)
+    log(f"  steps taken gpu {taken.tolist()} oracle {otaken.tolist()}; locked gpu {lk.sum(1).tolist()} "
+        f"oracle {olk.sum(1).tolist()}")
+    # the planted setting does what it is for: early stops at different steps
+    assert otaken.min() < cfg.steps and len(set(otaken.tolist())) > 1
+    assert taken.tolist() == otaken.tolist()
+    assert np.array_equal(lk, olk)
+    assert np.array_equal(cv, ocv)
+    # a stopped canvas stays a fixed point: the same loop without stopping ends identically
+    cv2, lk2, taken2, _ = _run(model, cfg, ws, False, seed)
+    assert np.array_equal(cv2, cv) and np.array_equal(lk2, lk)
+    assert taken2.tolist() == [cfg.steps] * cfg.batch
+
+
+def test_stopped_batch_skips_the_remaining_passes():
+    cfg = configs.C2.replace(n_layers=6, prefix=1024, tau=0.01, lock_threshold=0.9, steps=48, adaptive=True)
+    log(f"[adaptive gate] {cfg.n_layers} layers, V {cfg.vocab}, prefix {cfg.prefix}, cap {cfg.steps}")
+    model, W, kv = build(cfg)
+    ws = model.workspace(cfg.batch, cfg.canvas, cfg.prefix)
+    _run(model, cfg, ws, False, 7)                       # warm-up (first launches, LDS attributes)
+    cv_f, lk_f, taken_f, t_full = _run(model, cfg, ws, False, 7)
+    cv_a, lk_a, taken_a, t_adapt = _run(model, cfg, ws, True, 7)
+    per_step = t_full / cfg.steps
+    log(f"  full {t_full:.2f} ms ({per_step:.3f} ms/step); adaptive {t_adapt:.2f} ms, steps taken "
+        f"{taken_a.tolist()}, locked {lk_a.sum(1).tolist()} of {cfg.canvas}")
+    assert taken_f.tolist() == [cfg.steps] * cfg.batch
+    assert int(taken_a.max()) <= 6, "the planted temperature should lock every position within a few steps"
+    assert np.array_equal(cv_a, cv_f) and np.array_equal(lk_a, lk_f)
+    # the skipped passes cost their launches only: well under the time of the steps they replace
+    assert t_adapt < (int(taken_a.max()) + 0.25 * (cfg.steps - int(taken_a.max()))) * per_step
+    assert t_adapt < 0.35 * t_full
+
+
+def test_device_prefix_is_clamped_to_the_bound_and_flagged():
+    cfg = configs.C0.replace(kv_source="random")
+    model, W, kv = build(cfg)
+    B, L = cfg.batch, cfg.canvas
+    ws = model.workspace(B, L, cfg.prefix)
+    cv = torch.empty(B, L, dtype=torch.int32, device=DEV)
+    dg.dg_init_canvas(cv, None, B, L, cfg.vocab, cfg.seed)
+    H1 = torch.empty(B * L, cfg.d_model, dtype=torch.float32, device=DEV)
+    model.denoise_step(cv, L, ws, hidden_out=H1)
+    torch.cuda.synchronize()
+    assert dg.dg_query_status(model.ctx, ws) == dg.DG_OK
+    # a device prefix beyond the host bound: read as the bound, flagged in the status word
+    model.plen_dev.fill_(cfg.prefix + 1000)
+    H2 = torch.empty_like(H1)
+    model.denoise_step(cv, L, ws, hidden_out=H2)
+    torch.cuda.synchronize()
+    assert dg.dg_query_status(model.ctx, ws) == dg.DG_EINVAL
+    assert torch.equal(H1, H2)
+    dg.dg_clear_status(model.ctx, ws)
+    model.plen_dev.fill_(cfg.prefix)
+
+
+def test_mixed_pass_advances_the_append_canvases_on_the_device():
+    cfg = configs.C0.replace(n_layers=2, window=40, global_every=2, batch=3, canvas=16)
+    model, W, kv = build(cfg, kv_mode="empty")
+    B, L = cfg.batch, cfg.canvas
+    ws = model.workspace(B, L, 64)
+    plen = [40, 25, 48]
+    caps = [cfg.kv_cap(l) for l in range(cfg.n_layers)]
+    log(f"[mixed prefix] caps {caps}")
+    model.set_kv(kv, plen)
+    toks = torch.randint(0, cfg.vocab, (B, L), dtype=torch.int32, device=DEV)
+    append = torch.tensor([1, 0, 1], dtype=torch.int32, device=DEV)
+    H = torch.empty(B * L, cfg.d_model, dtype=torch.float32, device=DEV)
+    model.mixed_forward(toks, append, H, ws)
+    assert model.prefix_len == [40 + L, 25, 48 + L]
+    assert model.max_prefix == 48 + L
