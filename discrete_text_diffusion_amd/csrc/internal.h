@@ -150,6 +150,7 @@ struct SampArgs {
   uint32_t k0, k1, step;          // Philox key (seed) and step index
   int slices, v_per_slice;        // vocabulary split
   float* part;                    // [slices][rows][6] partial (m2, s, a, g2, y, w) as floats/ints
+  const uint32_t* canvas_rng;     // device [B][4] (k0, k1, step, -) per canvas, or null: k0, k1, step
   const int32_t* gate;            // launch gate (set by the launcher)
 };
 hipError_t launch_lmhead_sampler(const SampArgs& a, int act_bf16, hipStream_t s);
@@ -172,6 +173,8 @@ struct StepArgs {
   int32_t* steps_taken;           // incremented for canvases that stepped (or null)
   int32_t* done_out;              // set when all positions locked (adaptive), or null
   int stats_only;                 // merge and write stats; leave canvas / lock / counts alone
+  const uint32_t* canvas_rng;     // device [B][4] (k0, k1, step, -) per canvas, or null: k0, k1, step
+  const float* lam_table;         // with canvas_rng: device [steps], lambda of canvas b = lam_table[step_b]
   const int32_t* gate;            // launch gate (set by the launcher)
 };
 constexpr int STAT_FIELDS = 6;
@@ -196,6 +199,25 @@ hipError_t launch_eb_select(EbArgs a, hipStream_t s);
 
 hipError_t launch_init_canvas(int32_t* canvas, uint8_t* lock, int B, int L, int V, uint32_t k0,
                               uint32_t k1, hipStream_t s);
+
+// Continuous block-AR scheduling: one sequence per block, after each pass (or, with init, before the
+// first).  A sequence is denoising canvas k at step s, appending its finished canvas, or finished.
+enum SeqPhase : int32_t { SEQ_DENOISE = 0, SEQ_APPEND = 1, SEQ_FINISHED = 2 };
+struct SeqArgs {
+  int B, L, K, T, V, adaptive, init;
+  uint64_t seed;                  // canvas k draws from seed + k
+  int32_t* state;                 // [B][4]: phase, k, s, steps taken on canvas k
+  uint32_t* rng;                  // [B][4] out: key of seed + k, step s (the next pass's draws)
+  int32_t* cur; uint8_t* lock;    // [B][L] working canvas and its locks
+  const int32_t* n_locked;        // [B] from the Step of this pass
+  int32_t* out; int32_t* steps;   // [K][B][L] finished canvases, [K][B] their steps (or null)
+  int32_t* append; int32_t* skip; int32_t* finished;  // [B] flags for the next pass
+  int32_t* passes;                // [1] passes that ran (or null)
+  const int32_t* gate;            // set by the launcher
+};
+hipError_t launch_seq_schedule(SeqArgs a, hipStream_t s);
+// dst[0..n) = vals[0..n), n <= 256 (never gated)
+hipError_t launch_write_f32(float* dst, const float* vals, int n, hipStream_t s);
 hipError_t launch_noise(const int32_t* x0, int32_t* xt, int B, int L, int V, float kappa,
                         uint32_t k0, uint32_t k1, uint32_t step, hipStream_t s);
 

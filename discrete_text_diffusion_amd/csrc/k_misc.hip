@@ -175,6 +175,7 @@ __global__ void kv_append_kernel(AppendArgs a) {
     if (a.mask && a.mask[b] == 0) return;
     const int pos = prefix_of(a.plen, b, a.max_prefix) + j;
     const int slot = a.is_global ? pos : pos % a.window;
+    if (slot >= a.cap) return;                      // never past the slots the host validated
     const int64_t src = (((int64_t)b * a.Hkv + g) * a.n + j) * a.row_bytes + ch * 16;
     const int64_t dst = (((int64_t)b * a.Hkv + g) * a.cap + slot) * a.row_bytes + ch * 16;
     *reinterpret_cast<u32x4*>(a.kc + dst) = *reinterpret_cast<const u32x4*>(a.kn + src);
@@ -191,6 +192,7 @@ __global__ void kv_append_kernel(AppendArgs a) {
   if (a.mask && a.mask[b] == 0) return;
   const int pos = prefix_of(a.plen, b, a.max_prefix) + j;
   const int slot = a.is_global ? pos : pos % a.window;
+  if (slot >= a.cap) return;
   if (a.esz == 2)
     reinterpret_cast<uint16_t*>(a.vc)[row * a.cap + slot] = reinterpret_cast<const uint16_t*>(a.vn)[row * a.vn_ld + j];
   else

@@ -79,7 +79,8 @@ DG_DEV float gumbel_key2(float z2, uint32_t w) { return gumbel_key2_nc(z2, w) + 
 // it, the argmax and the best Gumbel key with shuffles, and one lane merges the result into the
 // wave's running state of that row, which lives in LDS (the registers hold only the
 // accumulators); the WN states of a row are merged in wave order at the end.
-template <class TA, int BM, int BN, int WM, int WN, int NS>
+// PCR: each canvas takes its own Philox key and step index from p.canvas_rng
+template <class TA, int BM, int BN, int WM, int WN, int NS, bool PCR>
 __global__ __launch_bounds__(WM * WN * 64) void lmhead_sampler_kernel(SampArgs p, int n_mt) {
   if (gate_closed(p.gate)) return;
   using G = GemmDma<TA, BM, BN, WM, WN, NS>;
@@ -158,6 +159,11 @@ __global__ __launch_bounds__(WM * WN * 64) void lmhead_sampler_kernel(SampArgs p
     for (int i = 0; i < G::FM; ++i) {
       const int rb = m0 + G::row_of(i, 0);       // first of this lane's 4 consecutive rows
       const int b = rb / p.L, ii = rb - b * p.L;
+      uint32_t rk0 = p.k0, rk1 = p.k1, rstep = p.step;
+      if constexpr (PCR) {
+        const uint4 cr = *reinterpret_cast<const uint4*>(p.canvas_rng + 4 * min(b, p.rows / p.L - 1));
+        rk0 = cr.x; rk1 = cr.y; rstep = cr.z;
+      }
       // the row max over the tile (lowest token on ties): lane-local, then over the 16 lanes
       float rm[4];
       int ra[4];
@@ -185,7 +191,7 @@ __global__ __launch_bounds__(WM * WN * 64) void lmhead_sampler_kernel(SampArgs p
       for (int j = 0; j < G::FN; ++j) {
         const int v = v0 + G::col_of(j);
         if (v < v_end) {
-          const u32x4 w = philox((uint32_t)v, (uint32_t)(ii >> 2), p.step, ((uint32_t)b << 8) | TAG_GUMBEL, p.k0, p.k1);
+          const u32x4 w = philox((uint32_t)v, (uint32_t)(ii >> 2), rstep, ((uint32_t)b << 8) | TAG_GUMBEL, rk0, rk1);
           const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -236,19 +242,25 @@ __global__ __launch_bounds__(WM * WN * 64) void lmhead_sampler_kernel(SampArgs p
   }
 }
 
-template <class TA, int BM, int BN, int WM, int WN, int NS>
-static hipError_t launch_sampler_t(SampArgs a, hipStream_t s) {
+template <class TA, int BM, int BN, int WM, int WN, int NS, bool PCR>
+static hipError_t launch_sampler_p(const SampArgs& a, hipStream_t s) {
   using G = GemmDma<TA, BM, BN, WM, WN, NS>;
-  a.gate = launch_gate();
   const int n_mt = (a.rows + BM - 1) / BM;
   const int blocks = n_mt * ((a.slices + 7) / 8 * 8);
   const size_t lds = G::LDS_BYTES + (size_t)WN * BM * PART * 4;
   if (a.d % G::KT) return hipErrorInvalidValue;
-  static const hipError_t attr = allow_lds(lmhead_sampler_kernel<TA, BM, BN, WM, WN, NS>, lds);
+  static const hipError_t attr = allow_lds(lmhead_sampler_kernel<TA, BM, BN, WM, WN, NS, PCR>, lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((lmhead_sampler_kernel<TA, BM, BN, WM, WN, NS>), dim3(blocks), dim3(WM * WN * 64), lds, s, a,
-                     n_mt);
+  hipLaunchKernelGGL((lmhead_sampler_kernel<TA, BM, BN, WM, WN, NS, PCR>), dim3(blocks), dim3(WM * WN * 64), lds, s,
+                     a, n_mt);
   return hipGetLastError();
+}
+
+template <class TA, int BM, int BN, int WM, int WN, int NS>
+static hipError_t launch_sampler_t(SampArgs a, hipStream_t s) {
+  a.gate = launch_gate();
+  if (a.canvas_rng) return launch_sampler_p<TA, BM, BN, WM, WN, NS, true>(a, s);
+  return launch_sampler_p<TA, BM, BN, WM, WN, NS, false>(a, s);
 }
 
 // tiles: bf16 256 rows x 256 vocabulary entries on 8 waves of 32 rows (a row's statistics stay
@@ -359,8 +371,15 @@ __global__ __launch_bounds__(256) void step_merge_kernel(StepArgs p) {
     p.canvas[r] = s.a;
     p.lock[r] = 1;
   } else {
-    const u32x4 w = philox((uint32_t)(i >> 2), 0u, p.step, ((uint32_t)b << 8) | TAG_JUMP, p.k0, p.k1);
-    if (unit_co(pick(w, i & 3)) < p.lam) p.canvas[r] = s.y;
+    uint32_t k0 = p.k0, k1 = p.k1, stp = p.step;
+    float lam = p.lam;
+    if (p.canvas_rng) {
+      const uint4 cr = *reinterpret_cast<const uint4*>(p.canvas_rng + 4 * b);
+      k0 = cr.x; k1 = cr.y; stp = cr.z;
+      lam = p.lam_table[stp];
+    }
+    const u32x4 w = philox((uint32_t)(i >> 2), 0u, stp, ((uint32_t)b << 8) | TAG_JUMP, k0, k1);
+    if (unit_co(pick(w, i & 3)) < lam) p.canvas[r] = s.y;
   }
 }
 
@@ -529,6 +548,84 @@ hipError_t launch_noise(const int32_t* x0, int32_t* xt, int B, int L, int V, flo
   const int n = B * L;
   hipLaunchKernelGGL(noise_kernel, dim3((n + 255) / 256), dim3(256), 0, s, x0, xt, B, L, V, log2_exact(V),
                      kappa, k0, k1, step);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ continuous block-AR ----------
+// One block per sequence.  After a pass: a denoising sequence counts the step; once it stops (all
+// positions locked, adaptive) or reaches T steps, its canvas is stored as canvas k and the next pass
+// appends it to the cache (or the sequence finishes after canvas K - 1).  After an append pass the
+// sequence starts canvas k + 1 at t = 1: uniform tokens from the canvas-init stream of seed + k + 1,
+// locks cleared.  The flags and Philox keys written here drive the next pass.
+__global__ __launch_bounds__(256) void seq_schedule_kernel(SeqArgs a) {
+  if (gate_closed(a.gate)) return;
+  const int b = blockIdx.x;
+  __shared__ int sh_copy, sh_fresh, sh_k;
+  if (threadIdx.x == 0) {
+    int32_t* st = a.state + 4 * b;
+    int phase = SEQ_DENOISE, k = 0, s = 0, taken = 0, copy = -1, fresh = 1;
+    if (!a.init) {
+      phase = st[0]; k = st[1]; s = st[2]; taken = st[3];
+      fresh = 0;
+      if (phase == SEQ_DENOISE) {
+        ++s;
+        ++taken;
+        if ((a.adaptive && a.n_locked[b] == a.L) || s == a.T) {
+          copy = k;
+          if (a.steps) a.steps[(int64_t)k * a.B + b] = taken;
+          phase = k + 1 < a.K ? SEQ_APPEND : SEQ_FINISHED;
+        }
+      } else if (phase == SEQ_APPEND) {
+        ++k;
+        s = 0;
+        taken = 0;
+        phase = SEQ_DENOISE;
+        fresh = 1;
+      }
+    }
+    st[0] = phase; st[1] = k; st[2] = s; st[3] = taken;
+    const uint64_t seed = a.seed + (uint64_t)k;
+    uint32_t* r = a.rng + 4 * b;
+    r[0] = (uint32_t)(seed & 0xffffffffu); r[1] = (uint32_t)(seed >> 32); r[2] = (uint32_t)s; r[3] = 0u;
+    a.append[b] = phase == SEQ_APPEND;
+    a.skip[b] = phase != SEQ_DENOISE;
+    a.finished[b] = phase == SEQ_FINISHED;
+    if (b == 0 && a.passes) a.passes[0] = a.init ? 0 : a.passes[0] + 1;
+    sh_copy = copy; sh_fresh = fresh; sh_k = k;
+  }
+  __syncthreads();
+  const int copy = sh_copy, k = sh_k;
+  int32_t* cur = a.cur + (int64_t)b * a.L;
+  if (copy >= 0)
+    for (int i = threadIdx.x; i < a.L; i += blockDim.x) a.out[((int64_t)copy * a.B + b) * a.L + i] = cur[i];
+  if (sh_fresh) {
+    const uint64_t seed = a.seed + (uint64_t)k;
+    const uint32_t k0 = (uint32_t)(seed & 0xffffffffu), k1 = (uint32_t)(seed >> 32);
+    const int vlog2 = (a.V & (a.V - 1)) ? -1 : 31 - __clz(a.V);
+    for (int i = threadIdx.x; i < a.L; i += blockDim.x) {
+      const u32x4 w = philox((uint32_t)(i >> 2), 0u, 0u, ((uint32_t)b << 8) | TAG_INIT, k0, k1);
+      cur[i] = token_of(pick(w, i & 3), a.V, vlog2);
+      a.lock[(int64_t)b * a.L + i] = 0;
+    }
+  }
+}
+
+hipError_t launch_seq_schedule(SeqArgs a, hipStream_t s) {
+  a.gate = launch_gate();
+  hipLaunchKernelGGL(seq_schedule_kernel, dim3(a.B), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+struct F32Vals { float v[256]; };
+__global__ void write_f32_kernel(float* dst, F32Vals vals, int n) {
+  if ((int)threadIdx.x < n) dst[threadIdx.x] = vals.v[threadIdx.x];
+}
+
+hipError_t launch_write_f32(float* dst, const float* vals, int n, hipStream_t s) {
+  if (n < 0 || n > 256) return hipErrorInvalidValue;
+  F32Vals v{};
+  for (int i = 0; i < n; ++i) v.v[i] = vals[i];
+  hipLaunchKernelGGL(write_f32_kernel, dim3(1), dim3(256), 0, s, dst, v, n);
   return hipGetLastError();
 }
 

@@ -100,6 +100,7 @@ struct Layout {
   size_t resid, xhat, rope, q, kn, vn, attn_o, part_o, part_ml, rparts, o_parts, sh_parts;
   size_t counts, offsets, perm, inv_perm, tok, work, n_items;
   size_t a_grp, y, sh_a, samp_part, hidden, done, n_locked, prev, lockbuf, all_done;
+  size_t seq_state, seq_rng, seq_flags, lam_table;
   size_t total;
   int max_items;
 };
@@ -148,6 +149,10 @@ Layout layout(const dg_model_desc& d, int B, int n, int max_prefix) {
   w.prev = take(R * 4);
   w.lockbuf = take(R);
   w.all_done = take(4);
+  w.seq_state = take((size_t)B * 16);
+  w.seq_rng = take((size_t)B * 16);
+  w.seq_flags = take((size_t)B * 12);     // append, skip, finished
+  w.lam_table = take(256 * 4);
   w.total = o;
   return w;
 }
@@ -489,7 +494,8 @@ dg_status check_rows(int B, int L) {
 
 dg_status sample_into(dg_ctx* c, const void* hidden, int32_t* canvas, uint8_t* lock, int32_t* n_locked,
                       const int32_t* done, int B, int L, const dg_step_params* p, float lam, void* ws,
-                      const Layout& w, int32_t* steps_taken, int32_t* done_out, hipStream_t s) {
+                      const Layout& w, int32_t* steps_taken, int32_t* done_out, hipStream_t s,
+                      const uint32_t* canvas_rng = nullptr, const float* lam_table = nullptr) {
   const dg_model_desc& d = c->d;
   const int R = B * L;
   SampArgs sa{};
@@ -499,6 +505,7 @@ dg_status sample_into(dg_ctx* c, const void* hidden, int32_t* canvas, uint8_t* l
   sa.k0 = key0(p->seed); sa.k1 = key1(p->seed); sa.step = p->step;
   sa.slices = sampler_slices(d, R, &sa.v_per_slice);
   sa.part = at<float>(ws, w.samp_part);
+  sa.canvas_rng = canvas_rng;
   {
     ProfScope ps(c, DG_PROF_SAMPLER, s);
     HIPCHK(launch_lmhead_sampler(sa, d.act_dtype == DG_BF16, s));
@@ -510,6 +517,7 @@ dg_status sample_into(dg_ctx* c, const void* hidden, int32_t* canvas, uint8_t* l
   st.k0 = sa.k0; st.k1 = sa.k1; st.step = p->step;
   st.stats = at<float>(ws, w.stats); st.status = at<int>(ws, w.status);
   st.steps_taken = steps_taken; st.done_out = done_out;
+  st.canvas_rng = canvas_rng; st.lam_table = lam_table;
   HIPCHK(launch_step_merge(st, s));
   return DG_OK;
 }
@@ -748,6 +756,28 @@ dg_status dg_denoise_step(dg_ctx* ctx, const dg_kv* kv, const int32_t* canvas, c
   return DG_OK;
 }
 
+// one mixed pass (arguments already validated): append canvases take the causal encoder pass and
+// advance their device prefix length, the others the bidirectional decoder pass
+dg_status mixed_pass(dg_ctx* ctx, const dg_kv* kv, const int32_t* tokens, const int32_t* append, int L,
+                     void* hidden_out, void* ws, const Layout& w, hipStream_t stream) {
+  const dg_model_desc& d = ctx->d;
+  Pass P{ctx, kv, kv->batch, L, 0, ws, w, stream, append};
+  const int R = P.B * L;
+  HIPCHK(launch_embed(tokens, ctx->embed, at<float>(ws, P.w.resid), R, d.d_model, d.vocab, d.act_dtype == DG_BF16,
+                      stream));
+  HIPCHK(launch_rope_table(at<float2>(ws, P.w.rope), R, L, d.head_dim, std::log2((double)d.rope_theta),
+                           kv->prefix_len, kv->max_prefix, at<int>(ws, P.w.status), stream));
+  dg_status st;
+  for (int l = 0; l < d.n_layers; ++l) {
+    const bool last = l + 1 == d.n_layers;
+    if ((st = run_layer(P, l, true, l > 0, last ? ctx->final_norm : ctx->layers[l + 1].attn_norm,
+                        last ? hidden_out : at<void>(ws, P.w.xhat))) != DG_OK)
+      return st;
+  }
+  HIPCHK(launch_advance_prefix(kv->prefix_len, P.B, L, append, stream));
+  return DG_OK;
+}
+
 dg_status dg_mixed_forward(dg_ctx* ctx, const dg_kv* kv, const int32_t* tokens, const int32_t* append, int32_t L,
                            void* hidden_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   g_err.clear();
@@ -759,21 +789,7 @@ dg_status dg_mixed_forward(dg_ctx* ctx, const dg_kv* kv, const int32_t* tokens, 
   if (st != DG_OK) return st;
   if ((st = check_rows(kv->batch, L)) != DG_OK) return st;
   if ((st = check_ws(ctx, ws, ws_bytes, kv->batch, L, mp)) != DG_OK) return st;
-  const dg_model_desc& d = ctx->d;
-  Pass P{ctx, kv, kv->batch, L, 0, ws, layout(d, kv->batch, L, mp), stream, append};
-  const int R = P.B * L;
-  HIPCHK(launch_embed(tokens, ctx->embed, at<float>(ws, P.w.resid), R, d.d_model, d.vocab, d.act_dtype == DG_BF16,
-                      stream));
-  HIPCHK(launch_rope_table(at<float2>(ws, P.w.rope), R, L, d.head_dim, std::log2((double)d.rope_theta),
-                           kv->prefix_len, kv->max_prefix, at<int>(ws, P.w.status), stream));
-  for (int l = 0; l < d.n_layers; ++l) {
-    const bool last = l + 1 == d.n_layers;
-    if ((st = run_layer(P, l, true, l > 0, last ? ctx->final_norm : ctx->layers[l + 1].attn_norm,
-                        last ? hidden_out : at<void>(ws, P.w.xhat))) != DG_OK)
-      return st;
-  }
-  HIPCHK(launch_advance_prefix(kv->prefix_len, P.B, L, append, stream));
-  return DG_OK;
+  return mixed_pass(ctx, kv, tokens, append, L, hidden_out, ws, layout(ctx->d, kv->batch, L, mp), stream);
 }
 
 dg_status dg_step_sample(dg_ctx* ctx, const void* hidden, int32_t* canvas, uint8_t* lock, int32_t* n_locked,
@@ -928,6 +944,67 @@ dg_status dg_generate(dg_ctx* ctx, const dg_kv* kv, int32_t* out, int32_t* steps
                             stream)) != DG_OK)
       return st;
     if (k + 1 < K && (st = dg_prefill_kv(ctx, &cur, canvas, L, ws, ws_bytes, stream)) != DG_OK) return st;
+  }
+  if (valid) HIPCHK(launch_valid_tokens(out, K, B, L, eos_id, valid, eos_seen, stream));
+  return DG_OK;
+}
+
+dg_status dg_generate_continuous(dg_ctx* ctx, const dg_kv* kv, int32_t* out, int32_t* steps, int32_t* valid,
+                                 int32_t* eos_seen, int32_t* passes, int32_t K, int32_t L, int32_t eos_id,
+                                 const dg_run_params* params, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err.clear();
+  if (!ctx || !kv || !out || !params || !kv->prefix_len) return fail(DG_EINVAL, "NULL argument");
+  if (!ctx->embed) return fail(DG_EINVAL, "generation needs the embedding");
+  if (K < 1) return fail(DG_EINVAL, "K must be >= 1");
+  if (params->sampler != DG_SAMPLER_EULER) return fail(DG_EUNSUPPORTED, "continuous generation runs the Euler sampler");
+  const int T = params->max_steps;
+  if (T < 1 || T > 256) return fail(DG_EUNSUPPORTED, "max_steps %d not in [1, 256]", T);
+  dg_step_params sp{};
+  sp.schedule = params->schedule; sp.tau = params->tau; sp.lock_threshold = params->lock_threshold;
+  sp.seed = params->seed; sp.t = 1.f; sp.h = 1.f / T;
+  dg_status st = check_step_params(&sp);
+  if (st != DG_OK) return st;
+  const int B = kv->batch;
+  if ((st = check_rows(B, L)) != DG_OK) return st;
+  // every pass reads prefixes up to the largest one a sequence reaches, (K - 1) canvases on; an append
+  // starts at most one canvas earlier, so the caches need room for exactly that bound
+  dg_kv run = *kv;
+  run.max_prefix = kv->max_prefix + (K - 1) * L;
+  int mp = 0;
+  if ((st = check_kv(ctx, &run, 0, &mp)) != DG_OK) return st;
+  if ((st = check_ws(ctx, ws, ws_bytes, B, L, mp)) != DG_OK) return st;
+  const Layout w = layout(ctx->d, B, L, mp);
+  // lambda of each grid point, as the step-by-step loop takes it (double grid point, float result)
+  std::vector<float> lam(T);
+  for (int s = 0; s < T; ++s) lam[s] = jump_prob(params->schedule, 1.0 - s * (1.0 / T), 1.0 / T);
+  float* lam_dev = at<float>(ws, w.lam_table);
+  HIPCHK(launch_write_f32(lam_dev, lam.data(), T, stream));
+  int32_t* flags = at<int32_t>(ws, w.seq_flags);
+  int32_t* append = flags, *skip = flags + B, *finished = flags + 2 * B;
+  int32_t* all_done = at<int32_t>(ws, w.all_done);
+  HIPCHK(launch_fill_i32(all_done, 0, 1, stream));
+  SeqArgs sa{};
+  sa.B = B; sa.L = L; sa.K = K; sa.T = T; sa.V = ctx->d.vocab; sa.adaptive = params->adaptive != 0;
+  sa.seed = params->seed;
+  sa.state = at<int32_t>(ws, w.seq_state); sa.rng = at<uint32_t>(ws, w.seq_rng);
+  sa.cur = at<int32_t>(ws, w.prev); sa.lock = at<uint8_t>(ws, w.lockbuf);
+  sa.n_locked = at<int32_t>(ws, w.n_locked);
+  sa.out = out; sa.steps = steps; sa.append = append; sa.skip = skip; sa.finished = finished; sa.passes = passes;
+  {
+    // every pass is enqueued up front; once every sequence has finished, the gate turns the rest away
+    GateScope gate(all_done);
+    sa.init = 1;
+    HIPCHK(launch_seq_schedule(sa, stream));
+    sa.init = 0;
+    const int max_passes = K * T + K - 1;
+    for (int p = 0; p < max_passes; ++p) {
+      if ((st = mixed_pass(ctx, &run, sa.cur, append, L, at<void>(ws, w.hidden), ws, w, stream)) != DG_OK) return st;
+      if ((st = sample_into(ctx, at<void>(ws, w.hidden), sa.cur, sa.lock, at<int32_t>(ws, w.n_locked), skip, B, L,
+                            &sp, 0.f, ws, w, nullptr, nullptr, stream, sa.rng, lam_dev)) != DG_OK)
+        return st;
+      HIPCHK(launch_seq_schedule(sa, stream));
+      HIPCHK(launch_all_set(finished, B, all_done, stream));
+    }
   }
   if (valid) HIPCHK(launch_valid_tokens(out, K, B, L, eos_id, valid, eos_seen, stream));
   return DG_OK;

@@ -87,6 +87,9 @@ EXPORTS = {
     "dg_jump_prob": (C.c_float, [C.c_int, C.c_float, C.c_float]),
     "dg_generate": (C.c_int, [C.c_void_p, C.POINTER(KV), C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
                               C.c_int32, C.c_int32, C.POINTER(RunParams), C.c_void_p, C.c_size_t, C.c_void_p]),
+    "dg_generate_continuous": (C.c_int, [C.c_void_p, C.POINTER(KV), C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                         C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.POINTER(RunParams),
+                                         C.c_void_p, C.c_size_t, C.c_void_p]),
     "dg_test_step_from_logits": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
                                            C.c_int32, C.POINTER(StepParams), C.c_void_p, C.c_size_t, C.c_void_p]),
     "dg_test_read_stats": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
@@ -211,6 +214,13 @@ def dg_canvas_run(ctx, kv: KV, canvas, lock, steps_taken, L, params: RunParams, 
 def dg_generate(ctx, kv: KV, out, steps, valid, eos_seen, K, L, eos_id, params: RunParams, ws, stream=None):
     _check(load().dg_generate(ctx, C.byref(kv), _ptr(out), _ptr(steps), _ptr(valid), _ptr(eos_seen), K, L, eos_id,
                               C.byref(params), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def dg_generate_continuous(ctx, kv: KV, out, steps, valid, eos_seen, passes, K, L, eos_id, params: RunParams, ws,
+                           stream=None):
+    _check(load().dg_generate_continuous(ctx, C.byref(kv), _ptr(out), _ptr(steps), _ptr(valid), _ptr(eos_seen),
+                                         _ptr(passes), K, L, eos_id, C.byref(params), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def dg_jump_prob(schedule, t, h):

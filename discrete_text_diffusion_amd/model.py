@@ -132,6 +132,15 @@ class Model:
         dg.dg_generate(self.ctx, self.kv_struct, out, steps, valid, eos_seen, K, L, eos_id, params, ws, stream)
         self._grew((K - 1) * L)
 
+    def generate_continuous(self, out, steps, valid, eos_seen, passes, eos_id, params: dg.RunParams, ws,
+                            stream=None):
+        """Block-AR generation with every sequence on its own schedule (stopped canvases appended in
+        the next mixed pass while others keep denoising); `passes` receives the passes that ran."""
+        K, _, L = out.shape
+        dg.dg_generate_continuous(self.ctx, self.kv_struct, out, steps, valid, eos_seen, passes, K, L, eos_id,
+                                  params, ws, stream)
+        self._grew((K - 1) * L)
+
     def close(self):
         if self.ctx:
             dg.dg_destroy(self.ctx)

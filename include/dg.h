@@ -285,6 +285,24 @@ dg_status dg_generate(dg_ctx *ctx, const dg_kv *kv, int32_t *out, int32_t *steps
                       int32_t *eos_seen, int32_t K, int32_t L, int32_t eos_id, const dg_run_params *params,
                       void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Block-AR generation with every sequence on its own schedule ([TR §CPU-GPU 동기화 제거]: denoising
+ * canvases and cache updates share a batch, told apart by a per-sequence flag; [TR §DiffusionGemma
+ * 샘플러]: a canvas stops refining once settled).  Same results per sequence as dg_generate with the
+ * Euler sampler: canvas k of sequence b is denoised from a uniform canvas with the random streams of
+ * seed + k and, except the last, appended to the cache at positions prefix_len[b] ..  But each pass
+ * is one dg_mixed_forward over all sequences: a sequence whose canvas has stopped (every position
+ * locked with `adaptive`, or max_steps steps taken) appends it in the next pass while the others keep
+ * denoising, then starts its next canvas — all decided on the device.  Sequence b thus uses
+ * sum_k steps[k][b] + K - 1 passes (the denominator of tokens per forward pass, [TR §추론 효율
+ * 지표]); the batch runs until its longest sequence finishes.  All K max_steps + K - 1 passes are
+ * enqueued at once; those after the last sequence finishes return at kernel entry.
+ * Arguments as for dg_generate (params->sampler must be DG_SAMPLER_EULER, max_steps <= 256); passes
+ * (device int32 [1], may be NULL) receives the number of passes that ran.  Global-layer caches need
+ * cap >= max_prefix + (K - 1) L; on return kv->prefix_len has grown by (K - 1) L. */
+dg_status dg_generate_continuous(dg_ctx *ctx, const dg_kv *kv, int32_t *out, int32_t *steps, int32_t *valid,
+                                 int32_t *eos_seen, int32_t *passes, int32_t K, int32_t L, int32_t eos_id,
+                                 const dg_run_params *params, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* lambda of one Step as the library computes it (host function, float32 result). */
 float dg_jump_prob(dg_schedule schedule, float t, float h);
 

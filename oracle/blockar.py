@@ -67,6 +67,18 @@ def metrics(steps, valid, eos_seen):
     return out
 
 
+def continuous_passes(steps):
+    """Forward passes of the continuous schedule [TR §CPU-GPU 동기화 제거: denoising canvases and
+    cache updates share a batch; TR §추론 효율 지표: K - 1 append passes]: every sequence proceeds on
+    its own, s_k,b denoising passes for canvas k and one append pass after every canvas but the
+    last, and a batch runs until its longest sequence is done: max_b (sum_k s_k,b + K - 1).
+    The lockstep schedule (every canvas k waits for the slowest sequence, then all append together)
+    takes sum_k max_b s_k,b + K - 1.  steps [K][B]; returns (continuous, lockstep)."""
+    steps = np.asarray(steps, dtype=np.int64)
+    K = steps.shape[0]
+    return int(steps.sum(axis=0).max() + K - 1), int(steps.max(axis=1).sum() + K - 1)
+
+
 def eos_mask(out, eos):
     out = np.asarray(out)
     return (out == eos).any(axis=2)

@@ -90,3 +90,56 @@ def test_valid_token_counts_planted():
     g = out.cpu().numpy()
     assert np.array_equal(valid.cpu().numpy(), BA.valid_counts(g, eos))
     assert seen.cpu().numpy()[0, 0] == 1 and seen.cpu().numpy()[0, 2] == 0
+
+
+def test_continuous_generation_matches_oracle_and_saves_passes():
+    """dg_generate_continuous: every sequence on its own schedule, a stopped canvas appended in the
+    next mixed pass while the other sequences keep denoising.  Per sequence the canvases, step counts
+    and appended caches equal the oracle's block-AR generation (and the lockstep dg_generate's); the
+    passes that ran equal max_b (sum_k s_k,b + K - 1)."""
+    K, P0 = 3, 48
+    cfg = configs.C0.replace(batch=3, prefix=P0 + (K - 1) * 32, steps=8, tau=0.03, lock_threshold=0.9)
+    B, L, V = cfg.batch, cfg.canvas, cfg.vocab
+    prompt = torch.from_numpy(np.random.default_rng(5).integers(0, V, (B, P0)).astype(np.int32)).to(DEV)
+    rp = dg.RunParams(schedule=cfg.schedule, max_steps=cfg.steps, tau=cfg.tau, lock_threshold=cfg.lock_threshold,
+                      seed=11, adaptive=1, init_canvas=1, sampler=dg.DG_SAMPLER_EULER)
+    eos = 17
+
+    def encoded():
+        model, W, kv = build(cfg, kv_mode="empty")
+        model.set_kv(kv, [0] * B)
+        ws = model.workspace(B, max(L, P0), cfg.prefix)
+        model.prefill_kv(prompt, ws)
+        return model, W, kv, ws
+
+    outs = {}
+    for mode in ("continuous", "lockstep"):
+        model, W, kv, ws = encoded()
+        out = torch.empty(K, B, L, dtype=torch.int32, device=DEV)
+        steps = torch.empty(K, B, dtype=torch.int32, device=DEV)
+        valid = torch.empty(K, B, dtype=torch.int32, device=DEV)
+        seen = torch.empty(K, B, dtype=torch.int32, device=DEV)
+        passes = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+        if mode == "continuous":
+            model.generate_continuous(out, steps, valid, seen, passes, eos, rp, ws)
+        else:
+            model.generate(out, steps, valid, seen, eos, rp, ws)
+        torch.cuda.synchronize()
+        assert dg.dg_query_status(model.ctx, ws) == dg.DG_OK
+        outs[mode] = (out.cpu().numpy(), steps.cpu().numpy(), valid.cpu().numpy(), seen.cpu().numpy(),
+                      int(passes.item()), model.prefix_len, [np64(kv[l][0]) for l in range(cfg.n_layers)])
+    g, gs, gv, gseen, npass, gplen, gk = outs["continuous"]
+    OW = oracle_weights(W, cfg)
+    okv, plen = M.prefill(cfg, OW, oracle_kv(gen.empty_kv(cfg)), [0] * B, prompt.cpu().numpy())
+    oout, osteps, okv2, oplen = BA.generate(cfg.replace(adaptive=True), OW, okv, plen, K, eos, seed=11)
+    want_cont, want_lock = BA.continuous_passes(osteps)
+    log(f"  steps gpu {gs.T.tolist()} oracle {osteps.T.tolist()}; passes {npass} (oracle {want_cont}, "
+        f"lockstep schedule {want_lock})")
+    assert np.array_equal(g, oout) and np.array_equal(gs, osteps)
+    assert np.array_equal(g, outs["lockstep"][0]) and np.array_equal(gs, outs["lockstep"][1])
+    assert npass == want_cont
+    assert gplen == oplen == [P0 + (K - 1) * L] * B
+    for l in range(cfg.n_layers):
+        assert np.abs(gk[l][:, :, :oplen[0]] - okv2[l][0][:, :, :oplen[0]]).max() <= 1e-4
+    assert np.array_equal(gv, BA.valid_counts(g, eos))
+    assert np.array_equal(gseen.astype(bool), BA.eos_mask(g, eos))

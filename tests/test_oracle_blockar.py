@@ -129,3 +129,14 @@ def test_mixed_pass_equals_each_canvas_alone():
                 assert np.array_equal(K2[b], K0[b]) and np.array_equal(V2[b], V0[b])
             Hb, _ = M.denoise_forward(cfg, OW, kvb, [plen[b]], canvas=toks[b:b + 1])
         assert np.allclose(H[rows], Hb, rtol=0, atol=1e-12)
+
+
+def test_continuous_pass_count_by_hand():
+    """Two sequences, three canvases: sequence 0 takes 2, 5, 1 steps, sequence 1 takes 4, 1, 3.
+    Continuous: 8 + 2 and 8 + 2 passes -> 10; lockstep: 4 + 5 + 3 + 2 = 14.  One canvas: the
+    continuous count is the slowest sequence's steps."""
+    steps = np.array([[2, 4], [5, 1], [1, 3]])
+    assert BA.continuous_passes(steps) == (10, 14)
+    assert BA.continuous_passes(np.array([[3, 7, 5]])) == (7, 7)
+    # equal step counts everywhere: the two schedules coincide
+    assert BA.continuous_passes(np.full((4, 3), 6)) == (27, 27)
