@@ -49,6 +49,32 @@ def read_stats(model, ws, rows):
             "best": best.cpu().numpy(), "H": H.cpu().numpy()}
 
 
+def check_routing(cfg, gidx, g_r, info):
+    """Routing parity of one layer.  The GPU's selection gidx must be exactly the top-k of its own fp32
+    router scores g_r (bit-exact given equal scores).  It may differ from the oracle's own selection
+    (info["idx"] from scores info["r32"]) only on a row whose k-th/(k+1)-th oracle score gap is within
+    twice that row's own measured score error, and on at most max(2, 2.5%) of the rows: a systematic
+    score error could otherwise excuse many rows.  Returns (selection for the oracle to take,
+    rerouted rows, max score error)."""
+    from oracle import model as M
+    sel_from_gpu_scores, _ = M.router_topk(g_r, cfg.top_k)
+    assert np.array_equal(gidx, sel_from_gpu_scores), "GPU top-k is not the top-k of its own scores"
+    row_err = np.abs(g_r - info["r32"]).max(axis=1)
+    lg_err = float(row_err.max())
+    assert lg_err <= (1e-4 if cfg.act_dtype == "f32" else 2e-2), f"router logits differ by {lg_err}"
+    r = info["r32"].astype(np.float64)
+    srt = -np.sort(-r, axis=1)
+    gap = srt[:, cfg.top_k - 1] - srt[:, cfg.top_k] if cfg.top_k < cfg.n_experts else np.full(len(r), np.inf)
+    near = gap <= 2 * row_err + 1e-6
+    mism = np.any(np.sort(gidx, 1) != np.sort(info["idx"], 1), axis=1)
+    n = int(mism.sum())
+    print(f"  routing: score error max {lg_err:.2e} (row median {np.median(row_err):.2e}); rows within their "
+          f"own error of a tie {int(near.sum())}; rerouted {n} of {len(r)}", flush=True)
+    assert not (mism & ~near).any(), f"routing differs beyond the row's score error at rows {np.nonzero(mism & ~near)[0][:8]}"
+    assert n <= max(2, len(r) * 25 // 1000), f"{n} of {len(r)} rows rerouted"
+    return np.where(mism[:, None], gidx, info["idx"]), n, lg_err
+
+
 def top2_gap(z):
     p = np.partition(z, -2, axis=-1)
     return p[..., -1] - p[..., -2]
@@ -58,7 +84,8 @@ def compare_step(gpu_canvas, gpu_lock, gpu_stats, orc_canvas, orc_lock, orc_stat
                  y_gap_tol=1e-3, a_gap_tol=1e-5, c_tol=1e-5):
     """Selection parity: token ids, argmaxes and locks equal except where the oracle's own margin
     says floating-point order may decide (Gumbel top-2 gap < y_gap_tol, logit top-2 gap <
-    a_gap_tol, |c - theta| < c_tol).  Returns the number of excused rows."""
+    a_gap_tol, |c - theta| < c_tol).  Returns the number of rows whose token or lock actually
+    differs under such an excuse (rows that agree are not counted)."""
     ga, gy, gc = gpu_stats["a"], gpu_stats["y"], gpu_stats["c"]
     oa, oy, oc = orc_stats["a"], orc_stats["y"], orc_stats["c"]
     excuse_a = z_gap < a_gap_tol
@@ -69,8 +96,12 @@ def compare_step(gpu_canvas, gpu_lock, gpu_stats, orc_canvas, orc_lock, orc_stat
     assert not bad_a.any(), f"argmax differs at rows {np.nonzero(bad_a)[0][:10]}"
     assert not bad_y.any(), f"Gumbel argmax differs at rows {np.nonzero(bad_y)[0][:10]}"
     excused = ((ga != oa) | (gy != oy) | excuse_c).reshape(gpu_canvas.shape)
-    diff_c = (gpu_canvas != orc_canvas) & ~excused
-    diff_l = (gpu_lock.astype(bool) != orc_lock) & ~excused
-    assert not diff_c.any(), f"canvas differs at {np.argwhere(diff_c)[:10]}"
-    assert not diff_l.any(), f"lock differs at {np.argwhere(diff_l)[:10]}"
-    return int(excused.sum())
+    differ = (gpu_canvas != orc_canvas) | (gpu_lock.astype(bool) != orc_lock)
+    diff = differ & ~excused
+    assert not diff.any(), f"canvas or lock differs at {np.argwhere(diff)[:10]}"
+    return int((differ & excused).sum())
+
+
+def max_excused(rows):
+    """Disagreements the 99.9% agreement rule allows among `rows` checked rows."""
+    return rows // 1000

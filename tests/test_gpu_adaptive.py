@@ -21,7 +21,8 @@ from discrete_text_diffusion_amd import dg
 from oracle import model as M
 from oracle import step as S
 from synth import configs, gen
-from tests.gpu_util import build, log
+from oracle.numerics import rounder
+from tests.gpu_util import build, check_routing, compare_step, log, max_excused, read_stats, top2_gap
 from tests.helpers import oracle_kv_dev, oracle_weights
 
 pytestmark = pytest.mark.gpu
@@ -127,3 +128,91 @@ def test_mixed_pass_advances_the_append_canvases_on_the_device():
     model.mixed_forward(toks, append, H, ws)
     assert model.prefix_len == [40 + L, 25, 48 + L]
     assert model.max_prefix == 48 + L
+
+
+def test_batched_fp8_zipf_adaptive_loop_teacher_forced():
+    """The batched adaptive workload's settings (8 canvases of 256 over their own 4096-token prefixes,
+    fp8 e4m3 experts, Zipf(1.1) router prior, cosine schedule, lock-in at 0.95, adaptive with a cap
+    of 48), cut to one decoder layer and a 16,384-token vocabulary so the oracle stays tractable,
+    with tau 0.004 so canvases lock everything within a few steps.  bf16 arithmetic: the loop is
+    compared step by step, teacher-forced (each Step recomputed by the oracle from the GPU's hidden
+    states and canvas: tokens, locks and counts equal; the decoder pass at step 0 reported); then
+    dg_canvas_run must reproduce the step-by-step loop bit for bit, steps taken included."""
+    cfg = configs.C4.replace(n_layers=1, vocab=16384, tau=0.004)
+    B, L, V, T = cfg.batch, cfg.canvas, cfg.vocab, cfg.steps
+    log(f"[adaptive batched] B {B} L {L} V {V} prefix {cfg.prefix} fp8 zipf cosine theta {cfg.lock_threshold}")
+    model, W, kv = build(cfg)
+    ws = model.workspace(B, L, cfg.prefix)
+    OW = oracle_weights(W, cfg)
+    okv = oracle_kv_dev(kv)
+    E64 = OW["embed"]
+    plen = [cfg.prefix] * B
+    cv = torch.empty(B, L, dtype=torch.int32, device=DEV)
+    lk = torch.zeros(B, L, dtype=torch.uint8, device=DEV)
+    dg.dg_init_canvas(cv, lk, B, L, V, cfg.seed)
+    nl = torch.empty(B, dtype=torch.int32, device=DEV)
+    done = torch.zeros(B, dtype=torch.int32, device=DEV)
+    H = torch.empty(B * L, cfg.d_model, dtype=torch.bfloat16, device=DEV)
+    R = torch.empty(B * L, cfg.d_model, dtype=torch.float32, device=DEV)
+    ts, h = S.time_grid(T)
+    taken = np.zeros(B, np.int64)
+    excused = 0
+    for s, t in enumerate(ts):
+        if done.all():
+            break
+        before = cv.cpu().numpy().copy()
+        lock_before = lk.cpu().numpy().astype(bool)
+        done_before = done.cpu().numpy().astype(bool)
+        model.denoise_step(cv, L, ws, hidden_out=H, resid_out=R)
+        model.step_sample(H, cv, lk, nl, gpu_step(cfg, t, h, s), ws, done=done)
+        torch.cuda.synchronize()
+        if s == 0:
+            # the decoder layer from the same canvas: fp32 residual within 2e-2, with the GPU's
+            # expert choice taken where a router near-tie explains a different one
+            r_logits = torch.empty(B * L, cfg.n_experts, dtype=torch.float32, device=DEV)
+            r_idx = torch.empty(B * L, cfg.top_k, dtype=torch.int32, device=DEV)
+            dg.dg_test_read_routing(model.ctx, ws, B * L, r_logits, r_idx, None)
+            torch.cuda.synchronize()
+            h0 = E64[before.reshape(-1)]
+            rnd = rounder(cfg.act_dtype)
+            _, info = M.denoise_layer(cfg, 0, h0, OW["layers"][0], okv[0][0], okv[0][1], plen, rnd)
+            forced, n_rer, lg_err = check_routing(cfg, r_idx.cpu().numpy(), r_logits.cpu().numpy(), info)
+            oR, _ = M.denoise_layer(cfg, 0, h0, OW["layers"][0], okv[0][0], okv[0][1], plen, rnd, forced_idx=forced)
+            err = float(np.abs(R.cpu().numpy() - oR).max())
+            log(f"  step 0 decoder: max |resid - oracle| {err:.2e}; router logits err {lg_err:.2e}, "
+                f"near-tie reroutes {n_rer}")
+            # reported: the input here is the raw embedding (RMS 0.02), which the attention norm
+            # scales up about 50x, so absolute errors grow with it; the same layer from an O(1)
+            # residual is held to 2e-2 by the layer parity tests
+            assert err <= 5e-2
+        Hg = H.float().cpu().numpy().astype(np.float64)
+        z = (Hg @ E64.T) / np.float64(np.float32(cfg.tau))
+        ocv, olk, onl, ost, _ = S.step_from_logits(z, before, lock_before, float(np.float32(t)),
+                                                   float(np.float32(h)), cfg.schedule, cfg.lock_threshold,
+                                                   cfg.seed, s, done_before)
+        st = read_stats(model, ws, B * L)
+        excused += compare_step(cv.cpu().numpy(), lk.cpu().numpy(), st, ocv, olk, ost, top2_gap(z),
+                                cfg.lock_threshold)
+        taken += ~done_before
+        assert nl.cpu().numpy().tolist() == lk.cpu().numpy().sum(axis=1).tolist()
+        done = (nl == L).to(torch.int32)          # the adaptive rule, on the GPU's own locks
+        log(f"  step {s}: locked {lk.cpu().numpy().sum(axis=1).tolist()}")
+    log(f"  steps taken {taken.tolist()}; excused rows {excused}")
+    assert excused <= max_excused(B * L * int(taken.max()))
+    assert taken.max() < T and len(set(taken.tolist())) > 1, "planted run should stop early, canvases at different steps"
+    # the library's own loop: same canvas, locks and steps taken, with no host read in between
+    cv2 = torch.empty(B, L, dtype=torch.int32, device=DEV)
+    lk2 = torch.empty(B, L, dtype=torch.uint8, device=DEV)
+    tk2 = torch.empty(B, dtype=torch.int32, device=DEV)
+    rp = dg.RunParams(schedule=cfg.schedule, max_steps=T, tau=cfg.tau, lock_threshold=cfg.lock_threshold,
+                      seed=cfg.seed, adaptive=1, init_canvas=1)
+    model.canvas_run(cv2, lk2, tk2, rp, ws)
+    torch.cuda.synchronize()
+    assert tk2.cpu().numpy().tolist() == taken.tolist()
+    assert np.array_equal(cv2.cpu().numpy(), cv.cpu().numpy())
+    assert np.array_equal(lk2.cpu().numpy(), lk.cpu().numpy())
+
+
+def gpu_step(cfg, t, h, s):
+    return dg.StepParams(schedule=cfg.schedule, t=t, h=h, tau=cfg.tau, lock_threshold=cfg.lock_threshold,
+                         seed=cfg.seed, step=s)

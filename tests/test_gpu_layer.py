@@ -15,7 +15,7 @@ from discrete_text_diffusion_amd import dg
 from oracle import model as M
 from oracle.numerics import rounder
 from synth import configs, gen
-from tests.gpu_util import build, log
+from tests.gpu_util import build, check_routing, log
 from tests.helpers import np64, oracle_layer
 
 pytestmark = pytest.mark.gpu
@@ -72,31 +72,14 @@ def _layer_parity(cfg, layer, tol, resid=None):
     K, V = np64(kv[layer][0]), np64(kv[layer][1].transpose(-1, -2))
     h0 = rin.cpu().numpy().astype(np.float64)
     rnd = rounder(cfg.act_dtype)
-    # routing: the GPU's selection must be the top-k of the GPU's own fp32 scores (bit-exact given
-    # equal scores); where it differs from the oracle's own selection, the scores' difference must
-    # explain it (the oracle's k-th/(k+1)-th gap is within the measured score error)
+    # routing: the GPU's own top-k, reroutes only where the score error explains them (bounded)
     _, info = M.denoise_layer(cfg, layer, h0, lw, K, V, [cfg.prefix] * B, rnd)
-    gidx = r_idx.cpu().numpy()
-    g_r = r_logits.cpu().numpy()
-    sel_from_gpu_scores, _ = M.router_topk(g_r, cfg.top_k)
-    assert np.array_equal(gidx, sel_from_gpu_scores), "GPU top-k is not the top-k of its own scores"
-    lg_err = float(np.abs(g_r - info["r32"]).max())
-    r = info["r32"].astype(np.float64)
-    srt = -np.sort(-r, axis=1)
-    if cfg.top_k < cfg.n_experts:
-        gap = srt[:, cfg.top_k - 1] - srt[:, cfg.top_k]
-    else:
-        gap = np.full(len(r), np.inf)
-    near = gap <= 2 * lg_err + 1e-6
-    mism = np.any(np.sort(gidx, 1) != np.sort(info["idx"], 1), axis=1)
-    assert lg_err <= (1e-4 if cfg.act_dtype == "f32" else 2e-2), f"router logits differ by {lg_err}"
-    assert not (mism & ~near).any(), f"routing differs beyond the score error at rows {np.nonzero(mism & ~near)[0][:8]}"
-    forced = np.where(mism[:, None], gidx, info["idx"])
+    forced, n_rer, lg_err = check_routing(cfg, r_idx.cpu().numpy(), r_logits.cpu().numpy(), info)
     h1, _ = M.denoise_layer(cfg, layer, h0, lw, K, V, [cfg.prefix] * B, rnd, forced_idx=forced)
     got = rout.cpu().numpy()
     err = np.abs(got - h1).max()
     log(f"  max |resid - oracle| = {err:.3e} (tol {tol}); router logits max err {lg_err:.2e}; "
-        f"near-tie reroutes {int(mism.sum())}")
+        f"near-tie reroutes {n_rer}")
     assert err <= tol
     return err
 

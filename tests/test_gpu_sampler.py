@@ -10,7 +10,7 @@ from oracle import eb
 from oracle import philox
 from oracle import step as S
 from synth import configs, gen
-from tests.gpu_util import build, compare_step, log, read_stats, step_params, top2_gap
+from tests.gpu_util import build, compare_step, log, max_excused, read_stats, step_params, top2_gap
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -70,7 +70,7 @@ def test_step_from_logits_selection_parity(B, L, V, tau, t, h, theta):
                                                  float(np.float32(t)), float(np.float32(h)), 0, theta, 99, 2)
     excused = compare_step(cv.cpu().numpy(), lk.cpu().numpy(), st, ocv, olk, ost, top2_gap(z64), theta)
     log(f"  excused rows: {excused}")
-    assert excused <= max(1, B * L // 1000)
+    assert excused <= max_excused(B * L)
     assert np.array_equal(nl.cpu().numpy(), olk.sum(axis=1))
     assert np.allclose(st["c"], ost["c"], rtol=1e-5, atol=1e-7)
     assert np.allclose(st["m"], ost["m"], atol=1e-5)
@@ -96,14 +96,15 @@ def test_locked_canvas_is_fixed_point_on_gpu():
 
 @pytest.mark.parametrize("case", ["tiny-fp32", "vocab262k-bf16", "vocab262k-bf16-b8", "vocab262k-bf16-ragged"])
 def test_fused_sampler_parity(case):
-    """Row tiles of 256: one canvas is one tile; eight canvases (2048 rows, the batched workload)
-    are 8 row tiles per vocabulary slice; 3 canvases of 112 end in a ragged 80-row tile."""
+    """Row tiles of 256: one canvas is one tile (all 256 rows checked); eight canvases (2048 rows, the
+    batched workload) are 8 row tiles per vocabulary slice; 3 canvases of 112 end in a ragged 80-row
+    tile.  Fewer than 1000 rows are checked per case, so no disagreement is allowed (99.9% rule)."""
     if case == "tiny-fp32":
         cfg = configs.C0
         rows_checked = None
     elif case == "vocab262k-bf16":
         cfg = configs.C2.replace(n_layers=1)
-        rows_checked = np.arange(0, 256, 4)            # 64 sampled rows, every 4th position
+        rows_checked = np.arange(0, 256)               # every row of the canvas
     elif case == "vocab262k-bf16-b8":
         cfg = configs.C2.replace(n_layers=1, batch=8)
         rows_checked = np.arange(5, 2048, 32)          # 64 rows, two in every row tile
@@ -140,7 +141,7 @@ def test_fused_sampler_parity(case):
     excused = compare_step(cv.cpu().numpy().reshape(-1)[rows], lk.cpu().numpy().reshape(-1)[rows], gst,
                            want_cv, conf, ost, top2_gap(z), cfg.lock_threshold)
     log(f"  excused rows: {excused} of {len(rows)}")
-    assert excused <= max(1, len(rows) // 1000)
+    assert excused <= max_excused(len(rows))
     tol = 1e-4 if cfg.act_dtype == "f32" else 2e-3
     assert np.allclose(gst["m"], ost["m"], atol=tol), np.abs(gst["m"] - ost["m"]).max()
     assert np.allclose(gst["c"], ost["c"], rtol=10 * tol)
