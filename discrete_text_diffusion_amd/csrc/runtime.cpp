@@ -759,7 +759,7 @@ dg_status dg_denoise_step(dg_ctx* ctx, const dg_kv* kv, const int32_t* canvas, c
 // one mixed pass (arguments already validated): append canvases take the causal encoder pass and
 // advance their device prefix length, the others the bidirectional decoder pass
 dg_status mixed_pass(dg_ctx* ctx, const dg_kv* kv, const int32_t* tokens, const int32_t* append, int L,
-                     void* hidden_out, void* ws, const Layout& w, hipStream_t stream) {
+                     void* hidden_out, float* resid_out, void* ws, const Layout& w, hipStream_t stream) {
   const dg_model_desc& d = ctx->d;
   Pass P{ctx, kv, kv->batch, L, 0, ws, w, stream, append};
   const int R = P.B * L;
@@ -774,12 +774,13 @@ dg_status mixed_pass(dg_ctx* ctx, const dg_kv* kv, const int32_t* tokens, const 
                         last ? hidden_out : at<void>(ws, P.w.xhat))) != DG_OK)
       return st;
   }
+  if (resid_out) HIPCHK(launch_copy_f32(at<float>(ws, P.w.resid), resid_out, (int64_t)R * d.d_model, stream));
   HIPCHK(launch_advance_prefix(kv->prefix_len, P.B, L, append, stream));
   return DG_OK;
 }
 
 dg_status dg_mixed_forward(dg_ctx* ctx, const dg_kv* kv, const int32_t* tokens, const int32_t* append, int32_t L,
-                           void* hidden_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+                           void* hidden_out, float* resid_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   g_err.clear();
   if (!ctx || !tokens || !append || !hidden_out) return fail(DG_EINVAL, "NULL argument");
   if (!ctx->embed) return fail(DG_EINVAL, "embedding tokens needs the embedding");
@@ -789,7 +790,7 @@ dg_status dg_mixed_forward(dg_ctx* ctx, const dg_kv* kv, const int32_t* tokens, 
   if (st != DG_OK) return st;
   if ((st = check_rows(kv->batch, L)) != DG_OK) return st;
   if ((st = check_ws(ctx, ws, ws_bytes, kv->batch, L, mp)) != DG_OK) return st;
-  return mixed_pass(ctx, kv, tokens, append, L, hidden_out, ws, layout(ctx->d, kv->batch, L, mp), stream);
+  return mixed_pass(ctx, kv, tokens, append, L, hidden_out, resid_out, ws, layout(ctx->d, kv->batch, L, mp), stream);
 }
 
 dg_status dg_step_sample(dg_ctx* ctx, const void* hidden, int32_t* canvas, uint8_t* lock, int32_t* n_locked,
@@ -998,7 +999,8 @@ dg_status dg_generate_continuous(dg_ctx* ctx, const dg_kv* kv, int32_t* out, int
     sa.init = 0;
     const int max_passes = K * T + K - 1;
     for (int p = 0; p < max_passes; ++p) {
-      if ((st = mixed_pass(ctx, &run, sa.cur, append, L, at<void>(ws, w.hidden), ws, w, stream)) != DG_OK) return st;
+      if ((st = mixed_pass(ctx, &run, sa.cur, append, L, at<void>(ws, w.hidden), nullptr, ws, w, stream)) != DG_OK)
+        return st;
       if ((st = sample_into(ctx, at<void>(ws, w.hidden), sa.cur, sa.lock, at<int32_t>(ws, w.n_locked), skip, B, L,
                             &sp, 0.f, ws, w, nullptr, nullptr, stream, sa.rng, lam_dev)) != DG_OK)
         return st;

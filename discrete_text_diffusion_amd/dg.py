@@ -79,7 +79,7 @@ EXPORTS = {
     "dg_denoise_step": (C.c_int, [C.c_void_p, C.POINTER(KV), C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
                                   C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "dg_mixed_forward": (C.c_int, [C.c_void_p, C.POINTER(KV), C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p,
-                                   C.c_void_p, C.c_size_t, C.c_void_p]),
+                                   C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "dg_step_sample": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                  C.c_int32, C.c_int32, C.POINTER(StepParams), C.c_void_p, C.c_size_t, C.c_void_p]),
     "dg_canvas_run": (C.c_int, [C.c_void_p, C.POINTER(KV), C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
@@ -196,9 +196,9 @@ def dg_denoise_step(ctx, kv: KV, canvas, resid_in, L, layer_begin, layer_end, hi
                                   _stream(stream)))
 
 
-def dg_mixed_forward(ctx, kv: KV, tokens, append, L, hidden_out, ws, stream=None):
-    _check(load().dg_mixed_forward(ctx, C.byref(kv), _ptr(tokens), _ptr(append), L, _ptr(hidden_out), _ptr(ws),
-                                   ws.numel() * ws.element_size(), _stream(stream)))
+def dg_mixed_forward(ctx, kv: KV, tokens, append, L, hidden_out, ws, stream=None, resid_out=None):
+    _check(load().dg_mixed_forward(ctx, C.byref(kv), _ptr(tokens), _ptr(append), L, _ptr(hidden_out),
+                                   _ptr(resid_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def dg_step_sample(ctx, hidden, canvas, lock, n_locked, done, batch, L, params: StepParams, ws, stream=None):

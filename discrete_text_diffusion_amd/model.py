@@ -111,11 +111,12 @@ class Model:
         dg.dg_denoise_step(self.ctx, self.kv_struct, canvas, resid_in, L, layer_begin, le, hidden_out, resid_out,
                            ws, stream)
 
-    def mixed_forward(self, tokens, append, hidden_out, ws, stream=None):
+    def mixed_forward(self, tokens, append, hidden_out, ws, stream=None, resid_out=None):
         """One pass over canvases of two kinds: append[b] != 0 (device int32 [B]) encodes canvas b
         causally into the cache (its device prefix length grows by L), the others take the
         bidirectional denoising pass."""
-        dg.dg_mixed_forward(self.ctx, self.kv_struct, tokens, append, tokens.shape[1], hidden_out, ws, stream)
+        dg.dg_mixed_forward(self.ctx, self.kv_struct, tokens, append, tokens.shape[1], hidden_out, ws, stream,
+                            resid_out)
         self._grew(tokens.shape[1], known=False)
 
     def step_sample(self, hidden, canvas, lock, n_locked, params: dg.StepParams, ws, done=None, stream=None):

@@ -230,10 +230,11 @@ dg_status dg_denoise_step(dg_ctx *ctx, const dg_kv *kv, const int32_t *canvas,
  * canvas, its cache untouched.  Every row then runs the MoE FFN of every layer; hidden_out
  * [batch*L][d] act = RMSNorm(residual) * final_norm for all rows (for an append canvas, the causal
  * encoder's output).  Pass `append` as dg_step_sample's `done` to step only the denoising
- * canvases.  The global-layer caches need cap >= max_prefix + L. */
+ * canvases.  resid_out (nullable, [batch*L][d] fp32) receives the residual before the final norm.
+ * The global-layer caches need cap >= max_prefix + L. */
 dg_status dg_mixed_forward(dg_ctx *ctx, const dg_kv *kv, const int32_t *tokens,
-                           const int32_t *append, int32_t L, void *hidden_out, void *ws,
-                           size_t ws_bytes, hipStream_t stream);
+                           const int32_t *append, int32_t L, void *hidden_out, float *resid_out,
+                           void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Fused LM head + Step: logits = hidden [batch*L][d] . embed^T are streamed through an online
  * max / sum-exp / Philox-Gumbel argmax and never stored; then every position of canvas

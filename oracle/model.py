@@ -314,7 +314,7 @@ def prefill(cfg, W, kv, prefix_len, tokens):
     return kv, [p + n for p in prefix_len]
 
 
-def mixed_forward(cfg, W, kv, prefix_len, tokens, append):
+def mixed_forward(cfg, W, kv, prefix_len, tokens, append, with_resid=False):
     """One pass over a batch whose canvases take different passes [TR §CPU-GPU 동기화 제거: denoising
     steps and KV-cache updates share a batch, told apart by a per-sequence causal flag].
 
@@ -322,7 +322,8 @@ def mixed_forward(cfg, W, kv, prefix_len, tokens, append):
     attention to its cache and itself; its keys and values written to its caches); false: the
     bidirectional decoder pass of `denoise_forward` (its cache untouched).  Every row runs every
     layer's FFN.  Canvases share nothing but the weights, so each canvas's result is that of its
-    own pass run alone.  Returns (H [B*n][d] = stored(RMSNorm(resid) * g_final), new caches)."""
+    own pass run alone.  Returns (H [B*n][d] = stored(RMSNorm(resid) * g_final), new caches); with
+    `with_resid` also the residual before the final norm."""
     rnd = rounder(cfg.act_dtype)
     tokens = np.asarray(tokens)
     B, n = tokens.shape
@@ -354,4 +355,4 @@ def mixed_forward(cfg, W, kv, prefix_len, tokens, append):
         f, _ = moe(cfg, a2, lw, rnd)
         h = h + f
     H = rnd(rmsnorm(h, W["final_norm"], cfg.norm_eps))
-    return H, kv
+    return (H, kv, h) if with_resid else (H, kv)
