@@ -200,6 +200,11 @@ hipError_t launch_eb_select(EbArgs a, hipStream_t s);
 hipError_t launch_init_canvas(int32_t* canvas, uint8_t* lock, int B, int L, int V, uint32_t k0,
                               uint32_t k1, hipStream_t s);
 
+// Static device scratch of dg_step_sample_noalloc: STATIC_SCRATCH_BYTES per device, 256-byte aligned.
+// static_scratch returns the current device's copy (its address is looked up once per device).
+constexpr size_t STATIC_SCRATCH_BYTES = size_t(2) << 20;
+hipError_t static_scratch(void** out);
+
 // Continuous block-AR scheduling: one sequence per block, after each pass (or, with init, before the
 // first).  A sequence is denoising canvas k at step s, appending its finished canvas, or finished.
 enum SeqPhase : int32_t { SEQ_DENOISE = 0, SEQ_APPEND = 1, SEQ_FINISHED = 2 };

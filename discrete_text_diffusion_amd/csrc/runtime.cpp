@@ -492,9 +492,20 @@ dg_status check_rows(int B, int L) {
   return DG_OK;
 }
 
+// Where the fused sampler and the Step keep their scratch: the status word, per-row statistics and
+// the per-(slice, row) partials.
+struct SampScratch {
+  int* status;
+  float* stats;
+  float* part;
+};
+SampScratch samp_scratch(void* ws, const Layout& w) {
+  return {at<int>(ws, w.status), at<float>(ws, w.stats), at<float>(ws, w.samp_part)};
+}
+
 dg_status sample_into(dg_ctx* c, const void* hidden, int32_t* canvas, uint8_t* lock, int32_t* n_locked,
-                      const int32_t* done, int B, int L, const dg_step_params* p, float lam, void* ws,
-                      const Layout& w, int32_t* steps_taken, int32_t* done_out, hipStream_t s,
+                      const int32_t* done, int B, int L, const dg_step_params* p, float lam, const SampScratch& sc,
+                      int32_t* steps_taken, int32_t* done_out, hipStream_t s,
                       const uint32_t* canvas_rng = nullptr, const float* lam_table = nullptr) {
   const dg_model_desc& d = c->d;
   const int R = B * L;
@@ -504,7 +515,7 @@ dg_status sample_into(dg_ctx* c, const void* hidden, int32_t* canvas, uint8_t* l
   sa.zscale_log2 = (float)(1.4426950408889634 / (double)p->tau);
   sa.k0 = key0(p->seed); sa.k1 = key1(p->seed); sa.step = p->step;
   sa.slices = sampler_slices(d, R, &sa.v_per_slice);
-  sa.part = at<float>(ws, w.samp_part);
+  sa.part = sc.part;
   sa.canvas_rng = canvas_rng;
   {
     ProfScope ps(c, DG_PROF_SAMPLER, s);
@@ -515,7 +526,7 @@ dg_status sample_into(dg_ctx* c, const void* hidden, int32_t* canvas, uint8_t* l
   st.B = B; st.L = L; st.canvas = canvas; st.lock = lock; st.n_locked = n_locked; st.done = done;
   st.lam = lam; st.theta = p->lock_threshold;
   st.k0 = sa.k0; st.k1 = sa.k1; st.step = p->step;
-  st.stats = at<float>(ws, w.stats); st.status = at<int>(ws, w.status);
+  st.stats = sc.stats; st.status = sc.status;
   st.steps_taken = steps_taken; st.done_out = done_out;
   st.canvas_rng = canvas_rng; st.lam_table = lam_table;
   HIPCHK(launch_step_merge(st, s));
@@ -805,7 +816,38 @@ dg_status dg_step_sample(dg_ctx* ctx, const void* hidden, int32_t* canvas, uint8
   if ((st = check_ws(ctx, ws, ws_bytes, batch, L, 0)) != DG_OK) return st;
   const Layout w = layout(ctx->d, batch, L, 0);
   return sample_into(ctx, hidden, canvas, lock, n_locked, done, batch, L, params,
-                     jump_prob(params->schedule, params->t, params->h), ws, w, nullptr, nullptr, stream);
+                     jump_prob(params->schedule, params->t, params->h), samp_scratch(ws, w), nullptr, nullptr,
+                     stream);
+}
+
+dg_status dg_step_sample_noalloc(dg_ctx* ctx, const void* hidden, int32_t* canvas, uint8_t* lock, int32_t* n_locked,
+                                 const int32_t* done, int32_t batch, int32_t L, const dg_step_params* params,
+                                 hipStream_t stream) {
+  g_err.clear();
+  if (!ctx || !hidden || !canvas || !lock) return fail(DG_EINVAL, "NULL argument");
+  if (!ctx->embed) return fail(DG_EINVAL, "the LM head needs the embedding");
+  dg_status st = check_step_params(params);
+  if (st != DG_OK) return st;
+  if ((st = check_rows(batch, L)) != DG_OK) return st;
+  // the status word, the per-row statistics and the partials of every (vocabulary slice, row)
+  const size_t R = (size_t)batch * L;
+  int vps;
+  const int slices = sampler_slices(ctx->d, (int)R, &vps);
+  const size_t o_stats = up(256), o_part = o_stats + up(R * STAT_FIELDS * 4);
+  const size_t need = o_part + up((size_t)slices * R * SAMPLER_PART * 4);
+  if (need > STATIC_SCRATCH_BYTES)
+    return fail(DG_EUNSUPPORTED, "%d x %d rows need %zu bytes of static scratch, more than its %zu; use dg_step_sample",
+                batch, L, need, STATIC_SCRATCH_BYTES);
+  void* base = nullptr;
+  HIPCHK(static_scratch(&base));
+  char* b = static_cast<char*>(base);
+  const SampScratch sc{reinterpret_cast<int*>(b), reinterpret_cast<float*>(b + o_stats),
+                       reinterpret_cast<float*>(b + o_part)};
+  // the array keeps the previous call's contents: the status word starts from zero (a fill kernel);
+  // statistics and partials are written in full before they are read
+  HIPCHK(launch_fill_i32(sc.status, 0, 64, stream));
+  return sample_into(ctx, hidden, canvas, lock, n_locked, done, batch, L, params,
+                     jump_prob(params->schedule, params->t, params->h), sc, nullptr, nullptr, stream);
 }
 
 // dg_canvas_run with the entropy-bounded sampler
@@ -908,8 +950,8 @@ dg_status dg_canvas_run(dg_ctx* ctx, const dg_kv* kv, int32_t* canvas, uint8_t* 
     sp.step = (uint32_t)s;
     // the jump probability is taken at the double-precision grid point t_s = 1 - s/T
     if ((st = sample_into(ctx, at<void>(ws, w.hidden), canvas, lock, at<int32_t>(ws, w.n_locked),
-                          p->adaptive ? done : nullptr, B, L, &sp, jump_prob(p->schedule, t, h), ws, w, steps_taken,
-                          p->adaptive ? done : nullptr, stream)) != DG_OK)
+                          p->adaptive ? done : nullptr, B, L, &sp, jump_prob(p->schedule, t, h), samp_scratch(ws, w),
+                          steps_taken, p->adaptive ? done : nullptr, stream)) != DG_OK)
       return st;
     if (p->adaptive) HIPCHK(launch_all_set(done, B, all_done, stream));
   }
@@ -1002,7 +1044,7 @@ dg_status dg_generate_continuous(dg_ctx* ctx, const dg_kv* kv, int32_t* out, int
       if ((st = mixed_pass(ctx, &run, sa.cur, append, L, at<void>(ws, w.hidden), nullptr, ws, w, stream)) != DG_OK)
         return st;
       if ((st = sample_into(ctx, at<void>(ws, w.hidden), sa.cur, sa.lock, at<int32_t>(ws, w.n_locked), skip, B, L,
-                            &sp, 0.f, ws, w, nullptr, nullptr, stream, sa.rng, lam_dev)) != DG_OK)
+                            &sp, 0.f, samp_scratch(ws, w), nullptr, nullptr, stream, sa.rng, lam_dev)) != DG_OK)
         return st;
       HIPCHK(launch_seq_schedule(sa, stream));
       HIPCHK(launch_all_set(finished, B, all_done, stream));

@@ -82,6 +82,8 @@ EXPORTS = {
                                    C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "dg_step_sample": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                  C.c_int32, C.c_int32, C.POINTER(StepParams), C.c_void_p, C.c_size_t, C.c_void_p]),
+    "dg_step_sample_noalloc": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                         C.c_int32, C.c_int32, C.POINTER(StepParams), C.c_void_p]),
     "dg_canvas_run": (C.c_int, [C.c_void_p, C.POINTER(KV), C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
                                 C.POINTER(RunParams), C.c_void_p, C.c_size_t, C.c_void_p]),
     "dg_jump_prob": (C.c_float, [C.c_int, C.c_float, C.c_float]),
@@ -204,6 +206,11 @@ def dg_mixed_forward(ctx, kv: KV, tokens, append, L, hidden_out, ws, stream=None
 def dg_step_sample(ctx, hidden, canvas, lock, n_locked, done, batch, L, params: StepParams, ws, stream=None):
     _check(load().dg_step_sample(ctx, _ptr(hidden), _ptr(canvas), _ptr(lock), _ptr(n_locked), _ptr(done), batch, L,
                                  C.byref(params), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def dg_step_sample_noalloc(ctx, hidden, canvas, lock, n_locked, done, B, L, params: StepParams, stream=None):
+    _check(load().dg_step_sample_noalloc(ctx, _ptr(hidden), _ptr(canvas), _ptr(lock), _ptr(n_locked), _ptr(done),
+                                         B, L, C.byref(params), _stream(stream)))
 
 
 def dg_canvas_run(ctx, kv: KV, canvas, lock, steps_taken, L, params: RunParams, ws, stream=None):

@@ -247,6 +247,18 @@ dg_status dg_step_sample(dg_ctx *ctx, const void *hidden, int32_t *canvas, uint8
                          const dg_step_params *params, void *ws, size_t ws_bytes,
                          hipStream_t stream);
 
+/* dg_step_sample for callers that cannot allocate device memory or hand over a workspace (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): the same kernels and
+ * outputs, with the scratch (status word, per-row statistics, vocabulary-slice partials, about 1.6 MB
+ * for up to 16,384 rows) in a static array of 2 MiB that the library holds on every GPU it runs on
+ * until the process ends.  Nothing is allocated.  Shapes whose scratch exceeds 2 MiB are rejected with
+ * DG_EUNSUPPORTED before anything is enqueued.  Every call on one GPU shares that GPU's array, so calls
+ * that overlap on one GPU (two streams, two threads) race; calls in order on one stream do not.
+ * A non-finite statistic shows as n_locked[b] = -1 (there is no workspace status word to query). */
+dg_status dg_step_sample_noalloc(dg_ctx *ctx, const void *hidden, int32_t *canvas, uint8_t *lock,
+                                 int32_t *n_locked, const int32_t *done, int32_t batch, int32_t L,
+                                 const dg_step_params *params, hipStream_t stream);
+
 /* One entropy-bounded step (see dg_eb_params) from final-normed hidden states [batch*L][d]:
  * the fused LM head accumulates argmax, Gumbel-max draw and entropy in one pass over the
  * vocabulary, then one block per canvas selects.  canvas device int32 [batch][L] (out for

@@ -162,3 +162,24 @@ def test_validation_enqueues_nothing_on_bad_calls():
         assert e.value.status == dg.DG_EWORKSPACE
     finally:
         dg.dg_destroy(ctx)
+
+
+def test_noalloc_step_rejects_shapes_beyond_its_static_scratch():
+    """dg_step_sample_noalloc keeps its scratch in a 2 MiB static array: 64 canvases of 1024 rows
+    need more (statistics and partials of 65,536 rows), so the call fails on the host with
+    DG_EUNSUPPORTED before any HIP call (no GPU needed to see it)."""
+    cfg = configs.C0
+    ctx, keep = _ctx_with_fake_pointers(cfg)
+    try:
+        p = dg.StepParams(schedule=0, t=1.0, h=0.25, tau=1.0, lock_threshold=0.9, seed=0, step=0)
+        t = _FakeTensor(0x7000, 16)
+        with pytest.raises(dg.DGError) as e:
+            dg.dg_step_sample_noalloc(ctx, t, t, t, t, None, 64, 1024, p, 0)
+        assert e.value.status == dg.DG_EUNSUPPORTED
+        assert "static scratch" in str(e.value)
+        # bad arguments are caught first, as for dg_step_sample
+        with pytest.raises(dg.DGError) as e:
+            dg.dg_step_sample_noalloc(ctx, t, t, None, t, None, 1, 32, p, 0)
+        assert e.value.status == dg.DG_EINVAL
+    finally:
+        dg.dg_destroy(ctx)
