@@ -16,5 +16,7 @@ Parity status per function:
   model.denoise_layer / denoise_forward
                          pinned by zero-weight reductions to independently written attention and
                          MoE expectations (pre-norm composition, both residual adds)
+  selfcond               pinned by closed forms (argmax row at low temperature, mean row at equal
+                         logits), an explicit loop, relabelling invariance and the zero-signal loop
   everything else        pinned by closed forms, invariants or brute force in tests/test_oracle_*.py
 """

@@ -247,11 +247,12 @@ def denoise_layer(cfg, layer, h, lw, K, V, prefix_len, rnd, forced_idx=None):
     return h + f, info
 
 
-def denoise_forward(cfg, W, kv, prefix_len, canvas=None, resid_in=None, n_layers=None):
-    """Decoder pass over the canvases (self-conditioning input s = 0).
+def denoise_forward(cfg, W, kv, prefix_len, canvas=None, resid_in=None, n_layers=None, sc=None):
+    """Decoder pass over the canvases.
 
     W: {"embed": [V][d] | None, "final_norm": [d], "layers": [layer_arrays ...]};
-    kv: per layer (K, V) float64 [B][Hkv][cap][dh]; canvas: int [B][L] or resid_in [B*L][d].
+    kv: per layer (K, V) float64 [B][Hkv][cap][dh]; canvas: int [B][L] or resid_in [B*L][d];
+    sc: the self-conditioning signal s_t [B*L][d], added to the embedded canvas (None: s = 0).
     Returns (H, resid): H = stored(RMSNorm(resid) * g_final), resid = pre-norm residual.
     Reading: the embedding is a plain row lookup of the tied matrix (no sqrt(d) scale)."""
     rnd = rounder(cfg.act_dtype)
@@ -259,6 +260,8 @@ def denoise_forward(cfg, W, kv, prefix_len, canvas=None, resid_in=None, n_layers
         h = np.asarray(resid_in, dtype=np.float64).copy()
     else:
         h = W["embed"][np.asarray(canvas).reshape(-1)].astype(np.float64)
+        if sc is not None:
+            h = h + np.asarray(sc, np.float64)
     nl = cfg.n_layers if n_layers is None else n_layers
     for l in range(nl):
         h, _ = denoise_layer(cfg, l, h, W["layers"][l], kv[l][0], kv[l][1], prefix_len, rnd)

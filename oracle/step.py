@@ -151,12 +151,14 @@ def step_from_logits(z32, canvas, lock, t, h, schedule, theta, seed, s, done=Non
 
 
 def canvas_run(cfg, W, kv, prefix_len, forward, canvas=None, lock=None, steps=None,
-               tau=None, theta=None, schedule=None, adaptive=None, seed=None):
+               tau=None, theta=None, schedule=None, adaptive=None, seed=None, self_cond=None):
     """The denoising loop for one block of canvases.
 
-    `forward(canvas) -> H` is the decoder pass.  At t = 1 the canvas is drawn uniform (unless
-    given).  For s = 0..T-1: canvases that are done are skipped, the rest take one Step at t_s;
-    with adaptive stopping a canvas is done once all its positions are locked.
+    `forward(canvas) -> H` is the decoder pass; with `self_cond` (a function H -> s) it is called
+    as forward(canvas, s) with s = None at the first step and s = self_cond(H) of the previous
+    step afterwards [TR §디노이징 반복과 self-conditioning].  At t = 1 the canvas is drawn uniform
+    (unless given).  For s = 0..T-1: canvases that are done are skipped, the rest take one Step at
+    t_s; with adaptive stopping a canvas is done once all its positions are locked.
     Returns canvas, lock, steps_taken[B]."""
     B, L = cfg.batch, cfg.canvas
     T = cfg.steps if steps is None else steps
@@ -173,10 +175,13 @@ def canvas_run(cfg, W, kv, prefix_len, forward, canvas=None, lock=None, steps=No
     done = np.zeros(B, dtype=bool)
     taken = np.zeros(B, dtype=np.int64)
     ts, h = time_grid(T)
+    sc = None
     for s, t in enumerate(ts):
         if adaptive and done.all():
             break
-        H = forward(canvas)
+        H = forward(canvas) if self_cond is None else forward(canvas, sc)
+        if self_cond is not None:
+            sc = self_cond(H)
         canvas, lock, nl, _, _ = step(H, W["embed"], canvas, lock, t, h, schedule, tau, theta, seed, s,
                                       done if adaptive else None)
         taken += ~done if adaptive else 1
