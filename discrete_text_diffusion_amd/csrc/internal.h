@@ -103,8 +103,12 @@ constexpr int FLASH_QROWS = 16 * FLASH_QPW * FLASH_WAVES;
 hipError_t launch_attn_merge(const AttnArgs& a, int act_bf16, hipStream_t s);
 
 // ---- elementwise / small kernels -------------------------------------------------------------
+// resid[r] = embed[tokens[r]] (+ add[r] when add is non-null: the self-conditioning signal)
 hipError_t launch_embed(const int32_t* tokens, const void* embed, float* resid, int rows, int d,
-                        int vocab, int act_bf16, hipStream_t s);
+                        int vocab, int act_bf16, hipStream_t s, const float* add = nullptr);
+// out[i] = act(sum over nparts of parts[p * pstride + i]), parts summed in order
+hipError_t launch_sum_parts_cast(const float* parts, int nparts, int64_t pstride, void* out, int64_t n, int act_bf16,
+                                 hipStream_t s);
 hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
 hipError_t launch_rmsnorm(const float* x, const void* g, void* y, int rows, int d, float eps,
                           int act_bf16, int* status, hipStream_t s);
@@ -151,12 +155,22 @@ struct SampArgs {
   int slices, v_per_slice;        // vocabulary split
   float* part;                    // [slices][rows][6] partial (m2, s, a, g2, y, w) as floats/ints
   const uint32_t* canvas_rng;     // device [B][4] (k0, k1, step, -) per canvas, or null: k0, k1, step
+  void* pmat;                     // or null: [rows][V] act, 2^(z2 - the row's max over its vocabulary tile)
+  float* ptile;                   // with pmat: [rows][n_vtiles] those tile maxima (log2 units)
+  int n_vtiles;                   // vocabulary tiles of the sampler (V / its tile width, rounded up)
   const int32_t* gate;            // launch gate (set by the launcher)
 };
 hipError_t launch_lmhead_sampler(const SampArgs& a, int act_bf16, hipStream_t s);
+// vocabulary tile width of the fused sampler for the activation dtype
+inline int sampler_bn(int act_bf16) { return act_bf16 ? 256 : 128; }
+// p_hat_0 in place: P[r][v] *= 2^(ptile[r][v / bn] - lse2[r]), lse2 = log2 of the row's partition sum
+// (from the merged statistics: m * log2(e) - log2(c))
+hipError_t launch_p_rescale(void* P, const float* ptile, const float* stats, int rows, int V, int bn, int n_vtiles,
+                            int act_bf16, hipStream_t s);
 // fused LM head tiles: rows x vocabulary entries per block step (bf16: 256 x 256 on 8 waves of 32
 // rows, so a 256-row canvas is one row tile and every embedding tile streams once)
 constexpr int SAMPLER_BM_BF16 = 256, SAMPLER_BN_BF16 = 256, SAMPLER_BM_F32 = 128, SAMPLER_BN_F32 = 128;
+static_assert(SAMPLER_BN_BF16 == 256 && SAMPLER_BN_F32 == 128, "sampler_bn");
 constexpr int SAMPLER_PART = 6;   // floats per (row, slice) partial: m2, s, a, g2, y, w
 hipError_t launch_logits_partials(const float* z, int rows, int V, int L, float zscale_log2,
                                   uint32_t k0, uint32_t k1, uint32_t step, int slices,
@@ -218,6 +232,8 @@ struct SeqArgs {
   int32_t* out; int32_t* steps;   // [K][B][L] finished canvases, [K][B] their steps (or null)
   int32_t* append; int32_t* skip; int32_t* finished;  // [B] flags for the next pass
   int32_t* passes;                // [1] passes that ran (or null)
+  float* sc; int d;               // [B*L][d] self-conditioning signal (or null): cleared for canvases whose
+                                  // next pass appends or starts a canvas
   const int32_t* gate;            // set by the launcher
 };
 hipError_t launch_seq_schedule(SeqArgs a, hipStream_t s);

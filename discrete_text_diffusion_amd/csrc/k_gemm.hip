@@ -422,6 +422,12 @@ static hipError_t dense_pick(const DenseArgs& a, int n_eff, hipStream_t s) {
   } else {
     if (small) return launch_dense_t<TA, TB, 64, 64, 2, 2, EPI, MAP>(a, n_eff, s);
     if (a.N <= 256) return launch_dense_t<TA, TB, 64, 32, 4, 1, EPI, MAP>(a, n_eff, s);
+    if constexpr (sizeof(TB) == 2) {
+      // a vocabulary-long contraction (the self-conditioning product, K = V) over one canvas: every
+      // row in one 256 x 256 tile of 8 waves, split over K, so each K slice of the probabilities is
+      // read once per 256 output columns and the embedding once
+      if (a.K >= 16384 && a.M <= 256) return launch_dense_t<TA, TB, 256, 256, 2, 4, EPI, MAP, 2>(a, n_eff, s);
+    }
     if (a.M > 256) {
       // bf16 weights: 128 x 192 tiles on 8 waves (64 x 48 per wave): at 2048 x 2816 (the attention
       // output projection of 8 canvases) 240 blocks where 256 x 128 tiles give 176 of 256 CUs

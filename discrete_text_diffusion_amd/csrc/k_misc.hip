@@ -15,21 +15,46 @@ GateScope::GateScope(const int32_t* gate) : prev(t_gate) { t_gate = gate; }
 GateScope::~GateScope() { t_gate = prev; }
 
 template <class T>
-__global__ void embed_kernel(const int32_t* tok, const T* E, float* resid, int d, int V, const int32_t* gate) {
+__global__ void embed_kernel(const int32_t* tok, const T* E, float* resid, int d, int V, const float* add,
+                             const int32_t* gate) {
   if (gate_closed(gate)) return;
   const int r = blockIdx.x;
   const int t = min(max(tok[r], 0), V - 1);     // out-of-range ids are clamped, never read past E
   const T* src = E + (int64_t)t * d;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) resid[(int64_t)r * d + c] = Elem<T>::to_f(src[c]);
+  for (int c = threadIdx.x; c < d; c += blockDim.x)
+    resid[(int64_t)r * d + c] = Elem<T>::to_f(src[c]) + (add ? add[(int64_t)r * d + c] : 0.f);
 }
 
 hipError_t launch_embed(const int32_t* tok, const void* E, float* resid, int rows, int d, int V, int bf,
-                        hipStream_t s) {
+                        hipStream_t s, const float* add) {
   if (bf)
-    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(rows), dim3(256), 0, s, tok, (const bf16_t*)E, resid, d, V,
+    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(rows), dim3(256), 0, s, tok, (const bf16_t*)E, resid, d, V, add,
                        launch_gate());
   else
-    hipLaunchKernelGGL(embed_kernel<float>, dim3(rows), dim3(256), 0, s, tok, (const float*)E, resid, d, V,
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(rows), dim3(256), 0, s, tok, (const float*)E, resid, d, V, add,
+                       launch_gate());
+  return hipGetLastError();
+}
+
+template <class T>
+__global__ void sum_parts_cast_kernel(const float* parts, int nparts, int64_t pstride, T* out, int64_t n,
+                                      const int32_t* gate) {
+  if (gate_closed(gate)) return;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float a = 0.f;
+  for (int q = 0; q < nparts; ++q) a += parts[q * pstride + i];
+  out[i] = Elem<T>::from_f(a);
+}
+
+hipError_t launch_sum_parts_cast(const float* parts, int nparts, int64_t pstride, void* out, int64_t n, int bf,
+                                 hipStream_t s) {
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (bf)
+    hipLaunchKernelGGL(sum_parts_cast_kernel<bf16_t>, grid, dim3(256), 0, s, parts, nparts, pstride, (bf16_t*)out, n,
+                       launch_gate());
+  else
+    hipLaunchKernelGGL(sum_parts_cast_kernel<float>, grid, dim3(256), 0, s, parts, nparts, pstride, (float*)out, n,
                        launch_gate());
   return hipGetLastError();
 }

@@ -18,6 +18,7 @@
 namespace dg {
 
 constexpr float LN2 = 0.69314718055994531f;
+constexpr float LOG2E_F = 1.44269504088896341f;
 // G * log2(e) = -log2(-log2(u)) - log2(ln 2)
 constexpr float NEG_LOG2_LN2 = 0.52876637294904302f;
 constexpr int PART = SAMPLER_PART;  // m2, s, a, g2, y, w
@@ -79,8 +80,10 @@ DG_DEV float gumbel_key2(float z2, uint32_t w) { return gumbel_key2_nc(z2, w) + 
 // it, the argmax and the best Gumbel key with shuffles, and one lane merges the result into the
 // wave's running state of that row, which lives in LDS (the registers hold only the
 // accumulators); the WN states of a row are merged in wave order at the end.
-// PCR: each canvas takes its own Philox key and step index from p.canvas_rng
-template <class TA, int BM, int BN, int WM, int WN, int NS, bool PCR>
+// PCR: each canvas takes its own Philox key and step index from p.canvas_rng.  PW: the tile's
+// probabilities relative to each row's tile maximum, 2^(z2 - max), go to p.pmat (for the
+// self-conditioning product), the maxima to p.ptile.
+template <class TA, int BM, int BN, int WM, int WN, int NS, bool PCR, bool PW>
 __global__ __launch_bounds__(WM * WN * 64) void lmhead_sampler_kernel(SampArgs p, int n_mt) {
   if (gate_closed(p.gate)) return;
   using G = GemmDma<TA, BM, BN, WM, WN, NS>;
@@ -187,6 +190,15 @@ __global__ __launch_bounds__(WM * WN * 64) void lmhead_sampler_kernel(SampArgs p
       float ss[4] = {0.f, 0.f, 0.f, 0.f}, ww[4] = {0.f, 0.f, 0.f, 0.f};
       float g2[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       int yy[4] = {0x7fffffff, 0x7fffffff, 0x7fffffff, 0x7fffffff};
+      TA* prow[4];
+      if constexpr (PW) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = m0 + G::row_of(i, e);
+          prow[e] = row < p.rows ? static_cast<TA*>(p.pmat) + (int64_t)row * p.V : nullptr;
+          if (prow[e] && l16 == 0) p.ptile[(int64_t)row * p.n_vtiles + v0 / BN] = rm[e];
+        }
+      }
 #pragma unroll
       for (int j = 0; j < G::FN; ++j) {
         const int v = v0 + G::col_of(j);
@@ -198,6 +210,9 @@ __global__ __launch_bounds__(WM * WN * 64) void lmhead_sampler_kernel(SampArgs p
             const float z = acc[i][j][e];
             const float dz = z - rm[e];
             const float ex = __builtin_amdgcn_exp2f(dz);   // dz <= 0; terms below 2^-126 do not count
+            if constexpr (PW) {
+              if (prow[e]) prow[e][v] = Elem<TA>::from_f(ex);
+            }
             ss[e] += ex;
             ww[e] += ex * dz;
             const float key = gumbel_key2_nc(z, wd[e]);
@@ -242,25 +257,59 @@ __global__ __launch_bounds__(WM * WN * 64) void lmhead_sampler_kernel(SampArgs p
   }
 }
 
-template <class TA, int BM, int BN, int WM, int WN, int NS, bool PCR>
+template <class TA, int BM, int BN, int WM, int WN, int NS, bool PCR, bool PW>
 static hipError_t launch_sampler_p(const SampArgs& a, hipStream_t s) {
   using G = GemmDma<TA, BM, BN, WM, WN, NS>;
   const int n_mt = (a.rows + BM - 1) / BM;
   const int blocks = n_mt * ((a.slices + 7) / 8 * 8);
   const size_t lds = G::LDS_BYTES + (size_t)WN * BM * PART * 4;
   if (a.d % G::KT) return hipErrorInvalidValue;
-  static const hipError_t attr = allow_lds(lmhead_sampler_kernel<TA, BM, BN, WM, WN, NS, PCR>, lds);
+  if (PW && (a.v_per_slice % BN || a.n_vtiles != (a.V + BN - 1) / BN)) return hipErrorInvalidValue;
+  static const hipError_t attr = allow_lds(lmhead_sampler_kernel<TA, BM, BN, WM, WN, NS, PCR, PW>, lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((lmhead_sampler_kernel<TA, BM, BN, WM, WN, NS, PCR>), dim3(blocks), dim3(WM * WN * 64), lds, s,
-                     a, n_mt);
+  hipLaunchKernelGGL((lmhead_sampler_kernel<TA, BM, BN, WM, WN, NS, PCR, PW>), dim3(blocks), dim3(WM * WN * 64), lds,
+                     s, a, n_mt);
   return hipGetLastError();
 }
 
 template <class TA, int BM, int BN, int WM, int WN, int NS>
 static hipError_t launch_sampler_t(SampArgs a, hipStream_t s) {
   a.gate = launch_gate();
-  if (a.canvas_rng) return launch_sampler_p<TA, BM, BN, WM, WN, NS, true>(a, s);
-  return launch_sampler_p<TA, BM, BN, WM, WN, NS, false>(a, s);
+  if (a.pmat) {
+    if (a.canvas_rng) return launch_sampler_p<TA, BM, BN, WM, WN, NS, true, true>(a, s);
+    return launch_sampler_p<TA, BM, BN, WM, WN, NS, false, true>(a, s);
+  }
+  if (a.canvas_rng) return launch_sampler_p<TA, BM, BN, WM, WN, NS, true, false>(a, s);
+  return launch_sampler_p<TA, BM, BN, WM, WN, NS, false, false>(a, s);
+}
+
+// p_hat_0 = 2^(z2 - lse2): each thread rescales 8 consecutive probabilities of one row (one tile)
+template <class T>
+__global__ void p_rescale_kernel(T* P, const float* ptile, const float* stats, int V, int bn, int n_vtiles,
+                                 const int32_t* gate) {
+  if (gate_closed(gate)) return;
+  const int r = blockIdx.y;
+  const int v0 = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (v0 >= V) return;
+  const float* st = stats + (size_t)r * STAT_FIELDS;
+  const float lse2 = st[0] * LOG2E_F - __log2f(st[2]);      // m2 + log2(sum): c = 1 / sum
+  const float f = exp2f(ptile[(size_t)r * n_vtiles + v0 / bn] - lse2);
+  T* q = P + (size_t)r * V + v0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) q[e] = Elem<T>::from_f(Elem<T>::to_f(q[e]) * f);
+}
+
+hipError_t launch_p_rescale(void* P, const float* ptile, const float* stats, int rows, int V, int bn, int n_vtiles,
+                            int bf, hipStream_t s) {
+  if (V % 8 || bn % 8) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((V / 8 + 255) / 256), (unsigned)rows);
+  if (bf)
+    hipLaunchKernelGGL(p_rescale_kernel<bf16_t>, grid, dim3(256), 0, s, (bf16_t*)P, ptile, stats, V, bn, n_vtiles,
+                       launch_gate());
+  else
+    hipLaunchKernelGGL(p_rescale_kernel<float>, grid, dim3(256), 0, s, (float*)P, ptile, stats, V, bn, n_vtiles,
+                       launch_gate());
+  return hipGetLastError();
 }
 
 // tiles: bf16 256 rows x 256 vocabulary entries on 8 waves of 32 rows (a row's statistics stay
@@ -560,7 +609,7 @@ hipError_t launch_noise(const int32_t* x0, int32_t* xt, int B, int L, int V, flo
 __global__ __launch_bounds__(256) void seq_schedule_kernel(SeqArgs a) {
   if (gate_closed(a.gate)) return;
   const int b = blockIdx.x;
-  __shared__ int sh_copy, sh_fresh, sh_k;
+  __shared__ int sh_copy, sh_fresh, sh_k, sh_phase;
   if (threadIdx.x == 0) {
     int32_t* st = a.state + 4 * b;
     int phase = SEQ_DENOISE, k = 0, s = 0, taken = 0, copy = -1, fresh = 1;
@@ -591,11 +640,16 @@ __global__ __launch_bounds__(256) void seq_schedule_kernel(SeqArgs a) {
     a.skip[b] = phase != SEQ_DENOISE;
     a.finished[b] = phase == SEQ_FINISHED;
     if (b == 0 && a.passes) a.passes[0] = a.init ? 0 : a.passes[0] + 1;
-    sh_copy = copy; sh_fresh = fresh; sh_k = k;
+    sh_copy = copy; sh_fresh = fresh; sh_k = k; sh_phase = phase;
   }
   __syncthreads();
   const int copy = sh_copy, k = sh_k;
   int32_t* cur = a.cur + (int64_t)b * a.L;
+  if (a.sc && (sh_phase != SEQ_DENOISE || sh_fresh)) {
+    // the encoder pass of an appended canvas and the first step of a new one take no signal
+    float* sc = a.sc + (int64_t)b * a.L * a.d;
+    for (int64_t i = threadIdx.x; i < (int64_t)a.L * a.d; i += blockDim.x) sc[i] = 0.f;
+  }
   if (copy >= 0)
     for (int i = threadIdx.x; i < a.L; i += blockDim.x) a.out[((int64_t)copy * a.B + b) * a.L + i] = cur[i];
   if (sh_fresh) {

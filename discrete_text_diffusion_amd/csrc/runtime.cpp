@@ -39,6 +39,8 @@ struct dg_ctx {
   std::vector<dg_layer_weights> layers;
   const void* embed;
   const void* final_norm;
+  const void* embed_t;                       // self-conditioning: E transposed, [d][V]
+  const void* sc_gate; const void* sc_up; const void* sc_down;
   Prof* prof;
 };
 
@@ -93,6 +95,17 @@ int sampler_slices(const dg_model_desc& d, int rows, int* v_per_slice) {
   return (d.vocab + *v_per_slice - 1) / *v_per_slice;
 }
 
+// split-K parts of the self-conditioning product p_hat_0 . E (K = the vocabulary): a power of two
+// up to 32 that divides the K tiles and keeps the block count near 512
+int sc_splits(const dg_model_desc& d, int R) {
+  const int kt = d.act_dtype == DG_BF16 ? 64 : 32;
+  const int ktiles = d.vocab / kt;
+  const int blocks = ((R + 255) / 256) * ((d.d_model + 255) / 256);
+  int s = 1;
+  while (s < 32 && ktiles % (2 * s) == 0 && blocks * 2 * s <= 512) s *= 2;
+  return s;
+}
+
 // Workspace layout.  The inspectable regions (status, stats, routing) come first and depend only
 // on the row count, so the test hooks can find them from `rows` alone.
 struct Layout {
@@ -101,6 +114,7 @@ struct Layout {
   size_t counts, offsets, perm, inv_perm, tok, work, n_items;
   size_t a_grp, y, sh_a, samp_part, hidden, done, n_locked, prev, lockbuf, all_done;
   size_t seq_state, seq_rng, seq_flags, lam_table;
+  size_t sc_p, sc_ptile, sc_parts, sc_x, sc_a, sc_state;   // self-conditioning (sc_hidden > 0)
   size_t total;
   int max_items;
 };
@@ -153,6 +167,15 @@ Layout layout(const dg_model_desc& d, int B, int n, int max_prefix) {
   w.seq_rng = take((size_t)B * 16);
   w.seq_flags = take((size_t)B * 12);     // append, skip, finished
   w.lam_table = take(256 * 4);
+  if (d.sc_hidden > 0) {
+    const int bn = sampler_bn(d.act_dtype == DG_BF16);
+    w.sc_p = take(R * d.vocab * ab);
+    w.sc_ptile = take(R * ((d.vocab + bn - 1) / bn) * 4);
+    w.sc_parts = take((size_t)sc_splits(d, (int)R) * R * d.d_model * 4);
+    w.sc_x = take(R * d.d_model * ab);
+    w.sc_a = take(R * d.sc_hidden * ab);
+    w.sc_state = take(R * d.d_model * 4);
+  }
   w.total = o;
   return w;
 }
@@ -475,6 +498,8 @@ dg_status check_desc(const dg_model_desc& d) {
     return fail(DG_EUNSUPPORTED, "d_model, expert_hidden and shared_hidden must be multiples of 64");
   if (d.d_model > 4096) return fail(DG_EUNSUPPORTED, "d_model %d > 4096", d.d_model);
   if (d.vocab % 16) return fail(DG_EUNSUPPORTED, "vocab %% 16 != 0");
+  if (d.sc_hidden < 0 || d.sc_hidden % 64) return fail(DG_EUNSUPPORTED, "sc_hidden %d not a multiple of 64", d.sc_hidden);
+  if (d.sc_hidden > 0 && d.vocab % 64) return fail(DG_EUNSUPPORTED, "self-conditioning needs vocab %% 64 == 0");
   if (d.n_experts > 256 || d.n_experts % 4 || d.top_k > 16 || d.top_k > d.n_experts)
     return fail(DG_EUNSUPPORTED, "need top_k <= 16, top_k <= n_experts <= 256 and n_experts %% 4 == 0");
   if (d.act_dtype != DG_F32 && d.act_dtype != DG_BF16) return fail(DG_EUNSUPPORTED, "act_dtype must be F32 or BF16");
@@ -503,13 +528,63 @@ SampScratch samp_scratch(void* ws, const Layout& w) {
   return {at<int>(ws, w.status), at<float>(ws, w.stats), at<float>(ws, w.samp_part)};
 }
 
+// The self-conditioning signal s = FFW(p_hat_0 . E) of R rows [TR §디노이징 반복과 self-conditioning],
+// once the fused sampler has written the tile-relative probabilities and the merge the statistics:
+// p_hat_0 in place, the split-K product with E (through its transpose, K-contiguous), the parts
+// summed in order into the block's input, then the gated feed-forward block into sc_out (fp32).
+dg_status self_cond_into(const dg_ctx* c, int R, void* ws, const Layout& w, float* sc_out, hipStream_t s) {
+  const dg_model_desc& d = c->d;
+  const int bf = d.act_dtype == DG_BF16;
+  const int bn = sampler_bn(bf);
+  HIPCHK(launch_p_rescale(at<void>(ws, w.sc_p), at<float>(ws, w.sc_ptile), at<float>(ws, w.stats), R, d.vocab, bn,
+                          (d.vocab + bn - 1) / bn, bf, s));
+  DenseArgs pe{};
+  pe.epi = EPI_STORE_F32;
+  pe.A = at<void>(ws, w.sc_p); pe.lda = d.vocab;
+  pe.B = c->embed_t; pe.ldb = d.vocab;
+  pe.M = R; pe.N = d.d_model; pe.K = d.vocab;
+  pe.C = at<void>(ws, w.sc_parts); pe.ldc = d.d_model;
+  pe.ksplit = sc_splits(d, R);
+  pe.c_split = (int64_t)R * d.d_model;
+  HIPCHK(launch_dense(pe, bf, bf ? W_BF16 : W_F32, s));
+  HIPCHK(launch_sum_parts_cast(at<float>(ws, w.sc_parts), pe.ksplit, pe.c_split, at<void>(ws, w.sc_x),
+                               (int64_t)R * d.d_model, bf, s));
+  DenseArgs g{};
+  g.epi = EPI_SWIGLU;
+  g.A = at<void>(ws, w.sc_x); g.lda = d.d_model;
+  g.B = c->sc_gate; g.B2 = c->sc_up; g.ldb = d.d_model;
+  g.M = R; g.N = d.sc_hidden; g.K = d.d_model;
+  g.C = at<void>(ws, w.sc_a); g.ldc = d.sc_hidden;
+  HIPCHK(launch_dense(g, bf, bf ? W_BF16 : W_F32, s));
+  DenseArgs dn{};
+  dn.epi = EPI_STORE_F32;
+  dn.A = at<void>(ws, w.sc_a); dn.lda = d.sc_hidden;
+  dn.B = c->sc_down; dn.ldb = d.sc_hidden;
+  dn.M = R; dn.N = d.d_model; dn.K = d.sc_hidden;
+  dn.C = sc_out; dn.ldc = d.d_model; dn.ksplit = 1; dn.c_split = 0;
+  HIPCHK(launch_dense(dn, bf, bf ? W_BF16 : W_F32, s));
+  return DG_OK;
+}
+
+// sampler arguments shared by the Euler and the entropy-bounded steps; with sc the probabilities
+// are also written for the self-conditioning product
+void samp_sc_args(const dg_ctx* c, SampArgs& sa, void* ws, const Layout& w, bool sc) {
+  if (!sc) return;
+  const int bn = sampler_bn(c->d.act_dtype == DG_BF16);
+  sa.pmat = at<void>(ws, w.sc_p);
+  sa.ptile = at<float>(ws, w.sc_ptile);
+  sa.n_vtiles = (c->d.vocab + bn - 1) / bn;
+}
+
 dg_status sample_into(dg_ctx* c, const void* hidden, int32_t* canvas, uint8_t* lock, int32_t* n_locked,
                       const int32_t* done, int B, int L, const dg_step_params* p, float lam, const SampScratch& sc,
                       int32_t* steps_taken, int32_t* done_out, hipStream_t s,
-                      const uint32_t* canvas_rng = nullptr, const float* lam_table = nullptr) {
+                      const uint32_t* canvas_rng = nullptr, const float* lam_table = nullptr,
+                      float* sc_out = nullptr, void* ws = nullptr, const Layout* w = nullptr) {
   const dg_model_desc& d = c->d;
   const int R = B * L;
   SampArgs sa{};
+  if (sc_out) samp_sc_args(c, sa, ws, *w, true);
   sa.H = hidden; sa.E = c->embed;
   sa.rows = R; sa.d = d.d_model; sa.V = d.vocab; sa.L = L;
   sa.zscale_log2 = (float)(1.4426950408889634 / (double)p->tau);
@@ -530,6 +605,7 @@ dg_status sample_into(dg_ctx* c, const void* hidden, int32_t* canvas, uint8_t* l
   st.steps_taken = steps_taken; st.done_out = done_out;
   st.canvas_rng = canvas_rng; st.lam_table = lam_table;
   HIPCHK(launch_step_merge(st, s));
+  if (sc_out) return self_cond_into(c, R, ws, *w, sc_out, s);
   return DG_OK;
 }
 
@@ -565,7 +641,7 @@ EbArgs eb_args(const dg_ctx* c, int32_t* canvas, int32_t* prev, int32_t* done, i
 // states, or from given logits), merged without touching the canvas, then the per-canvas selection
 dg_status eb_into(dg_ctx* c, const void* src, bool from_logits, int32_t* canvas, int32_t* prev, int32_t* done,
                   int32_t* n_accepted, float* mean_entropy, int B, int L, const dg_eb_params* p, void* ws,
-                  const Layout& w, int32_t* steps_taken, hipStream_t s) {
+                  const Layout& w, int32_t* steps_taken, hipStream_t s, float* sc_out = nullptr) {
   const dg_model_desc& d = c->d;
   const int R = B * L;
   const uint32_t k0 = key0(p->seed), k1 = key1(p->seed);
@@ -584,6 +660,7 @@ dg_status eb_into(dg_ctx* c, const void* src, bool from_logits, int32_t* canvas,
       sa.rows = R; sa.d = d.d_model; sa.V = d.vocab; sa.L = L;
       sa.zscale_log2 = zs; sa.k0 = k0; sa.k1 = k1; sa.step = p->step;
       sa.slices = slices; sa.v_per_slice = vps; sa.part = part;
+      samp_sc_args(c, sa, ws, w, sc_out != nullptr);
       HIPCHK(launch_lmhead_sampler(sa, d.act_dtype == DG_BF16, s));
     }
   }
@@ -591,6 +668,10 @@ dg_status eb_into(dg_ctx* c, const void* src, bool from_logits, int32_t* canvas,
   st.part = part; st.slices = slices; st.B = B; st.L = L;
   st.stats = at<float>(ws, w.stats); st.status = at<int>(ws, w.status); st.stats_only = 1;
   HIPCHK(launch_step_merge(st, s));
+  if (sc_out && !from_logits) {
+    const dg_status r = self_cond_into(c, R, ws, w, sc_out, s);
+    if (r != DG_OK) return r;
+  }
   HIPCHK(launch_eb_select(eb_args(c, canvas, prev, done, n_accepted, mean_entropy, B, L, p, ws, w, steps_taken), s));
   return DG_OK;
 }
@@ -634,11 +715,19 @@ dg_status dg_create(const dg_model_desc* desc, const dg_weights* wts, dg_ctx** o
   }
   if (((uintptr_t)wts->final_norm & 15) || ((uintptr_t)wts->embed & 15))
     return fail(DG_EINVAL, "weights: embed / final_norm not 16-byte aligned");
+  if (desc->sc_hidden > 0) {
+    if (!wts->embed || !wts->embed_t || !wts->sc_gate || !wts->sc_up || !wts->sc_down)
+      return fail(DG_EINVAL, "weights: self-conditioning needs embed, embed_t, sc_gate, sc_up and sc_down");
+    if (((uintptr_t)wts->embed_t | (uintptr_t)wts->sc_gate | (uintptr_t)wts->sc_up | (uintptr_t)wts->sc_down) & 15)
+      return fail(DG_EINVAL, "weights: self-conditioning matrices not 16-byte aligned");
+  }
   dg_ctx* c = new dg_ctx;
   c->d = *desc;
   c->layers.assign(wts->layers, wts->layers + desc->n_layers);
   c->embed = wts->embed;
   c->final_norm = wts->final_norm;
+  c->embed_t = wts->embed_t;
+  c->sc_gate = wts->sc_gate; c->sc_up = wts->sc_up; c->sc_down = wts->sc_down;
   c->prof = new Prof;
   *out = c;
   return DG_OK;
@@ -731,13 +820,15 @@ dg_status dg_prefill_kv(dg_ctx* ctx, const dg_kv* kv, const int32_t* tokens, int
   return DG_OK;
 }
 
-dg_status dg_denoise_step(dg_ctx* ctx, const dg_kv* kv, const int32_t* canvas, const float* resid_in, int32_t L,
-                          int32_t layer_begin, int32_t layer_end, void* hidden_out, float* resid_out, void* ws,
-                          size_t ws_bytes, hipStream_t stream) {
+dg_status dg_denoise_step(dg_ctx* ctx, const dg_kv* kv, const int32_t* canvas, const float* resid_in,
+                          const float* sc_in, int32_t L, int32_t layer_begin, int32_t layer_end, void* hidden_out,
+                          float* resid_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   g_err.clear();
   if (!ctx) return fail(DG_EINVAL, "NULL context");
   const dg_model_desc& d = ctx->d;
   if (!canvas && !resid_in) return fail(DG_EINVAL, "need canvas or resid_in");
+  if (sc_in && (resid_in || layer_begin != 0))
+    return fail(DG_EINVAL, "sc_in is added to the embedded canvas: no resid_in, layer_begin 0");
   if (!resid_in && !ctx->embed) return fail(DG_EINVAL, "embedding canvas tokens needs the embedding");
   if (layer_begin < 0 || layer_end > d.n_layers || layer_begin > layer_end)
     return fail(DG_EINVAL, "layer range [%d, %d) outside [0, %d]", layer_begin, layer_end, d.n_layers);
@@ -750,7 +841,7 @@ dg_status dg_denoise_step(dg_ctx* ctx, const dg_kv* kv, const int32_t* canvas, c
   const int R = P.B * L;
   const int bf = d.act_dtype == DG_BF16;
   if (resid_in) HIPCHK(launch_copy_f32(resid_in, at<float>(ws, P.w.resid), (int64_t)R * d.d_model, stream));
-  else HIPCHK(launch_embed(canvas, ctx->embed, at<float>(ws, P.w.resid), R, d.d_model, d.vocab, bf, stream));
+  else HIPCHK(launch_embed(canvas, ctx->embed, at<float>(ws, P.w.resid), R, d.d_model, d.vocab, bf, stream, sc_in));
   HIPCHK(launch_rope_table(at<float2>(ws, P.w.rope), R, L, d.head_dim, std::log2((double)d.rope_theta),
                            kv->prefix_len, kv->max_prefix, at<int>(ws, P.w.status), stream));
   // each layer's combine writes the next layer's normalised rows, the last one the final norm
@@ -770,12 +861,13 @@ dg_status dg_denoise_step(dg_ctx* ctx, const dg_kv* kv, const int32_t* canvas, c
 // one mixed pass (arguments already validated): append canvases take the causal encoder pass and
 // advance their device prefix length, the others the bidirectional decoder pass
 dg_status mixed_pass(dg_ctx* ctx, const dg_kv* kv, const int32_t* tokens, const int32_t* append, int L,
-                     void* hidden_out, float* resid_out, void* ws, const Layout& w, hipStream_t stream) {
+                     void* hidden_out, float* resid_out, void* ws, const Layout& w, hipStream_t stream,
+                     const float* sc_in = nullptr) {
   const dg_model_desc& d = ctx->d;
   Pass P{ctx, kv, kv->batch, L, 0, ws, w, stream, append};
   const int R = P.B * L;
   HIPCHK(launch_embed(tokens, ctx->embed, at<float>(ws, P.w.resid), R, d.d_model, d.vocab, d.act_dtype == DG_BF16,
-                      stream));
+                      stream, sc_in));
   HIPCHK(launch_rope_table(at<float2>(ws, P.w.rope), R, L, d.head_dim, std::log2((double)d.rope_theta),
                            kv->prefix_len, kv->max_prefix, at<int>(ws, P.w.status), stream));
   dg_status st;
@@ -805,10 +897,11 @@ dg_status dg_mixed_forward(dg_ctx* ctx, const dg_kv* kv, const int32_t* tokens, 
 }
 
 dg_status dg_step_sample(dg_ctx* ctx, const void* hidden, int32_t* canvas, uint8_t* lock, int32_t* n_locked,
-                         const int32_t* done, int32_t batch, int32_t L, const dg_step_params* params, void* ws,
-                         size_t ws_bytes, hipStream_t stream) {
+                         const int32_t* done, float* sc_out, int32_t batch, int32_t L, const dg_step_params* params,
+                         void* ws, size_t ws_bytes, hipStream_t stream) {
   g_err.clear();
   if (!ctx || !hidden || !canvas || !lock) return fail(DG_EINVAL, "NULL argument");
+  if (sc_out && ctx->d.sc_hidden <= 0) return fail(DG_EINVAL, "sc_out needs a model with a self-conditioning block");
   if (!ctx->embed) return fail(DG_EINVAL, "the LM head needs the embedding");
   dg_status st = check_step_params(params);
   if (st != DG_OK) return st;
@@ -817,7 +910,7 @@ dg_status dg_step_sample(dg_ctx* ctx, const void* hidden, int32_t* canvas, uint8
   const Layout w = layout(ctx->d, batch, L, 0);
   return sample_into(ctx, hidden, canvas, lock, n_locked, done, batch, L, params,
                      jump_prob(params->schedule, params->t, params->h), samp_scratch(ws, w), nullptr, nullptr,
-                     stream);
+                     stream, nullptr, nullptr, sc_out, ws, &w);
 }
 
 dg_status dg_step_sample_noalloc(dg_ctx* ctx, const void* hidden, int32_t* canvas, uint8_t* lock, int32_t* n_locked,
@@ -861,6 +954,7 @@ dg_status eb_run(dg_ctx* ctx, const dg_kv* kv, int32_t* canvas, uint8_t* lock, i
   if ((st = check_rows(kv->batch, L)) != DG_OK) return st;
   if ((st = check_ws(ctx, ws, ws_bytes, kv->batch, L, mp)) != DG_OK) return st;
   if (L > 1024) return fail(DG_EUNSUPPORTED, "entropy-bounded sampler: L %d > 1024", L);
+  if (p->self_condition && ctx->d.sc_hidden <= 0) return fail(DG_EINVAL, "self_condition needs a self-conditioning block");
   dg_eb_params ep{};
   ep.t = 1.f; ep.tau_start = p->tau; ep.tau_end = p->tau_end; ep.gamma = p->gamma; ep.stop_entropy = p->stop_entropy;
   ep.seed = p->seed; ep.adaptive = p->adaptive != 0;
@@ -876,17 +970,19 @@ dg_status eb_run(dg_ctx* ctx, const dg_kv* kv, int32_t* canvas, uint8_t* lock, i
   const double h = 1.0 / p->max_steps;
   // every pass is enqueued up front; once all canvases have stopped, the gate turns the remaining
   // passes' kernels away at entry (adaptive mode)
+  // self-conditioning: the signal of step s feeds the decoder of step s + 1 (none at step 0)
+  float* sc = p->self_condition ? at<float>(ws, w.sc_state) : nullptr;
   GateScope gate(p->adaptive ? all_done : nullptr);
   for (int s = 0; s < p->max_steps; ++s) {
-    if ((st = dg_denoise_step(ctx, kv, canvas, nullptr, L, 0, ctx->d.n_layers, at<void>(ws, w.hidden), nullptr, ws,
-                              ws_bytes, stream)) != DG_OK)
+    if ((st = dg_denoise_step(ctx, kv, canvas, nullptr, s > 0 ? sc : nullptr, L, 0, ctx->d.n_layers,
+                              at<void>(ws, w.hidden), nullptr, ws, ws_bytes, stream)) != DG_OK)
       return st;
     ep.t = (float)(1.0 - s * h);
     ep.step = (uint32_t)s;
     ep.has_prev = s > 0;
     ep.final_step = s == p->max_steps - 1;
     if ((st = eb_into(ctx, at<void>(ws, w.hidden), false, canvas, at<int32_t>(ws, w.prev), done, nullptr, nullptr,
-                      B, L, &ep, ws, w, steps_taken, stream)) != DG_OK)
+                      B, L, &ep, ws, w, steps_taken, stream, s + 1 < p->max_steps ? sc : nullptr)) != DG_OK)
       return st;
     if (p->adaptive) HIPCHK(launch_all_set(done, B, all_done, stream));
   }
@@ -919,6 +1015,7 @@ dg_status dg_canvas_run(dg_ctx* ctx, const dg_kv* kv, int32_t* canvas, uint8_t* 
   if (!lock) return fail(DG_EINVAL, "NULL argument");
   if (!ctx->embed) return fail(DG_EINVAL, "the canvas loop needs the embedding");
   if (p->max_steps < 1) return fail(DG_EINVAL, "max_steps must be >= 1");
+  if (p->self_condition && ctx->d.sc_hidden <= 0) return fail(DG_EINVAL, "self_condition needs a self-conditioning block");
   int mp = 0;
   dg_status st = check_kv(ctx, kv, 0, &mp);
   if (st != DG_OK) return st;
@@ -939,10 +1036,12 @@ dg_status dg_canvas_run(dg_ctx* ctx, const dg_kv* kv, int32_t* canvas, uint8_t* 
   const double h = 1.0 / p->max_steps;
   // every pass is enqueued up front (no host read of `done`); once all canvases have locked every
   // position, the gate turns the remaining passes' kernels away at entry (adaptive mode)
+  // self-conditioning: the signal of step s feeds the decoder of step s + 1 (none at step 0)
+  float* sc = p->self_condition ? at<float>(ws, w.sc_state) : nullptr;
   GateScope gate(p->adaptive ? all_done : nullptr);
   for (int s = 0; s < p->max_steps; ++s) {
-    if ((st = dg_denoise_step(ctx, kv, canvas, nullptr, L, 0, ctx->d.n_layers, at<void>(ws, w.hidden), nullptr, ws,
-                              ws_bytes, stream)) != DG_OK)
+    if ((st = dg_denoise_step(ctx, kv, canvas, nullptr, s > 0 ? sc : nullptr, L, 0, ctx->d.n_layers,
+                              at<void>(ws, w.hidden), nullptr, ws, ws_bytes, stream)) != DG_OK)
       return st;
     const double t = 1.0 - s * h;
     sp.t = (float)t;
@@ -951,7 +1050,8 @@ dg_status dg_canvas_run(dg_ctx* ctx, const dg_kv* kv, int32_t* canvas, uint8_t* 
     // the jump probability is taken at the double-precision grid point t_s = 1 - s/T
     if ((st = sample_into(ctx, at<void>(ws, w.hidden), canvas, lock, at<int32_t>(ws, w.n_locked),
                           p->adaptive ? done : nullptr, B, L, &sp, jump_prob(p->schedule, t, h), samp_scratch(ws, w),
-                          steps_taken, p->adaptive ? done : nullptr, stream)) != DG_OK)
+                          steps_taken, p->adaptive ? done : nullptr, stream, nullptr, nullptr,
+                          s + 1 < p->max_steps ? sc : nullptr, ws, &w)) != DG_OK)
       return st;
     if (p->adaptive) HIPCHK(launch_all_set(done, B, all_done, stream));
   }
@@ -1000,6 +1100,8 @@ dg_status dg_generate_continuous(dg_ctx* ctx, const dg_kv* kv, int32_t* out, int
   if (!ctx->embed) return fail(DG_EINVAL, "generation needs the embedding");
   if (K < 1) return fail(DG_EINVAL, "K must be >= 1");
   if (params->sampler != DG_SAMPLER_EULER) return fail(DG_EUNSUPPORTED, "continuous generation runs the Euler sampler");
+  if (params->self_condition && ctx->d.sc_hidden <= 0)
+    return fail(DG_EINVAL, "self_condition needs a self-conditioning block");
   const int T = params->max_steps;
   if (T < 1 || T > 256) return fail(DG_EUNSUPPORTED, "max_steps %d not in [1, 256]", T);
   dg_step_params sp{};
@@ -1033,6 +1135,9 @@ dg_status dg_generate_continuous(dg_ctx* ctx, const dg_kv* kv, int32_t* out, int
   sa.cur = at<int32_t>(ws, w.prev); sa.lock = at<uint8_t>(ws, w.lockbuf);
   sa.n_locked = at<int32_t>(ws, w.n_locked);
   sa.out = out; sa.steps = steps; sa.append = append; sa.skip = skip; sa.finished = finished; sa.passes = passes;
+  // self-conditioning: each sequence's signal, cleared whenever its next pass appends or starts a canvas
+  sa.sc = params->self_condition ? at<float>(ws, w.sc_state) : nullptr;
+  sa.d = ctx->d.d_model;
   {
     // every pass is enqueued up front; once every sequence has finished, the gate turns the rest away
     GateScope gate(all_done);
@@ -1041,10 +1146,12 @@ dg_status dg_generate_continuous(dg_ctx* ctx, const dg_kv* kv, int32_t* out, int
     sa.init = 0;
     const int max_passes = K * T + K - 1;
     for (int p = 0; p < max_passes; ++p) {
-      if ((st = mixed_pass(ctx, &run, sa.cur, append, L, at<void>(ws, w.hidden), nullptr, ws, w, stream)) != DG_OK)
+      if ((st = mixed_pass(ctx, &run, sa.cur, append, L, at<void>(ws, w.hidden), nullptr, ws, w, stream, sa.sc)) !=
+          DG_OK)
         return st;
       if ((st = sample_into(ctx, at<void>(ws, w.hidden), sa.cur, sa.lock, at<int32_t>(ws, w.n_locked), skip, B, L,
-                            &sp, 0.f, samp_scratch(ws, w), nullptr, nullptr, stream, sa.rng, lam_dev)) != DG_OK)
+                            &sp, 0.f, samp_scratch(ws, w), nullptr, nullptr, stream, sa.rng, lam_dev, sa.sc, ws,
+                            &w)) != DG_OK)
         return st;
       HIPCHK(launch_seq_schedule(sa, stream));
       HIPCHK(launch_all_set(finished, B, all_done, stream));

@@ -27,7 +27,8 @@ class ModelDesc(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("n_layers", "d_model", "n_q_heads", "n_kv_heads", "head_dim",
                                           "n_experts", "top_k", "expert_hidden", "shared_hidden", "vocab",
                                           "window", "global_every")] + \
-               [("rope_theta", C.c_float), ("norm_eps", C.c_float), ("act_dtype", C.c_int), ("expert_dtype", C.c_int)]
+               [("rope_theta", C.c_float), ("norm_eps", C.c_float), ("act_dtype", C.c_int), ("expert_dtype", C.c_int),
+                ("sc_hidden", C.c_int32)]
 
 
 LAYER_FIELDS = ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_router", "router_bias", "w_gate", "w_up", "w_down",
@@ -39,7 +40,8 @@ class LayerWeights(C.Structure):
 
 
 class Weights(C.Structure):
-    _fields_ = [("embed", C.c_void_p), ("final_norm", C.c_void_p), ("layers", C.POINTER(LayerWeights))]
+    _fields_ = [("embed", C.c_void_p), ("final_norm", C.c_void_p), ("layers", C.POINTER(LayerWeights)),
+                ("embed_t", C.c_void_p), ("sc_gate", C.c_void_p), ("sc_up", C.c_void_p), ("sc_down", C.c_void_p)]
 
 
 class KV(C.Structure):
@@ -55,7 +57,8 @@ class StepParams(C.Structure):
 class RunParams(C.Structure):
     _fields_ = [("schedule", C.c_int), ("max_steps", C.c_int32), ("tau", C.c_float), ("lock_threshold", C.c_float),
                 ("seed", C.c_uint64), ("adaptive", C.c_int32), ("init_canvas", C.c_int32), ("sampler", C.c_int),
-                ("gamma", C.c_float), ("stop_entropy", C.c_float), ("tau_end", C.c_float)]
+                ("gamma", C.c_float), ("stop_entropy", C.c_float), ("tau_end", C.c_float),
+                ("self_condition", C.c_int32)]
 
 
 DG_SAMPLER_EULER, DG_SAMPLER_ENTROPY_BOUNDED = 0, 1
@@ -76,12 +79,14 @@ EXPORTS = {
     "dg_clear_status": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p]),
     "dg_prefill_kv": (C.c_int, [C.c_void_p, C.POINTER(KV), C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t,
                                 C.c_void_p]),
-    "dg_denoise_step": (C.c_int, [C.c_void_p, C.POINTER(KV), C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
-                                  C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "dg_denoise_step": (C.c_int, [C.c_void_p, C.POINTER(KV), C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
+                                  C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
+                                  C.c_void_p]),
     "dg_mixed_forward": (C.c_int, [C.c_void_p, C.POINTER(KV), C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p,
                                    C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "dg_step_sample": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
-                                 C.c_int32, C.c_int32, C.POINTER(StepParams), C.c_void_p, C.c_size_t, C.c_void_p]),
+                                 C.c_void_p, C.c_int32, C.c_int32, C.POINTER(StepParams), C.c_void_p, C.c_size_t,
+                                 C.c_void_p]),
     "dg_step_sample_noalloc": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                          C.c_int32, C.c_int32, C.POINTER(StepParams), C.c_void_p]),
     "dg_canvas_run": (C.c_int, [C.c_void_p, C.POINTER(KV), C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
@@ -192,10 +197,10 @@ def dg_prefill_kv(ctx, kv: KV, tokens, n, ws, stream=None):
 
 
 def dg_denoise_step(ctx, kv: KV, canvas, resid_in, L, layer_begin, layer_end, hidden_out, resid_out, ws,
-                    stream=None):
-    _check(load().dg_denoise_step(ctx, C.byref(kv), _ptr(canvas), _ptr(resid_in), L, layer_begin, layer_end,
-                                  _ptr(hidden_out), _ptr(resid_out), _ptr(ws), ws.numel() * ws.element_size(),
-                                  _stream(stream)))
+                    stream=None, sc_in=None):
+    _check(load().dg_denoise_step(ctx, C.byref(kv), _ptr(canvas), _ptr(resid_in), _ptr(sc_in), L, layer_begin,
+                                  layer_end, _ptr(hidden_out), _ptr(resid_out), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def dg_mixed_forward(ctx, kv: KV, tokens, append, L, hidden_out, ws, stream=None, resid_out=None):
@@ -203,9 +208,11 @@ def dg_mixed_forward(ctx, kv: KV, tokens, append, L, hidden_out, ws, stream=None
                                    _ptr(resid_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
-def dg_step_sample(ctx, hidden, canvas, lock, n_locked, done, batch, L, params: StepParams, ws, stream=None):
-    _check(load().dg_step_sample(ctx, _ptr(hidden), _ptr(canvas), _ptr(lock), _ptr(n_locked), _ptr(done), batch, L,
-                                 C.byref(params), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+def dg_step_sample(ctx, hidden, canvas, lock, n_locked, done, batch, L, params: StepParams, ws, stream=None,
+                   sc_out=None):
+    _check(load().dg_step_sample(ctx, _ptr(hidden), _ptr(canvas), _ptr(lock), _ptr(n_locked), _ptr(done),
+                                 _ptr(sc_out), batch, L, C.byref(params), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _stream(stream)))
 
 
 def dg_step_sample_noalloc(ctx, hidden, canvas, lock, n_locked, done, B, L, params: StepParams, stream=None):

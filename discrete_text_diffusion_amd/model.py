@@ -21,7 +21,7 @@ def model_desc(cfg) -> dg.ModelDesc:
                         top_k=cfg.top_k, expert_hidden=cfg.expert_hidden, shared_hidden=cfg.shared_hidden,
                         vocab=cfg.vocab, window=cfg.window, global_every=cfg.global_every,
                         rope_theta=cfg.rope_theta, norm_eps=cfg.norm_eps, act_dtype=_DT[cfg.act_dtype],
-                        expert_dtype=_DT[cfg.expert_dtype])
+                        expert_dtype=_DT[cfg.expert_dtype], sc_hidden=getattr(cfg, "sc_hidden", 0))
 
 
 def _p(t):
@@ -50,7 +50,9 @@ class Model:
             for f in dg.LAYER_FIELDS:
                 setattr(self._layers[l], f, _p(L.get(f)))
         self.weights = dg.Weights(embed=_p(weights.get("embed")), final_norm=_p(weights["final_norm"]),
-                                  layers=C.cast(self._layers, C.POINTER(dg.LayerWeights)))
+                                  layers=C.cast(self._layers, C.POINTER(dg.LayerWeights)),
+                                  embed_t=_p(weights.get("embed_t")), sc_gate=_p(weights.get("sc_gate")),
+                                  sc_up=_p(weights.get("sc_up")), sc_down=_p(weights.get("sc_down")))
         self.ctx = dg.dg_create(self.desc, self.weights)
         self.kv_struct = None
         if kv is not None:
@@ -106,10 +108,10 @@ class Model:
         self._grew(tokens.shape[1])
 
     def denoise_step(self, canvas, L, ws, hidden_out=None, resid_out=None, resid_in=None, layer_begin=0,
-                     layer_end=None, stream=None):
+                     layer_end=None, stream=None, sc_in=None):
         le = self.cfg.n_layers if layer_end is None else layer_end
         dg.dg_denoise_step(self.ctx, self.kv_struct, canvas, resid_in, L, layer_begin, le, hidden_out, resid_out,
-                           ws, stream)
+                           ws, stream, sc_in)
 
     def mixed_forward(self, tokens, append, hidden_out, ws, stream=None, resid_out=None):
         """One pass over canvases of two kinds: append[b] != 0 (device int32 [B]) encodes canvas b
@@ -119,9 +121,10 @@ class Model:
                             resid_out)
         self._grew(tokens.shape[1], known=False)
 
-    def step_sample(self, hidden, canvas, lock, n_locked, params: dg.StepParams, ws, done=None, stream=None):
+    def step_sample(self, hidden, canvas, lock, n_locked, params: dg.StepParams, ws, done=None, stream=None,
+                    sc_out=None):
         B, L = canvas.shape
-        dg.dg_step_sample(self.ctx, hidden, canvas, lock, n_locked, done, B, L, params, ws, stream)
+        dg.dg_step_sample(self.ctx, hidden, canvas, lock, n_locked, done, B, L, params, ws, stream, sc_out)
 
     def canvas_run(self, canvas, lock, steps_taken, params: dg.RunParams, ws, stream=None):
         dg.dg_canvas_run(self.ctx, self.kv_struct, canvas, lock, steps_taken, canvas.shape[1], params, ws, stream)

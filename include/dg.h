@@ -74,6 +74,8 @@ typedef struct {
   float rope_theta; /* RoPE base (rotate-half pairs j, j + head_dim/2) */
   float norm_eps;   /* RMSNorm epsilon */
   dg_dtype act_dtype, expert_dtype;
+  int32_t sc_hidden; /* hidden width of the self-conditioning block (multiple of 64; vocab % 64 == 0),
+                        0: the model has none [TR §디노이징 반복과 self-conditioning] */
 } dg_model_desc;
 
 /* One layer's weights: device pointers, borrowed until dg_destroy().  Every matrix is stored
@@ -105,6 +107,12 @@ typedef struct {
                                only for calls that take resid_in and produce no logits        */
   const void *final_norm;   /* [d] act                                                        */
   const dg_layer_weights *layers; /* host array [n_layers]                                    */
+  /* self-conditioning (sc_hidden > 0, else NULL): s = FFW(p_hat_0 . E) with the gated block
+   * A = silu(x sc_gate^T) * (x sc_up^T), s = A sc_down^T, x = p_hat_0 . E stored in act.      */
+  const void *embed_t;      /* [d][V] act: E transposed, so the product over the vocabulary
+                               streams K-contiguous rows (same values as embed)                */
+  const void *sc_gate, *sc_up; /* [sc_hidden][d] act                                          */
+  const void *sc_down;      /* [d][sc_hidden] act                                              */
 } dg_weights;
 
 /* Prefix KV cache, filled by the causal encoder (dg_prefill_kv) or by the caller.  The prefix
@@ -174,6 +182,8 @@ typedef struct {
   int32_t init_canvas;          /* 1: draw the canvas uniformly at t = 1 (and clear the lock) */
   dg_sampler sampler;           /* DG_SAMPLER_EULER (0) or DG_SAMPLER_ENTROPY_BOUNDED */
   float gamma, stop_entropy, tau_end;   /* entropy-bounded sampler only */
+  int32_t self_condition;       /* 1: feed s = FFW(p_hat_0 . E) of each step into the next step's
+                                   decoder (s = 0 at a canvas's first step); needs sc_hidden > 0 */
 } dg_run_params;
 
 typedef struct dg_ctx dg_ctx;   /* opaque, host-side; holds the descriptor and borrowed weights */
@@ -214,9 +224,12 @@ dg_status dg_prefill_kv(dg_ctx *ctx, const dg_kv *kv, const int32_t *tokens, int
  * lookup of `embed`) or, when resid_in is non-NULL, the fp32 residual stream [batch*L][d].
  * Output: hidden_out [batch*L][d] act = RMSNorm(residual) * final_norm (may be NULL), and
  * resid_out [batch*L][d] fp32 = the residual after layer_end - 1 (may be NULL).
+ * sc_in (nullable, device [batch*L][d] fp32): the self-conditioning signal s_t, added to the
+ * embedded canvas ([TR §디노이징 반복과 self-conditioning]: the decoder takes x_t, the cache and s_t);
+ * only with canvas tokens and layer_begin 0.
  * Canvas position i of canvas b has RoPE position prefix_len[b] + i. */
 dg_status dg_denoise_step(dg_ctx *ctx, const dg_kv *kv, const int32_t *canvas,
-                          const float *resid_in, int32_t L, int32_t layer_begin,
+                          const float *resid_in, const float *sc_in, int32_t L, int32_t layer_begin,
                           int32_t layer_end, void *hidden_out, float *resid_out,
                           void *ws, size_t ws_bytes, hipStream_t stream);
 
@@ -241,10 +254,13 @@ dg_status dg_mixed_forward(dg_ctx *ctx, const dg_kv *kv, const int32_t *tokens,
  * (device int32 [batch][L], in/out) and lock (device uint8 [batch][L], in/out) is updated as
  * described at dg_step_params.  n_locked (device int32 [batch], out, may be NULL) receives the
  * locked count per canvas, or -1 if a non-finite value was seen in that canvas.
- * `done` (device int32 [batch], may be NULL): canvases with done[b] != 0 are left unchanged. */
+ * `done` (device int32 [batch], may be NULL): canvases with done[b] != 0 are left unchanged.
+ * sc_out (nullable, device [batch*L][d] fp32; needs sc_hidden > 0): the self-conditioning signal
+ * for the next step, s = FFW(p_hat_0 . E) with p_hat_0 the Step's softmax(logits / tau), formed
+ * from the same vocabulary pass (its probabilities kept for a second product with E). */
 dg_status dg_step_sample(dg_ctx *ctx, const void *hidden, int32_t *canvas, uint8_t *lock,
-                         int32_t *n_locked, const int32_t *done, int32_t batch, int32_t L,
-                         const dg_step_params *params, void *ws, size_t ws_bytes,
+                         int32_t *n_locked, const int32_t *done, float *sc_out, int32_t batch,
+                         int32_t L, const dg_step_params *params, void *ws, size_t ws_bytes,
                          hipStream_t stream);
 
 /* dg_step_sample for callers that cannot allocate device memory or hand over a workspace (code under

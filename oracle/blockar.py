@@ -84,9 +84,12 @@ def eos_mask(out, eos):
     return (out == eos).any(axis=2)
 
 
-def generate(cfg, W, kv, prefix_len, K, eos, sampler="euler", steps=None, seed=None, eb_kw=None, trace=None):
+def generate(cfg, W, kv, prefix_len, K, eos, sampler="euler", steps=None, seed=None, eb_kw=None, trace=None,
+             self_cond=None):
     """K canvases after an encoded prompt (kv, prefix_len).  Returns out [K][B][L], steps [K][B],
-    the caches and prefix lengths after the appends."""
+    the caches and prefix lengths after the appends.  With `self_cond` ((H, tau) -> s) every canvas
+    starts from s = 0 and feeds each step's signal into its next decoder pass; the appending
+    encoder pass takes none."""
     B, L = cfg.batch, cfg.canvas
     seed = cfg.seed if seed is None else seed
     T = cfg.steps if steps is None else steps
@@ -94,11 +97,11 @@ def generate(cfg, W, kv, prefix_len, K, eos, sampler="euler", steps=None, seed=N
     taken = np.zeros((K, B), np.int64)
     plen = list(prefix_len)
     for k in range(K):
-        fwd = lambda c, kv=kv, plen=plen: M.denoise_forward(cfg, W, kv, plen, canvas=c)[0]
+        fwd = lambda c, sc=None, kv=kv, plen=plen: M.denoise_forward(cfg, W, kv, plen, canvas=c, sc=sc)[0]
         if sampler == "euler":
-            x, _, tk = S.canvas_run(cfg, W, kv, plen, fwd, steps=T, seed=seed + k)
+            x, _, tk = S.canvas_run(cfg, W, kv, plen, fwd, steps=T, seed=seed + k, self_cond=self_cond)
         else:
-            x, tk = eb.run(cfg, W, fwd, steps=T, seed=seed + k, **(eb_kw or {}))
+            x, tk = eb.run(cfg, W, fwd, steps=T, seed=seed + k, self_cond=self_cond, **(eb_kw or {}))
         out[k], taken[k] = x, tk
         if trace is not None:
             trace.append({"k": k, "prefix": list(plen)})

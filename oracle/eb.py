@@ -113,21 +113,26 @@ def stats_from_logits(z, seed, s, B, L):
 
 
 def run(cfg, W, forward, steps=48, tau_start=TAU_START, tau_end=TAU_END, gamma=GAMMA,
-        stop_entropy=STOP_ENTROPY, adaptive=True, seed=None, canvas=None, trace=None):
+        stop_entropy=STOP_ENTROPY, adaptive=True, seed=None, canvas=None, trace=None, self_cond=None):
     """The sampler's loop over one block of canvases: uniform canvas at t = 1, then at most `steps`
-    forward passes.  Returns canvas, steps_taken [B]."""
+    forward passes.  With `self_cond` ((H, tau_t) -> s) the decoder is called as forward(x, s) with
+    s = None at the first step and the previous step's signal afterwards.  Returns canvas,
+    steps_taken [B]."""
     B, L = cfg.batch, cfg.canvas
     seed = cfg.seed if seed is None else seed
     x = S.init_canvas(seed, B, L, cfg.vocab) if canvas is None else np.asarray(canvas).copy()
     done = np.zeros(B, dtype=bool)
     taken = np.zeros(B, dtype=np.int64)
     prev = None
+    sc = None
     ts, h = S.time_grid(steps)
     for s, t in enumerate(ts):
         if done.all():
             break
         tau = temperature(t, tau_start, tau_end)
-        Hh = forward(x)
+        Hh = forward(x) if self_cond is None else forward(x, sc)
+        if self_cond is not None:
+            sc = self_cond(Hh, tau)
         z = S.logits(Hh, W["embed"], tau)
         st = stats_from_logits(z, seed, s, B, L)
         a, y = st["a"].reshape(B, L), st["y"].reshape(B, L)

@@ -154,9 +154,9 @@ def canvas_run(cfg, W, kv, prefix_len, forward, canvas=None, lock=None, steps=No
                tau=None, theta=None, schedule=None, adaptive=None, seed=None, self_cond=None):
     """The denoising loop for one block of canvases.
 
-    `forward(canvas) -> H` is the decoder pass; with `self_cond` (a function H -> s) it is called
-    as forward(canvas, s) with s = None at the first step and s = self_cond(H) of the previous
-    step afterwards [TR §디노이징 반복과 self-conditioning].  At t = 1 the canvas is drawn uniform
+    `forward(canvas) -> H` is the decoder pass; with `self_cond` (a function (H, tau) -> s) it is
+    called as forward(canvas, s) with s = None at the first step and s = self_cond(H, tau) of the
+    previous step afterwards [TR §디노이징 반복과 self-conditioning].  At t = 1 the canvas is drawn uniform
     (unless given).  For s = 0..T-1: canvases that are done are skipped, the rest take one Step at
     t_s; with adaptive stopping a canvas is done once all its positions are locked.
     Returns canvas, lock, steps_taken[B]."""
@@ -181,7 +181,7 @@ def canvas_run(cfg, W, kv, prefix_len, forward, canvas=None, lock=None, steps=No
             break
         H = forward(canvas) if self_cond is None else forward(canvas, sc)
         if self_cond is not None:
-            sc = self_cond(H)
+            sc = self_cond(H, tau)
         canvas, lock, nl, _, _ = step(H, W["embed"], canvas, lock, t, h, schedule, tau, theta, seed, s,
                                       done if adaptive else None)
         taken += ~done if adaptive else 1

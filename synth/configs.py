@@ -56,6 +56,7 @@ class Workload:
     rope_theta: float = 10000.0
     norm_eps: float = 1e-6
     weight_std: float = 0.02
+    sc_hidden: int = 0     # >0: a self-conditioning block of this hidden width (896 at the Gemma-like widths)
 
     def is_global(self, layer: int) -> bool:
         if self.window <= 0 or self.global_every <= 0:

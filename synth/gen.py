@@ -17,6 +17,8 @@ Layouts (row-major; every weight matrix is [out][in] so both GEMM operands are K
   mxfp4:     expert matrices as codes uint8 [..][N][K/2] (element 2j in the low nibble of byte j)
              with scales uint8 [..][N][K/32] (e8m0: 2^(s - 127)) under the same s_* names
   kv         per layer K and V [B][Hkv][cap][dh]
+  self-conditioning (sc_hidden > 0): embed_t [d][V] (embed transposed), sc_gate, sc_up [f][d],
+             sc_down [d][f] in the activation dtype
 """
 from __future__ import annotations
 
@@ -156,6 +158,14 @@ def make_weights(cfg: Workload, device="cpu") -> dict:
     else:
         W["embed"] = store_act(normal((cfg.vocab, cfg.d_model), cfg.weight_std, cfg.seed, "embed",
                                       device), cfg.act_dtype)
+    if cfg.sc_hidden > 0:
+        # the self-conditioning block: the embedding transposed ([d][V], the same values) and a
+        # gated feed-forward block d -> sc_hidden -> d in the activation dtype
+        W["embed_t"] = W["embed"].t().contiguous()
+        f, d = cfg.sc_hidden, cfg.d_model
+        W["sc_gate"] = store_act(normal((f, d), cfg.weight_std, cfg.seed, "sc.gate", device), cfg.act_dtype)
+        W["sc_up"] = store_act(normal((f, d), cfg.weight_std, cfg.seed, "sc.up", device), cfg.act_dtype)
+        W["sc_down"] = store_act(normal((d, f), cfg.weight_std, cfg.seed, "sc.down", device), cfg.act_dtype)
     return W
 
 

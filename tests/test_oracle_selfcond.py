@@ -126,7 +126,7 @@ def test_zero_signal_leaves_the_loop_unchanged_and_first_step_sees_zero():
         return M.denoise_forward(cfg, W, kv, [5, 5], canvas=c, sc=s)[0]
     base = S.canvas_run(cfg, W, kv, [5, 5], lambda c: fwd(c))
     seen.clear()
-    zero = S.canvas_run(cfg, W, kv, [5, 5], fwd, self_cond=lambda H: np.zeros_like(H))
+    zero = S.canvas_run(cfg, W, kv, [5, 5], fwd, self_cond=lambda H, tau: np.zeros_like(H))
     assert seen[0] is None and all(x is not None for x in seen[1:])
     for a, b in zip(base, zero):
         assert np.array_equal(a, b)
@@ -134,7 +134,7 @@ def test_zero_signal_leaves_the_loop_unchanged_and_first_step_sees_zero():
     seen.clear()
     sc_w = (rng.standard_normal((8, 16)), rng.standard_normal((8, 16)), rng.standard_normal((16, 8)))
     cond = S.canvas_run(cfg, W, kv, [5, 5], fwd, steps=1,
-                        self_cond=lambda H: SC.self_condition(H, W["embed"], cfg.tau, sc_w, identity))
+                        self_cond=lambda H, tau: SC.self_condition(H, W["embed"], tau, sc_w, identity))
     first = S.canvas_run(cfg, W, kv, [5, 5], lambda c: fwd(c), steps=1)
     for a, b in zip(cond, first):
         assert np.array_equal(a, b)
