@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--experts", choices=("bf16", "fp8", "mxfp4"), default=None,
                     help="expert weight format (default: the workload's); fp8 and mxfp4 are weights-only "
                          "formats with bf16 activations")
+    ap.add_argument("--self-cond", action="store_true",
+                    help="give the model a self-conditioning block (hidden width 896) and feed each step's "
+                         "signal into the next step (a variant of the workload, not the headline)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed region, copy 512 MiB device to device 4 times (a plain copy of known "
                          "size for scaling hardware byte counters)")
@@ -102,7 +105,11 @@ def class_roofs(cfg, uniq, gate_up_bytes):
     samp_bytes = cfg.vocab * d * ab
     samp_flops = 2.0 * R * cfg.vocab * d
     ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    return {
+    # self-conditioning: p_hat_0 . E streams E once more (same bytes and FLOPs as the logits); the
+    # feed-forward block's weights are negligible beside it
+    sc = {"self_condition": hbm(samp_bytes) if samp_flops / samp_bytes < ridge else mfma(samp_flops)} \
+        if getattr(cfg, "sc_hidden", 0) else {}
+    return {**sc,
         "moe_gate_up": hbm(nl * gate_up_bytes),
         "moe_down": hbm(nl * down),
         "attention": mfma(flops),
@@ -180,6 +187,11 @@ def main():
     cfg = configs.get(args.workload)
     if args.experts is not None and args.experts != cfg.expert_dtype:
         cfg = cfg.replace(expert_dtype=args.experts, name=f"{cfg.name}-{args.experts}experts")
+    if args.self_cond:
+        if args.sampler == "eb":
+            print("--self-cond runs with the Euler sampler's step calls", file=sys.stderr)
+            sys.exit(2)
+        cfg = cfg.replace(sc_hidden=896, name=f"{cfg.name}-selfcond")
     dev = torch.device("cuda:0")
     log(f"[bench] workload {cfg.name}: building inputs on {torch.cuda.get_device_name(0)}")
     t0 = time.time()
@@ -201,6 +213,8 @@ def main():
 
     prev = torch.zeros(B, L, dtype=torch.int32, device=dev)
     done = torch.zeros(B, dtype=torch.int32, device=dev)
+    # self-conditioning signal carried from one step to the next (none at a canvas's first step)
+    sc = torch.zeros(B * L, cfg.d_model, dtype=torch.float32, device=dev) if args.self_cond else None
 
     def step(s):
         k = s % T
@@ -208,7 +222,7 @@ def main():
             dg.dg_init_canvas(canvas, lock, B, L, cfg.vocab, cfg.seed + s // T, stream)
             if args.sampler == "eb":
                 done.zero_()
-        model.denoise_step(canvas, L, ws, hidden_out=hidden, stream=stream)
+        model.denoise_step(canvas, L, ws, hidden_out=hidden, stream=stream, sc_in=sc if k > 0 else None)
         if args.sampler == "eb":
             p = dg.EbParams(t=1.0 - k * h, tau_start=0.8, tau_end=0.4, gamma=0.1, stop_entropy=0.005,
                             seed=cfg.seed, step=k, has_prev=int(k > 0), final_step=int(k == T - 1), adaptive=1)
@@ -216,7 +230,8 @@ def main():
             return
         p = dg.StepParams(schedule=cfg.schedule, t=1.0 - k * h, h=h, tau=cfg.tau, lock_threshold=cfg.lock_threshold,
                           seed=cfg.seed, step=k)
-        model.step_sample(hidden, canvas, lock, n_locked, p, ws, stream=stream)
+        model.step_sample(hidden, canvas, lock, n_locked, p, ws, stream=stream,
+                          sc_out=sc if k + 1 < T else None)
 
     for s in range(args.warmup):
         step(s)
@@ -277,7 +292,7 @@ def main():
 
     breakdown = None
     if not args.no_breakdown:
-        dg.dg_profile_enable(model.ctx, (1 << 8) - 1)
+        dg.dg_profile_enable(model.ctx, (1 << len(dg.PROF_NAMES)) - 1)
         for s in range(T):
             step(s)
         torch.cuda.synchronize()
@@ -322,7 +337,8 @@ def main():
         "config": {"workload": f"{args.workload}: {cfg.name}", "layers": cfg.n_layers, "batch": B, "canvas": L,
                    "prefix": cfg.prefix, "vocab": cfg.vocab, "d_model": cfg.d_model, "experts": cfg.n_experts,
                    "top_k": cfg.top_k, "schedule_steps": T,
-                   "sampler": "entropy-bounded" if args.sampler == "eb" else "euler+lock-in"},
+                   "sampler": "entropy-bounded" if args.sampler == "eb" else "euler+lock-in",
+                   "self_conditioning": bool(args.self_cond)},
         "roofline": {"kernel": "moe_gate_up (routed + shared experts gate/up + SwiGLU, one launch)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,

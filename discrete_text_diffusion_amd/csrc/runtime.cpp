@@ -410,8 +410,11 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn, bool xhat_ready, const vo
     ProfScope ps(P.c, DG_PROF_O_PROJ, P.s);
     HIPCHK(launch_dense(oa, bf, bf ? W_BF16 : W_F32, P.s));
   }
-  HIPCHK(launch_resid_add_rmsnorm(at<float>(ws, w.resid), at<float>(ws, w.o_parts), oa.ksplit, oa.c_split,
-                                  L.ffn_norm, at<void>(ws, w.xhat), R, d.d_model, d.norm_eps, bf, status, P.s));
+  {
+    ProfScope ps(P.c, DG_PROF_NORM_COMBINE, P.s);
+    HIPCHK(launch_resid_add_rmsnorm(at<float>(ws, w.resid), at<float>(ws, w.o_parts), oa.ksplit, oa.c_split,
+                                    L.ffn_norm, at<void>(ws, w.xhat), R, d.d_model, d.norm_eps, bf, status, P.s));
+  }
   if (!do_ffn) return DG_OK;
 
   // FFN: router, top-k, grouping
@@ -481,9 +484,12 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn, bool xhat_ready, const vo
     ProfScope ps(P.c, DG_PROF_MOE_DOWN, P.s);
     HIPCHK(launch_grouped(da, bf, wk, max_items, P.s));
   }
-  HIPCHK(launch_moe_combine_norm(at<float>(ws, w.resid), at<float>(ws, w.y), at<float>(ws, w.sh_parts),
-                                 at<float>(ws, w.gates), at<int32_t>(ws, w.inv_perm), R, d.d_model, d.top_k, next_g,
-                                 next_out, d.norm_eps, bf, status, P.s));
+  {
+    ProfScope ps(P.c, DG_PROF_NORM_COMBINE, P.s);
+    HIPCHK(launch_moe_combine_norm(at<float>(ws, w.resid), at<float>(ws, w.y), at<float>(ws, w.sh_parts),
+                                   at<float>(ws, w.gates), at<int32_t>(ws, w.inv_perm), R, d.d_model, d.top_k, next_g,
+                                   next_out, d.norm_eps, bf, status, P.s));
+  }
   return DG_OK;
 }
 
@@ -533,6 +539,7 @@ SampScratch samp_scratch(void* ws, const Layout& w) {
 // p_hat_0 in place, the split-K product with E (through its transpose, K-contiguous), the parts
 // summed in order into the block's input, then the gated feed-forward block into sc_out (fp32).
 dg_status self_cond_into(const dg_ctx* c, int R, void* ws, const Layout& w, float* sc_out, hipStream_t s) {
+  ProfScope ps(c, DG_PROF_SELF_COND, s);
   const dg_model_desc& d = c->d;
   const int bf = d.act_dtype == DG_BF16;
   const int bn = sampler_bn(bf);
@@ -604,7 +611,10 @@ dg_status sample_into(dg_ctx* c, const void* hidden, int32_t* canvas, uint8_t* l
   st.stats = sc.stats; st.status = sc.status;
   st.steps_taken = steps_taken; st.done_out = done_out;
   st.canvas_rng = canvas_rng; st.lam_table = lam_table;
-  HIPCHK(launch_step_merge(st, s));
+  {
+    ProfScope ps(c, DG_PROF_STEP, s);
+    HIPCHK(launch_step_merge(st, s));
+  }
   if (sc_out) return self_cond_into(c, R, ws, *w, sc_out, s);
   return DG_OK;
 }
@@ -840,10 +850,13 @@ dg_status dg_denoise_step(dg_ctx* ctx, const dg_kv* kv, const int32_t* canvas, c
   Pass P{ctx, kv, kv->batch, L, 0, ws, layout(d, kv->batch, L, mp), stream};
   const int R = P.B * L;
   const int bf = d.act_dtype == DG_BF16;
-  if (resid_in) HIPCHK(launch_copy_f32(resid_in, at<float>(ws, P.w.resid), (int64_t)R * d.d_model, stream));
-  else HIPCHK(launch_embed(canvas, ctx->embed, at<float>(ws, P.w.resid), R, d.d_model, d.vocab, bf, stream, sc_in));
-  HIPCHK(launch_rope_table(at<float2>(ws, P.w.rope), R, L, d.head_dim, std::log2((double)d.rope_theta),
-                           kv->prefix_len, kv->max_prefix, at<int>(ws, P.w.status), stream));
+  {
+    ProfScope ps(ctx, DG_PROF_EMBED, stream);
+    if (resid_in) HIPCHK(launch_copy_f32(resid_in, at<float>(ws, P.w.resid), (int64_t)R * d.d_model, stream));
+    else HIPCHK(launch_embed(canvas, ctx->embed, at<float>(ws, P.w.resid), R, d.d_model, d.vocab, bf, stream, sc_in));
+    HIPCHK(launch_rope_table(at<float2>(ws, P.w.rope), R, L, d.head_dim, std::log2((double)d.rope_theta),
+                             kv->prefix_len, kv->max_prefix, at<int>(ws, P.w.status), stream));
+  }
   // each layer's combine writes the next layer's normalised rows, the last one the final norm
   for (int l = layer_begin; l < layer_end; ++l) {
     const bool last = l + 1 == layer_end;

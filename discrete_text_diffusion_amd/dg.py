@@ -291,8 +291,9 @@ def dg_init_canvas(canvas, lock, batch, L, vocab, seed, stream=None):
 
 
 PROF_MOE_GATE_UP, PROF_MOE_DOWN, PROF_ATTENTION, PROF_SAMPLER, PROF_QKV, PROF_O_PROJ, PROF_SHARED, \
-    PROF_ROUTING = range(8)
-PROF_NAMES = ("moe_gate_up", "moe_down", "attention", "sampler", "qkv_rope", "o_proj", "shared_expert", "routing")
+    PROF_ROUTING, PROF_SELF_COND, PROF_NORM_COMBINE, PROF_STEP, PROF_EMBED = range(12)
+PROF_NAMES = ("moe_gate_up", "moe_down", "attention", "sampler", "qkv_rope", "o_proj", "shared_expert", "routing",
+              "self_condition", "norm_combine", "step_merge", "embed_rope")
 
 
 def dg_profile_enable(ctx, mask):

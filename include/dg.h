@@ -346,7 +346,12 @@ typedef enum {
   DG_PROF_MOE_GATE_UP = 0, DG_PROF_MOE_DOWN = 1, DG_PROF_ATTENTION = 2, DG_PROF_SAMPLER = 3,
   DG_PROF_QKV = 4, DG_PROF_O_PROJ = 5,
   DG_PROF_SHARED = 6,   /* records nothing: the shared expert runs inside the two MoE launches */
-  DG_PROF_ROUTING = 7, DG_PROF_N = 8
+  DG_PROF_ROUTING = 7,
+  DG_PROF_SELF_COND = 8,   /* the self-conditioning product with E and its feed-forward block */
+  DG_PROF_NORM_COMBINE = 9,/* residual adds fused with RMSNorm, and the MoE combine (with the next norm) */
+  DG_PROF_STEP = 10,       /* the merge of the sampler's partials and the Step */
+  DG_PROF_EMBED = 11,      /* canvas embedding and the RoPE angle table */
+  DG_PROF_N = 12
 } dg_prof_class;
 
 /* Starts recording a pair of events around every launch of the classes in `mask` (bit i =
