@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--self-cond", action="store_true",
                     help="give the model a self-conditioning block (hidden width 896) and feed each step's "
                          "signal into the next step (a variant of the workload, not the headline)")
+    ap.add_argument("--prefill", action="store_true",
+                    help="time the causal encoder instead: context encoding of the workload's prefix in one call, "
+                         "then the append-after-encode pass of one canvas (one JSON line of its own)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed region, copy 512 MiB device to device 4 times (a plain copy of known "
                          "size for scaling hardware byte counters)")
@@ -172,12 +175,89 @@ def cpu_baseline(cfg, W, kv, H_dev):
                        f"global layers = {t_step:.1f} s per step; {sample_s:.1f} s measured")}
 
 
+def run_prefill(args):
+    """dg_prefill_kv at the workload's widths: encoding a `prefix`-token prompt from an empty cache in
+    one call, then appending one `canvas`-token block at that prefix (the K - 1 append passes of
+    block-AR generation).  Tokens per second of each, the median of the timed runs, with a per-class
+    breakdown of one run each."""
+    import numpy as np
+    import torch
+    from discrete_text_diffusion_amd import dg
+    from discrete_text_diffusion_amd.model import Model, values_dmajor
+    from synth import configs, gen
+
+    cfg0 = configs.get(args.workload)
+    P, L = cfg0.prefix, cfg0.canvas
+    cfg = cfg0.replace(batch=1, prefix=P + L)                # cache room for the appended block
+    dev = torch.device("cuda:0")
+    log(f"[prefill] {cfg.name}: encode {P} tokens, then append {L}")
+    W = gen.make_weights(cfg, dev)
+    kv = values_dmajor(gen.empty_kv(cfg, dev))
+    model = Model(cfg, W, kv, [0])
+    ws = model.workspace(1, P, P + L)
+    toks = gen.uniform_tokens((1, P + L), cfg.vocab, cfg.seed, "prefill-tokens", dev)
+    prompt, block = toks[:, :P].contiguous(), toks[:, P:].contiguous()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps, profile=False):
+        out = []
+        for _ in range(reps):
+            model.set_kv(kv, [0])
+            fn(True)
+            torch.cuda.synchronize()
+            if profile:
+                dg.dg_profile_enable(model.ctx, (1 << len(dg.PROF_NAMES)) - 1)
+            ev0.record(stream)
+            fn(False)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            dg.dg_profile_enable(model.ctx, 0)
+            out.append(ev0.elapsed_time(ev1))
+        return out
+
+    def encode(setup):
+        if not setup:
+            model.prefill_kv(prompt, ws, stream=stream)
+
+    def append(setup):
+        if setup:
+            model.prefill_kv(prompt, ws, stream=stream)
+        else:
+            model.prefill_kv(block, ws, stream=stream)
+
+    res = {}
+    for name, fn, n in (("encode", encode, P), ("append", append, L)):
+        timed(fn, 1)                                            # warm-up
+        runs = timed(fn, max(args.repeats, 1))
+        ms = float(np.median(runs))
+        timed(fn, 1, profile=True)
+        bd = {}
+        for c, cname in enumerate(dg.PROF_NAMES):
+            t, k = dg.dg_profile_read(model.ctx, c)
+            if k:
+                bd[cname] = {"ms": round(t, 3), "launches": k}
+        res[name] = {"tokens": n, "ms": round(ms, 3), "ms_runs": [round(x, 3) for x in runs],
+                     "tokens_per_s": round(n / (ms * 1e-3), 1), "breakdown": bd}
+        log(f"[prefill] {name}: {n} tokens in {ms:.3f} ms ({n / (ms * 1e-3):.0f} tokens/s)")
+    assert dg.dg_query_status(model.ctx, ws) == dg.DG_OK
+    out = {"metric": "causal encoder tokens/s (context encoding and append-after-encode, 1 MI355X)",
+           "value": res["encode"]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True,
+           "dtype": cfg.act_dtype, "data": "synthetic (seeded N(0,0.02) weights, uniform tokens)",
+           "config": {"workload": f"{args.workload} widths: prefill {P} + append {L}", "layers": cfg.n_layers,
+                      "d_model": cfg.d_model, "experts": cfg.n_experts, "top_k": cfg.top_k},
+           "encode": res["encode"], "append": res["append"]}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
+    if args.prefill:
+        return run_prefill(args)
     import numpy as np
     import torch
     from discrete_text_diffusion_amd import dg
