@@ -18,5 +18,8 @@ Parity status per function:
                          MoE expectations (pre-norm composition, both residual adds)
   selfcond               pinned by closed forms (argmax row at low temperature, mean row at equal
                          logits), an explicit loop, relabelling invariance and the zero-signal loop
+  numerics.quant_rows_e4m3 / model.act_quantiser (W8A8 experts)
+                         pinned to torch's e4m3 cast, code round trips, hand ties, saturation, the
+                         half-step error bound and an exact special case
   everything else        pinned by closed forms, invariants or brute force in tests/test_oracle_*.py
 """

@@ -18,7 +18,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .numerics import dequant_rows, mxfp4_dequant, rounder
+from .numerics import dequant_rows, mxfp4_dequant, quant_rows_e4m3, rounder
 
 
 # ---------------------------------------------------------------- weights in float64 -----------
@@ -177,10 +177,27 @@ def silu(x):
     return x / (1.0 + np.exp(-x))
 
 
-def swiglu(x, Wg, Wu, Wd, rnd):
-    """SwiGLU FFN: A = silu(x Wg^T) * (x Wu^T), stored (rnd); y = A Wd^T (wide)."""
+def swiglu(x, Wg, Wu, Wd, rnd, act_q=None):
+    """SwiGLU FFN: A = silu(x Wg^T) * (x Wu^T), stored (rnd); y = A Wd^T (wide).  With act_q (W8A8
+    experts) both GEMM inputs, x and A, pass through it (per-row e4m3 quantisation) first."""
+    if act_q is not None:
+        x = act_q(x)
     A = rnd(silu(x @ Wg.T) * (x @ Wu.T))
+    if act_q is not None:
+        A = act_q(A)
     return A @ Wd.T
+
+
+def act_quantiser(cfg):
+    """The expert GEMMs' activation quantisation: per-row dynamic e4m3 (W8A8 experts), or None.
+
+    Reading (the pages measure FP8 builds but fix no scheme): each row of the expert input (the
+    normalised rows, and the SwiGLU product before the down matrix) is scaled by its own
+    max|x| / 448 and rounded to e4m3; the weights keep their per-output-row scales, so a product is
+    (codes . codes) * s_row * s_col."""
+    if getattr(cfg, "act_quant", "") != "fp8":
+        return None
+    return lambda x: quant_rows_e4m3(x)[0]
 
 
 def moe(cfg, a2, lw, rnd, forced_idx=None):
@@ -200,14 +217,15 @@ def moe(cfg, a2, lw, rnd, forced_idx=None):
         w = np.exp(sel - sel.max(axis=1, keepdims=True))
         gates = w / w.sum(axis=1, keepdims=True)
     T = a2.shape[0]
+    aq = act_quantiser(cfg)
     y = np.zeros((T, cfg.top_k, a2.shape[1]))
     for e in np.unique(idx):
         rows, slots = np.nonzero(idx == e)
-        y[rows, slots] = swiglu(a2[rows], lw["w_gate"][e], lw["w_up"][e], lw["w_down"][e], rnd)
+        y[rows, slots] = swiglu(a2[rows], lw["w_gate"][e], lw["w_up"][e], lw["w_down"][e], rnd, aq)
     out = np.zeros_like(a2)
     for s in range(cfg.top_k):
         out = out + gates[:, s:s + 1] * y[:, s]
-    out = out + swiglu(a2, lw["sh_gate"], lw["sh_up"], lw["sh_down"], rnd)
+    out = out + swiglu(a2, lw["sh_gate"], lw["sh_up"], lw["sh_down"], rnd, aq)
     return out, {"r32": r32, "idx": idx, "gates": gates}
 
 

@@ -68,6 +68,37 @@ def dequant_rows(codes, scales):
     return _E4M3[np.asarray(codes, dtype=np.uint8)] * np.asarray(scales, dtype=np.float64)[..., None]
 
 
+E4M3_MAX = 448.0
+
+
+def round_e4m3(x):
+    """Nearest e4m3 value (ties to even) of float64 x, saturating at +-448.
+
+    For |x| in [2^e, 2^(e+1)) with e >= -6 the spacing is 2^(e-3); below 2^-6 (subnormals) it is
+    2^-9.  Ties to even: np.round halves to even, and scaling by a power of two is exact."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    out = np.zeros_like(a)
+    nz = a > 0
+    _, ex = np.frexp(a[nz])                  # a = m * 2^ex, m in [0.5, 1)  ->  e = ex - 1
+    e = np.maximum(ex - 1, -6)
+    ulp = np.ldexp(1.0, e - 3)
+    out[nz] = np.minimum(np.round(a[nz] / ulp) * ulp, E4M3_MAX)
+    return np.sign(x) * out
+
+
+def quant_rows_e4m3(x):
+    """Per-row dynamic e4m3 quantisation of activations x [..., K] (bf16-valued float64): the row's
+    scale s = fp32(max|x|) / 448 in float32, each element coded as the nearest e4m3 value of the
+    float32 quotient fp32(x) / s (IEEE division, the decision the kernels take in float32); an
+    all-zero row has s = 1.  Returns (dequantised values q * s as float64, s as float64)."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    amax = np.max(np.abs(x32), axis=-1, keepdims=True)
+    s = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    q = round_e4m3((x32 / s).astype(np.float64))
+    return q * s.astype(np.float64), s[..., 0].astype(np.float64)
+
+
 def e2m1_decode_table():
     """Value of each of the 16 e2m1 codes, from the format definition: exponent field 0 is
     subnormal (m / 2), otherwise (1 + m / 2) * 2^(e - 1)."""

@@ -57,6 +57,7 @@ class Workload:
     norm_eps: float = 1e-6
     weight_std: float = 0.02
     sc_hidden: int = 0     # >0: a self-conditioning block of this hidden width (896 at the Gemma-like widths)
+    act_quant: str = ""    # "fp8": the expert GEMMs take per-row e4m3 activations (W8A8, with fp8 experts)
 
     def is_global(self, layer: int) -> bool:
         if self.window <= 0 or self.global_every <= 0:
