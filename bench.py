@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--experts", choices=("bf16", "fp8", "mxfp4"), default=None,
                     help="expert weight format (default: the workload's); fp8 and mxfp4 are weights-only "
                          "formats with bf16 activations")
+    ap.add_argument("--act-fp8", action="store_true",
+                    help="W8A8 experts: fp8 weights and per-row e4m3 activation codes on the fp8 MFMA "
+                         "(a variant of the workload, not the headline)")
     ap.add_argument("--self-cond", action="store_true",
                     help="give the model a self-conditioning block (hidden width 896) and feed each step's "
                          "signal into the next step (a variant of the workload, not the headline)")
@@ -267,6 +270,11 @@ def main():
     cfg = configs.get(args.workload)
     if args.experts is not None and args.experts != cfg.expert_dtype:
         cfg = cfg.replace(expert_dtype=args.experts, name=f"{cfg.name}-{args.experts}experts")
+    if args.act_fp8:
+        if cfg.expert_dtype != "fp8":
+            print("--act-fp8 needs fp8 expert weights (--experts fp8)", file=sys.stderr)
+            sys.exit(2)
+        cfg = cfg.replace(act_quant="fp8", name=f"{cfg.name}-w8a8")
     if args.self_cond:
         if args.sampler == "eb":
             print("--self-cond runs with the Euler sampler's step calls", file=sys.stderr)
@@ -412,7 +420,8 @@ def main():
         "repeats": len(reps), "ms_per_step_runs": [round(x, 4) for x in reps],
         "steps_per_s": round(steps_per_s, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": cfg.act_dtype if cfg.expert_dtype in ("f32", "bf16") else f"bf16+{cfg.expert_dtype}w",
+        "dtype": (cfg.act_dtype if cfg.expert_dtype in ("f32", "bf16") else f"bf16+{cfg.expert_dtype}w"
+                  + ("+fp8a" if getattr(cfg, "act_quant", "") == "fp8" else "")),
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) caches, uniform canvas)",
         "config": {"workload": f"{args.workload}: {cfg.name}", "layers": cfg.n_layers, "batch": B, "canvas": L,
                    "prefix": cfg.prefix, "vocab": cfg.vocab, "d_model": cfg.d_model, "experts": cfg.n_experts,

@@ -15,8 +15,10 @@ namespace dg {
 
 struct fp8_t { uint8_t v; };    // storage tag for e4m3 weights
 struct fp4x2_t { uint8_t v; };  // storage tag for MXFP4 weights: two e2m1 codes per byte, element 2j low
+struct fp8a_t { uint8_t v; };   // storage tag for e4m3 activation codes (W8A8: a scale per row)
 template <class T> constexpr bool is_fp8_v = std::is_same<T, fp8_t>::value;
 template <class T> constexpr bool is_fp4_v = std::is_same<T, fp4x2_t>::value;
+template <class T> constexpr bool is_fp8a_v = std::is_same<T, fp8a_t>::value;
 
 constexpr int ROW_BYTES = 128;            // data bytes of one operand row per K tile
 constexpr int ROW_STRIDE = 144;           // + 16 bytes of padding against bank conflicts

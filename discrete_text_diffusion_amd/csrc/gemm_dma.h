@@ -341,4 +341,124 @@ struct GemmDmaQ {
   }
 };
 
+// W8A8: both operands as e4m3 codes on the direct-to-LDS ring, multiplied by the fp8 MFMA
+// (v_mfma_f32_16x16x32_fp8_fp8, fp32 accumulation); the per-row and per-column scales are the
+// caller's epilogue.  A stage is 64 K-elements: A and B rows of 64 bytes, the 16-byte chunk c of row
+// r stored in slot c ^ ((r >> 1) & 3) (the conflict-free pattern of the fp8 weight ring).  Lane
+// group kg = lane >> 4 takes chunk kg (elements 16 kg .. + 15) of its A row and of its B row; the
+// low 8 bytes feed one MFMA and the high 8 bytes a second, so both operands carry the same K
+// elements in each MFMA slot and the sum over the stage is the plain dot product.
+template <int BM, int BN, int WM, int WN, int NS>
+struct GemmDmaQQ {
+  static constexpr int NW = WM * WN;
+  static constexpr int FM = BM / WM / 16, FN = BN / WN / 16;
+  static_assert(FM >= 1 && FN >= 1, "wave tile at least 16 x 16");
+  static constexpr int KT = 64;                          // K elements (bytes) per stage
+  static constexpr int IA = BM / (16 * NW), IB = BN / (16 * NW);   // 16 rows per load instruction
+  static_assert(IA * 16 * NW == BM && IB * 16 * NW == BN, "rows per tile: whole load instructions");
+  static constexpr int LPT = IA + IB;                    // load instructions per wave per stage
+  static constexpr int A_BYTES = BM * 64, B_BYTES = BN * 64;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int LDS_BYTES = NS * STAGE;
+  static_assert(NS >= 2 && (NS - 2) * LPT < 64, "stages / vmcnt range");
+
+  const char* a_src[IA];
+  const char* b_src[IB];
+
+  template <class ARow, class BRow, class SRow>
+  DG_DEV void setup(ARow arow, BRow brow, SRow) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rr = lane >> 2, slot = lane & 3;
+#pragma unroll
+    for (int i = 0; i < IA; ++i) {
+      const int r = (wave + NW * i) * 16 + rr;
+      const char* p = reinterpret_cast<const char*>(arow(r));
+      if (!p) p = reinterpret_cast<const char*>(arow(0));
+      a_src[i] = p + ((slot ^ ((r >> 1) & 3)) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < IB; ++i) {
+      const int r = (wave + NW * i) * 16 + rr;
+      const char* p = reinterpret_cast<const char*>(brow(r));
+      if (!p) p = reinterpret_cast<const char*>(brow(0));
+      b_src[i] = p + ((slot ^ ((r >> 1) & 3)) * 16);
+    }
+  }
+
+  DG_DEV void issue(char* lds, int kt, int stage) {
+    const int wave = threadIdx.x >> 6;
+    char* st = lds + stage * STAGE;
+#pragma unroll
+    for (int i = 0; i < IA; ++i) dma16(a_src[i] + (size_t)kt * 64, st + (wave + NW * i) * 1024);
+#pragma unroll
+    for (int i = 0; i < IB; ++i)
+      dma16<DMA_STREAM>(b_src[i] + (size_t)kt * 64, st + A_BYTES + (wave + NW * i) * 1024);
+  }
+
+  template <int P>
+  DG_DEV static void wait_pending(int pending) {
+    if constexpr (P > 1) {
+      if (pending >= P) { wait_vm<(P - 1) * LPT>(); return; }
+      wait_pending<P - 1>(pending);
+    } else {
+      wait_vm<0>();
+    }
+  }
+  DG_DEV static void wait_oldest(int pending) { wait_pending<NS - 1>(pending); }
+
+  DG_DEV static void compute(const char* st, f32x4_v (&acc)[FM][FN]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int l16 = lane & 15, kg = lane >> 4;
+    u32x4 bf[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = wn * FN * 16 + j * 16 + l16;
+      bf[j] = *reinterpret_cast<const u32x4*>(st + A_BYTES + n * 64 + ((kg ^ ((n >> 1) & 3)) * 16));
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int m = wm * FM * 16 + i * 16 + l16;
+      const u32x4 af = *reinterpret_cast<const u32x4*>(st + m * 64 + ((kg ^ ((m >> 1) & 3)) * 16));
+      const long a_lo = (long)(((uint64_t)af.y << 32) | af.x), a_hi = (long)(((uint64_t)af.w << 32) | af.z);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const long b_lo = (long)(((uint64_t)bf[j].y << 32) | bf[j].x);
+        const long b_hi = (long)(((uint64_t)bf[j].w << 32) | bf[j].z);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a_lo, b_lo, acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a_hi, b_hi, acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
+  DG_DEV void run(char* lds, int K, f32x4_v (&acc)[FM][FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+    const int nk = K / KT;
+    int issued = 0;
+    for (; issued < NS - 1 && issued < nk; ++issued) issue(lds, issued, issued);
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_oldest(issued - kt);
+      lds_barrier();
+      if (issued < nk) {
+        issue(lds, issued, issued % NS);
+        ++issued;
+      }
+      compute(lds + (kt % NS) * STAGE, acc);
+    }
+    __syncthreads();
+  }
+
+  DG_DEV static int row_of(int i, int e) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    return (wave / WN) * FM * 16 + i * 16 + 4 * (lane >> 4) + e;
+  }
+  DG_DEV static int col_of(int j) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    return (wave % WN) * FN * 16 + j * 16 + (lane & 15);
+  }
+};
+
 }  // namespace dg

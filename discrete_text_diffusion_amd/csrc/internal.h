@@ -20,10 +20,11 @@ struct GateScope {
 constexpr int MAX_BATCH = 64;     // canvases per call
 constexpr int GROUP_BM = 32;       // rows per expert tile of the grouped GEMMs
 constexpr int GROUP_BM_WIDE = 128; // ... once experts average 64 rows or more (batched canvases)
+constexpr int GROUP_BM_Q8 = 64;    // rows per routed tile below that with W8A8 experts
 // rows per routed expert tile for `picks` = rows x top_k routed rows over E experts
 inline int group_bm(int64_t picks, int E) { return picks >= (int64_t)64 * E ? GROUP_BM_WIDE : GROUP_BM; }
 
-enum WKind { W_F32 = 0, W_BF16 = 1, W_FP8 = 2, W_MXFP4 = 3 };
+enum WKind { W_F32 = 0, W_BF16 = 1, W_FP8 = 2, W_MXFP4 = 3, W_FP8A8 = 4 };  // W_FP8A8: fp8 weights, e4m3 activations
 enum Epi { EPI_STORE_F32 = 0, EPI_ADD_F32 = 1, EPI_STORE_ACT = 2, EPI_SWIGLU = 3, EPI_QKV = 4 };
 
 struct DenseArgs {
@@ -68,7 +69,8 @@ struct GroupedArgs {
   const void* sh_sB; const void* sh_sB2; int64_t sh_s_ld;
   int shN, shK, sh_rows;
   void* shC; int64_t sh_ldc;
-  int bm;                                             // rows per routed tile: GROUP_BM or GROUP_BM_WIDE
+  int bm;                                             // rows per routed tile: GROUP_BM, GROUP_BM_Q8 or GROUP_BM_WIDE
+  const float* sA; const float* sh_sA;                // W8A8: fp32 scale per A row (source row or grouped position)
   int nt_r, nt_s, sh_blocks, n_sh_items;              // filled by the launcher
   const int32_t* gate;                                // launch gate (set by the launcher)
 };
@@ -106,6 +108,9 @@ hipError_t launch_attn_merge(const AttnArgs& a, int act_bf16, hipStream_t s);
 // resid[r] = embed[tokens[r]] (+ add[r] when add is non-null: the self-conditioning signal)
 hipError_t launch_embed(const int32_t* tokens, const void* embed, float* resid, int rows, int d,
                         int vocab, int act_bf16, hipStream_t s, const float* add = nullptr);
+// per-row dynamic e4m3 quantisation of bf16 rows x [rows][K] (row stride ldx): s[r] = max|x| / 448
+// (fp32; 1 for an all-zero row), q[r][k] = nearest e4m3 code of x / s (ties to even, saturating)
+hipError_t launch_quant_rows(const void* x, int64_t ldx, int rows, int K, uint8_t* q, float* s, hipStream_t st);
 // out[i] = act(sum over nparts of parts[p * pstride + i]), parts summed in order
 hipError_t launch_sum_parts_cast(const float* parts, int nparts, int64_t pstride, void* out, int64_t n, int act_bf16,
                                  hipStream_t s);

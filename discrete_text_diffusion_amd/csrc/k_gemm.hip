@@ -24,9 +24,11 @@ using TileFor = std::conditional_t<sizeof(TB) == 1, GemmTile<TA, TB, BM, BN, WM,
 // registers (12 KB stages x 6, two blocks per CU); MXFP4 weights go through the register-staged
 // engine, which measured faster for them (its stages carry 64 elements of all 128 rows widened
 // once per block, where the ring's per-stage scale loads and short stages cost more)
+// W8A8 (e4m3 activation codes with fp8 weights): both operands as codes on the ring, fp8 MFMA
 template <class TA, class TB, int BM, int BN, int WM, int WN, int NS = 0, int QNS = 6>
-using GroupTileFor = std::conditional_t<is_fp8_v<TB>, GemmDmaQ<TB, BM, BN, WM, WN, QNS>,
-                                        TileFor<TA, TB, BM, BN, WM, WN, NS>>;
+using GroupTileFor = std::conditional_t<
+    is_fp8a_v<TA>, GemmDmaQQ<BM, BN, WM, WN, QNS>,
+    std::conditional_t<is_fp8_v<TB>, GemmDmaQ<TB, BM, BN, WM, WN, QNS>, TileFor<TA, TB, BM, BN, WM, WN, NS>>>;
 
 // ---------------------------------------------------------------- B-row maps ----------------
 // A tile column block of 16 columns; "paired" maps put the two members of a pair (gate/up, or
@@ -224,10 +226,16 @@ hipError_t launch_rope_table(float2* tab, int rows, int rows_per_canvas, int hea
 // ---------------------------------------------------------------- grouped (MoE) ----------------
 // One tile: rows [row0, row0 + rows) of A (through a_tok, or in order) times the weight rows from
 // n0 (gate/up rows paired for SwiGLU) over the full K, then the tile's epilogue.
+// W8A8: A holds e4m3 codes with the row scale sA[source row]; the SwiGLU product is stored in bf16.
 template <class G, int BN, int WN, int EPI, class TA, class TB>
 DG_DEV void grouped_tile(char* lds, const TA* A, int64_t lda, const int32_t* a_tok, int row0, int rows,
                          const TB* B, const TB* B2, int64_t ldb, const char* sB, const char* sB2, int64_t s_ld,
-                         int N, int K, int n0, void* Cout, int64_t ldc) {
+                         int N, int K, int n0, void* Cout, int64_t ldc, const float* sA) {
+  using TO = std::conditional_t<is_fp8a_v<TA>, bf16_t, TA>;
+  auto ascale = [&](int r) -> float {
+    if constexpr (is_fp8a_v<TA>) return sA[a_tok ? a_tok[row0 + r] : row0 + r];
+    else return 1.f;
+  };
   auto arow = [&](int r) -> const TA* {
     if (r >= rows) return nullptr;
     const int src = a_tok ? a_tok[row0 + r] : row0 + r;
@@ -285,9 +293,10 @@ DG_DEV void grouped_tile(char* lds, const TA* A, int64_t lda, const int32_t* a_t
         for (int q = 0; q < 4; ++q) {
           const int r = G::row_of(i, q);
           if (r >= rows) continue;
-          const float gt = acc[i][j][q] * sg, up = acc[i][j + 1][q] * su;
+          const float sa = ascale(r);
+          const float gt = acc[i][j][q] * sg * sa, up = acc[i][j + 1][q] * su * sa;
           const float a = gt / (1.f + __expf(-gt)) * up;
-          static_cast<TA*>(Cout)[(int64_t)(row0 + r) * ldc + oc] = Elem<TA>::from_f(a);
+          static_cast<TO*>(Cout)[(int64_t)(row0 + r) * ldc + oc] = Elem<TO>::from_f(a);
         }
     }
   } else {  // EPI_STORE_F32
@@ -303,7 +312,7 @@ DG_DEV void grouped_tile(char* lds, const TA* A, int64_t lda, const int32_t* a_t
         for (int q = 0; q < 4; ++q) {
           const int r = G::row_of(i, q);
           if (r >= rows) continue;
-          static_cast<float*>(Cout)[(int64_t)(row0 + r) * ldc + n] = acc[i][j][q] * sc;
+          static_cast<float*>(Cout)[(int64_t)(row0 + r) * ldc + n] = acc[i][j][q] * sc * ascale(r);
         }
     }
   }
@@ -344,7 +353,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_grouped_kernel(GroupedArgs 
     }
     if (item >= *p.n_items) return;
     const int e = p.work[2 * item], m0 = p.work[2 * item + 1], rows = min(BM, p.counts[e] - m0);
-    if constexpr (XCDR) {
+    if constexpr (XCDR && !is_fp8a_v<TA>) {
       if (rows <= BM / 2) {
         using GH = GroupTileFor<TA, TB, BM / 2, BN, WM, WN, NS, QNS>;
         grouped_tile<GH, BN, WN, EPI>(lds, static_cast<const TA*>(p.A), p.lda, p.a_tok, p.offsets[e] + m0, rows,
@@ -352,7 +361,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_grouped_kernel(GroupedArgs 
                                       p.B2 ? static_cast<const TB*>(p.B2) + (int64_t)e * p.b_estride : nullptr, p.ldb,
                                       p.sB ? static_cast<const char*>(p.sB) + (int64_t)e * p.s_estride : nullptr,
                                       p.sB2 ? static_cast<const char*>(p.sB2) + (int64_t)e * p.s_estride : nullptr,
-                                      p.s_ld, p.N, p.K, col * BN, p.C, p.ldc);
+                                      p.s_ld, p.N, p.K, col * BN, p.C, p.ldc, p.sA);
         return;
       }
     }
@@ -361,7 +370,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_grouped_kernel(GroupedArgs 
                                  p.B2 ? static_cast<const TB*>(p.B2) + (int64_t)e * p.b_estride : nullptr, p.ldb,
                                  p.sB ? static_cast<const char*>(p.sB) + (int64_t)e * p.s_estride : nullptr,
                                  p.sB2 ? static_cast<const char*>(p.sB2) + (int64_t)e * p.s_estride : nullptr,
-                                 p.s_ld, p.N, p.K, col * BN, p.C, p.ldc);
+                                 p.s_ld, p.N, p.K, col * BN, p.C, p.ldc, p.sA);
   } else {
     const int j = id >> 3;
     const int it = j % p.n_sh_items, nt = (j / p.n_sh_items) * 8 + (id & 7);
@@ -370,7 +379,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_grouped_kernel(GroupedArgs 
                                   min(BMS, p.sh_rows - it * BMS), static_cast<const TB*>(p.shB),
                                   static_cast<const TB*>(p.shB2), p.sh_ldb, static_cast<const char*>(p.sh_sB),
                                   static_cast<const char*>(p.sh_sB2), p.sh_s_ld, p.shN, p.shK, nt * BN,
-                                  p.shC, p.sh_ldc);
+                                  p.shC, p.sh_ldc, p.sh_sA);
   }
 }
 
@@ -526,7 +535,24 @@ static hipError_t grouped_dispatch(const GroupedArgs& a, int max_items, hipStrea
   }
 }
 
+// W8A8: routed tiles of GROUP_BM_Q8 rows (four waves side by side) or, for batched canvases, 128 x 256
+// tiles on 8 waves (2 x 4); shared-expert tiles of 128 rows; fp8 MFMA throughout
+static hipError_t grouped_q8(const GroupedArgs& a, int max_items, hipStream_t s) {
+  if (a.bm == GROUP_BM_WIDE) {
+    constexpr int W = GROUP_BM_WIDE;
+    if (a.epi == EPI_SWIGLU)
+      return launch_grouped_t<fp8a_t, fp8_t, W, W, 256, 2, 4, EPI_SWIGLU, 0, 3, 1>(a, 2 * a.N, 2 * a.shN, max_items, s);
+    return launch_grouped_t<fp8a_t, fp8_t, W, W, 256, 2, 4, EPI_STORE_F32, 0, 3, 1>(a, a.N, a.shN, max_items, s);
+  }
+  if (a.bm != GROUP_BM_Q8) return hipErrorInvalidValue;
+  if (a.epi == EPI_SWIGLU)
+    return launch_grouped_t<fp8a_t, fp8_t, GROUP_BM_Q8, 128, 128, 1, 4, EPI_SWIGLU, 0, 4>(a, 2 * a.N, 2 * a.shN,
+                                                                                       max_items, s);
+  return launch_grouped_t<fp8a_t, fp8_t, GROUP_BM_Q8, 128, 128, 1, 4, EPI_STORE_F32, 0, 4>(a, a.N, a.shN, max_items, s);
+}
+
 hipError_t launch_grouped(const GroupedArgs& a, int act_bf16, int w_kind, int max_items, hipStream_t s) {
+  if (w_kind == W_FP8A8) return grouped_q8(a, max_items, s);
   if (!act_bf16) return grouped_dispatch<float, float>(a, max_items, s);
   if (w_kind == W_FP8) return grouped_dispatch<bf16_t, fp8_t>(a, max_items, s);
   if (w_kind == W_MXFP4) return grouped_dispatch<bf16_t, fp4x2_t>(a, max_items, s);

@@ -59,6 +59,75 @@ hipError_t launch_sum_parts_cast(const float* parts, int nparts, int64_t pstride
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- W8A8 activation codes --------
+// Nearest OCP e4m3 (e4m3fn) code of a float32 value, ties to even, saturating at +-448.  From the
+// format: 4 exponent bits (bias 7), 3 mantissa bits, no infinities, S.1111.111 is NaN.  Below
+// 2^-6 the codes are subnormal with spacing 2^-9, so code = round(|q| / 2^-9); from 2^-6 up the
+// spacing in [2^e, 2^(e+1)) is 2^(e-3) and code = 8 (e + 7) + round(|q| / 2^(e-3)) - 8.  A mantissa
+// that rounds up to 16 lands on the next binade's first code, so both formulas run on into the
+// next range; 448 = 1.75 * 2^8 is code 0x7e, the largest finite one.
+DG_DEV uint32_t e4m3_code(float q) {
+  const uint32_t sign = (__float_as_uint(q) >> 24) & 0x80u;
+  const float a = fabsf(q);
+  uint32_t code;
+  if (!(a < 448.f)) {
+    code = 0x7eu;
+  } else if (a < 0.015625f) {                                  // 2^-6
+    code = (uint32_t)rintf(a * 512.f);                         // exact scaling by 2^9, then RNE
+  } else {
+    const int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;   // a is a normal float here
+    const float m = rintf(ldexpf(a, 3 - e));                   // in [8, 16], exact scaling
+    code = (uint32_t)((e + 7) * 8 + (int)m - 8);
+    code = code > 0x7eu ? 0x7eu : code;
+  }
+  return sign | code;
+}
+
+// One wave per row: s = max|x| / 448 in float32 (1 for a zero row), codes of x / s.  The build keeps
+// IEEE float division (no fast-math), so both quotients are correctly rounded.
+template <int WPB>
+__global__ __launch_bounds__(WPB * 64) void quant_rows_kernel(const bf16_t* x, int64_t ldx, int rows, int K,
+                                                             uint8_t* q, float* s, const int32_t* gate) {
+  if (gate_closed(gate)) return;
+  const int lane = threadIdx.x & 63, r = blockIdx.x * WPB + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const bf16_t* xr = x + (int64_t)r * ldx;
+  float amax = 0.f;
+  for (int k = lane * 8; k < K; k += 512) {
+    const uint4 v = *reinterpret_cast<const uint4*>(xr + k);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(w[h] << 16)), fabsf(__uint_as_float(w[h] & 0xffff0000u))));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  const float sc = amax > 0.f ? amax / 448.f : 1.f;
+  if (lane == 0) s[r] = sc;
+  uint8_t* qr = q + (int64_t)r * K;
+  for (int k = lane * 8; k < K; k += 512) {
+    const uint4 v = *reinterpret_cast<const uint4*>(xr + k);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t out[2] = {0u, 0u};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const uint32_t lo = e4m3_code(__uint_as_float(w[h] << 16) / sc);
+      const uint32_t hi = e4m3_code(__uint_as_float(w[h] & 0xffff0000u) / sc);
+      out[h >> 1] |= (lo | (hi << 8)) << (16 * (h & 1));
+    }
+    *reinterpret_cast<uint2*>(qr + k) = make_uint2(out[0], out[1]);
+  }
+}
+
+hipError_t launch_quant_rows(const void* x, int64_t ldx, int rows, int K, uint8_t* q, float* s, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (K % 8 || ldx % 8) return hipErrorInvalidValue;
+  constexpr int WPB = 4;
+  hipLaunchKernelGGL(quant_rows_kernel<WPB>, dim3((unsigned)((rows + WPB - 1) / WPB)), dim3(WPB * 64), 0, st,
+                     static_cast<const bf16_t*>(x), ldx, rows, K, q, s, launch_gate());
+  return hipGetLastError();
+}
+
 __global__ void copy_f32_kernel(const float* a, float* b, int64_t n, const int32_t* gate) {
   if (gate_closed(gate)) return;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;

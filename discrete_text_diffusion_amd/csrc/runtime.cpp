@@ -73,6 +73,7 @@ inline size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 inline int up8(int x) { return (x + 7) / 8 * 8; }
 inline int act_bytes(const dg_model_desc& d) { return d.act_dtype == DG_BF16 ? 2 : 4; }
 inline int w_kind(const dg_model_desc& d) {
+  if (d.expert_act_fp8) return W_FP8A8;
   return d.expert_dtype == DG_FP8E4M3 ? W_FP8 : d.expert_dtype == DG_MXFP4 ? W_MXFP4
                                       : d.expert_dtype == DG_BF16 ? W_BF16 : W_F32;
 }
@@ -115,6 +116,7 @@ struct Layout {
   size_t a_grp, y, sh_a, samp_part, hidden, done, n_locked, prev, lockbuf, all_done;
   size_t seq_state, seq_rng, seq_flags, lam_table;
   size_t sc_p, sc_ptile, sc_parts, sc_x, sc_a, sc_state;   // self-conditioning (sc_hidden > 0)
+  size_t q_x, q_xs, q_a, q_as, q_sh, q_shs;                // W8A8: e4m3 codes and row scales of the expert inputs
   size_t total;
   int max_items;
 };
@@ -175,6 +177,14 @@ Layout layout(const dg_model_desc& d, int B, int n, int max_prefix) {
     w.sc_x = take(R * d.d_model * ab);
     w.sc_a = take(R * d.sc_hidden * ab);
     w.sc_state = take(R * d.d_model * 4);
+  }
+  if (d.expert_act_fp8) {
+    w.q_x = take(R * d.d_model);
+    w.q_xs = take(R * 4);
+    w.q_a = take(Rk * d.expert_hidden);
+    w.q_as = take(Rk * 4);
+    w.q_sh = take(R * d.shared_hidden);
+    w.q_shs = take(R * 4);
   }
   w.total = o;
   return w;
@@ -431,7 +441,10 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn, bool xhat_ready, const vo
   HIPCHK(launch_dense(ra, bf, bf ? W_BF16 : W_F32, P.s));
   HIPCHK(launch_router_topk(at<float>(ws, w.rparts), ra.ksplit, ra.c_split, L.router_bias, R, d.n_experts, d.top_k,
                             at<float>(ws, w.rlogits), at<int32_t>(ws, w.idx), at<float>(ws, w.gates), P.s));
-  const int gbm = group_bm((int64_t)R * d.top_k, d.n_experts);
+  const int wk = w_kind(d);
+  const bool q8 = wk == W_FP8A8;
+  int gbm = group_bm((int64_t)R * d.top_k, d.n_experts);
+  if (q8 && gbm == GROUP_BM) gbm = GROUP_BM_Q8;
   // tiles the grouped launches may see: the workspace's bound is for GROUP_BM-row tiles
   const int max_items = gbm == GROUP_BM ? w.max_items : (R * d.top_k + gbm - 1) / gbm + d.n_experts;
   HIPCHK(launch_route_tables(at<int32_t>(ws, w.idx), R, d.n_experts, d.top_k, at<int32_t>(ws, w.counts),
@@ -439,7 +452,6 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn, bool xhat_ready, const vo
                              at<int32_t>(ws, w.tok), at<int32_t>(ws, w.work), at<int32_t>(ws, w.n_items),
                              gbm, P.s));
   route_scope.close();
-  const int wk = w_kind(d);
   // routed experts and the shared expert in one launch each: gate/up + SwiGLU, then down
   GroupedArgs ga{};
   ga.epi = EPI_SWIGLU;
@@ -463,6 +475,13 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn, bool xhat_ready, const vo
   ga.shC = at<void>(ws, w.sh_a); ga.sh_ldc = d.shared_hidden;
   {
     ProfScope ps(P.c, DG_PROF_MOE_GATE_UP, P.s);
+    if (q8) {
+      // W8A8: the normalised rows as e4m3 codes with a float32 scale per row, for both expert kinds
+      HIPCHK(launch_quant_rows(at<void>(ws, w.xhat), d.d_model, R, d.d_model, at<uint8_t>(ws, w.q_x),
+                               at<float>(ws, w.q_xs), P.s));
+      ga.A = ga.shA = at<void>(ws, w.q_x);
+      ga.sA = ga.sh_sA = at<float>(ws, w.q_xs);
+    }
     HIPCHK(launch_grouped(ga, bf, wk, max_items, P.s));
   }
   GroupedArgs da{};
@@ -482,6 +501,15 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn, bool xhat_ready, const vo
   da.shC = at<void>(ws, w.sh_parts); da.sh_ldc = d.d_model;
   {
     ProfScope ps(P.c, DG_PROF_MOE_DOWN, P.s);
+    if (q8) {
+      // the SwiGLU products (stored bf16) coded per row: routed rows in grouped order, shared rows in order
+      HIPCHK(launch_quant_rows(at<void>(ws, w.a_grp), d.expert_hidden, R * d.top_k, d.expert_hidden,
+                               at<uint8_t>(ws, w.q_a), at<float>(ws, w.q_as), P.s));
+      HIPCHK(launch_quant_rows(at<void>(ws, w.sh_a), d.shared_hidden, R, d.shared_hidden, at<uint8_t>(ws, w.q_sh),
+                               at<float>(ws, w.q_shs), P.s));
+      da.A = at<void>(ws, w.q_a); da.sA = at<float>(ws, w.q_as);
+      da.shA = at<void>(ws, w.q_sh); da.sh_sA = at<float>(ws, w.q_shs);
+    }
     HIPCHK(launch_grouped(da, bf, wk, max_items, P.s));
   }
   {
@@ -512,6 +540,9 @@ dg_status check_desc(const dg_model_desc& d) {
   if (!(d.expert_dtype == d.act_dtype ||
         (d.act_dtype == DG_BF16 && (d.expert_dtype == DG_FP8E4M3 || d.expert_dtype == DG_MXFP4))))
     return fail(DG_EUNSUPPORTED, "expert_dtype must equal act_dtype, or be FP8E4M3 / MXFP4 with BF16 activations");
+  if (d.expert_act_fp8 != 0 && d.expert_act_fp8 != 1) return fail(DG_EINVAL, "expert_act_fp8 must be 0 or 1");
+  if (d.expert_act_fp8 && !(d.expert_dtype == DG_FP8E4M3 && d.act_dtype == DG_BF16))
+    return fail(DG_EUNSUPPORTED, "expert_act_fp8 needs FP8E4M3 expert weights and BF16 activations");
   if (!(d.norm_eps >= 0.f) || !(d.rope_theta > 0.f)) return fail(DG_EINVAL, "bad norm_eps or rope_theta");
   if (d.window > 0 && d.global_every > 0 && d.window < 1) return fail(DG_EINVAL, "bad window");
   return DG_OK;
@@ -1297,5 +1328,37 @@ dg_status dg_test_noise(const int32_t* x0, int32_t* xt, int32_t batch, int32_t L
   return DG_OK;
 }
 
+dg_status dg_test_read_expert_inputs(const dg_ctx* ctx, const void* ws, int32_t batch, int32_t L, void* xhat,
+                                     uint8_t* xq, float* xs, void* a_grp, uint8_t* aq, float* as, void* sh_a,
+                                     uint8_t* shq, float* shs, hipStream_t stream) {
+  g_err.clear();
+  if (!ctx || !ws || batch < 1 || L < 1) return fail(DG_EINVAL, "bad argument");
+  const dg_model_desc& d = ctx->d;
+  if (!d.expert_act_fp8 && (xq || xs || aq || as || shq || shs))
+    return fail(DG_EINVAL, "activation codes exist only with expert_act_fp8 = 1");
+  const Layout w = layout(d, batch, L, 0);
+  const char* base = static_cast<const char*>(ws);
+  const size_t R = (size_t)batch * L, Rk = R * d.top_k, ab = act_bytes(d);
+  auto cp = [&](void* dst, size_t off, size_t bytes) -> hipError_t {
+    return dst ? hipMemcpyAsync(dst, base + off, bytes, hipMemcpyDeviceToDevice, stream) : hipSuccess;
+  };
+  HIPCHK(cp(xhat, w.xhat, R * d.d_model * ab));
+  HIPCHK(cp(a_grp, w.a_grp, Rk * d.expert_hidden * ab));
+  HIPCHK(cp(sh_a, w.sh_a, R * d.shared_hidden * ab));
+  HIPCHK(cp(xq, w.q_x, R * d.d_model));
+  HIPCHK(cp(xs, w.q_xs, R * 4));
+  HIPCHK(cp(aq, w.q_a, Rk * d.expert_hidden));
+  HIPCHK(cp(as, w.q_as, Rk * 4));
+  HIPCHK(cp(shq, w.q_sh, R * d.shared_hidden));
+  HIPCHK(cp(shs, w.q_shs, R * 4));
+  return DG_OK;
+}
+
+dg_status dg_test_quant_rows(const void* x, int32_t rows, int32_t K, uint8_t* q, float* s, hipStream_t stream) {
+  g_err.clear();
+  if (!x || !q || !s || rows < 1 || K < 8 || K % 8) return fail(DG_EINVAL, "bad argument");
+  HIPCHK(launch_quant_rows(x, K, rows, K, q, s, stream));
+  return DG_OK;
+}
 
 }  // extern "C"

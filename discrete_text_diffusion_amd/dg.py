@@ -28,7 +28,7 @@ class ModelDesc(C.Structure):
                                           "n_experts", "top_k", "expert_hidden", "shared_hidden", "vocab",
                                           "window", "global_every")] + \
                [("rope_theta", C.c_float), ("norm_eps", C.c_float), ("act_dtype", C.c_int), ("expert_dtype", C.c_int),
-                ("sc_hidden", C.c_int32)]
+                ("sc_hidden", C.c_int32), ("expert_act_fp8", C.c_int32)]
 
 
 LAYER_FIELDS = ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_router", "router_bias", "w_gate", "w_up", "w_down",
@@ -114,6 +114,8 @@ EXPORTS = {
                                       C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "dg_test_read_routing": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
                                        C.c_void_p]),
+    "dg_test_read_expert_inputs": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32] + [C.c_void_p] * 10),
+    "dg_test_quant_rows": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]),
     "dg_test_noise": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int, C.c_float,
                                 C.c_uint64, C.c_uint32, C.c_void_p]),
     "dg_init_canvas": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_uint64, C.c_void_p]),
@@ -280,6 +282,17 @@ def dg_test_router_topk(scores, T, E, k, idx, gates, counts, offsets, perm, ws, 
 
 def dg_test_read_routing(ctx, ws, rows, logits=None, idx=None, gates=None, stream=None):
     _check(load().dg_test_read_routing(ctx, _ptr(ws), rows, _ptr(logits), _ptr(idx), _ptr(gates), _stream(stream)))
+
+
+def dg_test_read_expert_inputs(ctx, ws, batch, L, xhat=None, xq=None, xs=None, a_grp=None, aq=None, as_=None,
+                               sh_a=None, shq=None, shs=None, stream=None):
+    _check(load().dg_test_read_expert_inputs(ctx, _ptr(ws), batch, L, _ptr(xhat), _ptr(xq), _ptr(xs), _ptr(a_grp),
+                                             _ptr(aq), _ptr(as_), _ptr(sh_a), _ptr(shq), _ptr(shs),
+                                             _stream(stream)))
+
+
+def dg_test_quant_rows(x, rows, K, q, s, stream=None):
+    _check(load().dg_test_quant_rows(_ptr(x), rows, K, _ptr(q), _ptr(s), _stream(stream)))
 
 
 def dg_test_noise(x0, xt, batch, L, vocab, schedule, t, seed, step, stream=None):

@@ -21,7 +21,8 @@ def model_desc(cfg) -> dg.ModelDesc:
                         top_k=cfg.top_k, expert_hidden=cfg.expert_hidden, shared_hidden=cfg.shared_hidden,
                         vocab=cfg.vocab, window=cfg.window, global_every=cfg.global_every,
                         rope_theta=cfg.rope_theta, norm_eps=cfg.norm_eps, act_dtype=_DT[cfg.act_dtype],
-                        expert_dtype=_DT[cfg.expert_dtype], sc_hidden=getattr(cfg, "sc_hidden", 0))
+                        expert_dtype=_DT[cfg.expert_dtype], sc_hidden=getattr(cfg, "sc_hidden", 0),
+                        expert_act_fp8=int(getattr(cfg, "act_quant", "") == "fp8"))
 
 
 def _p(t):

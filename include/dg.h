@@ -66,7 +66,8 @@ typedef enum {
  * and shared_hidden multiples of 64; vocab % 16 == 0; top_k <= n_experts <= 256, n_experts % 4 == 0, top_k <= 16;
  * act_dtype F32 or BF16;
  * expert_dtype = act_dtype, or FP8E4M3 / MXFP4 when act_dtype is BF16 (weights-only: the codes are
- * widened exactly to bf16 and the math is bf16 MFMA). */
+ * widened exactly to bf16 and the math is bf16 MFMA; with expert_act_fp8 = 1 and FP8E4M3 weights the
+ * expert inputs are quantised too, W8A8, and the products run on the fp8 MFMA). */
 typedef struct {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim;
   int32_t n_experts, top_k, expert_hidden, shared_hidden, vocab;
@@ -76,6 +77,13 @@ typedef struct {
   dg_dtype act_dtype, expert_dtype;
   int32_t sc_hidden; /* hidden width of the self-conditioning block (multiple of 64; vocab % 64 == 0),
                         0: the model has none [TR §디노이징 반복과 self-conditioning] */
+  int32_t expert_act_fp8; /* 1: W8A8 experts (needs expert_dtype FP8E4M3, act_dtype BF16; the pages
+                        measure fp8 builds [TR §배치 크기 1 처리량] and fix no activation scheme): each
+                        row of an expert GEMM's input, the FFN-normalised rows and the SwiGLU products
+                        (stored bf16 first), is coded to e4m3 with the float32 scale max|row| / 448 (1 for a
+                        zero row; codes by round-to-nearest-even of the float32 quotient, saturating);
+                        a product is (codes . codes) * row scale * weight scale.  0: the expert inputs
+                        stay in act_dtype */
 } dg_model_desc;
 
 /* One layer's weights: device pointers, borrowed until dg_destroy().  Every matrix is stored
@@ -408,6 +416,23 @@ dg_status dg_test_read_routing(const dg_ctx *ctx, const void *ws, int32_t rows, 
 dg_status dg_test_noise(const int32_t *x0, int32_t *xt, int32_t batch, int32_t L, int32_t vocab,
                         dg_schedule schedule, float t, uint64_t seed, uint32_t step,
                         hipStream_t stream);
+
+/* The expert inputs of the last layer run by dg_denoise_step over batch x L rows (R = batch*L),
+ * read from the workspace (device outputs, any may be NULL): xhat [R][d] act (the FFN-normalised
+ * rows), a_grp [R*top_k][expert_hidden] act (the routed SwiGLU products in expert-grouped order:
+ * experts ascending, each expert's assignments t*top_k+s ascending), sh_a [R][shared_hidden] act;
+ * with expert_act_fp8 = 1 also their e4m3 codes and float32 row scales (xq/xs, aq/as, shq/shs;
+ * asking for them otherwise is DG_EINVAL). */
+dg_status dg_test_read_expert_inputs(const dg_ctx *ctx, const void *ws, int32_t batch, int32_t L,
+                                     void *xhat, uint8_t *xq, float *xs, void *a_grp, uint8_t *aq,
+                                     float *as, void *sh_a, uint8_t *shq, float *shs,
+                                     hipStream_t stream);
+
+/* W8A8 activation coding of bf16 rows x [rows][K] (device, row stride K, K % 8 == 0), as the
+ * experts take their inputs when expert_act_fp8 = 1: s [rows] float32 = max|row| / 448 (1 for a
+ * zero row), q [rows][K] e4m3 codes of x / s (round to nearest even, saturating at 448). */
+dg_status dg_test_quant_rows(const void *x, int32_t rows, int32_t K, uint8_t *q, float *s,
+                             hipStream_t stream);
 
 #ifdef __cplusplus
 }

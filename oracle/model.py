@@ -200,12 +200,16 @@ def act_quantiser(cfg):
     return lambda x: quant_rows_e4m3(x)[0]
 
 
-def moe(cfg, a2, lw, rnd, forced_idx=None):
+def moe(cfg, a2, lw, rnd, forced_idx=None, forced_q=None):
     """Routed experts plus the always-on shared expert.
 
     out[t] = sum over slots s in order of gate[t,s] * FFN_{idx[t,s]}(a2[t]) + FFN_shared(a2[t]).
     The shared expert enters with weight 1.  `forced_idx` replaces the top-k choice (used only
-    when comparing against another implementation that saw a near-tie)."""
+    when comparing against another implementation that saw a near-tie).  `forced_q(e, x)`, for
+    W8A8 experts only, replaces the activation quantiser of expert e ("shared" for the shared
+    expert; its rows in ascending token-then-slot order, first with the expert's input, then with
+    its SwiGLU product): it lets a comparison hand in another implementation's code decisions,
+    which tiny input differences can move, the way forced_idx hands in its expert choice."""
     r = a2 @ lw["w_router"].T
     if lw["router_bias"] is not None:
         r = r + lw["router_bias"]
@@ -218,14 +222,19 @@ def moe(cfg, a2, lw, rnd, forced_idx=None):
         gates = w / w.sum(axis=1, keepdims=True)
     T = a2.shape[0]
     aq = act_quantiser(cfg)
+    if forced_q is not None:
+        assert aq is not None, "forced_q needs W8A8 experts"
+        q_of = lambda e: (lambda x: forced_q(e, x))
+    else:
+        q_of = lambda e: aq
     y = np.zeros((T, cfg.top_k, a2.shape[1]))
     for e in np.unique(idx):
         rows, slots = np.nonzero(idx == e)
-        y[rows, slots] = swiglu(a2[rows], lw["w_gate"][e], lw["w_up"][e], lw["w_down"][e], rnd, aq)
+        y[rows, slots] = swiglu(a2[rows], lw["w_gate"][e], lw["w_up"][e], lw["w_down"][e], rnd, q_of(int(e)))
     out = np.zeros_like(a2)
     for s in range(cfg.top_k):
         out = out + gates[:, s:s + 1] * y[:, s]
-    out = out + swiglu(a2, lw["sh_gate"], lw["sh_up"], lw["sh_down"], rnd, aq)
+    out = out + swiglu(a2, lw["sh_gate"], lw["sh_up"], lw["sh_down"], rnd, q_of("shared"))
     return out, {"r32": r32, "idx": idx, "gates": gates}
 
 
@@ -242,9 +251,10 @@ def qkv(cfg, x_hat, lw, pos, rnd):
     return rnd(rope(q, pos, cfg.rope_theta)), rnd(rope(k, pos, cfg.rope_theta)), rnd(v)
 
 
-def denoise_layer(cfg, layer, h, lw, K, V, prefix_len, rnd, forced_idx=None):
+def denoise_layer(cfg, layer, h, lw, K, V, prefix_len, rnd, forced_idx=None, forced_q=None):
     """One pre-norm decoder layer over all canvases.  h: [B*L][d] residual (float64).
-    K, V: this layer's caches [B][Hkv][cap][dh].  Returns (h_new, info)."""
+    K, V: this layer's caches [B][Hkv][cap][dh].  Returns (h_new, info); forced_idx and
+    forced_q as in moe."""
     B, L = len(prefix_len), h.shape[0] // len(prefix_len)
     Hq, dh = cfg.n_q_heads, cfg.head_dim
     x = rnd(rmsnorm(h, lw["attn_norm"], cfg.norm_eps))
@@ -259,7 +269,7 @@ def denoise_layer(cfg, layer, h, lw, K, V, prefix_len, rnd, forced_idx=None):
     o = rnd(o)
     h = h + o @ lw["w_o"].T
     a2 = rnd(rmsnorm(h, lw["ffn_norm"], cfg.norm_eps))
-    f, info = moe(cfg, a2, lw, rnd, forced_idx)
+    f, info = moe(cfg, a2, lw, rnd, forced_idx, forced_q)
     info["o"] = o
     info["a2"] = a2
     return h + f, info

@@ -58,6 +58,13 @@ def test_create_rejects_unsupported_shapes_and_null_weights():
         with pytest.raises(dg.DGError) as e:
             dg.dg_create(bad, w)
         assert e.value.status == dg.DG_EUNSUPPORTED
+    # W8A8 needs fp8 weights and bf16 activations
+    for kw in (dict(act_dtype="bf16", expert_dtype="bf16"), dict(act_dtype="bf16", expert_dtype="mxfp4"),
+               dict(act_dtype="f32", expert_dtype="f32")):
+        bad = model_desc(configs.C0.replace(act_quant="fp8", **kw))
+        with pytest.raises(dg.DGError) as e:
+            dg.dg_create(bad, w)
+        assert e.value.status == dg.DG_EUNSUPPORTED and "expert_act_fp8" in dg.dg_last_error()
     ok = model_desc(configs.C0)
     with pytest.raises(dg.DGError) as e:
         dg.dg_create(ok, w)                     # NULL matrices

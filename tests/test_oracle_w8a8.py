@@ -97,3 +97,31 @@ def test_w8a8_moe_is_exact_on_representable_inputs_and_differs_otherwise():
     g = xs @ lw["sh_gate"].T
     A = (g / (1 + np.exp(-g))) * (xs @ lw["sh_up"].T)
     assert np.allclose(want, quant_rows_e4m3(A)[0] @ lw["sh_down"].T, rtol=1e-12, atol=1e-12)
+
+
+def test_forced_quantiser_hook():
+    """forced_q hands each expert's quantiser calls to the caller: input rows first, then the SwiGLU
+    product, in token-then-slot order; handing back the quantiser's own output reproduces the layer,
+    and handing back anything else changes it."""
+    rng = np.random.default_rng(43)
+    cfg = _tiny().replace(act_quant="fp8")
+    lw = _layer(cfg, rng)
+    x = rng.standard_normal((7, cfg.d_model))
+    want, info = M.moe(cfg, x, lw, identity)
+    calls = []
+
+    def same(e, v):
+        calls.append((e, v.shape))
+        return quant_rows_e4m3(v)[0]
+    got, _ = M.moe(cfg, x, lw, identity, forced_q=same)
+    assert np.array_equal(got, want)
+    idx = info["idx"]
+    routed = [c for c in calls if c[0] != "shared"]
+    assert [c[0] for c in routed] == [e for e in np.unique(idx) for _ in (0, 1)]
+    for j in range(0, len(routed), 2):
+        e = routed[j][0]
+        n = int((idx == e).sum())
+        assert routed[j][1] == (n, cfg.d_model) and routed[j + 1][1] == (n, cfg.expert_hidden)
+    assert [c for c in calls if c[0] == "shared"] == [("shared", (7, cfg.d_model)), ("shared", (7, cfg.shared_hidden))]
+    other, _ = M.moe(cfg, x, lw, identity, forced_q=lambda e, v: v)
+    assert not np.allclose(other, want, rtol=0, atol=1e-12)
