@@ -20,7 +20,8 @@
 //                      exact in fp32; O / l is unchanged)
 //   O^T += V^T . P^T   (A = V^T from LDS, B = P^T built in registers from the S^T accumulators)
 // The key list is the prefix slots [0, np) in 64-key tiles, then the canvas keys [0, n) in
-// 64-key tiles; a split covers a contiguous run of tiles.  Rows of a partial tile are loaded
+// 64-key tiles (for the causal encoder only the canvas tiles that some query of the block can see);
+// a split covers a contiguous run of tiles.  Rows of a partial tile are loaded
 // from the range's last valid key (finite data) and masked out of the softmax; the value
 // columns of a partial tile are zeroed in LDS so that P = 0 never meets an unwritten slot.
 #include "common.h"
@@ -78,7 +79,21 @@ __global__ __launch_bounds__(NW * 64) void flash_kernel(AttnArgs p) {
 
   const int P = prefix_of(p.plen, b, p.max_prefix);
   const int np = p.is_global ? P : min(P, p.window);
-  const int TP = (np + C::KEYS - 1) / C::KEYS, TC = (p.n + C::KEYS - 1) / C::KEYS;
+  const int TP = (np + C::KEYS - 1) / C::KEYS;
+  // canvas key tiles [c_lo, c_hi] are the ones some query of this block can see: all of them for a
+  // bidirectional pass; for the causal encoder, none past the block's last query position and, on
+  // a sliding-window layer, none wholly older than its first query's window.  The block's rows are
+  // (head, position) pairs in head-major order, so the positions form one range unless the block
+  // straddles two heads (then every position counts).
+  int c_lo = 0, c_hi = (p.n + C::KEYS - 1) / C::KEYS - 1;
+  if constexpr (CAUSAL) {
+    const int mq0 = qblk * C::QROWS, mq1 = min(mrows, mq0 + C::QROWS) - 1;
+    const bool one_head = mq0 / p.n == mq1 / p.n;
+    const int qlo = one_head ? mq0 % p.n : 0, qhi = one_head ? mq1 % p.n : p.n - 1;
+    c_hi = min(c_hi, qhi / C::KEYS);
+    if (!p.is_global) c_lo = max(0, qlo - p.window + 1) / C::KEYS;
+  }
+  const int TC = c_hi - c_lo + 1;
   const int t_begin = split * p.tiles_per_split;
   const int t_end = min(TP + TC, t_begin + p.tiles_per_split);
   const int ring_lo = max(0, P - p.window);
@@ -111,7 +126,7 @@ __global__ __launch_bounds__(NW * 64) void flash_kernel(AttnArgs p) {
   // tile t -> range (prefix / canvas), first key of the tile within the range, valid keys
   auto tile_info = [&](int t, bool& canvas, int& kt0, int& nv) {
     canvas = t >= TP;
-    kt0 = (canvas ? t - TP : t) * C::KEYS;
+    kt0 = (canvas ? c_lo + t - TP : t) * C::KEYS;
     nv = min(C::KEYS, (canvas ? p.n : np) - kt0);
   };
 

@@ -143,6 +143,29 @@ def test_small_bf16_prefill_and_mixed_pass_match_oracle():
             assert torch.equal(k[b], k0[b]) and torch.equal(v[b], v0[b]), "a denoising canvas's cache changed"
 
 
+def test_long_causal_chunk_prefill_matches_oracle():
+    """A 400-token chunk per canvas through the causal encoder: key tiles past a query block's last
+    position, and on the 64-slot sliding-window layer tiles wholly older than its first query's
+    window, are skipped; blocks of 128 query rows straddle the two heads' row ranges at 400."""
+    cfg = SMALL_BF16.replace(batch=2, prefix=448)
+    B, n = cfg.batch, 400
+    plen = [0, 37]
+    model, W, kv = build(cfg)
+    model.set_kv(kv, plen)
+    okv = oracle_kv_dev(kv)
+    OW = oracle_weights(W, cfg)
+    toks = _tokens(cfg, B, n, 43)
+    ws = model.workspace(B, n, cfg.prefix)
+    log(f"  long causal chunk: prefixes {plen}, {n} tokens")
+    model.prefill_kv(toks, ws)
+    torch.cuda.synchronize()
+    okv_p, oplen = M.prefill(cfg, OW, okv, plen, toks.cpu().numpy())
+    ek = _cache_err(kv, okv_p, range(B))
+    log(f"  prefill: max |cache - oracle| {ek:.2e}; prefix lengths {model.prefix_len} (oracle {list(oplen)})")
+    assert ek <= 2e-2
+    assert list(model.prefix_len) == [int(x) for x in oplen]
+
+
 @pytest.mark.parametrize("flags", [[1, 0, 0], [0, 1, 1]])
 def test_mixed_pass_equals_uniform_passes_bit_exact(flags):
     """Two layers at the assumed Gemma-like widths (a 1024-slot ring layer, then a global layer),
