@@ -20,6 +20,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8_v;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_v;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16 bytes, lives in VGPRs
+typedef int i32x8 __attribute__((ext_vector_type(8)));       // 32 bytes: one f8f6f4 MFMA operand
 
 // ---------------------------------------------------------------- bf16 <-> f32 -------------------
 DG_DEV float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }

@@ -341,58 +341,68 @@ struct GemmDmaQ {
   }
 };
 
-// W8A8: both operands as e4m3 codes on the direct-to-LDS ring, multiplied by the fp8 MFMA
-// (v_mfma_f32_16x16x32_fp8_fp8, fp32 accumulation); the per-row and per-column scales are the
-// caller's epilogue.  A stage is 64 K-elements: A and B rows of 64 bytes, the 16-byte chunk c of row
-// r stored in slot c ^ ((r >> 1) & 3) (the conflict-free pattern of the fp8 weight ring).  Lane
-// group kg = lane >> 4 takes chunk kg (elements 16 kg .. + 15) of its A row and of its B row; the
-// low 8 bytes feed one MFMA and the high 8 bytes a second, so both operands carry the same K
-// elements in each MFMA slot and the sum over the stage is the plain dot product.
+// W8A8: both operands as e4m3 codes on the direct-to-LDS ring, multiplied by the gfx950
+// block-scaled MFMA v_mfma_scale_f32_16x16x128_f8f6f4 with both formats e4m3 and both block
+// scales 1 (e8m0 code 127): 128 K-elements per instruction at twice the bf16 rate, fp32
+// accumulation; the per-row and per-column scales are the caller's epilogue.  A stage is 128
+// K-elements: A and B rows of 128 bytes laid out like the bf16 ring's (8 rows per load
+// instruction, the 16-byte chunk c of row r in slot c ^ ((r >> 1) & 7)).  Lane group kg = lane >> 4
+// feeds the MFMA chunks kg and 4 + kg of its A row and of its B row as its 32 bytes, the same
+// 16-byte reads as the bf16 ring's (conflict-free); A and B use the same map, so the sum over the
+// stage is the plain dot product.  K may end half-way through a stage (K % 128 == 64): there the
+// lanes of chunks 4..7 fetch chunk c - 4 of the same row instead (no access past K), and their A
+// halves are zeroed in registers, so those products add exact zeros.
 template <int BM, int BN, int WM, int WN, int NS>
 struct GemmDmaQQ {
   static constexpr int NW = WM * WN;
   static constexpr int FM = BM / WM / 16, FN = BN / WN / 16;
   static_assert(FM >= 1 && FN >= 1, "wave tile at least 16 x 16");
-  static constexpr int KT = 64;                          // K elements (bytes) per stage
-  static constexpr int IA = BM / (16 * NW), IB = BN / (16 * NW);   // 16 rows per load instruction
-  static_assert(IA * 16 * NW == BM && IB * 16 * NW == BN, "rows per tile: whole load instructions");
+  static constexpr int KT = 128;                         // K elements (bytes) per stage
+  static constexpr int IA = BM / (8 * NW), IB = BN / (8 * NW);   // 8 rows per load instruction
+  static_assert(IA * 8 * NW == BM && IB * 8 * NW == BN, "rows per tile: whole load instructions");
   static constexpr int LPT = IA + IB;                    // load instructions per wave per stage
-  static constexpr int A_BYTES = BM * 64, B_BYTES = BN * 64;
+  static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int LDS_BYTES = NS * STAGE;
   static_assert(NS >= 2 && (NS - 2) * LPT < 64, "stages / vmcnt range");
 
   const char* a_src[IA];
   const char* b_src[IB];
+  int hi_back;                 // bytes this lane steps back on a half stage (64 for chunks 4..7, else 0)
 
   template <class ARow, class BRow, class SRow>
   DG_DEV void setup(ARow arow, BRow brow, SRow) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int rr = lane >> 2, slot = lane & 3;
+    const int rr = lane >> 3, slot = lane & 7;
 #pragma unroll
     for (int i = 0; i < IA; ++i) {
-      const int r = (wave + NW * i) * 16 + rr;
+      const int r = (wave + NW * i) * 8 + rr;
       const char* p = reinterpret_cast<const char*>(arow(r));
       if (!p) p = reinterpret_cast<const char*>(arow(0));
-      a_src[i] = p + ((slot ^ ((r >> 1) & 3)) * 16);
+      a_src[i] = p + ((slot ^ ((r >> 1) & 7)) * 16);
     }
 #pragma unroll
     for (int i = 0; i < IB; ++i) {
-      const int r = (wave + NW * i) * 16 + rr;
+      const int r = (wave + NW * i) * 8 + rr;
       const char* p = reinterpret_cast<const char*>(brow(r));
       if (!p) p = reinterpret_cast<const char*>(brow(0));
-      b_src[i] = p + ((slot ^ ((r >> 1) & 3)) * 16);
+      b_src[i] = p + ((slot ^ ((r >> 1) & 7)) * 16);
     }
+    // the chunk this lane fetches, slot ^ ((r >> 1) & 7), is the same for all its instructions:
+    // their rows differ by multiples of 8 x NW (NW even), which leave (r >> 1) & 7 unchanged
+    static_assert(NW % 2 == 0, "even wave count");
+    hi_back = ((slot ^ (((wave * 8 + rr) >> 1) & 7)) >= 4) ? 64 : 0;
   }
 
-  DG_DEV void issue(char* lds, int kt, int stage) {
+  // stage `stage` <- K elements [128 kt, 128 kt + 128); half: only [128 kt, 128 kt + 64) exist
+  DG_DEV void issue(char* lds, int kt, int stage, bool half = false) {
     const int wave = threadIdx.x >> 6;
     char* st = lds + stage * STAGE;
+    const size_t off = (size_t)kt * 128 - (half ? hi_back : 0);
 #pragma unroll
-    for (int i = 0; i < IA; ++i) dma16(a_src[i] + (size_t)kt * 64, st + (wave + NW * i) * 1024);
+    for (int i = 0; i < IA; ++i) dma16(a_src[i] + off, st + (wave + NW * i) * 8 * 128);
 #pragma unroll
-    for (int i = 0; i < IB; ++i)
-      dma16<DMA_STREAM>(b_src[i] + (size_t)kt * 64, st + A_BYTES + (wave + NW * i) * 1024);
+    for (int i = 0; i < IB; ++i) dma16<DMA_STREAM>(b_src[i] + off, st + A_BYTES + (wave + NW * i) * 8 * 128);
   }
 
   template <int P>
@@ -406,47 +416,49 @@ struct GemmDmaQQ {
   }
   DG_DEV static void wait_oldest(int pending) { wait_pending<NS - 1>(pending); }
 
-  DG_DEV static void compute(const char* st, f32x4_v (&acc)[FM][FN]) {
+  DG_DEV static void compute(const char* st, f32x4_v (&acc)[FM][FN], bool half = false) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    const int l16 = lane & 15, kg = lane >> 4;
-    u32x4 bf[FN];
+    const int l16 = lane & 15, kg = lane >> 4, swz = l16 >> 1;
+    const int s0 = (kg ^ swz) * 16, s1 = ((4 + kg) ^ swz) * 16;
+    i32x8 bf[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int n = wn * FN * 16 + j * 16 + l16;
-      bf[j] = *reinterpret_cast<const u32x4*>(st + A_BYTES + n * 64 + ((kg ^ ((n >> 1) & 3)) * 16));
+      const char* row = st + A_BYTES + (wn * FN * 16 + j * 16 + l16) * 128;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(row + s0), hi = *reinterpret_cast<const u32x4*>(row + s1);
+      bf[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int m = wm * FM * 16 + i * 16 + l16;
-      const u32x4 af = *reinterpret_cast<const u32x4*>(st + m * 64 + ((kg ^ ((m >> 1) & 3)) * 16));
-      const long a_lo = (long)(((uint64_t)af.y << 32) | af.x), a_hi = (long)(((uint64_t)af.w << 32) | af.z);
+      const char* row = st + (wm * FM * 16 + i * 16 + l16) * 128;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(row + s0);
+      u32x4 hi = *reinterpret_cast<const u32x4*>(row + s1);
+      if (half) hi = u32x4{0u, 0u, 0u, 0u};
+      const i32x8 af = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const long b_lo = (long)(((uint64_t)bf[j].y << 32) | bf[j].x);
-        const long b_hi = (long)(((uint64_t)bf[j].w << 32) | bf[j].z);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a_lo, b_lo, acc[i][j], 0, 0, 0);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a_hi, b_hi, acc[i][j], 0, 0, 0);
-      }
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0, 127, 0, 127);
     }
   }
 
+  // nk = ceil(K / 128) stages, the last one half when K % 128 == 64
   DG_DEV void run(char* lds, int K, f32x4_v (&acc)[FM][FN]) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-    const int nk = K / KT;
+    const int nk = (K + KT - 1) / KT;
+    const bool tail = (K % KT) != 0;
     int issued = 0;
-    for (; issued < NS - 1 && issued < nk; ++issued) issue(lds, issued, issued);
+    for (; issued < NS - 1 && issued < nk; ++issued) issue(lds, issued, issued, tail && issued == nk - 1);
     for (int kt = 0; kt < nk; ++kt) {
       wait_oldest(issued - kt);
       lds_barrier();
       if (issued < nk) {
-        issue(lds, issued, issued % NS);
+        issue(lds, issued, issued % NS, tail && issued == nk - 1);
         ++issued;
       }
-      compute(lds + (kt % NS) * STAGE, acc);
+      compute(lds + (kt % NS) * STAGE, acc, tail && kt == nk - 1);
     }
     __syncthreads();
   }

@@ -487,7 +487,9 @@ static hipError_t launch_grouped_t(GroupedArgs a, int n_eff, int sh_eff, int max
   const int units = (max_items + XG - 1) / XG * a.nt_r;
   const int blocks = a.sh_blocks + (XCDR ? (units + 7) / 8 * 8 * XG : max_items * a.nt_r);
   if (blocks == 0) return hipSuccess;
-  if (a.K % G::KT || (a.shB && a.shK % GS::KT)) return hipErrorInvalidValue;
+  // the W8A8 engine takes a K ending half-way through its 128-element stage
+  constexpr int KQ = is_fp8a_v<TA> ? 64 : G::KT, KQS = is_fp8a_v<TA> ? 64 : GS::KT;
+  if (a.K % KQ || (a.shB && a.shK % KQS)) return hipErrorInvalidValue;
   a.gate = launch_gate();
   static const hipError_t attr = allow_lds(gemm_grouped_kernel<TA, TB, BM, BMS, BN, WM, WN, EPI, NS, QNS, XCDR>, LDS);
   if (attr != hipSuccess) return attr;
@@ -536,19 +538,23 @@ static hipError_t grouped_dispatch(const GroupedArgs& a, int max_items, hipStrea
 }
 
 // W8A8: routed tiles of GROUP_BM_Q8 rows (four waves side by side) or, for batched canvases, 128 x 256
-// tiles on 8 waves (2 x 4); shared-expert tiles of 128 rows; fp8 MFMA throughout
+// tiles on 8 waves (2 x 4); shared-expert tiles of 128 rows; block-scaled fp8 MFMA throughout.
+// Rings of 128-element stages: 3 x 48 KB for the batched gate/up (one block per CU, K = d_model);
+// the batched down (K = expert width: six stages) on 128 x 128 tiles, 2 x 32 KB, two blocks per CU
+// to hide each other's ring fill (measured at eight canvases: 199 us per launch against 264 us
+// for 128 x 256 tiles on one block per CU); 3 stages of 24 / 32 KB otherwise.
 static hipError_t grouped_q8(const GroupedArgs& a, int max_items, hipStream_t s) {
   if (a.bm == GROUP_BM_WIDE) {
     constexpr int W = GROUP_BM_WIDE;
     if (a.epi == EPI_SWIGLU)
       return launch_grouped_t<fp8a_t, fp8_t, W, W, 256, 2, 4, EPI_SWIGLU, 0, 3, 1>(a, 2 * a.N, 2 * a.shN, max_items, s);
-    return launch_grouped_t<fp8a_t, fp8_t, W, W, 256, 2, 4, EPI_STORE_F32, 0, 3, 1>(a, a.N, a.shN, max_items, s);
+    return launch_grouped_t<fp8a_t, fp8_t, W, W, 128, 2, 4, EPI_STORE_F32, 0, 2, 1>(a, a.N, a.shN, max_items, s);
   }
   if (a.bm != GROUP_BM_Q8) return hipErrorInvalidValue;
   if (a.epi == EPI_SWIGLU)
-    return launch_grouped_t<fp8a_t, fp8_t, GROUP_BM_Q8, 128, 128, 1, 4, EPI_SWIGLU, 0, 4>(a, 2 * a.N, 2 * a.shN,
+    return launch_grouped_t<fp8a_t, fp8_t, GROUP_BM_Q8, 128, 128, 1, 4, EPI_SWIGLU, 0, 3>(a, 2 * a.N, 2 * a.shN,
                                                                                        max_items, s);
-  return launch_grouped_t<fp8a_t, fp8_t, GROUP_BM_Q8, 128, 128, 1, 4, EPI_STORE_F32, 0, 4>(a, a.N, a.shN, max_items, s);
+  return launch_grouped_t<fp8a_t, fp8_t, GROUP_BM_Q8, 128, 128, 1, 4, EPI_STORE_F32, 0, 3>(a, a.N, a.shN, max_items, s);
 }
 
 hipError_t launch_grouped(const GroupedArgs& a, int act_bf16, int w_kind, int max_items, hipStream_t s) {

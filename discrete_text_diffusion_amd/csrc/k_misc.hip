@@ -83,19 +83,27 @@ DG_DEV uint32_t e4m3_code(float q) {
   return sign | code;
 }
 
-// One wave per row: s = max|x| / 448 in float32 (1 for a zero row), codes of x / s.  The build keeps
-// IEEE float division (no fast-math), so both quotients are correctly rounded.
-template <int WPB>
+// One wave per row: s = max|x| / 448 in float32 (1 for a zero row), codes of x / s.  The row stays
+// in registers between the max and the coding (CH 16-byte chunks per lane, K <= 512 CH), so it is
+// read once.  The build keeps IEEE float division (no fast-math): both quotients are correctly
+// rounded.
+template <int WPB, int CH>
 __global__ __launch_bounds__(WPB * 64) void quant_rows_kernel(const bf16_t* x, int64_t ldx, int rows, int K,
                                                              uint8_t* q, float* s, const int32_t* gate) {
   if (gate_closed(gate)) return;
   const int lane = threadIdx.x & 63, r = blockIdx.x * WPB + (threadIdx.x >> 6);
   if (r >= rows) return;
   const bf16_t* xr = x + (int64_t)r * ldx;
+  uint4 v[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int k = (c * 64 + lane) * 8;
+    v[c] = k < K ? *reinterpret_cast<const uint4*>(xr + k) : make_uint4(0u, 0u, 0u, 0u);
+  }
   float amax = 0.f;
-  for (int k = lane * 8; k < K; k += 512) {
-    const uint4 v = *reinterpret_cast<const uint4*>(xr + k);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const uint32_t w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
 #pragma unroll
     for (int h = 0; h < 4; ++h)
       amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(w[h] << 16)), fabsf(__uint_as_float(w[h] & 0xffff0000u))));
@@ -105,9 +113,11 @@ __global__ __launch_bounds__(WPB * 64) void quant_rows_kernel(const bf16_t* x, i
   const float sc = amax > 0.f ? amax / 448.f : 1.f;
   if (lane == 0) s[r] = sc;
   uint8_t* qr = q + (int64_t)r * K;
-  for (int k = lane * 8; k < K; k += 512) {
-    const uint4 v = *reinterpret_cast<const uint4*>(xr + k);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int k = (c * 64 + lane) * 8;
+    if (k >= K) continue;
+    const uint32_t w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
     uint32_t out[2] = {0u, 0u};
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
@@ -119,13 +129,27 @@ __global__ __launch_bounds__(WPB * 64) void quant_rows_kernel(const bf16_t* x, i
   }
 }
 
-hipError_t launch_quant_rows(const void* x, int64_t ldx, int rows, int K, uint8_t* q, float* s, hipStream_t st) {
-  if (rows <= 0) return hipSuccess;
-  if (K % 8 || ldx % 8) return hipErrorInvalidValue;
+template <int CH>
+static hipError_t launch_quant_ch(const void* x, int64_t ldx, int rows, int K, uint8_t* q, float* s, hipStream_t st) {
   constexpr int WPB = 4;
-  hipLaunchKernelGGL(quant_rows_kernel<WPB>, dim3((unsigned)((rows + WPB - 1) / WPB)), dim3(WPB * 64), 0, st,
+  hipLaunchKernelGGL((quant_rows_kernel<WPB, CH>), dim3((unsigned)((rows + WPB - 1) / WPB)), dim3(WPB * 64), 0, st,
                      static_cast<const bf16_t*>(x), ldx, rows, K, q, s, launch_gate());
   return hipGetLastError();
+}
+
+hipError_t launch_quant_rows(const void* x, int64_t ldx, int rows, int K, uint8_t* q, float* s, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (K % 8 || ldx % 8 || K > 4096) return hipErrorInvalidValue;
+  switch ((K + 511) / 512) {
+    case 1: return launch_quant_ch<1>(x, ldx, rows, K, q, s, st);
+    case 2: return launch_quant_ch<2>(x, ldx, rows, K, q, s, st);
+    case 3: return launch_quant_ch<3>(x, ldx, rows, K, q, s, st);
+    case 4: return launch_quant_ch<4>(x, ldx, rows, K, q, s, st);
+    case 5: return launch_quant_ch<5>(x, ldx, rows, K, q, s, st);
+    case 6: return launch_quant_ch<6>(x, ldx, rows, K, q, s, st);
+    case 7: return launch_quant_ch<7>(x, ldx, rows, K, q, s, st);
+    default: return launch_quant_ch<8>(x, ldx, rows, K, q, s, st);
+  }
 }
 
 __global__ void copy_f32_kernel(const float* a, float* b, int64_t n, const int32_t* gate) {

@@ -543,6 +543,8 @@ dg_status check_desc(const dg_model_desc& d) {
   if (d.expert_act_fp8 != 0 && d.expert_act_fp8 != 1) return fail(DG_EINVAL, "expert_act_fp8 must be 0 or 1");
   if (d.expert_act_fp8 && !(d.expert_dtype == DG_FP8E4M3 && d.act_dtype == DG_BF16))
     return fail(DG_EUNSUPPORTED, "expert_act_fp8 needs FP8E4M3 expert weights and BF16 activations");
+  if (d.expert_act_fp8 && (d.expert_hidden > 4096 || d.shared_hidden > 4096))
+    return fail(DG_EUNSUPPORTED, "expert_act_fp8 needs expert_hidden and shared_hidden <= 4096");
   if (!(d.norm_eps >= 0.f) || !(d.rope_theta > 0.f)) return fail(DG_EINVAL, "bad norm_eps or rope_theta");
   if (d.window > 0 && d.global_every > 0 && d.window < 1) return fail(DG_EINVAL, "bad window");
   return DG_OK;
@@ -1356,7 +1358,7 @@ dg_status dg_test_read_expert_inputs(const dg_ctx* ctx, const void* ws, int32_t 
 
 dg_status dg_test_quant_rows(const void* x, int32_t rows, int32_t K, uint8_t* q, float* s, hipStream_t stream) {
   g_err.clear();
-  if (!x || !q || !s || rows < 1 || K < 8 || K % 8) return fail(DG_EINVAL, "bad argument");
+  if (!x || !q || !s || rows < 1 || K < 8 || K % 8 || K > 4096) return fail(DG_EINVAL, "bad argument");
   HIPCHK(launch_quant_rows(x, K, rows, K, q, s, stream));
   return DG_OK;
 }

@@ -82,8 +82,8 @@ typedef struct {
                         row of an expert GEMM's input, the FFN-normalised rows and the SwiGLU products
                         (stored bf16 first), is coded to e4m3 with the float32 scale max|row| / 448 (1 for a
                         zero row; codes by round-to-nearest-even of the float32 quotient, saturating);
-                        a product is (codes . codes) * row scale * weight scale.  0: the expert inputs
-                        stay in act_dtype */
+                        a product is (codes . codes) * row scale * weight scale; needs expert_hidden
+                        and shared_hidden <= 4096.  0: the expert inputs stay in act_dtype */
 } dg_model_desc;
 
 /* One layer's weights: device pointers, borrowed until dg_destroy().  Every matrix is stored
@@ -428,7 +428,7 @@ dg_status dg_test_read_expert_inputs(const dg_ctx *ctx, const void *ws, int32_t 
                                      float *as, void *sh_a, uint8_t *shq, float *shs,
                                      hipStream_t stream);
 
-/* W8A8 activation coding of bf16 rows x [rows][K] (device, row stride K, K % 8 == 0), as the
+/* W8A8 activation coding of bf16 rows x [rows][K] (device, row stride K, K % 8 == 0, K <= 4096), as the
  * experts take their inputs when expert_act_fp8 = 1: s [rows] float32 = max|row| / 448 (1 for a
  * zero row), q [rows][K] e4m3 codes of x / s (round to nearest even, saturating at 448). */
 dg_status dg_test_quant_rows(const void *x, int32_t rows, int32_t K, uint8_t *q, float *s,

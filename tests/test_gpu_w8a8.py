@@ -27,10 +27,9 @@ import pytest
 import torch
 
 from discrete_text_diffusion_amd import dg
-from oracle.numerics import e4m3_decode_table, quant_rows_e4m3
-from synth import configs, gen
 from oracle import model as M
-from oracle.numerics import rounder
+from oracle.numerics import e4m3_decode_table, quant_rows_e4m3, rounder
+from synth import configs, gen
 from tests.gpu_util import build, check_routing, log
 from tests.helpers import np64, oracle_layer
 
