@@ -68,8 +68,8 @@ def parse():
 # (FETCH_SIZE, WRITE_SIZE; KiB per dispatch, mean of 90 launches), each scaled by the same counter
 # on a 512 MiB device-to-device copy (FETCH_SIZE reads 262155.5 KiB for 524288 KiB read: x1.9999;
 # WRITE_SIZE reads 524288 KiB: x1).  Valid only while the kernel sources hash to `sources`.
-MOE_TRAFFIC = {"sources": "1236a6494d419fab5078079aebf4a8aac57e398780059e61e0d90191b55c1160",
-               "fetch_kib": 527794.2, "write_kib": 3872.1, "bytes_per_launch": 1084839620}
+MOE_TRAFFIC = {"sources": "8433ca12d2315df0843f37bd557ff08da6c09a2dabd9a38f05f721d4a6021bf9",
+               "fetch_kib": 528500.5, "write_kib": 3872.1, "bytes_per_launch": 1086286574}
 TRAFFIC_SOURCES = ("k_gemm.hip", "gemm_dma.h", "gemm_core.h", "common.h", "internal.h")
 
 
