@@ -292,15 +292,15 @@ __global__ __launch_bounds__(NW * 64) void flash_kernel(AttnArgs p) {
     }
 
     // ---- O^T += V^T . P^T: lane (d = l16, kg) supplies keys 32c2 + 8kg .. + 7 of row d -------
+    // (the key half c2 outermost: consecutive MFMAs feed different accumulators; each accumulator
+    // still takes its two halves in the order c2 = 0, 1)
     const char* vt = st + C::K_BYTES;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
-      const int d = db * 16 + l16;
-      const char* vr = vt + d * 128;
-      const int sw = (d >> 1) & 7;
+    for (int c2 = 0; c2 < 2; ++c2) {
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const u32x4 va = *reinterpret_cast<const u32x4*>(vr + (((4 * c2 + kg) ^ sw) * 16));
+      for (int db = 0; db < C::DB; ++db) {
+        const int d = db * 16 + l16;
+        const u32x4 va = *reinterpret_cast<const u32x4*>(vt + d * 128 + (((4 * c2 + kg) ^ ((d >> 1) & 7)) * 16));
 #pragma unroll
         for (int qb = 0; qb < QPW; ++qb) Mfma<bf16_t>::mma(acc[db][qb], va, pb[qb][c2]);
       }
