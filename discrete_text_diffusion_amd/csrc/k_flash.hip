@@ -215,15 +215,28 @@ __global__ __launch_bounds__(NW * 64) void flash_kernel(AttnArgs p) {
 #pragma unroll
       for (int qb = 0; qb < QPW; ++qb) s[nb][qb] = f32x4_v{0.f, 0.f, 0.f, 0.f};
     const int swz = l16 >> 1;
+    // K fragments of head-dim chunk c+1 are read while the MFMAs of chunk c run (two register
+    // sets), so each group of reads has a group of MFMAs to hide behind
+    auto kfrag = [&](int c, int nb) -> u32x4 {
+      return *reinterpret_cast<const u32x4*>(st + (c >> 1) * 8192 + l16 * 128 + (((4 * (c & 1) + kg) ^ swz) * 16) +
+                                             nb * 16 * 128);
+    };
+    u32x4 kf[2][4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) kf[0][nb] = kfrag(0, nb);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);         // the first group's 4 LDS reads
 #pragma unroll
     for (int c = 0; c < C::NCH; ++c) {
-      const char* kb = st + (c >> 1) * 8192 + l16 * 128 + (((4 * (c & 1) + kg) ^ swz) * 16);
+      if (c + 1 < C::NCH) {
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(kb + nb * 16 * 128);
-#pragma unroll
-        for (int qb = 0; qb < QPW; ++qb) Mfma<bf16_t>::mma(s[nb][qb], kf, qf[qb][c]);
+        for (int nb = 0; nb < 4; ++nb) kf[(c + 1) & 1][nb] = kfrag(c + 1, nb);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);     // then the next group's reads ...
       }
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int qb = 0; qb < QPW; ++qb) Mfma<bf16_t>::mma(s[nb][qb], kf[c & 1][nb], qf[qb][c]);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * QPW, 0);  // ... ahead of this group's MFMAs
     }
 
     // ---- mask, scale, online softmax with conditional rescale -----------------------------
@@ -294,16 +307,31 @@ __global__ __launch_bounds__(NW * 64) void flash_kernel(AttnArgs p) {
     // ---- O^T += V^T . P^T: lane (d = l16, kg) supplies keys 32c2 + 8kg .. + 7 of row d -------
     // (the key half c2 outermost: consecutive MFMAs feed different accumulators; each accumulator
     // still takes its two halves in the order c2 = 0, 1)
+    // (V fragments read one group of four ahead of the MFMAs that use them, as for K above)
     const char* vt = st + C::K_BYTES;
+    auto vfrag = [&](int g) -> u32x4 {            // g = c2 * DB + db
+      const int c2 = g / C::DB, d = (g % C::DB) * 16 + l16;
+      return *reinterpret_cast<const u32x4*>(vt + d * 128 + (((4 * c2 + kg) ^ ((d >> 1) & 7)) * 16));
+    };
+    constexpr int NG = 2 * C::DB / 4;             // groups of four fragments
+    u32x4 vf[2][4];
 #pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
+    for (int e = 0; e < 4; ++e) vf[0][e] = vfrag(e);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        const int d = db * 16 + l16;
-        const u32x4 va = *reinterpret_cast<const u32x4*>(vt + d * 128 + (((4 * c2 + kg) ^ ((d >> 1) & 7)) * 16));
+    for (int gi = 0; gi < NG; ++gi) {
+      if (gi + 1 < NG) {
 #pragma unroll
-        for (int qb = 0; qb < QPW; ++qb) Mfma<bf16_t>::mma(acc[db][qb], va, pb[qb][c2]);
+        for (int e = 0; e < 4; ++e) vf[(gi + 1) & 1][e] = vfrag(4 * (gi + 1) + e);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int g = 4 * gi + e, c2 = g / C::DB, db = g % C::DB;
+#pragma unroll
+        for (int qb = 0; qb < QPW; ++qb) Mfma<bf16_t>::mma(acc[db][qb], vf[gi & 1][e], pb[qb][c2]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * QPW, 0);
     }
   }
 
