@@ -126,6 +126,38 @@ struct GemmDma {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int swz = (lane & 15) >> 1, kg = lane >> 4;
+    if constexpr (FN >= 8 && KPS == 1) {
+      // wide wave tiles (a row strip against many columns): the second chunk's B fragments are
+      // read one by one as the first chunk's products free their registers, so those reads run
+      // under the matrix work instead of after it (scheduling groups pin the interleaving; each
+      // accumulator still adds chunk 0, then chunk 1)
+      const char* la = st + (wm * FM * 16 + (lane & 15)) * 128;
+      const char* lb = st + BM * 128 + (wn * FN * 16 + (lane & 15)) * 128;
+      const int s0 = (kg ^ swz) * 16, s1 = ((4 + kg) ^ swz) * 16;
+      u32x4 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const u32x4*>(la + i * 16 * 128 + s0);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const u32x4*>(lb + j * 16 * 128 + s0);
+      __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) Mfma<T>::mma(acc[i][j], af[i], bfr[j]);
+        bfr[j] = *reinterpret_cast<const u32x4*>(lb + j * 16 * 128 + s1);
+        __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const u32x4*>(la + i * 16 * 128 + s1);
+      __builtin_amdgcn_sched_group_barrier(0x100, FM, 0);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) Mfma<T>::mma(acc[i][j], af[i], bfr[j]);
+      __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
+      return;
+    }
 #pragma unroll
     for (int p = 0; p < KPS; ++p) {
       const char* la = st + p * SUB + (wm * FM * 16 + (lane & 15)) * 128;
