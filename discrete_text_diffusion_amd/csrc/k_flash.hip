@@ -336,41 +336,53 @@ __global__ __launch_bounds__(NW * 64) void flash_kernel(AttnArgs p) {
   }
 
   // ---- finish --------------------------------------------------------------------------------
+  // Lane (l16, kg) holds head-dim indices 16db + 4kg .. + 3 of query column l16: stored directly,
+  // each instruction would write 32 bytes into each of 16 rows.  The wave's 16 x DH block goes
+  // through LDS instead (the ring is idle once every wave has left the key loop), and each store
+  // instruction then writes whole rows.
+  // Split partials are the split's output normalised by its own sum, O_s / l_s (a convex
+  // combination of value rows, so bounded by max |v|), as IEEE half: half the bytes of fp32 sums at
+  // 2^-11 relative precision; (m_s, l_s) stay fp32.  One split writes the bf16 output itself.
+  constexpr int ROWB = DH * 2 + 16;                  // padded LDS row of one query (bytes)
+  static_assert(NW * 16 * ROWB <= C::LDS, "finish staging");
+  char* tb = lds + wave * 16 * ROWB;
+  const bool partial = p.splits > 1;
+  lds_barrier();
 #pragma unroll
   for (int qb = 0; qb < QPW; ++qb) {
     float l = l_lane[qb] + __shfl_xor(l_lane[qb], 16, 64);
     l += __shfl_xor(l, 32, 64);
-    if (!qok[qb]) continue;
-    const int64_t row = qrow[qb];
-    if (p.splits == 1) {
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      bf16_t* o = static_cast<bf16_t*>(p.out) + (row * p.Hq + qhead[qb]) * DH;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        uint2 w;
-        w.x = pack_bf2(acc[db][qb][0] * inv, acc[db][qb][1] * inv);
-        w.y = pack_bf2(acc[db][qb][2] * inv, acc[db][qb][3] * inv);
-        *reinterpret_cast<uint2*>(o + db * 16 + 4 * kg) = w;
-      }
-    } else {
-      // the split's output normalised by its own sum, O_s / l_s (a convex combination of value
-      // rows, so bounded by max |v|), as IEEE half: half the bytes of the fp32 sums at 2^-11
-      // relative precision; (m_s, l_s) stay fp32
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      uint32_t* o = reinterpret_cast<uint32_t*>(p.part_o) + ((((int64_t)split * p.B * p.n + row) * p.Hq + qhead[qb]) * DH) / 2;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        uint2 w;
-        w.x = pack_h2(acc[db][qb][0] * inv, acc[db][qb][1] * inv);
-        w.y = pack_h2(acc[db][qb][2] * inv, acc[db][qb][3] * inv);
-        *reinterpret_cast<uint2*>(o + (db * 16 + 4 * kg) / 2) = w;
-      }
-      if (kg == 0) {
-        float* ml = p.part_ml + (((int64_t)split * p.B * p.n + row) * p.Hq + qhead[qb]) * 2;
-        ml[0] = m_run[qb];
-        ml[1] = l;
-      }
+    for (int db = 0; db < C::DB; ++db) {
+      const f32x4_v v = acc[db][qb] * inv;
+      uint2 w;
+      w.x = partial ? pack_h2(v[0], v[1]) : pack_bf2(v[0], v[1]);
+      w.y = partial ? pack_h2(v[2], v[3]) : pack_bf2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(tb + l16 * ROWB + (db * 16 + 4 * kg) * 2) = w;
     }
+    if (partial && kg == 0 && qok[qb]) {
+      float* ml = p.part_ml + (((int64_t)split * p.B * p.n + qrow[qb]) * p.Hq + qhead[qb]) * 2;
+      ml[0] = m_run[qb];
+      ml[1] = l;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's own LDS writes, in order
+    constexpr int CPR = DH / 8, RPI = 64 / CPR;          // 16-byte chunks per row, rows per store
+    static_assert(CPR * RPI == 64 && 16 % RPI == 0, "finish store shape");
+    const int ch = lane % CPR;
+#pragma unroll
+    for (int it = 0; it < 16 / RPI; ++it) {
+      const int r = RPI * it + lane / CPR;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(tb + r * ROWB + ch * 16);
+      const int mq = qblk * C::QROWS + wave * C::QW + qb * 16 + r;
+      if (mq >= mrows) continue;
+      const int hj = mq / p.n, qi = mq - hj * p.n;
+      const int64_t rh = (int64_t)(b * p.n + qi) * p.Hq + g * G + hj;
+      char* dst = partial ? reinterpret_cast<char*>(p.part_o) + (((int64_t)split * p.B * p.n * p.Hq + rh) * DH) * 2
+                          : static_cast<char*>(p.out) + rh * DH * 2;
+      *reinterpret_cast<u32x4*>(dst + ch * 16) = v;
+    }
+    if (qb + 1 < QPW) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
 }
 
