@@ -276,44 +276,54 @@ DG_DEV void put4<bf16_t>(bf16_t* dst, f32x4_v v) {
 template <class T, int S>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p) {
   if (gate_closed(p.gate)) return;
+  constexpr bool HALF = sizeof(T) == 2;            // bf16 path: IEEE-half O_s / l_s partials
+  constexpr int DPT = HALF ? 8 : 4;                // head-dim entries per thread (one 16-byte load)
+  constexpr int NV = DPT / 4;
   const int64_t rows = (int64_t)p.B * p.n * p.Hq;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (row, head, d/4)
-  const int dq = p.dh / 4;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (row, head, d/DPT)
+  const int dq = p.dh / DPT;
   if (idx >= rows * dq) return;
   const int64_t rh = idx / dq;
-  const int d4 = (int)(idx - rh * dq) * 4;
+  const int d0 = (int)(idx - rh * dq) * DPT;
   float mv[S], lv[S];
-  f32x4_v ov[S];
+  f32x4_v ov[S][NV];
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int64_t sr = (int64_t)s * rows + rh;
     const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + sr * 2);
     mv[s] = ml.x;
     lv[s] = ml.y;
-    if constexpr (sizeof(T) == 2) {
-      const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint32_t*>(p.part_o) + (sr * p.dh + d4) / 2);
-      float a, b, c, d;
-      unpack_h2(w.x, a, b);
-      unpack_h2(w.y, c, d);
-      ov[s] = f32x4_v{a, b, c, d};
+    if constexpr (HALF) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(p.part_o) + (sr * p.dh + d0) * 2);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        float a, b, c, d;
+        unpack_h2(w[2 * v], a, b);
+        unpack_h2(w[2 * v + 1], c, d);
+        ov[s][v] = f32x4_v{a, b, c, d};
+      }
     } else {
-      ov[s] = *reinterpret_cast<const f32x4_v*>(p.part_o + sr * p.dh + d4);
+      ov[s][0] = *reinterpret_cast<const f32x4_v*>(p.part_o + sr * p.dh + d0);
     }
   }
   float M = -INFINITY;
 #pragma unroll
   for (int s = 0; s < S; ++s) M = fmaxf(M, mv[s]);
   float L = 0.f;
-  f32x4_v o = {0.f, 0.f, 0.f, 0.f};
+  f32x4_v o[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) o[v] = f32x4_v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     if (mv[s] == -INFINITY) continue;
     const float w = exp2f(mv[s] - M);
     L += lv[s] * w;
-    o += ov[s] * (sizeof(T) == 2 ? lv[s] * w : w);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) o[v] += ov[s][v] * (HALF ? lv[s] * w : w);
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  put4<T>(static_cast<T*>(p.out) + rh * p.dh + d4, o * inv);
+#pragma unroll
+  for (int v = 0; v < NV; ++v) put4<T>(static_cast<T*>(p.out) + rh * p.dh + d0 + 4 * v, o[v] * inv);
 }
 
 template <class T, int S>
@@ -348,8 +358,9 @@ hipError_t launch_attention(const AttnArgs& a, int act_bf16, hipStream_t s) {
 }
 
 hipError_t launch_attn_merge(const AttnArgs& a, int act_bf16, hipStream_t s) {
-  if (a.splits < 2 || a.splits > MERGE_MAX || a.dh % 4) return hipErrorInvalidValue;
-  const int64_t n = (int64_t)a.B * a.n * a.Hq * (a.dh / 4);
+  const int dpt = act_bf16 ? 8 : 4;                  // head-dim entries per merge thread
+  if (a.splits < 2 || a.splits > MERGE_MAX || a.dh % dpt) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)a.B * a.n * a.Hq * (a.dh / dpt);
   const int blocks = (int)((n + 255) / 256);
   if (act_bf16) launch_merge_s<bf16_t, 2>(a, blocks, s);
   else launch_merge_s<float, 2>(a, blocks, s);

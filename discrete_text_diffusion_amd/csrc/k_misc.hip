@@ -335,35 +335,30 @@ hipError_t launch_kv_append(const void* kn, const void* vn, int vn_ld, void* kc,
 
 // resid[t] += (sum_{s<k} gate[t][s] * y[inv_perm[t*k+s]] + shared[t]), slots in order; then,
 // when g is given, out[t] = RMSNorm(resid[t]) * g (the next layer's attention norm, or the final
-// norm).  One block per row; each thread owns CPT groups of 4 columns, and every load of the
-// row (k gathered expert rows, the shared row, the residual) issues before the sums.
-constexpr int CPT = 4;   // d <= 256 * 4 * CPT
+// norm).  One block per row and one thread per 4 columns (d / 4 threads rounded up to whole waves,
+// so a 2816-wide row runs 11 waves): every load of the row (k gathered expert rows, the shared
+// row, the residual) issues before the sums.
 template <int K, class T>
-__global__ __launch_bounds__(256) void moe_combine_norm_kernel(float* resid, const float* y, const float* shared,
-                                                               const float* gates, const int32_t* inv_perm,
-                                                               int rows, int d, int k, const T* g, T* out,
-                                                               float eps, int* status, const int32_t* gate) {
+__global__ __launch_bounds__(1024) void moe_combine_norm_kernel(float* resid, const float* y, const float* shared,
+                                                                const float* gates, const int32_t* inv_perm,
+                                                                int rows, int d, int k, const T* g, T* out,
+                                                                float eps, int* status, const int32_t* gate) {
   if (gate_closed(gate)) return;
+  __shared__ float red[16];
   const int t = blockIdx.x;
-  float gv[K];
-  int pos[K];
-#pragma unroll
-  for (int s = 0; s < K; ++s) {
-    const int sc = min(s, k - 1);
-    // grouped positions are a permutation of [0, rows*k); the clamp only guards the read
-    pos[s] = min(max(inv_perm[(int64_t)t * k + sc], 0), rows * k - 1);
-    gv[s] = s < k ? gates[(int64_t)t * k + sc] : 0.f;
-  }
-  f32x4_v a[CPT];
-  float ss = 0.f;
-#pragma unroll
-  for (int j = 0; j < CPT; ++j) {
-    const int c = (threadIdx.x + 256 * j) * 4;
-    a[j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-    if (c >= d) continue;
+  const int c = threadIdx.x * 4;
+  f32x4_v a = {0.f, 0.f, 0.f, 0.f};
+  if (c < d) {
     f32x4_v yv[K];
+    float gv[K];
 #pragma unroll
-    for (int s = 0; s < K; ++s) yv[s] = *reinterpret_cast<const f32x4_v*>(y + (int64_t)pos[s] * d + c);
+    for (int s = 0; s < K; ++s) {
+      const int sc = min(s, k - 1);
+      // grouped positions are a permutation of [0, rows*k); the clamp only guards the read
+      const int pos = min(max(inv_perm[(int64_t)t * k + sc], 0), rows * k - 1);
+      gv[s] = s < k ? gates[(int64_t)t * k + sc] : 0.f;
+      yv[s] = *reinterpret_cast<const f32x4_v*>(y + (int64_t)pos * d + c);
+    }
     const f32x4_v sh = *reinterpret_cast<const f32x4_v*>(shared + (int64_t)t * d + c);
     f32x4_v* rp = reinterpret_cast<f32x4_v*>(resid + (int64_t)t * d + c);
     const f32x4_v r0 = *rp;
@@ -371,44 +366,35 @@ __global__ __launch_bounds__(256) void moe_combine_norm_kernel(float* resid, con
 #pragma unroll
     for (int s = 0; s < K; ++s)
       if (s < k) acc += gv[s] * yv[s];
-    const f32x4_v r1 = r0 + (acc + sh);
-    *rp = r1;
-    a[j] = r1;
-    ss += r1[0] * r1[0] + r1[1] * r1[1] + r1[2] * r1[2] + r1[3] * r1[3];
+    a = r0 + (acc + sh);
+    *rp = a;
   }
   if (!g) return;
-  ss = wave_sum(ss);
-  __shared__ float part[4];
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float tot = part[0] + part[1] + part[2] + part[3];
+  const float tot = block_sum_f(a[0] * a[0] + a[1] * a[1] + a[2] * a[2] + a[3] * a[3], red);
   const float inv = rsqrtf(tot / (float)d + eps);
   if (threadIdx.x == 0 && status && !isfinite(tot)) atomicOr(status, 2);
-#pragma unroll
-  for (int j = 0; j < CPT; ++j) {
-    const int c = (threadIdx.x + 256 * j) * 4;
-    if (c >= d) continue;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) out[(int64_t)t * d + c + e] = Elem<T>::from_f(a[j][e] * inv * Elem<T>::to_f(g[c + e]));
-  }
+  if (c < d) store4<T>(out + (int64_t)t * d + c, a * inv * load4<T>(g + c));
 }
 
 template <int K>
 static void combine_k(int bf, float* resid, const float* y, const float* shared, const float* gates,
                       const int32_t* inv_perm, int rows, int d, int k, const void* g, void* out, float eps,
                       int* status, hipStream_t s) {
+  const dim3 block((d / 4 + 63) / 64 * 64);
   if (bf)
-    hipLaunchKernelGGL((moe_combine_norm_kernel<K, bf16_t>), dim3(rows), dim3(256), 0, s, resid, y, shared, gates,
+    hipLaunchKernelGGL((moe_combine_norm_kernel<K, bf16_t>), dim3(rows), block, 0, s, resid, y, shared, gates,
                        inv_perm, rows, d, k, (const bf16_t*)g, (bf16_t*)out, eps, status, launch_gate());
   else
-    hipLaunchKernelGGL((moe_combine_norm_kernel<K, float>), dim3(rows), dim3(256), 0, s, resid, y, shared, gates,
+    hipLaunchKernelGGL((moe_combine_norm_kernel<K, float>), dim3(rows), block, 0, s, resid, y, shared, gates,
                        inv_perm, rows, d, k, (const float*)g, (float*)out, eps, status, launch_gate());
 }
 
 hipError_t launch_moe_combine_norm(float* resid, const float* y, const float* shared, const float* gates,
                                    const int32_t* inv_perm, int rows, int d, int k, const void* g, void* out,
                                    float eps, int bf, int* status, hipStream_t s) {
-  if (d % 4 || d > 256 * 4 * CPT) return hipErrorInvalidValue;
+  if (d % 4 || d > 4096) return hipErrorInvalidValue;
+  const uintptr_t al = bf ? 7 : 15;   // 4-column vector accesses of g and out
+  if (g && (((uintptr_t)g & al) || ((uintptr_t)out & al))) return hipErrorInvalidValue;
   if (k <= 2) combine_k<2>(bf, resid, y, shared, gates, inv_perm, rows, d, k, g, out, eps, status, s);
   else if (k <= 8) combine_k<8>(bf, resid, y, shared, gates, inv_perm, rows, d, k, g, out, eps, status, s);
   else combine_k<16>(bf, resid, y, shared, gates, inv_perm, rows, d, k, g, out, eps, status, s);
