@@ -68,8 +68,8 @@ def parse():
 # (FETCH_SIZE, WRITE_SIZE; KiB per dispatch, mean of 90 launches), each scaled by the same counter
 # on a 512 MiB device-to-device copy (FETCH_SIZE reads 262155.5 KiB for 524288 KiB read: x1.9999;
 # WRITE_SIZE reads 524288 KiB: x1).  Valid only while the kernel sources hash to `sources`.
-MOE_TRAFFIC = {"sources": "8433ca12d2315df0843f37bd557ff08da6c09a2dabd9a38f05f721d4a6021bf9",
-               "fetch_kib": 528500.5, "write_kib": 3872.1, "bytes_per_launch": 1086286574}
+MOE_TRAFFIC = {"sources": "c6dd63a6bfc4ddbb4dfb4b1b0ae7e1dafcbb1c4e9edbfa6bde1043d7f07925d9",
+               "fetch_kib": 528091.7, "write_kib": 3872.1, "bytes_per_launch": 1085449388}
 TRAFFIC_SOURCES = ("k_gemm.hip", "gemm_dma.h", "gemm_core.h", "common.h", "internal.h")
 
 
