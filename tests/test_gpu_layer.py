@@ -23,11 +23,13 @@ DEV = torch.device("cuda:0")
 
 
 @pytest.mark.parametrize("T,E,k,shift", [(256, 128, 8, 0), (2048, 128, 8, 0), (2048, 128, 8, 1), (37, 8, 2, 0),
-                                         (37, 8, 2, 3), (64, 256, 16, 0)])
-def test_router_topk_and_grouping_bit_exact(T, E, k, shift):
+                                         (37, 8, 2, 3), (64, 256, 16, 0), (4096, 128, 8, 0), (4096, 128, 8, 1)])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_router_topk_and_grouping_bit_exact(T, E, k, shift, seed):
     """shift > 0 places the caller's pick buffer `shift` int32 past a 16-byte boundary: the routing
-    tables then stage the picks element by element instead of in 16-byte loads."""
-    g = torch.Generator(device="cpu").manual_seed(T * 7 + E)
+    tables then stage the picks element by element instead of in 16-byte loads.  4096 rows take the
+    tables' unstaged path (more picks than the LDS stage holds).  Two seeds per shape."""
+    g = torch.Generator(device="cpu").manual_seed(T * 7 + E + 1000 * seed)
     s = torch.randn(T, E, generator=g)
     s[::9, 5] = s[::9, 6] = s[::9, 7] = 3.5           # exact ties at the top
     s[1::13] = 0.0                                      # all-equal rows
