@@ -130,7 +130,7 @@ __global__ __launch_bounds__(NW * 64) void flash_kernel(AttnArgs p) {
     nv = min(C::KEYS, (canvas ? p.n : np) - kt0);
   };
 
-  auto issue = [&](int t, int stage) {
+  auto issue_k = [&](int t, int stage) {
     bool canvas; int kt0, nv;
     tile_info(t, canvas, kt0, nv);
     char* st = lds + stage * C::STAGE;
@@ -144,6 +144,12 @@ __global__ __launch_bounds__(NW * 64) void flash_kernel(AttnArgs p) {
       const char* src = kb + (int64_t)key * DH * 2 + sub * 128 + ((slot ^ ((row >> 1) & 7)) * 16);
       dma16(src, st + sub * 8192 + (gi & 7) * 8 * 128);
     }
+  };
+  auto issue_v = [&](int t, int stage) {
+    bool canvas; int kt0, nv;
+    tile_info(t, canvas, kt0, nv);
+    char* st = lds + stage * C::STAGE;
+    const int rr = lane >> 3, slot = lane & 7;
     const char* vb = canvas ? vcan : vpre;
     const int vstride = canvas ? p.vn_ld : p.cap;
     const int last_chunk = ((canvas ? p.n : np) - 1) & ~7;    // first key of the range's last 8-key chunk
@@ -167,56 +173,15 @@ __global__ __launch_bounds__(NW * 64) void flash_kernel(AttnArgs p) {
     for (int i = 0; i < C::DB; ++i) acc[i][qb] = f32x4_v{0.f, 0.f, 0.f, 0.f};
   }
 
-  int issued = t_begin;
-  for (; issued < t_end && issued < t_begin + C::NS - 1; ++issued) issue(issued, issued - t_begin);
-  for (int t = t_begin; t < t_end; ++t) {
-    const int pending = issued - t;
-    if constexpr (C::NS >= 4) {
-      if (pending >= 3) wait_vm<2 * C::LPT>();
-      else if (pending == 2) wait_vm<C::LPT>();
-      else wait_vm<0>();
-    } else if constexpr (C::NS == 3) {
-      if (pending >= 2) wait_vm<C::LPT>();
-      else wait_vm<0>();
-    } else {
-      wait_vm<0>();
-    }
-    lds_barrier();
-    if (issued < t_end) {
-      issue(issued, (issued - t_begin) % C::NS);
-      ++issued;
-    }
-    bool canvas; int kt0, nv;
-    tile_info(t, canvas, kt0, nv);
-    char* st = lds + ((t - t_begin) % C::NS) * C::STAGE;
-    if (nv < C::KEYS) {
-      // zero the value columns of keys nv..63 (their slots may hold anything)
-      char* vt = st + C::K_BYTES;
-      for (int idx = threadIdx.x; idx < DH * 8; idx += NW * 64) {
-        const int d = idx >> 3, c = idx & 7;
-        if (8 * c + 8 <= nv) continue;
-        u32x4* w = reinterpret_cast<u32x4*>(vt + d * 128 + ((c ^ ((d >> 1) & 7)) * 16));
-        u32x4 v = *w;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (8 * c + e < nv) continue;
-          const uint32_t mask = (e & 1) ? 0x0000ffffu : 0xffff0000u;
-          v[e >> 1] &= mask;
-        }
-        *w = v;
-      }
-      lds_barrier();
-    }
-
-    // ---- S^T = K . Q^T ------------------------------------------------------------------------
-    f32x4_v s[4][QPW];
+  // ---- phases of one tile ----------------------------------------------------------------------
+  // S^T = K . Q^T.  K fragments of head-dim chunk c+1 are read while the MFMAs of chunk c run (two
+  // register sets), so each group of reads has a group of MFMAs to hide behind.
+  const int swz = l16 >> 1;
+  auto phase_s = [&](const char* st, f32x4_v (&s)[4][QPW]) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
       for (int qb = 0; qb < QPW; ++qb) s[nb][qb] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-    const int swz = l16 >> 1;
-    // K fragments of head-dim chunk c+1 are read while the MFMAs of chunk c run (two register
-    // sets), so each group of reads has a group of MFMAs to hide behind
     auto kfrag = [&](int c, int nb) -> u32x4 {
       return *reinterpret_cast<const u32x4*>(st + (c >> 1) * 8192 + l16 * 128 + (((4 * (c & 1) + kg) ^ swz) * 16) +
                                              nb * 16 * 128);
@@ -238,12 +203,15 @@ __global__ __launch_bounds__(NW * 64) void flash_kernel(AttnArgs p) {
         for (int qb = 0; qb < QPW; ++qb) Mfma<bf16_t>::mma(s[nb][qb], kf[c & 1][nb], qf[qb][c]);
       __builtin_amdgcn_sched_group_barrier(0x008, 4 * QPW, 0);  // ... ahead of this group's MFMAs
     }
+  };
 
-    // ---- mask, scale, online softmax with conditional rescale -----------------------------
-    // The column max (over the 4 lanes sharing a query column) is only formed when some lane's
-    // scores exceed its running max by more than 8 (log2 units): rare after the first tile.
+  // mask, scale, online softmax with conditional rescale, P^T packed to bf16.  The column max (over
+  // the 4 lanes sharing a query column) is only formed when some lane's scores exceed its running
+  // max by more than 8 (log2 units): rare after the first tile.
+  auto phase_softmax = [&](int t, f32x4_v (&s)[4][QPW], u32x4 (&pb)[QPW][2]) {
+    bool canvas; int kt0, nv;
+    tile_info(t, canvas, kt0, nv);
     const bool full = !CAUSAL && nv == C::KEYS;
-    u32x4 pb[QPW][2];
 #pragma unroll
     for (int qb = 0; qb < QPW; ++qb) {
       float ml = -INFINITY;
@@ -303,11 +271,13 @@ __global__ __launch_bounds__(NW * 64) void flash_kernel(AttnArgs p) {
         pb[qb][c2].w = pack_bf2(s[2 * c2 + 1][qb][2], s[2 * c2 + 1][qb][3]);
       }
     }
+  };
 
-    // ---- O^T += V^T . P^T: lane (d = l16, kg) supplies keys 32c2 + 8kg .. + 7 of row d -------
-    // (the key half c2 outermost: consecutive MFMAs feed different accumulators; each accumulator
-    // still takes its two halves in the order c2 = 0, 1)
-    // (V fragments read one group of four ahead of the MFMAs that use them, as for K above)
+  // O^T += V^T . P^T: lane (d = l16, kg) supplies keys 32c2 + 8kg .. + 7 of row d.  The key half c2
+  // is outermost, so consecutive MFMAs feed different accumulators (each accumulator still takes
+  // its two halves in the order c2 = 0, 1); V fragments are read one group of four ahead of the
+  // MFMAs that use them, as for K above.
+  auto phase_pv = [&](const char* st, const u32x4 (&pb)[QPW][2]) {
     const char* vt = st + C::K_BYTES;
     auto vfrag = [&](int g) -> u32x4 {            // g = c2 * DB + db
       const int c2 = g / C::DB, d = (g % C::DB) * 16 + l16;
@@ -333,7 +303,66 @@ __global__ __launch_bounds__(NW * 64) void flash_kernel(AttnArgs p) {
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4 * QPW, 0);
     }
+  };
+
+  // ---- key loop ----------------------------------------------------------------------------------
+  // Two wave groups, one wave of each per SIMD, half a tile apart.  Between the tile's two barriers
+  // the leading group (waves 0 .. NW/2-1) forms S(t) while the lagging group adds P(t-1) V(t-1);
+  // after the second, the leading group takes the softmax and P(t) V(t) while the lagging group forms
+  // S(t) and its softmax.  One group's softmax thus meets the other's matrix products on each SIMD
+  // (a single barrier per tile would keep the two waves of a SIMD in the same phase).  Each
+  // accumulator still sees rescale(t), then + P(t) V(t), in tile order.  K(t+1) is loaded after the
+  // first barrier (every wave is done with S(t-1)); V(t+1) after the second (the lagging group is
+  // done with P(t-1) V(t-1)).
+  const bool lag = wave >= NW / 2;
+  auto stage_of = [&](int t) -> char* { return lds + ((t - t_begin) % C::NS) * C::STAGE; };
+  u32x4 pb[QPW][2];
+  if (t_begin < t_end) {
+    issue_k(t_begin, 0);
+    issue_v(t_begin, 0);
   }
+  for (int t = t_begin; t < t_end; ++t) {
+    const bool more = t + 1 < t_end;
+    char* st = stage_of(t);
+    wait_vm<C::V_INS>();                 // K(t): only V(t) was issued after it
+    lds_barrier();
+    if (more) issue_k(t + 1, (t + 1 - t_begin) % C::NS);
+    f32x4_v s[4][QPW];
+    if (!lag) phase_s(st, s);
+    else if (t > t_begin) phase_pv(stage_of(t - 1), pb);
+    if (more) wait_vm<C::K_INS>();       // V(t): only K(t+1) was issued after it
+    else wait_vm<0>();
+    lds_barrier();
+    bool canvas; int kt0, nv;
+    tile_info(t, canvas, kt0, nv);
+    if (nv < C::KEYS) {
+      // zero the value columns of keys nv..63 (their slots may hold anything)
+      char* vt = st + C::K_BYTES;
+      for (int idx = threadIdx.x; idx < DH * 8; idx += NW * 64) {
+        const int d = idx >> 3, c = idx & 7;
+        if (8 * c + 8 <= nv) continue;
+        u32x4* w = reinterpret_cast<u32x4*>(vt + d * 128 + ((c ^ ((d >> 1) & 7)) * 16));
+        u32x4 v = *w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (8 * c + e < nv) continue;
+          const uint32_t mask = (e & 1) ? 0x0000ffffu : 0xffff0000u;
+          v[e >> 1] &= mask;
+        }
+        *w = v;
+      }
+      lds_barrier();
+    }
+    if (more) issue_v(t + 1, (t + 1 - t_begin) % C::NS);
+    if (!lag) {
+      phase_softmax(t, s, pb);
+      phase_pv(st, pb);
+    } else {
+      phase_s(st, s);
+      phase_softmax(t, s, pb);
+    }
+  }
+  if (lag && t_begin < t_end) phase_pv(stage_of(t_end - 1), pb);
 
   // ---- finish --------------------------------------------------------------------------------
   // Lane (l16, kg) holds head-dim indices 16db + 4kg .. + 3 of query column l16: stored directly,
