@@ -38,7 +38,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=24)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=60,
+                    help="untimed steps first (60 at C2 is ~0.7 s: a GPU that idled between processes "
+                         "takes ~0.5 s of load to reach its steady clocks)")
     ap.add_argument("--repeats", type=int, default=5,
                     help="timed runs of K steps each; ms_per_step is their median")
     ap.add_argument("--workload", default="C2")
