@@ -55,10 +55,15 @@ def test_router_topk_and_grouping_bit_exact(T, E, k, shift, seed):
     assert np.array_equal(perm.cpu().numpy(), op)
 
 
-def _layer_parity(cfg, layer, tol, resid=None):
+def _layer_parity(cfg, layer, tol, resid=None, scale_v=None):
     log(f"layer parity: {cfg.name} layer {layer} ({'global' if cfg.is_global(layer) else 'local'}), "
-        f"rows={cfg.rows} prefix={cfg.prefix} experts={cfg.expert_dtype}")
+        f"rows={cfg.rows} prefix={cfg.prefix} experts={cfg.expert_dtype}"
+        + (f", prefix values x{scale_v:g}, W_o x{1 / scale_v:g}" if scale_v else ""))
     model, W, kv = build(cfg)
+    if scale_v:
+        # powers of two: exact in bf16 on both sides (the model holds these very tensors)
+        kv[layer][1].mul_(scale_v)
+        W["layers"][layer]["w_o"].mul_(1.0 / scale_v)
     B, L = cfg.batch, cfg.canvas
     ws = model.workspace(B, L, cfg.prefix)
     rin = gen.resid_input(cfg, DEV) if resid is None else resid
@@ -102,6 +107,15 @@ def test_local_and_global_layers_parity_bf16():
     cfg = configs.C2.replace(n_layers=6, resid_input=True)
     _layer_parity(cfg, 0, 2e-2)
     _layer_parity(cfg, 5, 2e-2)
+
+
+def test_large_prefix_values_through_split_attention():
+    """Prefix values x 2^12 (split partials O_s / l_s up to ~2^14.5, inside the half-precision range
+    the split partials are stored in) and W_o x 2^-12, so the residual keeps its scale: the split
+    partials and their merge at large magnitude, on a local and a global layer of C2 shapes."""
+    cfg = configs.C2.replace(n_layers=6, resid_input=True)
+    for layer in (0, 5):
+        _layer_parity(cfg, layer, 2e-2, scale_v=4096.0)
 
 
 def test_fp8_experts_batched_layer_parity():
