@@ -127,8 +127,9 @@ hipError_t launch_kv_append(const void* kn, const void* vn, int vn_ld, void* kc,
 hipError_t launch_advance_prefix(int32_t* plen, int B, int n, const int32_t* seq_mask, hipStream_t s);
 // *flag = 1 if every v[0..n) is nonzero, else 0 (never gated, nor is launch_fill_i32)
 hipError_t launch_all_set(const int32_t* v, int n, int32_t* flag, hipStream_t s);
-// resid += MoE output (gated expert rows + shared row); with g, out = RMSNorm(resid) * g
-hipError_t launch_moe_combine_norm(float* resid, const float* y, const float* shared, const float* gates,
+// resid += MoE output (gated expert rows + shared row; y and shared in the activation type, bf
+// selecting bf16); with g, out = RMSNorm(resid) * g
+hipError_t launch_moe_combine_norm(float* resid, const void* y, const void* shared, const float* gates,
                                    const int32_t* inv_perm, int rows, int d, int k, const void* g, void* out,
                                    float eps, int bf, int* status, hipStream_t s);
 // resid += sum of nparts split-K partials; y = RMSNorm(resid) * g (d <= 4096)

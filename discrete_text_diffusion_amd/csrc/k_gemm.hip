@@ -299,7 +299,8 @@ DG_DEV void grouped_tile(char* lds, const TA* A, int64_t lda, const int32_t* a_t
           static_cast<TO*>(Cout)[(int64_t)(row0 + r) * ldc + oc] = Elem<TO>::from_f(a);
         }
     }
-  } else {  // EPI_STORE_F32
+  } else {  // EPI_STORE_F32 (fp32 rows) or EPI_STORE_ACT (rows of the activation type)
+    using TS = std::conditional_t<EPI == EPI_STORE_ACT, TO, float>;
 #pragma unroll
     for (int j = 0; j < G::FN; ++j) {
       const int n = n0 + G::col_of(j);
@@ -312,7 +313,7 @@ DG_DEV void grouped_tile(char* lds, const TA* A, int64_t lda, const int32_t* a_t
         for (int q = 0; q < 4; ++q) {
           const int r = G::row_of(i, q);
           if (r >= rows) continue;
-          static_cast<float*>(Cout)[(int64_t)(row0 + r) * ldc + n] = acc[i][j][q] * sc * ascale(r);
+          static_cast<TS*>(Cout)[(int64_t)(row0 + r) * ldc + n] = Elem<TS>::from_f(acc[i][j][q] * sc * ascale(r));
         }
     }
   }
@@ -523,17 +524,17 @@ template <class TA, class TB>
 static hipError_t grouped_dispatch(const GroupedArgs& a, int max_items, hipStream_t s) {
   if (a.bm == GROUP_BM_WIDE) {
     if (a.epi == EPI_SWIGLU) return grouped_wide<TA, TB, EPI_SWIGLU>(a, 2 * a.N, 2 * a.shN, max_items, s);
-    return grouped_wide<TA, TB, EPI_STORE_F32>(a, a.N, a.shN, max_items, s);
+    return grouped_wide<TA, TB, EPI_STORE_ACT>(a, a.N, a.shN, max_items, s);
   }
   if (a.bm != GROUP_BM) return hipErrorInvalidValue;
   if constexpr (sizeof(TB) == 1) {
     if (a.epi == EPI_SWIGLU)
       return launch_grouped_t<TA, TB, GROUP_BM, GROUP_BM, 128, 1, 4, EPI_SWIGLU>(a, 2 * a.N, 2 * a.shN, max_items, s);
-    return launch_grouped_t<TA, TB, GROUP_BM, GROUP_BM, 128, 1, 4, EPI_STORE_F32>(a, a.N, a.shN, max_items, s);
+    return launch_grouped_t<TA, TB, GROUP_BM, GROUP_BM, 128, 1, 4, EPI_STORE_ACT>(a, a.N, a.shN, max_items, s);
   } else {
     if (a.epi == EPI_SWIGLU)
       return launch_grouped_t<TA, TB, GROUP_BM, 4 * GROUP_BM, 128, 1, 4, EPI_SWIGLU>(a, 2 * a.N, 2 * a.shN, max_items, s);
-    return launch_grouped_t<TA, TB, GROUP_BM, 4 * GROUP_BM, 128, 1, 4, EPI_STORE_F32>(a, a.N, a.shN, max_items, s);
+    return launch_grouped_t<TA, TB, GROUP_BM, 4 * GROUP_BM, 128, 1, 4, EPI_STORE_ACT>(a, a.N, a.shN, max_items, s);
   }
 }
 
@@ -548,16 +549,17 @@ static hipError_t grouped_q8(const GroupedArgs& a, int max_items, hipStream_t s)
     constexpr int W = GROUP_BM_WIDE;
     if (a.epi == EPI_SWIGLU)
       return launch_grouped_t<fp8a_t, fp8_t, W, W, 256, 2, 4, EPI_SWIGLU, 0, 3, 1>(a, 2 * a.N, 2 * a.shN, max_items, s);
-    return launch_grouped_t<fp8a_t, fp8_t, W, W, 128, 2, 4, EPI_STORE_F32, 0, 2, 1>(a, a.N, a.shN, max_items, s);
+    return launch_grouped_t<fp8a_t, fp8_t, W, W, 128, 2, 4, EPI_STORE_ACT, 0, 2, 1>(a, a.N, a.shN, max_items, s);
   }
   if (a.bm != GROUP_BM_Q8) return hipErrorInvalidValue;
   if (a.epi == EPI_SWIGLU)
     return launch_grouped_t<fp8a_t, fp8_t, GROUP_BM_Q8, 128, 128, 1, 4, EPI_SWIGLU, 0, 3>(a, 2 * a.N, 2 * a.shN,
                                                                                        max_items, s);
-  return launch_grouped_t<fp8a_t, fp8_t, GROUP_BM_Q8, 128, 128, 1, 4, EPI_STORE_F32, 0, 3>(a, a.N, a.shN, max_items, s);
+  return launch_grouped_t<fp8a_t, fp8_t, GROUP_BM_Q8, 128, 128, 1, 4, EPI_STORE_ACT, 0, 3>(a, a.N, a.shN, max_items, s);
 }
 
 hipError_t launch_grouped(const GroupedArgs& a, int act_bf16, int w_kind, int max_items, hipStream_t s) {
+  if (a.epi != EPI_SWIGLU && a.epi != EPI_STORE_ACT) return hipErrorInvalidValue;
   if (w_kind == W_FP8A8) return grouped_q8(a, max_items, s);
   if (!act_bf16) return grouped_dispatch<float, float>(a, max_items, s);
   if (w_kind == W_FP8) return grouped_dispatch<bf16_t, fp8_t>(a, max_items, s);

@@ -333,13 +333,13 @@ hipError_t launch_kv_append(const void* kn, const void* vn, int vn_ld, void* kc,
   return hipGetLastError();
 }
 
-// resid[t] += (sum_{s<k} gate[t][s] * y[inv_perm[t*k+s]] + shared[t]), slots in order; then,
-// when g is given, out[t] = RMSNorm(resid[t]) * g (the next layer's attention norm, or the final
-// norm).  One block per row and one thread per 4 columns (d / 4 threads rounded up to whole waves,
+// resid[t] += (sum_{s<k} gate[t][s] * y[inv_perm[t*k+s]] + shared[t]), slots in order, with the
+// expert rows y and shared in the activation type T; then, when g is given, out[t] =
+// RMSNorm(resid[t]) * g (the next layer's attention norm, or the final norm).  One block per row and one thread per 4 columns (d / 4 threads rounded up to whole waves,
 // so a 2816-wide row runs 11 waves): every load of the row (k gathered expert rows, the shared
 // row, the residual) issues before the sums.
 template <int K, class T>
-__global__ __launch_bounds__(1024) void moe_combine_norm_kernel(float* resid, const float* y, const float* shared,
+__global__ __launch_bounds__(1024) void moe_combine_norm_kernel(float* resid, const T* y, const T* shared,
                                                                 const float* gates, const int32_t* inv_perm,
                                                                 int rows, int d, int k, const T* g, T* out,
                                                                 float eps, int* status, const int32_t* gate) {
@@ -357,9 +357,9 @@ __global__ __launch_bounds__(1024) void moe_combine_norm_kernel(float* resid, co
       // grouped positions are a permutation of [0, rows*k); the clamp only guards the read
       const int pos = min(max(inv_perm[(int64_t)t * k + sc], 0), rows * k - 1);
       gv[s] = s < k ? gates[(int64_t)t * k + sc] : 0.f;
-      yv[s] = *reinterpret_cast<const f32x4_v*>(y + (int64_t)pos * d + c);
+      yv[s] = load4<T>(y + (int64_t)pos * d + c);
     }
-    const f32x4_v sh = *reinterpret_cast<const f32x4_v*>(shared + (int64_t)t * d + c);
+    const f32x4_v sh = load4<T>(shared + (int64_t)t * d + c);
     f32x4_v* rp = reinterpret_cast<f32x4_v*>(resid + (int64_t)t * d + c);
     const f32x4_v r0 = *rp;
     f32x4_v acc = {0.f, 0.f, 0.f, 0.f};
@@ -377,19 +377,21 @@ __global__ __launch_bounds__(1024) void moe_combine_norm_kernel(float* resid, co
 }
 
 template <int K>
-static void combine_k(int bf, float* resid, const float* y, const float* shared, const float* gates,
+static void combine_k(int bf, float* resid, const void* y, const void* shared, const float* gates,
                       const int32_t* inv_perm, int rows, int d, int k, const void* g, void* out, float eps,
                       int* status, hipStream_t s) {
   const dim3 block((d / 4 + 63) / 64 * 64);
   if (bf)
-    hipLaunchKernelGGL((moe_combine_norm_kernel<K, bf16_t>), dim3(rows), block, 0, s, resid, y, shared, gates,
-                       inv_perm, rows, d, k, (const bf16_t*)g, (bf16_t*)out, eps, status, launch_gate());
+    hipLaunchKernelGGL((moe_combine_norm_kernel<K, bf16_t>), dim3(rows), block, 0, s, resid, (const bf16_t*)y,
+                       (const bf16_t*)shared, gates, inv_perm, rows, d, k, (const bf16_t*)g, (bf16_t*)out, eps, status,
+                       launch_gate());
   else
-    hipLaunchKernelGGL((moe_combine_norm_kernel<K, float>), dim3(rows), block, 0, s, resid, y, shared, gates,
-                       inv_perm, rows, d, k, (const float*)g, (float*)out, eps, status, launch_gate());
+    hipLaunchKernelGGL((moe_combine_norm_kernel<K, float>), dim3(rows), block, 0, s, resid, (const float*)y,
+                       (const float*)shared, gates, inv_perm, rows, d, k, (const float*)g, (float*)out, eps, status,
+                       launch_gate());
 }
 
-hipError_t launch_moe_combine_norm(float* resid, const float* y, const float* shared, const float* gates,
+hipError_t launch_moe_combine_norm(float* resid, const void* y, const void* shared, const float* gates,
                                    const int32_t* inv_perm, int rows, int d, int k, const void* g, void* out,
                                    float eps, int bf, int* status, hipStream_t s) {
   if (d % 4 || d > 4096) return hipErrorInvalidValue;

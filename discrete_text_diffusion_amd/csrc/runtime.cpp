@@ -144,7 +144,7 @@ Layout layout(const dg_model_desc& d, int B, int n, int max_prefix) {
   w.part_ml = take((size_t)MAX_SPLITS * R * d.n_q_heads * 2 * 4);
   w.rparts = take((size_t)MAX_RSPLIT * R * d.n_experts * 4);
   w.o_parts = take((size_t)MAX_KSPLIT * R * d.d_model * 4);
-  w.sh_parts = take(R * d.d_model * 4);
+  w.sh_parts = take(R * d.d_model * ab);     // shared-expert output rows (activation type)
   w.counts = take(d.n_experts * 4);
   w.offsets = take(d.n_experts * 4);
   w.perm = take(Rk * 4);
@@ -154,7 +154,7 @@ Layout layout(const dg_model_desc& d, int B, int n, int max_prefix) {
   w.work = take((size_t)w.max_items * 2 * 4);
   w.n_items = take(4);
   w.a_grp = take(Rk * d.expert_hidden * ab);
-  w.y = take(Rk * d.d_model * 4);
+  w.y = take(Rk * d.d_model * ab);           // routed expert output rows (activation type)
   w.sh_a = take(R * d.shared_hidden * ab);
   int vps;
   const int slices = sampler_slices(d, (int)R, &vps);
@@ -485,7 +485,7 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn, bool xhat_ready, const vo
     HIPCHK(launch_grouped(ga, bf, wk, max_items, P.s));
   }
   GroupedArgs da{};
-  da.epi = EPI_STORE_F32;
+  da.epi = EPI_STORE_ACT;           // expert outputs in the activation type
   da.A = at<void>(ws, w.a_grp); da.lda = d.expert_hidden; da.a_tok = nullptr;
   da.B = L.w_down; da.B2 = nullptr; da.ldb = d.expert_hidden / pk;
   da.b_estride = (int64_t)d.d_model * d.expert_hidden / pk;
@@ -514,7 +514,7 @@ dg_status run_layer(const Pass& P, int l, bool do_ffn, bool xhat_ready, const vo
   }
   {
     ProfScope ps(P.c, DG_PROF_NORM_COMBINE, P.s);
-    HIPCHK(launch_moe_combine_norm(at<float>(ws, w.resid), at<float>(ws, w.y), at<float>(ws, w.sh_parts),
+    HIPCHK(launch_moe_combine_norm(at<float>(ws, w.resid), at<void>(ws, w.y), at<void>(ws, w.sh_parts),
                                    at<float>(ws, w.gates), at<int32_t>(ws, w.inv_perm), R, d.d_model, d.top_k, next_g,
                                    next_out, d.norm_eps, bf, status, P.s));
   }

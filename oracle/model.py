@@ -178,14 +178,15 @@ def silu(x):
 
 
 def swiglu(x, Wg, Wu, Wd, rnd, act_q=None):
-    """SwiGLU FFN: A = silu(x Wg^T) * (x Wu^T), stored (rnd); y = A Wd^T (wide).  With act_q (W8A8
-    experts) both GEMM inputs, x and A, pass through it (per-row e4m3 quantisation) first."""
+    """SwiGLU FFN: A = silu(x Wg^T) * (x Wu^T), stored (rnd); y = A Wd^T, stored (rnd): an expert's
+    output rows are activations like the others (reading 13).  With act_q (W8A8 experts) both GEMM
+    inputs, x and A, pass through it (per-row e4m3 quantisation) first."""
     if act_q is not None:
         x = act_q(x)
     A = rnd(silu(x @ Wg.T) * (x @ Wu.T))
     if act_q is not None:
         A = act_q(A)
-    return A @ Wd.T
+    return rnd(A @ Wd.T)
 
 
 def act_quantiser(cfg):

@@ -73,7 +73,10 @@ def test_tiny_adaptive_run_stops_like_the_oracle(tau, seed):
 
 
 def test_stopped_batch_skips_the_remaining_passes():
-    cfg = configs.C2.replace(n_layers=6, prefix=1024, tau=0.01, lock_threshold=0.9, steps=48, adaptive=True)
+    # tau 0.001: a position locks once its top-2 logit gap passes 0.001 ln 9, so every position of
+    # this random instance locks within a few steps (at 0.01 a few positions whose gaps stay small
+    # can hold the canvas open for tens of steps, depending on the instance's rounding)
+    cfg = configs.C2.replace(n_layers=6, prefix=1024, tau=0.001, lock_threshold=0.9, steps=48, adaptive=True)
     log(f"[adaptive gate] {cfg.n_layers} layers, V {cfg.vocab}, prefix {cfg.prefix}, cap {cfg.steps}")
     model, W, kv = build(cfg)
     ws = model.workspace(cfg.batch, cfg.canvas, cfg.prefix)
