@@ -70,8 +70,8 @@ def parse():
 # (FETCH_SIZE, WRITE_SIZE; KiB per dispatch, mean of 90 launches), each scaled by the same counter
 # on a 512 MiB device-to-device copy (FETCH_SIZE reads 262155.5 KiB for 524288 KiB read: x1.9999;
 # WRITE_SIZE reads 524288 KiB: x1).  Valid only while the kernel sources hash to `sources`.
-MOE_TRAFFIC = {"sources": "c6dd63a6bfc4ddbb4dfb4b1b0ae7e1dafcbb1c4e9edbfa6bde1043d7f07925d9",
-               "fetch_kib": 528091.7, "write_kib": 3872.1, "bytes_per_launch": 1085449388}
+MOE_TRAFFIC = {"sources": "4e802097c351d6f4137324ad04ffafb3f9e0f3d6d0e7bd9e08021dc2bef50169",
+               "fetch_kib": 528680.3, "write_kib": 3872.1, "bytes_per_launch": 1086654788}
 TRAFFIC_SOURCES = ("k_gemm.hip", "gemm_dma.h", "gemm_core.h", "common.h", "internal.h")
 
 
@@ -104,8 +104,9 @@ def class_roofs(cfg, uniq, gate_up_bytes):
     R = B * L
     hbm = lambda b: ("hbm", b, "GB/s", HBM_PEAK_GBS)
     mfma = lambda f: ("mfma", f, "TFLOP/s", MFMA_BF16_PEAK_TFLOPS)
+    # weights, the SwiGLU rows read, the expert output rows written (activation type)
     down = ((uniq * cfg.expert_hidden + cfg.shared_hidden) * d * wb
-            + (R * cfg.top_k * cfg.expert_hidden + R * cfg.shared_hidden) * ab + (R * cfg.top_k + R) * d * 4)
+            + (R * cfg.top_k * cfg.expert_hidden + R * cfg.shared_hidden) * ab + (R * cfg.top_k + R) * d * ab)
     flops = 0.0
     for l in range(nl):
         keys = (cfg.prefix if cfg.is_global(l) else min(cfg.window, cfg.prefix)) + L
