@@ -55,6 +55,7 @@ DG_DEV u32x4 widen_fp4_word(uint32_t w, float sc) {
 // carries the tiles congruent to s mod DEPTH, LDS double-buffers the tile being computed.
 template <class TA, class TB, int BM, int BN, int WM, int WN, int DEPTH = 1>
 struct GemmTile {
+  static constexpr int TILE_M = BM;
   static_assert(WM * WN == 4, "4 waves");
   static constexpr int FM = BM / WM / 16;
   static constexpr int FN = BN / WN / 16;

@@ -50,6 +50,7 @@ DG_DEV void wait_vm() {
 // one barrier per stage: two tiles per stage halve the per-step synchronisation of long K loops).
 template <class T, int BM, int BN, int WM, int WN, int NS, int B_AUX = DMA_STREAM, int KPS = 1>
 struct GemmDma {
+  static constexpr int TILE_M = BM;
   static constexpr int NW = WM * WN;                   // waves per block
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "rows per tile: multiples of 8 x waves");
@@ -226,6 +227,7 @@ struct GemmDma {
 // (2 kg + c) ^ (r >> 1), or a B swizzle on r >> 2, r & 3 or none, at ~110 (bank conflicts).
 template <class TB, int BM, int BN, int WM, int WN, int NS>
 struct GemmDmaQ {
+  static constexpr int TILE_M = BM;
   static constexpr bool FP4 = is_fp4_v<TB>;
   static_assert(FP4 || is_fp8_v<TB>, "quantised weights");
   static constexpr int NW = WM * WN;
@@ -386,6 +388,7 @@ struct GemmDmaQ {
 // halves are zeroed in registers, so those products add exact zeros.
 template <int BM, int BN, int WM, int WN, int NS>
 struct GemmDmaQQ {
+  static constexpr int TILE_M = BM;
   static constexpr int NW = WM * WN;
   static constexpr int FM = BM / WM / 16, FN = BN / WN / 16;
   static_assert(FM >= 1 && FN >= 1, "wave tile at least 16 x 16");

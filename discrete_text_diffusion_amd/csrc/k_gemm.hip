@@ -275,12 +275,26 @@ DG_DEV void grouped_tile(char* lds, const TA* A, int64_t lda, const int32_t* a_t
   f32x4_v acc[G::FM][G::FN];
   g.run(lds, K, acc);
 
+  // Epilogue.  The output tile goes through LDS (the ring is idle once the K loop has ended) so
+  // that the stores are whole 16-byte chunks of its rows, where a lane's own values (4 rows of one
+  // column per fragment) would give 2- or 4-byte stores scattered over four rows; a tile whose
+  // rows do not fit the ring's bytes stores directly.
   const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) % WN;
+  constexpr int NOUT = EPI == EPI_SWIGLU ? BN / 2 : BN;            // output columns of the tile
+  using TS = std::conditional_t<EPI == EPI_STORE_F32, float, TO>;
+  constexpr int ROWB = NOUT * (int)sizeof(TS) + 16;                 // padded LDS row
+  constexpr bool STAGED = G::TILE_M * ROWB <= G::LDS_BYTES;
+  const int c0 = EPI == EPI_SWIGLU ? n0 / 2 : n0;                   // first output column
+  if constexpr (STAGED) __syncthreads();                            // every wave is done with the ring
+  auto put = [&](int r, int cl, float v) {
+    if constexpr (STAGED) *reinterpret_cast<TS*>(lds + r * ROWB + cl * (int)sizeof(TS)) = Elem<TS>::from_f(v);
+    else static_cast<TS*>(Cout)[(int64_t)(row0 + r) * ldc + c0 + cl] = Elem<TS>::from_f(v);
+  };
   if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
     for (int j = 0; j < G::FN; j += 2) {
       const int u = (wn * G::FN + j) >> 1;
-      const int oc = n0 / 2 + u * 16 + (lane & 15);
+      const int cl = u * 16 + (lane & 15), oc = c0 + cl;
       if (oc >= N) continue;
       float sg = 1.f, su = 1.f;
       if constexpr (is_fp8_v<TB>) {
@@ -295,15 +309,13 @@ DG_DEV void grouped_tile(char* lds, const TA* A, int64_t lda, const int32_t* a_t
           if (r >= rows) continue;
           const float sa = ascale(r);
           const float gt = acc[i][j][q] * sg * sa, up = acc[i][j + 1][q] * su * sa;
-          const float a = gt / (1.f + __expf(-gt)) * up;
-          static_cast<TO*>(Cout)[(int64_t)(row0 + r) * ldc + oc] = Elem<TO>::from_f(a);
+          put(r, cl, gt / (1.f + __expf(-gt)) * up);
         }
     }
   } else {  // EPI_STORE_F32 (fp32 rows) or EPI_STORE_ACT (rows of the activation type)
-    using TS = std::conditional_t<EPI == EPI_STORE_ACT, TO, float>;
 #pragma unroll
     for (int j = 0; j < G::FN; ++j) {
-      const int n = n0 + G::col_of(j);
+      const int cl = G::col_of(j), n = c0 + cl;
       if (n >= N) continue;
       float sc = 1.f;
       if constexpr (is_fp8_v<TB>) sc = bf2f(reinterpret_cast<const bf16_t*>(sB)[n]);
@@ -313,8 +325,25 @@ DG_DEV void grouped_tile(char* lds, const TA* A, int64_t lda, const int32_t* a_t
         for (int q = 0; q < 4; ++q) {
           const int r = G::row_of(i, q);
           if (r >= rows) continue;
-          static_cast<TS*>(Cout)[(int64_t)(row0 + r) * ldc + n] = Elem<TS>::from_f(acc[i][j][q] * sc * ascale(r));
+          put(r, cl, acc[i][j][q] * sc * ascale(r));
         }
+    }
+  }
+  if constexpr (STAGED) {
+    __syncthreads();
+    constexpr int EPC = 16 / (int)sizeof(TS);                       // elements per 16-byte chunk
+    constexpr int CH = NOUT / EPC;                                   // chunks per tile row
+    const int ncols = min(NOUT, N - c0);
+    for (int idx = threadIdx.x; idx < rows * CH; idx += blockDim.x) {
+      const int r = idx / CH, ch = idx - r * CH, cl = ch * EPC;
+      if (cl >= ncols) continue;
+      TS* dst = static_cast<TS*>(Cout) + (int64_t)(row0 + r) * ldc + c0 + cl;
+      const char* src = lds + r * ROWB + ch * 16;
+      if (cl + EPC <= ncols && ((uintptr_t)dst & 15) == 0) {
+        *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+      } else {
+        for (int e = 0; e < EPC && cl + e < ncols; ++e) dst[e] = reinterpret_cast<const TS*>(src)[e];
+      }
     }
   }
 }
