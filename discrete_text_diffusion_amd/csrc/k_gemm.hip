@@ -277,8 +277,8 @@ DG_DEV void grouped_tile(char* lds, const TA* A, int64_t lda, const int32_t* a_t
 
   // Epilogue.  The output tile goes through LDS (the ring is idle once the K loop has ended) so
   // that the stores are whole 16-byte chunks of its rows, where a lane's own values (4 rows of one
-  // column per fragment) would give 2- or 4-byte stores scattered over four rows; a tile whose
-  // rows do not fit the ring's bytes stores directly.
+  // column per fragment) would give 2- or 4-byte stores scattered over four rows, and they are
+  // streaming stores; a tile whose rows do not fit the ring's bytes stores directly.
   const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) % WN;
   constexpr int NOUT = EPI == EPI_SWIGLU ? BN / 2 : BN;            // output columns of the tile
   using TS = std::conditional_t<EPI == EPI_STORE_F32, float, TO>;
@@ -340,7 +340,9 @@ DG_DEV void grouped_tile(char* lds, const TA* A, int64_t lda, const int32_t* a_t
       TS* dst = static_cast<TS*>(Cout) + (int64_t)(row0 + r) * ldc + c0 + cl;
       const char* src = lds + r * ROWB + ch * 16;
       if (cl + EPC <= ncols && ((uintptr_t)dst & 15) == 0) {
-        *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+        // streaming stores: the rows go out to memory instead of staying dirty in this XCD's L2
+        // (the next launch reads them, from any XCD)
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(src), reinterpret_cast<u32x4*>(dst));
       } else {
         for (int e = 0; e < EPC && cl + e < ncols; ++e) dst[e] = reinterpret_cast<const TS*>(src)[e];
       }
