@@ -409,7 +409,8 @@ __global__ __launch_bounds__(NW * 64) void flash_kernel(AttnArgs p) {
       const int64_t rh = (int64_t)(b * p.n + qi) * p.Hq + g * G + hj;
       char* dst = partial ? reinterpret_cast<char*>(p.part_o) + (((int64_t)split * p.B * p.n * p.Hq + rh) * DH) * 2
                           : static_cast<char*>(p.out) + rh * DH * 2;
-      *reinterpret_cast<u32x4*>(dst + ch * 16) = v;
+      // streaming stores: the merge or the output projection reads these rows from any XCD
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + ch * 16));
     }
     if (qb + 1 < QPW) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
