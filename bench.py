@@ -70,8 +70,8 @@ def parse():
 # (FETCH_SIZE, WRITE_SIZE; KiB per dispatch, mean of 90 launches), each scaled by the same counter
 # on a 512 MiB device-to-device copy (FETCH_SIZE reads 262155.5 KiB for 524288 KiB read: x1.9999;
 # WRITE_SIZE reads 524288 KiB: x1).  Valid only while the kernel sources hash to `sources`.
-MOE_TRAFFIC = {"sources": "4e802097c351d6f4137324ad04ffafb3f9e0f3d6d0e7bd9e08021dc2bef50169",
-               "fetch_kib": 528680.3, "write_kib": 3872.1, "bytes_per_launch": 1086654788}
+MOE_TRAFFIC = {"sources": "9ada3254b61c6e50adfa2bf4e27b17beccb2e46dfd3b7f6c01fc87d4db09d2ce",
+               "fetch_kib": 528871.9, "write_kib": 3872.0, "bytes_per_launch": 1087047065}
 TRAFFIC_SOURCES = ("k_gemm.hip", "gemm_dma.h", "gemm_core.h", "common.h", "internal.h")
 
 
