@@ -46,6 +46,19 @@ DG_DEV void paired_col(int r, int& u, int& half, int& c) {
 // 1-D grid, XCD-aware: block id mod 8 picks the XCD; the n_mt row tiles of one column (weight)
 // tile get ids congruent mod 8, so they run on one XCD and share its L2 copy of the weights.
 // blockIdx.y is the split-K part.
+// The QKV epilogue stages a q / k tile of BM rows (padded by 16 bytes) in LDS when it fits in a CU's
+// 160 KB; the dense launch's dynamic LDS is the larger of that and the ring.
+template <class TA, int BM, int BN, int EPI>
+constexpr int qkv_stage_bytes() {
+  const int b = BM * (BN * (int)sizeof(TA) + 16);
+  return EPI == EPI_QKV && b <= 160 * 1024 && (BN / 2) % (16 / (int)sizeof(TA)) == 0 ? b : 0;
+}
+template <class G, class TA, int BM, int BN, int EPI>
+constexpr size_t dense_lds_bytes() {
+  return (size_t)qkv_stage_bytes<TA, BM, BN, EPI>() > G::LDS_BYTES ? (size_t)qkv_stage_bytes<TA, BM, BN, EPI>()
+                                                                    : G::LDS_BYTES;
+}
+
 template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI, int MAP, int NS = 0, int KPS = 1>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_dense_kernel(DenseArgs p) {
   if (gate_closed(p.gate)) return;
@@ -84,11 +97,31 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dense_kernel(DenseArgs p) {
   };
   G g;
   g.setup(arow, brow);
+  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) % WN;
+  // QKV: where they take few registers, this lane's (cos, sin) table entries are loaded before the
+  // K loop, so their latency passes under it instead of trailing it (rows past M read row M - 1)
+  constexpr int NCS = G::FM * (G::FN / 2) * 4;
+  constexpr bool CS_AHEAD = EPI == EPI_QKV && NCS <= 16;
+  float2 cs_pre[CS_AHEAD ? NCS : 1];
+  if constexpr (CS_AHEAD) {
+    const int head = n0 / p.dh, pb = (n0 % p.dh) / 2, half_dh = p.dh / 2;
+    if (head < p.Hq + p.Hkv) {
+#pragma unroll
+      for (int j = 0; j < G::FN; j += 2)
+#pragma unroll
+        for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int m = min(m0 + G::row_of(i, e), p.M - 1);
+            const int jj = pb + ((wn * G::FN + j) >> 1) * 16 + (lane & 15);
+            cs_pre[((j >> 1) * G::FM + i) * 4 + e] = p.rope[(int64_t)m * half_dh + jj];
+          }
+    }
+  }
   f32x4_v acc[G::FM][G::FN];
   g.run(lds, kpart, acc);
   float* const C32 = static_cast<float*>(p.C) + (int64_t)blockIdx.y * p.c_split;
 
-  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) % WN;
   if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_ADD_F32 || EPI == EPI_STORE_ACT) {
 #pragma unroll
     for (int j = 0; j < G::FN; ++j) {
@@ -137,26 +170,60 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dense_kernel(DenseArgs p) {
     // angle table holds (cos, sin) of row m's position for pair jj
     const int dh = p.dh, half_dh = dh / 2;
     const int head = n0 / dh, pb = (n0 % dh) / 2;
+    // q / k rows of one head: the tile's BN columns are the dims pb + [0, BN/2) and half_dh + pb +
+    // [0, BN/2).  Where the ring's LDS holds the tile (rows padded by 16 bytes), the rotated values
+    // go there first, staged column c < BN/2 for dim pb + c and BN/2 + c for half_dh + pb + c, and
+    // leave as whole 16-byte row chunks rather than one element per lane and store.
+    constexpr int ROWB = BN * (int)sizeof(TA) + 16;
+    constexpr int EPC = 16 / (int)sizeof(TA);            // elements per 16-byte chunk
+    constexpr bool STAGED = qkv_stage_bytes<TA, BM, BN, EPI>() > 0;
+    auto qk_row = [&](int m) -> TA* {
+      if (head < p.Hq) return static_cast<TA*>(p.q_out) + ((int64_t)m * p.Hq + head) * dh;
+      const int b = m / p.rows_per_canvas, ii = m - b * p.rows_per_canvas;
+      return static_cast<TA*>(p.k_out) + (((int64_t)b * p.Hkv + head - p.Hq) * p.rows_per_canvas + ii) * dh;
+    };
     if (head < p.Hq + p.Hkv) {           // q [rows][Hq][dh], canvas k [B][Hkv][n][dh], rotated
 #pragma unroll
       for (int j = 0; j < G::FN; j += 2) {
         const int u = (wn * G::FN + j) >> 1;
-        const int jj = pb + u * 16 + (lane & 15);        // pair index in [0, dh/2)
+        const int c = u * 16 + (lane & 15);              // pair index - pb
+        const int jj = pb + c;                           // pair index in [0, dh/2)
 #pragma unroll
         for (int i = 0; i < G::FM; ++i)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int m = m0 + G::row_of(i, e);
+            const int r = G::row_of(i, e), m = m0 + r;
             if (m >= p.M) continue;
-            const int b = m / p.rows_per_canvas, ii = m - b * p.rows_per_canvas;
-            const float2 cs = p.rope[(int64_t)m * half_dh + jj];
+            float2 cs;
+            if constexpr (CS_AHEAD) cs = cs_pre[((j >> 1) * G::FM + i) * 4 + e];
+            else cs = p.rope[(int64_t)m * half_dh + jj];
             const float x1 = acc[i][j][e], x2 = acc[i][j + 1][e];
-            TA* dst = head < p.Hq ? static_cast<TA*>(p.q_out) + ((int64_t)m * p.Hq + head) * dh
-                                  : static_cast<TA*>(p.k_out) +
-                                        (((int64_t)b * p.Hkv + head - p.Hq) * p.rows_per_canvas + ii) * dh;
-            dst[jj] = Elem<TA>::from_f(x1 * cs.x - x2 * cs.y);
-            dst[jj + half_dh] = Elem<TA>::from_f(x2 * cs.x + x1 * cs.y);
+            const TA y1 = Elem<TA>::from_f(x1 * cs.x - x2 * cs.y), y2 = Elem<TA>::from_f(x2 * cs.x + x1 * cs.y);
+            if constexpr (STAGED) {
+              TA* row = reinterpret_cast<TA*>(lds + r * ROWB);
+              row[c] = y1;
+              row[BN / 2 + c] = y2;
+            } else {
+              TA* dst = qk_row(m);
+              dst[jj] = y1;
+              dst[jj + half_dh] = y2;
+            }
           }
+      }
+      if constexpr (STAGED) {
+        __syncthreads();
+        constexpr int CPR = BN / EPC;                    // chunks per staged row
+        for (int ch = threadIdx.x; ch < BM * CPR; ch += WM * WN * 64) {
+          const int r = ch / CPR, col = (ch - r * CPR) * EPC, m = m0 + r;
+          if (m >= p.M) continue;
+          TA* dst = qk_row(m) + (col < BN / 2 ? pb + col : half_dh + pb + col - BN / 2);
+          const char* src = lds + r * ROWB + col * (int)sizeof(TA);
+          if (((uintptr_t)dst & 15) == 0) {
+            *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+          } else {
+            for (int k = 0; k < EPC; ++k) dst[k] = reinterpret_cast<const TA*>(src)[k];
+          }
+        }
       }
     } else {                             // canvas v, d-major [B][Hkv][dh][v_ld], not rotated
       TA* vbase = static_cast<TA*>(p.v_out) + (int64_t)(head - p.Hq - p.Hkv) * dh * p.v_ld;
@@ -425,10 +492,11 @@ static hipError_t launch_dense_t(DenseArgs a, int n_eff, hipStream_t s) {
   if (a.K % (a.ksplit * G::KT * KPS)) return hipErrorInvalidValue;
   dim3 grid(a.n_mt * ((a.n_nt + 7) / 8 * 8), a.ksplit);
   a.gate = launch_gate();
-  static const hipError_t attr = allow_lds(gemm_dense_kernel<TA, TB, BM, BN, WM, WN, EPI, MAP, NS, KPS>, G::LDS_BYTES);
+  constexpr size_t LDS = dense_lds_bytes<G, TA, BM, BN, EPI>();
+  static const hipError_t attr = allow_lds(gemm_dense_kernel<TA, TB, BM, BN, WM, WN, EPI, MAP, NS, KPS>, LDS);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((gemm_dense_kernel<TA, TB, BM, BN, WM, WN, EPI, MAP, NS, KPS>), grid, dim3(WM * WN * 64),
-                     G::LDS_BYTES, s, a);
+                     LDS, s, a);
   return hipGetLastError();
 }
 
