@@ -70,8 +70,8 @@ def parse():
 # (FETCH_SIZE, WRITE_SIZE; KiB per dispatch, mean of 90 launches), each scaled by the same counter
 # on a 512 MiB device-to-device copy (FETCH_SIZE reads 262155.5 KiB for 524288 KiB read: x1.9999;
 # WRITE_SIZE reads 524288 KiB: x1).  Valid only while the kernel sources hash to `sources`.
-MOE_TRAFFIC = {"sources": "9ada3254b61c6e50adfa2bf4e27b17beccb2e46dfd3b7f6c01fc87d4db09d2ce",
-               "fetch_kib": 528871.9, "write_kib": 3872.0, "bytes_per_launch": 1087047065}
+MOE_TRAFFIC = {"sources": "295a1df35a417ac9be59f30c19c4994d1f981579ca12f17f3cbb9c083400bb3e",
+               "fetch_kib": 528903.8, "write_kib": 3872.0, "bytes_per_launch": 1087112394}
 TRAFFIC_SOURCES = ("k_gemm.hip", "gemm_dma.h", "gemm_core.h", "common.h", "internal.h")
 
 
