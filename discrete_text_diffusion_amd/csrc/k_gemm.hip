@@ -46,17 +46,25 @@ DG_DEV void paired_col(int r, int& u, int& half, int& c) {
 // 1-D grid, XCD-aware: block id mod 8 picks the XCD; the n_mt row tiles of one column (weight)
 // tile get ids congruent mod 8, so they run on one XCD and share its L2 copy of the weights.
 // blockIdx.y is the split-K part.
-// The QKV epilogue stages a q / k tile of BM rows (padded by 16 bytes) in LDS when it fits in a CU's
-// 160 KB; the dense launch's dynamic LDS is the larger of that and the ring.
+// Epilogues that stage the output tile in LDS (rows padded by 16 bytes) when it fits in a CU's
+// 160 KB: the QKV q / k rows (in the activation type) and the float32 (split-K) stores.  The dense
+// launch's dynamic LDS is the larger of that and the ring.
 template <class TA, int BM, int BN, int EPI>
 constexpr int qkv_stage_bytes() {
   const int b = BM * (BN * (int)sizeof(TA) + 16);
   return EPI == EPI_QKV && b <= 160 * 1024 && (BN / 2) % (16 / (int)sizeof(TA)) == 0 ? b : 0;
 }
+template <int BM, int BN, int EPI>
+constexpr int f32_stage_bytes() {
+  const int b = BM * (BN * 4 + 16);
+  return EPI == EPI_STORE_F32 && b <= 160 * 1024 && BN % 4 == 0 ? b : 0;
+}
 template <class G, class TA, int BM, int BN, int EPI>
 constexpr size_t dense_lds_bytes() {
-  return (size_t)qkv_stage_bytes<TA, BM, BN, EPI>() > G::LDS_BYTES ? (size_t)qkv_stage_bytes<TA, BM, BN, EPI>()
-                                                                    : G::LDS_BYTES;
+  size_t b = G::LDS_BYTES;
+  if ((size_t)qkv_stage_bytes<TA, BM, BN, EPI>() > b) b = qkv_stage_bytes<TA, BM, BN, EPI>();
+  if ((size_t)f32_stage_bytes<BM, BN, EPI>() > b) b = f32_stage_bytes<BM, BN, EPI>();
+  return b;
 }
 
 template <class TA, class TB, int BM, int BN, int WM, int WN, int EPI, int MAP, int NS = 0, int KPS = 1>
@@ -122,7 +130,38 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dense_kernel(DenseArgs p) {
   g.run(lds, kpart, acc);
   float* const C32 = static_cast<float*>(p.C) + (int64_t)blockIdx.y * p.c_split;
 
-  if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_ADD_F32 || EPI == EPI_STORE_ACT) {
+  if constexpr (f32_stage_bytes<BM, BN, EPI>() > 0) {
+    // float32 tile through LDS, then whole 16-byte row chunks, streamed (the next launch reads
+    // each partial once, from any XCD)
+    constexpr int ROWB = BN * 4 + 16;
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j) {
+      const int c = G::col_of(j), n = n0 + c;
+      float sc = 1.f, bias = 0.f;
+      if (n < p.N) {
+        if constexpr (sizeof(TB) == 1) sc = bf2f(p.sB[n]);
+        if (p.bias) bias = p.bias[n];
+      }
+#pragma unroll
+      for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          reinterpret_cast<float*>(lds + G::row_of(i, e) * ROWB)[c] = acc[i][j][e] * sc + bias;
+    }
+    __syncthreads();
+    constexpr int CPR = BN / 4;
+    for (int ch = threadIdx.x; ch < BM * CPR; ch += WM * WN * 64) {
+      const int r = ch / CPR, col = (ch - r * CPR) * 4, m = m0 + r, n = n0 + col;
+      if (m >= p.M || n >= p.N) continue;
+      float* dst = C32 + (int64_t)m * p.ldc + n;
+      const float* src = reinterpret_cast<const float*>(lds + r * ROWB) + col;
+      if (n + 4 <= p.N && ((uintptr_t)dst & 15) == 0) {
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(src), reinterpret_cast<u32x4*>(dst));
+      } else {
+        for (int k = 0; k < 4 && n + k < p.N; ++k) dst[k] = src[k];
+      }
+    }
+  } else if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_ADD_F32 || EPI == EPI_STORE_ACT) {
 #pragma unroll
     for (int j = 0; j < G::FN; ++j) {
       const int n = n0 + G::col_of(j);
