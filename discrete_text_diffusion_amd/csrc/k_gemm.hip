@@ -59,10 +59,17 @@ constexpr int f32_stage_bytes() {
   const int b = BM * (BN * 4 + 16);
   return EPI == EPI_STORE_F32 && b <= 160 * 1024 && BN % 4 == 0 ? b : 0;
 }
+// the QKV v tile, transposed: BN dims of BM positions each (padded by 16 bytes)
+template <class TA, int BM, int BN, int EPI>
+constexpr int v_stage_bytes() {
+  const int b = BN * (BM * (int)sizeof(TA) + 16);
+  return EPI == EPI_QKV && b <= 160 * 1024 && BM % (16 / (int)sizeof(TA)) == 0 ? b : 0;
+}
 template <class G, class TA, int BM, int BN, int EPI>
 constexpr size_t dense_lds_bytes() {
   size_t b = G::LDS_BYTES;
   if ((size_t)qkv_stage_bytes<TA, BM, BN, EPI>() > b) b = qkv_stage_bytes<TA, BM, BN, EPI>();
+  if ((size_t)v_stage_bytes<TA, BM, BN, EPI>() > b) b = v_stage_bytes<TA, BM, BN, EPI>();
   if ((size_t)f32_stage_bytes<BM, BN, EPI>() > b) b = f32_stage_bytes<BM, BN, EPI>();
   return b;
 }
@@ -261,6 +268,49 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dense_kernel(DenseArgs p) {
             *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
           } else {
             for (int k = 0; k < EPC; ++k) dst[k] = reinterpret_cast<const TA*>(src)[k];
+          }
+        }
+      }
+    } else if constexpr (v_stage_bytes<TA, BM, BN, EPI>() > 0) {
+      // canvas v, d-major [B][Hkv][dh][v_ld], not rotated: the tile goes to LDS transposed (staged
+      // row c < BN/2 holds dim pb + c, BN/2 + c dim half_dh + pb + c; four positions per 8- or
+      // 16-byte write), then leaves as whole 16-byte chunks of consecutive positions of one dim
+      constexpr int VROWB = BM * (int)sizeof(TA) + 16;
+      TA* vbase = static_cast<TA*>(p.v_out) + (int64_t)(head - p.Hq - p.Hkv) * dh * p.v_ld;
+      const int64_t bstride = (int64_t)p.Hkv * dh * p.v_ld;
+#pragma unroll
+      for (int j = 0; j < G::FN; ++j) {
+        const int c = (j & 1) * (BN / 2) + ((wn * G::FN + j) >> 1) * 16 + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < G::FM; ++i) {
+          char* dst = lds + c * VROWB + G::row_of(i, 0) * (int)sizeof(TA);
+          if constexpr (sizeof(TA) == 2) {
+            uint2 w;
+            w.x = pack_bf2(acc[i][j][0], acc[i][j][1]);
+            w.y = pack_bf2(acc[i][j][2], acc[i][j][3]);
+            *reinterpret_cast<uint2*>(dst) = w;
+          } else {
+            *reinterpret_cast<f32x4_v*>(dst) = acc[i][j];
+          }
+        }
+      }
+      __syncthreads();
+      constexpr int EPC = 16 / (int)sizeof(TA);
+      constexpr int CPR = BM / EPC;                      // chunks per staged dim
+      const bool whole = p.rows_per_canvas % EPC == 0 && (p.v_ld * (int)sizeof(TA)) % 16 == 0;
+      for (int ch = threadIdx.x; ch < BN * CPR; ch += WM * WN * 64) {
+        const int c = ch / CPR, r0 = (ch - c * CPR) * EPC, m = m0 + r0;
+        if (m >= p.M) continue;
+        const int d = c < BN / 2 ? pb + c : half_dh + pb + c - BN / 2;
+        const TA* src = reinterpret_cast<const TA*>(lds + c * VROWB) + r0;
+        const int b = m / p.rows_per_canvas, ii = m - b * p.rows_per_canvas;
+        TA* dst = vbase + b * bstride + (int64_t)d * p.v_ld + ii;
+        if (whole && m + EPC <= p.M && ((uintptr_t)dst & 15) == 0) {
+          *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+        } else {
+          for (int k = 0; k < EPC && m + k < p.M; ++k) {
+            const int be = (m + k) / p.rows_per_canvas, ie = m + k - be * p.rows_per_canvas;
+            vbase[be * bstride + (int64_t)d * p.v_ld + ie] = src[k];
           }
         }
       }
