@@ -70,8 +70,8 @@ def parse():
 # (FETCH_SIZE, WRITE_SIZE; KiB per dispatch, mean of 90 launches), each scaled by the same counter
 # on a 512 MiB device-to-device copy (FETCH_SIZE reads 262155.5 KiB for 524288 KiB read: x1.9999;
 # WRITE_SIZE reads 524288 KiB: x1).  Valid only while the kernel sources hash to `sources`.
-MOE_TRAFFIC = {"sources": "295a1df35a417ac9be59f30c19c4994d1f981579ca12f17f3cbb9c083400bb3e",
-               "fetch_kib": 528903.8, "write_kib": 3872.0, "bytes_per_launch": 1087112394}
+MOE_TRAFFIC = {"sources": "6937b3b3e5853e250b9dd770d3321a969d6102ed84401968a1d09ae5d3902821",
+               "fetch_kib": 528487.8, "write_kib": 3872.0, "bytes_per_launch": 1086260463}
 TRAFFIC_SOURCES = ("k_gemm.hip", "gemm_dma.h", "gemm_core.h", "common.h", "internal.h")
 
 

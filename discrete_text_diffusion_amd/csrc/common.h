@@ -170,15 +170,20 @@ DG_DEV float wave_max(float v) {
 // ---------------------------------------------------------------- Philox4x32-10 ---------------
 // Salmon et al., SC'11: ten rounds; each multiplies counter words 0 and 2 by fixed constants,
 // mixes the high halves with words 1, 3 and the round key; the key is bumped by Weyl constants.
+// One 32 x 32 -> 64-bit product per word (v_mad_u64_u32 gives both halves in one instruction);
+// the three-way exclusive or is one v_bitop3_b32 (truth table 0x96).
+DG_DEV uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) { return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96); }
+
+DG_DEV void philox_round(uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3, uint32_t k0, uint32_t k1) {
+  const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u, p1 = (uint64_t)c2 * 0xCD9E8D57u;
+  const uint32_t n0 = xor3((uint32_t)(p1 >> 32), c1, k0), n2 = xor3((uint32_t)(p0 >> 32), c3, k1);
+  c0 = n0; c1 = (uint32_t)p1; c2 = n2; c3 = (uint32_t)p0;
+}
+
 DG_DEV u32x4 philox(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    // one 32 x 32 -> 64-bit product per word (v_mad_u64_u32 gives both halves in one instruction)
-    const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u, p1 = (uint64_t)c2 * 0xCD9E8D57u;
-    const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
-    const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
-    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
-    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+    philox_round(c0, c1, c2, c3, k0, k1);
     k0 += 0x9E3779B9u; k1 += 0xBB67AE85u;
   }
   return u32x4{c0, c1, c2, c3};
