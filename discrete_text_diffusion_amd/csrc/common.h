@@ -167,6 +167,11 @@ DG_DEV float wave_max(float v) {
   return fmaxf(__uint_as_float(a), __uint_as_float(b));
 }
 
+// SiLU g * sigmoid(g) with the hardware reciprocal (about 1 ulp) in place of an IEEE division:
+// exp(-g) overflows to +inf for very negative g, whose reciprocal is 0, so the result is -0 as
+// with the division
+DG_DEV float silu(float g) { return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)); }
+
 // ---------------------------------------------------------------- Philox4x32-10 ---------------
 // Salmon et al., SC'11: ten rounds; each multiplies counter words 0 and 2 by fixed constants,
 // mixes the high halves with words 1, 3 and the round key; the key is bumped by Weyl constants.

@@ -207,7 +207,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dense_kernel(DenseArgs p) {
           const int m = m0 + G::row_of(i, e);
           if (m >= p.M) continue;
           const float gt = acc[i][j][e] * sg, up = acc[i][j + 1][e] * su;
-          const float a = gt / (1.f + __expf(-gt)) * up;
+          const float a = silu(gt) * up;
           static_cast<TA*>(p.C)[(int64_t)m * p.ldc + oc] = Elem<TA>::from_f(a);
         }
     }
@@ -465,7 +465,7 @@ DG_DEV void grouped_tile(char* lds, const TA* A, int64_t lda, const int32_t* a_t
           if (r >= rows) continue;
           const float sa = ascale(r);
           const float gt = acc[i][j][q] * sg * sa, up = acc[i][j + 1][q] * su * sa;
-          put(r, cl, gt / (1.f + __expf(-gt)) * up);
+          put(r, cl, silu(gt) * up);
         }
     }
   } else {  // EPI_STORE_F32 (fp32 rows) or EPI_STORE_ACT (rows of the activation type)
