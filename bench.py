@@ -70,8 +70,8 @@ def parse():
 # (FETCH_SIZE, WRITE_SIZE; KiB per dispatch, mean of 90 launches), each scaled by the same counter
 # on a 512 MiB device-to-device copy (FETCH_SIZE reads 262155.5 KiB for 524288 KiB read: x1.9999;
 # WRITE_SIZE reads 524288 KiB: x1).  Valid only while the kernel sources hash to `sources`.
-MOE_TRAFFIC = {"sources": "6937b3b3e5853e250b9dd770d3321a969d6102ed84401968a1d09ae5d3902821",
-               "fetch_kib": 528487.8, "write_kib": 3872.0, "bytes_per_launch": 1086260463}
+MOE_TRAFFIC = {"sources": "a788bd3f38ac425f9a1b5abad2545458f03ea03317db0891063df1b4d95bd561",
+               "fetch_kib": 527983.5, "write_kib": 3872.0, "bytes_per_launch": 1085227651}
 TRAFFIC_SOURCES = ("k_gemm.hip", "gemm_dma.h", "gemm_core.h", "common.h", "internal.h")
 
 
