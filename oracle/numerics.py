@@ -89,13 +89,17 @@ def round_e4m3(x):
 
 def quant_rows_e4m3(x):
     """Per-row dynamic e4m3 quantisation of activations x [..., K] (bf16-valued float64): the row's
-    scale s = fp32(max|x|) / 448 in float32, each element coded as the nearest e4m3 value of the
-    float32 quotient fp32(x) / s (IEEE division, the decision the kernels take in float32); an
-    all-zero row has s = 1.  Returns (dequantised values q * s as float64, s as float64)."""
+    scale s = fp32(max|x|) / 448 in float32, and its reciprocal r = 448 / fp32(max|x|) (one IEEE
+    float32 division per row); each element is coded as the nearest e4m3 value of the float32
+    product fp32(x) * r (the decision the kernels take in float32); an all-zero row has s = r = 1.
+    Returns (dequantised values q * s as float64, s as float64)."""
     x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
     amax = np.max(np.abs(x32), axis=-1, keepdims=True)
-    s = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
-    q = round_e4m3((x32 / s).astype(np.float64))
+    pos = amax > 0
+    safe = np.where(pos, amax, np.float32(1.0)).astype(np.float32)
+    s = np.where(pos, safe / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    r = np.where(pos, np.float32(E4M3_MAX) / safe, np.float32(1.0)).astype(np.float32)
+    q = round_e4m3((x32 * r).astype(np.float64))
     return q * s.astype(np.float64), s[..., 0].astype(np.float64)
 
 
