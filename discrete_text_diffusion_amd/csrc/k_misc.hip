@@ -83,10 +83,11 @@ DG_DEV uint32_t e4m3_code(float q) {
   return sign | code;
 }
 
-// One wave per row: s = max|x| / 448 in float32 (1 for a zero row), codes of x / s.  The row stays
-// in registers between the max and the coding (CH 16-byte chunks per lane, K <= 512 CH), so it is
-// read once.  The build keeps IEEE float division (no fast-math): both quotients are correctly
-// rounded.
+// One wave per row: s = max|x| / 448 in float32 (1 for a zero row), and the codes of the float32
+// products x * r with r = 448 / max|x| (1 for a zero row), one division per row.  The row stays in
+// registers between the max and the coding (CH 16-byte chunks per lane, K <= 512 CH), so it is read
+// once.  The build keeps IEEE float division (no fast-math): s and r are correctly rounded, and
+// each product is a single rounded multiply.
 template <int WPB, int CH>
 __global__ __launch_bounds__(WPB * 64) void quant_rows_kernel(const bf16_t* x, int64_t ldx, int rows, int K,
                                                              uint8_t* q, float* s, const int32_t* gate) {
@@ -111,6 +112,7 @@ __global__ __launch_bounds__(WPB * 64) void quant_rows_kernel(const bf16_t* x, i
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
   const float sc = amax > 0.f ? amax / 448.f : 1.f;
+  const float rc = amax > 0.f ? 448.f / amax : 1.f;
   if (lane == 0) s[r] = sc;
   uint8_t* qr = q + (int64_t)r * K;
 #pragma unroll
@@ -121,8 +123,8 @@ __global__ __launch_bounds__(WPB * 64) void quant_rows_kernel(const bf16_t* x, i
     uint32_t out[2] = {0u, 0u};
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const uint32_t lo = e4m3_code(__uint_as_float(w[h] << 16) / sc);
-      const uint32_t hi = e4m3_code(__uint_as_float(w[h] & 0xffff0000u) / sc);
+      const uint32_t lo = e4m3_code(__fmul_rn(__uint_as_float(w[h] << 16), rc));
+      const uint32_t hi = e4m3_code(__fmul_rn(__uint_as_float(w[h] & 0xffff0000u), rc));
       out[h >> 1] |= (lo | (hi << 8)) << (16 * (h & 1));
     }
     *reinterpret_cast<uint2*>(qr + k) = make_uint2(out[0], out[1]);
