@@ -60,34 +60,12 @@ hipError_t launch_sum_parts_cast(const float* parts, int nparts, int64_t pstride
 }
 
 // ---------------------------------------------------------------- W8A8 activation codes --------
-// Nearest OCP e4m3 (e4m3fn) code of a float32 value, ties to even, saturating at +-448.  From the
-// format: 4 exponent bits (bias 7), 3 mantissa bits, no infinities, S.1111.111 is NaN.  Below
-// 2^-6 the codes are subnormal with spacing 2^-9, so code = round(|q| / 2^-9); from 2^-6 up the
-// spacing in [2^e, 2^(e+1)) is 2^(e-3) and code = 8 (e + 7) + round(|q| / 2^(e-3)) - 8.  A mantissa
-// that rounds up to 16 lands on the next binade's first code, so both formulas run on into the
-// next range; 448 = 1.75 * 2^8 is code 0x7e, the largest finite one.
-DG_DEV uint32_t e4m3_code(float q) {
-  const uint32_t sign = (__float_as_uint(q) >> 24) & 0x80u;
-  const float a = fabsf(q);
-  uint32_t code;
-  if (!(a < 448.f)) {
-    code = 0x7eu;
-  } else if (a < 0.015625f) {                                  // 2^-6
-    code = (uint32_t)rintf(a * 512.f);                         // exact scaling by 2^9, then RNE
-  } else {
-    const int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;   // a is a normal float here
-    const float m = rintf(ldexpf(a, 3 - e));                   // in [8, 16], exact scaling
-    code = (uint32_t)((e + 7) * 8 + (int)m - 8);
-    code = code > 0x7eu ? 0x7eu : code;
-  }
-  return sign | code;
-}
-
-// One wave per row: s = max|x| / 448 in float32 (1 for a zero row), and the codes of the float32
-// products x * r with r = 448 / max|x| (1 for a zero row), one division per row.  The row stays in
-// registers between the max and the coding (CH 16-byte chunks per lane, K <= 512 CH), so it is read
-// once.  The build keeps IEEE float division (no fast-math): s and r are correctly rounded, and
-// each product is a single rounded multiply.
+// One wave per row: s = max|x| / 448 in float32 (1 for a zero row), and the nearest OCP e4m3
+// (e4m3fn: bias 7, 3 mantissa bits, largest finite 448) codes of the float32 products x * r with
+// r = 448 / max|x| (1 for a zero row), one division per row; ties go to the even code and values
+// beyond 448 saturate.  The row stays in registers between the max and the coding (CH 16-byte
+// chunks per lane, K <= 512 CH), so it is read once.  The build keeps IEEE float division (no
+// fast-math): s and r are correctly rounded, and each product is a single rounded multiply.
 template <int WPB, int CH>
 __global__ __launch_bounds__(WPB * 64) void quant_rows_kernel(const bf16_t* x, int64_t ldx, int rows, int K,
                                                              uint8_t* q, float* s, const int32_t* gate) {
@@ -120,12 +98,17 @@ __global__ __launch_bounds__(WPB * 64) void quant_rows_kernel(const bf16_t* x, i
     const int k = (c * 64 + lane) * 8;
     if (k >= K) continue;
     const uint32_t w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
-    uint32_t out[2] = {0u, 0u};
+    // the hardware conversion rounds to nearest even; the clamp to +-448 makes it saturate.  Two
+    // bf16 elements per word, four codes per output word (the second pair into its upper half)
+    auto prod = [&](uint32_t word, bool upper) {
+      const float v = __fmul_rn(__uint_as_float(upper ? word & 0xffff0000u : word << 16), rc);
+      return fminf(fmaxf(v, -448.f), 448.f);
+    };
+    uint32_t out[2];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const uint32_t lo = e4m3_code(__fmul_rn(__uint_as_float(w[h] << 16), rc));
-      const uint32_t hi = e4m3_code(__fmul_rn(__uint_as_float(w[h] & 0xffff0000u), rc));
-      out[h >> 1] |= (lo | (hi << 8)) << (16 * (h & 1));
+    for (int o = 0; o < 2; ++o) {
+      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(prod(w[2 * o], false), prod(w[2 * o], true), 0, false);
+      out[o] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(prod(w[2 * o + 1], false), prod(w[2 * o + 1], true), lo, true);
     }
     *reinterpret_cast<uint2*>(qr + k) = make_uint2(out[0], out[1]);
   }
